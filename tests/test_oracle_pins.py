@@ -1,0 +1,527 @@
+"""Pins of the fp64 oracle to facts other than itself (CPU only).
+
+Each test fixes one part of the oracle against brute force on tiny inputs, a
+closed form, a special case that reduces to a library routine (torch / scipy
+in fp64), or a number the pages print.  They are chosen so that a plausible
+slip -- swapped gate and up, a transposed down matrix, a wrong tie-break, a
+missing renormalisation, blocks laid out along the wrong axis -- fails one of
+them.
+"""
+import itertools
+import json
+import math
+import os
+
+import numpy as np
+import pytest
+import scipy.special
+import torch
+
+import oracle as O
+
+GOLDEN = os.path.join(os.path.dirname(__file__), "golden")
+
+
+def bf16_bits(x):
+    """Bits of fp32 values that are exactly representable in bf16 (test helper)."""
+    a = np.asarray(x, np.float32)
+    u = a.view(np.uint32)
+    assert np.all((u & 0xFFFF) == 0), "value not exactly representable in bf16"
+    return (u >> 16).astype(np.uint16)
+
+
+def rand_bf16(rng, shape, scale=0.5):
+    """Random bf16 bit patterns of moderate magnitude (truncation of fp32 draws)."""
+    f = (rng.standard_normal(shape) * scale).astype(np.float32)
+    return (f.view(np.uint32) >> 16).astype(np.uint16)
+
+
+# ---------------------------------------------------------------- formats
+
+def test_bf16_decoding_matches_format_definition():
+    # bf16 = sign(1) | exponent(8, bias 127) | fraction(7)
+    cases = {
+        0x3F80: 1.0, 0xBF80: -1.0, 0x4000: 2.0, 0x3F81: 1.0 + 2.0 ** -7,
+        0x0080: 2.0 ** -126, 0x0001: 2.0 ** -133, 0x7F7F: (2.0 - 2.0 ** -7) * 2.0 ** 127,
+        0x3C00: 2.0 ** -7, 0xC140: -12.0,
+    }
+    got = O.bf16_to_f64(np.array(list(cases), np.uint16))
+    assert list(got) == list(cases.values())
+    assert np.isinf(O.bf16_to_f64(np.array([0x7F80], np.uint16))[0])
+    z = O.bf16_to_f64(np.array([0x8000], np.uint16))[0]
+    assert z == 0.0 and math.copysign(1.0, z) < 0
+
+
+def test_silu_closed_forms():
+    x = np.array([0.0, math.log(3.0), -math.log(3.0), 40.0, -40.0])
+    got = O.silu(x)
+    want = [0.0, 0.75 * math.log(3.0), -0.25 * math.log(3.0), 40.0, 0.0]
+    np.testing.assert_allclose(got, want, rtol=1e-15, atol=1e-15)
+    assert O.silu(np.array([-1000.0]))[0] == 0.0  # no overflow warning leaks as nan
+
+
+# ---------------------------------------------------------------- router
+
+def test_router_logits_brute_force():
+    rng = np.random.default_rng(1)
+    M, H, E = 3, 7, 5
+    h = rng.standard_normal((M, H)).astype(np.float32)
+    W = rand_bf16(rng, (H, E))
+    bias = rng.standard_normal(E).astype(np.float32)
+    got = O.router_logits(h, W, bias)
+    Wf = O.bf16_to_f64(W)
+    for t in range(M):
+        for e in range(E):
+            acc = 0.0
+            for i in range(H):
+                acc += float(h[t, i]) * float(Wf[i, e])
+            assert abs(got[t, e] - (acc + float(bias[e]))) < 1e-12
+
+
+def test_topk_matches_full_sort_with_ties():
+    rng = np.random.default_rng(2)
+    for trial in range(200):
+        M, E = 3, int(rng.integers(2, 20))
+        k = int(rng.integers(1, E + 1))
+        l = rng.integers(-3, 4, size=(M, E)).astype(np.float64)  # many exact ties
+        ids = O.topk_select(l, k)
+        for t in range(M):
+            want = sorted(range(E), key=lambda e: (-l[t, e], e))[:k]
+            assert list(ids[t]) == want
+
+
+def test_topk_tie_goes_to_lower_expert_id():
+    l = np.array([[0.5, 2.0, 2.0, -1.0, 2.0]])
+    assert list(O.topk_select(l, 3)[0]) == [1, 2, 4]
+    assert list(O.topk_select(l, 4)[0]) == [1, 2, 4, 0]
+
+
+def test_affinity_with_k_equal_E_is_the_full_softmax():
+    rng = np.random.default_rng(3)
+    l = rng.standard_normal((4, 9)) * 3
+    ids = O.topk_select(l, 9)
+    a = O.affinities(l, ids)
+    want = np.take_along_axis(scipy.special.softmax(l, axis=1), ids, axis=1)
+    np.testing.assert_allclose(a, want, rtol=1e-14)
+
+
+def test_affinity_renormalises_and_is_shift_invariant():
+    rng = np.random.default_rng(4)
+    l = rng.standard_normal((5, 16))
+    ids = O.topk_select(l, 4)
+    a = O.affinities(l, ids)
+    np.testing.assert_allclose(a.sum(axis=1), 1.0, rtol=1e-15)
+    assert np.all(np.diff(a, axis=1) <= 0)                     # slots in descending order
+    np.testing.assert_allclose(O.affinities(l + 7.25, ids), a, rtol=1e-14)
+    # equals the full softmax restricted to the selection and renormalised
+    full = scipy.special.softmax(l, axis=1)
+    sel = np.take_along_axis(full, ids, axis=1)
+    np.testing.assert_allclose(a, sel / sel.sum(axis=1, keepdims=True), rtol=1e-13)
+
+
+def test_affinity_hand_value():
+    # logits (ln 3, 0): exp(0)/(exp(0)+exp(-ln 3)) = 1/(1+1/3) = 3/4
+    l = np.array([[0.0, math.log(3.0)]])
+    ids = O.topk_select(l, 2)
+    assert list(ids[0]) == [1, 0]
+    np.testing.assert_allclose(O.affinities(l, ids)[0], [0.75, 0.25], rtol=1e-15)
+
+
+# ---------------------------------------------------------------- alignment
+
+def brute_align(ids, E, b):
+    """Independent construction: sort (expert, route) pairs, then pad per expert."""
+    flat = list(np.asarray(ids).reshape(-1))
+    R = len(flat)
+    pairs = sorted((int(e), r) for r, e in enumerate(flat) if 0 <= e < E)
+    rows, blocks = [], []
+    for e, grp in itertools.groupby(pairs, key=lambda p: p[0]):
+        rs = [r for _, r in grp]
+        while len(rs) % b:
+            rs.append(R)
+        rows += rs
+        blocks += [e] * (len(rs) // b)
+    return rows, blocks
+
+
+def random_routings(rng, n):
+    """Uniform, skewed, all-one-expert, exact multiples of 8 and invalid ids."""
+    for i in range(n):
+        kind = i % 6
+        E = int(rng.choice([4, 8, 16, 128]))
+        k = int(rng.integers(1, min(E, 8) + 1))
+        M = int(rng.integers(1, 30))
+        if kind == 0:      # uniform distinct experts per token
+            ids = np.stack([rng.permutation(E)[:k] for _ in range(M)])
+        elif kind == 1:    # skewed: a few hot experts
+            p = np.ones(E)
+            p[: max(1, E // 8)] = 20.0
+            ids = np.stack([rng.choice(E, k, replace=False, p=p / p.sum()) for _ in range(M)])
+        elif kind == 2:    # every route on one expert (k = 1)
+            ids = np.full((M, 1), int(rng.integers(E)))
+        elif kind == 3:    # route counts that are exact multiples of 8
+            ids = np.full((8 * int(rng.integers(1, 4)), 1), int(rng.integers(E)))
+        elif kind == 4:    # duplicate ids inside a row (not produced by top-k, still alignable)
+            ids = rng.integers(0, E, size=(M, k))
+        else:              # invalid ids mixed in
+            ids = rng.integers(-2, E + 2, size=(M, k))
+        yield ids, E
+
+
+def test_alignment_matches_brute_force_on_randomised_routings():
+    rng = np.random.default_rng(5)
+    for ids, E in random_routings(rng, 150):
+        for b in (8, 4):
+            al = O.align_blocks(ids, E, b)
+            rows, blocks = brute_align(ids, E, b)
+            assert list(al["sorted_routes"]) == rows
+            assert list(al["block_expert"]) == blocks
+            assert al["num_padded"] == len(rows) == b * al["num_blocks"]
+
+
+def test_alignment_invariants():
+    rng = np.random.default_rng(6)
+    for ids, E in random_routings(rng, 120):
+        b = 8
+        al = O.align_blocks(ids, E, b)
+        flat = ids.reshape(-1)
+        R = flat.size
+        rows = al["sorted_routes"]
+        valid = [r for r in range(R) if 0 <= flat[r] < E]
+        assert sorted(r for r in rows if r != R) == valid            # each valid route once
+        assert al["num_padded"] <= O.align_capacity(ids.shape[0], ids.shape[1], E, b)
+        counts = np.bincount(flat[(flat >= 0) & (flat < E)], minlength=E)
+        assert al["num_blocks"] == sum(-(-c // b) for c in counts)
+        be = al["block_expert"]
+        assert np.all(np.diff(be) >= 0)                              # blocks in expert order
+        for blk in range(al["num_blocks"]):
+            seg = rows[blk * b:(blk + 1) * b]
+            real = [r for r in seg if r != R]
+            assert real, "every block holds a valid route"
+            assert all(flat[r] == be[blk] for r in real)
+            assert real == sorted(real)                               # ascending route id
+            pads = [i for i, r in enumerate(seg) if r == R]
+            assert pads == list(range(len(real), b))                  # pads only at the tail
+
+
+def test_alignment_reproduces_the_pages_fixture_totals():
+    g = json.load(open(os.path.join(GOLDEN, "route_block_fixture.json")))
+    M, k, E, b = g["M"], g["k"], g["E"], g["b"]
+    # Build a routing whose per-expert counts give the printed totals:
+    # 30 experts with 1 route (30 blocks) and 20 experts whose counts fill
+    # 20 blocks with the remaining 138 routes.
+    counts = [1] * 30 + [7] * 18 + [6, 6]
+    assert sum(counts) == g["routes"] and len(counts) == 50
+    experts = list(range(0, 100, 2))[: len(counts)]
+    need = {e: c for e, c in zip(experts, counts)}
+    rows = [[] for _ in range(M)]
+    for e in sorted(need, key=lambda e: -need[e]):
+        order = sorted(range(M), key=lambda t: (len(rows[t]), t))
+        for t in order[: need[e]]:
+            rows[t].append(e)
+    assert all(len(r) == k for r in rows)
+    ids = np.array(rows)
+    al = O.align_blocks(ids, E, b)
+    assert ids.size == g["routes"]
+    assert al["num_padded"] == g["rows"]
+    assert al["num_blocks"] == g["blocks"]
+
+
+def test_block_membership_definition():
+    # expert 3 has 10 routes -> blocks (3,0) and (3,1); expert 5 has 2.
+    ids = np.array([[3, 5]] * 2 + [[3, 0]] * 8)      # R = 20
+    al = O.align_blocks(ids, 8, 8)
+    mem = O.block_membership(al["sorted_routes"], al["block_expert"], ids.size)
+    assert mem[0] == (0, 0, tuple(range(5, 20, 2)))
+    assert mem[1] == (3, 0, (0, 2, 4, 6, 8, 10, 12, 14))
+    assert mem[2] == (3, 1, (16, 18))
+    assert mem[3] == (5, 0, (1, 3))
+    # a within-block permutation keeps membership; a cross-boundary exchange changes it
+    rows = al["sorted_routes"].copy()
+    i, j = 8, 9
+    rows[[i, j]] = rows[[j, i]]
+    assert O.block_membership(rows, al["block_expert"], ids.size) == mem
+    rows = al["sorted_routes"].copy()
+    i, j = 15, 16
+    rows[[i, j]] = rows[[j, i]]
+    assert O.block_membership(rows, al["block_expert"], ids.size) != mem
+
+
+# ---------------------------------------------------------------- dense expert
+
+def test_single_expert_is_the_textbook_gated_mlp():
+    rng = np.random.default_rng(7)
+    H, I, E = 24, 10, 3
+    G, V, D = (rand_bf16(rng, (E, I, H), 0.2) for _ in range(3))
+    h = rng.standard_normal((2, H)).astype(np.float32)
+    ids = np.array([[2], [0]])
+    y = O.dense_forward(h, ids, np.ones((2, 1)), G, V, D)
+    for t, e in ((0, 2), (1, 0)):
+        x = torch.tensor(h[t], dtype=torch.float64)
+        g = torch.tensor(O.bf16_to_f64(G[e])) @ x
+        u = torch.tensor(O.bf16_to_f64(V[e])) @ x
+        p = torch.nn.functional.silu(g) * u
+        want = torch.tensor(O.bf16_to_f64(D[e])).T @ p
+        np.testing.assert_allclose(y[t], want.numpy(), rtol=1e-12, atol=1e-14)
+
+
+def test_tiny_block_hand_derivation():
+    """H=2, I=1, E=2, top-2, h=(1,0), worked by hand.
+    Router row 0 = (1, 0): logits (1, 0), a = (e/(e+1), 1/(e+1)).
+    Expert 0: g = 1, u = 2 -> p0 = 2*silu(1) = 2e/(e+1); down column (1, -1).
+    Expert 1: g = -1, u = 1 -> p1 = silu(-1) = -1/(e+1); down column (0, 3).
+    y = a0*p0*(1,-1) + a1*p1*(0,3)."""
+    e_ = math.e
+    h = np.array([[1.0, 0.0]], np.float32)
+    Wr = bf16_bits([[1.0, 0.0], [0.0, 0.0]])
+    G = bf16_bits([[[1.0, 0.0]], [[-1.0, 0.0]]])
+    V = bf16_bits([[[2.0, 0.0]], [[1.0, 0.0]]])
+    D = bf16_bits([[[1.0, -1.0]], [[0.0, 3.0]]])
+    out = O.moe_step({"h": h, "router_w": Wr, "w_gate": G, "w_up": V, "w_down": D}, k=2)
+    assert list(out["ids"][0]) == [0, 1]
+    np.testing.assert_allclose(out["aff"][0], [e_ / (e_ + 1), 1 / (e_ + 1)], rtol=1e-15)
+    y0 = 2 * e_ ** 2 / (e_ + 1) ** 2
+    y1 = -2 * e_ ** 2 / (e_ + 1) ** 2 - 3 / (e_ + 1) ** 2
+    np.testing.assert_allclose(out["y"][0], [y0, y1], rtol=1e-14)
+
+
+def test_dense_matches_per_channel_brute_force():
+    """The channel view: y = sum_s a_s sum_j phi(g_j.x)(v_j.x) d_j, by explicit loops."""
+    rng = np.random.default_rng(8)
+    H, I, E, k, M = 6, 5, 4, 2, 2
+    G, V, D = (rand_bf16(rng, (E, I, H), 0.4) for _ in range(3))
+    h = rng.standard_normal((M, H)).astype(np.float32)
+    ids = np.array([[1, 3], [2, 1]])
+    a = np.array([[0.7, 0.3], [0.55, 0.45]])
+    y = O.dense_forward(h, ids, a, G, V, D)
+    Gf, Vf, Df = O.bf16_to_f64(G), O.bf16_to_f64(V), O.bf16_to_f64(D)
+    for t in range(M):
+        want = [0.0] * H
+        for s in range(k):
+            e = ids[t, s]
+            for j in range(I):
+                gj = sum(float(Gf[e, j, i]) * float(h[t, i]) for i in range(H))
+                vj = sum(float(Vf[e, j, i]) * float(h[t, i]) for i in range(H))
+                aj = gj / (1 + math.exp(-gj)) * vj
+                for i in range(H):
+                    want[i] += a[t, s] * aj * float(Df[e, j, i])
+        np.testing.assert_allclose(y[t], want, rtol=1e-12, atol=1e-15)
+
+
+def test_zero_input_gives_zero_output():
+    rng = np.random.default_rng(9)
+    G, V, D = (rand_bf16(rng, (4, 5, 8)) for _ in range(3))
+    y = O.dense_forward(np.zeros((1, 8), np.float32), np.array([[0, 2]]), np.array([[0.6, 0.4]]), G, V, D)
+    assert np.all(y == 0)
+
+
+def test_identical_experts_make_routing_irrelevant():
+    """With every expert equal, y equals that expert's output for any routing
+    (pins the renormalisation: the affinities sum to one)."""
+    rng = np.random.default_rng(10)
+    H, I, E, k = 16, 6, 8, 3
+    one = [rand_bf16(rng, (1, I, H), 0.3) for _ in range(3)]
+    G, V, D = (np.repeat(w, E, axis=0) for w in one)
+    Wr = rand_bf16(rng, (H, E), 0.5)
+    h = rng.standard_normal((3, H)).astype(np.float32)
+    out = O.moe_step({"h": h, "router_w": Wr, "w_gate": G, "w_up": V, "w_down": D}, k=k)
+    single = O.dense_forward(h, np.zeros((3, 1), np.int64), np.ones((3, 1)), G, V, D)
+    np.testing.assert_allclose(out["y"], single, rtol=1e-13, atol=1e-16)
+
+
+def test_output_is_linear_in_the_down_weights():
+    rng = np.random.default_rng(11)
+    H, I, E = 10, 6, 3
+    G, V = (rand_bf16(rng, (E, I, H)) for _ in range(2))
+    Da = rand_bf16(rng, (E, I, H))
+    Db = rand_bf16(rng, (E, I, H))
+    mask = rng.random((E, I, H)) < 0.5       # disjoint supports: Da + Db is exact in bf16
+    Da[mask] = 0
+    Db[~mask] = 0
+    D = Da | Db
+    h = rng.standard_normal((2, H)).astype(np.float32)
+    ids, a = np.array([[0, 2], [1, 0]]), np.array([[0.6, 0.4], [0.9, 0.1]])
+    y = O.dense_forward(h, ids, a, G, V, D)
+    ya = O.dense_forward(h, ids, a, G, V, Da)
+    yb = O.dense_forward(h, ids, a, G, V, Db)
+    np.testing.assert_allclose(y, ya + yb, rtol=1e-12, atol=1e-15)
+
+
+# ---------------------------------------------------------------- channel-sparse
+
+def test_candidate_count_and_keep_count_from_the_pages():
+    g = json.load(open(os.path.join(GOLDEN, "channel_candidates.json")))
+    assert g["experts_per_token"] * g["channels_per_expert"] == g["candidates"]
+    assert (g["keep_fraction_percent"] * g["candidates"] + 50) // 100 == g["keep_count_rounded"]
+
+
+def test_channel_norms_brute_force():
+    rng = np.random.default_rng(12)
+    E, I, H = 2, 3, 5
+    G, V, D = (rand_bf16(rng, (E, I, H)) for _ in range(3))
+    n = O.channel_norms(G, V, D)
+    for e in range(E):
+        for j in range(I):
+            ng = math.sqrt(sum(float(x) ** 2 for x in O.bf16_to_f64(G[e, j])))
+            nv = math.sqrt(sum(float(x) ** 2 for x in O.bf16_to_f64(V[e, j])))
+            nd = math.sqrt(sum(float(x) ** 2 for x in O.bf16_to_f64(D[e, j])))
+            assert n[e, j] == np.float32(ng * nv * nd)
+
+
+def test_channel_select_brute_force_lexsort():
+    rng = np.random.default_rng(13)
+    for trial in range(40):
+        E, I, k = 12, int(rng.integers(3, 20)), int(rng.integers(1, 5))
+        ids = np.stack([rng.permutation(E)[:k] for _ in range(2)])
+        a = rng.random((2, k)).astype(np.float32)
+        n = rng.integers(1, 6, size=(E, I)).astype(np.float32)   # many ties
+        K = int(rng.integers(0, k * I + 1))
+        kept = O.channel_select(a, ids, n, K)
+        for t in range(2):
+            s_idx = np.repeat(np.arange(k), I)
+            j_idx = np.tile(np.arange(I), k)
+            e_idx = ids[t][s_idx]
+            score = a[t][s_idx].astype(np.float64) * n[e_idx, j_idx].astype(np.float64)
+            order = np.lexsort((j_idx, e_idx, -score))
+            want = np.sort(s_idx[order[:K]] * I + j_idx[order[:K]])
+            assert list(kept[t]) == list(want)
+
+
+def test_channel_select_tie_order_hand_example():
+    # slot 0 -> expert 5 with a=0.5, slot 1 -> expert 2 with a=0.25
+    ids = np.array([[5, 2]])
+    a = np.array([[0.5, 0.25]], np.float32)
+    n = np.zeros((6, 3), np.float32)
+    n[5] = [1.0, 4.0, 2.0]          # scores 0.5, 2.0, 1.0
+    n[2] = [4.0, 8.0, 1.0]          # scores 1.0, 2.0, 0.25
+    # ranking: (2.0,e2,j1) (2.0,e5,j1) (1.0,e2,j0) (1.0,e5,j2) (0.5,e5,j0) (0.25,e2,j2)
+    assert list(O.channel_select(a, ids, n, 3)[0]) == [1, 3 + 0, 3 + 1]
+    assert list(O.channel_select(a, ids, n, 4)[0]) == [1, 2, 3, 4]
+
+
+def test_all_channels_kept_equals_dense_and_none_kept_is_zero():
+    rng = np.random.default_rng(14)
+    H, I, E, k = 20, 9, 6, 3
+    G, V, D = (rand_bf16(rng, (E, I, H), 0.3) for _ in range(3))
+    h = rng.standard_normal((2, H)).astype(np.float32)
+    ids = np.array([[4, 1, 0], [2, 5, 4]])
+    a = np.array([[0.5, 0.3, 0.2], [0.4, 0.35, 0.25]])
+    n = O.channel_norms(G, V, D)
+    dense = O.dense_forward(h, ids, a, G, V, D)
+    kept_all = O.channel_select(a.astype(np.float32), ids, n, k * I)
+    np.testing.assert_array_equal(kept_all, np.tile(np.arange(k * I), (2, 1)))
+    np.testing.assert_allclose(O.channel_sparse_forward(h, ids, a, G, V, D, kept_all), dense,
+                               rtol=1e-13, atol=1e-16)
+    kept_none = O.channel_select(a.astype(np.float32), ids, n, 0)
+    assert np.all(O.channel_sparse_forward(h, ids, a, G, V, D, kept_none) == 0)
+
+
+def test_sparse_forward_is_the_kept_subset_of_the_channel_sum():
+    rng = np.random.default_rng(15)
+    H, I, E = 8, 6, 4
+    G, V, D = (rand_bf16(rng, (E, I, H), 0.4) for _ in range(3))
+    h = rng.standard_normal((1, H)).astype(np.float32)
+    ids, a = np.array([[3, 1]]), np.array([[0.8, 0.2]])
+    kept = np.array([[0, 4, 6 + 2, 6 + 5]])
+    y = O.channel_sparse_forward(h, ids, a, G, V, D, kept)
+    Gf, Vf, Df = O.bf16_to_f64(G), O.bf16_to_f64(V), O.bf16_to_f64(D)
+    want = np.zeros(H)
+    for s, j in ((0, 0), (0, 4), (1, 2), (1, 5)):
+        e = ids[0, s]
+        g = Gf[e, j] @ h[0].astype(np.float64)
+        u = Vf[e, j] @ h[0].astype(np.float64)
+        want += a[0, s] * (g / (1 + math.exp(-g)) * u) * Df[e, j]
+    np.testing.assert_allclose(y[0], want, rtol=1e-12)
+
+
+# ---------------------------------------------------------------- VQ + low rank
+
+def test_vq_reconstruction_hand_example():
+    """H=4, d=2, K=2, one channel: blocks run along H inside channel j's column.
+    B = [[1,2],[3,4]], J = [[1,0]] -> VQ row (3,4,1,2); D = 0 -> no low-rank term."""
+    B = bf16_bits([[1.0, 2.0], [3.0, 4.0]])
+    J = np.array([[1, 0]], np.uint8)
+    D = bf16_bits(np.zeros((4, 1)))
+    C = bf16_bits(np.zeros((1, 1)))
+    W = O.vq_reconstruct(D, C, B, J)
+    assert W.tolist() == [[3.0, 4.0, 1.0, 2.0]]
+    h = np.array([1.0, 0.0, 0.0, 0.5], np.float32)
+    assert O.vqlr_project(h, D, C, B, J).tolist() == [4.0]
+    assert O.vqlr_project_shared(h, D, C, B, J).tolist() == [4.0]
+    # low-rank term alone: D = e_0 (x) (1), C = (2): adds 2*h[0] to channel 0
+    D1 = bf16_bits([[1.0], [0.0], [0.0], [0.0]])
+    C1 = bf16_bits([[2.0]])
+    assert O.vqlr_project(h, D1, C1, B, J).tolist() == [6.0]
+
+
+def test_shared_projection_form_equals_reconstruction_form():
+    rng = np.random.default_rng(16)
+    for (H, I, r, K, d) in [(32, 7, 3, 16, 4), (64, 12, 8, 256, 8), (2048, 16, 64, 256, 8)]:
+        D = rand_bf16(rng, (H, r), 0.05)
+        C = rand_bf16(rng, (I, r), 0.05)
+        B = rand_bf16(rng, (K, d), 0.05)
+        J = rng.integers(0, K, size=(I, H // d)).astype(np.uint8)
+        h = rng.standard_normal(H).astype(np.float32)
+        a = O.vqlr_project(h, D, C, B, J)
+        b = O.vqlr_project_shared(h, D, C, B, J)
+        np.testing.assert_allclose(a, b, rtol=1e-12, atol=1e-13 * np.abs(a).max())
+
+
+def test_projection_codebook_size_matches_the_pages():
+    g = json.load(open(os.path.join(GOLDEN, "projection_codebook_sizes.json")))
+    rng = np.random.default_rng(17)
+    h = rng.standard_normal(g["H"]).astype(np.float32)
+    D = rand_bf16(rng, (g["H"], 1))
+    for case in g["cases"]:
+        B = rand_bf16(rng, (g["K"], case["d"]))
+        _, T = O.shared_projections(h, D, B)
+        assert T.shape == (g["H"] // case["d"], g["K"])
+        mib = T.size * g["bytes_per_value"] * g["projections"] / 2 ** 20
+        assert mib == case["MiB"]
+
+
+def test_projection_codebook_closed_form_on_one_hot_input():
+    rng = np.random.default_rng(18)
+    H, K, d = 16, 8, 4
+    B = rand_bf16(rng, (K, d))
+    Bf = O.bf16_to_f64(B)
+    for i in range(H):
+        h = np.zeros(H, np.float32)
+        h[i] = 1.0
+        _, T = O.shared_projections(h, rand_bf16(rng, (H, 2)), B)
+        want = np.zeros((H // d, K))
+        want[i // d] = Bf[:, i % d]
+        np.testing.assert_array_equal(T, want)
+
+
+def test_vq_with_zero_low_rank_equals_dense_on_the_materialised_weights():
+    rng = np.random.default_rng(19)
+    H, I, E, k, r, K, d = 32, 6, 4, 2, 4, 16, 8
+    vq = {}
+    for P in ("gate", "up"):
+        vq["lr_basis_" + P] = rand_bf16(rng, (H, r))
+        vq["lr_coef_" + P] = np.zeros((E, I, r), np.uint16)
+        vq["vq_book_" + P] = rand_bf16(rng, (K, d))
+        vq["vq_idx_" + P] = rng.integers(0, K, size=(E, I, H // d)).astype(np.uint8)
+    Wd = rand_bf16(rng, (E, I, H))
+    # materialise Q_B(J) as plain bf16 dense weights by table lookup
+    Gd = vq["vq_book_gate"][vq["vq_idx_gate"].astype(np.int64)].reshape(E, I, H)
+    Vd = vq["vq_book_up"][vq["vq_idx_up"].astype(np.int64)].reshape(E, I, H)
+    h = rng.standard_normal((2, H)).astype(np.float32)
+    ids, a = np.array([[3, 0], [1, 3]]), np.array([[0.7, 0.3], [0.5, 0.5]])
+    np.testing.assert_allclose(O.vqlr_forward(h, ids, a, vq, Wd), O.dense_forward(h, ids, a, Gd, Vd, Wd),
+                               rtol=1e-13, atol=1e-16)
+
+
+def test_vq_on_a_zero_code_word_leaves_the_low_rank_gemv():
+    rng = np.random.default_rng(20)
+    H, I, r, K, d = 64, 9, 5, 4, 8
+    D = rand_bf16(rng, (H, r), 0.2)
+    C = rand_bf16(rng, (I, r), 0.2)
+    B = rand_bf16(rng, (K, d))
+    B[2] = 0
+    J = np.full((I, H // d), 2, np.uint8)
+    h = rng.standard_normal(H).astype(np.float32)
+    want = torch.tensor(O.bf16_to_f64(C)) @ (torch.tensor(O.bf16_to_f64(D)).T @ torch.tensor(h, dtype=torch.float64))
+    np.testing.assert_allclose(O.vqlr_project(h, D, C, B, J), want.numpy(), rtol=1e-13)
+    np.testing.assert_allclose(O.vqlr_project_shared(h, D, C, B, J), want.numpy(), rtol=1e-13)
