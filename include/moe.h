@@ -1,0 +1,282 @@
+/*
+ * moe.h -- C ABI of libmoe, a gfx950 (MI355X) library for the decode step of
+ * a routed Mixture-of-Experts block at batch 1 to small batch.
+ *
+ * What one step computes (page "A Multi-Engine Dataflow for MoE Decoding on
+ * Scratchpad-Based Tensor Accelerators", MoE-block background and Fig. 2):
+ *
+ *     y = sum_e a_e * W_down,e ( phi(W_gate,e h) * (W_up,e h) ),  phi = SiLU,
+ *
+ * over the k experts the router selects for h, in three calls:
+ *     moe_route_topk     router GEMV, top-k, renormalised softmax affinities
+ *     moe_align_blocks   canonical alignment of routes into padded b-row blocks
+ *     moe_expert_forward gate/up GEMV + SiLU, down GEMV, weighted combine
+ * plus moe_create / moe_destroy and a few helpers.
+ *
+ * Conventions (all entry points):
+ *  - Device pointers are device (HBM) addresses on the current HIP device;
+ *    `cfg`, `w` (the structs themselves), `out` and the *_host arguments are
+ *    host pointers.  Every device buffer is owned by the caller.  Weights are
+ *    borrowed zero-copy by moe_create and must outlive the context.  The
+ *    context owns only its workspace (allocated in moe_create, freed in
+ *    moe_destroy).
+ *  - Every call enqueues asynchronously on `stream` (a hipStream_t; NULL is
+ *    the default stream) and never synchronises, except where stated.
+ *    Counts produced on the device stay on the device.
+ *  - Errors are returned as moe_status.  All host-side checks run before any
+ *    launch: on an error nothing is enqueued.  Unsupported shapes or formats
+ *    fail closed at moe_create with MOE_ERR_UNSUPPORTED; there is no fallback
+ *    path.  Anomalies only visible on the device (an expert id outside
+ *    [0, E), an alignment plan inconsistent with the routes) are skipped,
+ *    never read or written out of bounds, and set a sticky flag readable with
+ *    moe_read_device_error.
+ *  - A context serves one stream at a time and is not thread-safe; calls
+ *    that overlap on one context race on its workspace.
+ *  - Layouts are row-major.  bf16 values are passed as their 16-bit patterns.
+ *  - Results are bitwise reproducible run to run: no floating-point atomics
+ *    are used and every reduction order is a function of the shape alone.
+ */
+#ifndef MOE_H
+#define MOE_H
+
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef struct moe_ctx moe_ctx;
+
+typedef enum {
+    MOE_OK = 0,
+    MOE_ERR_INVALID_ARG = 1,   /* null pointer, negative or oversized count, bad struct field */
+    MOE_ERR_UNSUPPORTED = 2,   /* shape/format outside what the kernels implement (fail closed) */
+    MOE_ERR_CAPACITY = 3,      /* M above the context's max_tokens, K above max_keep */
+    MOE_ERR_HIP = 4,           /* a HIP runtime call failed */
+    MOE_ERR_DEVICE = 5         /* moe_read_device_error found a sticky device flag */
+} moe_status;
+
+/* Weight formats of the gate and up projections (down is always dense bf16). */
+enum {
+    MOE_WFORMAT_DENSE = 0,     /* bf16 [E][I][H] */
+    MOE_WFORMAT_VQLR = 1       /* VQ + low rank (see moe_weights) */
+};
+
+/* Device error flag bits (moe_read_device_error). */
+enum {
+    MOE_DEVERR_BAD_ROUTE_ID = 1,      /* a top-k id outside [0, E) (route skipped) */
+    MOE_DEVERR_BAD_PLAN = 2,          /* a plan row whose id disagrees with its block (row skipped) */
+    MOE_DEVERR_BAD_BLOCK_EXPERT = 4,  /* a block_expert entry outside [0, E) (block skipped) */
+    MOE_DEVERR_BAD_COUNTS = 8         /* counts[] beyond the plan capacity (clamped) */
+};
+
+/*
+ * Shapes and options of one MoE layer.
+ *  H, I, E     hidden size, channels per expert, number of experts.
+ *              Supported: H % 8 == 0, 8 <= H <= 16384; 1 <= I <= 16384;
+ *              E % 8 == 0, 8 <= E <= 1024.
+ *  top_k       experts per token, 1 <= top_k <= min(E, 32).
+ *  block_b     alignment block size (8 on the pages); 1 <= block_b <= 64.
+ *  max_tokens  largest M any call will pass (sizes the workspace), 1..4096,
+ *              with ceil(max_tokens*top_k/64)*E <= 16384.
+ *  wformat     MOE_WFORMAT_DENSE or MOE_WFORMAT_VQLR.
+ *  vq_d, vq_K, lr_r   VQ block length, code book size and low-rank rank for
+ *              MOE_WFORMAT_VQLR: vq_d == 8, 1 <= vq_K <= 256, H % (8*vq_d)
+ *              == 0, lr_r % 8 == 0 and 8 <= lr_r <= 512.  Ignored for dense.
+ *  max_keep    largest channel top-K moe_expert_forward will be asked for
+ *              (0 = channel-sparse mode unused); <= top_k*I, top_k*I <= 16384.
+ */
+typedef struct {
+    int32_t H, I, E, top_k, block_b, max_tokens;
+    int32_t wformat;
+    int32_t vq_d, vq_K, lr_r;
+    int32_t max_keep;
+} moe_config;
+
+/*
+ * Device pointers to one layer's weights (borrowed; must outlive the ctx).
+ *  router_w     bf16 [H][E]                     required
+ *  router_bias  fp32 [E] added to the logits    or NULL
+ *  w_gate, w_up bf16 [E][I][H]; row j of expert e is channel j's gate/up row
+ *               (required for MOE_WFORMAT_DENSE, ignored for VQLR)
+ *  w_down       bf16 [E][I][H]; row j is channel j's down column, stored
+ *               contiguously ("transposed at load", page "Channel Selection
+ *               for Mixture-of-Experts Decoding Needs No Calibration Data",
+ *               Stage 2)                        required
+ *  chan_norm    fp32 [E][I], static channel scores n[e][j] for the
+ *               channel-sparse mode (see moe_channel_norms); or NULL
+ *  For MOE_WFORMAT_VQLR, index [0] is the gate projection and [1] the up
+ *  projection (page "A Multi-Engine Dataflow ...", Sec. 3.1 Eq. 1 and Sec. 2.3):
+ *  lr_basis[P]  bf16 [H][lr_r]   shared basis D_P
+ *  lr_coef[P]   bf16 [E][I][lr_r] private coefficients, row j = C_P,e^T column j
+ *  vq_book[P]   bf16 [vq_K][vq_d] shared weight code book B_P
+ *  vq_idx[P]    uint8 [E][I][H/vq_d] private index map: entry [e][j][b] picks
+ *               the code word of rows vq_d*b .. vq_d*b+vq_d-1 of channel j
+ *  The reconstructed gate/up weight of channel j, row i is
+ *      sum_rho D_P[i][rho] C_P,e[j][rho] + B_P[J_P,e[j][i / vq_d]][i % vq_d].
+ */
+typedef struct {
+    const uint16_t *router_w;
+    const float *router_bias;
+    const uint16_t *w_gate;
+    const uint16_t *w_up;
+    const uint16_t *w_down;
+    const float *chan_norm;
+    const uint16_t *lr_basis[2];
+    const uint16_t *lr_coef[2];
+    const uint16_t *vq_book[2];
+    const uint8_t *vq_idx[2];
+} moe_weights;
+
+/*
+ * Create a context for one layer: validates `cfg` and the required weight
+ * pointers (fail closed), allocates the workspace on the current device.
+ * On success *out holds the context; on error *out is NULL.
+ */
+moe_status moe_create(const moe_config *cfg, const moe_weights *w, moe_ctx **out);
+
+/* Free the workspace.  moe_destroy(NULL) is a no-op.  Waits for the device. */
+void moe_destroy(moe_ctx *ctx);
+
+/*
+ * Router (page "A Multi-Engine Dataflow ...", MoE-block background; page
+ * "Route-Block Membership Selects Packed-AWQ Arithmetic", Sec. 2.1: the
+ * router's M x k expert-id array).
+ *  h          fp32 [M][H]
+ *  M          0..max_tokens (0: nothing is enqueued)
+ *  topk_ids   int32 [M][k] out: per token the k largest logits, ties to the
+ *             lower expert id, slot s = s-th largest
+ *  topk_w     fp32 [M][k] out: softmax over the k selected logits
+ *  logits_out fp32 [M][E] out (may be NULL): l = h Wr + bias, fp32 accumulation
+ */
+moe_status moe_route_topk(moe_ctx *ctx, const float *h, int32_t M,
+                          int32_t *topk_ids, float *topk_w, float *logits_out, void *stream);
+
+/*
+ * Canonical alignment (page "Route-Block Membership ...", Sec. 2.1, Sec. 3.1
+ * Eq. 1, Sec. 5.3): flatten ids row-major into routes r = t*k + s; group the
+ * routes with 0 <= id < E by expert in (expert id, route id) order; pad each
+ * group with the sentinel M*k to a multiple of block_b; experts in ascending
+ * id; experts without routes own no block.  The result is a function of the
+ * ids alone (no atomic-order dependence).
+ *  topk_ids       int32 [M][k] (device)
+ *  sorted_routes  int32 [moe_align_capacity(M,k,E,b)] out; entries past
+ *                 num_padded are left untouched
+ *  block_expert   int32 [capacity / b] out; entries past num_blocks untouched
+ *  counts         int32 [2] out: num_blocks, num_padded (stay on the device)
+ * Ids outside [0, E) are skipped and set MOE_DEVERR_BAD_ROUTE_ID.
+ */
+moe_status moe_align_blocks(moe_ctx *ctx, const int32_t *topk_ids, int32_t M,
+                            int32_t *sorted_routes, int32_t *block_expert, int32_t *counts,
+                            void *stream);
+
+/*
+ * Experts and combine.
+ * Dense / VQ mode (keep_channels == 0): for every valid route (t, s) with
+ * expert e = topk_ids[t][s]:
+ *     p = SiLU(W_gate,e h_t) * (W_up,e h_t)            (fp32, I values)
+ *     y_(t,s) = W_down,e^T p                            (fp32, H values)
+ * and y[t] = sum_{s = 0..k-1} topk_w[t][s] * y_(t,s), added in slot order
+ * (page "A Multi-Engine Dataflow ...", Sec. 4.3, accumulated summation).
+ * Work is organised by the plan (sorted_routes, block_expert, counts from
+ * moe_align_blocks or any valid plan for the same ids): every expert's
+ * weights are streamed once for all of its routes.  The arithmetic of a route
+ * does not depend on its position in the plan, so any valid plan gives
+ * bitwise the same y.  A plan that omits a valid route leaves that route's
+ * contribution undefined.
+ *
+ * Channel-sparse mode (keep_channels = K > 0; needs chan_norm, dense format):
+ * page "Channel Selection for Mixture-of-Experts Decoding Needs No
+ * Calibration Data", Background and Stage 2.  Per token, candidate (s, j)
+ * scores a_s * n[e_s][j] (exact fp64 product of two fp32 values); the K best
+ * across all k experts are kept (ties: lower expert id, then lower channel);
+ * only the kept gate rows, up rows and down rows are read, and
+ *     y[t] = sum over kept (s, j) of a_s * SiLU(g_j.h_t)(v_j.h_t) * d_j.
+ * The plan arguments are ignored (may be NULL).  kept_out (int32 [M][K], may
+ * be NULL) receives the kept set as s*I + j in ascending order.
+ *
+ *  h        fp32 [M][H];  topk_ids int32 [M][k];  topk_w fp32 [M][k]
+ *  y        fp32 [M][H] out (fully overwritten)
+ */
+moe_status moe_expert_forward(moe_ctx *ctx, const float *h, int32_t M,
+                              const int32_t *topk_ids, const float *topk_w,
+                              const int32_t *sorted_routes, const int32_t *block_expert,
+                              const int32_t *counts, int32_t keep_channels,
+                              int32_t *kept_out, float *y, void *stream);
+
+/* ---------------------------------------------------------------- helpers */
+
+/* Rows moe_align_blocks may write: M*k + min(E, M*k)*(b-1); -1 on bad args. */
+int32_t moe_align_capacity(int32_t M, int32_t k, int32_t E, int32_t b);
+
+/* Static text for a status code. */
+const char *moe_status_string(moe_status s);
+
+/*
+ * Synchronises the device, copies the sticky device error flags of the
+ * context to *flags (host), and clears them when `clear` is non-zero.
+ * Returns MOE_ERR_DEVICE when any flag is set, MOE_OK otherwise.
+ */
+moe_status moe_read_device_error(moe_ctx *ctx, int32_t *flags, int32_t clear);
+
+/*
+ * Load-time channel scores for the channel-sparse mode:
+ *     norms[e][j] = fp32( ||G_e[j]|| * ||V_e[j]|| * ||D_e[j]|| )
+ * with the three Euclidean norms computed in fp64 and rounded once.
+ * Inputs bf16 [E][I][H] (device), output fp32 [E][I] (device).  Needs only
+ * cfg->H, I, E.  Asynchronous on `stream`.
+ */
+moe_status moe_channel_norms(const moe_config *cfg, const uint16_t *w_gate, const uint16_t *w_up,
+                             const uint16_t *w_down, float *norms, void *stream);
+
+/*
+ * Host-side check of an alignment plan against its routes (all host
+ * pointers; no GPU needed).  Checks: counts in range; every valid route
+ * exactly once; rows of a block belong to its expert; pads only at a block's
+ * tail and never a whole block; blocks of one expert contiguous and experts
+ * ascending; no id outside [0, E) present.  Canonical order inside an expert
+ * is NOT required (any valid plan passes).  On failure returns
+ * MOE_ERR_INVALID_ARG and writes a code to *reason (host, may be NULL):
+ *   1 counts out of range, 2 a route missing, 3 a route duplicated,
+ *   4 a row on the wrong expert's block, 5 a pad before a route inside a
+ *   block or an all-pad block, 6 blocks out of expert order, 7 an invalid
+ *   route id in the plan, 8 a row value out of range.
+ */
+moe_status moe_validate_plan(const int32_t *topk_ids_host, int32_t M, int32_t k, int32_t E, int32_t b,
+                             const int32_t *sorted_routes_host, const int32_t *block_expert_host,
+                             const int32_t *counts_host, int32_t *reason);
+
+/* ------------------------------------------------------------- profiling */
+
+/* Kernel identifiers for moe_profile_read. */
+enum {
+    MOE_KERNEL_ROUTER_GEMV = 0,  /* router logits (and VQ z = D^T h) partials */
+    MOE_KERNEL_ROUTER_TOPK = 1,
+    MOE_KERNEL_ALIGN = 2,
+    MOE_KERNEL_GATEUP = 3,       /* dense gate/up GEMV + SiLU */
+    MOE_KERNEL_GATEUP_VQLR = 4,  /* VQ + low-rank gate/up + SiLU */
+    MOE_KERNEL_DOWN = 5,         /* down GEMV partials */
+    MOE_KERNEL_COMBINE = 6,      /* fixed-order weighted combine */
+    MOE_KERNEL_CHAN_SELECT = 7,  /* channel top-K */
+    MOE_KERNEL_CHAN_GATHER = 8,  /* kept-channel gate/up + down partials */
+    MOE_KERNEL_CHAN_COMBINE = 9,
+    MOE_KERNEL_COUNT = 10
+};
+
+/*
+ * When enabled, every launch of the context is bracketed by HIP events
+ * recorded on the launch's stream.  moe_profile_read synchronises, adds the
+ * elapsed times of all recorded launches of each kernel into ms[kernel] and
+ * launches[kernel] (host arrays of MOE_KERNEL_COUNT), and clears the record.
+ */
+moe_status moe_profile_enable(moe_ctx *ctx, int32_t enable);
+moe_status moe_profile_read(moe_ctx *ctx, double *ms, int64_t *launches);
+
+/* Name of a kernel identifier ("gateup", ...), or NULL. */
+const char *moe_kernel_name(int32_t kernel);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* MOE_H */

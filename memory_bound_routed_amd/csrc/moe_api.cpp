@@ -1,0 +1,454 @@
+// libmoe C ABI: argument validation (fail closed), workspace, launch order.
+// The public contract of every function is documented in include/moe.h.
+#include "moe.h"
+
+#include <hip/hip_runtime.h>
+
+#include <cstdint>
+#include <cstring>
+#include <new>
+#include <vector>
+
+#include "launch.h"
+
+namespace {
+
+constexpr int kSliceRows = 64;     // rows per GEMV partial slice (router, z = D^T h)
+constexpr int kMinDownRows = 8;    // smallest down row chunk (sizes the partial buffer)
+constexpr int kChanChunk = 8;      // kept channels per gather workgroup
+
+struct Rec {
+    int kernel;
+    hipEvent_t a, b;
+};
+
+}  // namespace
+
+struct moe_ctx {
+    moe_config cfg;
+    moe_weights w;
+    int device = 0;
+    void* ws = nullptr;
+    size_t ws_bytes = 0;
+    int32_t* err = nullptr;
+    float* router_part = nullptr;
+    float* zpart[2] = {nullptr, nullptr};
+    float* p = nullptr;
+    float* down_part = nullptr;
+    int32_t* kept_ws = nullptr;
+    float* chan_part = nullptr;
+    int nslices = 0;
+    bool prof = false;
+    std::vector<Rec> recs;
+    std::vector<hipEvent_t> pool;
+};
+
+namespace {
+
+bool aligned(const void* p, size_t a) { return (reinterpret_cast<uintptr_t>(p) % a) == 0; }
+
+int64_t align_capacity64(int64_t M, int64_t k, int64_t E, int64_t b) {
+    const int64_t R = M * k;
+    return R + (E < R ? E : R) * (b - 1);
+}
+
+moe_status check_config(const moe_config* c) {
+    if (c->H <= 0 || c->I <= 0 || c->E <= 0 || c->top_k <= 0 || c->block_b <= 0 || c->max_tokens <= 0 ||
+        c->max_keep < 0)
+        return MOE_ERR_INVALID_ARG;
+    if (c->H % 8 || c->H < 8 || c->H > 8192) return MOE_ERR_UNSUPPORTED;
+    if (c->I > 16384) return MOE_ERR_UNSUPPORTED;
+    if (c->E % 8 || c->E < 8 || c->E > 1024) return MOE_ERR_UNSUPPORTED;
+    if (c->top_k > 32 || c->top_k > c->E) return MOE_ERR_UNSUPPORTED;
+    if (c->block_b > 64) return MOE_ERR_UNSUPPORTED;
+    if (c->max_tokens > 4096 || (int64_t)c->max_tokens * c->top_k > 4096) return MOE_ERR_UNSUPPORTED;
+    const int64_t nchunk = ((int64_t)c->max_tokens * c->top_k + 63) / 64;
+    if (nchunk * c->E > 6144) return MOE_ERR_UNSUPPORTED;
+    if (c->wformat != MOE_WFORMAT_DENSE && c->wformat != MOE_WFORMAT_VQLR) return MOE_ERR_UNSUPPORTED;
+    if (c->wformat == MOE_WFORMAT_VQLR) {
+        if (c->vq_d != 8 || c->vq_K < 1 || c->vq_K > 256 || c->H % (8 * c->vq_d)) return MOE_ERR_UNSUPPORTED;
+        if (c->lr_r % 8 || c->lr_r < 8 || c->lr_r > 512) return MOE_ERR_UNSUPPORTED;
+    }
+    if (c->max_keep > 0) {
+        if (c->wformat != MOE_WFORMAT_DENSE) return MOE_ERR_UNSUPPORTED;
+        if (c->max_keep > c->top_k * c->I || c->top_k * c->I > 8192) return MOE_ERR_UNSUPPORTED;
+    }
+    return MOE_OK;
+}
+
+moe_status check_weights(const moe_config* c, const moe_weights* w) {
+    if (!w->router_w || !w->w_down) return MOE_ERR_INVALID_ARG;
+    if (!aligned(w->router_w, 16) || !aligned(w->w_down, 16)) return MOE_ERR_INVALID_ARG;
+    if (w->router_bias && !aligned(w->router_bias, 4)) return MOE_ERR_INVALID_ARG;
+    if (c->wformat == MOE_WFORMAT_DENSE) {
+        if (!w->w_gate || !w->w_up) return MOE_ERR_INVALID_ARG;
+        if (!aligned(w->w_gate, 16) || !aligned(w->w_up, 16)) return MOE_ERR_INVALID_ARG;
+    } else {
+        for (int P = 0; P < 2; ++P) {
+            if (!w->lr_basis[P] || !w->lr_coef[P] || !w->vq_book[P] || !w->vq_idx[P]) return MOE_ERR_INVALID_ARG;
+            if (!aligned(w->lr_basis[P], 16) || !aligned(w->lr_coef[P], 2) || !aligned(w->vq_book[P], 16) ||
+                !aligned(w->vq_idx[P], 4))
+                return MOE_ERR_INVALID_ARG;
+        }
+    }
+    if (c->max_keep > 0 && (!w->chan_norm || !aligned(w->chan_norm, 4))) return MOE_ERR_INVALID_ARG;
+    return MOE_OK;
+}
+
+// Rows of the down GEMV handled per workgroup for a call with M tokens.
+int down_rows(int M) { return M == 1 ? 16 : kMinDownRows; }
+
+hipEvent_t take_event(moe_ctx* ctx) {
+    if (!ctx->pool.empty()) {
+        hipEvent_t e = ctx->pool.back();
+        ctx->pool.pop_back();
+        return e;
+    }
+    hipEvent_t e = nullptr;
+    if (hipEventCreate(&e) != hipSuccess) return nullptr;
+    return e;
+}
+
+// Brackets one launch with events when profiling is on.
+struct Launch {
+    moe_ctx* ctx;
+    hipStream_t s;
+    Rec rec{};
+    bool on = false;
+    Launch(moe_ctx* c, int kernel, hipStream_t st) : ctx(c), s(st) {
+        if (ctx->prof) {
+            rec.kernel = kernel;
+            rec.a = take_event(ctx);
+            rec.b = take_event(ctx);
+            on = rec.a && rec.b;
+            if (on) on = hipEventRecord(rec.a, s) == hipSuccess;
+        }
+    }
+    void done() {
+        if (on && hipEventRecord(rec.b, s) == hipSuccess) ctx->recs.push_back(rec);
+        on = false;
+    }
+};
+
+moe_status hip_status(hipError_t e) { return e == hipSuccess ? MOE_OK : MOE_ERR_HIP; }
+
+}  // namespace
+
+extern "C" {
+
+int32_t moe_align_capacity(int32_t M, int32_t k, int32_t E, int32_t b) {
+    if (M < 0 || k <= 0 || E <= 0 || b <= 0) return -1;
+    const int64_t c = align_capacity64(M, k, E, b);
+    return c > INT32_MAX ? -1 : (int32_t)c;
+}
+
+const char* moe_status_string(moe_status s) {
+    switch (s) {
+        case MOE_OK: return "ok";
+        case MOE_ERR_INVALID_ARG: return "invalid argument";
+        case MOE_ERR_UNSUPPORTED: return "unsupported shape or format";
+        case MOE_ERR_CAPACITY: return "capacity exceeded";
+        case MOE_ERR_HIP: return "HIP runtime error";
+        case MOE_ERR_DEVICE: return "device error flag set";
+    }
+    return "unknown status";
+}
+
+const char* moe_kernel_name(int32_t k) {
+    static const char* names[MOE_KERNEL_COUNT] = {"router_gemv", "router_topk",  "align",       "gateup",
+                                                  "gateup_vqlr", "down",         "combine",     "chan_select",
+                                                  "chan_gather", "chan_combine"};
+    return (k >= 0 && k < MOE_KERNEL_COUNT) ? names[k] : nullptr;
+}
+
+moe_status moe_create(const moe_config* cfg, const moe_weights* w, moe_ctx** out) {
+    if (!out) return MOE_ERR_INVALID_ARG;
+    *out = nullptr;
+    if (!cfg || !w) return MOE_ERR_INVALID_ARG;
+    moe_status st = check_config(cfg);
+    if (st != MOE_OK) return st;
+    st = check_weights(cfg, w);
+    if (st != MOE_OK) return st;
+
+    moe_ctx* ctx = new (std::nothrow) moe_ctx();
+    if (!ctx) return MOE_ERR_HIP;
+    ctx->cfg = *cfg;
+    ctx->w = *w;
+    if (hipGetDevice(&ctx->device) != hipSuccess) {
+        delete ctx;
+        return MOE_ERR_HIP;
+    }
+    const moe_config& c = *cfg;
+    const size_t MT = c.max_tokens, R = MT * c.top_k;
+    ctx->nslices = (c.H + kSliceRows - 1) / kSliceRows;
+    const size_t nrc = (c.I + (c.max_tokens == 1 ? 16 : kMinDownRows) - 1) / (c.max_tokens == 1 ? 16 : kMinDownRows);
+    const size_t nchan = c.max_keep > 0 ? (c.max_keep + kChanChunk - 1) / kChanChunk : 0;
+    size_t sizes[8] = {
+        256,                                                            // err flag
+        sizeof(float) * ctx->nslices * MT * c.E,                        // router partials
+        c.wformat == MOE_WFORMAT_VQLR ? sizeof(float) * ctx->nslices * MT * c.lr_r : 0,
+        c.wformat == MOE_WFORMAT_VQLR ? sizeof(float) * ctx->nslices * MT * c.lr_r : 0,
+        sizeof(float) * R * c.I,                                        // p
+        sizeof(float) * R * nrc * c.H,                                  // down partials
+        sizeof(int32_t) * MT * c.max_keep,                              // kept list
+        sizeof(float) * MT * nchan * c.H,                               // channel partials
+    };
+    size_t off[8], total = 0;
+    for (int i = 0; i < 8; ++i) {
+        off[i] = total;
+        total += (sizes[i] + 255) & ~(size_t)255;
+    }
+    if (hipMalloc(&ctx->ws, total) != hipSuccess) {
+        delete ctx;
+        return MOE_ERR_HIP;
+    }
+    ctx->ws_bytes = total;
+    char* base = static_cast<char*>(ctx->ws);
+    ctx->err = reinterpret_cast<int32_t*>(base + off[0]);
+    ctx->router_part = reinterpret_cast<float*>(base + off[1]);
+    ctx->zpart[0] = reinterpret_cast<float*>(base + off[2]);
+    ctx->zpart[1] = reinterpret_cast<float*>(base + off[3]);
+    ctx->p = reinterpret_cast<float*>(base + off[4]);
+    ctx->down_part = reinterpret_cast<float*>(base + off[5]);
+    ctx->kept_ws = reinterpret_cast<int32_t*>(base + off[6]);
+    ctx->chan_part = reinterpret_cast<float*>(base + off[7]);
+    if (hipMemset(ctx->err, 0, 256) != hipSuccess || hipDeviceSynchronize() != hipSuccess) {
+        hipFree(ctx->ws);
+        delete ctx;
+        return MOE_ERR_HIP;
+    }
+    *out = ctx;
+    return MOE_OK;
+}
+
+void moe_destroy(moe_ctx* ctx) {
+    if (!ctx) return;
+    hipDeviceSynchronize();
+    for (auto& r : ctx->recs) {
+        hipEventDestroy(r.a);
+        hipEventDestroy(r.b);
+    }
+    for (auto e : ctx->pool) hipEventDestroy(e);
+    if (ctx->ws) hipFree(ctx->ws);
+    delete ctx;
+}
+
+moe_status moe_route_topk(moe_ctx* ctx, const float* h, int32_t M, int32_t* topk_ids, float* topk_w,
+                          float* logits_out, void* stream) {
+    if (!ctx || M < 0) return MOE_ERR_INVALID_ARG;
+    if (M > ctx->cfg.max_tokens) return MOE_ERR_CAPACITY;
+    if (M == 0) return MOE_OK;
+    if (!h || !topk_ids || !topk_w || !aligned(h, 16)) return MOE_ERR_INVALID_ARG;
+    const moe_config& c = ctx->cfg;
+    hipStream_t s = static_cast<hipStream_t>(stream);
+    moe::GemvJob job{ctx->w.router_w, c.E, ctx->router_part};
+    Launch l1(ctx, MOE_KERNEL_ROUTER_GEMV, s);
+    hipError_t e = moe::launch_gemv_partials(h, M, c.H, kSliceRows, &job, 1, s);
+    l1.done();
+    if (e != hipSuccess) return MOE_ERR_HIP;
+    Launch l2(ctx, MOE_KERNEL_ROUTER_TOPK, s);
+    e = moe::launch_router_topk(ctx->router_part, ctx->nslices, M, c.E, c.top_k, ctx->w.router_bias, topk_ids, topk_w,
+                                logits_out, s);
+    l2.done();
+    return hip_status(e);
+}
+
+moe_status moe_align_blocks(moe_ctx* ctx, const int32_t* topk_ids, int32_t M, int32_t* sorted_routes,
+                            int32_t* block_expert, int32_t* counts, void* stream) {
+    if (!ctx || M < 0) return MOE_ERR_INVALID_ARG;
+    if (M > ctx->cfg.max_tokens) return MOE_ERR_CAPACITY;
+    if (!counts) return MOE_ERR_INVALID_ARG;
+    const moe_config& c = ctx->cfg;
+    hipStream_t s = static_cast<hipStream_t>(stream);
+    // M == 0: the kernel runs with no routes and only writes counts = {0, 0}
+    if (M > 0 && (!topk_ids || !sorted_routes || !block_expert)) return MOE_ERR_INVALID_ARG;
+    Launch l(ctx, MOE_KERNEL_ALIGN, s);
+    hipError_t e = moe::launch_align(topk_ids, M * c.top_k, c.E, c.block_b, sorted_routes, block_expert, counts,
+                                     ctx->err, s);
+    l.done();
+    return hip_status(e);
+}
+
+moe_status moe_expert_forward(moe_ctx* ctx, const float* h, int32_t M, const int32_t* topk_ids, const float* topk_w,
+                              const int32_t* sorted_routes, const int32_t* block_expert, const int32_t* counts,
+                              int32_t keep_channels, int32_t* kept_out, float* y, void* stream) {
+    if (!ctx || M < 0 || keep_channels < 0) return MOE_ERR_INVALID_ARG;
+    const moe_config& c = ctx->cfg;
+    if (M > c.max_tokens) return MOE_ERR_CAPACITY;
+    if (M == 0) return MOE_OK;
+    if (!h || !topk_ids || !topk_w || !y || !aligned(h, 16) || !aligned(y, 16)) return MOE_ERR_INVALID_ARG;
+    hipStream_t s = static_cast<hipStream_t>(stream);
+    hipError_t e;
+
+    if (keep_channels > 0) {
+        if (c.max_keep == 0 || c.wformat != MOE_WFORMAT_DENSE) return MOE_ERR_UNSUPPORTED;
+        if (keep_channels > c.max_keep) return MOE_ERR_CAPACITY;
+        const int K = keep_channels;
+        int32_t* kept = kept_out ? kept_out : ctx->kept_ws;
+        {
+            Launch l(ctx, MOE_KERNEL_CHAN_SELECT, s);
+            e = moe::launch_chan_select(topk_ids, topk_w, ctx->w.chan_norm, M, c.top_k, c.I, c.E, K, kept, s);
+            l.done();
+            if (e != hipSuccess) return MOE_ERR_HIP;
+        }
+        const int nchunks = (K + kChanChunk - 1) / kChanChunk;
+        {
+            Launch l(ctx, MOE_KERNEL_CHAN_GATHER, s);
+            e = moe::launch_chan_gather(topk_ids, topk_w, kept, M, c.top_k, c.I, c.E, c.H, K, kChanChunk, h,
+                                        ctx->w.w_gate, ctx->w.w_up, ctx->w.w_down, ctx->chan_part, s);
+            l.done();
+            if (e != hipSuccess) return MOE_ERR_HIP;
+        }
+        Launch l(ctx, MOE_KERNEL_CHAN_COMBINE, s);
+        e = moe::launch_chan_combine(M, c.H, nchunks, ctx->chan_part, y, s);
+        l.done();
+        return hip_status(e);
+    }
+
+    if (!sorted_routes || !block_expert || !counts) return MOE_ERR_INVALID_ARG;
+    moe::PlanArgs plan{};
+    plan.topk_ids = topk_ids;
+    plan.sorted_routes = sorted_routes;
+    plan.block_expert = block_expert;
+    plan.counts = counts;
+    plan.R = M * c.top_k;
+    plan.k = c.top_k;
+    plan.b = c.block_b;
+    plan.max_blocks = (int)(align_capacity64(M, c.top_k, c.E, c.block_b) / c.block_b);
+    plan.E = c.E;
+
+    if (c.wformat == MOE_WFORMAT_DENSE) {
+        Launch l(ctx, MOE_KERNEL_GATEUP, s);
+        e = moe::launch_gateup_dense(plan, h, c.H, c.I, ctx->w.w_gate, ctx->w.w_up, ctx->p, ctx->err, s);
+        l.done();
+        if (e != hipSuccess) return MOE_ERR_HIP;
+    } else {
+        moe::GemvJob jobs[2] = {{ctx->w.lr_basis[0], c.lr_r, ctx->zpart[0]}, {ctx->w.lr_basis[1], c.lr_r, ctx->zpart[1]}};
+        {
+            Launch l(ctx, MOE_KERNEL_ROUTER_GEMV, s);
+            e = moe::launch_gemv_partials(h, M, c.H, kSliceRows, jobs, 2, s);
+            l.done();
+            if (e != hipSuccess) return MOE_ERR_HIP;
+        }
+        moe::VqArgs vq{};
+        for (int P = 0; P < 2; ++P) {
+            vq.C[P] = ctx->w.lr_coef[P];
+            vq.B[P] = ctx->w.vq_book[P];
+            vq.J[P] = ctx->w.vq_idx[P];
+            vq.zpart[P] = ctx->zpart[P];
+        }
+        vq.zslices = ctx->nslices;
+        vq.M = M;
+        vq.r = c.lr_r;
+        vq.K = c.vq_K;
+        vq.d = c.vq_d;
+        Launch l(ctx, MOE_KERNEL_GATEUP_VQLR, s);
+        e = moe::launch_gateup_vqlr(plan, vq, h, c.H, c.I, ctx->p, ctx->err, s);
+        l.done();
+        if (e != hipSuccess) return MOE_ERR_HIP;
+    }
+    const int RC = down_rows(M);
+    const int nrc = (c.I + RC - 1) / RC;
+    {
+        Launch l(ctx, MOE_KERNEL_DOWN, s);
+        e = moe::launch_down(plan, c.H, c.I, RC, ctx->w.w_down, ctx->p, ctx->down_part, ctx->err, s);
+        l.done();
+        if (e != hipSuccess) return MOE_ERR_HIP;
+    }
+    Launch l(ctx, MOE_KERNEL_COMBINE, s);
+    e = moe::launch_combine(topk_ids, topk_w, M, c.top_k, c.E, c.H, nrc, ctx->down_part, y, s);
+    l.done();
+    return hip_status(e);
+}
+
+moe_status moe_read_device_error(moe_ctx* ctx, int32_t* flags, int32_t clear) {
+    if (!ctx || !flags) return MOE_ERR_INVALID_ARG;
+    if (hipDeviceSynchronize() != hipSuccess) return MOE_ERR_HIP;
+    int32_t v = 0;
+    if (hipMemcpy(&v, ctx->err, sizeof(v), hipMemcpyDeviceToHost) != hipSuccess) return MOE_ERR_HIP;
+    if (clear && v && hipMemset(ctx->err, 0, sizeof(int32_t)) != hipSuccess) return MOE_ERR_HIP;
+    *flags = v;
+    return v ? MOE_ERR_DEVICE : MOE_OK;
+}
+
+moe_status moe_channel_norms(const moe_config* cfg, const uint16_t* w_gate, const uint16_t* w_up,
+                             const uint16_t* w_down, float* norms, void* stream) {
+    if (!cfg || !w_gate || !w_up || !w_down || !norms) return MOE_ERR_INVALID_ARG;
+    if (cfg->H <= 0 || cfg->I <= 0 || cfg->E <= 0) return MOE_ERR_INVALID_ARG;
+    if (cfg->H % 8 || (int64_t)cfg->E * cfg->I > INT32_MAX) return MOE_ERR_UNSUPPORTED;
+    if (!aligned(w_gate, 16) || !aligned(w_up, 16) || !aligned(w_down, 16) || !aligned(norms, 4))
+        return MOE_ERR_INVALID_ARG;
+    return hip_status(moe::launch_channel_norms(cfg->E, cfg->I, cfg->H, w_gate, w_up, w_down, norms,
+                                                static_cast<hipStream_t>(stream)));
+}
+
+moe_status moe_validate_plan(const int32_t* ids, int32_t M, int32_t k, int32_t E, int32_t b, const int32_t* rows,
+                             const int32_t* blocks, const int32_t* counts, int32_t* reason) {
+    auto fail = [&](int code) {
+        if (reason) *reason = code;
+        return MOE_ERR_INVALID_ARG;
+    };
+    if (reason) *reason = 0;
+    if (M < 0 || k <= 0 || E <= 0 || b <= 0) return MOE_ERR_INVALID_ARG;
+    if (M > 0 && (!ids || !counts)) return MOE_ERR_INVALID_ARG;
+    if (M == 0) return MOE_OK;
+    const int64_t R = (int64_t)M * k;
+    const int64_t cap = align_capacity64(M, k, E, b);
+    const int64_t nb = counts[0], np = counts[1];
+    if (nb < 0 || np != nb * b || np > cap) return fail(1);
+    if (nb > 0 && (!rows || !blocks)) return MOE_ERR_INVALID_ARG;
+    std::vector<int> seen((size_t)R, 0);
+    int prev_e = -1;
+    for (int64_t blk = 0; blk < nb; ++blk) {
+        const int e = blocks[blk];
+        if (e < 0 || e >= E) return fail(6);
+        if (e < prev_e) return fail(6);
+        prev_e = e;
+        bool pad_seen = false;
+        int nvalid = 0;
+        for (int q = 0; q < b; ++q) {
+            const int64_t r = rows[blk * b + q];
+            if (r == R) {
+                pad_seen = true;
+                continue;
+            }
+            if (r < 0 || r > R) return fail(8);
+            if (pad_seen) return fail(5);
+            const int id = ids[r];
+            if (id < 0 || id >= E) return fail(7);
+            if (id != e) return fail(4);
+            if (seen[(size_t)r]++) return fail(3);
+            ++nvalid;
+        }
+        if (nvalid == 0) return fail(5);
+    }
+    for (int64_t r = 0; r < R; ++r)
+        if (ids[r] >= 0 && ids[r] < E && !seen[(size_t)r]) return fail(2);
+    return MOE_OK;
+}
+
+moe_status moe_profile_enable(moe_ctx* ctx, int32_t enable) {
+    if (!ctx) return MOE_ERR_INVALID_ARG;
+    ctx->prof = enable != 0;
+    return MOE_OK;
+}
+
+moe_status moe_profile_read(moe_ctx* ctx, double* ms, int64_t* launches) {
+    if (!ctx || !ms || !launches) return MOE_ERR_INVALID_ARG;
+    moe_status st = MOE_OK;
+    for (auto& r : ctx->recs) {
+        float t = 0.f;
+        if (hipEventSynchronize(r.b) != hipSuccess || hipEventElapsedTime(&t, r.a, r.b) != hipSuccess) {
+            st = MOE_ERR_HIP;
+        } else {
+            ms[r.kernel] += t;
+            launches[r.kernel] += 1;
+        }
+        ctx->pool.push_back(r.a);
+        ctx->pool.push_back(r.b);
+    }
+    ctx->recs.clear();
+    return st;
+}
+
+}  // extern "C"

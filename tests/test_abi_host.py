@@ -1,0 +1,204 @@
+"""CPU tests of the C ABI: the library loads and exports every declared symbol,
+host-side checks fail closed before touching the GPU, and the host plan
+validator rejects each class of broken plan (in the spirit of the mutation
+rejections of "Route-Block Membership Selects Packed-AWQ Arithmetic", Sec. 4.2)."""
+import ctypes
+import os
+import re
+import shutil
+import subprocess
+import sys
+
+import numpy as np
+import pytest
+
+import oracle as O
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+
+
+@pytest.fixture(scope="module")
+def mb():
+    import memory_bound_routed_amd as m
+    return m
+
+
+def declared_functions():
+    src = open(os.path.join(ROOT, "include", "moe.h")).read()
+    src = re.sub(r"/\*.*?\*/", "", src, flags=re.S)
+    return sorted(set(re.findall(r"\b(moe_[a-z_]+)\s*\(", src)))
+
+
+def test_header_declares_the_five_calls_and_helpers():
+    names = declared_functions()
+    for n in ("moe_create", "moe_route_topk", "moe_align_blocks", "moe_expert_forward", "moe_destroy"):
+        assert n in names
+
+
+def test_library_exports_every_declared_symbol(mb):
+    lib = ctypes.CDLL(mb.LIB_PATH)
+    for name in declared_functions():
+        assert hasattr(lib, name), name
+    assert sorted(mb.EXPORTS) == declared_functions()
+    nm = subprocess.run(["nm", "-D", "--defined-only", mb.LIB_PATH], capture_output=True, text=True).stdout
+    for name in declared_functions():
+        assert re.search(r"\bT %s\b" % name, nm), name
+
+
+def test_status_strings_and_capacity(mb):
+    for s in range(6):
+        assert mb.moe_status_string(s)
+    assert mb.moe_status_string(99) == "unknown status"
+    assert mb.moe_align_capacity(21, 8, 128, 8) == 168 + 128 * 7 == O.align_capacity(21, 8, 128, 8)
+    assert mb.moe_align_capacity(1, 8, 128, 8) == 8 + 8 * 7
+    assert mb.moe_align_capacity(0, 8, 128, 8) == 0
+    assert mb.moe_align_capacity(-1, 8, 128, 8) == -1
+    assert mb.moe_kernel_name(3) == "gateup" and mb.moe_kernel_name(99) is None
+
+
+def base_cfg(mb, **kw):
+    d = dict(H=2048, I=768, E=128, top_k=8, block_b=8, max_tokens=1)
+    d.update(kw)
+    return mb.make_config(**d)
+
+
+FAKE = 0x10000  # 16-byte aligned fake address: never dereferenced by host checks
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(H=0), 1), (dict(I=-1), 1), (dict(top_k=0), 1), (dict(max_tokens=0), 1), (dict(max_keep=-1), 1),
+    (dict(H=2044), 2), (dict(H=8200), 2), (dict(E=20), 2), (dict(E=2048), 2), (dict(top_k=33, E=64), 2),
+    (dict(top_k=9, E=8), 2), (dict(block_b=65), 2), (dict(max_tokens=4097), 2), (dict(max_tokens=600), 2),
+    (dict(wformat=7), 2), (dict(wformat=1, vq_d=4, vq_K=256, lr_r=64), 2),
+    (dict(wformat=1, vq_d=8, vq_K=257, lr_r=64), 2), (dict(wformat=1, vq_d=8, vq_K=256, lr_r=60), 2),
+    (dict(max_keep=8 * 768 + 1), 2), (dict(wformat=1, vq_d=8, vq_K=256, lr_r=64, max_keep=10), 2),
+])
+def test_create_rejects_bad_configs_before_any_gpu_call(mb, kw, status):
+    cfg = base_cfg(mb, **kw)
+    w = mb.make_weights(FAKE, FAKE, w_gate=FAKE, w_up=FAKE)
+    st, ctx = mb.moe_create_status(cfg, w)
+    assert st == status and ctx is None
+
+
+def test_create_rejects_missing_or_misaligned_weights(mb):
+    cfg = base_cfg(mb)
+    assert mb.moe_create_status(cfg, mb.make_weights(FAKE, FAKE))[0] == mb.MOE_ERR_INVALID_ARG  # no gate/up
+    assert mb.moe_create_status(cfg, mb.make_weights(None, FAKE, w_gate=FAKE, w_up=FAKE))[0] == 1
+    assert mb.moe_create_status(cfg, mb.make_weights(FAKE, FAKE, w_gate=FAKE + 2, w_up=FAKE))[0] == 1
+    vq = base_cfg(mb, wformat=1, vq_d=8, vq_K=256, lr_r=64)
+    ok = dict(lr_basis=(FAKE, FAKE), lr_coef=(FAKE, FAKE), vq_book=(FAKE, FAKE), vq_idx=(FAKE, FAKE))
+    bad = dict(ok, vq_idx=(FAKE, None))
+    assert mb.moe_create_status(vq, mb.make_weights(FAKE, FAKE, **bad))[0] == 1
+    bad = dict(ok, vq_idx=(FAKE, FAKE + 1))
+    assert mb.moe_create_status(vq, mb.make_weights(FAKE, FAKE, **bad))[0] == 1
+    keep = base_cfg(mb, max_keep=799)
+    assert mb.moe_create_status(keep, mb.make_weights(FAKE, FAKE, w_gate=FAKE, w_up=FAKE))[0] == 1  # no norms
+    assert mb.moe_create_status(None, mb.make_weights(FAKE, FAKE))[0] == 1
+
+
+def test_calls_on_null_context_fail_closed(mb):
+    lib = mb._lib
+    assert lib.moe_route_topk(None, FAKE, 1, FAKE, FAKE, None, None) == 1
+    assert lib.moe_align_blocks(None, FAKE, 1, FAKE, FAKE, FAKE, None) == 1
+    assert lib.moe_expert_forward(None, FAKE, 1, FAKE, FAKE, FAKE, FAKE, FAKE, 0, None, FAKE, None) == 1
+    assert lib.moe_profile_enable(None, 1) == 1
+    flags = ctypes.c_int32(0)
+    assert lib.moe_read_device_error(None, ctypes.byref(flags), 0) == 1
+    lib.moe_destroy(None)  # no-op
+    cfg = base_cfg(mb)
+    assert lib.moe_channel_norms(ctypes.byref(cfg), None, FAKE, FAKE, FAKE, None) == 1
+    bad = base_cfg(mb, H=2044)
+    assert lib.moe_channel_norms(ctypes.byref(bad), FAKE, FAKE, FAKE, FAKE, None) == 2
+
+
+# ---------------------------------------------------------------- plan validator
+
+def plan_of(ids, E, b):
+    al = O.align_blocks(ids, E, b)
+    return (al["sorted_routes"].astype(np.int32), al["block_expert"].astype(np.int32),
+            np.array([al["num_blocks"], al["num_padded"]], np.int32))
+
+
+def routing(seed, M=21, k=8, E=128, hot=True):
+    rng = np.random.default_rng(seed)
+    p = np.ones(E)
+    if hot:
+        p[:4] = 30.0
+    return np.stack([rng.choice(E, k, replace=False, p=p / p.sum()) for _ in range(M)]).astype(np.int32)
+
+
+def test_validator_accepts_canonical_and_noncanonical_valid_plans(mb):
+    for seed in range(30):
+        ids = routing(seed)
+        rows, blocks, counts = plan_of(ids, 128, 8)
+        assert mb.moe_validate_plan(ids, 21, 8, 128, 8, rows, blocks, counts) == (0, 0)
+        R = ids.size
+        # within-block permutation
+        perm = rows.copy()
+        seg = perm[:8]
+        v = seg[seg != R]
+        seg[: v.size] = v[::-1]
+        assert mb.moe_validate_plan(ids, 21, 8, 128, 8, perm, blocks, counts) == (0, 0)
+        # cross-boundary exchange between two blocks of one expert
+        multi = [e for e in set(blocks.tolist()) if (blocks == e).sum() >= 2]
+        if multi:
+            b0 = int(np.nonzero(blocks == multi[0])[0][0])
+            sw = rows.copy()
+            sw[b0 * 8], sw[b0 * 8 + 8] = rows[b0 * 8 + 8], rows[b0 * 8]
+            assert mb.moe_validate_plan(ids, 21, 8, 128, 8, sw, blocks, counts) == (0, 0)
+
+
+def test_validator_rejects_each_mutation_class(mb):
+    ids = routing(7)
+    R = ids.size
+    rows, blocks, counts = plan_of(ids, 128, 8)
+    V = lambda r=rows, b=blocks, c=counts, i=ids: mb.moe_validate_plan(i, 21, 8, 128, 8, r, b, c)
+    assert V() == (0, 0)
+    # 1: counts out of range / inconsistent
+    assert V(c=np.array([counts[0], counts[1] + 1], np.int32))[1] == 1
+    assert V(c=np.array([-1, -8], np.int32))[1] == 1
+    # 2: a route dropped (replaced by a pad at a block tail that keeps another route)
+    blk = next(i for i in range(counts[0]) if (rows[i * 8:i * 8 + 8] != R).sum() >= 2)
+    last = blk * 8 + int((rows[blk * 8:blk * 8 + 8] != R).sum()) - 1
+    m = rows.copy(); m[last] = R
+    assert V(r=m)[1] == 2
+    # 3: a route duplicated
+    m = rows.copy(); m[last] = rows[blk * 8]
+    assert V(r=m)[1] == 3
+    # 4: a row placed in another expert's block
+    other = next(i for i in range(counts[0]) if blocks[i] != blocks[blk])
+    m = rows.copy(); m[blk * 8], m[other * 8] = rows[other * 8], rows[blk * 8]
+    assert V(r=m)[1] == 4
+    # 5: a pad before a route inside a block
+    m = rows.copy(); m[blk * 8], m[last] = R, rows[blk * 8]
+    assert V(r=m)[1] == 5
+    # 6: blocks out of expert order
+    b = blocks.copy(); b[0], b[-1] = blocks[-1], blocks[0]
+    assert V(b=b)[1] in (4, 6)
+    b = blocks.copy(); b[0] = 128
+    assert V(b=b)[1] == 6
+    # 7: an invalid route id present in the plan
+    bad = ids.copy(); bad.flat[rows[0]] = -1
+    assert V(i=bad)[1] in (4, 7)
+    # 8: a row value outside [0, R]
+    m = rows.copy(); m[0] = R + 5
+    assert V(r=m)[1] == 8
+
+
+def test_product_package_never_imports_the_oracle():
+    pkg = os.path.join(ROOT, "memory_bound_routed_amd")
+    for dirpath, _, files in os.walk(pkg):
+        for f in files:
+            if f.endswith((".py", ".cpp", ".hip", ".h")):
+                text = open(os.path.join(dirpath, f)).read()
+                assert not re.search(r"^\s*(from|import)\s+oracle\b", text, re.M), f
+                assert "moe_oracle" not in text, f
+
+
+def test_binding_fails_loudly_without_the_library(tmp_path):
+    dst = tmp_path / "memory_bound_routed_amd"
+    dst.mkdir()
+    shutil.copy(os.path.join(ROOT, "memory_bound_routed_amd", "__init__.py"), dst / "__init__.py")
+    r = subprocess.run([sys.executable, "-c", "import memory_bound_routed_amd"], cwd=tmp_path,
+                       capture_output=True, text=True)
+    assert r.returncode != 0 and "libmoe.so is not built" in r.stderr

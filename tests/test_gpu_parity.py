@@ -1,0 +1,466 @@
+"""GPU parity: the HIP library, called through its C ABI, against the fp64
+oracle on the same seeded inputs.
+
+Comparison rules
+  * integer outputs (top-k ids, alignment plan, kept channel list) are
+    compared bit-exactly: stage-isolated (each stage fed the GPU's previous
+    outputs, the oracle stage given the same inputs) always, and end-to-end
+    wherever the certified margin of the router decision holds;
+  * the GPU top-k must equal the oracle's top-k applied to the GPU's own fp32
+    logits (the decision taken in the kernel's precision);
+  * floating outputs: rel-L2 <= 1e-3 and max-abs <= 5e-3 * max|y_ref|.
+"""
+import os
+import subprocess
+import sys
+
+import numpy as np
+import pytest
+
+import oracle as O
+import synth
+from helpers import (certified_tokens, check_close, logit_error_bound, to_dev, upload_layer)
+
+pytestmark = pytest.mark.gpu
+
+
+@pytest.fixture(scope="module")
+def mb():
+    import torch
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+    import memory_bound_routed_amd as m
+    return m
+
+
+def say(*a):
+    print(*a, flush=True)
+
+
+def make_layer(mb, wl, inp, max_tokens, norms_dev=None, max_keep=0):
+    dev = upload_layer(inp)
+    if norms_dev is not None:
+        dev["chan_norm"] = norms_dev
+    if wl.vq:
+        cfg = mb.make_config(wl.H, wl.I, wl.E, wl.k, wl.block_b, max_tokens, mb.MOE_WFORMAT_VQLR, wl.vq_d, wl.vq_K,
+                             wl.lr_r, max_keep)
+    else:
+        cfg = mb.make_config(wl.H, wl.I, wl.E, wl.k, wl.block_b, max_tokens, max_keep=max_keep)
+    return mb.Layer(cfg, dev)
+
+
+def run_step(mb, layer, h_np, keep=0):
+    import torch
+    M = h_np.shape[0]
+    h = to_dev(h_np)
+    layer.route(h, M, logits=True)
+    if not keep:
+        layer.align(M)
+    layer.forward(h, M, keep=keep)
+    torch.cuda.synchronize()
+    out = {
+        "ids": layer.ids[:M].cpu().numpy().astype(np.int64),
+        "w": layer.w[:M].cpu().numpy(),
+        "logits": layer.logits[:M].cpu().numpy(),
+        "y": layer.y[:M].cpu().numpy().copy(),
+    }
+    if not keep:
+        cnt = layer.counts.cpu().numpy()
+        out["num_blocks"], out["num_padded"] = int(cnt[0]), int(cnt[1])
+        out["sorted_routes"] = layer.sorted_routes[: cnt[1]].cpu().numpy().astype(np.int64)
+        out["block_expert"] = layer.block_expert[: cnt[0]].cpu().numpy().astype(np.int64)
+    else:
+        out["kept"] = layer.kept.view(-1)[: M * keep].view(M, keep).cpu().numpy().astype(np.int64)
+    out["err"] = mb.moe_read_device_error(layer.ctx)
+    return out
+
+
+def check_router(g, inp, k, H):
+    """Ids: exact in the kernel's precision; exact vs fp64 where certified."""
+    ref_l = O.router_logits(inp["h"], inp["router_w"], inp.get("router_bias"))
+    bound = logit_error_bound(inp["h"], inp["router_w"], H, inp.get("router_bias"))
+    err = np.abs(g["logits"].astype(np.float64) - ref_l)
+    assert np.all(err <= bound), "logit error above the fp32 bound"
+    own = O.topk_select(g["logits"].astype(np.float64), k)
+    np.testing.assert_array_equal(g["ids"], own)
+    np.testing.assert_allclose(g["w"], O.affinities(g["logits"].astype(np.float64), own), rtol=2e-6, atol=1e-7)
+    ok = certified_tokens(ref_l, bound, k)
+    ref_ids = O.topk_select(ref_l, k)
+    for t in range(len(ok)):
+        if ok[t]:
+            np.testing.assert_array_equal(g["ids"][t], ref_ids[t])
+        else:
+            say("  token %d: top-%d not certified by the fp32 bound (ill-posed seed); ids %s vs oracle %s"
+                % (t, k, g["ids"][t], ref_ids[t]))
+    return ref_l, ok
+
+
+def check_plan(g, E, b):
+    al = O.align_blocks(g["ids"], E, b)
+    assert g["num_blocks"] == al["num_blocks"] and g["num_padded"] == al["num_padded"]
+    np.testing.assert_array_equal(g["sorted_routes"], al["sorted_routes"])
+    np.testing.assert_array_equal(g["block_expert"], al["block_expert"])
+
+
+# ----------------------------------------------------------------------------
+
+def test_tiny_end_to_end(mb):
+    wl = synth.WORKLOADS["tiny_h256_i128_e16_k2"]
+    say("tiny_h256_i128_e16_k2 layer 0")
+    inp = synth.layer_inputs(wl, 0)
+    layer = make_layer(mb, wl, inp, 1)
+    g = run_step(mb, layer, inp["h"])
+    assert g["err"] == 0
+    _, ok = check_router(g, inp, wl.k, wl.H)
+    check_plan(g, wl.E, wl.block_b)
+    ref = O.dense_forward(inp["h"], g["ids"], g["w"].astype(np.float64), inp["w_gate"], inp["w_up"], inp["w_down"])
+    say("  stage-isolated", check_close(g["y"], ref))
+    if ok.all():
+        full = O.moe_step(inp, wl.k)
+        say("  end-to-end", check_close(g["y"], full["y"]))
+    layer.close()
+
+
+def test_dense_b1_full_layer(mb):
+    wl = synth.WORKLOADS["dense_h2048_i768_e128_k8_m1"]
+    say("dense_h2048_i768_e128_k8_m1 layer 0 (full size)")
+    inp = synth.layer_inputs(wl, 0)
+    layer = make_layer(mb, wl, inp, 1)
+    for step in range(3):  # three independent tokens on the same layer
+        h = synth.hidden(wl, 0, step)
+        g = run_step(mb, layer, h)
+        assert g["err"] == 0
+        stage_inp = dict(inp, h=h)
+        _, ok = check_router(g, stage_inp, wl.k, wl.H)
+        check_plan(g, wl.E, wl.block_b)
+        assert g["num_blocks"] == wl.k and g["num_padded"] == 8 * wl.k
+        ref = O.dense_forward(h, g["ids"], g["w"].astype(np.float64), inp["w_gate"], inp["w_up"], inp["w_down"])
+        say("  step", step, "stage-isolated", check_close(g["y"], ref))
+        if ok.all():
+            full = O.moe_step(stage_inp, wl.k)
+            check_close(g["y"], full["y"])
+    layer.close()
+
+
+def test_aligned_m21_hot_experts_and_plan_injection(mb):
+    import torch
+    wl = synth.WORKLOADS["aligned_h2048_i768_e128_k8_m21"]
+    say("aligned_h2048_i768_e128_k8_m21 layer 0 (full size)")
+    inp = synth.layer_inputs(wl, 0)
+    layer = make_layer(mb, wl, inp, wl.M)
+    g = run_step(mb, layer, inp["h"])
+    assert g["err"] == 0
+    check_router(g, inp, wl.k, wl.H)
+    check_plan(g, wl.E, wl.block_b)
+    hot = np.nonzero(inp["router_bias"])[0]
+    frac = float(np.isin(g["ids"], hot).mean())
+    say("  hot-expert share of routes %.3f, blocks %d, rows %d, distinct experts %d"
+        % (frac, g["num_blocks"], g["num_padded"], len(set(g["ids"].ravel()))))
+    ref = O.dense_forward(inp["h"], g["ids"], g["w"].astype(np.float64), inp["w_gate"], inp["w_up"], inp["w_down"])
+    say("  stage-isolated", check_close(g["y"], ref))
+
+    # plan injection: valid non-canonical plans give bitwise the same y
+    M = wl.M
+    h = to_dev(inp["h"])
+    base = g["y"]
+    rows = g["sorted_routes"].copy()
+    blocks = g["block_expert"].copy()
+    cap = mb.moe_align_capacity(M, wl.k, wl.E, wl.block_b)
+
+    def forward_with(rows_np):
+        sr = torch.full((cap,), -7, dtype=torch.int32, device="cuda")
+        sr[: rows_np.size] = torch.from_numpy(rows_np.astype(np.int32)).cuda()
+        be = torch.from_numpy(blocks.astype(np.int32)).cuda()
+        ct = torch.tensor([g["num_blocks"], g["num_padded"]], dtype=torch.int32, device="cuda")
+        st, why = mb.moe_validate_plan(g["ids"], M, wl.k, wl.E, wl.block_b, rows_np, blocks,
+                                       np.array([g["num_blocks"], g["num_padded"]]))
+        assert st == 0, why
+        layer.forward(h, M, plan=(sr, be, ct))
+        torch.cuda.synchronize()
+        assert mb.moe_read_device_error(layer.ctx) == 0
+        return layer.y[:M].cpu().numpy()
+
+    # within-block permutation: reverse the valid rows of every block
+    perm = rows.copy()
+    R = M * wl.k
+    for blk in range(g["num_blocks"]):
+        seg = perm[blk * 8:(blk + 1) * 8]
+        valid = seg[seg != R]
+        seg[: valid.size] = valid[::-1]
+    assert np.array_equal(forward_with(perm), base)
+    # cross-boundary exchange: swap rows across two blocks of one expert
+    multi = [e for e in set(blocks.tolist()) if (blocks == e).sum() >= 2]
+    assert multi, "expected an expert with more than one block"
+    e = multi[0]
+    b0 = int(np.nonzero(blocks == e)[0][0])
+    swap = rows.copy()
+    swap[b0 * 8], swap[(b0 + 1) * 8] = rows[(b0 + 1) * 8], rows[b0 * 8]
+    mem_a = O.block_membership(rows, blocks, R)
+    mem_b = O.block_membership(swap, blocks, R)
+    assert mem_a != mem_b
+    assert np.array_equal(forward_with(swap), base)
+    layer.close()
+
+
+def test_chansparse_keep799(mb):
+    import torch
+    wl = synth.WORKLOADS["chansparse_h2048_i768_e128_k8_m1_keep799"]
+    say("chansparse_h2048_i768_e128_k8_m1_keep799 layer 0 (full size)")
+    inp = synth.layer_inputs(wl, 0)
+    dev = upload_layer(inp)
+    norms = torch.empty((wl.E, wl.I), dtype=torch.float32, device="cuda")
+    cfg = mb.make_config(wl.H, wl.I, wl.E, wl.k, wl.block_b, 1, max_keep=wl.keep)
+    mb.moe_channel_norms(cfg, dev["w_gate"], dev["w_up"], dev["w_down"], norms)
+    torch.cuda.synchronize()
+    gn = norms.cpu().numpy()
+    ref_n = O.channel_norms(inp["w_gate"], inp["w_up"], inp["w_down"], experts=range(0, wl.E, 9))
+    sel = list(range(0, wl.E, 9))
+    ulp = np.abs(gn[sel].view(np.int32).astype(np.int64) - ref_n[sel].view(np.int32).astype(np.int64))
+    assert ulp.max() <= 1, "norms differ by %d ulp" % ulp.max()
+    dev["chan_norm"] = norms
+    layer = mb.Layer(cfg, dev)
+    for step in range(2):
+        h = synth.hidden(wl, 0, step)
+        g = run_step(mb, layer, h, keep=wl.keep)
+        assert g["err"] == 0
+        _, ok = check_router(g, dict(inp, h=h), wl.k, wl.H)
+        kept_ref = O.channel_select(g["w"], g["ids"], gn, wl.keep)
+        np.testing.assert_array_equal(g["kept"], kept_ref)
+        per_slot = np.bincount(g["kept"][0] // wl.I, minlength=wl.k)
+        say("  step", step, "kept per slot", per_slot.tolist())
+        ref = O.channel_sparse_forward(h, g["ids"], g["w"].astype(np.float64), inp["w_gate"], inp["w_up"],
+                                       inp["w_down"], kept_ref)
+        say("  stage-isolated", check_close(g["y"], ref))
+    layer.close()
+
+
+def test_chansparse_all_channels_equals_dense(mb):
+    import torch
+    wl = synth.small_workload("sparse_all", H=264, I=40, E=16, k=3, M=2, seed=77)
+    inp = synth.layer_inputs(wl, 0)
+    inp["h"] = synth.hidden(wl, 0, 0, M=2)
+    dev = upload_layer(inp)
+    norms = torch.empty((wl.E, wl.I), dtype=torch.float32, device="cuda")
+    cfg = mb.make_config(wl.H, wl.I, wl.E, wl.k, 8, 2, max_keep=wl.k * wl.I)
+    mb.moe_channel_norms(cfg, dev["w_gate"], dev["w_up"], dev["w_down"], norms)
+    dev["chan_norm"] = norms
+    layer = mb.Layer(cfg, dev)
+    gs = run_step(mb, layer, inp["h"], keep=wl.k * wl.I)
+    np.testing.assert_array_equal(gs["kept"], np.tile(np.arange(wl.k * wl.I), (2, 1)))
+    gd = run_step(mb, layer, inp["h"])
+    ref = O.dense_forward(inp["h"], gd["ids"], gd["w"].astype(np.float64), inp["w_gate"], inp["w_up"], inp["w_down"])
+    check_close(gs["y"], ref)
+    check_close(gd["y"], ref)
+    # K = 1: a single channel
+    g1 = run_step(mb, layer, inp["h"], keep=1)
+    k1 = O.channel_select(g1["w"], g1["ids"], norms.cpu().numpy(), 1)
+    np.testing.assert_array_equal(g1["kept"], k1)
+    check_close(g1["y"], O.channel_sparse_forward(inp["h"], g1["ids"], g1["w"].astype(np.float64), inp["w_gate"],
+                                                  inp["w_up"], inp["w_down"], k1))
+    layer.close()
+
+
+def test_vqlr_b4(mb):
+    wl = synth.WORKLOADS["vqlr_h2048_i768_e128_k8_m4_d8_K256_r64"]
+    say("vqlr_h2048_i768_e128_k8_m4_d8_K256_r64 layer 0 (full size)")
+    inp = synth.layer_inputs(wl, 0)
+    layer = make_layer(mb, wl, inp, wl.M)
+    g = run_step(mb, layer, inp["h"])
+    assert g["err"] == 0
+    check_router(g, inp, wl.k, wl.H)
+    check_plan(g, wl.E, wl.block_b)
+    say("  distinct experts", len(set(g["ids"].ravel())))
+    ref = O.vqlr_forward(inp["h"], g["ids"], g["w"].astype(np.float64), inp, inp["w_down"])
+    say("  stage-isolated", check_close(g["y"], ref))
+    layer.close()
+
+
+def test_vq_exact_codebook_equals_dense_path(mb):
+    """With C = 0 the VQ weights are exactly bf16 (a code-book lookup), so the
+    GPU VQ path and the GPU dense path on the materialised weights must both
+    meet the tolerance against one oracle output."""
+    wl = synth.small_workload("vq_exact", H=512, I=48, E=16, k=4, M=3, seed=91, vq=True, lr_r=16)
+    inp = synth.layer_inputs(wl, 0)
+    inp["h"] = synth.hidden(wl, 0, 0, M=3)
+    for P in ("gate", "up"):
+        inp["lr_coef_" + P][:] = 0
+    lv = make_layer(mb, wl, inp, 3)
+    gv = run_step(mb, lv, inp["h"])
+    dense = {k: v for k, v in inp.items() if not k.startswith(("lr_", "vq_"))}
+    dense["w_gate"] = inp["vq_book_gate"][inp["vq_idx_gate"].astype(np.int64)].reshape(wl.E, wl.I, wl.H)
+    dense["w_up"] = inp["vq_book_up"][inp["vq_idx_up"].astype(np.int64)].reshape(wl.E, wl.I, wl.H)
+    wd = synth.small_workload("vq_exact_dense", H=512, I=48, E=16, k=4, M=3, seed=91)
+    ld = make_layer(mb, wd, dense, 3)
+    gd = run_step(mb, ld, inp["h"])
+    np.testing.assert_array_equal(gv["ids"], gd["ids"])
+    ref = O.dense_forward(inp["h"], gd["ids"], gd["w"].astype(np.float64), dense["w_gate"], dense["w_up"],
+                          dense["w_down"])
+    check_close(gv["y"], ref, "vq")
+    check_close(gd["y"], ref, "dense")
+    check_close(gv["y"], gd["y"], "vq vs dense")
+    lv.close()
+    ld.close()
+
+
+@pytest.mark.parametrize("H,I,E,k,M,b", [
+    (520, 37, 24, 3, 5, 8),     # ragged hidden tail (not a multiple of 512) and channel tail
+    (8, 1, 8, 1, 1, 8),         # smallest shapes
+    (4104, 9, 8, 2, 3, 4),      # > 4096 hidden (16-load register tile), block size 4
+    (1024, 70, 64, 6, 12, 16),  # block size 16, several tokens
+    (256, 33, 16, 16, 2, 8),    # k = E: every expert routed
+])
+def test_ragged_shapes(mb, H, I, E, k, M, b):
+    say("ragged", dict(H=H, I=I, E=E, k=k, M=M, b=b))
+    wl = synth.small_workload("ragged_%d_%d_%d_%d_%d" % (H, I, E, k, M), H=H, I=I, E=E, k=k, M=M, seed=H + I, block_b=b)
+    inp = synth.layer_inputs(wl, 0)
+    inp["h"] = synth.hidden(wl, 0, 0, M=M)
+    layer = make_layer(mb, wl, inp, M)
+    g = run_step(mb, layer, inp["h"])
+    assert g["err"] == 0
+    check_router(g, inp, k, H)
+    check_plan(g, E, b)
+    ref = O.dense_forward(inp["h"], g["ids"], g["w"].astype(np.float64), inp["w_gate"], inp["w_up"], inp["w_down"])
+    check_close(g["y"], ref)
+    layer.close()
+
+
+def test_alignment_randomised_stage_isolated(mb):
+    import torch
+    rng = np.random.default_rng(2024)
+    E, k, b, maxM = 128, 8, 8, 64
+    wl = synth.small_workload("align_only", H=64, I=8, E=E, k=k, M=1, seed=3)
+    inp = synth.layer_inputs(wl, 0)
+    layer = make_layer(mb, wl, inp, maxM)
+    cap = mb.moe_align_capacity(maxM, k, E, b)
+    n = 0
+    for trial in range(120):
+        M = int(rng.integers(1, maxM + 1))
+        kind = trial % 5
+        if kind == 0:
+            ids = np.stack([rng.permutation(E)[:k] for _ in range(M)])
+        elif kind == 1:
+            p = np.ones(E); p[:4] = 60.0
+            ids = np.stack([rng.choice(E, k, replace=False, p=p / p.sum()) for _ in range(M)])
+        elif kind == 2:
+            ids = np.full((M, k), int(rng.integers(E)))
+        elif kind == 3:
+            ids = rng.integers(0, E, size=(M, k))
+        else:
+            ids = rng.integers(-3, E + 3, size=(M, k))
+        dids = torch.from_numpy(ids.astype(np.int32)).cuda()
+        sr = torch.full((cap,), -7, dtype=torch.int32, device="cuda")
+        be = torch.full((cap // b,), -7, dtype=torch.int32, device="cuda")
+        ct = torch.zeros(2, dtype=torch.int32, device="cuda")
+        mb.moe_align_blocks(layer.ctx, dids, M, sr, be, ct)
+        torch.cuda.synchronize()
+        flags = mb.moe_read_device_error(layer.ctx)
+        al = O.align_blocks(ids, E, b)
+        c = ct.cpu().numpy()
+        assert int(c[0]) == al["num_blocks"] and int(c[1]) == al["num_padded"]
+        np.testing.assert_array_equal(sr[: c[1]].cpu().numpy(), al["sorted_routes"])
+        np.testing.assert_array_equal(be[: c[0]].cpu().numpy(), al["block_expert"])
+        assert np.all(sr[c[1]:].cpu().numpy() == -7), "wrote past num_padded"
+        assert (flags == mb.DEVERR_BAD_ROUTE_ID) == (al["invalid_routes"] > 0)
+        n += 1
+    say("  %d randomised routings matched" % n)
+    layer.close()
+
+
+def test_empty_batch_and_max_tokens(mb):
+    import torch
+    wl = synth.small_workload("edge", H=256, I=32, E=16, k=2, M=6, seed=5)
+    inp = synth.layer_inputs(wl, 0)
+    inp["h"] = synth.hidden(wl, 0, 0, M=6)
+    layer = make_layer(mb, wl, inp, 6)
+    h = to_dev(inp["h"])
+    layer.y.fill_(123.0)
+    layer.counts.fill_(99)
+    layer.route(h, 0)
+    layer.align(0)
+    layer.forward(h, 0)
+    torch.cuda.synchronize()
+    assert layer.counts.cpu().tolist() == [0, 0]
+    assert torch.all(layer.y == 123.0)
+    with pytest.raises(mb.MoeError) as ei:
+        layer.route(h, 7)
+    assert ei.value.status == mb.MOE_ERR_CAPACITY
+    g = run_step(mb, layer, inp["h"])     # M == max_tokens
+    ref = O.dense_forward(inp["h"], g["ids"], g["w"].astype(np.float64), inp["w_gate"], inp["w_up"], inp["w_down"])
+    check_close(g["y"], ref)
+    layer.close()
+
+
+def test_bitwise_reproducible_over_repeated_calls(mb):
+    import torch
+    wl = synth.WORKLOADS["aligned_h2048_i768_e128_k8_m21"]
+    say("100 repeated steps, aligned_h2048_i768_e128_k8_m21")
+    inp = synth.layer_inputs(wl, 0)
+    layer = make_layer(mb, wl, inp, wl.M)
+    h = to_dev(inp["h"])
+    first = None
+    for i in range(100):
+        y = layer.step(h, wl.M).clone()
+        outs = (y, layer.ids.clone(), layer.w.clone(), layer.sorted_routes.clone(), layer.counts.clone())
+        if first is None:
+            first = outs
+        else:
+            for a, b in zip(first, outs):
+                assert torch.equal(a.view(torch.int32) if a.dtype == torch.float32 else a,
+                                   b.view(torch.int32) if b.dtype == torch.float32 else b)
+    torch.cuda.synchronize()
+    layer.close()
+
+
+_HISTORY_SCRIPT = r"""
+import hashlib, sys, numpy as np, torch
+sys.path.insert(0, sys.argv[1]); sys.path.insert(0, sys.argv[1] + '/tests')
+import synth, memory_bound_routed_amd as mb
+from helpers import upload_layer, to_dev
+keep = []
+if sys.argv[2] == 'H1':   # allocate and keep extra tensors before building the layer
+    for n in (3, 777, 12345):
+        keep.append(torch.randn(n, device='cuda'))
+    torch.cuda.synchronize()
+wl = synth.WORKLOADS['aligned_h2048_i768_e128_k8_m21']
+inp = synth.layer_inputs(wl, 0)
+cfg = mb.make_config(wl.H, wl.I, wl.E, wl.k, wl.block_b, wl.M)
+layer = mb.Layer(cfg, upload_layer(inp))
+y = layer.step(to_dev(inp['h']), wl.M)
+torch.cuda.synchronize()
+print(hashlib.sha256(y.cpu().numpy().tobytes()).hexdigest())
+"""
+
+
+def test_bitwise_identical_across_process_histories(mb):
+    root = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+    hashes = {}
+    for hist in ("H0", "H1"):
+        say("fresh process, history", hist)
+        r = subprocess.run([sys.executable, "-c", _HISTORY_SCRIPT, root, hist], capture_output=True, text=True,
+                           timeout=300)
+        assert r.returncode == 0, r.stderr[-2000:]
+        hashes[hist] = r.stdout.strip().splitlines()[-1]
+    say("  ", hashes)
+    assert hashes["H0"] == hashes["H1"]
+
+
+def test_device_error_flags_on_invalid_ids(mb):
+    import torch
+    wl = synth.small_workload("bad_ids", H=256, I=16, E=16, k=2, M=3, seed=8)
+    inp = synth.layer_inputs(wl, 0)
+    inp["h"] = synth.hidden(wl, 0, 0, M=3)
+    layer = make_layer(mb, wl, inp, 3)
+    ids = torch.tensor([[1, 99], [-1, 2], [3, 4]], dtype=torch.int32, device="cuda")
+    w = torch.full((3, 2), 0.5, dtype=torch.float32, device="cuda")
+    layer.align(3, ids=ids)
+    h = to_dev(inp["h"])
+    layer.forward(h, 3, ids=ids, w=w)
+    torch.cuda.synchronize()
+    flags = mb.moe_read_device_error(layer.ctx)
+    assert flags & mb.DEVERR_BAD_ROUTE_ID
+    idn = ids.cpu().numpy().astype(np.int64)
+    ref = O.dense_forward(inp["h"], idn, w.cpu().numpy().astype(np.float64), inp["w_gate"], inp["w_up"],
+                          inp["w_down"])
+    check_close(layer.y[:3].cpu().numpy(), ref)
+    assert mb.moe_read_device_error(layer.ctx) == 0  # cleared
+    layer.close()
