@@ -1,0 +1,344 @@
+#!/usr/bin/env python3
+"""Benchmark of the MoE decode step on one MI355X.
+
+    python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload NAME]
+
+A step is one pass of the whole hot path over one token batch:
+moe_route_topk + moe_align_blocks + moe_expert_forward on one layer.  The
+default workload is the Qwen3-30B-A3B-shaped batch-1 layer (H=2048, I=768,
+E=128, top-8): 48 independent layers are resident in HBM and step i runs on
+layer i mod 48, so every step streams its routed weights cold from HBM
+(47 x 75.5 MB are read between two visits of a layer, far beyond the 256 MB
+Infinity Cache).  The steps of one 48-layer cycle are captured in a HIP graph
+(the library never allocates or synchronises inside a call) and the graph is
+replayed; eager (uncaptured) timing is reported beside it.
+
+Printed: one JSON line with the metric, the per-kernel roofline of the
+dominant kernel (durations from HIP events recorded by the library on its
+launch stream) and the fp64 oracle timed on the host cores.
+"""
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import os
+import sys
+import time
+
+import numpy as np
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+METRIC = "µs per MoE layer decode step + routed-weight HBM GB/s (% of 8 TB/s peak)"
+HBM_PEAK_GBS = 8000.0
+LAYERS = 48
+
+
+def routed_bytes_per_step(wl, n_experts: int) -> int:
+    """Routed expert bytes of one step (each distinct expert read once); the
+    VQ format adds its layer-shared basis and code books, read once per step."""
+    shared = 2 * (wl.H * wl.lr_r * 2 + wl.vq_K * wl.vq_d * 2) if wl.vq else 0
+    return n_experts * wl.routed_bytes_per_expert + shared
+
+
+def kernel_algorithmic_bytes(wl, kernel: str, n_experts: int, M: int, K: int = 0) -> int:
+    """Bytes a kernel must move by definition (weights it streams once plus
+    its small activation inputs/outputs)."""
+    H, I = wl.H, wl.I
+    if kernel == "expert_fused":
+        return n_experts * 3 * I * H * 2
+    if kernel == "gateup":
+        return n_experts * 2 * I * H * 2
+    if kernel == "down":
+        return n_experts * I * H * 2
+    if kernel == "gateup_vqlr":
+        return n_experts * 2 * (I * (H // wl.vq_d) + I * wl.lr_r * 2)
+    if kernel == "chan_gather":
+        return K * 3 * H * 2
+    return 0
+
+
+def source_digest(files) -> str:
+    h = hashlib.sha256()
+    for f in files:
+        h.update(open(os.path.join(ROOT, f), "rb").read())
+    return h.hexdigest()[:16]
+
+
+KERNEL_SOURCES = {
+    "expert_fused": ["memory_bound_routed_amd/csrc/dense.hip", "memory_bound_routed_amd/csrc/device_common.h"],
+    "gateup": ["memory_bound_routed_amd/csrc/dense.hip", "memory_bound_routed_amd/csrc/device_common.h"],
+    "down": ["memory_bound_routed_amd/csrc/dense.hip", "memory_bound_routed_amd/csrc/device_common.h"],
+    "gateup_vqlr": ["memory_bound_routed_amd/csrc/vqlr.hip", "memory_bound_routed_amd/csrc/device_common.h"],
+    "chan_gather": ["memory_bound_routed_amd/csrc/chansparse.hip", "memory_bound_routed_amd/csrc/device_common.h"],
+}
+
+
+def measured_traffic(kernel: str, workload: str):
+    """HBM bytes per launch from the committed rocprofv3 FETCH_SIZE/WRITE_SIZE
+    summary, if it was taken on the current kernel source; else None."""
+    path = os.path.join(ROOT, "profiles", "traffic_%s_%s.json" % (kernel, workload))
+    if not os.path.exists(path):
+        return None
+    d = json.load(open(path))
+    if d.get("source_digest") != source_digest(KERNEL_SOURCES[kernel]):
+        return None
+    return d.get("hbm_bytes_per_launch")
+
+
+# ----------------------------------------------------------------------------
+
+def build_layers(wl, n_layers, M, keep=0):
+    """Layer 0 from the seeded host generator, the rest drawn on the device."""
+    import torch
+    import synth
+    import memory_bound_routed_amd as mb
+
+    def dev_bf16(shape, gen):
+        x = torch.empty(shape, dtype=torch.float32, device="cuda")
+        x.normal_(0.0, synth.SIGMA_W, generator=gen)
+        return x.to(torch.bfloat16).view(torch.int16)
+
+    layers = []
+    gen = torch.Generator(device="cuda")
+    gen.manual_seed(wl.seed)
+    for L in range(n_layers):
+        if L == 0:
+            inp = synth.layer_inputs(wl, 0)
+            t = {k: torch.from_numpy(v.view(np.int16) if v.dtype == np.uint16 else v).cuda()
+                 for k, v in inp.items() if v is not None and k != "h"}
+        else:
+            t = {"router_w": dev_bf16((wl.H, wl.E), gen)}
+            if wl.hot_experts:
+                t["router_bias"] = torch.from_numpy(synth.router_bias(wl, L)).cuda()
+            # one allocation per layer for the three expert matrices
+            big = dev_bf16((3, wl.E, wl.I, wl.H), gen) if not wl.vq else None
+            if wl.vq:
+                t["w_down"] = dev_bf16((wl.E, wl.I, wl.H), gen)
+                for P in ("gate", "up"):
+                    t["lr_basis_" + P] = dev_bf16((wl.H, wl.lr_r), gen)
+                    t["lr_coef_" + P] = dev_bf16((wl.E, wl.I, wl.lr_r), gen)
+                    t["vq_book_" + P] = dev_bf16((wl.vq_K, wl.vq_d), gen)
+                    t["vq_idx_" + P] = torch.randint(0, 256, (wl.E, wl.I, wl.H // wl.vq_d), dtype=torch.uint8,
+                                                     device="cuda", generator=gen)
+            else:
+                t["w_gate"], t["w_up"], t["w_down"] = big[0], big[1], big[2]
+        if wl.vq:
+            cfg = mb.make_config(wl.H, wl.I, wl.E, wl.k, wl.block_b, M, mb.MOE_WFORMAT_VQLR, wl.vq_d, wl.vq_K,
+                                 wl.lr_r)
+        else:
+            cfg = mb.make_config(wl.H, wl.I, wl.E, wl.k, wl.block_b, M, max_keep=keep)
+        if keep:
+            norms = torch.empty((wl.E, wl.I), dtype=torch.float32, device="cuda")
+            mb.moe_channel_norms(cfg, t["w_gate"], t["w_up"], t["w_down"], norms)
+            t["chan_norm"] = norms
+        layers.append(mb.Layer(cfg, t))
+    torch.cuda.synchronize()
+    return layers
+
+
+def run_steps(layers, hs, M, keep, order):
+    for i in order:
+        L = layers[i % len(layers)]
+        L.step(hs[i], M, keep=keep)
+
+
+def cpu_baseline(wl, budget_s=15.0, max_steps=40):
+    """The fp64 oracle timed on the host (single BLAS thread) on a bounded
+    sample: steps over the first 4 layers, each layer's routed experts drawn
+    from the seeded generator beforehand (generation is not timed)."""
+    import synth
+    import oracle as O
+    from threadpoolctl import threadpool_limits
+    with threadpool_limits(limits=1):
+        return _cpu_baseline(wl, budget_s, max_steps, synth, O)
+
+
+def _cpu_baseline(wl, budget_s, max_steps, synth, O):
+    keep = wl.keep
+    layers = []
+    for L in range(min(4, wl.layers)):
+        inp = {"h": synth.hidden(wl, L), "router_w": synth.router_weight(wl, L),
+               "router_bias": synth.router_bias(wl, L)}
+        ids, _, _ = O.route_topk(inp["h"], inp["router_w"], wl.k, inp["router_bias"])
+        ex = sorted(set(ids.ravel().tolist()))
+        full = synth.layer_inputs(wl, L, experts=ex)
+        norms = O.channel_norms(full["w_gate"], full["w_up"], full["w_down"], experts=ex) if keep else None
+        layers.append((full, norms, len(ex)))
+    t_total, n, bytes_total = 0.0, 0, 0
+    while n < max_steps and t_total < budget_s:
+        full, norms, nex = layers[n % len(layers)]
+        t0 = time.perf_counter()
+        O.moe_step(full, wl.k, keep=keep, norms=norms)
+        t_total += time.perf_counter() - t0
+        bytes_total += (keep * 3 * wl.H * 2) if keep else routed_bytes_per_step(wl, nex)
+        n += 1
+    return {"value": round(bytes_total / t_total / 1e9, 4), "unit": "GB/s",
+            "us_per_step": round(t_total / n * 1e6, 1), "cores": 1, "kind": "oracle",
+            "sample": "%d steps of %s cycling over %d host-resident layers (only routed experts drawn); "
+                      "fp64 numpy, one BLAS thread" % (n, wl.name, len(layers))}
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=960)
+    ap.add_argument("--warmup", type=int, default=96)
+    ap.add_argument("--workload", default="dense_h2048_i768_e128_k8_m1")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--counter-pass", action="store_true",
+                    help="short run for rocprofv3 --pmc: a 256 MiB elementwise copy (calibration) then 96 steps")
+    args = ap.parse_args()
+
+    if args.gpus != 1:
+        print("bench.py runs on one GPU only: the decode step is measured on a single MI355X "
+              "(multi-GPU sharding is a design note, not built); got --gpus %d" % args.gpus, file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+    import synth
+    import memory_bound_routed_amd as mb
+
+    wl = synth.WORKLOADS[args.workload]
+    M, keep = wl.M, wl.keep
+    n_layers = LAYERS if wl.layers > 1 else 1
+    if wl.layers == 1 and args.workload != "tiny_h256_i128_e16_k2":
+        n_layers = LAYERS  # rotate layers for cold reads on every full-size workload
+    layers = build_layers(wl, n_layers, M, keep)
+
+    n_h = max(n_layers, 48)
+    hs = torch.from_numpy(np.stack([synth.hidden(wl, 0, step=i) for i in range(n_h)])).cuda()
+
+    if args.counter_pass:
+        x = torch.empty(64 * 2 ** 20, dtype=torch.float32, device="cuda").normal_()
+        y = torch.empty_like(x)
+        for _ in range(3):
+            torch.neg(x, out=y)
+        torch.cuda.synchronize()
+        run_steps(layers, hs, M, keep, range(96))
+        torch.cuda.synchronize()
+        print(json.dumps({"counter_pass": True, "copy_bytes": x.numel() * 4, "workload": wl.name}))
+        return
+
+    cycle = list(range(n_h))
+    reps = max(1, round(args.steps / len(cycle)))
+    wreps = max(1, round(args.warmup / len(cycle)))
+    K = reps * len(cycle)
+    W = wreps * len(cycle)
+
+    # distinct routed experts per layer for the byte count: route every layer once (eager)
+    n_ex = []
+    for i in cycle:
+        L = layers[i % n_layers]
+        L.route(hs[i], M)
+        n_ex.append(len(set(L.ids[:M].flatten().tolist())))
+    torch.cuda.synchronize()
+    bytes_per_cycle = sum((keep * 3 * wl.H * 2 * M) if keep else routed_bytes_per_step(wl, n) for n in n_ex)
+
+    # ---- graph-captured steps
+    s = torch.cuda.Stream()
+    s.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(s):
+        run_steps(layers, hs, M, keep, cycle)  # eager warm-up on the capture stream
+    torch.cuda.current_stream().wait_stream(s)
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        run_steps(layers, hs, M, keep, cycle)
+    torch.cuda.synchronize()
+    for _ in range(wreps):
+        g.replay()
+    torch.cuda.synchronize()
+    t0 = torch.cuda.Event(enable_timing=True)
+    t1 = torch.cuda.Event(enable_timing=True)
+    t0.record()
+    for _ in range(reps):
+        g.replay()
+    t1.record()
+    torch.cuda.synchronize()
+    ms_graph = t0.elapsed_time(t1)
+    ms_per_step = ms_graph / K
+
+    # ---- eager steps (no graph)
+    run_steps(layers, hs, M, keep, cycle)
+    torch.cuda.synchronize()
+    e0 = torch.cuda.Event(enable_timing=True)
+    e1 = torch.cuda.Event(enable_timing=True)
+    e0.record()
+    for _ in range(reps):
+        run_steps(layers, hs, M, keep, cycle)
+    e1.record()
+    torch.cuda.synchronize()
+    ms_eager = e0.elapsed_time(e1) / K
+
+    # ---- per-kernel durations: the library attaches a pair of HIP events to
+    # every launch (stamped by the kernel's own dispatch on its stream) while
+    # profiling is enabled; same steps, eager, right after the timed region
+    for L in layers:
+        mb.moe_profile_enable(L.ctx, True)
+    for _ in range(reps):
+        run_steps(layers, hs, M, keep, cycle)
+    torch.cuda.synchronize()
+    kern = {}
+    for L in layers:
+        for name, (ms, n) in mb.moe_profile_read(L.ctx).items():
+            a = kern.setdefault(name, [0.0, 0])
+            a[0] += ms
+            a[1] += n
+        mb.moe_profile_enable(L.ctx, False)
+    kernels = {k: {"avg_us": round(v[0] / v[1] * 1e3, 3), "launches": v[1]} for k, v in kern.items()}
+    dominant = max(kern, key=lambda k: kern[k][0])
+    avg_ex = float(np.mean(n_ex))
+    alg = kernel_algorithmic_bytes(wl, dominant, round(avg_ex), M, keep * M)
+    dur_s = kernels[dominant]["avg_us"] / 1e6
+    achieved = alg / dur_s / 1e9 if alg else None
+    expert_kernels = [k for k in kern if k not in ("router", "align", "router_align")]
+    expert_us = sum(kernels[k]["avg_us"] * kernels[k]["launches"] for k in expert_kernels) / K
+
+    us_step = ms_per_step * 1e3
+    gbs = bytes_per_cycle * reps / (ms_graph / 1e3) / 1e9
+    out = {
+        "metric": METRIC,
+        "value": round(gbs, 2),
+        "unit": "GB/s",
+        "n_gpus": 1,
+        "steps": K,
+        "warmup": W,
+        "ms_per_step": round(ms_per_step, 6),
+        "us_per_step": round(us_step, 3),
+        "pct_of_hbm_peak": round(100 * gbs / HBM_PEAK_GBS, 2),
+        "us_per_step_eager": round(ms_eager * 1e3, 3),
+        "expert_path_us_sum_of_kernels": round(expert_us, 3),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16 weights, fp32 activations and accumulation",
+        "data": "synthetic: layer 0 from the seeded host generator, layers 1..%d drawn on the device; "
+                "N(0,0.02) bf16 weights, N(0,1) fp32 hidden states" % (n_layers - 1),
+        "config": {"workload": wl.name, "H": wl.H, "I": wl.I, "E": wl.E, "top_k": wl.k, "tokens": M,
+                   "block_b": wl.block_b, "layers_rotated": n_layers, "keep_channels": keep or None,
+                   "routed_bytes_per_step": int(bytes_per_cycle / len(cycle)),
+                   "avg_distinct_experts": round(avg_ex, 2), "timing": "HIP graph of one 48-step layer cycle, "
+                   "replayed %d times; HIP events around all replays" % reps},
+        "kernels": kernels,
+        "roofline": {
+            "kernel": dominant,
+            "duration_us": kernels[dominant]["avg_us"],
+            "bound": "hbm",
+            "achieved": round(achieved, 1) if achieved else None,
+            "peak": HBM_PEAK_GBS,
+            "unit": "GB/s",
+            "frac": round(achieved / HBM_PEAK_GBS, 4) if achieved else None,
+            "algorithmic_bytes_per_launch": alg,
+            "traffic": measured_traffic(dominant, wl.name),
+        },
+    }
+    if not args.no_cpu_baseline:
+        out["cpu_baseline"] = cpu_baseline(wl)
+    print(json.dumps(out), flush=True)
+
+
+if __name__ == "__main__":
+    main()

@@ -73,18 +73,21 @@ enum {
 /*
  * Shapes and options of one MoE layer.
  *  H, I, E     hidden size, channels per expert, number of experts.
- *              Supported: H % 8 == 0, 8 <= H <= 16384; 1 <= I <= 16384;
+ *              Supported: H % 8 == 0, 8 <= H <= 8192; 1 <= I <= 16384;
  *              E % 8 == 0, 8 <= E <= 1024.
  *  top_k       experts per token, 1 <= top_k <= min(E, 32).
  *  block_b     alignment block size (8 on the pages); 1 <= block_b <= 64.
  *  max_tokens  largest M any call will pass (sizes the workspace), 1..4096,
- *              with ceil(max_tokens*top_k/64)*E <= 16384.
+ *              with max_tokens*top_k <= 4096 and
+ *              ceil(max_tokens*top_k/64)*E <= 6144 (alignment runs in one
+ *              workgroup's LDS).
  *  wformat     MOE_WFORMAT_DENSE or MOE_WFORMAT_VQLR.
  *  vq_d, vq_K, lr_r   VQ block length, code book size and low-rank rank for
  *              MOE_WFORMAT_VQLR: vq_d == 8, 1 <= vq_K <= 256, H % (8*vq_d)
  *              == 0, lr_r % 8 == 0 and 8 <= lr_r <= 512.  Ignored for dense.
  *  max_keep    largest channel top-K moe_expert_forward will be asked for
- *              (0 = channel-sparse mode unused); <= top_k*I, top_k*I <= 16384.
+ *              (0 = channel-sparse mode unused); <= top_k*I, top_k*I <= 8192,
+ *              dense format only.
  */
 typedef struct {
     int32_t H, I, E, top_k, block_b, max_tokens;
@@ -148,6 +151,11 @@ void moe_destroy(moe_ctx *ctx);
  *             lower expert id, slot s = s-th largest
  *  topk_w     fp32 [M][k] out: softmax over the k selected logits
  *  logits_out fp32 [M][E] out (may be NULL): l = h Wr + bias, fp32 accumulation
+ * Each logit is an fp32 sum whose summation tree has depth at most
+ * 4 + ceil(log2 rpp) + ceil(H / (4 rpp)) + 1 with rpp = floor(2048 / E), so
+ * |l - exact| <= gamma_depth * (sum_i |h_i Wr_ie| + |bias_e|).  The top-k
+ * decision is exact for these fp32 logits.  One launch; the last workgroup
+ * to finish reduces the row slices (an integer ticket, no spinning).
  */
 moe_status moe_route_topk(moe_ctx *ctx, const float *h, int32_t M,
                           int32_t *topk_ids, float *topk_w, float *logits_out, void *stream);
@@ -169,6 +177,15 @@ moe_status moe_route_topk(moe_ctx *ctx, const float *h, int32_t M,
 moe_status moe_align_blocks(moe_ctx *ctx, const int32_t *topk_ids, int32_t M,
                             int32_t *sorted_routes, int32_t *block_expert, int32_t *counts,
                             void *stream);
+
+/*
+ * moe_route_topk followed by moe_align_blocks, in one launch: the last
+ * workgroup of the router aligns the ids it has just written.  Outputs are
+ * identical to the two separate calls (same arguments, same meaning).
+ */
+moe_status moe_route_align(moe_ctx *ctx, const float *h, int32_t M, int32_t *topk_ids, float *topk_w,
+                           float *logits_out, int32_t *sorted_routes, int32_t *block_expert, int32_t *counts,
+                           void *stream);
 
 /*
  * Experts and combine.
@@ -250,24 +267,28 @@ moe_status moe_validate_plan(const int32_t *topk_ids_host, int32_t M, int32_t k,
 
 /* Kernel identifiers for moe_profile_read. */
 enum {
-    MOE_KERNEL_ROUTER_GEMV = 0,  /* router logits (and VQ z = D^T h) partials */
-    MOE_KERNEL_ROUTER_TOPK = 1,
+    MOE_KERNEL_ROUTER = 0,        /* router GEMV + top-k + softmax (one launch) */
+    MOE_KERNEL_VQ_SHARED = 1,     /* shared projection z = D^T h partials (VQ + low rank) */
     MOE_KERNEL_ALIGN = 2,
-    MOE_KERNEL_GATEUP = 3,       /* dense gate/up GEMV + SiLU */
-    MOE_KERNEL_GATEUP_VQLR = 4,  /* VQ + low-rank gate/up + SiLU */
-    MOE_KERNEL_DOWN = 5,         /* down GEMV partials */
-    MOE_KERNEL_COMBINE = 6,      /* fixed-order weighted combine */
-    MOE_KERNEL_CHAN_SELECT = 7,  /* channel top-K */
-    MOE_KERNEL_CHAN_GATHER = 8,  /* kept-channel gate/up + down partials */
+    MOE_KERNEL_GATEUP = 3,        /* dense gate/up GEMV + SiLU (several routes per block) */
+    MOE_KERNEL_GATEUP_VQLR = 4,   /* VQ + low-rank gate/up + SiLU */
+    MOE_KERNEL_DOWN = 5,          /* down GEMV partials */
+    MOE_KERNEL_COMBINE = 6,       /* fixed-order weighted combine */
+    MOE_KERNEL_CHAN_SELECT = 7,   /* channel top-K */
+    MOE_KERNEL_CHAN_GATHER = 8,   /* kept-channel gate/up + down partials */
     MOE_KERNEL_CHAN_COMBINE = 9,
-    MOE_KERNEL_COUNT = 10
+    MOE_KERNEL_EXPERT_FUSED = 10, /* dense gate/up + SiLU + down partials (one route per block) */
+    MOE_KERNEL_ROUTER_ALIGN = 11, /* router + top-k + softmax + alignment (one launch) */
+    MOE_KERNEL_COUNT = 12
 };
 
 /*
- * When enabled, every launch of the context is bracketed by HIP events
- * recorded on the launch's stream.  moe_profile_read synchronises, adds the
- * elapsed times of all recorded launches of each kernel into ms[kernel] and
- * launches[kernel] (host arrays of MOE_KERNEL_COUNT), and clears the record.
+ * When enabled, every launch of the context carries a pair of HIP events
+ * stamped by the kernel's own dispatch (hipExtLaunchKernelGGL), so their
+ * elapsed time is the kernel's execution time on its stream.
+ * moe_profile_read synchronises, adds the elapsed times of all recorded
+ * launches of each kernel into ms[kernel] and launches[kernel] (host arrays
+ * of MOE_KERNEL_COUNT), and clears the record.
  */
 moe_status moe_profile_enable(moe_ctx *ctx, int32_t enable);
 moe_status moe_profile_read(moe_ctx *ctx, double *ms, int64_t *launches);

@@ -26,12 +26,12 @@ _lib = ctypes.CDLL(LIB_PATH)
 MOE_OK, MOE_ERR_INVALID_ARG, MOE_ERR_UNSUPPORTED, MOE_ERR_CAPACITY, MOE_ERR_HIP, MOE_ERR_DEVICE = range(6)
 MOE_WFORMAT_DENSE, MOE_WFORMAT_VQLR = 0, 1
 DEVERR_BAD_ROUTE_ID, DEVERR_BAD_PLAN, DEVERR_BAD_BLOCK_EXPERT, DEVERR_BAD_COUNTS = 1, 2, 4, 8
-KERNELS = ["router_gemv", "router_topk", "align", "gateup", "gateup_vqlr", "down", "combine",
-           "chan_select", "chan_gather", "chan_combine"]
+KERNELS = ["router", "vq_shared", "align", "gateup", "gateup_vqlr", "down", "combine",
+           "chan_select", "chan_gather", "chan_combine", "expert_fused", "router_align"]
 MOE_KERNEL_COUNT = len(KERNELS)
 
 # Every symbol include/moe.h declares (checked by the CPU test suite).
-EXPORTS = ["moe_create", "moe_destroy", "moe_route_topk", "moe_align_blocks", "moe_expert_forward",
+EXPORTS = ["moe_create", "moe_destroy", "moe_route_topk", "moe_route_align", "moe_align_blocks", "moe_expert_forward",
            "moe_align_capacity", "moe_status_string", "moe_read_device_error", "moe_channel_norms",
            "moe_validate_plan", "moe_profile_enable", "moe_profile_read", "moe_kernel_name"]
 
@@ -56,6 +56,7 @@ _sig = {
     "moe_destroy": (None, [_vp]),
     "moe_route_topk": (_i32, [_vp, _vp, _i32, _vp, _vp, _vp, _vp]),
     "moe_align_blocks": (_i32, [_vp, _vp, _i32, _vp, _vp, _vp, _vp]),
+    "moe_route_align": (_i32, [_vp, _vp, _i32, _vp, _vp, _vp, _vp, _vp, _vp, _vp]),
     "moe_expert_forward": (_i32, [_vp, _vp, _i32, _vp, _vp, _vp, _vp, _vp, _i32, _vp, _vp, _vp]),
     "moe_align_capacity": (_i32, [_i32, _i32, _i32, _i32]),
     "moe_status_string": (ctypes.c_char_p, [_i32]),
@@ -157,6 +158,11 @@ def moe_route_topk(ctx, h, M, topk_ids, topk_w, logits_out=None, stream=None) ->
            "moe_route_topk")
 
 
+def moe_route_align(ctx, h, M, topk_ids, topk_w, logits_out, sorted_routes, block_expert, counts, stream=None) -> None:
+    _check(_lib.moe_route_align(ctx, _ptr(h), M, _ptr(topk_ids), _ptr(topk_w), _ptr(logits_out), _ptr(sorted_routes),
+                                _ptr(block_expert), _ptr(counts), _stream(stream)), "moe_route_align")
+
+
 def moe_align_blocks(ctx, topk_ids, M, sorted_routes, block_expert, counts, stream=None) -> None:
     _check(_lib.moe_align_blocks(ctx, _ptr(topk_ids), M, _ptr(sorted_routes), _ptr(block_expert), _ptr(counts),
                                  _stream(stream)), "moe_align_blocks")
@@ -249,9 +255,19 @@ class Layer:
         moe_expert_forward(self.ctx, h, M, self.ids if ids is None else ids, self.w if w is None else w,
                            sr, be, ct, keep, self.kept if keep else None, self.y if y is None else y, stream)
 
-    def step(self, h, M, keep=0, stream=None):
-        self.route(h, M, stream=stream)
-        if not keep:
+    def route_align(self, h, M, logits=False, stream=None):
+        moe_route_align(self.ctx, h, M, self.ids, self.w, self.logits if logits else None, self.sorted_routes,
+                        self.block_expert, self.counts, stream)
+
+    def step(self, h, M, keep=0, stream=None, fused_route_align=True):
+        """One decode step: routing, alignment (not needed by the channel-sparse
+        mode) and the experts."""
+        if keep:
+            self.route(h, M, stream=stream)
+        elif fused_route_align:
+            self.route_align(h, M, stream=stream)
+        else:
+            self.route(h, M, stream=stream)
             self.align(M, stream=stream)
         self.forward(h, M, keep=keep, stream=stream)
         return self.y[:M]

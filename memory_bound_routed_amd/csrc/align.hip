@@ -3,12 +3,9 @@
 // blocks, Sec. 3.1 Eq. 1 route-block membership, Sec. 5.3 stable (expert id,
 // route id) construction).
 //
-// One workgroup.  The placement of a route is computed, not raced for:
-//   pos(r) = off[e] + (# routes of e in earlier 64-route chunks)
-//                   + (# lanes below r in r's chunk with the same expert),
-// with e = id(r) and off[] the exclusive prefix of the padded counts.  The
-// per-chunk counts use LDS integer atomics, whose result does not depend on
-// their order, so the output is a pure function of the ids.
+// One workgroup; the body (align_workgroup) is shared with the router's last
+// workgroup and documented in align_device.h.
+#include "align_device.h"
 #include "device_common.h"
 #include "launch.h"
 
@@ -16,100 +13,20 @@ namespace moe {
 
 namespace {
 
-constexpr int kAlignThreads = 256;
-
 __global__ void __launch_bounds__(kAlignThreads)
 align_kernel(const int32_t* __restrict__ topk_ids, int R, int E, int b, int32_t* __restrict__ sorted_routes,
              int32_t* __restrict__ block_expert, int32_t* __restrict__ counts, int32_t* __restrict__ err) {
     extern __shared__ int smem[];
-    const int nchunk = (R + MOE_WAVE - 1) / MOE_WAVE;
-    int* sid = smem;                 // [R]  expert of each route, -1 if invalid
-    int* srank = sid + R;            // [R]  rank inside its chunk among same-expert routes
-    int* cnt = srank + R;            // [nchunk][E]  counts, then exclusive prefix over chunks
-    int* tot = cnt + nchunk * E;     // [E]
-    int* off = tot + E;              // [E + 1]
-    __shared__ int bad;
-    const int tid = threadIdx.x;
-    const int wave = tid / MOE_WAVE;
-    const int lane = tid % MOE_WAVE;
-
-    for (int i = tid; i < nchunk * E; i += kAlignThreads) cnt[i] = 0;
-    if (tid == 0) bad = 0;
-    __syncthreads();
-    for (int r = tid; r < R; r += kAlignThreads) {
-        const int id = topk_ids[r];
-        const bool ok = id >= 0 && id < E;
-        sid[r] = ok ? id : -1;
-        if (!ok) bad = 1;
-    }
-    __syncthreads();
-    if (tid == 0 && bad) atomicOr(err, DEVERR_BAD_ROUTE_ID);
-
-    for (int c = wave; c < nchunk; c += kAlignThreads / MOE_WAVE) {
-        const int r = c * MOE_WAVE + lane;
-        const int id = r < R ? sid[r] : -1;
-        int rank = 0;
-        for (int l2 = 0; l2 < MOE_WAVE; ++l2) {
-            const int o = __shfl(id, l2, MOE_WAVE);
-            rank += (l2 < lane && o == id) ? 1 : 0;
-        }
-        if (r < R) srank[r] = rank;
-        if (id >= 0) atomicAdd(&cnt[c * E + id], 1);
-    }
-    __syncthreads();
-    for (int e = tid; e < E; e += kAlignThreads) {
-        int run = 0;
-        for (int c = 0; c < nchunk; ++c) {
-            const int x = cnt[c * E + e];
-            cnt[c * E + e] = run;
-            run += x;
-        }
-        tot[e] = run;
-    }
-    __syncthreads();
-    if (wave == 0) {  // exclusive scan of the padded counts, 64 experts at a time
-        int carry = 0;
-        for (int e0 = 0; e0 < E; e0 += MOE_WAVE) {
-            const int e = e0 + lane;
-            const int pc = e < E ? ((tot[e] + b - 1) / b) * b : 0;
-            int x = pc;
-#pragma unroll
-            for (int d = 1; d < MOE_WAVE; d <<= 1) {
-                const int y = __shfl_up(x, d, MOE_WAVE);
-                if (lane >= d) x += y;
-            }
-            if (e < E) off[e] = carry + x - pc;
-            carry += __shfl(x, MOE_WAVE - 1, MOE_WAVE);
-        }
-        if (lane == 0) off[E] = carry;
-    }
-    __syncthreads();
-    for (int r = tid; r < R; r += kAlignThreads) {
-        const int id = sid[r];
-        if (id >= 0) sorted_routes[off[id] + cnt[(r / MOE_WAVE) * E + id] + srank[r]] = r;
-    }
-    for (int e = tid; e < E; e += kAlignThreads) {
-        const int o = off[e];
-        const int padded = off[e + 1] - o;
-        for (int q = tot[e]; q < padded; ++q) sorted_routes[o + q] = R;
-        for (int j = 0; j < padded / b; ++j) block_expert[o / b + j] = e;
-    }
-    if (tid == 0) {
-        counts[0] = off[E] / b;
-        counts[1] = off[E];
-    }
+    align_workgroup(topk_ids, R, E, b, sorted_routes, block_expert, counts, err, smem);
 }
 
 }  // namespace
 
-size_t align_lds_bytes(int R, int E) {
-    const int nchunk = (R + MOE_WAVE - 1) / MOE_WAVE;
-    return sizeof(int) * ((size_t)2 * R + (size_t)nchunk * E + 2 * (size_t)E + 1);
-}
+size_t align_lds_bytes(int R, int E) { return align_lds_bytes_inline(R, E); }
 
 hipError_t launch_align(const int32_t* topk_ids, int R, int E, int b, int32_t* sorted_routes,
                         int32_t* block_expert, int32_t* counts, int32_t* err, hipStream_t stream) {
-    hipLaunchKernelGGL(align_kernel, dim3(1), dim3(kAlignThreads), align_lds_bytes(R, E), stream, topk_ids, R, E, b,
+    MOE_LAUNCH(align_kernel, dim3(1), dim3(kAlignThreads), align_lds_bytes(R, E), stream, topk_ids, R, E, b,
                        sorted_routes, block_expert, counts, err);
     return hipGetLastError();
 }

@@ -337,13 +337,13 @@ hipError_t gather_q(const int32_t* topk_ids, const float* topk_w, const int32_t*
     const dim3 grid((K + KC - 1) / KC, M);
     const int CQ = (H + 2047) / 2048;
     if (CQ <= 1)
-        hipLaunchKernelGGL((chan_gather_kernel<Q, 1>), grid, dim3(kThreads), 0, stream, topk_ids, topk_w, kept, k, I,
+        MOE_LAUNCH((chan_gather_kernel<Q, 1>), grid, dim3(kThreads), 0, stream, topk_ids, topk_w, kept, k, I,
                            E, H, K, h, Wg, Wu, Wd, part);
     else if (CQ <= 2)
-        hipLaunchKernelGGL((chan_gather_kernel<Q, 2>), grid, dim3(kThreads), 0, stream, topk_ids, topk_w, kept, k, I,
+        MOE_LAUNCH((chan_gather_kernel<Q, 2>), grid, dim3(kThreads), 0, stream, topk_ids, topk_w, kept, k, I,
                            E, H, K, h, Wg, Wu, Wd, part);
     else if (CQ <= 4)
-        hipLaunchKernelGGL((chan_gather_kernel<Q, 4>), grid, dim3(kThreads), 0, stream, topk_ids, topk_w, kept, k, I,
+        MOE_LAUNCH((chan_gather_kernel<Q, 4>), grid, dim3(kThreads), 0, stream, topk_ids, topk_w, kept, k, I,
                            E, H, K, h, Wg, Wu, Wd, part);
     else
         return hipErrorInvalidValue;
@@ -356,7 +356,7 @@ size_t chan_select_lds_bytes(int n) { return (size_t)n * (sizeof(float) + 2); }
 
 hipError_t launch_chan_select(const int32_t* topk_ids, const float* topk_w, const float* norms, int M, int k, int I,
                               int E, int K, int32_t* kept, hipStream_t stream) {
-    hipLaunchKernelGGL(chan_select_kernel, dim3(M), dim3(kThreads), chan_select_lds_bytes(k * I), stream, topk_ids,
+    MOE_LAUNCH(chan_select_kernel, dim3(M), dim3(kThreads), chan_select_lds_bytes(k * I), stream, topk_ids,
                        topk_w, norms, k, I, E, K, kept);
     return hipGetLastError();
 }
@@ -376,14 +376,14 @@ hipError_t launch_chan_gather(const int32_t* topk_ids, const float* topk_w, cons
 
 hipError_t launch_chan_combine(int M, int H, int nchunks, const float* part, float* y, hipStream_t stream) {
     const dim3 grid((H / 4 + kThreads - 1) / kThreads, M);
-    hipLaunchKernelGGL(chan_combine_kernel, grid, dim3(kThreads), 0, stream, H, nchunks, part, y);
+    MOE_LAUNCH(chan_combine_kernel, grid, dim3(kThreads), 0, stream, H, nchunks, part, y);
     return hipGetLastError();
 }
 
 hipError_t launch_channel_norms(int E, int I, int H, const uint16_t* Wg, const uint16_t* Wu, const uint16_t* Wd,
                                 float* norms, hipStream_t stream) {
     const int EI = E * I;
-    hipLaunchKernelGGL(channel_norms_kernel, dim3((EI + kWaves - 1) / kWaves), dim3(kThreads), 0, stream, EI, H, Wg,
+    MOE_LAUNCH(channel_norms_kernel, dim3((EI + kWaves - 1) / kWaves), dim3(kThreads), 0, stream, EI, H, Wg,
                        Wu, Wd, norms);
     return hipGetLastError();
 }

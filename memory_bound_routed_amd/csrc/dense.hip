@@ -1,18 +1,34 @@
-// Dense bf16 experts: fused gate/up GEMV with SiLU(gate)*up kept in
-// registers, down GEMV row-chunk partials, and the fixed-order weighted
-// combine (page "A Multi-Engine Dataflow for MoE Decoding on Scratchpad-Based
-// Tensor Accelerators", MoE-block background and Sec. 4.3; page "Channel
-// Selection for Mixture-of-Experts Decoding Needs No Calibration Data",
-// Background: the channel view of the same computation).
+// Dense bf16 experts: gate/up GEMV with SiLU(gate)*up kept in registers, the
+// down GEMV and the fixed-order weighted combine (page "A Multi-Engine
+// Dataflow for MoE Decoding on Scratchpad-Based Tensor Accelerators",
+// MoE-block background and Sec. 4.3; page "Channel Selection for
+// Mixture-of-Experts Decoding Needs No Calibration Data", Background: the
+// channel view of the same computation).
 //
-// Work is expert-major: the workgroups of an alignment block that starts an
+// Work is expert-major: the workgroups of the alignment block that starts an
 // expert's run of blocks walk every block of that run, so each routed
 // expert's weights are streamed from HBM once per step whatever its number of
-// routes.  The weights of a workgroup's channel chunk are loaded into
-// registers first (all loads in flight at once) and reused for every route.
-// The arithmetic of one route never depends on its position in the plan or on
-// the grid: per lane the hidden dimension is walked in ascending order, lanes
-// are summed by a fixed butterfly, and results are stored by route id.
+// routes.  Weights a workgroup needs are requested before anything else and
+// kept in registers for every route that uses them.
+//
+// The arithmetic of one route never depends on its position in the plan or
+// on the grid: per lane the hidden dimension is walked in ascending order,
+// lanes are added by a fixed butterfly, channel chunks have a size fixed by
+// the shape, and every result is stored by route id.  The combine adds the
+// partials of a token in a fixed order, so y is bitwise reproducible.
+//
+// Two schedules:
+//  * fused (one route per block row, the batch-1 case): a workgroup owns a
+//    chunk of CH channels of one expert.  It issues the loads of the CH gate
+//    rows, CH up rows and CH down rows at once, so the down weights stream
+//    while gate/up is still being reduced (the GPU form of issuing the down
+//    transfers during gate/up compute), then writes a down partial
+//    part[route][chunk][:] = sum_{j in chunk} (a_route * p_j) * d_j.
+//  * split (several routes per block): the gate/up kernel writes p, then a
+//    down kernel over 64-row chunks writes the same kind of partial.
+// Both feed combine_kernel: y[t] = sum over the token's routes and chunks.
+#include <type_traits>
+
 #include "device_common.h"
 #include "launch.h"
 
@@ -55,9 +71,244 @@ __device__ __forceinline__ int plan_route(const PlanArgs& plan, int bb, int q, i
     return r;
 }
 
-// Gate/up + SiLU.  Grid (plan blocks, ceil(I / (4*CPW))); wave w of
-// workgroup (blk, cy) owns channels (cy*4 + w)*CPW + c.  Lane l covers hidden
-// columns 8*(l + 64*q), q < Q (one 16-byte load per row and q).
+// ---------------------------------------------------------------------------
+// Fused schedule.  Grid (plan blocks, ceil(I / (NCH*CH))).  A workgroup owns
+// NCH consecutive chunks of CH = NW*CPW channels of one expert and walks
+// them with the weights of chunk i+1 requested before chunk i is computed
+// (double buffering in registers), so its arithmetic overlaps the stream
+// instead of piling up after it.  Per chunk, wave w computes gate/up of
+// CPW channels (lane l covers hidden columns 8*(l + 64*q)) from h held in
+// LDS; thread t multiplies its row group's down rows at hidden columns
+// 8*(t%256 + 256*cq) and accumulates across the chunks; the row groups are
+// added in group order at the end and the workgroup writes one partial
+//     part[route][range][:] = sum_{j in range} (a_route * p_j) * d_j.
+// Every load whose address depends on data (plan rows, route ids, affinity,
+// h) is issued before the weight stream: a load queued behind it would wait
+// for the whole stream to drain.
+template <int Q, int CQ, int NW, int CPW, int NCH, bool FULL>
+__global__ void __launch_bounds__(NW * MOE_WAVE)
+expert_fused_kernel(PlanArgs plan, const float* __restrict__ h, const float* __restrict__ topk_w, int H, int I,
+                    const uint16_t* __restrict__ Wg, const uint16_t* __restrict__ Wu,
+                    const uint16_t* __restrict__ Wd, float* __restrict__ part, int nrange,
+                    int32_t* __restrict__ err) {
+    constexpr int NT = NW * MOE_WAVE;     // threads
+    constexpr int CH = NW * CPW;          // channels per chunk
+    constexpr int RG = NT / kThreads;     // down row groups (256 column threads each)
+    constexpr int RPG = CH / RG;          // down rows per row group and chunk
+    static_assert(NT % kThreads == 0 && CH % RG == 0, "tile");
+    __shared__ float sp[CH];
+    __shared__ float4 hs[Q * MOE_WAVE * 2];
+    __shared__ float4 red[RG > 1 ? (RG - 1) * kThreads * CQ * 2 : 1];
+    const int blk = blockIdx.x;
+    const int range = blockIdx.y;
+    const int b = plan.b;
+    const int tid = threadIdx.x;
+    const int wave = tid / MOE_WAVE;
+    const int lane = tid % MOE_WAVE;
+    const int ct = tid % kThreads;        // down column thread
+    const int rgp = tid / kThreads;       // down row group
+
+    // One round of independent loads: counts, this and the previous block's
+    // expert, and the block's rows (lane q holds row q; b <= 64).
+    int nb = plan.counts[0];
+    const int e = plan.block_expert[blk];
+    const int eprev = blk > 0 ? plan.block_expert[blk - 1] : -1;
+    int rv = lane < b ? plan.sorted_routes[(size_t)blk * b + lane] : plan.R;
+    if (nb < 0 || nb > plan.max_blocks) {
+        if (blk == 0 && range == 0 && tid == 0) atomicOr(err, DEVERR_BAD_COUNTS);
+        nb = nb < 0 ? 0 : plan.max_blocks;
+    }
+    if (blk >= nb) return;
+    if (e < 0 || e >= plan.E) {
+        if (range == 0 && tid == 0) atomicOr(err, DEVERR_BAD_BLOCK_EXPERT);
+        return;
+    }
+    if (eprev == e) return;  // not the first block of the expert's run (uniform)
+    // Second round: each row's route id check and affinity.
+    float av = 0.f;
+    {
+        const bool ok = rv >= 0 && rv < plan.R && plan.topk_ids[rv] == e;
+        if (ok) av = topk_w[rv];
+        if (!ok && rv != plan.R && range == 0 && tid < MOE_WAVE) atomicOr(err, DEVERR_BAD_PLAN);
+        if (!ok) rv = -1;
+    }
+    uint64_t todo = __ballot(rv >= 0);  // valid rows of the first block (wave-uniform)
+
+    const int cbase = range * NCH * CH;
+    const size_t ebase = (size_t)e * I * H;
+    const uint16_t* gbase = Wg + ebase + lane * 8;
+    const uint16_t* ubase = Wu + ebase + lane * 8;
+    const uint16_t* dbase = Wd + ebase + ct * 8;
+    uint4 wg[2][CPW][Q], wu[2][CPW][Q], wd[2][RPG][CQ];
+    // Rows past I load row 0 of the expert and are multiplied by zero; with
+    // FULL (H == 512*Q == 2048*CQ) every column is in range and the loads
+    // share one base address with constant offsets.
+    auto issue = [&](int ci, int buf) {
+        const int j0 = cbase + ci * CH;
+#pragma unroll
+        for (int c = 0; c < CPW; ++c) {
+            const int j = j0 + wave * CPW + c;
+            const size_t row = (size_t)(j < I ? j : 0) * H;
+#pragma unroll
+            for (int q = 0; q < Q; ++q) {
+                if (FULL || (lane + MOE_WAVE * q) * 8 < H) {
+                    wg[buf][c][q] = load_stream16(gbase + row + MOE_WAVE * 8 * q);
+                    wu[buf][c][q] = load_stream16(ubase + row + MOE_WAVE * 8 * q);
+                } else {
+                    wg[buf][c][q] = wu[buf][c][q] = make_uint4(0, 0, 0, 0);
+                }
+            }
+        }
+#pragma unroll
+        for (int rr = 0; rr < RPG; ++rr) {
+            const int j = j0 + rgp * RPG + rr;
+            const size_t row = (size_t)(j < I ? j : 0) * H;
+#pragma unroll
+            for (int cq = 0; cq < CQ; ++cq) {
+                if (FULL || (ct + kThreads * cq) * 8 < H)
+                    wd[buf][rr][cq] = load_stream16(dbase + row + kThreads * 8 * cq);
+                else
+                    wd[buf][rr][cq] = make_uint4(0, 0, 0, 0);
+            }
+        }
+    };
+
+    // One route: h to LDS, the chunk loop, the row-group sum and the store.
+    // PIPE double-buffers the weights; the single-buffered copy serves the
+    // rare extra routes (an expert routed more than once by one token), so
+    // that the common single-route path keeps its small register footprint.
+    auto run_route = [&](int r, float a, auto pipe) {
+        constexpr bool PIPE = decltype(pipe)::value;
+        // h of the route into LDS, requested before the weights
+        const float* hr = h + (size_t)(r / plan.k) * H;
+        for (int i = tid; i < Q * MOE_WAVE * 2; i += NT) {
+            const int col = i * 4;
+            hs[i] = col < H ? *reinterpret_cast<const float4*>(hr + col) : make_float4(0.f, 0.f, 0.f, 0.f);
+        }
+        float acc[CQ][8];
+#pragma unroll
+        for (int cq = 0; cq < CQ; ++cq)
+#pragma unroll
+            for (int x = 0; x < 8; ++x) acc[cq][x] = 0.f;
+        if (PIPE) issue(0, 0);
+        __syncthreads();  // hs ready
+#pragma unroll
+        for (int ci = 0; ci < NCH; ++ci) {
+            const int buf = PIPE ? (ci & 1) : 0;
+            if (PIPE) {
+                if (ci + 1 < NCH) issue(ci + 1, buf ^ 1);
+            } else {
+                issue(ci, 0);
+            }
+            const int j0 = cbase + ci * CH;
+            float ag[CPW], au[CPW];
+#pragma unroll
+            for (int c = 0; c < CPW; ++c) ag[c] = au[c] = 0.f;
+#pragma unroll
+            for (int q = 0; q < Q; ++q) {
+                if (!FULL && (lane + MOE_WAVE * q) * 8 >= H) continue;
+                const float4 h0 = hs[(lane + MOE_WAVE * q) * 2];
+                const float4 h1 = hs[(lane + MOE_WAVE * q) * 2 + 1];
+                const float hv[8] = {h0.x, h0.y, h0.z, h0.w, h1.x, h1.y, h1.z, h1.w};
+#pragma unroll
+                for (int c = 0; c < CPW; ++c) {
+                    float gf[8], uf[8];
+                    unpack8(wg[buf][c][q], gf);
+                    unpack8(wu[buf][c][q], uf);
+#pragma unroll
+                    for (int x = 0; x < 8; ++x) {
+                        ag[c] = fmaf(gf[x], hv[x], ag[c]);
+                        au[c] = fmaf(uf[x], hv[x], au[c]);
+                    }
+                }
+            }
+#pragma unroll
+            for (int c = 0; c < CPW; ++c) {
+                const float g = wave_sum(ag[c]);
+                const float u = wave_sum(au[c]);
+                const int j = j0 + wave * CPW + c;
+                if (lane == 0) sp[wave * CPW + c] = j < I ? a * silu_mul(g, u) : 0.f;
+            }
+            __syncthreads();
+#pragma unroll
+            for (int cq = 0; cq < CQ; ++cq)
+#pragma unroll
+                for (int rr = 0; rr < RPG; ++rr) {
+                    float wf[8];
+                    unpack8(wd[buf][rr][cq], wf);
+                    const float s = sp[rgp * RPG + rr];
+#pragma unroll
+                    for (int x = 0; x < 8; ++x) acc[cq][x] = fmaf(s, wf[x], acc[cq][x]);
+                }
+            __syncthreads();
+        }
+        if (RG > 1) {  // row groups 1.. hand their sums to row group 0, added in group order
+            if (rgp > 0) {
+#pragma unroll
+                for (int cq = 0; cq < CQ; ++cq) {
+                    float4* o = red + (((size_t)(rgp - 1) * kThreads + ct) * CQ + cq) * 2;
+                    o[0] = make_float4(acc[cq][0], acc[cq][1], acc[cq][2], acc[cq][3]);
+                    o[1] = make_float4(acc[cq][4], acc[cq][5], acc[cq][6], acc[cq][7]);
+                }
+            }
+            __syncthreads();
+            if (rgp == 0) {
+#pragma unroll
+                for (int g2 = 1; g2 < RG; ++g2)
+#pragma unroll
+                    for (int cq = 0; cq < CQ; ++cq) {
+                        const float4* o = red + (((size_t)(g2 - 1) * kThreads + ct) * CQ + cq) * 2;
+                        const float4 u0 = o[0], u1 = o[1];
+                        acc[cq][0] += u0.x; acc[cq][1] += u0.y; acc[cq][2] += u0.z; acc[cq][3] += u0.w;
+                        acc[cq][4] += u1.x; acc[cq][5] += u1.y; acc[cq][6] += u1.z; acc[cq][7] += u1.w;
+                    }
+            }
+        }
+        if (rgp == 0) {
+#pragma unroll
+            for (int cq = 0; cq < CQ; ++cq) {
+                const int col = (ct + kThreads * cq) * 8;
+                if (col >= H) continue;
+                float* dst = part + ((size_t)r * nrange + range) * H + col;
+                *reinterpret_cast<float4*>(dst) = make_float4(acc[cq][0], acc[cq][1], acc[cq][2], acc[cq][3]);
+                *reinterpret_cast<float4*>(dst + 4) = make_float4(acc[cq][4], acc[cq][5], acc[cq][6], acc[cq][7]);
+            }
+        }
+        __syncthreads();  // red and hs are reused by the next route
+    };
+
+    if (todo) {  // the first valid row of the block (every valid block has one)
+        const int q = __builtin_ctzll(todo);
+        todo &= todo - 1;
+        run_route(__builtin_amdgcn_readlane(rv, q),
+                  __int_as_float(__builtin_amdgcn_readlane(__float_as_int(av), q)), std::integral_constant<bool, true>{});
+    }
+    int bb = blk + 1, q0 = 0;
+    for (;;) {
+        // Further routes: the remaining valid rows of the first block, then
+        // the following blocks of the run, resolved row by row.
+        int r;
+        float a;
+        if (todo) {
+            const int q = __builtin_ctzll(todo);
+            todo &= todo - 1;
+            r = __builtin_amdgcn_readlane(rv, q);
+            a = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(av), q));
+        } else {
+            if (bb >= nb || plan.block_expert[bb] != e) break;
+            r = plan_route(plan, bb, q0, e, err);
+            a = r >= 0 ? topk_w[r] : 0.f;
+            if (++q0 == b) { ++bb; q0 = 0; }
+            if (r < 0) continue;  // uniform
+        }
+        run_route(r, a, std::integral_constant<bool, false>{});
+    }
+}
+
+// ---------------------------------------------------------------------------
+// Split schedule, gate/up.  Grid (plan blocks, ceil(I / (4*CPW))); wave w of
+// workgroup (blk, cy) owns channels (cy*4 + w)*CPW + c; RT plan rows are
+// processed together against the weights held in registers.
 template <int Q, int CPW, int RT>
 __global__ void __launch_bounds__(kThreads)
 gateup_dense_kernel(PlanArgs plan, const float* __restrict__ h, int H, int I, const uint16_t* __restrict__ Wg,
@@ -146,34 +397,28 @@ gateup_dense_kernel(PlanArgs plan, const float* __restrict__ h, int H, int I, co
     }
 }
 
-// Down GEMV partials.  Grid (plan blocks, ceil(I / RC)); workgroup (blk, rc)
-// multiplies rows rc*RC .. rc*RC+RC-1 of W_down,e by the matching p values of
-// each route of the run; thread t covers hidden columns 8*(t + 256*cq).  The
-// RC rows are added in ascending order into
-// part[route][rc][col] = sum_{j in chunk} p[route][j] * Wd[e][j][col].
-template <int CQ, int RC, int RT>
+// Split schedule, down.  Grid (plan blocks, ceil(I / kDownRows)).  Workgroup
+// (blk, rc) handles rows rc*kDownRows ... of W_down,e for the RT routes of
+// each row group of the run: the scaled intermediates a_route * p[route][j]
+// are staged in LDS, the rows are streamed in sub-chunks of kDownSub, and
+// thread t accumulates hidden columns 8*(t + 256*cq) in row order.
+constexpr int kDownRows = 64;
+constexpr int kDownSub = 16;
+
+template <int CQ, int RT>
 __global__ void __launch_bounds__(kThreads)
-down_kernel(PlanArgs plan, int H, int I, int nrc, const uint16_t* __restrict__ Wd, const float* __restrict__ p,
-            float* __restrict__ part, int32_t* __restrict__ err) {
+down_kernel(PlanArgs plan, int H, int I, int nchunk, const uint16_t* __restrict__ Wd, const float* __restrict__ p,
+            const float* __restrict__ topk_w, float* __restrict__ part, int32_t* __restrict__ err) {
+    __shared__ float sp[RT][kDownRows];
     const int blk = blockIdx.x;
     const int rc = blockIdx.y;
     int nb;
     const int e = run_expert(plan, blk, &nb, err);
-    if (e < 0) return;
+    if (e < 0) return;  // uniform
     const int tid = threadIdx.x;
-    const int j0 = rc * RC;
-
-    uint4 w[RC][CQ];
-#pragma unroll
-    for (int jr = 0; jr < RC; ++jr) {
-        const int j = min(j0 + jr, I - 1);
-        const uint16_t* row = Wd + ((size_t)e * I + j) * H;
-#pragma unroll
-        for (int cq = 0; cq < CQ; ++cq) {
-            const int col = (tid + kThreads * cq) * 8;
-            w[jr][cq] = (col < H && j0 + jr < I) ? load_stream16(row + col) : make_uint4(0, 0, 0, 0);
-        }
-    }
+    const int j0 = rc * kDownRows;
+    const int nrows = min(kDownRows, I - j0);
+    const uint16_t* base = Wd + ((size_t)e * I + j0) * H;
 
     for (int bb = blk; bb < nb; ++bb) {
         if (bb > blk && plan.block_expert[bb] != e) break;
@@ -185,13 +430,17 @@ down_kernel(PlanArgs plan, int H, int I, int nrc, const uint16_t* __restrict__ W
                 rt[i] = plan_route(plan, bb, q0 + i, e, err);
                 any |= rt[i] >= 0;
             }
-            if (!any) continue;
-            float pv[RT][RC];
+            if (!any) continue;  // uniform
+            __syncthreads();     // sp of the previous group is no longer read
+            for (int idx = tid; idx < RT * kDownRows; idx += kThreads) {
+                const int i = idx / kDownRows, jr = idx % kDownRows;
+                float v = 0.f;
 #pragma unroll
-            for (int i = 0; i < RT; ++i)
-#pragma unroll
-                for (int jr = 0; jr < RC; ++jr)
-                    pv[i][jr] = (rt[i] >= 0 && j0 + jr < I) ? p[(size_t)rt[i] * I + j0 + jr] : 0.f;
+                for (int ii = 0; ii < RT; ++ii)
+                    if (ii == i && rt[ii] >= 0 && jr < nrows) v = topk_w[rt[ii]] * p[(size_t)rt[ii] * I + j0 + jr];
+                sp[i][jr] = v;
+            }
+            __syncthreads();
 #pragma unroll
             for (int cq = 0; cq < CQ; ++cq) {
                 const int col = (tid + kThreads * cq) * 8;
@@ -201,19 +450,28 @@ down_kernel(PlanArgs plan, int H, int I, int nrc, const uint16_t* __restrict__ W
                 for (int i = 0; i < RT; ++i)
 #pragma unroll
                     for (int x = 0; x < 8; ++x) acc[i][x] = 0.f;
+                for (int js = 0; js < nrows; js += kDownSub) {
+                    uint4 w[kDownSub];
 #pragma unroll
-                for (int jr = 0; jr < RC; ++jr) {
-                    float wf[8];
-                    unpack8(w[jr][cq], wf);
+                    for (int jr = 0; jr < kDownSub; ++jr)
+                        w[jr] = (js + jr < nrows) ? load_stream16(base + (size_t)(js + jr) * H + col)
+                                                  : make_uint4(0, 0, 0, 0);
 #pragma unroll
-                    for (int i = 0; i < RT; ++i)
+                    for (int jr = 0; jr < kDownSub; ++jr) {
+                        float wf[8];
+                        unpack8(w[jr], wf);
 #pragma unroll
-                        for (int x = 0; x < 8; ++x) acc[i][x] = fmaf(pv[i][jr], wf[x], acc[i][x]);
+                        for (int i = 0; i < RT; ++i) {
+                            const float s = sp[i][js + jr];
+#pragma unroll
+                            for (int x = 0; x < 8; ++x) acc[i][x] = fmaf(s, wf[x], acc[i][x]);
+                        }
+                    }
                 }
 #pragma unroll
                 for (int i = 0; i < RT; ++i) {
                     if (rt[i] < 0) continue;
-                    float* dst = part + ((size_t)rt[i] * nrc + rc) * H + col;
+                    float* dst = part + ((size_t)rt[i] * nchunk + rc) * H + col;
                     *reinterpret_cast<float4*>(dst) = make_float4(acc[i][0], acc[i][1], acc[i][2], acc[i][3]);
                     *reinterpret_cast<float4*>(dst + 4) = make_float4(acc[i][4], acc[i][5], acc[i][6], acc[i][7]);
                 }
@@ -222,32 +480,62 @@ down_kernel(PlanArgs plan, int H, int I, int nrc, const uint16_t* __restrict__ W
     }
 }
 
-// y[t][col] = sum_{s=0..k-1} w[t][s] * (sum_{c=0..nchunks-1} part[t*k+s][c][col]),
-// slots in order, chunks in order; routes with an id outside [0, E) add nothing.
+// ---------------------------------------------------------------------------
+// y[t][col] = sum over the valid routes s of token t and the chunks c of
+// part[t*k+s][c][col].  Workgroup (column block, t): kCombCG float4 column
+// groups x kCombRG row groups; row group g adds rows g, g+kCombRG, ...
+// (row = s*nchunk + c) in order -- their loads are issued together -- then
+// the row groups are added pairwise in LDS.  Routes with an id outside
+// [0, E) have no partial and add nothing.
+constexpr int kCombRG = 64;
+constexpr int kCombCG = kThreads / kCombRG;
+constexpr int kCombBatch = 8;
+
 __global__ void __launch_bounds__(kThreads)
-combine_kernel(const int32_t* __restrict__ topk_ids, const float* __restrict__ topk_w, int M, int k, int E, int H,
-               int nchunks, const float* __restrict__ part, float* __restrict__ y) {
+combine_kernel(const int32_t* __restrict__ topk_ids, int M, int k, int E, int H, int nchunk,
+               const float* __restrict__ part, float* __restrict__ y) {
+    __shared__ float4 red[kCombRG][kCombCG];
     const int t = blockIdx.y;
-    const int col = (blockIdx.x * kThreads + threadIdx.x) * 4;
-    if (col >= H) return;
-    float4 acc = make_float4(0.f, 0.f, 0.f, 0.f);
+    const int tid = threadIdx.x;
+    const int cg = tid % kCombCG;
+    const int rg = tid / kCombCG;
+    const int col = (blockIdx.x * kCombCG + cg) * 4;
+    uint32_t valid = 0;
     for (int s = 0; s < k; ++s) {
-        const int r = t * k + s;
-        const int e = topk_ids[r];
-        if (e < 0 || e >= E) continue;
-        const float w = topk_w[r];
-        float4 ys = make_float4(0.f, 0.f, 0.f, 0.f);
-        const float* src = part + (size_t)r * nchunks * H + col;
-        for (int c = 0; c < nchunks; ++c) {
-            const float4 v = *reinterpret_cast<const float4*>(src + (size_t)c * H);
-            ys.x += v.x; ys.y += v.y; ys.z += v.z; ys.w += v.w;
-        }
-        acc.x = fmaf(w, ys.x, acc.x);
-        acc.y = fmaf(w, ys.y, acc.y);
-        acc.z = fmaf(w, ys.z, acc.z);
-        acc.w = fmaf(w, ys.w, acc.w);
+        const int e = topk_ids[(size_t)t * k + s];
+        if (e >= 0 && e < E) valid |= 1u << s;
     }
-    *reinterpret_cast<float4*>(y + (size_t)t * H + col) = acc;
+    const int rows = k * nchunk;
+    float4 acc = make_float4(0.f, 0.f, 0.f, 0.f);
+    if (col < H) {
+        const float* src = part + (size_t)t * k * nchunk * H + col;
+        for (int row0 = rg; row0 < rows; row0 += kCombBatch * kCombRG) {
+            float4 v[kCombBatch];
+#pragma unroll
+            for (int u = 0; u < kCombBatch; ++u) {
+                const int rr = row0 + u * kCombRG;
+                v[u] = (rr < rows && ((valid >> (rr / nchunk)) & 1u))
+                           ? *reinterpret_cast<const float4*>(src + (size_t)rr * H)
+                           : make_float4(0.f, 0.f, 0.f, 0.f);
+            }
+#pragma unroll
+            for (int u = 0; u < kCombBatch; ++u) {
+                acc.x += v[u].x; acc.y += v[u].y; acc.z += v[u].z; acc.w += v[u].w;
+            }
+        }
+    }
+    red[rg][cg] = acc;
+    __syncthreads();
+    for (int half = kCombRG / 2; half > 0; half >>= 1) {
+        if (rg < half) {
+            const float4 o = red[rg + half][cg];
+            float4 a = red[rg][cg];
+            a.x += o.x; a.y += o.y; a.z += o.z; a.w += o.w;
+            red[rg][cg] = a;
+        }
+        __syncthreads();
+    }
+    if (rg == 0 && col < H) *reinterpret_cast<float4*>(y + (size_t)t * H + col) = red[0][cg];
 }
 
 template <int Q, int CPW>
@@ -255,47 +543,88 @@ hipError_t gateup_q(const PlanArgs& plan, int RT, const float* h, int H, int I, 
                     const uint16_t* Wu, float* p, int32_t* err, hipStream_t stream) {
     const dim3 grid(plan.max_blocks, (I + kWaves * CPW - 1) / (kWaves * CPW));
     if (RT == 1)
-        hipLaunchKernelGGL((gateup_dense_kernel<Q, CPW, 1>), grid, dim3(kThreads), 0, stream, plan, h, H, I, Wg, Wu,
+        MOE_LAUNCH((gateup_dense_kernel<Q, CPW, 1>), grid, dim3(kThreads), 0, stream, plan, h, H, I, Wg, Wu,
                            p, err);
     else if (RT == 4)
-        hipLaunchKernelGGL((gateup_dense_kernel<Q, CPW, 4>), grid, dim3(kThreads), 0, stream, plan, h, H, I, Wg, Wu,
+        MOE_LAUNCH((gateup_dense_kernel<Q, CPW, 4>), grid, dim3(kThreads), 0, stream, plan, h, H, I, Wg, Wu,
                            p, err);
     else
-        hipLaunchKernelGGL((gateup_dense_kernel<Q, CPW, 8>), grid, dim3(kThreads), 0, stream, plan, h, H, I, Wg, Wu,
+        MOE_LAUNCH((gateup_dense_kernel<Q, CPW, 8>), grid, dim3(kThreads), 0, stream, plan, h, H, I, Wg, Wu,
                            p, err);
     return hipGetLastError();
 }
 
 template <int CQ>
-hipError_t down_cq(const PlanArgs& plan, int RT, int H, int I, int RC, const uint16_t* Wd, const float* p,
-                   float* part, int32_t* err, hipStream_t stream) {
-    const int nrc = (I + RC - 1) / RC;
-    const dim3 grid(plan.max_blocks, nrc);
-    if (RT == 1 && RC == 16)
-        hipLaunchKernelGGL((down_kernel<CQ, 16, 1>), grid, dim3(kThreads), 0, stream, plan, H, I, nrc, Wd, p, part,
-                           err);
-    else if (RT == 1 && RC == 32)
-        hipLaunchKernelGGL((down_kernel<CQ, 32, 1>), grid, dim3(kThreads), 0, stream, plan, H, I, nrc, Wd, p, part,
-                           err);
-    else if (RT == 4 && RC == 8)
-        hipLaunchKernelGGL((down_kernel<CQ, 8, 4>), grid, dim3(kThreads), 0, stream, plan, H, I, nrc, Wd, p, part,
-                           err);
-    else if (RT == 8 && RC == 8)
-        hipLaunchKernelGGL((down_kernel<CQ, 8, 8>), grid, dim3(kThreads), 0, stream, plan, H, I, nrc, Wd, p, part,
-                           err);
+hipError_t down_cq(const PlanArgs& plan, int RT, int H, int I, const uint16_t* Wd, const float* p,
+                   const float* topk_w, float* part, int32_t* err, hipStream_t stream) {
+    const int nchunk = (I + kDownRows - 1) / kDownRows;
+    const dim3 grid(plan.max_blocks, nchunk);
+    if (RT == 1)
+        MOE_LAUNCH((down_kernel<CQ, 1>), grid, dim3(kThreads), 0, stream, plan, H, I, nchunk, Wd, p, topk_w,
+                           part, err);
+    else if (RT == 4)
+        MOE_LAUNCH((down_kernel<CQ, 4>), grid, dim3(kThreads), 0, stream, plan, H, I, nchunk, Wd, p, topk_w,
+                           part, err);
     else
-        return hipErrorInvalidValue;
+        MOE_LAUNCH((down_kernel<CQ, 8>), grid, dim3(kThreads), 0, stream, plan, H, I, nchunk, Wd, p, topk_w,
+                           part, err);
     return hipGetLastError();
+}
+
+// Fused tiling: 8 waves, one gate/up channel per wave and chunk; three
+// double-buffered chunks per workgroup (24 channels) up to H = 2048, one
+// chunk (8 channels, no second buffer) up to H = 4096.
+constexpr int kFusedNW = 8;
+constexpr int kFusedCPW = 1;
+constexpr int fused_nch(int Q) { return Q <= 4 ? 3 : 1; }
+constexpr int fused_range(int Q) { return kFusedNW * kFusedCPW * fused_nch(Q); }
+
+template <int Q, int CQ>
+hipError_t fused_q(const PlanArgs& plan, const float* h, const float* topk_w, int H, int I, const uint16_t* Wg,
+                   const uint16_t* Wu, const uint16_t* Wd, float* part, int32_t* err, hipStream_t stream) {
+    constexpr int NCH = fused_nch(Q);
+    const int nrange = (I + fused_range(Q) - 1) / fused_range(Q);
+    const dim3 grid(plan.max_blocks, nrange);
+    const dim3 block(kFusedNW * MOE_WAVE);
+    if (H == 512 * Q && H == 2048 * CQ)
+        MOE_LAUNCH((expert_fused_kernel<Q, CQ, kFusedNW, kFusedCPW, NCH, true>), grid, block, 0, stream, plan,
+                           h, topk_w, H, I, Wg, Wu, Wd, part, nrange, err);
+    else
+        MOE_LAUNCH((expert_fused_kernel<Q, CQ, kFusedNW, kFusedCPW, NCH, false>), grid, block, 0, stream, plan,
+                           h, topk_w, H, I, Wg, Wu, Wd, part, nrange, err);
+    return hipGetLastError();
+}
+
+// Register tile of routes: one route per block row at M == 1, else up to 4
+// or 8 rows of a block at a time.
+int route_tile(int M, int b) {
+    if (M == 1) return 1;
+    if (M <= 4 || b <= 4) return 4;
+    return 8;
 }
 
 }  // namespace
 
-// Register tile of routes for a plan with M tokens: one route per block at
-// M == 1, else up to 4 or 8 rows of a block at a time.
-static int route_tile(int M, int b) {
-    if (M == 1) return 1;
-    if (M <= 4 || b <= 4) return 4;
-    return 8;
+bool dense_uses_fused(int M, int H) { return M == 1 && H <= 4096; }
+
+int dense_chunks(int M, int H, int I) {
+    if (dense_uses_fused(M, H)) {
+        const int range = fused_range((H + 511) / 512 <= 4 ? 4 : 8);
+        return (I + range - 1) / range;
+    }
+    return (I + kDownRows - 1) / kDownRows;
+}
+
+int down_chunks(int I) { return (I + kDownRows - 1) / kDownRows; }
+
+hipError_t launch_expert_fused(const PlanArgs& plan, const float* h, const float* topk_w, int H, int I,
+                               const uint16_t* Wg, const uint16_t* Wu, const uint16_t* Wd, float* part, int32_t* err,
+                               hipStream_t stream) {
+    const int Q = (H + 511) / 512;
+    const int CQ = (H + 2047) / 2048;
+    if (Q <= 4) return fused_q<4, 1>(plan, h, topk_w, H, I, Wg, Wu, Wd, part, err, stream);
+    if (Q <= 8) return fused_q<8, 2>(plan, h, topk_w, H, I, Wg, Wu, Wd, part, err, stream);
+    return hipErrorInvalidValue;  // H > 4096: the register tile would spill; the split schedule is used
 }
 
 hipError_t launch_gateup_dense(const PlanArgs& plan, const float* h, int H, int I, const uint16_t* Wg,
@@ -310,23 +639,20 @@ hipError_t launch_gateup_dense(const PlanArgs& plan, const float* h, int H, int 
     return hipErrorInvalidValue;
 }
 
-int down_rows_per_chunk(int M, int b) { return route_tile(M, b) == 1 ? 16 : 8; }
-
-hipError_t launch_down(const PlanArgs& plan, int H, int I, int RC, const uint16_t* Wd, const float* p, float* part,
-                       int32_t* err, hipStream_t stream) {
+hipError_t launch_down(const PlanArgs& plan, int H, int I, const uint16_t* Wd, const float* p, const float* topk_w,
+                       float* part, int32_t* err, hipStream_t stream) {
     const int RT = route_tile(plan.R / plan.k, plan.b);
     const int CQ = (H + 2047) / 2048;
-    if (CQ <= 1) return down_cq<1>(plan, RT, H, I, RC, Wd, p, part, err, stream);
-    if (CQ <= 2) return down_cq<2>(plan, RT, H, I, RC, Wd, p, part, err, stream);
-    if (CQ <= 4) return down_cq<4>(plan, RT, H, I, RC, Wd, p, part, err, stream);
+    if (CQ <= 1) return down_cq<1>(plan, RT, H, I, Wd, p, topk_w, part, err, stream);
+    if (CQ <= 2) return down_cq<2>(plan, RT, H, I, Wd, p, topk_w, part, err, stream);
+    if (CQ <= 4) return down_cq<4>(plan, RT, H, I, Wd, p, topk_w, part, err, stream);
     return hipErrorInvalidValue;
 }
 
-hipError_t launch_combine(const int32_t* topk_ids, const float* topk_w, int M, int k, int E, int H, int nchunks,
-                          const float* part, float* y, hipStream_t stream) {
-    const dim3 grid((H / 4 + kThreads - 1) / kThreads, M);
-    hipLaunchKernelGGL(combine_kernel, grid, dim3(kThreads), 0, stream, topk_ids, topk_w, M, k, E, H, nchunks, part,
-                       y);
+hipError_t launch_combine(const int32_t* topk_ids, int M, int k, int E, int H, int nchunk, const float* part, float* y,
+                          hipStream_t stream) {
+    const dim3 grid((H / 4 + kCombCG - 1) / kCombCG, M);
+    MOE_LAUNCH(combine_kernel, grid, dim3(kThreads), 0, stream, topk_ids, M, k, E, H, nchunk, part, y);
     return hipGetLastError();
 }
 

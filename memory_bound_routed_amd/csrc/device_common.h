@@ -27,17 +27,44 @@ __device__ __forceinline__ uint4 load_stream16(const uint16_t* p) {
     return make_uint4(v.x, v.y, v.z, v.w);
 }
 
+// Hides a value from loop-invariant code motion: weights held in registers
+// across a loop are unpacked inside the loop (8 fp32 per 16 bytes) instead of
+// all at once before it.  Emits no instruction.
+__device__ __forceinline__ uint4 opaque(uint4 v) {
+    asm volatile("" : "+v"(v.x), "+v"(v.y), "+v"(v.z), "+v"(v.w));
+    return v;
+}
+
 __device__ __forceinline__ uint4 load16(const void* p) {
     return *reinterpret_cast<const uint4*>(p);
 }
 
-// Butterfly sum over the 64 lanes of a wave.  Partners add the same two
-// values (commutative), so every lane ends with the same bits, and the order
-// is fixed by the lane pattern alone.
+// DPP lane permutations used by wave_sum (gfx9 DPP control encodings).
+#define MOE_DPP_QUAD_XOR1 0xB1     // quad_perm [1,0,3,2]
+#define MOE_DPP_QUAD_XOR2 0x4E     // quad_perm [2,3,0,1]
+#define MOE_DPP_ROW_HALF_MIRROR 0x141
+#define MOE_DPP_ROW_MIRROR 0x140
+
+template <int CTRL>
+__device__ __forceinline__ float dpp(float v) {
+    return __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), CTRL, 0xF, 0xF, false));
+}
+
+// Sum over the 64 lanes of a wave, returned wave-uniform.  Inside each row of
+// 16 lanes the partners of every step hold the same two values (quad pairs,
+// quads, half-row mirror, row mirror), so after four DPP adds every lane of
+// a row holds the row sum; the four row sums are then added as
+// (r0 + r1) + (r2 + r3).  The order is fixed by the lane pattern alone.
 __device__ __forceinline__ float wave_sum(float v) {
-#pragma unroll
-    for (int off = 32; off > 0; off >>= 1) v += __shfl_xor(v, off, MOE_WAVE);
-    return v;
+    v += dpp<MOE_DPP_QUAD_XOR1>(v);
+    v += dpp<MOE_DPP_QUAD_XOR2>(v);
+    v += dpp<MOE_DPP_ROW_HALF_MIRROR>(v);
+    v += dpp<MOE_DPP_ROW_MIRROR>(v);
+    const float r0 = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(v), 0));
+    const float r1 = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(v), 16));
+    const float r2 = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(v), 32));
+    const float r3 = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(v), 48));
+    return (r0 + r1) + (r2 + r3);
 }
 
 __device__ __forceinline__ double wave_sum_f64(double v) {

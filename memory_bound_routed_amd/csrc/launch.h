@@ -2,10 +2,30 @@
 // Every launcher only enqueues on `stream` and returns the launch status.
 #pragma once
 
+#include <hip/hip_ext.h>
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
 namespace moe {
+
+// Events attached to the next launch while the context is profiling (set by
+// the host API around each launcher).  With events, the launch goes through
+// hipExtLaunchKernelGGL, which stamps them from the kernel's own dispatch:
+// their elapsed time is the kernel's execution time.
+struct LaunchEvents {
+    hipEvent_t start = nullptr;
+    hipEvent_t stop = nullptr;
+};
+LaunchEvents& launch_events();
+
+#define MOE_LAUNCH(kernel, grid, block, shmem, stream, ...)                                                  \
+    do {                                                                                                     \
+        const ::moe::LaunchEvents ev_ = ::moe::launch_events();                                              \
+        if (ev_.start)                                                                                       \
+            hipExtLaunchKernelGGL(kernel, grid, block, shmem, stream, ev_.start, ev_.stop, 0, __VA_ARGS__);  \
+        else                                                                                                 \
+            hipLaunchKernelGGL(kernel, grid, block, shmem, stream, __VA_ARGS__);                             \
+    } while (0)
 
 // ---- router.hip
 // Row-slice partials of skinny GEMVs  part_m[slice][t][n] = sum_{i in slice} h[t][i] * W_m[i][n]
@@ -13,12 +33,20 @@ namespace moe {
 struct GemvJob {
     const uint16_t* W;   // bf16 [H][N]
     int N;               // columns, N % 8 == 0, N <= 2048
-    float* part;         // fp32 [nslices][M][N]
+    float* part;         // fp32 [gemv_slices(H, N)][M][N]
 };
-hipError_t launch_gemv_partials(const float* h, int M, int H, int slice_rows, const GemvJob* jobs, int njobs,
-                                hipStream_t stream);
-hipError_t launch_router_topk(const float* part, int nslices, int M, int E, int k, const float* bias,
-                              int32_t* ids, float* wts, float* logits_out, hipStream_t stream);
+int gemv_slices(int H, int N);
+hipError_t launch_gemv_partials(const float* h, int M, int H, const GemvJob* jobs, int njobs, hipStream_t stream);
+// Router GEMV + (last workgroup) slice sum, top-k and softmax in one launch.
+// part: fp32 [gemv_slices(H, E)][M][E]; ticket: zeroed uint32, left zeroed.
+hipError_t launch_router(const float* h, int M, int H, const uint16_t* Wr, int E, const float* bias, int k,
+                         float* part, unsigned* ticket, int32_t* ids, float* wts, float* logits_out,
+                         hipStream_t stream);
+// The same, followed (in the last workgroup) by the canonical alignment of the ids.
+hipError_t launch_router_align(const float* h, int M, int H, const uint16_t* Wr, int E, const float* bias, int k,
+                               float* part, unsigned* ticket, int32_t* ids, float* wts, float* logits_out, int b,
+                               int32_t* sorted_routes, int32_t* block_expert, int32_t* counts, int32_t* err,
+                               hipStream_t stream);
 
 // ---- align.hip
 size_t align_lds_bytes(int R, int E);
@@ -37,12 +65,22 @@ struct PlanArgs {
     int max_blocks;                // cap / b
     int E;
 };
+// Fused gate/up + down partials (one route per plan row group; H <= 4096).
+bool dense_uses_fused(int M, int H);
+// Number of down partial chunks per route of the schedule used for (M, H, I).
+int dense_chunks(int M, int H, int I);
+int down_chunks(int I);
+hipError_t launch_expert_fused(const PlanArgs& plan, const float* h, const float* topk_w, int H, int I,
+                               const uint16_t* Wg, const uint16_t* Wu, const uint16_t* Wd, float* part, int32_t* err,
+                               hipStream_t stream);
 hipError_t launch_gateup_dense(const PlanArgs& plan, const float* h, int H, int I, const uint16_t* Wg,
                                const uint16_t* Wu, float* p, int32_t* err, hipStream_t stream);
-hipError_t launch_down(const PlanArgs& plan, int H, int I, int rows_per_chunk, const uint16_t* Wd,
-                       const float* p, float* part, int32_t* err, hipStream_t stream);
-hipError_t launch_combine(const int32_t* topk_ids, const float* topk_w, int M, int k, int E, int H,
-                          int nchunks, const float* part, float* y, hipStream_t stream);
+// part[route][chunk][H] = sum over the chunk's rows of (a_route * p[route][j]) * Wd[e][j][:]
+hipError_t launch_down(const PlanArgs& plan, int H, int I, const uint16_t* Wd, const float* p, const float* topk_w,
+                       float* part, int32_t* err, hipStream_t stream);
+// y[t][:] = sum over valid routes of token t and chunks of part[route][chunk][:]
+hipError_t launch_combine(const int32_t* topk_ids, int M, int k, int E, int H, int nchunk, const float* part, float* y,
+                          hipStream_t stream);
 
 // ---- vqlr.hip
 struct VqArgs {

@@ -13,8 +13,6 @@
 
 namespace {
 
-constexpr int kSliceRows = 64;     // rows per GEMV partial slice (router, z = D^T h)
-constexpr int kMinDownRows = 8;    // smallest down row chunk (sizes the partial buffer)
 constexpr int kChanChunk = 8;      // kept channels per gather workgroup
 
 struct Rec {
@@ -31,17 +29,24 @@ struct moe_ctx {
     void* ws = nullptr;
     size_t ws_bytes = 0;
     int32_t* err = nullptr;
+    unsigned* ticket = nullptr;        // router last-workgroup ticket (zero between calls)
     float* router_part = nullptr;
     float* zpart[2] = {nullptr, nullptr};
     float* p = nullptr;
     float* down_part = nullptr;
     int32_t* kept_ws = nullptr;
     float* chan_part = nullptr;
-    int nslices = 0;
     bool prof = false;
     std::vector<Rec> recs;
     std::vector<hipEvent_t> pool;
 };
+
+namespace moe {
+LaunchEvents& launch_events() {
+    thread_local LaunchEvents ev;
+    return ev;
+}
+}  // namespace moe
 
 namespace {
 
@@ -95,9 +100,6 @@ moe_status check_weights(const moe_config* c, const moe_weights* w) {
     return MOE_OK;
 }
 
-// Rows of the down GEMV handled per workgroup for a call with M tokens.
-int down_rows(int M) { return M == 1 ? 16 : kMinDownRows; }
-
 hipEvent_t take_event(moe_ctx* ctx) {
     if (!ctx->pool.empty()) {
         hipEvent_t e = ctx->pool.back();
@@ -109,23 +111,24 @@ hipEvent_t take_event(moe_ctx* ctx) {
     return e;
 }
 
-// Brackets one launch with events when profiling is on.
+// While profiling, hands a start/stop event pair to the next launch, which
+// stamps them from its own dispatch (see MOE_LAUNCH).
 struct Launch {
     moe_ctx* ctx;
-    hipStream_t s;
     Rec rec{};
     bool on = false;
-    Launch(moe_ctx* c, int kernel, hipStream_t st) : ctx(c), s(st) {
+    Launch(moe_ctx* c, int kernel, hipStream_t) : ctx(c) {
         if (ctx->prof) {
             rec.kernel = kernel;
             rec.a = take_event(ctx);
             rec.b = take_event(ctx);
             on = rec.a && rec.b;
-            if (on) on = hipEventRecord(rec.a, s) == hipSuccess;
+            if (on) moe::launch_events() = moe::LaunchEvents{rec.a, rec.b};
         }
     }
     void done() {
-        if (on && hipEventRecord(rec.b, s) == hipSuccess) ctx->recs.push_back(rec);
+        moe::launch_events() = moe::LaunchEvents{};
+        if (on) ctx->recs.push_back(rec);
         on = false;
     }
 };
@@ -155,9 +158,9 @@ const char* moe_status_string(moe_status s) {
 }
 
 const char* moe_kernel_name(int32_t k) {
-    static const char* names[MOE_KERNEL_COUNT] = {"router_gemv", "router_topk",  "align",       "gateup",
-                                                  "gateup_vqlr", "down",         "combine",     "chan_select",
-                                                  "chan_gather", "chan_combine"};
+    static const char* names[MOE_KERNEL_COUNT] = {"router",      "vq_shared",   "align",        "gateup",
+                                                  "gateup_vqlr", "down",        "combine",      "chan_select",
+                                                  "chan_gather", "chan_combine", "expert_fused", "router_align"};
     return (k >= 0 && k < MOE_KERNEL_COUNT) ? names[k] : nullptr;
 }
 
@@ -180,16 +183,20 @@ moe_status moe_create(const moe_config* cfg, const moe_weights* w, moe_ctx** out
     }
     const moe_config& c = *cfg;
     const size_t MT = c.max_tokens, R = MT * c.top_k;
-    ctx->nslices = (c.H + kSliceRows - 1) / kSliceRows;
-    const size_t nrc = (c.I + (c.max_tokens == 1 ? 16 : kMinDownRows) - 1) / (c.max_tokens == 1 ? 16 : kMinDownRows);
+    const size_t zsl = c.wformat == MOE_WFORMAT_VQLR ? moe::gemv_slices(c.H, c.lr_r) : 0;
+    size_t nchunk = moe::down_chunks(c.I);
+    if (moe::dense_uses_fused(1, c.H)) {
+        const size_t f = moe::dense_chunks(1, c.H, c.I);
+        nchunk = f > nchunk ? f : nchunk;
+    }
     const size_t nchan = c.max_keep > 0 ? (c.max_keep + kChanChunk - 1) / kChanChunk : 0;
     size_t sizes[8] = {
-        256,                                                            // err flag
-        sizeof(float) * ctx->nslices * MT * c.E,                        // router partials
-        c.wformat == MOE_WFORMAT_VQLR ? sizeof(float) * ctx->nslices * MT * c.lr_r : 0,
-        c.wformat == MOE_WFORMAT_VQLR ? sizeof(float) * ctx->nslices * MT * c.lr_r : 0,
+        256,                                                            // err flag, router ticket
+        sizeof(float) * moe::gemv_slices(c.H, c.E) * MT * c.E,          // router partials
+        sizeof(float) * zsl * MT * c.lr_r,                              // z = D^T h partials (gate)
+        sizeof(float) * zsl * MT * c.lr_r,                              // z partials (up)
         sizeof(float) * R * c.I,                                        // p
-        sizeof(float) * R * nrc * c.H,                                  // down partials
+        sizeof(float) * R * nchunk * c.H,                               // down partials
         sizeof(int32_t) * MT * c.max_keep,                              // kept list
         sizeof(float) * MT * nchan * c.H,                               // channel partials
     };
@@ -205,6 +212,7 @@ moe_status moe_create(const moe_config* cfg, const moe_weights* w, moe_ctx** out
     ctx->ws_bytes = total;
     char* base = static_cast<char*>(ctx->ws);
     ctx->err = reinterpret_cast<int32_t*>(base + off[0]);
+    ctx->ticket = reinterpret_cast<unsigned*>(base + off[0] + 64);
     ctx->router_part = reinterpret_cast<float*>(base + off[1]);
     ctx->zpart[0] = reinterpret_cast<float*>(base + off[2]);
     ctx->zpart[1] = reinterpret_cast<float*>(base + off[3]);
@@ -241,15 +249,28 @@ moe_status moe_route_topk(moe_ctx* ctx, const float* h, int32_t M, int32_t* topk
     if (!h || !topk_ids || !topk_w || !aligned(h, 16)) return MOE_ERR_INVALID_ARG;
     const moe_config& c = ctx->cfg;
     hipStream_t s = static_cast<hipStream_t>(stream);
-    moe::GemvJob job{ctx->w.router_w, c.E, ctx->router_part};
-    Launch l1(ctx, MOE_KERNEL_ROUTER_GEMV, s);
-    hipError_t e = moe::launch_gemv_partials(h, M, c.H, kSliceRows, &job, 1, s);
-    l1.done();
-    if (e != hipSuccess) return MOE_ERR_HIP;
-    Launch l2(ctx, MOE_KERNEL_ROUTER_TOPK, s);
-    e = moe::launch_router_topk(ctx->router_part, ctx->nslices, M, c.E, c.top_k, ctx->w.router_bias, topk_ids, topk_w,
-                                logits_out, s);
-    l2.done();
+    Launch l(ctx, MOE_KERNEL_ROUTER, s);
+    hipError_t e = moe::launch_router(h, M, c.H, ctx->w.router_w, c.E, ctx->w.router_bias, c.top_k, ctx->router_part,
+                                      ctx->ticket, topk_ids, topk_w, logits_out, s);
+    l.done();
+    return hip_status(e);
+}
+
+moe_status moe_route_align(moe_ctx* ctx, const float* h, int32_t M, int32_t* topk_ids, float* topk_w,
+                           float* logits_out, int32_t* sorted_routes, int32_t* block_expert, int32_t* counts,
+                           void* stream) {
+    if (!ctx || M < 0) return MOE_ERR_INVALID_ARG;
+    if (M > ctx->cfg.max_tokens) return MOE_ERR_CAPACITY;
+    if (!counts) return MOE_ERR_INVALID_ARG;
+    if (M == 0) return moe_align_blocks(ctx, nullptr, 0, nullptr, nullptr, counts, stream);
+    if (!h || !topk_ids || !topk_w || !sorted_routes || !block_expert || !aligned(h, 16)) return MOE_ERR_INVALID_ARG;
+    const moe_config& c = ctx->cfg;
+    hipStream_t s = static_cast<hipStream_t>(stream);
+    Launch l(ctx, MOE_KERNEL_ROUTER_ALIGN, s);
+    hipError_t e = moe::launch_router_align(h, M, c.H, ctx->w.router_w, c.E, ctx->w.router_bias, c.top_k,
+                                            ctx->router_part, ctx->ticket, topk_ids, topk_w, logits_out, c.block_b,
+                                            sorted_routes, block_expert, counts, ctx->err, s);
+    l.done();
     return hip_status(e);
 }
 
@@ -317,46 +338,53 @@ moe_status moe_expert_forward(moe_ctx* ctx, const float* h, int32_t M, const int
     plan.max_blocks = (int)(align_capacity64(M, c.top_k, c.E, c.block_b) / c.block_b);
     plan.E = c.E;
 
-    if (c.wformat == MOE_WFORMAT_DENSE) {
-        Launch l(ctx, MOE_KERNEL_GATEUP, s);
-        e = moe::launch_gateup_dense(plan, h, c.H, c.I, ctx->w.w_gate, ctx->w.w_up, ctx->p, ctx->err, s);
+    int nchunk = moe::down_chunks(c.I);
+    if (c.wformat == MOE_WFORMAT_DENSE && moe::dense_uses_fused(M, c.H)) {
+        nchunk = moe::dense_chunks(M, c.H, c.I);
+        Launch l(ctx, MOE_KERNEL_EXPERT_FUSED, s);
+        e = moe::launch_expert_fused(plan, h, topk_w, c.H, c.I, ctx->w.w_gate, ctx->w.w_up, ctx->w.w_down,
+                                     ctx->down_part, ctx->err, s);
         l.done();
         if (e != hipSuccess) return MOE_ERR_HIP;
     } else {
-        moe::GemvJob jobs[2] = {{ctx->w.lr_basis[0], c.lr_r, ctx->zpart[0]}, {ctx->w.lr_basis[1], c.lr_r, ctx->zpart[1]}};
-        {
-            Launch l(ctx, MOE_KERNEL_ROUTER_GEMV, s);
-            e = moe::launch_gemv_partials(h, M, c.H, kSliceRows, jobs, 2, s);
+        if (c.wformat == MOE_WFORMAT_DENSE) {
+            Launch l(ctx, MOE_KERNEL_GATEUP, s);
+            e = moe::launch_gateup_dense(plan, h, c.H, c.I, ctx->w.w_gate, ctx->w.w_up, ctx->p, ctx->err, s);
+            l.done();
+            if (e != hipSuccess) return MOE_ERR_HIP;
+        } else {
+            moe::GemvJob jobs[2] = {{ctx->w.lr_basis[0], c.lr_r, ctx->zpart[0]},
+                                    {ctx->w.lr_basis[1], c.lr_r, ctx->zpart[1]}};
+            {
+                Launch l(ctx, MOE_KERNEL_VQ_SHARED, s);
+                e = moe::launch_gemv_partials(h, M, c.H, jobs, 2, s);
+                l.done();
+                if (e != hipSuccess) return MOE_ERR_HIP;
+            }
+            moe::VqArgs vq{};
+            for (int P = 0; P < 2; ++P) {
+                vq.C[P] = ctx->w.lr_coef[P];
+                vq.B[P] = ctx->w.vq_book[P];
+                vq.J[P] = ctx->w.vq_idx[P];
+                vq.zpart[P] = ctx->zpart[P];
+            }
+            vq.zslices = moe::gemv_slices(c.H, c.lr_r);
+            vq.M = M;
+            vq.r = c.lr_r;
+            vq.K = c.vq_K;
+            vq.d = c.vq_d;
+            Launch l(ctx, MOE_KERNEL_GATEUP_VQLR, s);
+            e = moe::launch_gateup_vqlr(plan, vq, h, c.H, c.I, ctx->p, ctx->err, s);
             l.done();
             if (e != hipSuccess) return MOE_ERR_HIP;
         }
-        moe::VqArgs vq{};
-        for (int P = 0; P < 2; ++P) {
-            vq.C[P] = ctx->w.lr_coef[P];
-            vq.B[P] = ctx->w.vq_book[P];
-            vq.J[P] = ctx->w.vq_idx[P];
-            vq.zpart[P] = ctx->zpart[P];
-        }
-        vq.zslices = ctx->nslices;
-        vq.M = M;
-        vq.r = c.lr_r;
-        vq.K = c.vq_K;
-        vq.d = c.vq_d;
-        Launch l(ctx, MOE_KERNEL_GATEUP_VQLR, s);
-        e = moe::launch_gateup_vqlr(plan, vq, h, c.H, c.I, ctx->p, ctx->err, s);
-        l.done();
-        if (e != hipSuccess) return MOE_ERR_HIP;
-    }
-    const int RC = down_rows(M);
-    const int nrc = (c.I + RC - 1) / RC;
-    {
         Launch l(ctx, MOE_KERNEL_DOWN, s);
-        e = moe::launch_down(plan, c.H, c.I, RC, ctx->w.w_down, ctx->p, ctx->down_part, ctx->err, s);
+        e = moe::launch_down(plan, c.H, c.I, ctx->w.w_down, ctx->p, topk_w, ctx->down_part, ctx->err, s);
         l.done();
         if (e != hipSuccess) return MOE_ERR_HIP;
     }
     Launch l(ctx, MOE_KERNEL_COMBINE, s);
-    e = moe::launch_combine(topk_ids, topk_w, M, c.top_k, c.E, c.H, nrc, ctx->down_part, y, s);
+    e = moe::launch_combine(topk_ids, M, c.top_k, c.E, c.H, nchunk, ctx->down_part, y, s);
     l.done();
     return hip_status(e);
 }

@@ -1,11 +1,14 @@
-// Router: skinny bf16 GEMV partials and the wavefront top-k with the
-// renormalised softmax (page "A Multi-Engine Dataflow for MoE Decoding on
-// Scratchpad-Based Tensor Accelerators", MoE-block background; page
-// "Route-Block Membership Selects Packed-AWQ Arithmetic", Sec. 2.1).
+// Router: bf16 GEMV over row slices, then -- in the last workgroup to finish
+// -- the fixed-order sum of the slices, the wavefront top-k and the
+// renormalised softmax, all in one launch (page "A Multi-Engine Dataflow for
+// MoE Decoding on Scratchpad-Based Tensor Accelerators", MoE-block
+// background; page "Route-Block Membership Selects Packed-AWQ Arithmetic",
+// Sec. 2.1: the router's M x k expert-id array).
 //
-// The GEMV kernel also serves the routing-independent shared projection
-// z = D^T h of the VQ + low-rank format (same shape: h [M][H] times a bf16
-// [H][N] matrix), so both can share one launch.
+// The same row-slice GEMV (without the top-k) computes the
+// routing-independent shared projection z = D^T h of the VQ + low-rank
+// format.
+#include "align_device.h"
 #include "device_common.h"
 #include "launch.h"
 
@@ -13,170 +16,252 @@ namespace moe {
 
 namespace {
 
-constexpr int kGemvThreads = 256;
+constexpr int kThreads = 256;
 constexpr int kTokTile = 4;
+constexpr int kRowsPerThread = 4;
 constexpr int kMaxJobs = 3;
+constexpr int kMaxExpertsPerLane = 16;  // E <= 1024
 
 struct GemvJobs {
     GemvJob job[kMaxJobs];
 };
 
-// One workgroup per (row slice, matrix).  Thread layout: N/8 threads cover a
-// row with one 16-byte load each, 256/(N/8) rows are in flight per pass.
-// Per-thread partial sums run over the slice's rows in ascending order, the
-// row groups are then added pairwise in LDS (a fixed tree), and the result is
-// the slice partial.  The total summation depth of a logit is therefore at
-// most ceil(slice_rows/rpp) + ceil(log2 rpp) + nslices (+1 for a bias).
-__global__ void __launch_bounds__(kGemvThreads)
-gemv_partials_kernel(const float* __restrict__ h, int M, int H, int slice_rows, GemvJobs jobs) {
-    extern __shared__ float red[];  // [rpp][kTokTile][N]
-    const GemvJob& jb = jobs.job[blockIdx.y];
-    const int N = jb.N;
-    const uint16_t* __restrict__ W = jb.W;
+// Slice partial of one matrix: part[slice][t][n] = sum_{i in slice} h[t][i] W[i][n].
+// N/8 threads cover a row with one 16-byte load each; rpp = 256/(N/8) row
+// groups; each thread handles kRowsPerThread rows of the slice (all loads
+// issued together), the row groups are added pairwise in LDS.  Summation
+// depth per partial: kRowsPerThread + ceil(log2 rpp).
+template <int TT>
+__device__ __forceinline__ void slice_partial(const float* __restrict__ h, int M, int H,
+                                              const uint16_t* __restrict__ W, int N, int slice, float* __restrict__ part,
+                                              float* red) {
     const int tpr = N >> 3;
-    const int rpp = kGemvThreads / tpr;
+    const int rpp = kThreads / tpr;
     const int tid = threadIdx.x;
     const int col8 = tid % tpr;
     const int rg = tid / tpr;
     const bool active = rg < rpp;
-    const int r0 = blockIdx.x * slice_rows;
-    const int r1 = min(H, r0 + slice_rows);
+    const int slice_rows = rpp * kRowsPerThread;
+    const int r0 = slice * slice_rows;
 
-    for (int t0 = 0; t0 < M; t0 += kTokTile) {
-        const int nt = min(kTokTile, M - t0);
+    for (int t0 = 0; t0 < M; t0 += TT) {
+        const int nt = min(TT, M - t0);
         if (active) {
-            float acc[kTokTile][8];
+            float wf[kRowsPerThread][8];
+            float hv[kRowsPerThread][TT];
 #pragma unroll
-            for (int t = 0; t < kTokTile; ++t)
+            for (int u = 0; u < kRowsPerThread; ++u) {
+                const int i = r0 + rg + u * rpp;
+                if (i < H) {
+                    unpack8(load_stream16(W + (size_t)i * N + col8 * 8), wf[u]);
 #pragma unroll
-                for (int c = 0; c < 8; ++c) acc[t][c] = 0.f;
-            for (int i = r0 + rg; i < r1; i += rpp) {
-                float wf[8];
-                unpack8(load16(W + (size_t)i * N + col8 * 8), wf);
+                    for (int t = 0; t < TT; ++t) hv[u][t] = t < nt ? h[(size_t)(t0 + t) * H + i] : 0.f;
+                } else {
 #pragma unroll
-                for (int t = 0; t < kTokTile; ++t) {
-                    if (t < nt) {
-                        const float hv = h[(size_t)(t0 + t) * H + i];
+                    for (int c = 0; c < 8; ++c) wf[u][c] = 0.f;
 #pragma unroll
-                        for (int c = 0; c < 8; ++c) acc[t][c] = fmaf(hv, wf[c], acc[t][c]);
-                    }
+                    for (int t = 0; t < TT; ++t) hv[u][t] = 0.f;
                 }
             }
+            float acc[TT][8];
 #pragma unroll
-            for (int t = 0; t < kTokTile; ++t)
+            for (int t = 0; t < TT; ++t)
 #pragma unroll
-                for (int c = 0; c < 8; ++c) red[(rg * kTokTile + t) * N + col8 * 8 + c] = acc[t][c];
+                for (int c = 0; c < 8; ++c) acc[t][c] = 0.f;
+#pragma unroll
+            for (int u = 0; u < kRowsPerThread; ++u)
+#pragma unroll
+                for (int t = 0; t < TT; ++t)
+#pragma unroll
+                    for (int c = 0; c < 8; ++c) acc[t][c] = fmaf(hv[u][t], wf[u][c], acc[t][c]);
+#pragma unroll
+            for (int t = 0; t < TT; ++t)
+#pragma unroll
+                for (int c = 0; c < 8; ++c) red[(rg * TT + t) * N + col8 * 8 + c] = acc[t][c];
         }
         __syncthreads();
-        // pairwise tree over the rpp row groups: cnt -> ceil(cnt/2)
         for (int cnt = rpp; cnt > 1;) {
             const int half = (cnt + 1) >> 1;
             const int pairs = cnt - half;
-            for (int idx = tid; idx < pairs * kTokTile * N; idx += kGemvThreads) {
-                const int g = idx / (kTokTile * N);
-                const int rest = idx % (kTokTile * N);
-                red[g * kTokTile * N + rest] += red[(g + half) * kTokTile * N + rest];
+            for (int idx = tid; idx < pairs * TT * N; idx += kThreads) {
+                const int g = idx / (TT * N);
+                const int rest = idx % (TT * N);
+                red[g * TT * N + rest] += red[(g + half) * TT * N + rest];
             }
             cnt = half;
             __syncthreads();
         }
-        for (int idx = tid; idx < nt * N; idx += kGemvThreads) {
+        for (int idx = tid; idx < nt * N; idx += kThreads) {
             const int t = idx / N, n = idx % N;
-            jb.part[((size_t)blockIdx.x * M + t0 + t) * N + n] = red[t * N + n];
+            part[((size_t)slice * M + t0 + t) * N + n] = red[t * N + n];
         }
         __syncthreads();
     }
 }
 
-constexpr int kMaxExpertsPerLane = 16;  // E <= 1024
+__global__ void __launch_bounds__(kThreads)
+gemv_partials_kernel(const float* __restrict__ h, int M, int H, GemvJobs jobs) {
+    extern __shared__ float red[];
+    const GemvJob& jb = jobs.job[blockIdx.y];
+    const int rpp = kThreads / (jb.N >> 3);
+    const int nslices = (H + rpp * kRowsPerThread - 1) / (rpp * kRowsPerThread);
+    if ((int)blockIdx.x >= nslices) return;
+    if (M == 1)
+        slice_partial<1>(h, M, H, jb.W, jb.N, blockIdx.x, jb.part, red);
+    else
+        slice_partial<kTokTile>(h, M, H, jb.W, jb.N, blockIdx.x, jb.part, red);
+}
 
-// One wave per token.  Lane l holds the logits of experts l, l+64, ...; the
-// slice partials are added in slice order, then the bias.  Each of the k
-// rounds takes the largest remaining logit with a wave-wide reduction under
-// the total order (logit descending, expert id ascending), so the winner does
-// not depend on the reduction tree.  NaN logits rank below every number.
-__global__ void __launch_bounds__(MOE_WAVE)
-router_topk_kernel(const float* __restrict__ part, int nslices, int M, int E, int k,
-                   const float* __restrict__ bias, int32_t* __restrict__ ids, float* __restrict__ wts,
-                   float* __restrict__ logits_out) {
-    const int t = blockIdx.x;
-    const int lane = threadIdx.x;
-    float v[kMaxExpertsPerLane];
+// Router: slices as above; the last workgroup to finish (integer ticket)
+// adds the slices in slice order (+ bias) for up to four tokens at a time --
+// every partial load of a pass is issued before the first add.  The top-k is
+// taken by rank counting under the total order (logit desc, expert id asc):
+// rank(e) = #{e' : l[e'] > l[e] or (l[e'] == l[e] and e' < e)}, and the
+// expert of rank s < k goes to slot s.  The ranks are exact, so the result
+// does not depend on how the work is split.  NaN logits count as -inf.  The
+// softmax over the selected logits adds the denominator in slot order.
+constexpr int kSliceBatch = 32;
+
+// Returns true in the last workgroup (which has written ids and weights).
+template <int TT>
+__device__ __forceinline__ bool router_body(const float* __restrict__ h, int M, int H, const uint16_t* __restrict__ Wr,
+                                            int E, const float* __restrict__ bias, int k, float* __restrict__ part,
+                                            unsigned* __restrict__ ticket, int32_t* __restrict__ ids,
+                                            float* __restrict__ wts, float* __restrict__ logits_out, float* red) {
+    __shared__ int s_last;
+    __shared__ int sel_e[kTokTile][32];
+    __shared__ float sel_l[kTokTile][32];
+    const int nslices = gridDim.x;
+    slice_partial<TT>(h, M, H, Wr, E, blockIdx.x, part, red);
+
+    __threadfence();  // publish this workgroup's partials device-wide
+    __syncthreads();
+    if (threadIdx.x == 0) s_last = atomicAdd(ticket, 1u) == (unsigned)(nslices - 1);
+    __syncthreads();
+    if (!s_last) return false;
+    __threadfence();  // observe every other workgroup's partials
+
+    const int tid = threadIdx.x;
+    const int wave = tid / MOE_WAVE;
+    const int lane = tid % MOE_WAVE;
+    float* slog = red;  // [kTokTile][E] logits of the pass (red holds >= kTokTile * E floats)
+    for (int t0 = 0; t0 < M; t0 += TT) {
+        const int nt = min(TT, M - t0);
+        for (int pr = tid; pr < nt * E; pr += kThreads) {
+            const int t = t0 + pr / E, e = pr % E;
+            float s = 0.f;
+            for (int sl0 = 0; sl0 < nslices; sl0 += kSliceBatch) {
+                float x[kSliceBatch];
 #pragma unroll
-    for (int q = 0; q < kMaxExpertsPerLane; ++q) {
-        const int e = lane + MOE_WAVE * q;
-        float s = -INFINITY;
-        if (e < E) {
-            s = 0.f;
-            for (int sl = 0; sl < nslices; ++sl) s += part[((size_t)sl * M + t) * E + e];
+                for (int u = 0; u < kSliceBatch; ++u)
+                    x[u] = sl0 + u < nslices ? part[((size_t)(sl0 + u) * M + t) * E + e] : 0.f;
+#pragma unroll
+                for (int u = 0; u < kSliceBatch; ++u) s += x[u];  // slice order
+            }
             if (bias) s += bias[e];
             if (logits_out) logits_out[(size_t)t * E + e] = s;
-            if (s != s) s = -INFINITY;
+            slog[pr] = (s != s) ? -INFINITY : s;
         }
-        v[q] = s;
-    }
-    uint32_t taken = 0;
-    float my_l = -INFINITY;  // lane s keeps slot s
-    int my_e = 0;
-    for (int s = 0; s < k; ++s) {
-        float bv = -INFINITY;
-        int be = 0x7FFFFFFF;
-#pragma unroll
-        for (int q = 0; q < kMaxExpertsPerLane; ++q) {
-            const int e = lane + MOE_WAVE * q;
-            if (e < E && !((taken >> q) & 1u)) {
-                if (v[q] > bv || (v[q] == bv && e < be)) { bv = v[q]; be = e; }
+        __syncthreads();
+        for (int pr = tid; pr < nt * E; pr += kThreads) {
+            const int tl = pr / E, e = pr % E;
+            const float v = slog[pr];
+            const float* row = slog + tl * E;
+            int rank = 0;
+            for (int e2 = 0; e2 < E; e2 += 4) {  // E % 8 == 0
+                const float4 o = *reinterpret_cast<const float4*>(row + e2);
+                rank += (o.x > v || (o.x == v && e2 < e)) ? 1 : 0;
+                rank += (o.y > v || (o.y == v && e2 + 1 < e)) ? 1 : 0;
+                rank += (o.z > v || (o.z == v && e2 + 2 < e)) ? 1 : 0;
+                rank += (o.w > v || (o.w == v && e2 + 3 < e)) ? 1 : 0;
+            }
+            if (rank < k) {
+                sel_e[tl][rank] = e;
+                sel_l[tl][rank] = v;
             }
         }
-#pragma unroll
-        for (int off = 32; off > 0; off >>= 1) {
-            const float ov = __shfl_xor(bv, off, MOE_WAVE);
-            const int oe = __shfl_xor(be, off, MOE_WAVE);
-            if (ov > bv || (ov == bv && oe < be)) { bv = ov; be = oe; }
+        __syncthreads();
+        if (wave < nt && lane < k) {
+            const int t = t0 + wave;
+            const float l = sel_l[wave][lane];
+            const float x = expf(l - sel_l[wave][0]);
+            float den = 0.f;
+            for (int s = 0; s < k; ++s) den += expf(sel_l[wave][s] - sel_l[wave][0]);
+            ids[(size_t)t * k + lane] = sel_e[wave][lane];
+            wts[(size_t)t * k + lane] = x / den;
         }
-        if ((be & (MOE_WAVE - 1)) == lane) taken |= 1u << (be / MOE_WAVE);
-        if (lane == s) { my_l = bv; my_e = be; }
+        __syncthreads();
     }
-    // softmax over the selected logits, shifted by the largest one; the
-    // denominator adds the slots in slot order
-    const float l0 = __shfl(my_l, 0, MOE_WAVE);
-    const float x = (lane < k) ? expf(my_l - l0) : 0.f;
-    float den = 0.f;
-    for (int s = 0; s < k; ++s) den += __shfl(x, s, MOE_WAVE);
-    if (lane < k) {
-        ids[(size_t)t * k + lane] = my_e;
-        wts[(size_t)t * k + lane] = x / den;
-    }
+    if (tid == 0) atomicExch(ticket, 0u);  // ready for the next call on this context
+    return true;
 }
+
+__global__ void __launch_bounds__(kThreads)
+router_kernel(const float* __restrict__ h, int M, int H, const uint16_t* __restrict__ Wr, int E,
+              const float* __restrict__ bias, int k, float* __restrict__ part, unsigned* __restrict__ ticket,
+              int32_t* __restrict__ ids, float* __restrict__ wts, float* __restrict__ logits_out) {
+    extern __shared__ float red[];
+    if (M == 1)
+        router_body<1>(h, M, H, Wr, E, bias, k, part, ticket, ids, wts, logits_out, red);
+    else
+        router_body<kTokTile>(h, M, H, Wr, E, bias, k, part, ticket, ids, wts, logits_out, red);
+}
+
+// Router, then the canonical alignment of the ids in the last workgroup
+// (which wrote them; the workgroup barrier makes them visible to it).
+__global__ void __launch_bounds__(kThreads)
+router_align_kernel(const float* __restrict__ h, int M, int H, const uint16_t* __restrict__ Wr, int E,
+                    const float* __restrict__ bias, int k, float* __restrict__ part, unsigned* __restrict__ ticket,
+                    int32_t* __restrict__ ids, float* __restrict__ wts, float* __restrict__ logits_out, int b,
+                    int32_t* __restrict__ sorted_routes, int32_t* __restrict__ block_expert,
+                    int32_t* __restrict__ counts, int32_t* __restrict__ err) {
+    extern __shared__ float red[];
+    const bool last = M == 1 ? router_body<1>(h, M, H, Wr, E, bias, k, part, ticket, ids, wts, logits_out, red)
+                             : router_body<kTokTile>(h, M, H, Wr, E, bias, k, part, ticket, ids, wts, logits_out, red);
+    if (!last) return;
+    __syncthreads();
+    align_workgroup(ids, M * k, E, b, sorted_routes, block_expert, counts, err, reinterpret_cast<int*>(red));
+}
+
+size_t lds_bytes(int N) { return (size_t)(kThreads / (N / 8)) * kTokTile * N * sizeof(float); }
 
 }  // namespace
 
-hipError_t launch_gemv_partials(const float* h, int M, int H, int slice_rows, const GemvJob* jobs, int njobs,
-                                hipStream_t stream) {
+int gemv_slices(int H, int N) {
+    const int rpp = kThreads / (N / 8);
+    return (H + rpp * kRowsPerThread - 1) / (rpp * kRowsPerThread);
+}
+
+hipError_t launch_gemv_partials(const float* h, int M, int H, const GemvJob* jobs, int njobs, hipStream_t stream) {
     if (njobs < 1 || njobs > kMaxJobs) return hipErrorInvalidValue;
     GemvJobs js{};
-    int maxN = 0;
+    size_t lds = 0;
+    int grid = 0;
     for (int i = 0; i < njobs; ++i) {
         js.job[i] = jobs[i];
-        maxN = jobs[i].N > maxN ? jobs[i].N : maxN;
+        lds = lds_bytes(jobs[i].N) > lds ? lds_bytes(jobs[i].N) : lds;
+        grid = gemv_slices(H, jobs[i].N) > grid ? gemv_slices(H, jobs[i].N) : grid;
     }
-    // LDS: rpp * kTokTile * N floats; rpp * N <= 256 * 8 for every N
-    size_t lds = 0;
-    for (int i = 0; i < njobs; ++i) {
-        const int tpr = jobs[i].N / 8;
-        const size_t b = (size_t)(kGemvThreads / tpr) * kTokTile * jobs[i].N * sizeof(float);
-        lds = b > lds ? b : lds;
-    }
-    const int nslices = (H + slice_rows - 1) / slice_rows;
-    hipLaunchKernelGGL(gemv_partials_kernel, dim3(nslices, njobs), dim3(kGemvThreads), lds, stream, h, M, H,
-                       slice_rows, js);
+    MOE_LAUNCH(gemv_partials_kernel, dim3(grid, njobs), dim3(kThreads), lds, stream, h, M, H, js);
     return hipGetLastError();
 }
 
-hipError_t launch_router_topk(const float* part, int nslices, int M, int E, int k, const float* bias,
-                              int32_t* ids, float* wts, float* logits_out, hipStream_t stream) {
-    hipLaunchKernelGGL(router_topk_kernel, dim3(M), dim3(MOE_WAVE), 0, stream, part, nslices, M, E, k, bias, ids,
-                       wts, logits_out);
+hipError_t launch_router_align(const float* h, int M, int H, const uint16_t* Wr, int E, const float* bias, int k,
+                               float* part, unsigned* ticket, int32_t* ids, float* wts, float* logits_out, int b,
+                               int32_t* sorted_routes, int32_t* block_expert, int32_t* counts, int32_t* err,
+                               hipStream_t stream) {
+    const size_t la = align_lds_bytes(M * k, E);
+    const size_t lds = lds_bytes(E) > la ? lds_bytes(E) : la;
+    MOE_LAUNCH(router_align_kernel, dim3(gemv_slices(H, E)), dim3(kThreads), lds, stream, h, M, H, Wr, E, bias,
+                       k, part, ticket, ids, wts, logits_out, b, sorted_routes, block_expert, counts, err);
+    return hipGetLastError();
+}
+
+hipError_t launch_router(const float* h, int M, int H, const uint16_t* Wr, int E, const float* bias, int k,
+                         float* part, unsigned* ticket, int32_t* ids, float* wts, float* logits_out,
+                         hipStream_t stream) {
+    MOE_LAUNCH(router_kernel, dim3(gemv_slices(H, E)), dim3(kThreads), lds_bytes(E), stream, h, M, H, Wr, E,
+                       bias, k, part, ticket, ids, wts, logits_out);
     return hipGetLastError();
 }
 

@@ -181,13 +181,13 @@ hipError_t vq_rm(const PlanArgs& plan, const VqArgs& vq, const float* h, int H, 
     const dim3 grid(plan.max_blocks, (I + kWaves * kCPW - 1) / (kWaves * kCPW));
     const int RM = (vq.r + 63) / 64;
     if (RM <= 1)
-        hipLaunchKernelGGL((gateup_vqlr_kernel<QB, 1>), grid, dim3(kThreads), 0, stream, plan, vq, h, H, I, p, err);
+        MOE_LAUNCH((gateup_vqlr_kernel<QB, 1>), grid, dim3(kThreads), 0, stream, plan, vq, h, H, I, p, err);
     else if (RM <= 2)
-        hipLaunchKernelGGL((gateup_vqlr_kernel<QB, 2>), grid, dim3(kThreads), 0, stream, plan, vq, h, H, I, p, err);
+        MOE_LAUNCH((gateup_vqlr_kernel<QB, 2>), grid, dim3(kThreads), 0, stream, plan, vq, h, H, I, p, err);
     else if (RM <= 4)
-        hipLaunchKernelGGL((gateup_vqlr_kernel<QB, 4>), grid, dim3(kThreads), 0, stream, plan, vq, h, H, I, p, err);
+        MOE_LAUNCH((gateup_vqlr_kernel<QB, 4>), grid, dim3(kThreads), 0, stream, plan, vq, h, H, I, p, err);
     else if (RM <= 8)
-        hipLaunchKernelGGL((gateup_vqlr_kernel<QB, 8>), grid, dim3(kThreads), 0, stream, plan, vq, h, H, I, p, err);
+        MOE_LAUNCH((gateup_vqlr_kernel<QB, 8>), grid, dim3(kThreads), 0, stream, plan, vq, h, H, I, p, err);
     else
         return hipErrorInvalidValue;
     return hipGetLastError();

@@ -15,17 +15,18 @@ MAX_ABS_FRAC = 5e-3      # max|y - y_ref| <= MAX_ABS_FRAC * max|y_ref|
 U32 = 2.0 ** -24         # unit roundoff of fp32
 
 
-def router_depth(H: int) -> int:
-    """Upper bound on the summation depth of a router logit in the kernel
-    (documented in moe.h): 64 rows per slice, a pairwise tree over <= 256
-    row groups, ceil(H/64) slice partials added in order, one bias add."""
-    return 64 + 8 + math.ceil(H / 64) + 1
+def router_depth(H: int, E: int) -> int:
+    """Upper bound on the summation depth of a router logit, as documented in
+    moe.h: 4 rows per thread, a pairwise tree over rpp row groups, the row
+    slices added in order, one bias add."""
+    rpp = 2048 // E
+    return 4 + math.ceil(math.log2(rpp)) + math.ceil(H / (4 * rpp)) + 1
 
 
 def logit_error_bound(h: np.ndarray, router_w: np.ndarray, H: int, bias: Optional[np.ndarray] = None) -> np.ndarray:
     """Rigorous bound on |fp32 logit - exact logit|: gamma_n * sum of |terms|
     (the products h_i w_ie and the bias)."""
-    n = router_depth(H)
+    n = router_depth(H, router_w.shape[1])
     gamma = n * U32 / (1 - n * U32)
     s = np.abs(np.asarray(h, np.float64)) @ np.abs(O.bf16_to_f64(router_w))
     if bias is not None:

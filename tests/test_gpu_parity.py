@@ -464,3 +464,59 @@ def test_device_error_flags_on_invalid_ids(mb):
     check_close(layer.y[:3].cpu().numpy(), ref)
     assert mb.moe_read_device_error(layer.ctx) == 0  # cleared
     layer.close()
+
+
+@pytest.mark.parametrize("name", ["tiny_h256_i128_e16_k2", "dense_h2048_i768_e128_k8_m1",
+                                  "aligned_h2048_i768_e128_k8_m21"])
+def test_route_align_matches_separate_calls(mb, name):
+    import torch
+    wl = synth.WORKLOADS[name]
+    say("route+align in one launch vs two launches:", name)
+    inp = synth.layer_inputs(wl, 0, experts=[])   # router only: no expert weights needed
+    inp["w_gate"] = inp["w_up"] = inp["w_down"] = np.zeros((wl.E, 1, wl.H), np.uint16)
+    dev = upload_layer(inp)
+    cfg = mb.make_config(wl.H, 1, wl.E, wl.k, wl.block_b, wl.M)
+    layer = mb.Layer(cfg, dev)
+    h = to_dev(inp["h"])
+    layer.route(h, wl.M, logits=True)
+    layer.align(wl.M)
+    torch.cuda.synchronize()
+    a = [t.clone() for t in (layer.ids, layer.w, layer.logits, layer.sorted_routes, layer.block_expert, layer.counts)]
+    for t in (layer.ids, layer.w, layer.logits, layer.sorted_routes, layer.block_expert, layer.counts):
+        t.fill_(-3)
+    layer.route_align(h, wl.M, logits=True)
+    torch.cuda.synchronize()
+    b = (layer.ids, layer.w, layer.logits, layer.sorted_routes, layer.block_expert, layer.counts)
+    n = int(a[5][1])
+    for x, y, what in zip(a, b, ("ids", "w", "logits", "rows", "blocks", "counts")):
+        if what == "rows":
+            x, y = x[:n], y[:n]
+        if what == "blocks":
+            x, y = x[: n // wl.block_b], y[: n // wl.block_b]
+        assert torch.equal(x.view(torch.int32), y.view(torch.int32)), what
+    assert mb.moe_read_device_error(layer.ctx) == 0
+    layer.close()
+
+
+@pytest.mark.parametrize("ids,b", [
+    ([[3, 3, 5, 3]], 8),          # one token routed three times to expert 3: extra routes in one block
+    ([[6, 6, 6, 1, 6, 2]], 2),    # block size 2: expert 6 spans two blocks of the run
+])
+def test_fused_single_token_with_repeated_experts(mb, ids, b):
+    import torch
+    ids = np.array(ids)
+    k = ids.shape[1]
+    wl = synth.small_workload("repeat_%d_%d" % (k, b), H=2048, I=64, E=8, k=k, M=1, seed=31, block_b=b)
+    inp = synth.layer_inputs(wl, 0)
+    inp["h"] = synth.hidden(wl, 0, 0, M=1)
+    layer = make_layer(mb, wl, inp, 1)
+    dids = torch.from_numpy(ids.astype(np.int32)).cuda()
+    w = np.linspace(0.4, 0.1, k).astype(np.float32).reshape(1, k)
+    dw = torch.from_numpy(w).cuda()
+    layer.align(1, ids=dids)
+    layer.forward(to_dev(inp["h"]), 1, ids=dids, w=dw)
+    torch.cuda.synchronize()
+    assert mb.moe_read_device_error(layer.ctx) == 0
+    ref = O.dense_forward(inp["h"], ids, w.astype(np.float64), inp["w_gate"], inp["w_up"], inp["w_down"])
+    check_close(layer.y[:1].cpu().numpy(), ref)
+    layer.close()
