@@ -88,6 +88,47 @@ def measured_traffic(kernel: str, workload: str):
     return d.get("hbm_bytes_per_launch")
 
 
+def _pmc_rows(path, counter):
+    """(kernel name, value) per dispatch from a rocprofv3 --pmc counter CSV."""
+    import csv
+    out = []
+    with open(path, newline="") as f:
+        for row in csv.DictReader(f):
+            if row.get("Counter_Name") == counter:
+                out.append((row["Kernel_Name"], float(row["Counter_Value"])))
+    return out
+
+
+def traffic_from_counters(fetch_csv, write_csv, workload, kernel="expert_fused"):
+    """HBM bytes per launch of `kernel` from two rocprofv3 --pmc runs of
+    `bench.py --counter-pass` (FETCH_SIZE, then WRITE_SIZE; KiB per dispatch).
+    Each counter is scaled by what it reads for the calibration copy (a
+    256 MiB fp32 negation: 256 MiB read, 256 MiB written), so the result is
+    in bytes of the same kind as the algorithmic count."""
+    copy_bytes = 64 * 2 ** 20 * 4
+    res = {"workload": workload, "kernel": kernel, "source_digest": source_digest(KERNEL_SOURCES[kernel])}
+    total = 0.0
+    for name, path in (("FETCH_SIZE", fetch_csv), ("WRITE_SIZE", write_csv)):
+        rows = _pmc_rows(path, name)
+        cal = [v for k, v in rows if "neg" in k and "elementwise" in k]
+        ker = [v for k, v in rows if kernel + "_kernel" in k]
+        if not cal or not ker:
+            raise SystemExit("%s: no calibration (%d) or %s (%d) dispatches" % (path, len(cal), kernel, len(ker)))
+        cal_kib = float(np.median(cal))
+        factor = copy_bytes / (cal_kib * 1024.0)
+        per = float(np.mean(ker)) * 1024.0 * factor
+        res[name] = {"calibration_kib": cal_kib, "factor": round(factor, 4), "dispatches": len(ker),
+                     "kib_per_dispatch_mean": round(float(np.mean(ker)), 1),
+                     "kib_per_dispatch_min": round(float(np.min(ker)), 1),
+                     "kib_per_dispatch_max": round(float(np.max(ker)), 1), "bytes_per_launch": round(per)}
+        total += per
+    res["hbm_bytes_per_launch"] = round(total)
+    path = os.path.join(ROOT, "profiles", "traffic_%s_%s.json" % (kernel, workload))
+    with open(path, "w") as f:
+        json.dump(res, f, indent=1)
+    print(json.dumps(res))
+
+
 # ----------------------------------------------------------------------------
 
 def build_layers(wl, n_layers, M, keep=0):
@@ -142,7 +183,7 @@ def build_layers(wl, n_layers, M, keep=0):
 def run_steps(layers, hs, M, keep, order):
     for i in order:
         L = layers[i % len(layers)]
-        L.step(hs[i], M, keep=keep)
+        L.step(hs[i % len(hs)], M, keep=keep)
 
 
 def cpu_baseline(wl, budget_s=15.0, max_steps=40):
@@ -190,7 +231,14 @@ def main():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--counter-pass", action="store_true",
                     help="short run for rocprofv3 --pmc: a 256 MiB elementwise copy (calibration) then 96 steps")
+    ap.add_argument("--traffic-from", nargs=2, metavar=("FETCH_CSV", "WRITE_CSV"),
+                    help="host only: turn two rocprofv3 --pmc counter CSVs of --counter-pass into "
+                         "profiles/traffic_<kernel>_<workload>.json")
     args = ap.parse_args()
+
+    if args.traffic_from:
+        traffic_from_counters(args.traffic_from[0], args.traffic_from[1], args.workload)
+        return
 
     if args.gpus != 1:
         print("bench.py runs on one GPU only: the decode step is measured on a single MI355X "

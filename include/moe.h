@@ -152,7 +152,7 @@ void moe_destroy(moe_ctx *ctx);
  *  topk_w     fp32 [M][k] out: softmax over the k selected logits
  *  logits_out fp32 [M][E] out (may be NULL): l = h Wr + bias, fp32 accumulation
  * Each logit is an fp32 sum whose summation tree has depth at most
- * 4 + ceil(log2 rpp) + ceil(H / (4 rpp)) + 1 with rpp = floor(2048 / E), so
+ * 4 + rpp + ceil(H / (4 rpp)) + 1 with rpp = floor(2048 / E), so
  * |l - exact| <= gamma_depth * (sum_i |h_i Wr_ie| + |bias_e|).  The top-k
  * decision is exact for these fp32 logits.  One launch; the last workgroup
  * to finish reduces the row slices (an integer ticket, no spinning).

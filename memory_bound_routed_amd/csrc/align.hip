@@ -3,8 +3,9 @@
 // blocks, Sec. 3.1 Eq. 1 route-block membership, Sec. 5.3 stable (expert id,
 // route id) construction).
 //
-// One workgroup; the body (align_workgroup) is shared with the router's last
-// workgroup and documented in align_device.h.
+// One workgroup; the bodies (align_wave for up to 64 routes, else
+// align_workgroup) are shared with the router's last workgroup and documented
+// in align_device.h.
 #include "align_device.h"
 #include "device_common.h"
 #include "launch.h"
@@ -17,6 +18,11 @@ __global__ void __launch_bounds__(kAlignThreads)
 align_kernel(const int32_t* __restrict__ topk_ids, int R, int E, int b, int32_t* __restrict__ sorted_routes,
              int32_t* __restrict__ block_expert, int32_t* __restrict__ counts, int32_t* __restrict__ err) {
     extern __shared__ int smem[];
+    if (R <= MOE_WAVE) {
+        if (threadIdx.x < MOE_WAVE)
+            align_wave([&](int r) { return topk_ids[r]; }, R, E, b, sorted_routes, block_expert, counts, err);
+        return;
+    }
     align_workgroup(topk_ids, R, E, b, sorted_routes, block_expert, counts, err, smem);
 }
 

@@ -106,5 +106,49 @@ __device__ inline void align_workgroup(const int32_t* __restrict__ topk_ids, int
     }
 }
 
+// The same alignment for R <= 64 routes by one wave, in registers: lane r
+// holds route r.  With id the lane's expert (-1 if invalid),
+//   cnt(r)  = # routes with the same expert,   rank(r) = # of them below r,
+//   first   = the lowest route of its expert (rank 0),
+//   off(e)  = sum of the padded counts ceil(cnt/b)*b of the experts below e
+//             (summed over the first routes of those experts),
+// route r goes to off(e) + rank(r); each expert's first route writes its
+// padding rows and its blocks.  The output equals align_workgroup's: the same
+// (expert id, route id) order, the same padding, the same counts.
+// id_of(r) returns route r's id; every lane of the calling wave must call.
+template <typename IdOf>
+__device__ inline void align_wave(IdOf id_of, int R, int E, int b, int32_t* __restrict__ sorted_routes,
+                                  int32_t* __restrict__ block_expert, int32_t* __restrict__ counts,
+                                  int32_t* __restrict__ err) {
+    const int lane = threadIdx.x % MOE_WAVE;
+    const int raw = lane < R ? id_of(lane) : 0;
+    const bool ok = lane < R && raw >= 0 && raw < E;
+    const int id = ok ? raw : -1;
+    if (__ballot(lane < R && !ok) != 0 && lane == 0) atomicOr(err, DEVERR_BAD_ROUTE_ID);
+    int cnt = 0, rank = 0;
+    for (int r2 = 0; r2 < R; ++r2) {
+        const int o = __builtin_amdgcn_readlane(id, r2);
+        cnt += o == id ? 1 : 0;
+        rank += (o == id && r2 < lane) ? 1 : 0;
+    }
+    const int padded = ((cnt + b - 1) / b) * b;
+    const int first_pad = (ok && rank == 0) ? padded : 0;  // padded count, on the expert's first route only
+    int off = 0, total = 0;
+    for (int r2 = 0; r2 < R; ++r2) {
+        const int o = __builtin_amdgcn_readlane(id, r2);
+        const int pd = __builtin_amdgcn_readlane(first_pad, r2);
+        off += o < id ? pd : 0;
+        total += pd;
+    }
+    if (ok) sorted_routes[off + rank] = lane;
+    if (first_pad) {
+        for (int q = cnt; q < padded; ++q) sorted_routes[off + q] = R;
+        for (int j = 0; j < padded / b; ++j) block_expert[off / b + j] = id;
+    }
+    if (lane == 0) {
+        counts[0] = total / b;
+        counts[1] = total;
+    }
+}
 
 }  // namespace moe

@@ -500,28 +500,28 @@ combine_kernel(const int32_t* __restrict__ topk_ids, int M, int k, int E, int H,
     const int cg = tid % kCombCG;
     const int rg = tid / kCombCG;
     const int col = (blockIdx.x * kCombCG + cg) * 4;
-    uint32_t valid = 0;
-    for (int s = 0; s < k; ++s) {
-        const int e = topk_ids[(size_t)t * k + s];
-        if (e >= 0 && e < E) valid |= 1u << s;
-    }
     const int rows = k * nchunk;
     float4 acc = make_float4(0.f, 0.f, 0.f, 0.f);
-    if (col < H) {
-        const float* src = part + (size_t)t * k * nchunk * H + col;
-        for (int row0 = rg; row0 < rows; row0 += kCombBatch * kCombRG) {
-            float4 v[kCombBatch];
+    // The partial loads do not wait for the ids: rows are clamped into the
+    // token's range and the rows of invalid routes (never written) are
+    // dropped by a select once the ids have arrived.
+    const float* src = part + (size_t)t * k * nchunk * H + min(col, H - 4);
+    for (int row0 = rg; row0 < rows; row0 += kCombBatch * kCombRG) {
+        float4 v[kCombBatch];
+        int e[kCombBatch];
 #pragma unroll
-            for (int u = 0; u < kCombBatch; ++u) {
-                const int rr = row0 + u * kCombRG;
-                v[u] = (rr < rows && ((valid >> (rr / nchunk)) & 1u))
-                           ? *reinterpret_cast<const float4*>(src + (size_t)rr * H)
-                           : make_float4(0.f, 0.f, 0.f, 0.f);
-            }
+        for (int u = 0; u < kCombBatch; ++u) {
+            const int rr = min(row0 + u * kCombRG, rows - 1);
+            v[u] = *reinterpret_cast<const float4*>(src + (size_t)rr * H);
+            e[u] = topk_ids[(size_t)t * k + rr / nchunk];
+        }
 #pragma unroll
-            for (int u = 0; u < kCombBatch; ++u) {
-                acc.x += v[u].x; acc.y += v[u].y; acc.z += v[u].z; acc.w += v[u].w;
-            }
+        for (int u = 0; u < kCombBatch; ++u) {
+            const bool use = col < H && row0 + u * kCombRG < rows && e[u] >= 0 && e[u] < E;
+            acc.x += use ? v[u].x : 0.f;
+            acc.y += use ? v[u].y : 0.f;
+            acc.z += use ? v[u].z : 0.f;
+            acc.w += use ? v[u].w : 0.f;
         }
     }
     red[rg][cg] = acc;

@@ -29,8 +29,8 @@ struct GemvJobs {
 // Slice partial of one matrix: part[slice][t][n] = sum_{i in slice} h[t][i] W[i][n].
 // N/8 threads cover a row with one 16-byte load each; rpp = 256/(N/8) row
 // groups; each thread handles kRowsPerThread rows of the slice (all loads
-// issued together), the row groups are added pairwise in LDS.  Summation
-// depth per partial: kRowsPerThread + ceil(log2 rpp).
+// issued together), then one thread per output adds the row groups in group
+// order from LDS.  Summation depth per partial: kRowsPerThread + rpp - 1.
 template <int TT>
 __device__ __forceinline__ void slice_partial(const float* __restrict__ h, int M, int H,
                                               const uint16_t* __restrict__ W, int N, int slice, float* __restrict__ part,
@@ -47,21 +47,24 @@ __device__ __forceinline__ void slice_partial(const float* __restrict__ h, int M
     for (int t0 = 0; t0 < M; t0 += TT) {
         const int nt = min(TT, M - t0);
         if (active) {
-            float wf[kRowsPerThread][8];
+            // Every load of the pass is issued before the first use: rows past
+            // H read row H-1 and tokens past M read token M-1, and both are
+            // zeroed by a select afterwards (no load sits in a branch, which
+            // would make the compiler wait for it before the next one).
+            uint4 wv[kRowsPerThread];
             float hv[kRowsPerThread][TT];
 #pragma unroll
             for (int u = 0; u < kRowsPerThread; ++u) {
-                const int i = r0 + rg + u * rpp;
-                if (i < H) {
-                    unpack8(load_stream16(W + (size_t)i * N + col8 * 8), wf[u]);
+                const int i = min(r0 + rg + u * rpp, H - 1);
+                wv[u] = load_stream16(W + (size_t)i * N + col8 * 8);
 #pragma unroll
-                    for (int t = 0; t < TT; ++t) hv[u][t] = t < nt ? h[(size_t)(t0 + t) * H + i] : 0.f;
-                } else {
+                for (int t = 0; t < TT; ++t) hv[u][t] = h[(size_t)(t0 + min(t, nt - 1)) * H + i];
+            }
 #pragma unroll
-                    for (int c = 0; c < 8; ++c) wf[u][c] = 0.f;
+            for (int u = 0; u < kRowsPerThread; ++u) {
+                const bool row_ok = r0 + rg + u * rpp < H;
 #pragma unroll
-                    for (int t = 0; t < TT; ++t) hv[u][t] = 0.f;
-                }
+                for (int t = 0; t < TT; ++t) hv[u][t] = (row_ok && t < nt) ? hv[u][t] : 0.f;
             }
             float acc[TT][8];
 #pragma unroll
@@ -69,31 +72,26 @@ __device__ __forceinline__ void slice_partial(const float* __restrict__ h, int M
 #pragma unroll
                 for (int c = 0; c < 8; ++c) acc[t][c] = 0.f;
 #pragma unroll
-            for (int u = 0; u < kRowsPerThread; ++u)
+            for (int u = 0; u < kRowsPerThread; ++u) {
+                float wf[8];
+                unpack8(wv[u], wf);
 #pragma unroll
                 for (int t = 0; t < TT; ++t)
 #pragma unroll
-                    for (int c = 0; c < 8; ++c) acc[t][c] = fmaf(hv[u][t], wf[u][c], acc[t][c]);
+                    for (int c = 0; c < 8; ++c) acc[t][c] = fmaf(hv[u][t], wf[c], acc[t][c]);
+            }
 #pragma unroll
             for (int t = 0; t < TT; ++t)
 #pragma unroll
                 for (int c = 0; c < 8; ++c) red[(rg * TT + t) * N + col8 * 8 + c] = acc[t][c];
         }
         __syncthreads();
-        for (int cnt = rpp; cnt > 1;) {
-            const int half = (cnt + 1) >> 1;
-            const int pairs = cnt - half;
-            for (int idx = tid; idx < pairs * TT * N; idx += kThreads) {
-                const int g = idx / (TT * N);
-                const int rest = idx % (TT * N);
-                red[g * TT * N + rest] += red[(g + half) * TT * N + rest];
-            }
-            cnt = half;
-            __syncthreads();
-        }
+        // row groups added in group order: thread idx = t*N + n sums red[g][t][n]
         for (int idx = tid; idx < nt * N; idx += kThreads) {
-            const int t = idx / N, n = idx % N;
-            part[((size_t)slice * M + t0 + t) * N + n] = red[t * N + n];
+            float s = red[idx];
+#pragma unroll 8
+            for (int g = 1; g < rpp; ++g) s += red[g * TT * N + idx];
+            part[((size_t)slice * M + t0) * N + idx] = s;
         }
         __syncthreads();
     }
@@ -101,7 +99,7 @@ __device__ __forceinline__ void slice_partial(const float* __restrict__ h, int M
 
 __global__ void __launch_bounds__(kThreads)
 gemv_partials_kernel(const float* __restrict__ h, int M, int H, GemvJobs jobs) {
-    extern __shared__ float red[];
+    extern __shared__ __align__(16) float red[];
     const GemvJob& jb = jobs.job[blockIdx.y];
     const int rpp = kThreads / (jb.N >> 3);
     const int nslices = (H + rpp * kRowsPerThread - 1) / (rpp * kRowsPerThread);
@@ -120,77 +118,126 @@ gemv_partials_kernel(const float* __restrict__ h, int M, int H, GemvJobs jobs) {
 // expert of rank s < k goes to slot s.  The ranks are exact, so the result
 // does not depend on how the work is split.  NaN logits count as -inf.  The
 // softmax over the selected logits adds the denominator in slot order.
+//
+// Hand-off between workgroups: after a barrier, one thread per workgroup
+// makes the workgroup's partials visible device-wide (release fence) and
+// takes a ticket; the workgroup holding the last ticket acquires and reads
+// every slice.  Nothing waits on another workgroup.
 constexpr int kSliceBatch = 32;
 
-// Returns true in the last workgroup (which has written ids and weights).
+// Selected (expert, logit) of the tokens of the current pass, slot order.
+struct TopkLds {
+    int e[kTokTile][32];
+    float l[kTokTile][32];
+};
+
+// Total-order key of (logit, expert): a larger key ranks first.  The high
+// word maps the fp32 logit monotonically onto uint32 (-0 is first turned into
+// +0, so equal logits give equal words), the low word is ~e, so that equal
+// logits order by ascending expert id.  Keys are distinct within a token.
+__device__ __forceinline__ uint64_t order_key(float l, int e) {
+    uint32_t u = __float_as_uint(l + 0.0f);
+    u = (u & 0x80000000u) ? ~u : (u | 0x80000000u);
+    return ((uint64_t)u << 32) | (uint32_t)~(uint32_t)e;
+}
+
+// # keys in row[j0 .. j0+n) greater than kv (n % 4 == 0, 16-byte aligned).
+__device__ __forceinline__ int count_greater(const uint64_t* row, int j0, int n, uint64_t kv) {
+    const ulonglong2* r2 = reinterpret_cast<const ulonglong2*>(row + j0);
+    int c = 0;
+    int q = 0;
+    for (; q + 8 <= n / 2; q += 8) {  // eight 16-byte reads in flight
+        ulonglong2 o[8];
+#pragma unroll
+        for (int u = 0; u < 8; ++u) o[u] = r2[q + u];
+#pragma unroll
+        for (int u = 0; u < 8; ++u) c += (o[u].x > kv ? 1 : 0) + (o[u].y > kv ? 1 : 0);
+    }
+    for (; q < n / 2; ++q) {
+        const ulonglong2 o = r2[q];
+        c += (o.x > kv ? 1 : 0) + (o.y > kv ? 1 : 0);
+    }
+    return c;
+}
+
+// Returns true in the last workgroup (which has written ids and weights; the
+// selections of the last pass stay in sel).
 template <int TT>
 __device__ __forceinline__ bool router_body(const float* __restrict__ h, int M, int H, const uint16_t* __restrict__ Wr,
                                             int E, const float* __restrict__ bias, int k, float* __restrict__ part,
                                             unsigned* __restrict__ ticket, int32_t* __restrict__ ids,
-                                            float* __restrict__ wts, float* __restrict__ logits_out, float* red) {
+                                            float* __restrict__ wts, float* __restrict__ logits_out, float* red,
+                                            TopkLds& sel) {
     __shared__ int s_last;
-    __shared__ int sel_e[kTokTile][32];
-    __shared__ float sel_l[kTokTile][32];
     const int nslices = gridDim.x;
-    slice_partial<TT>(h, M, H, Wr, E, blockIdx.x, part, red);
+    slice_partial<TT>(h, M, H, Wr, E, blockIdx.x, part, red);  // ends with a barrier
 
-    __threadfence();  // publish this workgroup's partials device-wide
-    __syncthreads();
-    if (threadIdx.x == 0) s_last = atomicAdd(ticket, 1u) == (unsigned)(nslices - 1);
+    if (threadIdx.x == 0) {
+        __builtin_amdgcn_fence(__ATOMIC_RELEASE, "agent");  // the workgroup's partials, device-wide
+        const bool last = atomicAdd(ticket, 1u) == (unsigned)(nslices - 1);
+        if (last) __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "agent");  // every other workgroup's partials
+        s_last = last;
+    }
     __syncthreads();
     if (!s_last) return false;
-    __threadfence();  // observe every other workgroup's partials
 
     const int tid = threadIdx.x;
     const int wave = tid / MOE_WAVE;
     const int lane = tid % MOE_WAVE;
-    float* slog = red;  // [kTokTile][E] logits of the pass (red holds >= kTokTile * E floats)
+    // LDS of the pass (red holds router_lds_bytes): keys [TT][E], then the
+    // half-row rank counts [2][TT][E]
+    uint64_t* skey = reinterpret_cast<uint64_t*>(red);
+    int* prank = reinterpret_cast<int*>(skey + TT * E);
+    const int halfE = E / 2;  // E % 8 == 0: each half is a whole number of 16-byte key pairs
     for (int t0 = 0; t0 < M; t0 += TT) {
         const int nt = min(TT, M - t0);
         for (int pr = tid; pr < nt * E; pr += kThreads) {
             const int t = t0 + pr / E, e = pr % E;
+            const float bv = bias ? bias[e] : 0.f;  // issued with the slice loads
             float s = 0.f;
             for (int sl0 = 0; sl0 < nslices; sl0 += kSliceBatch) {
                 float x[kSliceBatch];
 #pragma unroll
                 for (int u = 0; u < kSliceBatch; ++u)
-                    x[u] = sl0 + u < nslices ? part[((size_t)(sl0 + u) * M + t) * E + e] : 0.f;
+                    x[u] = part[((size_t)min(sl0 + u, nslices - 1) * M + t) * E + e];
 #pragma unroll
-                for (int u = 0; u < kSliceBatch; ++u) s += x[u];  // slice order
+                for (int u = 0; u < kSliceBatch; ++u) s += sl0 + u < nslices ? x[u] : 0.f;  // slice order
             }
-            if (bias) s += bias[e];
+            if (bias) s += bv;
             if (logits_out) logits_out[(size_t)t * E + e] = s;
-            slog[pr] = (s != s) ? -INFINITY : s;
+            skey[pr] = order_key((s != s) ? -INFINITY : s, e);
+        }
+        __syncthreads();
+        // rank = # keys of the token above the expert's key, counted in two halves
+        for (int it = tid; it < 2 * nt * E; it += kThreads) {
+            const int half = it / (nt * E), pr = it - half * nt * E;
+            const int tl = pr / E;
+            prank[it] = count_greater(skey + tl * E, half * halfE, halfE, skey[pr]);
         }
         __syncthreads();
         for (int pr = tid; pr < nt * E; pr += kThreads) {
-            const int tl = pr / E, e = pr % E;
-            const float v = slog[pr];
-            const float* row = slog + tl * E;
-            int rank = 0;
-            for (int e2 = 0; e2 < E; e2 += 4) {  // E % 8 == 0
-                const float4 o = *reinterpret_cast<const float4*>(row + e2);
-                rank += (o.x > v || (o.x == v && e2 < e)) ? 1 : 0;
-                rank += (o.y > v || (o.y == v && e2 + 1 < e)) ? 1 : 0;
-                rank += (o.z > v || (o.z == v && e2 + 2 < e)) ? 1 : 0;
-                rank += (o.w > v || (o.w == v && e2 + 3 < e)) ? 1 : 0;
-            }
+            const int rank = prank[pr] + prank[nt * E + pr];
             if (rank < k) {
-                sel_e[tl][rank] = e;
-                sel_l[tl][rank] = v;
+                const int tl = pr / E;
+                const uint64_t key = skey[pr];
+                const uint32_t hi = (uint32_t)(key >> 32);
+                sel.e[tl][rank] = (int)~(uint32_t)key;
+                sel.l[tl][rank] = __uint_as_float((hi & 0x80000000u) ? (hi & 0x7FFFFFFFu) : ~hi);
             }
         }
         __syncthreads();
-        if (wave < nt && lane < k) {
+        if (wave < nt) {  // wave w: token t0 + w; lane s: slot s
             const int t = t0 + wave;
-            const float l = sel_l[wave][lane];
-            const float x = expf(l - sel_l[wave][0]);
+            const float l0 = sel.l[wave][0];
+            const float x = lane < k ? expf(sel.l[wave][lane] - l0) : 0.f;
             float den = 0.f;
-            for (int s = 0; s < k; ++s) den += expf(sel_l[wave][s] - sel_l[wave][0]);
-            ids[(size_t)t * k + lane] = sel_e[wave][lane];
-            wts[(size_t)t * k + lane] = x / den;
+            for (int s = 0; s < k; ++s) den += __int_as_float(__builtin_amdgcn_readlane(__float_as_int(x), s));
+            if (lane < k) {
+                ids[(size_t)t * k + lane] = sel.e[wave][lane];
+                wts[(size_t)t * k + lane] = x / den;
+            }
         }
-        __syncthreads();
+        if (t0 + TT < M) __syncthreads();  // sel and the keys are reused by the next pass
     }
     if (tid == 0) atomicExch(ticket, 0u);  // ready for the next call on this context
     return true;
@@ -200,30 +247,50 @@ __global__ void __launch_bounds__(kThreads)
 router_kernel(const float* __restrict__ h, int M, int H, const uint16_t* __restrict__ Wr, int E,
               const float* __restrict__ bias, int k, float* __restrict__ part, unsigned* __restrict__ ticket,
               int32_t* __restrict__ ids, float* __restrict__ wts, float* __restrict__ logits_out) {
-    extern __shared__ float red[];
+    extern __shared__ __align__(16) float red[];
+    __shared__ TopkLds sel;
     if (M == 1)
-        router_body<1>(h, M, H, Wr, E, bias, k, part, ticket, ids, wts, logits_out, red);
+        router_body<1>(h, M, H, Wr, E, bias, k, part, ticket, ids, wts, logits_out, red, sel);
     else
-        router_body<kTokTile>(h, M, H, Wr, E, bias, k, part, ticket, ids, wts, logits_out, red);
+        router_body<kTokTile>(h, M, H, Wr, E, bias, k, part, ticket, ids, wts, logits_out, red, sel);
 }
 
-// Router, then the canonical alignment of the ids in the last workgroup
-// (which wrote them; the workgroup barrier makes them visible to it).
+// Router, then the canonical alignment of the ids in the last workgroup.  Up
+// to 64 routes of a single pass are aligned by wave 0 from the selections
+// still in LDS; otherwise the whole workgroup aligns the ids it has written
+// (the barrier makes them visible to it).
 __global__ void __launch_bounds__(kThreads)
 router_align_kernel(const float* __restrict__ h, int M, int H, const uint16_t* __restrict__ Wr, int E,
                     const float* __restrict__ bias, int k, float* __restrict__ part, unsigned* __restrict__ ticket,
                     int32_t* __restrict__ ids, float* __restrict__ wts, float* __restrict__ logits_out, int b,
                     int32_t* __restrict__ sorted_routes, int32_t* __restrict__ block_expert,
                     int32_t* __restrict__ counts, int32_t* __restrict__ err) {
-    extern __shared__ float red[];
-    const bool last = M == 1 ? router_body<1>(h, M, H, Wr, E, bias, k, part, ticket, ids, wts, logits_out, red)
-                             : router_body<kTokTile>(h, M, H, Wr, E, bias, k, part, ticket, ids, wts, logits_out, red);
+    extern __shared__ __align__(16) float red[];
+    __shared__ TopkLds sel;
+    const int TT = M == 1 ? 1 : kTokTile;
+    const bool last =
+        M == 1 ? router_body<1>(h, M, H, Wr, E, bias, k, part, ticket, ids, wts, logits_out, red, sel)
+               : router_body<kTokTile>(h, M, H, Wr, E, bias, k, part, ticket, ids, wts, logits_out, red, sel);
     if (!last) return;
+    const int R = M * k;
+    if (M <= TT && R <= MOE_WAVE) {
+        __syncthreads();
+        if (threadIdx.x < MOE_WAVE)
+            align_wave([&](int r) { return sel.e[r / k][r % k]; }, R, E, b, sorted_routes, block_expert, counts, err);
+        return;
+    }
     __syncthreads();
-    align_workgroup(ids, M * k, E, b, sorted_routes, block_expert, counts, err, reinterpret_cast<int*>(red));
+    align_workgroup(ids, R, E, b, sorted_routes, block_expert, counts, err, reinterpret_cast<int*>(red));
 }
 
 size_t lds_bytes(int N) { return (size_t)(kThreads / (N / 8)) * kTokTile * N * sizeof(float); }
+
+// LDS of the router kernels: the slice sums, or the keys and rank counts of
+// the top-k (8 + 2*4 bytes per token and expert), whichever is larger.
+size_t router_lds_bytes(int E) {
+    const size_t topk = (size_t)kTokTile * E * (sizeof(uint64_t) + 2 * sizeof(int));
+    return lds_bytes(E) > topk ? lds_bytes(E) : topk;
+}
 
 }  // namespace
 
@@ -251,7 +318,7 @@ hipError_t launch_router_align(const float* h, int M, int H, const uint16_t* Wr,
                                int32_t* sorted_routes, int32_t* block_expert, int32_t* counts, int32_t* err,
                                hipStream_t stream) {
     const size_t la = align_lds_bytes(M * k, E);
-    const size_t lds = lds_bytes(E) > la ? lds_bytes(E) : la;
+    const size_t lds = router_lds_bytes(E) > la ? router_lds_bytes(E) : la;
     MOE_LAUNCH(router_align_kernel, dim3(gemv_slices(H, E)), dim3(kThreads), lds, stream, h, M, H, Wr, E, bias,
                        k, part, ticket, ids, wts, logits_out, b, sorted_routes, block_expert, counts, err);
     return hipGetLastError();
@@ -260,7 +327,7 @@ hipError_t launch_router_align(const float* h, int M, int H, const uint16_t* Wr,
 hipError_t launch_router(const float* h, int M, int H, const uint16_t* Wr, int E, const float* bias, int k,
                          float* part, unsigned* ticket, int32_t* ids, float* wts, float* logits_out,
                          hipStream_t stream) {
-    MOE_LAUNCH(router_kernel, dim3(gemv_slices(H, E)), dim3(kThreads), lds_bytes(E), stream, h, M, H, Wr, E,
+    MOE_LAUNCH(router_kernel, dim3(gemv_slices(H, E)), dim3(kThreads), router_lds_bytes(E), stream, h, M, H, Wr, E,
                        bias, k, part, ticket, ids, wts, logits_out);
     return hipGetLastError();
 }

@@ -17,10 +17,10 @@ U32 = 2.0 ** -24         # unit roundoff of fp32
 
 def router_depth(H: int, E: int) -> int:
     """Upper bound on the summation depth of a router logit, as documented in
-    moe.h: 4 rows per thread, a pairwise tree over rpp row groups, the row
+    moe.h: 4 rows per thread, the rpp row groups added in order, the row
     slices added in order, one bias add."""
     rpp = 2048 // E
-    return 4 + math.ceil(math.log2(rpp)) + math.ceil(H / (4 * rpp)) + 1
+    return 4 + rpp + math.ceil(H / (4 * rpp)) + 1
 
 
 def logit_error_bound(h: np.ndarray, router_w: np.ndarray, H: int, bias: Optional[np.ndarray] = None) -> np.ndarray:

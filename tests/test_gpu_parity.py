@@ -334,7 +334,8 @@ def test_alignment_randomised_stage_isolated(mb):
     cap = mb.moe_align_capacity(maxM, k, E, b)
     n = 0
     for trial in range(120):
-        M = int(rng.integers(1, maxM + 1))
+        # half the trials with at most 64 routes (one-wave path), half up to 512
+        M = int(rng.integers(1, maxM + 1)) if trial % 2 else int(rng.integers(1, 64 // k + 2))
         kind = trial % 5
         if kind == 0:
             ids = np.stack([rng.permutation(E)[:k] for _ in range(M)])
@@ -467,10 +468,15 @@ def test_device_error_flags_on_invalid_ids(mb):
 
 
 @pytest.mark.parametrize("name", ["tiny_h256_i128_e16_k2", "dense_h2048_i768_e128_k8_m1",
-                                  "aligned_h2048_i768_e128_k8_m21"])
+                                  "aligned_h2048_i768_e128_k8_m21", "small_m3_e128_k8", "small_m8_e64_k8"])
 def test_route_align_matches_separate_calls(mb, name):
     import torch
-    wl = synth.WORKLOADS[name]
+    if name.startswith("small_m3"):      # 24 routes of one 4-token pass: aligned from the selections in LDS
+        wl = synth.small_workload(name, H=256, I=8, E=128, k=8, M=3, seed=31)
+    elif name.startswith("small_m8"):    # 64 routes over two passes: aligned from the written ids
+        wl = synth.small_workload(name, H=512, I=8, E=64, k=8, M=8, seed=32)
+    else:
+        wl = synth.WORKLOADS[name]
     say("route+align in one launch vs two launches:", name)
     inp = synth.layer_inputs(wl, 0, experts=[])   # router only: no expert weights needed
     inp["w_gate"] = inp["w_up"] = inp["w_down"] = np.zeros((wl.E, 1, wl.H), np.uint16)
