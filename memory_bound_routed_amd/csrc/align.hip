@@ -16,11 +16,11 @@ namespace {
 
 __global__ void __launch_bounds__(kAlignThreads)
 align_kernel(const int32_t* __restrict__ topk_ids, int R, int E, int b, int32_t* __restrict__ sorted_routes,
-             int32_t* __restrict__ block_expert, int32_t* __restrict__ counts, int32_t* __restrict__ err) {
+             int32_t* __restrict__ block_expert, int32_t* __restrict__ counts, int32_t* __restrict__ err, FastDiv fb) {
     extern __shared__ int smem[];
     if (R <= MOE_WAVE) {
         if (threadIdx.x < MOE_WAVE)
-            align_wave([&](int r) { return topk_ids[r]; }, R, E, b, sorted_routes, block_expert, counts, err);
+            align_wave([&](int r) { return topk_ids[r]; }, R, E, fb, sorted_routes, block_expert, counts, err);
         return;
     }
     align_workgroup(topk_ids, R, E, b, sorted_routes, block_expert, counts, err, smem);
@@ -33,7 +33,7 @@ size_t align_lds_bytes(int R, int E) { return align_lds_bytes_inline(R, E); }
 hipError_t launch_align(const int32_t* topk_ids, int R, int E, int b, int32_t* sorted_routes,
                         int32_t* block_expert, int32_t* counts, int32_t* err, hipStream_t stream) {
     MOE_LAUNCH(align_kernel, dim3(1), dim3(kAlignThreads), align_lds_bytes(R, E), stream, topk_ids, R, E, b,
-                       sorted_routes, block_expert, counts, err);
+                       sorted_routes, block_expert, counts, err, FastDiv((uint32_t)b));
     return hipGetLastError();
 }
 

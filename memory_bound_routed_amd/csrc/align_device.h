@@ -117,7 +117,7 @@ __device__ inline void align_workgroup(const int32_t* __restrict__ topk_ids, int
 // (expert id, route id) order, the same padding, the same counts.
 // id_of(r) returns route r's id; every lane of the calling wave must call.
 template <typename IdOf>
-__device__ inline void align_wave(IdOf id_of, int R, int E, int b, int32_t* __restrict__ sorted_routes,
+__device__ inline void align_wave(IdOf id_of, int R, int E, FastDiv fb, int32_t* __restrict__ sorted_routes,
                                   int32_t* __restrict__ block_expert, int32_t* __restrict__ counts,
                                   int32_t* __restrict__ err) {
     const int lane = threadIdx.x % MOE_WAVE;
@@ -131,7 +131,8 @@ __device__ inline void align_wave(IdOf id_of, int R, int E, int b, int32_t* __re
         cnt += o == id ? 1 : 0;
         rank += (o == id && r2 < lane) ? 1 : 0;
     }
-    const int padded = ((cnt + b - 1) / b) * b;
+    const int b = (int)fb.d;
+    const int padded = fb.div(cnt + b - 1) * b;
     const int first_pad = (ok && rank == 0) ? padded : 0;  // padded count, on the expert's first route only
     int off = 0, total = 0;
     for (int r2 = 0; r2 < R; ++r2) {
@@ -143,10 +144,11 @@ __device__ inline void align_wave(IdOf id_of, int R, int E, int b, int32_t* __re
     if (ok) sorted_routes[off + rank] = lane;
     if (first_pad) {
         for (int q = cnt; q < padded; ++q) sorted_routes[off + q] = R;
-        for (int j = 0; j < padded / b; ++j) block_expert[off / b + j] = id;
+        const int b0 = fb.div(off);
+        for (int j = 0, nbk = fb.div(padded); j < nbk; ++j) block_expert[b0 + j] = id;
     }
     if (lane == 0) {
-        counts[0] = total / b;
+        counts[0] = fb.div(total);
         counts[1] = total;
     }
 }

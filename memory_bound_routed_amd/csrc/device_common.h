@@ -78,6 +78,45 @@ __device__ __forceinline__ float silu_mul(float g, float u) {
     return g / (1.0f + expf(-g)) * u;
 }
 
+// Accesses that are coherent across the whole device within one launch:
+// agent-scope relaxed atomics, which go through to memory past the XCD's L2,
+// so small data can be handed to another workgroup without an L2 writeback
+// or invalidate (the hand-off is ordered by waiting for the stores to
+// complete before an atomic counter is bumped).
+__device__ __forceinline__ void store_agent(float* p, float v) {
+    __hip_atomic_store(p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+__device__ __forceinline__ float load_agent(const float* p) {
+    return __hip_atomic_load(const_cast<float*>(p), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+
+// Quotient and remainder by a divisor fixed at launch, by multiply-high
+// (Granlund and Montgomery, "Division by Invariant Integers using
+// Multiplication", PLDI 1994): for 1 <= d < 2^31, s = ceil(log2 d) and
+// m = floor(2^32 (2^s - d) / d) + 1, every 0 <= x < 2^31 has
+// x / d = (umulhi(x, m) + x) >> s (the sum stays below 2^32).
+struct FastDiv {
+    uint32_t d = 1, m = 1, s = 0;
+    FastDiv() = default;
+    explicit FastDiv(uint32_t div) : d(div) {
+        s = 0;
+        while ((1u << s) < d) ++s;
+        m = (uint32_t)((((uint64_t)1 << 32) * (((uint64_t)1 << s) - d)) / d + 1);
+    }
+    __device__ __forceinline__ int div(int x) const { return (int)((__umulhi((uint32_t)x, m) + (uint32_t)x) >> s); }
+    __device__ __forceinline__ int mod(int x) const { return x - div(x) * (int)d; }
+};
+
+// Pins a kernel argument in scalar registers from the start of the kernel:
+// the value becomes the output of an (empty) asm statement, so the compiler
+// cannot re-read it from the kernel-argument segment where it is used late
+// (a dependent memory round trip on a serial path); under register pressure
+// it is spilled to a VGPR lane instead.
+template <typename T>
+__device__ __forceinline__ void pin_arg(T& v) {
+    asm volatile("" : "+s"(v));
+}
+
 // Make a value wave-uniform (lets the compiler keep it in a scalar register).
 __device__ __forceinline__ int uniform(int v) { return __builtin_amdgcn_readfirstlane(v); }
 

@@ -31,7 +31,9 @@ struct GemvJobs {
 // groups; each thread handles kRowsPerThread rows of the slice (all loads
 // issued together), then one thread per output adds the row groups in group
 // order from LDS.  Summation depth per partial: kRowsPerThread + rpp - 1.
-template <int TT>
+// COHERENT: the partials are read by another workgroup of the same launch,
+// so they are stored device-coherently.
+template <int TT, bool COHERENT>
 __device__ __forceinline__ void slice_partial(const float* __restrict__ h, int M, int H,
                                               const uint16_t* __restrict__ W, int N, int slice, float* __restrict__ part,
                                               float* red) {
@@ -91,7 +93,11 @@ __device__ __forceinline__ void slice_partial(const float* __restrict__ h, int M
             float s = red[idx];
 #pragma unroll 8
             for (int g = 1; g < rpp; ++g) s += red[g * TT * N + idx];
-            part[((size_t)slice * M + t0) * N + idx] = s;
+            float* dst = part + ((size_t)slice * M + t0) * N + idx;
+            if (COHERENT)
+                store_agent(dst, s);
+            else
+                *dst = s;
         }
         __syncthreads();
     }
@@ -105,9 +111,9 @@ gemv_partials_kernel(const float* __restrict__ h, int M, int H, GemvJobs jobs) {
     const int nslices = (H + rpp * kRowsPerThread - 1) / (rpp * kRowsPerThread);
     if ((int)blockIdx.x >= nslices) return;
     if (M == 1)
-        slice_partial<1>(h, M, H, jb.W, jb.N, blockIdx.x, jb.part, red);
+        slice_partial<1, false>(h, M, H, jb.W, jb.N, blockIdx.x, jb.part, red);
     else
-        slice_partial<kTokTile>(h, M, H, jb.W, jb.N, blockIdx.x, jb.part, red);
+        slice_partial<kTokTile, false>(h, M, H, jb.W, jb.N, blockIdx.x, jb.part, red);
 }
 
 // Router: slices as above; the last workgroup to finish (integer ticket)
@@ -119,10 +125,11 @@ gemv_partials_kernel(const float* __restrict__ h, int M, int H, GemvJobs jobs) {
 // does not depend on how the work is split.  NaN logits count as -inf.  The
 // softmax over the selected logits adds the denominator in slot order.
 //
-// Hand-off between workgroups: after a barrier, one thread per workgroup
-// makes the workgroup's partials visible device-wide (release fence) and
-// takes a ticket; the workgroup holding the last ticket acquires and reads
-// every slice.  Nothing waits on another workgroup.
+// Hand-off between workgroups: the slice partials are stored and read
+// device-coherently (past the XCD's L2); once every wave's stores have
+// completed, one thread per workgroup takes a ticket, and the workgroup
+// holding the last ticket reads every slice.  Nothing waits on another
+// workgroup, and no cache is written back or invalidated.
 constexpr int kSliceBatch = 32;
 
 // Selected (expert, logit) of the tokens of the current pass, slot order.
@@ -167,17 +174,13 @@ __device__ __forceinline__ bool router_body(const float* __restrict__ h, int M, 
                                             int E, const float* __restrict__ bias, int k, float* __restrict__ part,
                                             unsigned* __restrict__ ticket, int32_t* __restrict__ ids,
                                             float* __restrict__ wts, float* __restrict__ logits_out, float* red,
-                                            TopkLds& sel) {
+                                            TopkLds& sel, FastDiv fE) {
     __shared__ int s_last;
     const int nslices = gridDim.x;
-    slice_partial<TT>(h, M, H, Wr, E, blockIdx.x, part, red);  // ends with a barrier
-
-    if (threadIdx.x == 0) {
-        __builtin_amdgcn_fence(__ATOMIC_RELEASE, "agent");  // the workgroup's partials, device-wide
-        const bool last = atomicAdd(ticket, 1u) == (unsigned)(nslices - 1);
-        if (last) __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "agent");  // every other workgroup's partials
-        s_last = last;
-    }
+    slice_partial<TT, true>(h, M, H, Wr, E, blockIdx.x, part, red);
+    __builtin_amdgcn_s_waitcnt(0);  // this wave's partial stores have completed
+    __syncthreads();
+    if (threadIdx.x == 0) s_last = atomicAdd(ticket, 1u) == (unsigned)(nslices - 1);
     __syncthreads();
     if (!s_last) return false;
 
@@ -192,14 +195,15 @@ __device__ __forceinline__ bool router_body(const float* __restrict__ h, int M, 
     for (int t0 = 0; t0 < M; t0 += TT) {
         const int nt = min(TT, M - t0);
         for (int pr = tid; pr < nt * E; pr += kThreads) {
-            const int t = t0 + pr / E, e = pr % E;
+            const int tq = fE.div(pr);
+            const int t = t0 + tq, e = pr - tq * E;
             const float bv = bias ? bias[e] : 0.f;  // issued with the slice loads
             float s = 0.f;
             for (int sl0 = 0; sl0 < nslices; sl0 += kSliceBatch) {
                 float x[kSliceBatch];
 #pragma unroll
                 for (int u = 0; u < kSliceBatch; ++u)
-                    x[u] = part[((size_t)min(sl0 + u, nslices - 1) * M + t) * E + e];
+                    x[u] = load_agent(part + ((size_t)min(sl0 + u, nslices - 1) * M + t) * E + e);
 #pragma unroll
                 for (int u = 0; u < kSliceBatch; ++u) s += sl0 + u < nslices ? x[u] : 0.f;  // slice order
             }
@@ -210,15 +214,15 @@ __device__ __forceinline__ bool router_body(const float* __restrict__ h, int M, 
         __syncthreads();
         // rank = # keys of the token above the expert's key, counted in two halves
         for (int it = tid; it < 2 * nt * E; it += kThreads) {
-            const int half = it / (nt * E), pr = it - half * nt * E;
-            const int tl = pr / E;
+            const int half = it >= nt * E ? 1 : 0, pr = it - half * nt * E;
+            const int tl = fE.div(pr);
             prank[it] = count_greater(skey + tl * E, half * halfE, halfE, skey[pr]);
         }
         __syncthreads();
         for (int pr = tid; pr < nt * E; pr += kThreads) {
             const int rank = prank[pr] + prank[nt * E + pr];
             if (rank < k) {
-                const int tl = pr / E;
+                const int tl = fE.div(pr);
                 const uint64_t key = skey[pr];
                 const uint32_t hi = (uint32_t)(key >> 32);
                 sel.e[tl][rank] = (int)~(uint32_t)key;
@@ -246,13 +250,15 @@ __device__ __forceinline__ bool router_body(const float* __restrict__ h, int M, 
 __global__ void __launch_bounds__(kThreads)
 router_kernel(const float* __restrict__ h, int M, int H, const uint16_t* __restrict__ Wr, int E,
               const float* __restrict__ bias, int k, float* __restrict__ part, unsigned* __restrict__ ticket,
-              int32_t* __restrict__ ids, float* __restrict__ wts, float* __restrict__ logits_out) {
+              int32_t* __restrict__ ids, float* __restrict__ wts, float* __restrict__ logits_out, FastDiv fE) {
     extern __shared__ __align__(16) float red[];
     __shared__ TopkLds sel;
+    pin_arg(bias); pin_arg(k); pin_arg(E); pin_arg(M); pin_arg(ids); pin_arg(wts); pin_arg(logits_out);
+    pin_arg(ticket); pin_arg(part); pin_arg(fE.m); pin_arg(fE.s);
     if (M == 1)
-        router_body<1>(h, M, H, Wr, E, bias, k, part, ticket, ids, wts, logits_out, red, sel);
+        router_body<1>(h, M, H, Wr, E, bias, k, part, ticket, ids, wts, logits_out, red, sel, fE);
     else
-        router_body<kTokTile>(h, M, H, Wr, E, bias, k, part, ticket, ids, wts, logits_out, red, sel);
+        router_body<kTokTile>(h, M, H, Wr, E, bias, k, part, ticket, ids, wts, logits_out, red, sel, fE);
 }
 
 // Router, then the canonical alignment of the ids in the last workgroup.  Up
@@ -264,19 +270,23 @@ router_align_kernel(const float* __restrict__ h, int M, int H, const uint16_t* _
                     const float* __restrict__ bias, int k, float* __restrict__ part, unsigned* __restrict__ ticket,
                     int32_t* __restrict__ ids, float* __restrict__ wts, float* __restrict__ logits_out, int b,
                     int32_t* __restrict__ sorted_routes, int32_t* __restrict__ block_expert,
-                    int32_t* __restrict__ counts, int32_t* __restrict__ err) {
+                    int32_t* __restrict__ counts, int32_t* __restrict__ err, FastDiv fE, FastDiv fk, FastDiv fb) {
     extern __shared__ __align__(16) float red[];
     __shared__ TopkLds sel;
+    pin_arg(bias); pin_arg(k); pin_arg(E); pin_arg(M); pin_arg(ids); pin_arg(wts); pin_arg(logits_out);
+    pin_arg(ticket); pin_arg(part); pin_arg(b); pin_arg(sorted_routes); pin_arg(block_expert); pin_arg(counts);
+    pin_arg(err); pin_arg(fE.m); pin_arg(fE.s); pin_arg(fk.m); pin_arg(fk.s); pin_arg(fb.m); pin_arg(fb.s);
     const int TT = M == 1 ? 1 : kTokTile;
     const bool last =
-        M == 1 ? router_body<1>(h, M, H, Wr, E, bias, k, part, ticket, ids, wts, logits_out, red, sel)
-               : router_body<kTokTile>(h, M, H, Wr, E, bias, k, part, ticket, ids, wts, logits_out, red, sel);
+        M == 1 ? router_body<1>(h, M, H, Wr, E, bias, k, part, ticket, ids, wts, logits_out, red, sel, fE)
+               : router_body<kTokTile>(h, M, H, Wr, E, bias, k, part, ticket, ids, wts, logits_out, red, sel, fE);
     if (!last) return;
     const int R = M * k;
     if (M <= TT && R <= MOE_WAVE) {
         __syncthreads();
         if (threadIdx.x < MOE_WAVE)
-            align_wave([&](int r) { return sel.e[r / k][r % k]; }, R, E, b, sorted_routes, block_expert, counts, err);
+            align_wave([&](int r) { const int t = fk.div(r); return sel.e[t][r - t * k]; }, R, E, fb, sorted_routes,
+                       block_expert, counts, err);
         return;
     }
     __syncthreads();
@@ -320,7 +330,8 @@ hipError_t launch_router_align(const float* h, int M, int H, const uint16_t* Wr,
     const size_t la = align_lds_bytes(M * k, E);
     const size_t lds = router_lds_bytes(E) > la ? router_lds_bytes(E) : la;
     MOE_LAUNCH(router_align_kernel, dim3(gemv_slices(H, E)), dim3(kThreads), lds, stream, h, M, H, Wr, E, bias,
-                       k, part, ticket, ids, wts, logits_out, b, sorted_routes, block_expert, counts, err);
+                       k, part, ticket, ids, wts, logits_out, b, sorted_routes, block_expert, counts, err,
+                       FastDiv((uint32_t)E), FastDiv((uint32_t)k), FastDiv((uint32_t)b));
     return hipGetLastError();
 }
 
@@ -328,7 +339,7 @@ hipError_t launch_router(const float* h, int M, int H, const uint16_t* Wr, int E
                          float* part, unsigned* ticket, int32_t* ids, float* wts, float* logits_out,
                          hipStream_t stream) {
     MOE_LAUNCH(router_kernel, dim3(gemv_slices(H, E)), dim3(kThreads), router_lds_bytes(E), stream, h, M, H, Wr, E,
-                       bias, k, part, ticket, ids, wts, logits_out);
+                       bias, k, part, ticket, ids, wts, logits_out, FastDiv((uint32_t)E));
     return hipGetLastError();
 }
 

@@ -202,3 +202,24 @@ def test_binding_fails_loudly_without_the_library(tmp_path):
     r = subprocess.run([sys.executable, "-c", "import memory_bound_routed_amd"], cwd=tmp_path,
                        capture_output=True, text=True)
     assert r.returncode != 0 and "libmoe.so is not built" in r.stderr
+
+
+def test_multiply_high_division_identity():
+    """The kernels divide by launch-time constants (E, k, block size) with
+    multiply-high (Granlund & Montgomery 1994): s = ceil(log2 d),
+    m = floor(2^32 (2^s - d) / d) + 1, x / d = (umulhi(x, m) + x) >> s for
+    0 <= x < 2^31.  Checked against integer division over the divisors the
+    library can see and x at the range edges and in between."""
+    import numpy as np
+    rng = np.random.default_rng(5)
+    xs = np.unique(np.concatenate([np.arange(0, 70000, dtype=np.int64),
+                                   (2 ** 31 - 1) - np.arange(0, 5000, dtype=np.int64),
+                                   rng.integers(0, 2 ** 31, 20000, dtype=np.int64)]))
+    for d in list(range(1, 2049)) + [4095, 4096, 4097, 6144, 8191, 8192, 65537, 2 ** 30 + 3]:
+        s = 0
+        while (1 << s) < d:
+            s += 1
+        m = ((1 << 32) * ((1 << s) - d)) // d + 1
+        assert m < (1 << 32)
+        q = (((xs * m) >> 32) + xs) >> s
+        assert np.array_equal(q, xs // d), d

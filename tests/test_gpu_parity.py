@@ -391,10 +391,14 @@ def test_empty_batch_and_max_tokens(mb):
     layer.close()
 
 
-def test_bitwise_reproducible_over_repeated_calls(mb):
+@pytest.mark.parametrize("name", ["aligned_h2048_i768_e128_k8_m21", "fused_h2048_i768_e16_k8_m1"])
+def test_bitwise_reproducible_over_repeated_calls(mb, name):
     import torch
-    wl = synth.WORKLOADS["aligned_h2048_i768_e128_k8_m21"]
-    say("100 repeated steps, aligned_h2048_i768_e128_k8_m21")
+    if name.startswith("fused"):   # one token: the fused kernel, whose last workgroups sum y
+        wl = synth.small_workload(name, H=2048, I=768, E=16, k=8, M=1, seed=41)
+    else:
+        wl = synth.WORKLOADS[name]
+    say("100 repeated steps,", name)
     inp = synth.layer_inputs(wl, 0)
     layer = make_layer(mb, wl, inp, wl.M)
     h = to_dev(inp["h"])
@@ -409,6 +413,10 @@ def test_bitwise_reproducible_over_repeated_calls(mb):
                 assert torch.equal(a.view(torch.int32) if a.dtype == torch.float32 else a,
                                    b.view(torch.int32) if b.dtype == torch.float32 else b)
     torch.cuda.synchronize()
+    assert mb.moe_read_device_error(layer.ctx) == 0
+    ref = O.dense_forward(inp["h"], layer.ids[: wl.M].cpu().numpy().astype(np.int64),
+                          layer.w[: wl.M].cpu().numpy().astype(np.float64), inp["w_gate"], inp["w_up"], inp["w_down"])
+    check_close(first[0][: wl.M].cpu().numpy(), ref)
     layer.close()
 
 
