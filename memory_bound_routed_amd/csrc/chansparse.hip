@@ -24,9 +24,11 @@ __device__ __forceinline__ unsigned long long order_key(double x) {
     return (u >> 63) ? ~u : (u | 0x8000000000000000ull);
 }
 
-// Exclusive scan of one int per thread over the workgroup; returns the
-// exclusive prefix and writes the total to *total.
+// Exclusive scan of one int per thread over a workgroup of NT threads;
+// returns the exclusive prefix and writes the total to *total.
+template <int NT>
 __device__ __forceinline__ int block_exclusive_scan(int v, int* wsum, int* total) {
+    constexpr int NWV = NT / MOE_WAVE;
     const int lane = threadIdx.x % MOE_WAVE;
     const int wave = threadIdx.x / MOE_WAVE;
     int x = v;
@@ -38,35 +40,67 @@ __device__ __forceinline__ int block_exclusive_scan(int v, int* wsum, int* total
     if (lane == MOE_WAVE - 1) wsum[wave] = x;
     __syncthreads();
     int base = 0, all = 0;
-    for (int w = 0; w < kWaves; ++w) {
-        if (w < wave) base += wsum[w];
-        all += wsum[w];
+#pragma unroll
+    for (int w = 0; w < NWV; ++w) {
+        const int c = wsum[w];
+        base += w < wave ? c : 0;
+        all += c;
     }
     __syncthreads();
     *total = all;
     return base + x - v;
 }
 
-// One workgroup per token.  LDS: the token's candidate norms (fp32 [n]), a
-// tie flag and a take flag per candidate.
-__global__ void __launch_bounds__(kThreads)
+// Adds one to hist[d] for every lane with act set.  The scores of a token
+// often share their leading digits, which would serialise up to 64 atomics
+// on one bin: the lanes holding the digit of the first two pending lanes are
+// counted with one atomic each, the rest (spread digits) add one per lane.
+__device__ __forceinline__ void wave_hist_add(int* hist, bool act, int d) {
+    const int lane = threadIdx.x % MOE_WAVE;
+    uint64_t pend = __ballot(act);
+#pragma unroll
+    for (int it = 0; it < 2; ++it) {
+        if (!pend) break;
+        const int leader = __builtin_ctzll(pend);
+        const int dl = __builtin_amdgcn_readlane(d, leader);
+        const uint64_t same = __ballot(((pend >> lane) & 1ull) && d == dl);
+        if (lane == leader) atomicAdd(&hist[dl], __builtin_popcountll(same));
+        pend &= ~same;
+    }
+    if ((pend >> lane) & 1ull) atomicAdd(&hist[d], 1);
+}
+
+// One workgroup of kSelThreads per token; thread t owns the candidates
+// idx = t*per .. t*per + per - 1 (per <= 8, idx = s*I + j) and keeps their
+// keys in registers.  An MSD radix select over 8-bit digits narrows the
+// leading bits of the K-th best key until its bucket holds exactly the
+// candidates still needed; candidates above the bucket are kept, the
+// bucket's too, and only if whole keys tie at the K-th place are the first
+// `need` of them taken in (expert id, channel) order.  The kept list is
+// written in candidate order.  LDS: a tie mark per candidate.
+constexpr int kSelThreads = 1024;
+constexpr int kSelPer = 8;
+
+__global__ void __launch_bounds__(kSelThreads)
 chan_select_kernel(const int32_t* __restrict__ topk_ids, const float* __restrict__ topk_w,
-                   const float* __restrict__ norms, int k, int I, int E, int K, int32_t* __restrict__ kept) {
+                   const float* __restrict__ norms, int k, int I, int E, int K, FastDiv fI,
+                   int32_t* __restrict__ kept) {
     extern __shared__ unsigned char lds[];
     const int n = k * I;
-    float* sn = reinterpret_cast<float*>(lds);                // [n]
-    unsigned char* tie = lds + (size_t)n * sizeof(float);     // [n], indexed in (expert, channel) order
-    unsigned char* take = tie + n;                            // [n], natural (slot, channel) order
+    unsigned char* tie = lds;            // [n], indexed in (expert, channel) order
     __shared__ double sa[32];
     __shared__ int se[32];
     __shared__ int spos[32];  // rank of slot s when slots are ordered by expert id
     __shared__ int hist[256];
     __shared__ unsigned long long s_prefix;
     __shared__ int s_need;
-    __shared__ int wsum[kWaves];
+    __shared__ int s_cnt;
+    __shared__ int wsum[kSelThreads / MOE_WAVE];
     const int t = blockIdx.x;
     const int tid = threadIdx.x;
     const int lane = tid % MOE_WAVE;
+    const int per = (n + kSelThreads - 1) / kSelThreads;  // <= kSelPer (n <= 8192)
+    const int i0 = tid * per;
 
     if (tid < k) {
         const int e = topk_ids[(size_t)t * k + tid];
@@ -78,34 +112,43 @@ chan_select_kernel(const int32_t* __restrict__ topk_ids, const float* __restrict
         const int e = se[tid];
         int pos = 0;
         for (int s2 = 0; s2 < k; ++s2) {
-            const int e2 = se[s2];
-            const unsigned a = (unsigned)e, b2 = (unsigned)e2;  // -1 sorts last
+            const unsigned a = (unsigned)e, b2 = (unsigned)se[s2];  // -1 sorts last
             pos += (b2 < a || (b2 == a && s2 < tid)) ? 1 : 0;
         }
         spos[tid] = pos;
     }
-    for (int idx = tid; idx < n; idx += kThreads) {
-        const int s = idx / I, j = idx % I;
-        const int e = se[s];
-        sn[idx] = e >= 0 ? norms[(size_t)e * I + j] : 0.f;
+    // keys of the owned candidates (norm loads issued together)
+    unsigned long long key[kSelPer];
+    int tpos[kSelPer];  // (expert, channel)-order position
+    float nv[kSelPer];
+#pragma unroll
+    for (int u = 0; u < kSelPer; ++u) {
+        const int idx = min(i0 + u, n - 1);
+        const int sl = fI.div(idx), j = idx - sl * I;
+        const int e = se[sl];
+        nv[u] = norms[(size_t)(e < 0 ? 0 : e) * I + j];
     }
-    __syncthreads();
+    __syncthreads();  // spos ready
+#pragma unroll
+    for (int u = 0; u < kSelPer; ++u) {
+        const int idx = min(i0 + u, n - 1);
+        const int sl = fI.div(idx), j = idx - sl * I;
+        key[u] = se[sl] < 0 ? 0ull : order_key(sa[sl] * (double)nv[u]);
+        tpos[u] = spos[sl] * I + j;
+    }
 
-    auto key_of = [&](int idx) -> unsigned long long {
-        const int s = idx / I;
-        if (se[s] < 0) return 0ull;
-        return order_key(sa[s] * (double)sn[idx]);
-    };
-
+    // MSD passes until the bucket holding the K-th key contains exactly the
+    // candidates still needed (all of them kept), or the key is exhausted.
     unsigned long long prefix = 0;
-    int need = K;
+    int need = K, shift = 64, cnt = 0;
     for (int pass = 0; pass < 8; ++pass) {
-        const int shift = 56 - 8 * pass;
-        hist[tid] = 0;
+        const int sh = 56 - 8 * pass;
+        if (tid < 256) hist[tid] = 0;
         __syncthreads();
-        for (int idx = tid; idx < n; idx += kThreads) {
-            const unsigned long long key = key_of(idx);
-            if (pass == 0 || (key >> (shift + 8)) == prefix) atomicAdd(&hist[(key >> shift) & 255ull], 1);
+#pragma unroll
+        for (int u = 0; u < kSelPer; ++u) {
+            const bool act = u < per && i0 + u < n && (pass == 0 || (key[u] >> (sh + 8)) == prefix);
+            wave_hist_add(hist, act, (int)((key[u] >> sh) & 255ull));
         }
         __syncthreads();
         if (tid < MOE_WAVE) {
@@ -125,6 +168,7 @@ chan_select_kernel(const int32_t* __restrict__ topk_ids, const float* __restrict
                 if (before < need && before + c[x] >= need) {
                     s_prefix = (prefix << 8) | (unsigned long long)(255 - 4 * lane - x);
                     s_need = need - before;
+                    s_cnt = c[x];
                 }
                 before += c[x];
             }
@@ -132,49 +176,49 @@ chan_select_kernel(const int32_t* __restrict__ topk_ids, const float* __restrict
         __syncthreads();
         prefix = s_prefix;
         need = s_need;
+        cnt = s_cnt;
+        shift = sh;
+        if (cnt == need) break;  // uniform: every candidate of the bucket is kept
+    }
+    // kept: keys whose leading (64 - shift) bits exceed the bucket's, and of
+    // the bucket either all (cnt == need) or, for whole-key ties, the first
+    // `need` in (expert, channel) order
+    const bool ties = cnt > need;  // only after the last pass: equal full keys
+    if (ties) {
+        for (int i = tid; i < n; i += kSelThreads) tie[i] = 0;
         __syncthreads();
-    }
-    const unsigned long long T = prefix;  // key of the K-th best candidate
-
-    // take: above the threshold, or one of the first `need` ties in (expert, channel) order
-    for (int idx = tid; idx < n; idx += kThreads) {
-        const unsigned long long key = key_of(idx);
-        const int s = idx / I, j = idx % I;
-        take[idx] = key > T ? 1 : 0;
-        tie[spos[s] * I + j] = key == T ? 1 : 0;
-    }
-    __syncthreads();
-    const int per = (n + kThreads - 1) / kThreads;
-    {
-        const int u0 = tid * per, u1 = min(n, u0 + per);
+#pragma unroll
+        for (int u = 0; u < kSelPer; ++u)
+            if (u < per && i0 + u < n && (key[u] >> shift) == prefix) tie[tpos[u]] = 1;
+        __syncthreads();
         int c = 0;
-        for (int u = u0; u < u1; ++u) c += tie[u];
+        for (int u = 0; u < per; ++u) c += i0 + u < n ? tie[i0 + u] : 0;
         int total;
-        int rank = block_exclusive_scan(c, wsum, &total);
-        for (int u = u0; u < u1; ++u) {
-            const int is_tie = tie[u];
-            tie[u] = (is_tie && rank < need) ? 2 : is_tie;
+        int rank = block_exclusive_scan<kSelThreads>(c, wsum, &total);
+        for (int u = 0; u < per; ++u) {
+            if (i0 + u >= n) break;
+            const int is_tie = tie[i0 + u];
+            if (is_tie && rank < need) tie[i0 + u] = 2;
             rank += is_tie;
         }
+        __syncthreads();
     }
-    __syncthreads();
-    for (int idx = tid; idx < n; idx += kThreads) {
-        const int s = idx / I, j = idx % I;
-        if (tie[spos[s] * I + j] == 2) take[idx] = 1;
+    // compaction of the kept candidates in candidate order
+    unsigned takemask = 0;
+#pragma unroll
+    for (int u = 0; u < kSelPer; ++u) {
+        if (!(u < per && i0 + u < n)) continue;
+        const unsigned long long top = key[u] >> shift;
+        if (top > prefix || (top == prefix && (!ties || tie[tpos[u]] == 2))) takemask |= 1u << u;
     }
-    __syncthreads();
-    {
-        const int i0 = tid * per, i1 = min(n, i0 + per);
-        int c = 0;
-        for (int i = i0; i < i1; ++i) c += take[i];
-        int total;
-        int pos = block_exclusive_scan(c, wsum, &total);
-        for (int i = i0; i < i1; ++i)
-            if (take[i]) {
-                if (pos < K) kept[(size_t)t * K + pos] = i;  // exactly K are taken; never write past K
-                ++pos;
-            }
-    }
+    int total;
+    int pos = block_exclusive_scan<kSelThreads>(__builtin_popcount(takemask), wsum, &total);
+#pragma unroll
+    for (int u = 0; u < kSelPer; ++u)
+        if ((takemask >> u) & 1u) {
+            if (pos < K) kept[(size_t)t * K + pos] = i0 + u;  // exactly K are taken; never write past K
+            ++pos;
+        }
     (void)lane;
 }
 
@@ -285,19 +329,46 @@ chan_gather_kernel(const int32_t* __restrict__ topk_ids, const float* __restrict
     }
 }
 
-// y[t][col] = sum over chunks (ascending) of part[t][chunk][col].
-__global__ void __launch_bounds__(kThreads)
+// y[t][col] = sum over the chunks of part[t][chunk][col].  One wave per
+// workgroup: lane (row group g, float4 column c4); row group g adds chunks
+// g, g + kCombRG, ... in order (a batch of loads issued together), then the
+// row groups are combined by a butterfly over the lane bits above the column
+// bits (xor 4, 8, 16, 32): a fixed order.
+constexpr int kCombCG = 4;
+constexpr int kCombRG = MOE_WAVE / kCombCG;
+constexpr int kCombBatch = 8;
+
+__global__ void __launch_bounds__(MOE_WAVE)
 chan_combine_kernel(int H, int nchunks, const float* __restrict__ part, float* __restrict__ y) {
     const int t = blockIdx.y;
-    const int col = (blockIdx.x * kThreads + threadIdx.x) * 4;
-    if (col >= H) return;
+    const int lane = threadIdx.x;
+    const int cg = lane % kCombCG;
+    const int rg = lane / kCombCG;
+    const int col = (blockIdx.x * kCombCG + cg) * 4;
     float4 acc = make_float4(0.f, 0.f, 0.f, 0.f);
-    const float* src = part + (size_t)t * nchunks * H + col;
-    for (int c = 0; c < nchunks; ++c) {
-        const float4 v = *reinterpret_cast<const float4*>(src + (size_t)c * H);
-        acc.x += v.x; acc.y += v.y; acc.z += v.z; acc.w += v.w;
+    const float* src = part + (size_t)t * nchunks * H + min(col, H - 4);
+    for (int c0 = rg; c0 < nchunks; c0 += kCombBatch * kCombRG) {
+        float4 v[kCombBatch];
+#pragma unroll
+        for (int u = 0; u < kCombBatch; ++u)
+            v[u] = *reinterpret_cast<const float4*>(src + (size_t)min(c0 + u * kCombRG, nchunks - 1) * H);
+#pragma unroll
+        for (int u = 0; u < kCombBatch; ++u) {
+            const bool use = c0 + u * kCombRG < nchunks;
+            acc.x += use ? v[u].x : 0.f;
+            acc.y += use ? v[u].y : 0.f;
+            acc.z += use ? v[u].z : 0.f;
+            acc.w += use ? v[u].w : 0.f;
+        }
     }
-    *reinterpret_cast<float4*>(y + (size_t)t * H + col) = acc;
+#pragma unroll
+    for (int m = kCombCG; m < MOE_WAVE; m <<= 1) {
+        acc.x += __shfl_xor(acc.x, m, MOE_WAVE);
+        acc.y += __shfl_xor(acc.y, m, MOE_WAVE);
+        acc.z += __shfl_xor(acc.z, m, MOE_WAVE);
+        acc.w += __shfl_xor(acc.w, m, MOE_WAVE);
+    }
+    if (rg == 0 && col < H) *reinterpret_cast<float4*>(y + (size_t)t * H + col) = acc;
 }
 
 // One wave per channel: fp64 sums of squares of the gate row, up row and
@@ -352,12 +423,13 @@ hipError_t gather_q(const int32_t* topk_ids, const float* topk_w, const int32_t*
 
 }  // namespace
 
-size_t chan_select_lds_bytes(int n) { return (size_t)n * (sizeof(float) + 2); }
+size_t chan_select_lds_bytes(int n) { return (size_t)n; }
 
 hipError_t launch_chan_select(const int32_t* topk_ids, const float* topk_w, const float* norms, int M, int k, int I,
                               int E, int K, int32_t* kept, hipStream_t stream) {
-    MOE_LAUNCH(chan_select_kernel, dim3(M), dim3(kThreads), chan_select_lds_bytes(k * I), stream, topk_ids,
-                       topk_w, norms, k, I, E, K, kept);
+    if (k * I > kSelThreads * kSelPer) return hipErrorInvalidValue;
+    MOE_LAUNCH(chan_select_kernel, dim3(M), dim3(kSelThreads), chan_select_lds_bytes(k * I), stream, topk_ids,
+                       topk_w, norms, k, I, E, K, FastDiv((uint32_t)I), kept);
     return hipGetLastError();
 }
 
@@ -375,8 +447,8 @@ hipError_t launch_chan_gather(const int32_t* topk_ids, const float* topk_w, cons
 }
 
 hipError_t launch_chan_combine(int M, int H, int nchunks, const float* part, float* y, hipStream_t stream) {
-    const dim3 grid((H / 4 + kThreads - 1) / kThreads, M);
-    MOE_LAUNCH(chan_combine_kernel, grid, dim3(kThreads), 0, stream, H, nchunks, part, y);
+    const dim3 grid((H / 4 + kCombCG - 1) / kCombCG, M);
+    MOE_LAUNCH(chan_combine_kernel, grid, dim3(MOE_WAVE), 0, stream, H, nchunks, part, y);
     return hipGetLastError();
 }
 

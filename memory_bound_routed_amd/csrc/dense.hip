@@ -482,23 +482,24 @@ down_kernel(PlanArgs plan, int H, int I, int nchunk, const uint16_t* __restrict_
 
 // ---------------------------------------------------------------------------
 // y[t][col] = sum over the valid routes s of token t and the chunks c of
-// part[t*k+s][c][col].  Workgroup (column block, t): kCombCG float4 column
-// groups x kCombRG row groups; row group g adds rows g, g+kCombRG, ...
-// (row = s*nchunk + c) in order -- their loads are issued together -- then
-// the row groups are added pairwise in LDS.  Routes with an id outside
-// [0, E) have no partial and add nothing.
-constexpr int kCombRG = 64;
-constexpr int kCombCG = kThreads / kCombRG;
-constexpr int kCombBatch = 8;
+// part[t*k+s][c][col].  One wave per workgroup (column block, t): lane
+// (row group g, float4 column c4), kCombCG column groups x kCombRG row
+// groups.  Row group g adds rows g, g + kCombRG, ... (row = s*nchunk + c) in
+// order -- every load of a batch issued before the first add -- then the row
+// groups are combined by a butterfly over the lane bits above the column
+// bits (xor 4, 8, 16, 32: a fixed order).  No LDS, no barrier.  Routes with
+// an id outside [0, E) have no partial and add nothing.
+constexpr int kCombCG = 4;
+constexpr int kCombRG = MOE_WAVE / kCombCG;
+constexpr int kCombBatch = 16;
 
-__global__ void __launch_bounds__(kThreads)
+__global__ void __launch_bounds__(MOE_WAVE)
 combine_kernel(const int32_t* __restrict__ topk_ids, int M, int k, int E, int H, int nchunk,
-               const float* __restrict__ part, float* __restrict__ y) {
-    __shared__ float4 red[kCombRG][kCombCG];
+               const float* __restrict__ part, float* __restrict__ y, FastDiv fchunk) {
     const int t = blockIdx.y;
-    const int tid = threadIdx.x;
-    const int cg = tid % kCombCG;
-    const int rg = tid / kCombCG;
+    const int lane = threadIdx.x;
+    const int cg = lane % kCombCG;
+    const int rg = lane / kCombCG;
     const int col = (blockIdx.x * kCombCG + cg) * 4;
     const int rows = k * nchunk;
     float4 acc = make_float4(0.f, 0.f, 0.f, 0.f);
@@ -513,29 +514,25 @@ combine_kernel(const int32_t* __restrict__ topk_ids, int M, int k, int E, int H,
         for (int u = 0; u < kCombBatch; ++u) {
             const int rr = min(row0 + u * kCombRG, rows - 1);
             v[u] = *reinterpret_cast<const float4*>(src + (size_t)rr * H);
-            e[u] = topk_ids[(size_t)t * k + rr / nchunk];
+            e[u] = topk_ids[(size_t)t * k + fchunk.div(rr)];
         }
 #pragma unroll
         for (int u = 0; u < kCombBatch; ++u) {
-            const bool use = col < H && row0 + u * kCombRG < rows && e[u] >= 0 && e[u] < E;
+            const bool use = row0 + u * kCombRG < rows && e[u] >= 0 && e[u] < E;
             acc.x += use ? v[u].x : 0.f;
             acc.y += use ? v[u].y : 0.f;
             acc.z += use ? v[u].z : 0.f;
             acc.w += use ? v[u].w : 0.f;
         }
     }
-    red[rg][cg] = acc;
-    __syncthreads();
-    for (int half = kCombRG / 2; half > 0; half >>= 1) {
-        if (rg < half) {
-            const float4 o = red[rg + half][cg];
-            float4 a = red[rg][cg];
-            a.x += o.x; a.y += o.y; a.z += o.z; a.w += o.w;
-            red[rg][cg] = a;
-        }
-        __syncthreads();
+#pragma unroll
+    for (int m = kCombCG; m < MOE_WAVE; m <<= 1) {
+        acc.x += __shfl_xor(acc.x, m, MOE_WAVE);
+        acc.y += __shfl_xor(acc.y, m, MOE_WAVE);
+        acc.z += __shfl_xor(acc.z, m, MOE_WAVE);
+        acc.w += __shfl_xor(acc.w, m, MOE_WAVE);
     }
-    if (rg == 0 && col < H) *reinterpret_cast<float4*>(y + (size_t)t * H + col) = red[0][cg];
+    if (rg == 0 && col < H) *reinterpret_cast<float4*>(y + (size_t)t * H + col) = acc;
 }
 
 template <int Q, int CPW>
@@ -652,7 +649,8 @@ hipError_t launch_down(const PlanArgs& plan, int H, int I, const uint16_t* Wd, c
 hipError_t launch_combine(const int32_t* topk_ids, int M, int k, int E, int H, int nchunk, const float* part, float* y,
                           hipStream_t stream) {
     const dim3 grid((H / 4 + kCombCG - 1) / kCombCG, M);
-    MOE_LAUNCH(combine_kernel, grid, dim3(kThreads), 0, stream, topk_ids, M, k, E, H, nchunk, part, y);
+    MOE_LAUNCH(combine_kernel, grid, dim3(MOE_WAVE), 0, stream, topk_ids, M, k, E, H, nchunk, part, y,
+               FastDiv((uint32_t)nchunk));
     return hipGetLastError();
 }
 
