@@ -154,8 +154,10 @@ void moe_destroy(moe_ctx *ctx);
  * Each logit is an fp32 sum whose summation tree has depth at most
  * 4 + rpp + ceil(H / (4 rpp)) + 1 with rpp = floor(2048 / E), so
  * |l - exact| <= gamma_depth * (sum_i |h_i Wr_ie| + |bias_e|).  The top-k
- * decision is exact for these fp32 logits.  One launch; the last workgroup
- * to finish reduces the row slices (an integer ticket, no spinning).
+ * decision is exact for these fp32 logits.  Up to 4 tokens: one launch, the
+ * last workgroup to finish reduces the row slices (an integer ticket, no
+ * spinning).  More tokens: two launches (the row slices, then one workgroup
+ * per token), with the same arithmetic and summation order.
  */
 moe_status moe_route_topk(moe_ctx *ctx, const float *h, int32_t M,
                           int32_t *topk_ids, float *topk_w, float *logits_out, void *stream);
@@ -179,9 +181,9 @@ moe_status moe_align_blocks(moe_ctx *ctx, const int32_t *topk_ids, int32_t M,
                             void *stream);
 
 /*
- * moe_route_topk followed by moe_align_blocks, in one launch: the last
- * workgroup of the router aligns the ids it has just written.  Outputs are
- * identical to the two separate calls (same arguments, same meaning).
+ * moe_route_topk followed by moe_align_blocks, the alignment done by the
+ * router's last workgroup (one launch up to 4 tokens, two above).  Outputs
+ * are identical to the two separate calls (same arguments, same meaning).
  */
 moe_status moe_route_align(moe_ctx *ctx, const float *h, int32_t M, int32_t *topk_ids, float *topk_w,
                            float *logits_out, int32_t *sorted_routes, int32_t *block_expert, int32_t *counts,
@@ -279,7 +281,9 @@ enum {
     MOE_KERNEL_CHAN_COMBINE = 9,
     MOE_KERNEL_EXPERT_FUSED = 10, /* dense gate/up + SiLU + down partials (one route per block) */
     MOE_KERNEL_ROUTER_ALIGN = 11, /* router + top-k + softmax + alignment (one launch) */
-    MOE_KERNEL_COUNT = 12
+    MOE_KERNEL_ROUTER_SLICES = 12, /* router GEMV slice partials (batches above 4 tokens) */
+    MOE_KERNEL_ROUTER_TOKENS = 13, /* per-token top-k + softmax (+ alignment) (batches above 4 tokens) */
+    MOE_KERNEL_COUNT = 14
 };
 
 /*

@@ -23,7 +23,7 @@ align_kernel(const int32_t* __restrict__ topk_ids, int R, int E, int b, int32_t*
             align_wave([&](int r) { return topk_ids[r]; }, R, E, fb, sorted_routes, block_expert, counts, err);
         return;
     }
-    align_workgroup(topk_ids, R, E, b, sorted_routes, block_expert, counts, err, smem);
+    align_workgroup([&](int r) { return topk_ids[r]; }, R, E, b, sorted_routes, block_expert, counts, err, smem);
 }
 
 }  // namespace

@@ -24,7 +24,9 @@ __host__ __device__ inline size_t align_lds_bytes_inline(int R, int E) {
 }
 
 // Run by all 256 threads of one workgroup; smem holds align_lds_bytes(R, E) bytes.
-__device__ inline void align_workgroup(const int32_t* __restrict__ topk_ids, int R, int E, int b,
+// id_of(r) returns route r's id.
+template <typename IdOf>
+__device__ inline void align_workgroup(IdOf id_of, int R, int E, int b,
                                 int32_t* __restrict__ sorted_routes, int32_t* __restrict__ block_expert,
                                 int32_t* __restrict__ counts, int32_t* __restrict__ err, int* smem) {
     const int nchunk = (R + MOE_WAVE - 1) / MOE_WAVE;
@@ -42,7 +44,7 @@ __device__ inline void align_workgroup(const int32_t* __restrict__ topk_ids, int
     if (tid == 0) bad = 0;
     __syncthreads();
     for (int r = tid; r < R; r += kAlignThreads) {
-        const int id = topk_ids[r];
+        const int id = id_of(r);
         const bool ok = id >= 0 && id < E;
         sid[r] = ok ? id : -1;
         if (!ok) bad = 1;

@@ -89,6 +89,12 @@ __device__ __forceinline__ void store_agent(float* p, float v) {
 __device__ __forceinline__ float load_agent(const float* p) {
     return __hip_atomic_load(const_cast<float*>(p), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
+__device__ __forceinline__ void store_agent(int32_t* p, int32_t v) {
+    __hip_atomic_store(p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+__device__ __forceinline__ int32_t load_agent(const int32_t* p) {
+    return __hip_atomic_load(const_cast<int32_t*>(p), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
 
 // Quotient and remainder by a divisor fixed at launch, by multiply-high
 // (Granlund and Montgomery, "Division by Invariant Integers using

@@ -18,6 +18,7 @@ namespace {
 
 constexpr int kThreads = 256;
 constexpr int kTokTile = 4;
+constexpr int kHStage = 2048;  // floats of h staged in LDS per token stage (batches of several tokens)
 constexpr int kRowsPerThread = 4;
 constexpr int kMaxJobs = 3;
 constexpr int kMaxExpertsPerLane = 16;  // E <= 1024
@@ -46,21 +47,44 @@ __device__ __forceinline__ void slice_partial(const float* __restrict__ h, int M
     const int slice_rows = rpp * kRowsPerThread;
     const int r0 = slice * slice_rows;
 
-    for (int t0 = 0; t0 < M; t0 += TT) {
-        const int nt = min(TT, M - t0);
+    // The thread's weight rows are loaded once and reused for every token
+    // pass.  Every load is issued before the first use: rows past H read row
+    // H-1 and tokens past M read token M-1, and both are zeroed by a select
+    // afterwards (no load sits in a branch, which would make the compiler
+    // wait for it before the next one).
+    uint4 wv[kRowsPerThread];
+    if (active) {
+#pragma unroll
+        for (int u = 0; u < kRowsPerThread; ++u) {
+            const int i = min(r0 + rg + u * rpp, H - 1);
+            wv[u] = load_stream16(W + (size_t)i * N + col8 * 8);
+        }
+    }
+    // Several tokens: the slice's rows of h for a stage of tokens go to LDS
+    // in one round (one memory round trip per stage instead of one per pass).
+    __shared__ float hst[kHStage];
+    const int stage_tokens = TT == 1 ? 1 : max(1, kHStage / slice_rows);
+    for (int tc = 0; tc < M; tc += stage_tokens) {
+      const int ntc = min(stage_tokens, M - tc);
+      if (TT > 1) {
+        __syncthreads();  // the previous stage is no longer read
+        for (int idx = tid; idx < ntc * slice_rows; idx += kThreads) {
+            const int t = idx / slice_rows, i = idx - t * slice_rows;
+            hst[idx] = r0 + i < H ? h[(size_t)(tc + t) * H + r0 + i] : 0.f;
+        }
+        __syncthreads();
+      }
+      for (int t0 = tc; t0 < tc + ntc; t0 += TT) {
+        const int nt = min(TT, tc + ntc - t0);
         if (active) {
-            // Every load of the pass is issued before the first use: rows past
-            // H read row H-1 and tokens past M read token M-1, and both are
-            // zeroed by a select afterwards (no load sits in a branch, which
-            // would make the compiler wait for it before the next one).
-            uint4 wv[kRowsPerThread];
             float hv[kRowsPerThread][TT];
 #pragma unroll
             for (int u = 0; u < kRowsPerThread; ++u) {
                 const int i = min(r0 + rg + u * rpp, H - 1);
-                wv[u] = load_stream16(W + (size_t)i * N + col8 * 8);
 #pragma unroll
-                for (int t = 0; t < TT; ++t) hv[u][t] = h[(size_t)(t0 + min(t, nt - 1)) * H + i];
+                for (int t = 0; t < TT; ++t)
+                    hv[u][t] = TT == 1 ? h[(size_t)t0 * H + i]
+                                       : hst[(t0 - tc + min(t, nt - 1)) * slice_rows + min(rg + u * rpp, slice_rows - 1)];
             }
 #pragma unroll
             for (int u = 0; u < kRowsPerThread; ++u) {
@@ -100,6 +124,7 @@ __device__ __forceinline__ void slice_partial(const float* __restrict__ h, int M
                 *dst = s;
         }
         __syncthreads();
+      }
     }
 }
 
@@ -167,6 +192,78 @@ __device__ __forceinline__ int count_greater(const uint64_t* row, int j0, int n,
     return c;
 }
 
+// Slice sum, top-k and softmax of the nt tokens t0 .. t0+nt-1 (nt <= kTokTile)
+// by one workgroup.  LDS: keys [nt][E], then the half-row rank counts
+// [2][nt][E].  COHERENT: the slice partials were written by other workgroups
+// of this launch.  COHERENT_IDS: ids and weights are read back by another
+// workgroup of this launch.  Ends without a barrier.
+template <bool COHERENT, bool COHERENT_IDS>
+__device__ __forceinline__ void topk_pass(int t0, int nt, int M, int E, int k, int nslices,
+                                          const float* __restrict__ part, const float* __restrict__ bias,
+                                          float* __restrict__ logits_out, int32_t* __restrict__ ids,
+                                          float* __restrict__ wts, float* red, TopkLds& sel, FastDiv fE) {
+    const int tid = threadIdx.x;
+    const int wave = tid / MOE_WAVE;
+    const int lane = tid % MOE_WAVE;
+    uint64_t* skey = reinterpret_cast<uint64_t*>(red);
+    int* prank = reinterpret_cast<int*>(skey + nt * E);
+    const int halfE = E / 2;  // E % 8 == 0: each half is a whole number of 16-byte key pairs
+    for (int pr = tid; pr < nt * E; pr += kThreads) {
+        const int tq = fE.div(pr);
+        const int t = t0 + tq, e = pr - tq * E;
+        const float bv = bias ? bias[e] : 0.f;  // issued with the slice loads
+        float s = 0.f;
+        for (int sl0 = 0; sl0 < nslices; sl0 += kSliceBatch) {
+            float x[kSliceBatch];
+#pragma unroll
+            for (int u = 0; u < kSliceBatch; ++u) {
+                const float* q = part + ((size_t)min(sl0 + u, nslices - 1) * M + t) * E + e;
+                x[u] = COHERENT ? load_agent(q) : *q;
+            }
+#pragma unroll
+            for (int u = 0; u < kSliceBatch; ++u) s += sl0 + u < nslices ? x[u] : 0.f;  // slice order
+        }
+        if (bias) s += bv;
+        if (logits_out) logits_out[(size_t)t * E + e] = s;
+        skey[pr] = order_key((s != s) ? -INFINITY : s, e);
+    }
+    __syncthreads();
+    // rank = # keys of the token above the expert's key, counted in two halves
+    for (int it = tid; it < 2 * nt * E; it += kThreads) {
+        const int half = it >= nt * E ? 1 : 0, pr = it - half * nt * E;
+        const int tl = fE.div(pr);
+        prank[it] = count_greater(skey + tl * E, half * halfE, halfE, skey[pr]);
+    }
+    __syncthreads();
+    for (int pr = tid; pr < nt * E; pr += kThreads) {
+        const int rank = prank[pr] + prank[nt * E + pr];
+        if (rank < k) {
+            const int tl = fE.div(pr);
+            const uint64_t key = skey[pr];
+            const uint32_t hi = (uint32_t)(key >> 32);
+            sel.e[tl][rank] = (int)~(uint32_t)key;
+            sel.l[tl][rank] = __uint_as_float((hi & 0x80000000u) ? (hi & 0x7FFFFFFFu) : ~hi);
+        }
+    }
+    __syncthreads();
+    if (wave < nt) {  // wave w: token t0 + w; lane s: slot s
+        const int t = t0 + wave;
+        const float l0 = sel.l[wave][0];
+        const float x = lane < k ? expf(sel.l[wave][lane] - l0) : 0.f;
+        float den = 0.f;
+        for (int s = 0; s < k; ++s) den += __int_as_float(__builtin_amdgcn_readlane(__float_as_int(x), s));
+        if (lane < k) {
+            if (COHERENT_IDS) {
+                store_agent(ids + (size_t)t * k + lane, sel.e[wave][lane]);
+                store_agent(wts + (size_t)t * k + lane, x / den);
+            } else {
+                ids[(size_t)t * k + lane] = sel.e[wave][lane];
+                wts[(size_t)t * k + lane] = x / den;
+            }
+        }
+    }
+}
+
 // Returns true in the last workgroup (which has written ids and weights; the
 // selections of the last pass stay in sel).
 template <int TT>
@@ -183,67 +280,11 @@ __device__ __forceinline__ bool router_body(const float* __restrict__ h, int M, 
     if (threadIdx.x == 0) s_last = atomicAdd(ticket, 1u) == (unsigned)(nslices - 1);
     __syncthreads();
     if (!s_last) return false;
-
-    const int tid = threadIdx.x;
-    const int wave = tid / MOE_WAVE;
-    const int lane = tid % MOE_WAVE;
-    // LDS of the pass (red holds router_lds_bytes): keys [TT][E], then the
-    // half-row rank counts [2][TT][E]
-    uint64_t* skey = reinterpret_cast<uint64_t*>(red);
-    int* prank = reinterpret_cast<int*>(skey + TT * E);
-    const int halfE = E / 2;  // E % 8 == 0: each half is a whole number of 16-byte key pairs
     for (int t0 = 0; t0 < M; t0 += TT) {
-        const int nt = min(TT, M - t0);
-        for (int pr = tid; pr < nt * E; pr += kThreads) {
-            const int tq = fE.div(pr);
-            const int t = t0 + tq, e = pr - tq * E;
-            const float bv = bias ? bias[e] : 0.f;  // issued with the slice loads
-            float s = 0.f;
-            for (int sl0 = 0; sl0 < nslices; sl0 += kSliceBatch) {
-                float x[kSliceBatch];
-#pragma unroll
-                for (int u = 0; u < kSliceBatch; ++u)
-                    x[u] = load_agent(part + ((size_t)min(sl0 + u, nslices - 1) * M + t) * E + e);
-#pragma unroll
-                for (int u = 0; u < kSliceBatch; ++u) s += sl0 + u < nslices ? x[u] : 0.f;  // slice order
-            }
-            if (bias) s += bv;
-            if (logits_out) logits_out[(size_t)t * E + e] = s;
-            skey[pr] = order_key((s != s) ? -INFINITY : s, e);
-        }
-        __syncthreads();
-        // rank = # keys of the token above the expert's key, counted in two halves
-        for (int it = tid; it < 2 * nt * E; it += kThreads) {
-            const int half = it >= nt * E ? 1 : 0, pr = it - half * nt * E;
-            const int tl = fE.div(pr);
-            prank[it] = count_greater(skey + tl * E, half * halfE, halfE, skey[pr]);
-        }
-        __syncthreads();
-        for (int pr = tid; pr < nt * E; pr += kThreads) {
-            const int rank = prank[pr] + prank[nt * E + pr];
-            if (rank < k) {
-                const int tl = fE.div(pr);
-                const uint64_t key = skey[pr];
-                const uint32_t hi = (uint32_t)(key >> 32);
-                sel.e[tl][rank] = (int)~(uint32_t)key;
-                sel.l[tl][rank] = __uint_as_float((hi & 0x80000000u) ? (hi & 0x7FFFFFFFu) : ~hi);
-            }
-        }
-        __syncthreads();
-        if (wave < nt) {  // wave w: token t0 + w; lane s: slot s
-            const int t = t0 + wave;
-            const float l0 = sel.l[wave][0];
-            const float x = lane < k ? expf(sel.l[wave][lane] - l0) : 0.f;
-            float den = 0.f;
-            for (int s = 0; s < k; ++s) den += __int_as_float(__builtin_amdgcn_readlane(__float_as_int(x), s));
-            if (lane < k) {
-                ids[(size_t)t * k + lane] = sel.e[wave][lane];
-                wts[(size_t)t * k + lane] = x / den;
-            }
-        }
+        topk_pass<true, false>(t0, min(TT, M - t0), M, E, k, nslices, part, bias, logits_out, ids, wts, red, sel, fE);
         if (t0 + TT < M) __syncthreads();  // sel and the keys are reused by the next pass
     }
-    if (tid == 0) atomicExch(ticket, 0u);  // ready for the next call on this context
+    if (threadIdx.x == 0) atomicExch(ticket, 0u);  // ready for the next call on this context
     return true;
 }
 
@@ -290,7 +331,42 @@ router_align_kernel(const float* __restrict__ h, int M, int H, const uint16_t* _
         return;
     }
     __syncthreads();
-    align_workgroup(ids, R, E, b, sorted_routes, block_expert, counts, err, reinterpret_cast<int*>(red));
+    align_workgroup([&](int r) { return ids[r]; }, R, E, b, sorted_routes, block_expert, counts, err,
+                    reinterpret_cast<int*>(red));
+}
+
+// Batches of more than kTokTile tokens: the slice partials come from
+// gemv_partials_kernel (previous launch); here one workgroup per token sums
+// them, takes the top-k and the softmax (same arithmetic and order as the
+// one-launch router).  ALIGN: every workgroup publishes its ids device-
+// coherently and takes a ticket once its stores have completed; the last one
+// aligns all M*k routes, reading the ids device-coherently.
+template <bool ALIGN>
+__global__ void __launch_bounds__(kThreads)
+router_tokens_kernel(int M, int E, const float* __restrict__ bias, int k, int nslices, const float* __restrict__ part,
+                     unsigned* __restrict__ ticket, int32_t* __restrict__ ids, float* __restrict__ wts,
+                     float* __restrict__ logits_out, int b, int32_t* __restrict__ sorted_routes,
+                     int32_t* __restrict__ block_expert, int32_t* __restrict__ counts, int32_t* __restrict__ err,
+                     FastDiv fE, FastDiv fb) {
+    extern __shared__ __align__(16) float red[];
+    __shared__ TopkLds sel;
+    __shared__ int s_last;
+    topk_pass<false, ALIGN>(blockIdx.x, 1, M, E, k, nslices, part, bias, logits_out, ids, wts, red, sel, fE);
+    if (!ALIGN) return;
+    __builtin_amdgcn_s_waitcnt(0);  // this wave's id and weight stores have completed
+    __syncthreads();
+    if (threadIdx.x == 0) s_last = atomicAdd(ticket, 1u) == (unsigned)(M - 1);
+    __syncthreads();
+    if (!s_last) return;
+    const int R = M * k;
+    if (R <= MOE_WAVE) {
+        if (threadIdx.x < MOE_WAVE)
+            align_wave([&](int r) { return load_agent(ids + r); }, R, E, fb, sorted_routes, block_expert, counts, err);
+    } else {
+        align_workgroup([&](int r) { return load_agent(ids + r); }, R, E, b, sorted_routes, block_expert, counts,
+                        err, reinterpret_cast<int*>(red));
+    }
+    if (threadIdx.x == 0) atomicExch(ticket, 0u);  // ready for the next call on this context
 }
 
 size_t lds_bytes(int N) { return (size_t)(kThreads / (N / 8)) * kTokTile * N * sizeof(float); }
@@ -332,6 +408,24 @@ hipError_t launch_router_align(const float* h, int M, int H, const uint16_t* Wr,
     MOE_LAUNCH(router_align_kernel, dim3(gemv_slices(H, E)), dim3(kThreads), lds, stream, h, M, H, Wr, E, bias,
                        k, part, ticket, ids, wts, logits_out, b, sorted_routes, block_expert, counts, err,
                        FastDiv((uint32_t)E), FastDiv((uint32_t)k), FastDiv((uint32_t)b));
+    return hipGetLastError();
+}
+
+hipError_t launch_router_tokens(int M, int H, int E, const float* bias, int k, const float* part, unsigned* ticket,
+                                int32_t* ids, float* wts, float* logits_out, int b, int32_t* sorted_routes,
+                                int32_t* block_expert, int32_t* counts, int32_t* err, hipStream_t stream) {
+    const size_t topk = (size_t)E * (sizeof(uint64_t) + 2 * sizeof(int));
+    const int nslices = gemv_slices(H, E);
+    if (sorted_routes) {
+        const size_t la = align_lds_bytes(M * k, E);
+        MOE_LAUNCH(router_tokens_kernel<true>, dim3(M), dim3(kThreads), topk > la ? topk : la, stream, M, E, bias, k,
+                   nslices, part, ticket, ids, wts, logits_out, b, sorted_routes, block_expert, counts, err,
+                   FastDiv((uint32_t)E), FastDiv((uint32_t)b));
+    } else {
+        MOE_LAUNCH(router_tokens_kernel<false>, dim3(M), dim3(kThreads), topk, stream, M, E, bias, k, nslices, part,
+                   ticket, ids, wts, logits_out, b, sorted_routes, block_expert, counts, err, FastDiv((uint32_t)E),
+                   FastDiv((uint32_t)1));
+    }
     return hipGetLastError();
 }
 
