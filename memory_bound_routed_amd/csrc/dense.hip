@@ -82,9 +82,10 @@ __device__ __forceinline__ int plan_route(const PlanArgs& plan, int bb, int q, i
 // 8*(t%256 + 256*cq) and accumulates across the chunks; the row groups are
 // added in group order at the end and the workgroup writes one partial
 //     part[route][range][:] = sum_{j in range} (a_route * p_j) * d_j.
-// Every load whose address depends on data (plan rows, route ids, affinity,
-// h) is issued before the weight stream: a load queued behind it would wait
-// for the whole stream to drain.
+// The weight addresses depend only on the block's expert, so the first two
+// chunks are requested right after the plan rows arrive; the route checks,
+// affinities and h (whose addresses depend on the same rows) are issued just
+// before them, since a load queued behind the stream would wait for it.
 template <int Q, int CQ, int NW, int CPW, int NCH, bool FULL>
 __global__ void __launch_bounds__(NW * MOE_WAVE)
 expert_fused_kernel(PlanArgs plan, const float* __restrict__ h, const float* __restrict__ topk_w, int H, int I,
@@ -108,12 +109,13 @@ expert_fused_kernel(PlanArgs plan, const float* __restrict__ h, const float* __r
     const int ct = tid % kThreads;        // down column thread
     const int rgp = tid / kThreads;       // down row group
 
-    // One round of independent loads: counts, this and the previous block's
+    // First round of independent loads: counts, this and the previous block's
     // expert, and the block's rows (lane q holds row q; b <= 64).
     int nb = plan.counts[0];
     const int e = plan.block_expert[blk];
     const int eprev = blk > 0 ? plan.block_expert[blk - 1] : -1;
-    int rv = lane < b ? plan.sorted_routes[(size_t)blk * b + lane] : plan.R;
+    int rv = plan.sorted_routes[(size_t)blk * b + min(lane, b - 1)];
+    if (lane >= b) rv = plan.R;
     if (nb < 0 || nb > plan.max_blocks) {
         if (blk == 0 && range == 0 && tid == 0) atomicOr(err, DEVERR_BAD_COUNTS);
         nb = nb < 0 ? 0 : plan.max_blocks;
@@ -124,15 +126,6 @@ expert_fused_kernel(PlanArgs plan, const float* __restrict__ h, const float* __r
         return;
     }
     if (eprev == e) return;  // not the first block of the expert's run (uniform)
-    // Second round: each row's route id check and affinity.
-    float av = 0.f;
-    {
-        const bool ok = rv >= 0 && rv < plan.R && plan.topk_ids[rv] == e;
-        if (ok) av = topk_w[rv];
-        if (!ok && rv != plan.R && range == 0 && tid < MOE_WAVE) atomicOr(err, DEVERR_BAD_PLAN);
-        if (!ok) rv = -1;
-    }
-    uint64_t todo = __ballot(rv >= 0);  // valid rows of the first block (wave-uniform)
 
     const int cbase = range * NCH * CH;
     const size_t ebase = (size_t)e * I * H;
@@ -143,7 +136,7 @@ expert_fused_kernel(PlanArgs plan, const float* __restrict__ h, const float* __r
     // Rows past I load row 0 of the expert and are multiplied by zero; with
     // FULL (H == 512*Q == 2048*CQ) every column is in range and the loads
     // share one base address with constant offsets.
-    auto issue = [&](int ci, int buf) {
+    auto issue_gu = [&](int ci, int buf) {
         const int j0 = cbase + ci * CH;
 #pragma unroll
         for (int c = 0; c < CPW; ++c) {
@@ -159,6 +152,9 @@ expert_fused_kernel(PlanArgs plan, const float* __restrict__ h, const float* __r
                 }
             }
         }
+    };
+    auto issue_d = [&](int ci, int buf) {
+        const int j0 = cbase + ci * CH;
 #pragma unroll
         for (int rr = 0; rr < RPG; ++rr) {
             const int j = j0 + rgp * RPG + rr;
@@ -173,76 +169,86 @@ expert_fused_kernel(PlanArgs plan, const float* __restrict__ h, const float* __r
         }
     };
 
-    // One route: h to LDS, the chunk loop, the row-group sum and the store.
-    // PIPE double-buffers the weights; the single-buffered copy serves the
-    // rare extra routes (an expert routed more than once by one token), so
-    // that the common single-route path keeps its small register footprint.
-    auto run_route = [&](int r, float a, auto pipe) {
-        constexpr bool PIPE = decltype(pipe)::value;
-        // h of the route into LDS, requested before the weights
-        const float* hr = h + (size_t)(r / plan.k) * H;
-        for (int i = tid; i < Q * MOE_WAVE * 2; i += NT) {
-            const int col = i * 4;
-            hs[i] = col < H ? *reinterpret_cast<const float4*>(hr + col) : make_float4(0.f, 0.f, 0.f, 0.f);
+    // Second round, issued before any weight: every row's id check and
+    // affinity (unconditional loads, the row is in range) and h of row 0,
+    // which is the expert's first route whenever the plan is well formed.
+    // The loads take clamped, always-valid addresses and their values are
+    // selected afterwards: a load inside a branch would be waited for at the
+    // branch's end, one round trip at a time.
+    const bool inr = rv >= 0 && rv < plan.R;
+    const int rc = min(max(rv, 0), plan.R - 1);
+    const int idv0 = plan.topk_ids[rc];
+    const float avv0 = topk_w[rc];
+    const int r0 = __builtin_amdgcn_readfirstlane(rv);
+    const bool spec = r0 >= 0 && r0 < plan.R;  // uniform
+    constexpr int HPT = (Q * MOE_WAVE * 2 + NT - 1) / NT;  // float4 of h per thread
+    float4 hreg[HPT];
+    const float* h0row = h + (size_t)(min(max(r0, 0), plan.R - 1) / plan.k) * H;
+#pragma unroll
+    for (int u = 0; u < HPT; ++u)
+        hreg[u] = *reinterpret_cast<const float4*>(h0row + min((tid + NT * u) * 4, H - 4));
+    // The weight stream of the expert's first route starts now, two chunks deep.
+    issue_gu(0, 0);
+    issue_d(0, 0);
+    if (NCH > 1) {
+        issue_gu(1, 1);
+        issue_d(1, 1);
+    }
+    const bool ok = inr && idv0 == e;
+    if (!ok && rv != plan.R && range == 0 && tid < MOE_WAVE) atomicOr(err, DEVERR_BAD_PLAN);
+    if (!ok) rv = -1;
+    const float av = ok ? avv0 : 0.f;
+    uint64_t todo = __ballot(rv >= 0);  // valid rows of the first block (wave-uniform)
+
+    // Gate/up of one chunk from h in LDS: sp[c] = a * SiLU(g_j) * u_j.
+    auto gateup = [&](int ci, int buf, float a) {
+        const int j0 = cbase + ci * CH;
+        float ag[CPW], au[CPW];
+#pragma unroll
+        for (int c = 0; c < CPW; ++c) ag[c] = au[c] = 0.f;
+#pragma unroll
+        for (int q = 0; q < Q; ++q) {
+            if (!FULL && (lane + MOE_WAVE * q) * 8 >= H) continue;
+            const float4 h0 = hs[(lane + MOE_WAVE * q) * 2];
+            const float4 h1 = hs[(lane + MOE_WAVE * q) * 2 + 1];
+            const float hv[8] = {h0.x, h0.y, h0.z, h0.w, h1.x, h1.y, h1.z, h1.w};
+#pragma unroll
+            for (int c = 0; c < CPW; ++c) {
+                float gf[8], uf[8];
+                unpack8(wg[buf][c][q], gf);
+                unpack8(wu[buf][c][q], uf);
+#pragma unroll
+                for (int x = 0; x < 8; ++x) {
+                    ag[c] = fmaf(gf[x], hv[x], ag[c]);
+                    au[c] = fmaf(uf[x], hv[x], au[c]);
+                }
+            }
         }
-        float acc[CQ][8];
+#pragma unroll
+        for (int c = 0; c < CPW; ++c) {
+            const float g = wave_sum(ag[c]);
+            const float u = wave_sum(au[c]);
+            const int j = j0 + wave * CPW + c;
+            if (lane == 0) sp[wave * CPW + c] = j < I ? a * silu_mul(g, u) : 0.f;
+        }
+    };
+    // Down rows of one chunk scaled by sp, accumulated per column thread.
+    auto down = [&](int buf, float (&acc)[CQ][8]) {
 #pragma unroll
         for (int cq = 0; cq < CQ; ++cq)
 #pragma unroll
-            for (int x = 0; x < 8; ++x) acc[cq][x] = 0.f;
-        if (PIPE) issue(0, 0);
-        __syncthreads();  // hs ready
+            for (int rr = 0; rr < RPG; ++rr) {
+                float wf[8];
+                unpack8(wd[buf][rr][cq], wf);
+                const float s = sp[rgp * RPG + rr];
 #pragma unroll
-        for (int ci = 0; ci < NCH; ++ci) {
-            const int buf = PIPE ? (ci & 1) : 0;
-            if (PIPE) {
-                if (ci + 1 < NCH) issue(ci + 1, buf ^ 1);
-            } else {
-                issue(ci, 0);
+                for (int x = 0; x < 8; ++x) acc[cq][x] = fmaf(s, wf[x], acc[cq][x]);
             }
-            const int j0 = cbase + ci * CH;
-            float ag[CPW], au[CPW];
-#pragma unroll
-            for (int c = 0; c < CPW; ++c) ag[c] = au[c] = 0.f;
-#pragma unroll
-            for (int q = 0; q < Q; ++q) {
-                if (!FULL && (lane + MOE_WAVE * q) * 8 >= H) continue;
-                const float4 h0 = hs[(lane + MOE_WAVE * q) * 2];
-                const float4 h1 = hs[(lane + MOE_WAVE * q) * 2 + 1];
-                const float hv[8] = {h0.x, h0.y, h0.z, h0.w, h1.x, h1.y, h1.z, h1.w};
-#pragma unroll
-                for (int c = 0; c < CPW; ++c) {
-                    float gf[8], uf[8];
-                    unpack8(wg[buf][c][q], gf);
-                    unpack8(wu[buf][c][q], uf);
-#pragma unroll
-                    for (int x = 0; x < 8; ++x) {
-                        ag[c] = fmaf(gf[x], hv[x], ag[c]);
-                        au[c] = fmaf(uf[x], hv[x], au[c]);
-                    }
-                }
-            }
-#pragma unroll
-            for (int c = 0; c < CPW; ++c) {
-                const float g = wave_sum(ag[c]);
-                const float u = wave_sum(au[c]);
-                const int j = j0 + wave * CPW + c;
-                if (lane == 0) sp[wave * CPW + c] = j < I ? a * silu_mul(g, u) : 0.f;
-            }
-            __syncthreads();
-#pragma unroll
-            for (int cq = 0; cq < CQ; ++cq)
-#pragma unroll
-                for (int rr = 0; rr < RPG; ++rr) {
-                    float wf[8];
-                    unpack8(wd[buf][rr][cq], wf);
-                    const float s = sp[rgp * RPG + rr];
-#pragma unroll
-                    for (int x = 0; x < 8; ++x) acc[cq][x] = fmaf(s, wf[x], acc[cq][x]);
-                }
-            __syncthreads();
-        }
-        if (RG > 1) {  // row groups 1.. hand their sums to row group 0, added in group order
+    };
+    // Row groups 1.. hand their sums to row group 0 (added in group order),
+    // which writes part[route][range][:].
+    auto finish = [&](int r, float (&acc)[CQ][8]) {
+        if (RG > 1) {
             if (rgp > 0) {
 #pragma unroll
                 for (int cq = 0; cq < CQ; ++cq) {
@@ -277,16 +283,41 @@ expert_fused_kernel(PlanArgs plan, const float* __restrict__ h, const float* __r
         __syncthreads();  // red and hs are reused by the next route
     };
 
-    if (todo) {  // the first valid row of the block (every valid block has one)
-        const int q = __builtin_ctzll(todo);
-        todo &= todo - 1;
-        run_route(__builtin_amdgcn_readlane(rv, q),
-                  __int_as_float(__builtin_amdgcn_readlane(__float_as_int(av), q)), std::integral_constant<bool, true>{});
+    if (spec && (todo & 1ull)) {
+        // Row 0 is the first route: its h and the first two chunks are in
+        // flight.  Chunk ci+2 refills buffer ci&1 as soon as chunk ci's gate/up
+        // (then down) rows have been consumed.
+        todo &= ~1ull;
+        const float a = __int_as_float(__builtin_amdgcn_readfirstlane(__float_as_int(av)));
+#pragma unroll
+        for (int u = 0; u < HPT; ++u) {
+            const int i = tid + NT * u;
+            if (i < Q * MOE_WAVE * 2) hs[i] = i * 4 < H ? hreg[u] : make_float4(0.f, 0.f, 0.f, 0.f);
+        }
+        float acc[CQ][8];
+#pragma unroll
+        for (int cq = 0; cq < CQ; ++cq)
+#pragma unroll
+            for (int x = 0; x < 8; ++x) acc[cq][x] = 0.f;
+        __syncthreads();  // hs ready
+#pragma unroll
+        for (int ci = 0; ci < NCH; ++ci) {
+            const int buf = ci & 1;
+            gateup(ci, buf, a);
+            if (ci + 2 < NCH) issue_gu(ci + 2, buf);
+            __syncthreads();
+            down(buf, acc);
+            if (ci + 2 < NCH) issue_d(ci + 2, buf);
+            __syncthreads();
+        }
+        finish(r0, acc);
     }
+    // Every other route (an expert routed more than once by one token, or a
+    // plan whose row 0 is not a route): h to LDS, then the chunks one at a
+    // time, the rows of the first block first, then the following blocks of
+    // the run, resolved row by row.
     int bb = blk + 1, q0 = 0;
     for (;;) {
-        // Further routes: the remaining valid rows of the first block, then
-        // the following blocks of the run, resolved row by row.
         int r;
         float a;
         if (todo) {
@@ -301,7 +332,26 @@ expert_fused_kernel(PlanArgs plan, const float* __restrict__ h, const float* __r
             if (++q0 == b) { ++bb; q0 = 0; }
             if (r < 0) continue;  // uniform
         }
-        run_route(r, a, std::integral_constant<bool, false>{});
+        const float* hr = h + (size_t)(r / plan.k) * H;
+        for (int i = tid; i < Q * MOE_WAVE * 2; i += NT) {
+            const int col = i * 4;
+            hs[i] = col < H ? *reinterpret_cast<const float4*>(hr + col) : make_float4(0.f, 0.f, 0.f, 0.f);
+        }
+        float acc[CQ][8];
+#pragma unroll
+        for (int cq = 0; cq < CQ; ++cq)
+#pragma unroll
+            for (int x = 0; x < 8; ++x) acc[cq][x] = 0.f;
+        __syncthreads();  // hs ready
+        for (int ci = 0; ci < NCH; ++ci) {
+            issue_gu(ci, 0);
+            issue_d(ci, 0);
+            gateup(ci, 0, a);
+            __syncthreads();
+            down(0, acc);
+            __syncthreads();
+        }
+        finish(r, acc);
     }
 }
 
