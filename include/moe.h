@@ -152,12 +152,15 @@ void moe_destroy(moe_ctx *ctx);
  *  topk_w     fp32 [M][k] out: softmax over the k selected logits
  *  logits_out fp32 [M][E] out (may be NULL): l = h Wr + bias, fp32 accumulation
  * Each logit is an fp32 sum whose summation tree has depth at most
- * 4 + rpp + ceil(H / (4 rpp)) + 1 with rpp = floor(2048 / E), so
- * |l - exact| <= gamma_depth * (sum_i |h_i Wr_ie| + |bias_e|).  The top-k
- * decision is exact for these fp32 logits.  Up to 4 tokens: one launch, the
- * last workgroup to finish reduces the row slices (an integer ticket, no
- * spinning).  More tokens: two launches (the row slices, then one workgroup
- * per token), with the same arithmetic and summation order.
+ *   up to 4 tokens:  4 + rpt/8 + 3 + ceil(H / (4 rpt)) + 1, rpt = 2048 / c,
+ *                    c = 32 experts per column group (16 if E < 32, 8 if E < 16)
+ *   more tokens:     4 + rpp + ceil(H / (4 rpp)) + 1, rpp = floor(2048 / E)
+ * so |l - exact| <= gamma_depth * (sum_i |h_i Wr_ie| + |bias_e|).  The top-k
+ * decision is exact for these fp32 logits.  Up to 4 tokens: one launch over
+ * (row slice, column group) tiles; the last workgroup to finish adds the row
+ * slices in order (an integer ticket, no spinning).  More tokens: two
+ * launches (row slices over all experts, then one workgroup per token that
+ * adds them in order).
  */
 moe_status moe_route_topk(moe_ctx *ctx, const float *h, int32_t M,
                           int32_t *topk_ids, float *topk_w, float *logits_out, void *stream);

@@ -122,6 +122,25 @@ template <typename T>
 __device__ __forceinline__ void pin_arg(T& v) {
     asm volatile("" : "+s"(v));
 }
+// Pointer arguments (all of which point to global memory): after the asm the
+// compiler no longer knows the address space and would use FLAT instructions,
+// which also count against the LDS wait counter, so that every LDS wait would
+// wait for outstanding global stores and atomics too.  The pinned value is
+// therefore a global-space pointer.
+template <typename T>
+__device__ __forceinline__ T* pin_global(T* p) {
+    __attribute__((address_space(1))) T* g = (__attribute__((address_space(1))) T*)p;
+    asm volatile("" : "+s"(g));
+    return (T*)g;
+}
+template <typename T>
+__device__ __forceinline__ void pin_arg(T*& p) {
+    p = pin_global(p);
+}
+template <typename T>
+__device__ __forceinline__ void pin_arg(T* __restrict__& p) {
+    p = pin_global(p);
+}
 
 // Make a value wave-uniform (lets the compiler keep it in a scalar register).
 __device__ __forceinline__ int uniform(int v) { return __builtin_amdgcn_readfirstlane(v); }

@@ -141,6 +141,95 @@ gemv_partials_kernel(const float* __restrict__ h, int M, int H, GemvJobs jobs) {
         slice_partial<kTokTile, false>(h, M, H, jb.W, jb.N, blockIdx.x, jb.part, red);
 }
 
+// Router GEMV tiles (batches of up to kTokTile tokens): the grid covers
+// row slices x column groups of cgw experts (32, or 16 / 8 for small E);
+// tpr = cgw/8 threads cover a row of the group with one 16-byte load each,
+// rpt = 256/tpr rows per pass, kRowsPerThread passes per slice.  The rpt row
+// groups of an output are added by 8 lanes (rpt/8 groups each, in order),
+// then by a fixed xor butterfly over the 8 lanes.  A slice partial is then
+// part[slice][t][e] as for slice_partial, but there are cgw/E times fewer
+// slices for the last workgroup to add.
+constexpr int kRouterCG = 32;
+struct RouterTiles {
+    int cgw, tpr, rpt, rows, nrs, ncg;
+    __host__ __device__ RouterTiles(int H, int E) {
+        cgw = E >= 32 ? kRouterCG : (E >= 16 ? 16 : 8);
+        tpr = cgw / 8;
+        rpt = kThreads / tpr;
+        rows = rpt * kRowsPerThread;
+        nrs = (H + rows - 1) / rows;
+        ncg = (E + cgw - 1) / cgw;
+    }
+};
+
+template <int TT>
+__device__ __forceinline__ void router_tile(const float* __restrict__ h, int M, int H, const uint16_t* __restrict__ W,
+                                            int E, const RouterTiles& tl, int rs, int cg, float* __restrict__ part,
+                                            float* red) {
+    const int tid = threadIdx.x;
+    const int c8 = tid % tl.tpr;
+    const int rg = tid / tl.tpr;
+    const int r0 = rs * tl.rows;
+    const int e0 = cg * tl.cgw + c8 * 8;     // first of the thread's 8 experts
+    const int ec = min(e0, E - 8);           // E % 8 == 0: in range
+    // Every load first (rows past H read row H-1, tokens past M token M-1;
+    // both are zeroed by a select afterwards).
+    uint4 wv[kRowsPerThread];
+    float hv[kRowsPerThread][TT];
+#pragma unroll
+    for (int u = 0; u < kRowsPerThread; ++u) {
+        const int i = min(r0 + rg + u * tl.rpt, H - 1);
+        wv[u] = load_stream16(W + (size_t)i * E + ec);
+#pragma unroll
+        for (int t = 0; t < TT; ++t) hv[u][t] = h[(size_t)min(t, M - 1) * H + i];
+    }
+    const bool col_ok = e0 < E;
+#pragma unroll
+    for (int u = 0; u < kRowsPerThread; ++u) {
+        const bool row_ok = col_ok && r0 + rg + u * tl.rpt < H;
+#pragma unroll
+        for (int t = 0; t < TT; ++t) hv[u][t] = (row_ok && t < M) ? hv[u][t] : 0.f;
+    }
+    float acc[TT][8];
+#pragma unroll
+    for (int t = 0; t < TT; ++t)
+#pragma unroll
+        for (int c = 0; c < 8; ++c) acc[t][c] = 0.f;
+#pragma unroll
+    for (int u = 0; u < kRowsPerThread; ++u) {
+        float wf[8];
+        unpack8(wv[u], wf);
+#pragma unroll
+        for (int t = 0; t < TT; ++t)
+#pragma unroll
+            for (int c = 0; c < 8; ++c) acc[t][c] = fmaf(hv[u][t], wf[c], acc[t][c]);
+    }
+#pragma unroll
+    for (int t = 0; t < TT; ++t)
+#pragma unroll
+        for (int c = 0; c < 8; ++c) red[(rg * TT + t) * tl.cgw + c8 * 8 + c] = acc[t][c];
+    __syncthreads();
+    // output o = t*cgw + c: lanes 8o' .. 8o'+7 of a pass (every lane takes part
+    // in the butterfly)
+    const int sub = tid % 8;
+    const int gpl = tl.rpt / 8;  // row groups per lane
+    const int nout = min(M, TT) * tl.cgw;
+    for (int o0 = 0; o0 < nout; o0 += kThreads / 8) {
+        const int o = o0 + tid / 8;
+        const int t = o / tl.cgw, c = o - t * tl.cgw;
+        float v = 0.f;
+        if (o < nout) {
+            const float* src = red + ((size_t)sub * gpl * TT + t) * tl.cgw + c;
+            for (int g = 0; g < gpl; ++g) v += src[(size_t)g * TT * tl.cgw];
+        }
+        v += __shfl_xor(v, 1, MOE_WAVE);
+        v += __shfl_xor(v, 2, MOE_WAVE);
+        v += __shfl_xor(v, 4, MOE_WAVE);
+        const int e = cg * tl.cgw + c;
+        if (sub == 0 && o < nout && e < E) store_agent(part + ((size_t)rs * M + t) * E + e, v);
+    }
+}
+
 // Router: slices as above; the last workgroup to finish (integer ticket)
 // adds the slices in slice order (+ bias) for up to four tokens at a time --
 // every partial load of a pass is issued before the first add.  The top-k is
@@ -155,6 +244,11 @@ gemv_partials_kernel(const float* __restrict__ h, int M, int H, GemvJobs jobs) {
 // completed, one thread per workgroup takes a ticket, and the workgroup
 // holding the last ticket reads every slice.  Nothing waits on another
 // workgroup, and no cache is written back or invalidated.
+// Slice partials requested together per thread: the tiled router has at most
+// a few slices, and its device-coherent loads are served one instruction at
+// a time (so clamped duplicates would cost as much as real slices); the
+// two-launch path reads up to 32 slices with plain loads.
+constexpr int kSliceBatchTiles = 8;
 constexpr int kSliceBatch = 32;
 
 // Selected (expert, logit) of the tokens of the current pass, slot order.
@@ -197,7 +291,7 @@ __device__ __forceinline__ int count_greater(const uint64_t* row, int j0, int n,
 // [2][nt][E].  COHERENT: the slice partials were written by other workgroups
 // of this launch.  COHERENT_IDS: ids and weights are read back by another
 // workgroup of this launch.  Ends without a barrier.
-template <bool COHERENT, bool COHERENT_IDS>
+template <bool COHERENT, bool COHERENT_IDS, int SB>
 __device__ __forceinline__ void topk_pass(int t0, int nt, int M, int E, int k, int nslices,
                                           const float* __restrict__ part, const float* __restrict__ bias,
                                           float* __restrict__ logits_out, int32_t* __restrict__ ids,
@@ -213,15 +307,15 @@ __device__ __forceinline__ void topk_pass(int t0, int nt, int M, int E, int k, i
         const int t = t0 + tq, e = pr - tq * E;
         const float bv = bias ? bias[e] : 0.f;  // issued with the slice loads
         float s = 0.f;
-        for (int sl0 = 0; sl0 < nslices; sl0 += kSliceBatch) {
-            float x[kSliceBatch];
+        for (int sl0 = 0; sl0 < nslices; sl0 += SB) {
+            float x[SB];
 #pragma unroll
-            for (int u = 0; u < kSliceBatch; ++u) {
+            for (int u = 0; u < SB; ++u) {
                 const float* q = part + ((size_t)min(sl0 + u, nslices - 1) * M + t) * E + e;
                 x[u] = COHERENT ? load_agent(q) : *q;
             }
 #pragma unroll
-            for (int u = 0; u < kSliceBatch; ++u) s += sl0 + u < nslices ? x[u] : 0.f;  // slice order
+            for (int u = 0; u < SB; ++u) s += sl0 + u < nslices ? x[u] : 0.f;  // slice order
         }
         if (bias) s += bv;
         if (logits_out) logits_out[(size_t)t * E + e] = s;
@@ -273,19 +367,26 @@ __device__ __forceinline__ bool router_body(const float* __restrict__ h, int M, 
                                             float* __restrict__ wts, float* __restrict__ logits_out, float* red,
                                             TopkLds& sel, FastDiv fE) {
     __shared__ int s_last;
-    const int nslices = gridDim.x;
-    slice_partial<TT, true>(h, M, H, Wr, E, blockIdx.x, part, red);
+    const RouterTiles tl(H, E);
+    const int nslices = tl.nrs;
+    router_tile<TT>(h, M, H, Wr, E, tl, blockIdx.x % tl.nrs, blockIdx.x / tl.nrs, part, red);
     __builtin_amdgcn_s_waitcnt(0);  // this wave's partial stores have completed
     __syncthreads();
-    if (threadIdx.x == 0) s_last = atomicAdd(ticket, 1u) == (unsigned)(nslices - 1);
+    if (threadIdx.x == 0) s_last = atomicAdd(ticket, 1u) == (unsigned)(gridDim.x - 1);
     __syncthreads();
     if (!s_last) return false;
     for (int t0 = 0; t0 < M; t0 += TT) {
-        topk_pass<true, false>(t0, min(TT, M - t0), M, E, k, nslices, part, bias, logits_out, ids, wts, red, sel, fE);
+        topk_pass<true, false, kSliceBatchTiles>(t0, min(TT, M - t0), M, E, k, nslices, part, bias, logits_out, ids,
+                                                 wts, red, sel, fE);
         if (t0 + TT < M) __syncthreads();  // sel and the keys are reused by the next pass
     }
-    if (threadIdx.x == 0) atomicExch(ticket, 0u);  // ready for the next call on this context
     return true;
+}
+
+// The last workgroup re-arms the ticket for the next call on this context, as
+// its final action (no barrier follows, so nothing waits for the atomic).
+__device__ __forceinline__ void rearm_ticket(unsigned* ticket) {
+    if (threadIdx.x == 0) atomicExch(ticket, 0u);
 }
 
 __global__ void __launch_bounds__(kThreads)
@@ -296,10 +397,10 @@ router_kernel(const float* __restrict__ h, int M, int H, const uint16_t* __restr
     __shared__ TopkLds sel;
     pin_arg(bias); pin_arg(k); pin_arg(E); pin_arg(M); pin_arg(ids); pin_arg(wts); pin_arg(logits_out);
     pin_arg(ticket); pin_arg(part); pin_arg(fE.m); pin_arg(fE.s);
-    if (M == 1)
-        router_body<1>(h, M, H, Wr, E, bias, k, part, ticket, ids, wts, logits_out, red, sel, fE);
-    else
-        router_body<kTokTile>(h, M, H, Wr, E, bias, k, part, ticket, ids, wts, logits_out, red, sel, fE);
+    const bool last =
+        M == 1 ? router_body<1>(h, M, H, Wr, E, bias, k, part, ticket, ids, wts, logits_out, red, sel, fE)
+               : router_body<kTokTile>(h, M, H, Wr, E, bias, k, part, ticket, ids, wts, logits_out, red, sel, fE);
+    if (last) rearm_ticket(ticket);
 }
 
 // Router, then the canonical alignment of the ids in the last workgroup.  Up
@@ -324,15 +425,17 @@ router_align_kernel(const float* __restrict__ h, int M, int H, const uint16_t* _
     if (!last) return;
     const int R = M * k;
     if (M <= TT && R <= MOE_WAVE) {
-        __syncthreads();
+        // sel was complete at the top-k's last barrier and is only read since
         if (threadIdx.x < MOE_WAVE)
             align_wave([&](int r) { const int t = fk.div(r); return sel.e[t][r - t * k]; }, R, E, fb, sorted_routes,
                        block_expert, counts, err);
+        rearm_ticket(ticket);
         return;
     }
     __syncthreads();
     align_workgroup([&](int r) { return ids[r]; }, R, E, b, sorted_routes, block_expert, counts, err,
                     reinterpret_cast<int*>(red));
+    rearm_ticket(ticket);
 }
 
 // Batches of more than kTokTile tokens: the slice partials come from
@@ -351,7 +454,8 @@ router_tokens_kernel(int M, int E, const float* __restrict__ bias, int k, int ns
     extern __shared__ __align__(16) float red[];
     __shared__ TopkLds sel;
     __shared__ int s_last;
-    topk_pass<false, ALIGN>(blockIdx.x, 1, M, E, k, nslices, part, bias, logits_out, ids, wts, red, sel, fE);
+    topk_pass<false, ALIGN, kSliceBatch>(blockIdx.x, 1, M, E, k, nslices, part, bias, logits_out, ids, wts, red, sel,
+                                         fE);
     if (!ALIGN) return;
     __builtin_amdgcn_s_waitcnt(0);  // this wave's id and weight stores have completed
     __syncthreads();
@@ -371,11 +475,19 @@ router_tokens_kernel(int M, int E, const float* __restrict__ bias, int k, int ns
 
 size_t lds_bytes(int N) { return (size_t)(kThreads / (N / 8)) * kTokTile * N * sizeof(float); }
 
-// LDS of the router kernels: the slice sums, or the keys and rank counts of
-// the top-k (8 + 2*4 bytes per token and expert), whichever is larger.
-size_t router_lds_bytes(int E) {
+// LDS of the one-launch router: the tile's row-group sums, or the keys and
+// rank counts of the top-k (8 + 2*4 bytes per token and expert), whichever
+// is larger.
+size_t router_lds_bytes(int H, int E) {
+    const RouterTiles tl(H, E);
+    const size_t tile = (size_t)tl.rpt * kTokTile * tl.cgw * sizeof(float);
     const size_t topk = (size_t)kTokTile * E * (sizeof(uint64_t) + 2 * sizeof(int));
-    return lds_bytes(E) > topk ? lds_bytes(E) : topk;
+    return tile > topk ? tile : topk;
+}
+
+int router_grid(int H, int E) {
+    const RouterTiles tl(H, E);
+    return tl.nrs * tl.ncg;
 }
 
 }  // namespace
@@ -403,9 +515,10 @@ hipError_t launch_router_align(const float* h, int M, int H, const uint16_t* Wr,
                                float* part, unsigned* ticket, int32_t* ids, float* wts, float* logits_out, int b,
                                int32_t* sorted_routes, int32_t* block_expert, int32_t* counts, int32_t* err,
                                hipStream_t stream) {
+    if (M < 1 || M > kTokTile || E % 8 != 0) return hipErrorInvalidValue;
     const size_t la = align_lds_bytes(M * k, E);
-    const size_t lds = router_lds_bytes(E) > la ? router_lds_bytes(E) : la;
-    MOE_LAUNCH(router_align_kernel, dim3(gemv_slices(H, E)), dim3(kThreads), lds, stream, h, M, H, Wr, E, bias,
+    const size_t lds = router_lds_bytes(H, E) > la ? router_lds_bytes(H, E) : la;
+    MOE_LAUNCH(router_align_kernel, dim3(router_grid(H, E)), dim3(kThreads), lds, stream, h, M, H, Wr, E, bias,
                        k, part, ticket, ids, wts, logits_out, b, sorted_routes, block_expert, counts, err,
                        FastDiv((uint32_t)E), FastDiv((uint32_t)k), FastDiv((uint32_t)b));
     return hipGetLastError();
@@ -432,7 +545,8 @@ hipError_t launch_router_tokens(int M, int H, int E, const float* bias, int k, c
 hipError_t launch_router(const float* h, int M, int H, const uint16_t* Wr, int E, const float* bias, int k,
                          float* part, unsigned* ticket, int32_t* ids, float* wts, float* logits_out,
                          hipStream_t stream) {
-    MOE_LAUNCH(router_kernel, dim3(gemv_slices(H, E)), dim3(kThreads), router_lds_bytes(E), stream, h, M, H, Wr, E,
+    if (M < 1 || M > kTokTile || E % 8 != 0) return hipErrorInvalidValue;
+    MOE_LAUNCH(router_kernel, dim3(router_grid(H, E)), dim3(kThreads), router_lds_bytes(H, E), stream, h, M, H, Wr, E,
                        bias, k, part, ticket, ids, wts, logits_out, FastDiv((uint32_t)E));
     return hipGetLastError();
 }
