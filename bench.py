@@ -337,7 +337,11 @@ def main():
             a[1] += n
         mb.moe_profile_enable(L.ctx, False)
     kernels = {k: {"avg_us": round(v[0] / v[1] * 1e3, 3), "launches": v[1]} for k, v in kern.items()}
-    dominant = max(kern, key=lambda k: kern[k][0])
+    # the roofline is that of the dominant kernel among those streaming routed
+    # weights (routing, selection and combines are latency-bound and listed
+    # in "kernels" with their durations)
+    streaming = [k for k in kern if kernel_algorithmic_bytes(wl, k, 1, M, max(keep * M, 1)) > 0]
+    dominant = max(streaming or list(kern), key=lambda k: kern[k][0])
     avg_ex = float(np.mean(n_ex))
     alg = kernel_algorithmic_bytes(wl, dominant, round(avg_ex), M, keep * M)
     dur_s = kernels[dominant]["avg_us"] / 1e6
