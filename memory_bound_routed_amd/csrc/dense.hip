@@ -357,21 +357,63 @@ expert_fused_kernel(PlanArgs plan, const float* __restrict__ h, const float* __r
 
 // ---------------------------------------------------------------------------
 // Split schedule, gate/up.  Grid (plan blocks, ceil(I / (4*CPW))); wave w of
-// workgroup (blk, cy) owns channels (cy*4 + w)*CPW + c; RT plan rows are
-// processed together against the weights held in registers.
-template <int Q, int CPW, int RT>
+// workgroup (blk, cy) owns channels (cy*4 + w)*CPW + c of the expert whose
+// run of blocks starts at blk.  Its weights are loaded once into registers
+// and applied to every route of the run, G routes at a time: their h rows
+// are staged in LDS, then each wave forms its channels' p values (weights
+// unpacked per route, so that only the packed form stays live).
+// The plan rows of the first block arrive with the first round of loads; the
+// row checks and the h rows of the first G rows of the block (the expert's
+// first routes in a well-formed plan) follow as the second round and are in
+// LDS before the weights are requested, since a load queued behind the
+// weight stream would wait for all of it (the other workgroups on the CU keep
+// it streaming meanwhile).  Every such load has a clamped, always-valid
+// address.  A first group that turns out to differ from those rows, and every
+// later group, is staged again.
+template <int Q, int CPW, int G>
 __global__ void __launch_bounds__(kThreads)
 gateup_dense_kernel(PlanArgs plan, const float* __restrict__ h, int H, int I, const uint16_t* __restrict__ Wg,
                     const uint16_t* __restrict__ Wu, float* __restrict__ p, int32_t* __restrict__ err) {
+    extern __shared__ __align__(16) float4 hst[];  // [G][RS]: h rows, padded to RS float4
+    constexpr int PR = (Q * MOE_WAVE * 2 + kThreads - 1) / kThreads;  // float4 of one h row per thread
+    constexpr int RS = PR * kThreads;
     const int blk = blockIdx.x;
-    int nb;
-    const int e = run_expert(plan, blk, &nb, err);
-    if (e < 0) return;
-    const int wave = threadIdx.x / MOE_WAVE;
-    const int lane = threadIdx.x % MOE_WAVE;
-    const int j0 = (blockIdx.y * kWaves + wave) * CPW;
-    if (j0 >= I) return;  // no barriers below: a wave may leave on its own
+    const int b = plan.b;
+    const int tid = threadIdx.x;
+    const int wave = tid / MOE_WAVE;
+    const int lane = tid % MOE_WAVE;
+    const int H4 = H / 4;
 
+    // Round 1: counts, this and the previous block's expert, the block's rows.
+    int nb = plan.counts[0];
+    const int e = plan.block_expert[blk];
+    const int eprev = blk > 0 ? plan.block_expert[blk - 1] : -1;
+    int rv = plan.sorted_routes[(size_t)blk * b + min(lane, b - 1)];
+    if (lane >= b) rv = plan.R;
+    if (nb < 0 || nb > plan.max_blocks) {
+        if (blk == 0 && blockIdx.y == 0 && tid == 0) atomicOr(err, DEVERR_BAD_COUNTS);
+        nb = nb < 0 ? 0 : plan.max_blocks;
+    }
+    if (blk >= nb) return;
+    if (e < 0 || e >= plan.E) {
+        if (blockIdx.y == 0 && tid == 0) atomicOr(err, DEVERR_BAD_BLOCK_EXPERT);
+        return;
+    }
+    if (eprev == e) return;  // not the first block of the expert's run (uniform)
+
+    // Round 2, before the weights: the row checks, and h of rows 0..G-1
+    // staged in LDS (lanes past b hold the pad sentinel).
+    const int idv = plan.topk_ids[min(max(rv, 0), plan.R - 1)];
+#pragma unroll
+    for (int i = 0; i < G; ++i) {
+        const int r = __builtin_amdgcn_readlane(rv, i);
+        const float* hr = h + (size_t)plan.fk.div(min(max(r, 0), plan.R - 1)) * H;
+#pragma unroll
+        for (int v = 0; v < PR; ++v)
+            hst[i * RS + tid + kThreads * v] = *reinterpret_cast<const float4*>(hr + min(tid + kThreads * v, H4 - 1) * 4);
+    }
+
+    const int j0 = (blockIdx.y * kWaves + wave) * CPW;  // waves past I still take part in the barriers
     uint4 wg[CPW][Q], wu[CPW][Q];
 #pragma unroll
     for (int c = 0; c < CPW; ++c) {
@@ -380,68 +422,89 @@ gateup_dense_kernel(PlanArgs plan, const float* __restrict__ h, int H, int I, co
         const uint16_t* ru = Wu + ((size_t)e * I + j) * H;
 #pragma unroll
         for (int q = 0; q < Q; ++q) {
-            const int col = (lane + MOE_WAVE * q) * 8;
-            if (col < H) {
-                wg[c][q] = load_stream16(rg + col);
-                wu[c][q] = load_stream16(ru + col);
-            } else {
-                wg[c][q] = make_uint4(0, 0, 0, 0);
-                wu[c][q] = make_uint4(0, 0, 0, 0);
-            }
+            const int col = min((lane + MOE_WAVE * q) * 8, H - 8);
+            wg[c][q] = load_stream16(rg + col);
+            wu[c][q] = load_stream16(ru + col);
         }
     }
 
-    for (int bb = blk; bb < nb; ++bb) {
-        if (bb > blk && plan.block_expert[bb] != e) break;
-        for (int q0 = 0; q0 < plan.b; q0 += RT) {
-            int rt[RT];
-            bool any = false;
+    auto rows_ok = [&](int rvx, int idx) {
+        const bool ok = rvx >= 0 && rvx < plan.R && idx == e;
+        if (!ok && rvx != plan.R && blockIdx.y == 0 && tid < MOE_WAVE) atomicOr(err, DEVERR_BAD_PLAN);
+        return __ballot(ok);
+    };
+    uint64_t todo = rows_ok(rv, idv);
+    // the staged rows 0..n-1 are the first group iff the valid rows begin with them
+    const int n0 = min(G, __popcll(todo));
+    bool staged = (todo & ((1ull << G) - 1)) == ((1ull << n0) - 1);  // else staged again below
+    int bb = blk;
+    for (;;) {
+        if (!todo) {  // the run's next block: its rows, then their checks
+            if (++bb >= nb || plan.block_expert[bb] != e) break;
+            int rv2 = plan.sorted_routes[(size_t)bb * b + min(lane, b - 1)];
+            if (lane >= b) rv2 = plan.R;
+            todo = rows_ok(rv2, plan.topk_ids[min(max(rv2, 0), plan.R - 1)]);
+            rv = rv2;
+            continue;
+        }
+        int rt[G];
+        int ng = 0;
 #pragma unroll
-            for (int i = 0; i < RT; ++i) {
-                rt[i] = plan_route(plan, bb, q0 + i, e, err);
-                any |= rt[i] >= 0;
+        for (int i = 0; i < G; ++i) {
+            rt[i] = -1;
+            if (todo) {
+                const int q = __builtin_ctzll(todo);
+                todo &= todo - 1;
+                rt[i] = __builtin_amdgcn_readlane(rv, q);
+                ng = i + 1;
             }
-            if (!any) continue;
-            float ag[CPW][RT], au[CPW][RT];
+        }
+        if (!staged) {
+            __syncthreads();  // the previous group's h is no longer read
 #pragma unroll
-            for (int c = 0; c < CPW; ++c)
+            for (int i = 0; i < G; ++i) {
+                const float* hr = h + (size_t)plan.fk.div(max(rt[i], 0)) * H;
 #pragma unroll
-                for (int i = 0; i < RT; ++i) ag[c][i] = au[c][i] = 0.f;
+                for (int v = 0; v < PR; ++v)
+                    hst[i * RS + tid + kThreads * v] =
+                        *reinterpret_cast<const float4*>(hr + min(tid + kThreads * v, H4 - 1) * 4);
+            }
+        }
+        staged = false;
+        __syncthreads();
+        for (int i = 0; i < ng; ++i) {  // uniform
+            const float4* hr = hst + i * RS;
+            float ag[CPW], au[CPW];
+#pragma unroll
+            for (int c = 0; c < CPW; ++c) ag[c] = au[c] = 0.f;
 #pragma unroll
             for (int q = 0; q < Q; ++q) {
-                const int col = (lane + MOE_WAVE * q) * 8;
-                if (col >= H) continue;
-                float gf[CPW][8], uf[CPW][8];
+                const int c8 = lane + MOE_WAVE * q;
+                if (c8 * 8 >= H) continue;
+                const float4 h0 = hr[c8 * 2];
+                const float4 h1 = hr[c8 * 2 + 1];
+                const float hx[8] = {h0.x, h0.y, h0.z, h0.w, h1.x, h1.y, h1.z, h1.w};
 #pragma unroll
                 for (int c = 0; c < CPW; ++c) {
-                    unpack8(wg[c][q], gf[c]);
-                    unpack8(wu[c][q], uf[c]);
-                }
+                    float gf[8], uf[8];
+                    unpack8(opaque(wg[c][q]), gf);
+                    unpack8(opaque(wu[c][q]), uf);
 #pragma unroll
-                for (int i = 0; i < RT; ++i) {
-                    if (rt[i] < 0) continue;
-                    const float* hr = h + (size_t)(rt[i] / plan.k) * H + col;
-                    const float4 h0 = *reinterpret_cast<const float4*>(hr);
-                    const float4 h1 = *reinterpret_cast<const float4*>(hr + 4);
-                    const float hv[8] = {h0.x, h0.y, h0.z, h0.w, h1.x, h1.y, h1.z, h1.w};
-#pragma unroll
-                    for (int c = 0; c < CPW; ++c)
-#pragma unroll
-                        for (int x = 0; x < 8; ++x) {
-                            ag[c][i] = fmaf(gf[c][x], hv[x], ag[c][i]);
-                            au[c][i] = fmaf(uf[c][x], hv[x], au[c][i]);
-                        }
+                    for (int x = 0; x < 8; ++x) {
+                        ag[c] = fmaf(gf[x], hx[x], ag[c]);
+                        au[c] = fmaf(uf[x], hx[x], au[c]);
+                    }
                 }
             }
+            int r = rt[0];
 #pragma unroll
-            for (int i = 0; i < RT; ++i) {
-                if (rt[i] < 0) continue;
+            for (int ii = 1; ii < G; ++ii)
+                if (ii == i) r = rt[ii];
 #pragma unroll
-                for (int c = 0; c < CPW; ++c) {
-                    const float g = wave_sum(ag[c][i]);
-                    const float u = wave_sum(au[c][i]);
-                    if (lane == 0 && j0 + c < I) p[(size_t)rt[i] * I + j0 + c] = silu_mul(g, u);
-                }
+            for (int c = 0; c < CPW; ++c) {
+                const float g = wave_sum(ag[c]);
+                const float u = wave_sum(au[c]);
+                if (lane == 0 && j0 + c < I) p[(size_t)r * I + j0 + c] = silu_mul(g, u);
             }
         }
     }
@@ -585,19 +648,20 @@ combine_kernel(const int32_t* __restrict__ topk_ids, int M, int k, int E, int H,
     if (rg == 0 && col < H) *reinterpret_cast<float4*>(y + (size_t)t * H + col) = acc;
 }
 
+// Staged route group of the split gate/up: h rows of G routes in LDS, each
+// padded to a whole number of float4 per thread (at most 32 KiB).
+constexpr int gateup_group(int Q) { return Q <= 4 ? 4 : (Q <= 8 ? 2 : 1); }
+constexpr size_t gateup_lds(int Q) {
+    return (size_t)gateup_group(Q) * ((Q * MOE_WAVE * 2 + kThreads - 1) / kThreads) * kThreads * 16;
+}
+
 template <int Q, int CPW>
-hipError_t gateup_q(const PlanArgs& plan, int RT, const float* h, int H, int I, const uint16_t* Wg,
-                    const uint16_t* Wu, float* p, int32_t* err, hipStream_t stream) {
+hipError_t gateup_q(const PlanArgs& plan, const float* h, int H, int I, const uint16_t* Wg, const uint16_t* Wu,
+                    float* p, int32_t* err, hipStream_t stream) {
+    constexpr int G = gateup_group(Q);
     const dim3 grid(plan.max_blocks, (I + kWaves * CPW - 1) / (kWaves * CPW));
-    if (RT == 1)
-        MOE_LAUNCH((gateup_dense_kernel<Q, CPW, 1>), grid, dim3(kThreads), 0, stream, plan, h, H, I, Wg, Wu,
-                           p, err);
-    else if (RT == 4)
-        MOE_LAUNCH((gateup_dense_kernel<Q, CPW, 4>), grid, dim3(kThreads), 0, stream, plan, h, H, I, Wg, Wu,
-                           p, err);
-    else
-        MOE_LAUNCH((gateup_dense_kernel<Q, CPW, 8>), grid, dim3(kThreads), 0, stream, plan, h, H, I, Wg, Wu,
-                           p, err);
+    MOE_LAUNCH((gateup_dense_kernel<Q, CPW, G>), grid, dim3(kThreads), gateup_lds(Q), stream, plan, h,
+               H, I, Wg, Wu, p, err);
     return hipGetLastError();
 }
 
@@ -676,13 +740,12 @@ hipError_t launch_expert_fused(const PlanArgs& plan, const float* h, const float
 
 hipError_t launch_gateup_dense(const PlanArgs& plan, const float* h, int H, int I, const uint16_t* Wg,
                                const uint16_t* Wu, float* p, int32_t* err, hipStream_t stream) {
-    const int RT = route_tile(plan.R / plan.k, plan.b);
     const int Q = (H + 511) / 512;
-    if (Q <= 1) return gateup_q<1, 2>(plan, RT, h, H, I, Wg, Wu, p, err, stream);
-    if (Q <= 2) return gateup_q<2, 2>(plan, RT, h, H, I, Wg, Wu, p, err, stream);
-    if (Q <= 4) return gateup_q<4, 2>(plan, RT, h, H, I, Wg, Wu, p, err, stream);
-    if (Q <= 8) return gateup_q<8, 2>(plan, RT, h, H, I, Wg, Wu, p, err, stream);
-    if (Q <= 16) return gateup_q<16, 1>(plan, RT, h, H, I, Wg, Wu, p, err, stream);
+    if (Q <= 1) return gateup_q<1, 2>(plan, h, H, I, Wg, Wu, p, err, stream);
+    if (Q <= 2) return gateup_q<2, 2>(plan, h, H, I, Wg, Wu, p, err, stream);
+    if (Q <= 4) return gateup_q<4, 2>(plan, h, H, I, Wg, Wu, p, err, stream);
+    if (Q <= 8) return gateup_q<8, 2>(plan, h, H, I, Wg, Wu, p, err, stream);
+    if (Q <= 16) return gateup_q<16, 1>(plan, h, H, I, Wg, Wu, p, err, stream);
     return hipErrorInvalidValue;
 }
 

@@ -6,6 +6,8 @@
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
+#include "device_common.h"
+
 namespace moe {
 
 // Events attached to the next launch while the context is profiling (set by
@@ -70,6 +72,7 @@ struct PlanArgs {
     const int32_t* counts;         // [2]
     int R;                         // M*k (also the pad sentinel)
     int k;
+    FastDiv fk;                    // division by k (route -> token)
     int b;
     int max_blocks;                // cap / b
     int E;

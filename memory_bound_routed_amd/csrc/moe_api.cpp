@@ -361,6 +361,7 @@ moe_status moe_expert_forward(moe_ctx* ctx, const float* h, int32_t M, const int
     plan.counts = counts;
     plan.R = M * c.top_k;
     plan.k = c.top_k;
+    plan.fk = FastDiv((uint32_t)c.top_k);
     plan.b = c.block_b;
     plan.max_blocks = (int)(align_capacity64(M, c.top_k, c.E, c.block_b) / c.block_b);
     plan.E = c.E;
