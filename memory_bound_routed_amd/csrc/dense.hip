@@ -510,86 +510,209 @@ gateup_dense_kernel(PlanArgs plan, const float* __restrict__ h, int H, int I, co
     }
 }
 
-// Split schedule, down.  Grid (plan blocks, ceil(I / kDownRows)).  Workgroup
-// (blk, rc) handles rows rc*kDownRows ... of W_down,e for the RT routes of
-// each row group of the run: the scaled intermediates a_route * p[route][j]
-// are staged in LDS, the rows are streamed in sub-chunks of kDownSub, and
-// thread t accumulates hidden columns 8*(t + 256*cq) in row order.
-constexpr int kDownRows = 64;
-constexpr int kDownSub = 16;
+// Split schedule, down.  Grid (ceil(H / CB) column blocks, plan blocks).
+// Workgroup (cb, blk) multiplies the routes of plan block blk (8 rows at a
+// time) by columns [cb*CB, cb*CB + CB) of W_down,e over all I rows, so each
+// route's output for those columns is complete: one partial per route, and
+// the combine adds only the k routes of a token.  Column blocks run along x,
+// so the consecutive plan blocks of an expert's run land on one XCD next to
+// each other in dispatch order, and a second block's weight reads can hit in
+// that XCD's L2.
+// Thread t covers columns cb*CB + 8*(t % TPR) .. +8 and rows rg, rg + RGS, ...
+// (rg = t / TPR).  The scaled intermediates s[j][i] = a_i * p[route_i][j] of
+// the 8 rows are staged route-minor in LDS (kDownStage rows at a time), the
+// weight rows stream through registers kDownNB at a time, double-buffered,
+// and the RGS row groups are added at the end: by an xor butterfly inside
+// each wave, then the waves in wave order.  Rows that are not routes of the
+// expert (pads) get s = 0 and no output; RT = 2, 4 or 8 accumulators cover
+// the leading rows up to the last route.
+constexpr int kDownStage = 1024;  // rows of s staged at a time (32 KiB)
+constexpr int kDownNB = 4;        // weight rows per thread and buffer
 
-template <int CQ, int RT>
-__global__ void __launch_bounds__(kThreads)
-down_kernel(PlanArgs plan, int H, int I, int nchunk, const uint16_t* __restrict__ Wd, const float* __restrict__ p,
-            const float* __restrict__ topk_w, float* __restrict__ part, int32_t* __restrict__ err) {
-    __shared__ float sp[RT][kDownRows];
-    const int blk = blockIdx.x;
-    const int rc = blockIdx.y;
-    int nb;
-    const int e = run_expert(plan, blk, &nb, err);
-    if (e < 0) return;  // uniform
+template <int CB, int RT>
+__device__ __forceinline__ void down_pass(int e, int H, int I, const uint16_t* __restrict__ Wd,
+                                          const float* __restrict__ p, const int (&rr)[8], const float (&ra)[8],
+                                          uint32_t valid, float* __restrict__ part, float* dsm) {
+    constexpr int TPR = CB / 8;
+    constexpr int RGS = kThreads / TPR;
     const int tid = threadIdx.x;
-    const int j0 = rc * kDownRows;
-    const int nrows = min(kDownRows, I - j0);
-    const uint16_t* base = Wd + ((size_t)e * I + j0) * H;
+    const int lane = tid % MOE_WAVE;
+    const int wave = tid / MOE_WAVE;
+    const int c8 = tid % TPR;
+    const int rg = tid / TPR;
+    const int col = blockIdx.x * CB + c8 * 8;
+    const uint16_t* wbase = Wd + (size_t)e * I * H + min(col, H - 8);
+    // the route this thread stages (route-minor layout: thread t takes route t % 8)
+    const int si = tid & 7;
+    int sr = 0;
+    float sa = 0.f;
+#pragma unroll
+    for (int i = 0; i < 8; ++i)
+        if (i == si && ((valid >> i) & 1)) {
+            sr = rr[i];
+            sa = ra[i];
+        }
+    const bool sv = si < RT && ((valid >> si) & 1);
 
-    for (int bb = blk; bb < nb; ++bb) {
-        if (bb > blk && plan.block_expert[bb] != e) break;
-        for (int q0 = 0; q0 < plan.b; q0 += RT) {
-            int rt[RT];
-            bool any = false;
+    float acc[RT][8];
 #pragma unroll
-            for (int i = 0; i < RT; ++i) {
-                rt[i] = plan_route(plan, bb, q0 + i, e, err);
-                any |= rt[i] >= 0;
+    for (int i = 0; i < RT; ++i)
+#pragma unroll
+        for (int x = 0; x < 8; ++x) acc[i][x] = 0.f;
+    uint4 w0[kDownNB], w1[kDownNB];
+    for (int js = 0; js < I; js += kDownStage) {
+        const int jn = min(kDownStage, I - js);
+        const int nu = (jn + RGS - 1) / RGS;  // rows per thread in this stage (clamped beyond jn)
+        // Rows past the stage load its last row (same address for all, cached)
+        // and are multiplied by s = 0.
+        auto issue = [&](uint4 (&w)[kDownNB], int u0) {
+#pragma unroll
+            for (int r = 0; r < kDownNB; ++r) {
+                const int jl = min(rg + RGS * (u0 + r), jn - 1);
+                w[r] = load_stream16(wbase + (size_t)(js + jl) * H);
             }
-            if (!any) continue;  // uniform
-            __syncthreads();     // sp of the previous group is no longer read
-            for (int idx = tid; idx < RT * kDownRows; idx += kThreads) {
-                const int i = idx / kDownRows, jr = idx % kDownRows;
-                float v = 0.f;
+        };
+        auto compute = [&](const uint4 (&w)[kDownNB], int u0) {
 #pragma unroll
-                for (int ii = 0; ii < RT; ++ii)
-                    if (ii == i && rt[ii] >= 0 && jr < nrows) v = topk_w[rt[ii]] * p[(size_t)rt[ii] * I + j0 + jr];
-                sp[i][jr] = v;
-            }
-            __syncthreads();
-#pragma unroll
-            for (int cq = 0; cq < CQ; ++cq) {
-                const int col = (tid + kThreads * cq) * 8;
-                if (col >= H) continue;
-                float acc[RT][8];
-#pragma unroll
-                for (int i = 0; i < RT; ++i)
-#pragma unroll
-                    for (int x = 0; x < 8; ++x) acc[i][x] = 0.f;
-                for (int js = 0; js < nrows; js += kDownSub) {
-                    uint4 w[kDownSub];
-#pragma unroll
-                    for (int jr = 0; jr < kDownSub; ++jr)
-                        w[jr] = (js + jr < nrows) ? load_stream16(base + (size_t)(js + jr) * H + col)
-                                                  : make_uint4(0, 0, 0, 0);
-#pragma unroll
-                    for (int jr = 0; jr < kDownSub; ++jr) {
-                        float wf[8];
-                        unpack8(w[jr], wf);
-#pragma unroll
-                        for (int i = 0; i < RT; ++i) {
-                            const float s = sp[i][js + jr];
-#pragma unroll
-                            for (int x = 0; x < 8; ++x) acc[i][x] = fmaf(s, wf[x], acc[i][x]);
-                        }
-                    }
+            for (int r = 0; r < kDownNB; ++r) {
+                const int jl = rg + RGS * (u0 + r);
+                const float4* s4 = reinterpret_cast<const float4*>(dsm + (size_t)min(jl, jn - 1) * 8);
+                const float4 a = s4[0];
+                float sv8[8] = {a.x, a.y, a.z, a.w, 0.f, 0.f, 0.f, 0.f};
+                if (RT > 4) {
+                    const float4 b4 = s4[1];
+                    sv8[4] = b4.x; sv8[5] = b4.y; sv8[6] = b4.z; sv8[7] = b4.w;
                 }
+                const bool in = jl < jn;
+                float wf[8];
+                unpack8(w[r], wf);
 #pragma unroll
                 for (int i = 0; i < RT; ++i) {
-                    if (rt[i] < 0) continue;
-                    float* dst = part + ((size_t)rt[i] * nchunk + rc) * H + col;
-                    *reinterpret_cast<float4*>(dst) = make_float4(acc[i][0], acc[i][1], acc[i][2], acc[i][3]);
-                    *reinterpret_cast<float4*>(dst + 4) = make_float4(acc[i][4], acc[i][5], acc[i][6], acc[i][7]);
+                    const float sx = in ? sv8[i] : 0.f;
+#pragma unroll
+                    for (int x = 0; x < 8; ++x) acc[i][x] = fmaf(sx, wf[x], acc[i][x]);
                 }
             }
+        };
+        // stage s (the p loads go out before the first weights)
+        float pv[kDownStage / (kThreads / 8)];
+        constexpr int SPT = kDownStage / (kThreads / 8);  // staged rows per thread (upper bound)
+#pragma unroll
+        for (int u = 0; u < SPT; ++u) {
+            const int jj = min((tid >> 3) + (kThreads / 8) * u, jn - 1);
+            pv[u] = p[(size_t)sr * I + js + jj];
         }
+        issue(w0, 0);
+        __syncthreads();  // the previous stage's s is no longer read
+#pragma unroll
+        for (int u = 0; u < SPT; ++u) {
+            const int jj = (tid >> 3) + (kThreads / 8) * u;
+            if (jj < jn) dsm[jj * 8 + si] = sv ? sa * pv[u] : 0.f;
+        }
+        __syncthreads();
+        for (int u0 = 0; u0 < nu; u0 += 2 * kDownNB) {
+            issue(w1, u0 + kDownNB);
+            compute(w0, u0);
+            issue(w0, u0 + 2 * kDownNB);
+            compute(w1, u0 + kDownNB);
+        }
+    }
+    // row groups: xor butterfly over the lane bits above the column bits, then
+    // the waves added in wave order
+#pragma unroll
+    for (int i = 0; i < RT; ++i)
+#pragma unroll
+        for (int x = 0; x < 8; ++x)
+#pragma unroll
+            for (int m = TPR; m < MOE_WAVE; m <<= 1) acc[i][x] += __shfl_xor(acc[i][x], m, MOE_WAVE);
+    __syncthreads();  // s is no longer read
+    if (lane < TPR) {
+#pragma unroll
+        for (int i = 0; i < RT; ++i) {
+            float4* o = reinterpret_cast<float4*>(dsm + ((size_t)wave * RT + i) * CB + c8 * 8);
+            o[0] = make_float4(acc[i][0], acc[i][1], acc[i][2], acc[i][3]);
+            o[1] = make_float4(acc[i][4], acc[i][5], acc[i][6], acc[i][7]);
+        }
+    }
+    __syncthreads();
+    if (wave == 0 && lane < TPR && col < H) {
+#pragma unroll
+        for (int i = 0; i < RT; ++i) {
+            if (!((valid >> i) & 1)) continue;
+            float o[8];
+#pragma unroll
+            for (int x = 0; x < 8; ++x) o[x] = 0.f;
+            float4 v[kWaves][2];
+#pragma unroll
+            for (int w = 0; w < kWaves; ++w) {
+                const float4* q = reinterpret_cast<const float4*>(dsm + ((size_t)w * RT + i) * CB + c8 * 8);
+                v[w][0] = q[0];
+                v[w][1] = q[1];
+            }
+            // (w0 + w1) + (w2 + w3)
+            const float4 l0 = v[0][0], l1 = v[1][0], l2 = v[2][0], l3 = v[3][0];
+            const float4 h0 = v[0][1], h1 = v[1][1], h2 = v[2][1], h3 = v[3][1];
+            o[0] = (l0.x + l1.x) + (l2.x + l3.x); o[1] = (l0.y + l1.y) + (l2.y + l3.y);
+            o[2] = (l0.z + l1.z) + (l2.z + l3.z); o[3] = (l0.w + l1.w) + (l2.w + l3.w);
+            o[4] = (h0.x + h1.x) + (h2.x + h3.x); o[5] = (h0.y + h1.y) + (h2.y + h3.y);
+            o[6] = (h0.z + h1.z) + (h2.z + h3.z); o[7] = (h0.w + h1.w) + (h2.w + h3.w);
+            float* dst = part + (size_t)rr[i] * H + col;
+            *reinterpret_cast<float4*>(dst) = make_float4(o[0], o[1], o[2], o[3]);
+            *reinterpret_cast<float4*>(dst + 4) = make_float4(o[4], o[5], o[6], o[7]);
+        }
+    }
+    __syncthreads();  // dsm is reused by the next pass
+}
+
+template <int CB>
+__global__ void __launch_bounds__(kThreads)
+down_kernel(PlanArgs plan, int H, int I, const uint16_t* __restrict__ Wd, const float* __restrict__ p,
+            const float* __restrict__ topk_w, float* __restrict__ part, int32_t* __restrict__ err) {
+    static_assert(kWaves == 4, "the final wave sum is written for four waves");
+    extern __shared__ __align__(16) float dsm[];
+    const int blk = blockIdx.y;
+    const int b = plan.b;
+    const int tid = threadIdx.x;
+    const int lane = tid % MOE_WAVE;
+    // First round: counts, the block's expert, its rows (lane q holds row q).
+    int nb = plan.counts[0];
+    const int e = plan.block_expert[blk];
+    int rv = plan.sorted_routes[(size_t)blk * b + min(lane, b - 1)];
+    if (lane >= b) rv = plan.R;
+    if (nb < 0 || nb > plan.max_blocks) {
+        if (blk == 0 && blockIdx.x == 0 && tid == 0) atomicOr(err, DEVERR_BAD_COUNTS);
+        nb = nb < 0 ? 0 : plan.max_blocks;
+    }
+    if (blk >= nb) return;
+    if (e < 0 || e >= plan.E) {
+        if (blockIdx.x == 0 && tid == 0) atomicOr(err, DEVERR_BAD_BLOCK_EXPERT);
+        return;
+    }
+    // Second round: row checks and affinities (clamped addresses).
+    const int rc = min(max(rv, 0), plan.R - 1);
+    const int idv = plan.topk_ids[rc];
+    const float av = topk_w[rc];
+    const bool ok = rv >= 0 && rv < plan.R && idv == e;
+    if (!ok && rv != plan.R && blockIdx.x == 0 && tid < MOE_WAVE) atomicOr(err, DEVERR_BAD_PLAN);
+    const uint64_t m = __ballot(ok);
+    for (int q0 = 0; q0 < b; q0 += 8) {  // uniform
+        const uint32_t valid = (uint32_t)(m >> q0) & 0xFFu;
+        if (!valid) continue;
+        int rr[8];
+        float ra[8];
+#pragma unroll
+        for (int i = 0; i < 8; ++i) {
+            const int q = min(q0 + i, MOE_WAVE - 1);
+            rr[i] = ((valid >> i) & 1) ? __builtin_amdgcn_readlane(rv, q) : 0;
+            ra[i] = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(av), q));
+        }
+        const int nv = 32 - __builtin_clz(valid);  // rows up to the last route
+        if (nv <= 2)
+            down_pass<CB, 2>(e, H, I, Wd, p, rr, ra, valid, part, dsm);
+        else if (nv <= 4)
+            down_pass<CB, 4>(e, H, I, Wd, p, rr, ra, valid, part, dsm);
+        else
+            down_pass<CB, 8>(e, H, I, Wd, p, rr, ra, valid, part, dsm);
     }
 }
 
@@ -665,23 +788,6 @@ hipError_t gateup_q(const PlanArgs& plan, const float* h, int H, int I, const ui
     return hipGetLastError();
 }
 
-template <int CQ>
-hipError_t down_cq(const PlanArgs& plan, int RT, int H, int I, const uint16_t* Wd, const float* p,
-                   const float* topk_w, float* part, int32_t* err, hipStream_t stream) {
-    const int nchunk = (I + kDownRows - 1) / kDownRows;
-    const dim3 grid(plan.max_blocks, nchunk);
-    if (RT == 1)
-        MOE_LAUNCH((down_kernel<CQ, 1>), grid, dim3(kThreads), 0, stream, plan, H, I, nchunk, Wd, p, topk_w,
-                           part, err);
-    else if (RT == 4)
-        MOE_LAUNCH((down_kernel<CQ, 4>), grid, dim3(kThreads), 0, stream, plan, H, I, nchunk, Wd, p, topk_w,
-                           part, err);
-    else
-        MOE_LAUNCH((down_kernel<CQ, 8>), grid, dim3(kThreads), 0, stream, plan, H, I, nchunk, Wd, p, topk_w,
-                           part, err);
-    return hipGetLastError();
-}
-
 // Fused tiling: 8 waves, one gate/up channel per wave and chunk; three
 // double-buffered chunks per workgroup (24 channels) up to H = 2048, one
 // chunk (8 channels, no second buffer) up to H = 4096.
@@ -706,14 +812,6 @@ hipError_t fused_q(const PlanArgs& plan, const float* h, const float* topk_w, in
     return hipGetLastError();
 }
 
-// Register tile of routes: one route per block row at M == 1, else up to 4
-// or 8 rows of a block at a time.
-int route_tile(int M, int b) {
-    if (M == 1) return 1;
-    if (M <= 4 || b <= 4) return 4;
-    return 8;
-}
-
 }  // namespace
 
 bool dense_uses_fused(int M, int H) { return M == 1 && H <= 4096; }
@@ -723,10 +821,10 @@ int dense_chunks(int M, int H, int I) {
         const int range = fused_range((H + 511) / 512 <= 4 ? 4 : 8);
         return (I + range - 1) / range;
     }
-    return (I + kDownRows - 1) / kDownRows;
+    return down_chunks(I);
 }
 
-int down_chunks(int I) { return (I + kDownRows - 1) / kDownRows; }
+int down_chunks(int) { return 1; }
 
 hipError_t launch_expert_fused(const PlanArgs& plan, const float* h, const float* topk_w, int H, int I,
                                const uint16_t* Wg, const uint16_t* Wu, const uint16_t* Wd, float* part, int32_t* err,
@@ -751,12 +849,16 @@ hipError_t launch_gateup_dense(const PlanArgs& plan, const float* h, int H, int 
 
 hipError_t launch_down(const PlanArgs& plan, int H, int I, const uint16_t* Wd, const float* p, const float* topk_w,
                        float* part, int32_t* err, hipStream_t stream) {
-    const int RT = route_tile(plan.R / plan.k, plan.b);
-    const int CQ = (H + 2047) / 2048;
-    if (CQ <= 1) return down_cq<1>(plan, RT, H, I, Wd, p, topk_w, part, err, stream);
-    if (CQ <= 2) return down_cq<2>(plan, RT, H, I, Wd, p, topk_w, part, err, stream);
-    if (CQ <= 4) return down_cq<4>(plan, RT, H, I, Wd, p, topk_w, part, err, stream);
-    return hipErrorInvalidValue;
+    // 256-column blocks when that still gives two workgroups per CU, else 128
+    const size_t lds = (size_t)kDownStage * 8 * sizeof(float);
+    if ((size_t)plan.max_blocks * ((H + 255) / 256) >= 512) {
+        const dim3 grid((H + 255) / 256, plan.max_blocks);
+        MOE_LAUNCH(down_kernel<256>, grid, dim3(kThreads), lds, stream, plan, H, I, Wd, p, topk_w, part, err);
+    } else {
+        const dim3 grid((H + 127) / 128, plan.max_blocks);
+        MOE_LAUNCH(down_kernel<128>, grid, dim3(kThreads), lds, stream, plan, H, I, Wd, p, topk_w, part, err);
+    }
+    return hipGetLastError();
 }
 
 hipError_t launch_combine(const int32_t* topk_ids, int M, int k, int E, int H, int nchunk, const float* part, float* y,
