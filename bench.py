@@ -346,7 +346,7 @@ def main():
     alg = kernel_algorithmic_bytes(wl, dominant, round(avg_ex), M, keep * M)
     dur_s = kernels[dominant]["avg_us"] / 1e6
     achieved = alg / dur_s / 1e9 if alg else None
-    expert_kernels = [k for k in kern if k not in ("router", "align", "router_align", "router_slices", "router_tokens")]
+    expert_kernels = [k for k in kern if k not in ("router", "align", "router_align")]
     expert_us = sum(kernels[k]["avg_us"] * kernels[k]["launches"] for k in expert_kernels) / K
 
     us_step = ms_per_step * 1e3

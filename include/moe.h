@@ -152,15 +152,13 @@ void moe_destroy(moe_ctx *ctx);
  *  topk_w     fp32 [M][k] out: softmax over the k selected logits
  *  logits_out fp32 [M][E] out (may be NULL): l = h Wr + bias, fp32 accumulation
  * Each logit is an fp32 sum whose summation tree has depth at most
- *   up to 4 tokens:  4 + rpt/8 + 3 + ceil(H / (4 rpt)) + 1, rpt = 2048 / c,
- *                    c = 32 experts per column group (16 if E < 32, 8 if E < 16)
- *   more tokens:     4 + rpp + ceil(H / (4 rpp)) + 1, rpp = floor(2048 / E)
+ *   4 + rpt/8 + 3 + ceil(H / (4 rpt)) + 1, rpt = 2048 / c,
+ *   c = 32 experts per column group (16 if E < 32, 8 if E < 16),
  * so |l - exact| <= gamma_depth * (sum_i |h_i Wr_ie| + |bias_e|).  The top-k
- * decision is exact for these fp32 logits.  Up to 4 tokens: one launch over
- * (row slice, column group) tiles; the last workgroup to finish adds the row
- * slices in order (an integer ticket, no spinning).  More tokens: two
- * launches (row slices over all experts, then one workgroup per token that
- * adds them in order).
+ * decision is exact for these fp32 logits.  One launch over (row slice,
+ * column group) tiles x groups of 4 tokens; the last tile workgroup of a
+ * group to finish adds the row slices in order and takes the group's top-k
+ * (integer tickets, no spinning).
  */
 moe_status moe_route_topk(moe_ctx *ctx, const float *h, int32_t M,
                           int32_t *topk_ids, float *topk_w, float *logits_out, void *stream);
@@ -284,9 +282,7 @@ enum {
     MOE_KERNEL_CHAN_COMBINE = 9,
     MOE_KERNEL_EXPERT_FUSED = 10, /* dense gate/up + SiLU + down partials (one route per block) */
     MOE_KERNEL_ROUTER_ALIGN = 11, /* router + top-k + softmax + alignment (one launch) */
-    MOE_KERNEL_ROUTER_SLICES = 12, /* router GEMV slice partials (batches above 4 tokens) */
-    MOE_KERNEL_ROUTER_TOKENS = 13, /* per-token top-k + softmax (+ alignment) (batches above 4 tokens) */
-    MOE_KERNEL_COUNT = 14
+    MOE_KERNEL_COUNT = 12
 };
 
 /*

@@ -27,8 +27,7 @@ MOE_OK, MOE_ERR_INVALID_ARG, MOE_ERR_UNSUPPORTED, MOE_ERR_CAPACITY, MOE_ERR_HIP,
 MOE_WFORMAT_DENSE, MOE_WFORMAT_VQLR = 0, 1
 DEVERR_BAD_ROUTE_ID, DEVERR_BAD_PLAN, DEVERR_BAD_BLOCK_EXPERT, DEVERR_BAD_COUNTS = 1, 2, 4, 8
 KERNELS = ["router", "vq_shared", "align", "gateup", "gateup_vqlr", "down", "combine",
-           "chan_select", "chan_gather", "chan_combine", "expert_fused", "router_align", "router_slices",
-           "router_tokens"]
+           "chan_select", "chan_gather", "chan_combine", "expert_fused", "router_align"]
 MOE_KERNEL_COUNT = len(KERNELS)
 
 # Every symbol include/moe.h declares (checked by the CPU test suite).

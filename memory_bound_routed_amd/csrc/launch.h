@@ -39,21 +39,16 @@ struct GemvJob {
 };
 int gemv_slices(int H, int N);
 hipError_t launch_gemv_partials(const float* h, int M, int H, const GemvJob* jobs, int njobs, hipStream_t stream);
-// Tokens processed by the one-launch router; larger batches take two launches
-// (gemv_partials over all tokens, then launch_router_tokens).
-constexpr int kRouterOneLaunchTokens = 4;
-// Per-token slice sum, top-k and softmax from the partials of a previous
-// gemv_partials launch; with sorted_routes non-null the last workgroup also
-// aligns the routes (b, block_expert, counts, err as launch_align).
-hipError_t launch_router_tokens(int M, int H, int E, const float* bias, int k, const float* part, unsigned* ticket,
-                                int32_t* ids, float* wts, float* logits_out, int b, int32_t* sorted_routes,
-                                int32_t* block_expert, int32_t* counts, int32_t* err, hipStream_t stream);
-// Router GEMV + (last workgroup) slice sum, top-k and softmax in one launch.
-// part: fp32 [gemv_slices(H, E)][M][E]; ticket: zeroed uint32, left zeroed.
+// Token groups of the router (4 tokens each; one group at M == 1).
+int router_groups(int M);
+// Router GEMV + (last workgroup of each token group) slice sum, top-k and
+// softmax in one launch.  part: fp32 [gemv_slices(H, E)][M][E] (covers the
+// tiles' slices); ticket: 1 + router_groups(M) zeroed uint32, left zeroed.
 hipError_t launch_router(const float* h, int M, int H, const uint16_t* Wr, int E, const float* bias, int k,
                          float* part, unsigned* ticket, int32_t* ids, float* wts, float* logits_out,
                          hipStream_t stream);
-// The same, followed (in the last workgroup) by the canonical alignment of the ids.
+// The same, followed (in the last workgroup to finish) by the canonical
+// alignment of the ids.
 hipError_t launch_router_align(const float* h, int M, int H, const uint16_t* Wr, int E, const float* bias, int k,
                                float* part, unsigned* ticket, int32_t* ids, float* wts, float* logits_out, int b,
                                int32_t* sorted_routes, int32_t* block_expert, int32_t* counts, int32_t* err,

@@ -135,28 +135,6 @@ struct Launch {
 
 moe_status hip_status(hipError_t e) { return e == hipSuccess ? MOE_OK : MOE_ERR_HIP; }
 
-// Router for batches above kRouterOneLaunchTokens: the row-slice partials of
-// all tokens, then one workgroup per token (aligning too when sorted_routes
-// is given).  Arguments are checked by the caller.
-moe_status route_two_launches(moe_ctx* ctx, const float* h, int M, int32_t* topk_ids, float* topk_w,
-                              float* logits_out, int32_t* sorted_routes, int32_t* block_expert, int32_t* counts,
-                              hipStream_t s) {
-    const moe_config& c = ctx->cfg;
-    {
-        const moe::GemvJob job{ctx->w.router_w, c.E, ctx->router_part};
-        Launch l(ctx, MOE_KERNEL_ROUTER_SLICES, s);
-        const hipError_t e = moe::launch_gemv_partials(h, M, c.H, &job, 1, s);
-        l.done();
-        if (e != hipSuccess) return MOE_ERR_HIP;
-    }
-    Launch l(ctx, MOE_KERNEL_ROUTER_TOKENS, s);
-    const hipError_t e = moe::launch_router_tokens(M, c.H, c.E, ctx->w.router_bias, c.top_k, ctx->router_part,
-                                                   ctx->ticket, topk_ids, topk_w, logits_out, c.block_b,
-                                                   sorted_routes, block_expert, counts, ctx->err, s);
-    l.done();
-    return hip_status(e);
-}
-
 }  // namespace
 
 extern "C" {
@@ -182,8 +160,7 @@ const char* moe_status_string(moe_status s) {
 const char* moe_kernel_name(int32_t k) {
     static const char* names[MOE_KERNEL_COUNT] = {"router",      "vq_shared",   "align",        "gateup",
                                                   "gateup_vqlr", "down",        "combine",      "chan_select",
-                                                  "chan_gather", "chan_combine", "expert_fused", "router_align",
-                                                  "router_slices", "router_tokens"};
+                                                  "chan_gather", "chan_combine", "expert_fused", "router_align"};
     return (k >= 0 && k < MOE_KERNEL_COUNT) ? names[k] : nullptr;
 }
 
@@ -214,7 +191,7 @@ moe_status moe_create(const moe_config* cfg, const moe_weights* w, moe_ctx** out
     }
     const size_t nchan = c.max_keep > 0 ? (c.max_keep + kChanChunk - 1) / kChanChunk : 0;
     size_t sizes[8] = {
-        256,                                                            // err flag, router ticket
+        64 + sizeof(unsigned) * (1 + (size_t)moe::router_groups((int)MT)),  // err flag, router tickets
         sizeof(float) * moe::gemv_slices(c.H, c.E) * MT * c.E,          // router partials
         sizeof(float) * zsl * MT * c.lr_r,                              // z = D^T h partials (gate)
         sizeof(float) * zsl * MT * c.lr_r,                              // z partials (up)
@@ -243,7 +220,7 @@ moe_status moe_create(const moe_config* cfg, const moe_weights* w, moe_ctx** out
     ctx->down_part = reinterpret_cast<float*>(base + off[5]);
     ctx->kept_ws = reinterpret_cast<int32_t*>(base + off[6]);
     ctx->chan_part = reinterpret_cast<float*>(base + off[7]);
-    if (hipMemset(ctx->err, 0, 256) != hipSuccess || hipDeviceSynchronize() != hipSuccess) {
+    if (hipMemset(ctx->err, 0, sizes[0]) != hipSuccess || hipDeviceSynchronize() != hipSuccess) {
         hipFree(ctx->ws);
         delete ctx;
         return MOE_ERR_HIP;
@@ -272,8 +249,6 @@ moe_status moe_route_topk(moe_ctx* ctx, const float* h, int32_t M, int32_t* topk
     if (!h || !topk_ids || !topk_w || !aligned(h, 16)) return MOE_ERR_INVALID_ARG;
     const moe_config& c = ctx->cfg;
     hipStream_t s = static_cast<hipStream_t>(stream);
-    if (M > moe::kRouterOneLaunchTokens)
-        return route_two_launches(ctx, h, M, topk_ids, topk_w, logits_out, nullptr, nullptr, nullptr, s);
     Launch l(ctx, MOE_KERNEL_ROUTER, s);
     hipError_t e = moe::launch_router(h, M, c.H, ctx->w.router_w, c.E, ctx->w.router_bias, c.top_k, ctx->router_part,
                                       ctx->ticket, topk_ids, topk_w, logits_out, s);
@@ -291,8 +266,6 @@ moe_status moe_route_align(moe_ctx* ctx, const float* h, int32_t M, int32_t* top
     if (!h || !topk_ids || !topk_w || !sorted_routes || !block_expert || !aligned(h, 16)) return MOE_ERR_INVALID_ARG;
     const moe_config& c = ctx->cfg;
     hipStream_t s = static_cast<hipStream_t>(stream);
-    if (M > moe::kRouterOneLaunchTokens)
-        return route_two_launches(ctx, h, M, topk_ids, topk_w, logits_out, sorted_routes, block_expert, counts, s);
     Launch l(ctx, MOE_KERNEL_ROUTER_ALIGN, s);
     hipError_t e = moe::launch_router_align(h, M, c.H, ctx->w.router_w, c.E, ctx->w.router_bias, c.top_k,
                                             ctx->router_part, ctx->ticket, topk_ids, topk_w, logits_out, c.block_b,

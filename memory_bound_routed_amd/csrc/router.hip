@@ -141,8 +141,9 @@ gemv_partials_kernel(const float* __restrict__ h, int M, int H, GemvJobs jobs) {
         slice_partial<kTokTile, false>(h, M, H, jb.W, jb.N, blockIdx.x, jb.part, red);
 }
 
-// Router GEMV tiles (batches of up to kTokTile tokens): the grid covers
-// row slices x column groups of cgw experts (32, or 16 / 8 for small E);
+// Router GEMV tiles: the grid covers row slices x column groups of cgw
+// experts (32, or 16 / 8 for small E) along x, groups of kTokTile tokens
+// along y;
 // tpr = cgw/8 threads cover a row of the group with one 16-byte load each,
 // rpt = 256/tpr rows per pass, kRowsPerThread passes per slice.  The rpt row
 // groups of an output are added by 8 lanes (rpt/8 groups each, in order),
@@ -163,9 +164,10 @@ struct RouterTiles {
 };
 
 template <int TT>
-__device__ __forceinline__ void router_tile(const float* __restrict__ h, int M, int H, const uint16_t* __restrict__ W,
-                                            int E, const RouterTiles& tl, int rs, int cg, float* __restrict__ part,
-                                            float* red) {
+__device__ __forceinline__ void router_tile(const float* __restrict__ h, int M, int t0, int H,
+                                            const uint16_t* __restrict__ W, int E, const RouterTiles& tl, int rs,
+                                            int cg, float* __restrict__ part, float* red) {
+    const int Mg = min(TT, M - t0);  // tokens t0 .. t0+Mg-1 of this workgroup
     const int tid = threadIdx.x;
     const int c8 = tid % tl.tpr;
     const int rg = tid / tl.tpr;
@@ -181,14 +183,14 @@ __device__ __forceinline__ void router_tile(const float* __restrict__ h, int M, 
         const int i = min(r0 + rg + u * tl.rpt, H - 1);
         wv[u] = load_stream16(W + (size_t)i * E + ec);
 #pragma unroll
-        for (int t = 0; t < TT; ++t) hv[u][t] = h[(size_t)min(t, M - 1) * H + i];
+        for (int t = 0; t < TT; ++t) hv[u][t] = h[(size_t)(t0 + min(t, Mg - 1)) * H + i];
     }
     const bool col_ok = e0 < E;
 #pragma unroll
     for (int u = 0; u < kRowsPerThread; ++u) {
         const bool row_ok = col_ok && r0 + rg + u * tl.rpt < H;
 #pragma unroll
-        for (int t = 0; t < TT; ++t) hv[u][t] = (row_ok && t < M) ? hv[u][t] : 0.f;
+        for (int t = 0; t < TT; ++t) hv[u][t] = (row_ok && t < Mg) ? hv[u][t] : 0.f;
     }
     float acc[TT][8];
 #pragma unroll
@@ -213,7 +215,7 @@ __device__ __forceinline__ void router_tile(const float* __restrict__ h, int M, 
     // in the butterfly)
     const int sub = tid % 8;
     const int gpl = tl.rpt / 8;  // row groups per lane
-    const int nout = min(M, TT) * tl.cgw;
+    const int nout = Mg * tl.cgw;
     for (int o0 = 0; o0 < nout; o0 += kThreads / 8) {
         const int o = o0 + tid / 8;
         const int t = o / tl.cgw, c = o - t * tl.cgw;
@@ -226,13 +228,13 @@ __device__ __forceinline__ void router_tile(const float* __restrict__ h, int M, 
         v += __shfl_xor(v, 2, MOE_WAVE);
         v += __shfl_xor(v, 4, MOE_WAVE);
         const int e = cg * tl.cgw + c;
-        if (sub == 0 && o < nout && e < E) store_agent(part + ((size_t)rs * M + t) * E + e, v);
+        if (sub == 0 && o < nout && e < E) store_agent(part + ((size_t)rs * M + t0 + t) * E + e, v);
     }
 }
 
-// Router: slices as above; the last workgroup to finish (integer ticket)
-// adds the slices in slice order (+ bias) for up to four tokens at a time --
-// every partial load of a pass is issued before the first add.  The top-k is
+// Router: tiles as above; per group of tokens, the last tile workgroup to
+// finish (integer ticket) adds the slices in slice order (+ bias) -- every
+// partial load is issued before the first add.  The top-k is
 // taken by rank counting under the total order (logit desc, expert id asc):
 // rank(e) = #{e' : l[e'] > l[e] or (l[e'] == l[e] and e' < e)}, and the
 // expert of rank s < k goes to slot s.  The ranks are exact, so the result
@@ -244,12 +246,10 @@ __device__ __forceinline__ void router_tile(const float* __restrict__ h, int M, 
 // completed, one thread per workgroup takes a ticket, and the workgroup
 // holding the last ticket reads every slice.  Nothing waits on another
 // workgroup, and no cache is written back or invalidated.
-// Slice partials requested together per thread: the tiled router has at most
-// a few slices, and its device-coherent loads are served one instruction at
-// a time (so clamped duplicates would cost as much as real slices); the
-// two-launch path reads up to 32 slices with plain loads.
+// Slice partials requested together per thread: there are few slices, and
+// device-coherent loads are served one instruction at a time (clamped
+// duplicates would cost as much as real slices).
 constexpr int kSliceBatchTiles = 8;
-constexpr int kSliceBatch = 32;
 
 // Selected (expert, logit) of the tokens of the current pass, slot order.
 struct TopkLds {
@@ -358,9 +358,13 @@ __device__ __forceinline__ void topk_pass(int t0, int nt, int M, int E, int k, i
     }
 }
 
-// Returns true in the last workgroup (which has written ids and weights; the
-// selections of the last pass stay in sel).
-template <int TT>
+// Token group g = blockIdx.y (tokens g*TT ..): the group's tiles, then -- in
+// the last tile workgroup of the group to finish (ticket 1 + g) -- the slice
+// sum, top-k and softmax of the group's tokens.  Returns true in that
+// workgroup (which has written the group's ids and weights; its selections
+// stay in sel).  COHERENT_IDS: the ids are read by another workgroup of the
+// launch.
+template <int TT, bool COHERENT_IDS>
 __device__ __forceinline__ bool router_body(const float* __restrict__ h, int M, int H, const uint16_t* __restrict__ Wr,
                                             int E, const float* __restrict__ bias, int k, float* __restrict__ part,
                                             unsigned* __restrict__ ticket, int32_t* __restrict__ ids,
@@ -368,27 +372,25 @@ __device__ __forceinline__ bool router_body(const float* __restrict__ h, int M, 
                                             TopkLds& sel, FastDiv fE) {
     __shared__ int s_last;
     const RouterTiles tl(H, E);
-    const int nslices = tl.nrs;
-    router_tile<TT>(h, M, H, Wr, E, tl, blockIdx.x % tl.nrs, blockIdx.x / tl.nrs, part, red);
+    const int t0 = blockIdx.y * TT;
+    router_tile<TT>(h, M, t0, H, Wr, E, tl, blockIdx.x % tl.nrs, blockIdx.x / tl.nrs, part, red);
     __builtin_amdgcn_s_waitcnt(0);  // this wave's partial stores have completed
     __syncthreads();
-    if (threadIdx.x == 0) s_last = atomicAdd(ticket, 1u) == (unsigned)(gridDim.x - 1);
+    if (threadIdx.x == 0) s_last = atomicAdd(ticket + 1 + blockIdx.y, 1u) == (unsigned)(gridDim.x - 1);
     __syncthreads();
     if (!s_last) return false;
-    for (int t0 = 0; t0 < M; t0 += TT) {
-        topk_pass<true, false, kSliceBatchTiles>(t0, min(TT, M - t0), M, E, k, nslices, part, bias, logits_out, ids,
-                                                 wts, red, sel, fE);
-        if (t0 + TT < M) __syncthreads();  // sel and the keys are reused by the next pass
-    }
+    topk_pass<true, COHERENT_IDS, kSliceBatchTiles>(t0, min(TT, M - t0), M, E, k, tl.nrs, part, bias, logits_out, ids,
+                                                    wts, red, sel, fE);
     return true;
 }
 
-// The last workgroup re-arms the ticket for the next call on this context, as
-// its final action (no barrier follows, so nothing waits for the atomic).
+// A ticket's last workgroup re-arms it for the next call on this context
+// (after its last barrier, so nothing waits for the atomic).
 __device__ __forceinline__ void rearm_ticket(unsigned* ticket) {
     if (threadIdx.x == 0) atomicExch(ticket, 0u);
 }
 
+// ticket: [0] alignment ticket, [1 + g] token group g; zeroed, left zeroed.
 __global__ void __launch_bounds__(kThreads)
 router_kernel(const float* __restrict__ h, int M, int H, const uint16_t* __restrict__ Wr, int E,
               const float* __restrict__ bias, int k, float* __restrict__ part, unsigned* __restrict__ ticket,
@@ -398,15 +400,19 @@ router_kernel(const float* __restrict__ h, int M, int H, const uint16_t* __restr
     pin_arg(bias); pin_arg(k); pin_arg(E); pin_arg(M); pin_arg(ids); pin_arg(wts); pin_arg(logits_out);
     pin_arg(ticket); pin_arg(part); pin_arg(fE.m); pin_arg(fE.s);
     const bool last =
-        M == 1 ? router_body<1>(h, M, H, Wr, E, bias, k, part, ticket, ids, wts, logits_out, red, sel, fE)
-               : router_body<kTokTile>(h, M, H, Wr, E, bias, k, part, ticket, ids, wts, logits_out, red, sel, fE);
-    if (last) rearm_ticket(ticket);
+        M == 1 ? router_body<1, false>(h, M, H, Wr, E, bias, k, part, ticket, ids, wts, logits_out, red, sel, fE)
+               : router_body<kTokTile, false>(h, M, H, Wr, E, bias, k, part, ticket, ids, wts, logits_out, red, sel,
+                                              fE);
+    if (last) rearm_ticket(ticket + 1 + blockIdx.y);
 }
 
-// Router, then the canonical alignment of the ids in the last workgroup.  Up
-// to 64 routes of a single pass are aligned by wave 0 from the selections
-// still in LDS; otherwise the whole workgroup aligns the ids it has written
-// (the barrier makes them visible to it).
+// Router, then the canonical alignment of all M*k routes.  One token group
+// (M <= 4): its last workgroup aligns -- up to 64 routes by wave 0 from the
+// selections still in LDS, else the whole workgroup from the ids it has
+// written (the barrier makes them visible to it).  Several groups: each
+// group's last workgroup publishes its ids device-coherently and, once its
+// stores have completed, takes the alignment ticket; the last one aligns,
+// reading the ids device-coherently.
 __global__ void __launch_bounds__(kThreads)
 router_align_kernel(const float* __restrict__ h, int M, int H, const uint16_t* __restrict__ Wr, int E,
                     const float* __restrict__ bias, int k, float* __restrict__ part, unsigned* __restrict__ ticket,
@@ -415,62 +421,44 @@ router_align_kernel(const float* __restrict__ h, int M, int H, const uint16_t* _
                     int32_t* __restrict__ counts, int32_t* __restrict__ err, FastDiv fE, FastDiv fk, FastDiv fb) {
     extern __shared__ __align__(16) float red[];
     __shared__ TopkLds sel;
+    __shared__ int s_last;
     pin_arg(bias); pin_arg(k); pin_arg(E); pin_arg(M); pin_arg(ids); pin_arg(wts); pin_arg(logits_out);
     pin_arg(ticket); pin_arg(part); pin_arg(b); pin_arg(sorted_routes); pin_arg(block_expert); pin_arg(counts);
     pin_arg(err); pin_arg(fE.m); pin_arg(fE.s); pin_arg(fk.m); pin_arg(fk.s); pin_arg(fb.m); pin_arg(fb.s);
-    const int TT = M == 1 ? 1 : kTokTile;
     const bool last =
-        M == 1 ? router_body<1>(h, M, H, Wr, E, bias, k, part, ticket, ids, wts, logits_out, red, sel, fE)
-               : router_body<kTokTile>(h, M, H, Wr, E, bias, k, part, ticket, ids, wts, logits_out, red, sel, fE);
+        M == 1 ? router_body<1, false>(h, M, H, Wr, E, bias, k, part, ticket, ids, wts, logits_out, red, sel, fE)
+               : router_body<kTokTile, true>(h, M, H, Wr, E, bias, k, part, ticket, ids, wts, logits_out, red, sel,
+                                             fE);
     if (!last) return;
     const int R = M * k;
-    if (M <= TT && R <= MOE_WAVE) {
-        // sel was complete at the top-k's last barrier and is only read since
-        if (threadIdx.x < MOE_WAVE)
-            align_wave([&](int r) { const int t = fk.div(r); return sel.e[t][r - t * k]; }, R, E, fb, sorted_routes,
-                       block_expert, counts, err);
-        rearm_ticket(ticket);
+    if (gridDim.y == 1) {
+        if (R <= MOE_WAVE) {
+            // sel was complete at the top-k's last barrier and is only read since
+            if (threadIdx.x < MOE_WAVE)
+                align_wave([&](int r) { const int t = fk.div(r); return sel.e[t][r - t * k]; }, R, E, fb,
+                           sorted_routes, block_expert, counts, err);
+        } else {
+            __syncthreads();
+            align_workgroup([&](int r) { return ids[r]; }, R, E, b, sorted_routes, block_expert, counts, err,
+                            reinterpret_cast<int*>(red));
+        }
+        rearm_ticket(ticket + 1);
         return;
     }
+    rearm_ticket(ticket + 1 + blockIdx.y);  // every tile of the group has taken its ticket
+    __builtin_amdgcn_s_waitcnt(0);          // this wave's id and weight stores have completed
     __syncthreads();
-    align_workgroup([&](int r) { return ids[r]; }, R, E, b, sorted_routes, block_expert, counts, err,
-                    reinterpret_cast<int*>(red));
-    rearm_ticket(ticket);
-}
-
-// Batches of more than kTokTile tokens: the slice partials come from
-// gemv_partials_kernel (previous launch); here one workgroup per token sums
-// them, takes the top-k and the softmax (same arithmetic and order as the
-// one-launch router).  ALIGN: every workgroup publishes its ids device-
-// coherently and takes a ticket once its stores have completed; the last one
-// aligns all M*k routes, reading the ids device-coherently.
-template <bool ALIGN>
-__global__ void __launch_bounds__(kThreads)
-router_tokens_kernel(int M, int E, const float* __restrict__ bias, int k, int nslices, const float* __restrict__ part,
-                     unsigned* __restrict__ ticket, int32_t* __restrict__ ids, float* __restrict__ wts,
-                     float* __restrict__ logits_out, int b, int32_t* __restrict__ sorted_routes,
-                     int32_t* __restrict__ block_expert, int32_t* __restrict__ counts, int32_t* __restrict__ err,
-                     FastDiv fE, FastDiv fb) {
-    extern __shared__ __align__(16) float red[];
-    __shared__ TopkLds sel;
-    __shared__ int s_last;
-    topk_pass<false, ALIGN, kSliceBatch>(blockIdx.x, 1, M, E, k, nslices, part, bias, logits_out, ids, wts, red, sel,
-                                         fE);
-    if (!ALIGN) return;
-    __builtin_amdgcn_s_waitcnt(0);  // this wave's id and weight stores have completed
-    __syncthreads();
-    if (threadIdx.x == 0) s_last = atomicAdd(ticket, 1u) == (unsigned)(M - 1);
+    if (threadIdx.x == 0) s_last = atomicAdd(ticket, 1u) == (unsigned)(gridDim.y - 1);
     __syncthreads();
     if (!s_last) return;
-    const int R = M * k;
     if (R <= MOE_WAVE) {
         if (threadIdx.x < MOE_WAVE)
             align_wave([&](int r) { return load_agent(ids + r); }, R, E, fb, sorted_routes, block_expert, counts, err);
     } else {
-        align_workgroup([&](int r) { return load_agent(ids + r); }, R, E, b, sorted_routes, block_expert, counts,
-                        err, reinterpret_cast<int*>(red));
+        align_workgroup([&](int r) { return load_agent(ids + r); }, R, E, b, sorted_routes, block_expert, counts, err,
+                        reinterpret_cast<int*>(red));
     }
-    if (threadIdx.x == 0) atomicExch(ticket, 0u);  // ready for the next call on this context
+    rearm_ticket(ticket);
 }
 
 size_t lds_bytes(int N) { return (size_t)(kThreads / (N / 8)) * kTokTile * N * sizeof(float); }
@@ -491,6 +479,8 @@ int router_grid(int H, int E) {
 }
 
 }  // namespace
+
+int router_groups(int M) { return M == 1 ? 1 : (M + kTokTile - 1) / kTokTile; }
 
 int gemv_slices(int H, int N) {
     const int rpp = kThreads / (N / 8);
@@ -515,38 +505,22 @@ hipError_t launch_router_align(const float* h, int M, int H, const uint16_t* Wr,
                                float* part, unsigned* ticket, int32_t* ids, float* wts, float* logits_out, int b,
                                int32_t* sorted_routes, int32_t* block_expert, int32_t* counts, int32_t* err,
                                hipStream_t stream) {
-    if (M < 1 || M > kTokTile || E % 8 != 0) return hipErrorInvalidValue;
+    if (M < 1 || E % 8 != 0) return hipErrorInvalidValue;
     const size_t la = align_lds_bytes(M * k, E);
     const size_t lds = router_lds_bytes(H, E) > la ? router_lds_bytes(H, E) : la;
-    MOE_LAUNCH(router_align_kernel, dim3(router_grid(H, E)), dim3(kThreads), lds, stream, h, M, H, Wr, E, bias,
+    MOE_LAUNCH(router_align_kernel, dim3(router_grid(H, E), router_groups(M)), dim3(kThreads), lds, stream, h, M, H,
+               Wr, E, bias,
                        k, part, ticket, ids, wts, logits_out, b, sorted_routes, block_expert, counts, err,
                        FastDiv((uint32_t)E), FastDiv((uint32_t)k), FastDiv((uint32_t)b));
-    return hipGetLastError();
-}
-
-hipError_t launch_router_tokens(int M, int H, int E, const float* bias, int k, const float* part, unsigned* ticket,
-                                int32_t* ids, float* wts, float* logits_out, int b, int32_t* sorted_routes,
-                                int32_t* block_expert, int32_t* counts, int32_t* err, hipStream_t stream) {
-    const size_t topk = (size_t)E * (sizeof(uint64_t) + 2 * sizeof(int));
-    const int nslices = gemv_slices(H, E);
-    if (sorted_routes) {
-        const size_t la = align_lds_bytes(M * k, E);
-        MOE_LAUNCH(router_tokens_kernel<true>, dim3(M), dim3(kThreads), topk > la ? topk : la, stream, M, E, bias, k,
-                   nslices, part, ticket, ids, wts, logits_out, b, sorted_routes, block_expert, counts, err,
-                   FastDiv((uint32_t)E), FastDiv((uint32_t)b));
-    } else {
-        MOE_LAUNCH(router_tokens_kernel<false>, dim3(M), dim3(kThreads), topk, stream, M, E, bias, k, nslices, part,
-                   ticket, ids, wts, logits_out, b, sorted_routes, block_expert, counts, err, FastDiv((uint32_t)E),
-                   FastDiv((uint32_t)1));
-    }
     return hipGetLastError();
 }
 
 hipError_t launch_router(const float* h, int M, int H, const uint16_t* Wr, int E, const float* bias, int k,
                          float* part, unsigned* ticket, int32_t* ids, float* wts, float* logits_out,
                          hipStream_t stream) {
-    if (M < 1 || M > kTokTile || E % 8 != 0) return hipErrorInvalidValue;
-    MOE_LAUNCH(router_kernel, dim3(router_grid(H, E)), dim3(kThreads), router_lds_bytes(H, E), stream, h, M, H, Wr, E,
+    if (M < 1 || E % 8 != 0) return hipErrorInvalidValue;
+    MOE_LAUNCH(router_kernel, dim3(router_grid(H, E), router_groups(M)), dim3(kThreads), router_lds_bytes(H, E), stream,
+               h, M, H, Wr, E,
                        bias, k, part, ticket, ids, wts, logits_out, FastDiv((uint32_t)E));
     return hipGetLastError();
 }

@@ -17,17 +17,11 @@ U32 = 2.0 ** -24         # unit roundoff of fp32
 
 def router_depth(H: int, E: int) -> int:
     """Upper bound on the summation depth of a router logit, as documented in
-    moe.h, over both router schedules.  Tiles (up to 4 tokens): 4 rows per
-    thread, rpt/8 row groups in order per lane, a 3-level butterfly over 8
-    lanes, the row slices in order, one bias add.  Row slices (more tokens):
-    4 rows per thread, the rpp row groups in order, the row slices in order,
-    one bias add."""
+    moe.h: 4 rows per thread, rpt/8 row groups in order per lane, a 3-level
+    butterfly over 8 lanes, the row slices in order, one bias add."""
     c = 32 if E >= 32 else (16 if E >= 16 else 8)
     rpt = 2048 // c
-    tiles = 4 + rpt // 8 + 3 + math.ceil(H / (4 * rpt)) + 1
-    rpp = 2048 // E
-    slices = 4 + rpp + math.ceil(H / (4 * rpp)) + 1
-    return max(tiles, slices)
+    return 4 + rpt // 8 + 3 + math.ceil(H / (4 * rpt)) + 1
 
 
 def logit_error_bound(h: np.ndarray, router_w: np.ndarray, H: int, bias: Optional[np.ndarray] = None) -> np.ndarray:
