@@ -28,54 +28,91 @@ constexpr int kRT = 4;    // routes staged together
 constexpr int kD = 8;     // VQ block length supported by this kernel
 constexpr int kZBatch = 16;
 
-__device__ __forceinline__ int run_expert_vq(const PlanArgs& plan, int blk, int* nb_out, int32_t* err) {
-    int nb = plan.counts[0];
-    if (nb < 0 || nb > plan.max_blocks) {
-        if (blk == 0 && blockIdx.y == 0 && threadIdx.x == 0) atomicOr(err, DEVERR_BAD_COUNTS);
-        nb = nb < 0 ? 0 : plan.max_blocks;
-    }
-    *nb_out = nb;
-    if (blk >= nb) return -1;
-    const int e = plan.block_expert[blk];
-    if (e < 0 || e >= plan.E) {
-        if (blockIdx.y == 0 && threadIdx.x == 0) atomicOr(err, DEVERR_BAD_BLOCK_EXPERT);
-        return -1;
-    }
-    if (blk > 0 && plan.block_expert[blk - 1] == e) return -1;
-    return e;
-}
-
 // Grid (plan blocks, ceil(I / (4*CPW))): workgroup (blk, cy) owns 4*CPW
 // channels of the expert whose run of blocks starts at blk; wave w owns CPW
 // of them.  Lane l owns VQ blocks 4*(l + 64*qb) .. +3 (one 4-byte index load
 // per channel) and low-rank coordinates rho = l + 64*m.  The index maps and
-// coefficients are requested first and kept in registers for every route of
-// the expert; the two code books go to LDS.  Routes are taken rvq at a time:
-// their h rows and their finished z vectors (the slice partials added in
-// slice order) are staged in LDS, then every wave forms its channels'
-// outputs.
+// coefficients are kept in registers for every route of the expert; the two
+// code books go to LDS.  A route needs its h row and its finished z vectors
+// (the slice partials added in slice order) in LDS.
+// Loads are ordered by what they wait for: the plan rows come first; then,
+// before the index and coefficient stream, the row checks, the code books
+// and h and the z partials of row 0 (the expert's first route in a
+// well-formed plan, and at small batch usually its only one), since a load
+// queued behind the stream would wait for all of it.  Further routes are
+// staged rvq at a time.
 template <int QB, int RM, int CPW>
 __global__ void __launch_bounds__(kThreads)
 gateup_vqlr_kernel(PlanArgs plan, VqArgs vq, const float* __restrict__ h, int H, int I, int rvq, float* __restrict__ p,
                    int32_t* __restrict__ err) {
+    constexpr int HPT = QB * 2;                // float4 of one h row per thread (H <= QB * 2048)
+    constexpr int ZPT = RM > 2 ? RM / 2 : 1;   // (projection, rho) items of one route per thread
     __shared__ uint4 book[2][256];
     extern __shared__ __align__(16) float dyn[];
     float* hsm = dyn;                       // [rvq][H]
     float* zsm = dyn + (size_t)rvq * H;     // [kRT][2][r]
     const int blk = blockIdx.x;
-    int nb;
-    const int e = run_expert_vq(plan, blk, &nb, err);
-    if (e < 0) return;  // uniform over the workgroup
+    const int b = plan.b;
     const int tid = threadIdx.x;
     const int wave = tid / MOE_WAVE;
     const int lane = tid % MOE_WAVE;
-    const int nbk = H / kD;        // VQ blocks per channel
-    const int r = vq.r;
-    const int j0 = (blockIdx.y * kWaves + wave) * CPW;
-    const bool active = j0 < I;   // inactive waves still take part in the barriers
 
+    // Round 1: counts, the previous, this and the next block's expert, the
+    // block's rows.
+    int nb = plan.counts[0];
+    const int e = plan.block_expert[blk];
+    const int eprev = blk > 0 ? plan.block_expert[blk - 1] : -1;
+    const int enext = plan.block_expert[min(blk + 1, plan.max_blocks - 1)];  // checked against nb below
+    int rv = plan.sorted_routes[(size_t)blk * b + min(lane, b - 1)];
+    if (lane >= b) rv = plan.R;
+    if (nb < 0 || nb > plan.max_blocks) {
+        if (blk == 0 && blockIdx.y == 0 && tid == 0) atomicOr(err, DEVERR_BAD_COUNTS);
+        nb = nb < 0 ? 0 : plan.max_blocks;
+    }
+    if (blk >= nb) return;
+    if (e < 0 || e >= plan.E) {
+        if (blockIdx.y == 0 && tid == 0) atomicOr(err, DEVERR_BAD_BLOCK_EXPERT);
+        return;
+    }
+    if (eprev == e) return;  // not the first block of the expert's run (uniform)
+    const int nbk = H / kD;  // VQ blocks per channel
+    const int r = vq.r;
+    const int H4 = H / 4;
+    const int j0 = (blockIdx.y * kWaves + wave) * CPW;
+    const bool active = j0 < I;  // inactive waves still take part in the barriers
+
+    // Round 2 (clamped, always-valid addresses).
+    const int idv = plan.topk_ids[min(max(rv, 0), plan.R - 1)];
+    // (the argument struct's arrays are indexed by compile-time constants or
+    // through a select: a run-time index would load the pointer from the
+    // kernel-argument segment with a vector load)
+    const int r0 = __builtin_amdgcn_readfirstlane(rv);
+    const int t0 = plan.fk.div(min(max(r0, 0), plan.R - 1));
+    uint4 bk[2];
+#pragma unroll
+    for (int u = 0; u < 2; ++u) {
+        const int i = tid + kThreads * u;
+        bk[u] = load16(vq.B[i >> 8] + (size_t)min(i & 255, vq.K - 1) * kD);
+    }
+    float4 h0[HPT];
+#pragma unroll
+    for (int v = 0; v < HPT; ++v)
+        h0[v] = reinterpret_cast<const float4*>(h + (size_t)t0 * H)[min(tid + kThreads * v, H4 - 1)];
+    float zx[ZPT][kZBatch];
+#pragma unroll
+    for (int w = 0; w < ZPT; ++w) {
+        const int it = min(tid + kThreads * w, 2 * r - 1);
+        const int P = it >= r ? 1 : 0, rho = it - P * r;
+#pragma unroll
+        for (int u = 0; u < kZBatch; ++u)
+            zx[w][u] = (P ? vq.zpart[1] : vq.zpart[0])[((size_t)min(u, vq.zslices - 1) * vq.M + t0) * r + rho];
+    }
+
+    __builtin_amdgcn_sched_barrier(0);  // keeps the loads above ahead of the stream below
+
+    // The index and coefficient stream.
     uint32_t jw[2][CPW][QB];
-    float cv[2][CPW][RM];
+    uint32_t cw16[2][CPW][RM];  // bf16 patterns, converted (and masked) where used
 #pragma unroll
     for (int P = 0; P < 2; ++P)
 #pragma unroll
@@ -83,118 +120,160 @@ gateup_vqlr_kernel(PlanArgs plan, VqArgs vq, const float* __restrict__ h, int H,
             const int j = min(j0 + c, I - 1);
             const uint8_t* jrow = vq.J[P] + ((size_t)e * I + j) * nbk;
             const uint16_t* crow = vq.C[P] + ((size_t)e * I + j) * r;
+            // Unconditional loads of clamped addresses, used as loaded: a
+            // select here would let the compiler put the load in a branch,
+            // which is waited for at the branch's end, one load at a time.
+            // Lanes past the last block or coordinate are masked where used.
 #pragma unroll
             for (int qb = 0; qb < QB; ++qb) {
                 const int b4 = 4 * (lane + MOE_WAVE * qb);
-                jw[P][c][qb] = b4 < nbk ? __builtin_nontemporal_load(reinterpret_cast<const uint32_t*>(jrow + min(b4, nbk - 4))) : 0u;
+                jw[P][c][qb] = __builtin_nontemporal_load(reinterpret_cast<const uint32_t*>(jrow + min(b4, nbk - 4)));
             }
 #pragma unroll
             for (int m = 0; m < RM; ++m) {
                 const int rho = lane + MOE_WAVE * m;
-                cv[P][c][m] = rho < r ? bf16_lo(__builtin_nontemporal_load(crow + min(rho, r - 1))) : 0.f;
+                cw16[P][c][m] = __builtin_nontemporal_load(crow + min(rho, r - 1));
             }
         }
-    for (int i = tid; i < 2 * 256; i += kThreads) {
-        const int P = i / 256, c = i % 256;
-        book[P][c] = c < vq.K ? load16(vq.B[P] + (size_t)c * kD) : make_uint4(0, 0, 0, 0);
-    }
 
-    // routes of the expert's run, one block at a time (lane q holds row q)
-    for (int bb = blk; bb < nb; ++bb) {
-        if (bb > blk && plan.block_expert[bb] != e) break;
-        int rv = lane < plan.b ? plan.sorted_routes[(size_t)bb * plan.b + lane] : plan.R;
-        const bool ok = rv >= 0 && rv < plan.R && plan.topk_ids[rv] == e;
-        if (!ok && rv != plan.R && wave == 0 && blockIdx.y == 0) atomicOr(err, DEVERR_BAD_PLAN);
-        uint64_t todo = __ballot(ok);
-        while (todo) {
-            int rt[kRT];
-            int nr = 0;
+    // Round 2 into LDS (in the stream's basic block, so that nothing moves
+    // these loads behind it): the code books, and slot 0 with row 0's h and z.
 #pragma unroll
-            for (int i = 0; i < kRT; ++i) {
-                rt[i] = -1;
-                if (i < rvq && todo) {
-                    const int q = __builtin_ctzll(todo);
-                    todo &= todo - 1;
-                    rt[i] = __builtin_amdgcn_readlane(rv, q);
-                    nr = i + 1;
-                }
+    for (int u = 0; u < 2; ++u) {
+        const int i = tid + kThreads * u;
+        book[i >> 8][i & 255] = (i & 255) < vq.K ? bk[u] : make_uint4(0, 0, 0, 0);
+    }
+#pragma unroll
+    for (int v = 0; v < HPT; ++v)  // unconditional (clamped duplicates store the same value)
+        reinterpret_cast<float4*>(hsm)[min(tid + kThreads * v, H4 - 1)] = h0[v];
+#pragma unroll
+    for (int w = 0; w < ZPT; ++w) {
+        const int it = tid + kThreads * w;
+        float z = 0.f;
+#pragma unroll
+        for (int u = 0; u < kZBatch; ++u) z += u < vq.zslices ? zx[w][u] : 0.f;  // slice order
+        if (it < 2 * r) {
+            const int P = it >= r ? 1 : 0, rho = it - P * r;
+            for (int sl = kZBatch; sl < vq.zslices; ++sl) z += (P ? vq.zpart[1] : vq.zpart[0])[((size_t)sl * vq.M + t0) * r + rho];
+            zsm[it] = z;
+        }
+    }
+    auto rows_ok = [&](int rvx, int idx) {
+        const bool ok = rvx >= 0 && rvx < plan.R && idx == e;
+        if (!ok && rvx != plan.R && wave == 0 && blockIdx.y == 0) atomicOr(err, DEVERR_BAD_PLAN);
+        return __ballot(ok);
+    };
+    uint64_t todo = rows_ok(rv, idv);
+    __syncthreads();
+
+    // One route from LDS slot i: o_P[j] = C_e[j] . z + sum over blocks of the
+    // selected code words applied to h's blocks, then p = SiLU(o_gate) * o_up.
+    auto compute = [&](int i, int route) {
+        float acc[2][CPW];
+#pragma unroll
+        for (int P = 0; P < 2; ++P)
+#pragma unroll
+            for (int c = 0; c < CPW; ++c) acc[P][c] = 0.f;
+#pragma unroll
+        for (int P = 0; P < 2; ++P)
+#pragma unroll
+            for (int m = 0; m < RM; ++m) {
+                const int rho = lane + MOE_WAVE * m;
+                const float z = rho < r ? zsm[(i * 2 + P) * r + rho] : 0.f;
+#pragma unroll
+                for (int c = 0; c < CPW; ++c)
+                    acc[P][c] = fmaf(rho < r ? bf16_lo(cw16[P][c][m]) : 0.f, z, acc[P][c]);
             }
-            __syncthreads();  // the previous group's staging (and the book) is complete / no longer read
 #pragma unroll
-            for (int i = 0; i < kRT; ++i) {
-                if (i >= nr) break;
-                const float4* src = reinterpret_cast<const float4*>(h + (size_t)(rt[i] / plan.k) * H);
-                float4* dst = reinterpret_cast<float4*>(hsm + (size_t)i * H);
-                for (int c4 = tid; c4 < H / 4; c4 += kThreads) dst[c4] = src[c4];
+        for (int qb = 0; qb < QB; ++qb) {
+            const int b4 = 4 * (lane + MOE_WAVE * qb);
+            if (b4 >= nbk) continue;
+            const float4* hr = reinterpret_cast<const float4*>(hsm + (size_t)i * H + b4 * kD);
+            float hv[32];
+#pragma unroll
+            for (int v = 0; v < 8; ++v) {
+                const float4 x = hr[v];
+                hv[4 * v] = x.x; hv[4 * v + 1] = x.y; hv[4 * v + 2] = x.z; hv[4 * v + 3] = x.w;
             }
-            for (int it = tid; it < nr * 2 * r; it += kThreads) {
-                const int i = it / (2 * r), rem = it - i * 2 * r, P = rem / r, rho = rem - P * r;
-                int ti = 0;
 #pragma unroll
-                for (int ii = 0; ii < kRT; ++ii)
-                    if (ii == i) ti = rt[ii] / plan.k;
-                float z = 0.f;
-                for (int sl0 = 0; sl0 < vq.zslices; sl0 += kZBatch) {
-                    float x[kZBatch];
+            for (int P = 0; P < 2; ++P)
 #pragma unroll
-                    for (int u = 0; u < kZBatch; ++u)
-                        x[u] = vq.zpart[P][((size_t)min(sl0 + u, vq.zslices - 1) * vq.M + ti) * r + rho];
+                for (int c = 0; c < CPW; ++c)
 #pragma unroll
-                    for (int u = 0; u < kZBatch; ++u) z += sl0 + u < vq.zslices ? x[u] : 0.f;  // slice order
-                }
-                zsm[it] = z;
-            }
-            __syncthreads();
-            if (!active) continue;
+                    for (int x = 0; x < 4; ++x) {
+                        float cw[8];
+                        unpack8(book[P][(jw[P][c][qb] >> (8 * x)) & 255u], cw);
 #pragma unroll
-            for (int i = 0; i < kRT; ++i) {
-                if (i >= nr) break;
-                float acc[2][CPW];
-#pragma unroll
-                for (int P = 0; P < 2; ++P)
-#pragma unroll
-                    for (int c = 0; c < CPW; ++c) acc[P][c] = 0.f;
-                // low-rank term: C_e[j] . z
-#pragma unroll
-                for (int P = 0; P < 2; ++P)
-#pragma unroll
-                    for (int m = 0; m < RM; ++m) {
-                        const int rho = lane + MOE_WAVE * m;
-                        const float z = rho < r ? zsm[(i * 2 + P) * r + rho] : 0.f;
-#pragma unroll
-                        for (int c = 0; c < CPW; ++c) acc[P][c] = fmaf(cv[P][c][m], z, acc[P][c]);
+                        for (int y = 0; y < 8; ++y) acc[P][c] = fmaf(cw[y], hv[8 * x + y], acc[P][c]);
                     }
-                // VQ term: selected code words applied to the token's h blocks
+        }
 #pragma unroll
-                for (int qb = 0; qb < QB; ++qb) {
-                    const int b4 = 4 * (lane + MOE_WAVE * qb);
-                    if (b4 >= nbk) continue;
-                    const float4* hr = reinterpret_cast<const float4*>(hsm + (size_t)i * H + b4 * kD);
-                    float hv[32];
+        for (int c = 0; c < CPW; ++c) {
+            const float og = wave_sum(acc[0][c]);
+            const float ou = wave_sum(acc[1][c]);
+            if (lane == 0 && j0 + c < I) p[(size_t)route * I + j0 + c] = silu_mul(og, ou);
+        }
+    };
+
+    if (todo & 1ull) {  // row 0 is a route: slot 0 holds it
+        todo &= ~1ull;
+        if (active) compute(0, r0);
+    }
+    // Every other route of the run: the rest of the first block, then the
+    // following blocks, rvq at a time.
+    int bb = blk;
+    for (;;) {
+        if (!todo) {
+            if (++bb >= nb || (bb == blk + 1 ? enext : plan.block_expert[bb]) != e) break;
+            int rv2 = plan.sorted_routes[(size_t)bb * b + min(lane, b - 1)];
+            if (lane >= b) rv2 = plan.R;
+            todo = rows_ok(rv2, plan.topk_ids[min(max(rv2, 0), plan.R - 1)]);
+            rv = rv2;
+            continue;
+        }
+        int rt[kRT];
+        int nr = 0;
 #pragma unroll
-                    for (int v = 0; v < 8; ++v) {
-                        const float4 x = hr[v];
-                        hv[4 * v] = x.x; hv[4 * v + 1] = x.y; hv[4 * v + 2] = x.z; hv[4 * v + 3] = x.w;
-                    }
-#pragma unroll
-                    for (int P = 0; P < 2; ++P)
-#pragma unroll
-                        for (int c = 0; c < CPW; ++c)
-#pragma unroll
-                            for (int x = 0; x < 4; ++x) {
-                                float cw[8];
-                                unpack8(book[P][(jw[P][c][qb] >> (8 * x)) & 255u], cw);
-#pragma unroll
-                                for (int y = 0; y < 8; ++y) acc[P][c] = fmaf(cw[y], hv[8 * x + y], acc[P][c]);
-                            }
-                }
-#pragma unroll
-                for (int c = 0; c < CPW; ++c) {
-                    const float og = wave_sum(acc[0][c]);
-                    const float ou = wave_sum(acc[1][c]);
-                    if (lane == 0 && j0 + c < I) p[(size_t)rt[i] * I + j0 + c] = silu_mul(og, ou);
-                }
+        for (int i = 0; i < kRT; ++i) {
+            rt[i] = -1;
+            if (i < rvq && todo) {
+                const int q = __builtin_ctzll(todo);
+                todo &= todo - 1;
+                rt[i] = __builtin_amdgcn_readlane(rv, q);
+                nr = i + 1;
             }
+        }
+        __syncthreads();  // the previous routes' slots are no longer read
+#pragma unroll
+        for (int i = 0; i < kRT; ++i) {
+            if (i >= nr) break;
+            const float4* src = reinterpret_cast<const float4*>(h + (size_t)plan.fk.div(rt[i]) * H);
+            float4* dst = reinterpret_cast<float4*>(hsm + (size_t)i * H);
+            for (int c4 = tid; c4 < H4; c4 += kThreads) dst[c4] = src[c4];
+        }
+        for (int it = tid; it < nr * 2 * r; it += kThreads) {
+            const int i = it / (2 * r), rem = it - i * 2 * r, P = rem / r, rho = rem - P * r;
+            int ti = 0;
+#pragma unroll
+            for (int ii = 0; ii < kRT; ++ii)
+                if (ii == i) ti = plan.fk.div(rt[ii]);
+            float z = 0.f;
+            for (int sl0 = 0; sl0 < vq.zslices; sl0 += kZBatch) {
+                float x[kZBatch];
+#pragma unroll
+                for (int u = 0; u < kZBatch; ++u)
+                    x[u] = (P ? vq.zpart[1] : vq.zpart[0])[((size_t)min(sl0 + u, vq.zslices - 1) * vq.M + ti) * r + rho];
+#pragma unroll
+                for (int u = 0; u < kZBatch; ++u) z += sl0 + u < vq.zslices ? x[u] : 0.f;  // slice order
+            }
+            zsm[it] = z;
+        }
+        __syncthreads();
+        if (!active) continue;
+#pragma unroll
+        for (int i = 0; i < kRT; ++i) {
+            if (i >= nr) break;
+            compute(i, rt[i]);
         }
     }
 }
