@@ -52,14 +52,16 @@ __device__ __forceinline__ int block_exclusive_scan(int v, int* wsum, int* total
 }
 
 // Adds one to hist[d] for every lane with act set.  The scores of a token
-// often share their leading digits, which would serialise up to 64 atomics
-// on one bin: the lanes holding the digit of the first two pending lanes are
-// counted with one atomic each, the rest (spread digits) add one per lane.
+// often share their leading digits, and LDS atomics of many lanes on one bin
+// serialise in the CU's LDS: the lanes holding the digit of each of the
+// first kHistLeaders pending lanes are counted with one atomic each, the rest
+// (spread digits) add one per lane.
+constexpr int kHistLeaders = 2;
 __device__ __forceinline__ void wave_hist_add(int* hist, bool act, int d) {
     const int lane = threadIdx.x % MOE_WAVE;
     uint64_t pend = __ballot(act);
 #pragma unroll
-    for (int it = 0; it < 2; ++it) {
+    for (int it = 0; it < kHistLeaders; ++it) {
         if (!pend) break;
         const int leader = __builtin_ctzll(pend);
         const int dl = __builtin_amdgcn_readlane(d, leader);
@@ -91,7 +93,8 @@ chan_select_kernel(const int32_t* __restrict__ topk_ids, const float* __restrict
     __shared__ double sa[32];
     __shared__ int se[32];
     __shared__ int spos[32];  // rank of slot s when slots are ordered by expert id
-    __shared__ int hist[256];
+    __shared__ int hist[2][kSelThreads / MOE_WAVE][256];  // per wave, double-buffered
+    __shared__ unsigned long long s_wmin[kSelThreads / MOE_WAVE], s_wmax[kSelThreads / MOE_WAVE];
     __shared__ unsigned long long s_prefix;
     __shared__ int s_need;
     __shared__ int s_cnt;
@@ -137,25 +140,64 @@ chan_select_kernel(const int32_t* __restrict__ topk_ids, const float* __restrict
         tpos[u] = spos[sl] * I + j;
     }
 
+    // Leading digits shared by every candidate's key cannot split them: the
+    // passes start below them (min and max over all candidates, the zero keys
+    // of invalid slots included, which then share no digit with valid ones).
+    unsigned long long kmin = ~0ull, kmax = 0ull;
+#pragma unroll
+    for (int u = 0; u < kSelPer; ++u) {
+        const bool v = u < per && i0 + u < n;
+        kmin = v && key[u] < kmin ? key[u] : kmin;
+        kmax = v && key[u] > kmax ? key[u] : kmax;
+    }
+#pragma unroll
+    for (int m = 1; m < MOE_WAVE; m <<= 1) {
+        const unsigned long long a = __shfl_xor(kmin, m, MOE_WAVE), c = __shfl_xor(kmax, m, MOE_WAVE);
+        kmin = a < kmin ? a : kmin;
+        kmax = c > kmax ? c : kmax;
+    }
+    if (lane == 0) {
+        s_wmin[tid / MOE_WAVE] = kmin;
+        s_wmax[tid / MOE_WAVE] = kmax;
+    }
+    for (int i = tid; i < 2 * (kSelThreads / MOE_WAVE) * 256; i += kSelThreads) (&hist[0][0][0])[i] = 0;
+    __syncthreads();
+    kmin = ~0ull;
+    kmax = 0ull;
+#pragma unroll
+    for (int w = 0; w < kSelThreads / MOE_WAVE; ++w) {
+        kmin = s_wmin[w] < kmin ? s_wmin[w] : kmin;
+        kmax = s_wmax[w] > kmax ? s_wmax[w] : kmax;
+    }
+    const int p0 = __builtin_clzll((kmin ^ kmax) | 1ull) / 8;  // whole shared digits (<= 7)
+
     // MSD passes until the bucket holding the K-th key contains exactly the
     // candidates still needed (all of them kept), or the key is exhausted.
-    unsigned long long prefix = 0;
-    int need = K, shift = 64, cnt = 0;
-    for (int pass = 0; pass < 8; ++pass) {
+    // Each wave counts into its own histogram (LDS atomics of one wave on one
+    // bin serialise, so concentrated digits would otherwise serialise all 16
+    // waves); the scanning wave adds the 16 counts of a digit in wave order.
+    // The histograms are double-buffered: the scan clears the next pass's.
+    unsigned long long prefix = p0 > 0 ? kmax >> (64 - 8 * p0) : 0ull;
+    int need = K, shift = 64 - 8 * p0, cnt = 0;
+    for (int pass = p0; pass < 8; ++pass) {
         const int sh = 56 - 8 * pass;
-        if (tid < 256) hist[tid] = 0;
-        __syncthreads();
+        const int cur = pass & 1;
 #pragma unroll
         for (int u = 0; u < kSelPer; ++u) {
             const bool act = u < per && i0 + u < n && (pass == 0 || (key[u] >> (sh + 8)) == prefix);
-            wave_hist_add(hist, act, (int)((key[u] >> sh) & 255ull));
+            wave_hist_add(hist[cur][tid / MOE_WAVE], act, (int)((key[u] >> sh) & 255ull));
         }
         __syncthreads();
         if (tid < MOE_WAVE) {
             // lane covers digits 255-4l .. 252-4l (descending)
             int c[4], tot = 0;
 #pragma unroll
-            for (int x = 0; x < 4; ++x) { c[x] = hist[255 - 4 * lane - x]; tot += c[x]; }
+            for (int x = 0; x < 4; ++x) {
+                c[x] = 0;
+#pragma unroll
+                for (int w = 0; w < kSelThreads / MOE_WAVE; ++w) c[x] += hist[cur][w][255 - 4 * lane - x];
+                tot += c[x];
+            }
             int incl = tot;
 #pragma unroll
             for (int d = 1; d < MOE_WAVE; d <<= 1) {
@@ -172,6 +214,9 @@ chan_select_kernel(const int32_t* __restrict__ topk_ids, const float* __restrict
                 }
                 before += c[x];
             }
+        } else {
+            for (int i = tid - MOE_WAVE; i < (kSelThreads / MOE_WAVE) * 256; i += kSelThreads - MOE_WAVE)
+                (&hist[cur ^ 1][0][0])[i] = 0;
         }
         __syncthreads();
         prefix = s_prefix;
@@ -230,7 +275,7 @@ __global__ void __launch_bounds__(kThreads)
 chan_gather_kernel(const int32_t* __restrict__ topk_ids, const float* __restrict__ topk_w,
                    const int32_t* __restrict__ kept, int k, int I, int E, int H, int K, const float* __restrict__ h,
                    const uint16_t* __restrict__ Wg, const uint16_t* __restrict__ Wu, const uint16_t* __restrict__ Wd,
-                   float* __restrict__ part) {
+                   float* __restrict__ part, FastDiv fI) {
     constexpr int KC = kWaves * 2;
     __shared__ float cs[KC];
     const int t = blockIdx.y;
@@ -241,19 +286,35 @@ chan_gather_kernel(const int32_t* __restrict__ topk_ids, const float* __restrict
     const int lane = tid % MOE_WAVE;
     const int q0 = chunk * KC;
 
-    // resolve all KC kept channels of the chunk (uniform per workgroup)
+    // h of the token first: it depends on nothing, and a load queued behind
+    // the weight stream would wait for all of it
+    float4 hq[Q][2];
+#pragma unroll
+    for (int q = 0; q < Q; ++q) {
+        const int col = min((lane + MOE_WAVE * q) * 8, H - 8);
+        hq[q][0] = *reinterpret_cast<const float4*>(h + (size_t)t * H + col);
+        hq[q][1] = *reinterpret_cast<const float4*>(h + (size_t)t * H + col + 4);
+    }
+    // Resolve the KC kept channels of the chunk: lane q of every wave takes
+    // channel q0 + q (two rounds of vector loads at clamped addresses, then
+    // broadcast), instead of a chain of dependent scalar loads.
     int ce[KC], cj[KC];
     float ca[KC];
+    {
+        const int q = lane % KC;
+        const bool qin = q0 + q < K;
+        const int v = kept[(size_t)t * K + min(q0 + q, K - 1)];
+        const bool vin = qin && v >= 0 && v < k * I;
+        const int vc = vin ? v : 0;
+        const int s = fI.div(vc), j = vc - s * (int)fI.d;
+        const int e = topk_ids[(size_t)t * k + s];
+        const float a = topk_w[(size_t)t * k + s];
+        const int ev = (vin && e >= 0 && e < E) ? e : -1;
 #pragma unroll
-    for (int qq = 0; qq < KC; ++qq) {
-        ce[qq] = -1; cj[qq] = 0; ca[qq] = 0.f;
-        if (q0 + qq < K) {
-            const int v = kept[(size_t)t * K + q0 + qq];
-            const int s = v / I;
-            if (v >= 0 && s < k) {
-                const int e = topk_ids[(size_t)t * k + s];
-                if (e >= 0 && e < E) { ce[qq] = e; cj[qq] = v % I; ca[qq] = topk_w[(size_t)t * k + s]; }
-            }
+        for (int qq = 0; qq < KC; ++qq) {
+            ce[qq] = __builtin_amdgcn_readlane(ev, qq);
+            cj[qq] = __builtin_amdgcn_readlane(j, qq);
+            ca[qq] = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(a), qq));
         }
     }
     // issue every load of the chunk: gate/up rows of this wave's two
@@ -287,8 +348,7 @@ chan_gather_kernel(const int32_t* __restrict__ topk_ids, const float* __restrict
     for (int q = 0; q < Q; ++q) {
         const int col = (lane + MOE_WAVE * q) * 8;
         if (col >= H) continue;
-        const float4 h0 = *reinterpret_cast<const float4*>(h + (size_t)t * H + col);
-        const float4 h1 = *reinterpret_cast<const float4*>(h + (size_t)t * H + col + 4);
+        const float4 h0 = hq[q][0], h1 = hq[q][1];
         const float hv[8] = {h0.x, h0.y, h0.z, h0.w, h1.x, h1.y, h1.z, h1.w};
 #pragma unroll
         for (int c = 0; c < 2; ++c) {
@@ -409,13 +469,13 @@ hipError_t gather_q(const int32_t* topk_ids, const float* topk_w, const int32_t*
     const int CQ = (H + 2047) / 2048;
     if (CQ <= 1)
         MOE_LAUNCH((chan_gather_kernel<Q, 1>), grid, dim3(kThreads), 0, stream, topk_ids, topk_w, kept, k, I,
-                           E, H, K, h, Wg, Wu, Wd, part);
+                           E, H, K, h, Wg, Wu, Wd, part, FastDiv((uint32_t)I));
     else if (CQ <= 2)
         MOE_LAUNCH((chan_gather_kernel<Q, 2>), grid, dim3(kThreads), 0, stream, topk_ids, topk_w, kept, k, I,
-                           E, H, K, h, Wg, Wu, Wd, part);
+                           E, H, K, h, Wg, Wu, Wd, part, FastDiv((uint32_t)I));
     else if (CQ <= 4)
         MOE_LAUNCH((chan_gather_kernel<Q, 4>), grid, dim3(kThreads), 0, stream, topk_ids, topk_w, kept, k, I,
-                           E, H, K, h, Wg, Wu, Wd, part);
+                           E, H, K, h, Wg, Wu, Wd, part, FastDiv((uint32_t)I));
     else
         return hipErrorInvalidValue;
     return hipGetLastError();
