@@ -534,3 +534,37 @@ def test_fused_single_token_with_repeated_experts(mb, ids, b):
     ref = O.dense_forward(inp["h"], ids, w.astype(np.float64), inp["w_gate"], inp["w_up"], inp["w_down"])
     check_close(layer.y[:1].cpu().numpy(), ref)
     layer.close()
+
+
+@pytest.mark.parametrize("b,hot", [
+    (16, 10),  # one block holds 10 routes of one expert: two 8-route passes of the down kernel, three gate/up groups
+    (8, 12),   # an expert with 12 routes spans two blocks of its run
+    (4, 7),    # block size 4: a run of two blocks, the second partly padded
+])
+def test_split_path_forced_hot_expert(mb, b, hot):
+    """Several tokens with forced routes: expert 3 takes `hot` routes, the
+    rest are spread; checked against the oracle on the same ids and weights."""
+    import torch
+    M, k, E = 12, 2, 16
+    ids = np.zeros((M, k), dtype=np.int64)
+    n = 0
+    for t in range(M):
+        for s in range(k):
+            ids[t, s] = 3 if n < hot and s == 0 else (5 + (t * k + s) % 9)
+            n += 1 if s == 0 else 0
+    assert all(len(set(r)) == k for r in ids) and (ids == 3).sum() == hot
+    wl = synth.small_workload("hot_%d_%d" % (b, hot), H=1032, I=72, E=E, k=k, M=M, seed=101 + b, block_b=b)
+    say("split forced", dict(b=b, hot=hot, H=wl.H, I=wl.I))
+    inp = synth.layer_inputs(wl, 0)
+    inp["h"] = synth.hidden(wl, 0, 0, M=M)
+    layer = make_layer(mb, wl, inp, M)
+    dids = torch.from_numpy(ids.astype(np.int32)).cuda()
+    w = np.tile(np.array([[0.7, 0.3]], dtype=np.float32), (M, 1))
+    dw = torch.from_numpy(w).cuda()
+    layer.align(M, ids=dids)
+    layer.forward(to_dev(inp["h"]), M, ids=dids, w=dw)
+    torch.cuda.synchronize()
+    assert mb.moe_read_device_error(layer.ctx) == 0
+    ref = O.dense_forward(inp["h"], ids, w.astype(np.float64), inp["w_gate"], inp["w_up"], inp["w_down"])
+    check_close(layer.y[:M].cpu().numpy(), ref)
+    layer.close()
