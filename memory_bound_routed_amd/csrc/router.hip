@@ -433,8 +433,11 @@ router_align_kernel(const float* __restrict__ h, int M, int H, const uint16_t* _
     const int R = M * k;
     if (gridDim.y == 1) {
         if (R <= MOE_WAVE) {
-            // sel was complete at the top-k's last barrier and is only read since
-            if (threadIdx.x < MOE_WAVE)
+            // sel was complete at the top-k's last barrier and is only read
+            // since; the wave after the softmax waves aligns (the last wave
+            // also does a softmax when M == 4), beside the softmax
+            const int aw = min(M, kThreads / MOE_WAVE - 1);
+            if ((int)threadIdx.x / MOE_WAVE == aw)
                 align_wave([&](int r) { const int t = fk.div(r); return sel.e[t][r - t * k]; }, R, E, fb,
                            sorted_routes, block_expert, counts, err);
         } else {
