@@ -28,6 +28,26 @@ constexpr int kRT = 4;    // routes staged together
 constexpr int kD = 8;     // VQ block length supported by this kernel
 constexpr int kZBatch = 16;
 
+// Overflow workgroups: runs of two or more routes (in block order, the first
+// kOverflow of them) share their routes with one more workgroup, which takes
+// the odd-numbered routes of the run while the run's own workgroup takes the
+// even-numbered ones, so that an expert routed twice ends with the others.
+constexpr int kOverflow = 4;
+
+// Per lane: whether plan block bb (< nb) starts a run of at least two routes.
+// A well-formed plan fills a run's first block first, so its row 1 is a route
+// exactly then (one-row blocks: the next block has the same expert).  Both
+// workgroups of a run evaluate this on the same plan, so they agree.
+__device__ __forceinline__ bool starts_multi_run(const PlanArgs& plan, int bb, int nb) {
+    const int bc = min(max(bb, 0), plan.max_blocks - 1);
+    const int e = plan.block_expert[bc];
+    const int ep = plan.block_expert[max(bc - 1, 0)];
+    const int en = plan.block_expert[min(bc + 1, plan.max_blocks - 1)];
+    const int r1 = plan.sorted_routes[(size_t)bc * plan.b + min(1, plan.b - 1)];
+    const bool two = plan.b > 1 ? r1 != plan.R : (bc + 1 < nb && en == e);
+    return bb >= 0 && bb < nb && (bc == 0 || ep != e) && e >= 0 && e < plan.E && two;
+}
+
 // Grid (plan blocks, ceil(I / (4*CPW))): workgroup (blk, cy) owns 4*CPW
 // channels of the expert whose run of blocks starts at blk; wave w owns CPW
 // of them.  Lane l owns VQ blocks 4*(l + 64*qb) .. +3 (one 4-byte index load
@@ -51,11 +71,31 @@ gateup_vqlr_kernel(PlanArgs plan, VqArgs vq, const float* __restrict__ h, int H,
     extern __shared__ __align__(16) float dyn[];
     float* hsm = dyn;                       // [rvq][H]
     float* zsm = dyn + (size_t)rvq * H;     // [kRT][2][r]
-    const int blk = blockIdx.x;
     const int b = plan.b;
     const int tid = threadIdx.x;
     const int wave = tid / MOE_WAVE;
     const int lane = tid % MOE_WAVE;
+    const bool ovf = (int)blockIdx.x >= plan.max_blocks;  // an overflow workgroup
+    int blk = blockIdx.x;
+    if (ovf) {  // find the run: the (x - max_blocks)-th block starting a run of two or more routes
+        int nbo = plan.counts[0];
+        nbo = nbo < 0 ? 0 : min(nbo, plan.max_blocks);
+        int o = (int)blockIdx.x - plan.max_blocks;
+        blk = -1;
+        for (int c0 = 0; c0 < nbo; c0 += MOE_WAVE) {  // uniform
+            const uint64_t m = __ballot(starts_multi_run(plan, c0 + lane, nbo));
+            const int c = __popcll(m);
+            if (o < c) {
+                uint64_t mm = m;
+                for (int i = 0; i < o; ++i) mm &= mm - 1;
+                blk = c0 + __builtin_ctzll(mm);
+                break;
+            }
+            o -= c;
+        }
+        if (blk < 0) return;  // fewer such runs than overflow workgroups (uniform)
+    }
+    const int sp = ovf ? 1 : 0;  // this workgroup's first route of the run
 
     // Round 1: counts, the previous, this and the next block's expert, the
     // block's rows.
@@ -66,15 +106,24 @@ gateup_vqlr_kernel(PlanArgs plan, VqArgs vq, const float* __restrict__ h, int H,
     int rv = plan.sorted_routes[(size_t)blk * b + min(lane, b - 1)];
     if (lane >= b) rv = plan.R;
     if (nb < 0 || nb > plan.max_blocks) {
-        if (blk == 0 && blockIdx.y == 0 && tid == 0) atomicOr(err, DEVERR_BAD_COUNTS);
+        if (blockIdx.x == 0 && blockIdx.y == 0 && tid == 0) atomicOr(err, DEVERR_BAD_COUNTS);
         nb = nb < 0 ? 0 : plan.max_blocks;
     }
     if (blk >= nb) return;
     if (e < 0 || e >= plan.E) {
-        if (blockIdx.y == 0 && tid == 0) atomicOr(err, DEVERR_BAD_BLOCK_EXPERT);
+        if (!ovf && blockIdx.y == 0 && tid == 0) atomicOr(err, DEVERR_BAD_BLOCK_EXPERT);
         return;
     }
     if (eprev == e) return;  // not the first block of the expert's run (uniform)
+    // A run's own workgroup shares it if it is among the first kOverflow runs
+    // of two or more routes (rank over the blocks before it).
+    bool split = ovf;
+    if (!ovf && starts_multi_run(plan, blk, min(max(nb, 0), plan.max_blocks))) {
+        int rank = 0;
+        for (int c0 = 0; c0 < blk; c0 += MOE_WAVE)  // uniform
+            rank += __popcll(__ballot(c0 + lane < blk && starts_multi_run(plan, c0 + lane, nb)));
+        split = rank < kOverflow;
+    }
     const int nbk = H / kD;  // VQ blocks per channel
     const int r = vq.r;
     const int H4 = H / 4;
@@ -86,7 +135,7 @@ gateup_vqlr_kernel(PlanArgs plan, VqArgs vq, const float* __restrict__ h, int H,
     // (the argument struct's arrays are indexed by compile-time constants or
     // through a select: a run-time index would load the pointer from the
     // kernel-argument segment with a vector load)
-    const int r0 = __builtin_amdgcn_readfirstlane(rv);
+    const int r0 = __builtin_amdgcn_readlane(rv, min(sp, MOE_WAVE - 1));  // row sp: the run's route sp if rows 0..sp are routes
     const int t0 = plan.fk.div(min(max(r0, 0), plan.R - 1));
     uint4 bk[2];
 #pragma unroll
@@ -160,7 +209,7 @@ gateup_vqlr_kernel(PlanArgs plan, VqArgs vq, const float* __restrict__ h, int H,
     }
     auto rows_ok = [&](int rvx, int idx) {
         const bool ok = rvx >= 0 && rvx < plan.R && idx == e;
-        if (!ok && rvx != plan.R && wave == 0 && blockIdx.y == 0) atomicOr(err, DEVERR_BAD_PLAN);
+        if (!ok && rvx != plan.R && wave == 0 && !ovf && blockIdx.y == 0) atomicOr(err, DEVERR_BAD_PLAN);
         return __ballot(ok);
     };
     uint64_t todo = rows_ok(rv, idv);
@@ -215,13 +264,13 @@ gateup_vqlr_kernel(PlanArgs plan, VqArgs vq, const float* __restrict__ h, int H,
         }
     };
 
-    if (todo & 1ull) {  // row 0 is a route: slot 0 holds it
-        todo &= ~1ull;
-        if (active) compute(0, r0);
-    }
-    // Every other route of the run: the rest of the first block, then the
-    // following blocks, rvq at a time.
-    int bb = blk;
+    // The routes of the run in order (the first block's valid rows, then the
+    // following blocks'): all of them, or -- for a shared run -- every other
+    // one from sp.  Row sp's h and z are in slot 0 already if rows 0..sp of
+    // the first block are routes; other routes are staged rvq at a time.
+    const uint64_t lowmask = (2ull << sp) - 1;
+    bool pre = sp < b && (todo & lowmask) == lowmask;
+    int bb = blk, n = 0;
     for (;;) {
         if (!todo) {
             if (++bb >= nb || (bb == blk + 1 ? enext : plan.block_expert[bb]) != e) break;
@@ -231,44 +280,60 @@ gateup_vqlr_kernel(PlanArgs plan, VqArgs vq, const float* __restrict__ h, int H,
             rv = rv2;
             continue;
         }
-        int rt[kRT];
+        // the next routes of this workgroup, at most rvq, the first possibly in slot 0
+        int rt[kRT], rq[kRT];
         int nr = 0;
 #pragma unroll
         for (int i = 0; i < kRT; ++i) {
             rt[i] = -1;
-            if (i < rvq && todo) {
-                const int q = __builtin_ctzll(todo);
-                todo &= todo - 1;
-                rt[i] = __builtin_amdgcn_readlane(rv, q);
-                nr = i + 1;
+            rq[i] = -1;
+        }
+        while (todo && nr < rvq) {  // uniform
+            const int q = __builtin_ctzll(todo);
+            todo &= todo - 1;
+            const bool mine = !split || (n & 1) == sp;
+            ++n;
+            if (!mine) continue;
+#pragma unroll
+            for (int i = 0; i < kRT; ++i)
+                if (i == nr) {
+                    rt[i] = __builtin_amdgcn_readlane(rv, q);
+                    rq[i] = q;
+                }
+            ++nr;
+        }
+        if (nr == 0) continue;
+        const bool have0 = pre && bb == blk && rq[0] == sp;  // slot 0 already holds the first
+        pre = false;
+        if (!have0 || nr > 1) {
+            __syncthreads();  // the previous routes' slots are no longer read
+#pragma unroll
+            for (int i = 0; i < kRT; ++i) {
+                if (i >= nr || (i == 0 && have0)) continue;
+                const float4* src = reinterpret_cast<const float4*>(h + (size_t)plan.fk.div(rt[i]) * H);
+                float4* dst = reinterpret_cast<float4*>(hsm + (size_t)i * H);
+                for (int c4 = tid; c4 < H4; c4 += kThreads) dst[c4] = src[c4];
             }
-        }
-        __syncthreads();  // the previous routes' slots are no longer read
+            for (int it = tid; it < nr * 2 * r; it += kThreads) {
+                const int i = it / (2 * r), rem = it - i * 2 * r, P = rem / r, rho = rem - P * r;
+                if (i == 0 && have0) continue;
+                int ti = 0;
 #pragma unroll
-        for (int i = 0; i < kRT; ++i) {
-            if (i >= nr) break;
-            const float4* src = reinterpret_cast<const float4*>(h + (size_t)plan.fk.div(rt[i]) * H);
-            float4* dst = reinterpret_cast<float4*>(hsm + (size_t)i * H);
-            for (int c4 = tid; c4 < H4; c4 += kThreads) dst[c4] = src[c4];
-        }
-        for (int it = tid; it < nr * 2 * r; it += kThreads) {
-            const int i = it / (2 * r), rem = it - i * 2 * r, P = rem / r, rho = rem - P * r;
-            int ti = 0;
+                for (int ii = 0; ii < kRT; ++ii)
+                    if (ii == i) ti = plan.fk.div(rt[ii]);
+                float z = 0.f;
+                for (int sl0 = 0; sl0 < vq.zslices; sl0 += kZBatch) {
+                    float x[kZBatch];
 #pragma unroll
-            for (int ii = 0; ii < kRT; ++ii)
-                if (ii == i) ti = plan.fk.div(rt[ii]);
-            float z = 0.f;
-            for (int sl0 = 0; sl0 < vq.zslices; sl0 += kZBatch) {
-                float x[kZBatch];
+                    for (int u = 0; u < kZBatch; ++u)
+                        x[u] = (P ? vq.zpart[1] : vq.zpart[0])[((size_t)min(sl0 + u, vq.zslices - 1) * vq.M + ti) * r + rho];
 #pragma unroll
-                for (int u = 0; u < kZBatch; ++u)
-                    x[u] = (P ? vq.zpart[1] : vq.zpart[0])[((size_t)min(sl0 + u, vq.zslices - 1) * vq.M + ti) * r + rho];
-#pragma unroll
-                for (int u = 0; u < kZBatch; ++u) z += sl0 + u < vq.zslices ? x[u] : 0.f;  // slice order
+                    for (int u = 0; u < kZBatch; ++u) z += sl0 + u < vq.zslices ? x[u] : 0.f;  // slice order
+                }
+                zsm[it] = z;
             }
-            zsm[it] = z;
+            __syncthreads();
         }
-        __syncthreads();
         if (!active) continue;
 #pragma unroll
         for (int i = 0; i < kRT; ++i) {
@@ -281,7 +346,8 @@ gateup_vqlr_kernel(PlanArgs plan, VqArgs vq, const float* __restrict__ h, int H,
 template <int QB, int RM, int CPW>
 hipError_t vq_launch(const PlanArgs& plan, const VqArgs& vq, const float* h, int H, int I, float* p, int32_t* err,
                      hipStream_t stream) {
-    const dim3 grid(plan.max_blocks, (I + kWaves * CPW - 1) / (kWaves * CPW));
+    // x: the plan blocks, then the overflow workgroups
+    const dim3 grid(plan.max_blocks + kOverflow, (I + kWaves * CPW - 1) / (kWaves * CPW));
     const int rvq = H <= 4096 ? kRT : 2;  // staged h rows: <= 64 KiB
     const size_t lds = ((size_t)rvq * H + (size_t)kRT * 2 * vq.r) * sizeof(float);
     MOE_LAUNCH((gateup_vqlr_kernel<QB, RM, CPW>), grid, dim3(kThreads), lds, stream, plan, vq, h, H, I, rvq, p, err);

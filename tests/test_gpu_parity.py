@@ -568,3 +568,31 @@ def test_split_path_forced_hot_expert(mb, b, hot):
     ref = O.dense_forward(inp["h"], ids, w.astype(np.float64), inp["w_gate"], inp["w_up"], inp["w_down"])
     check_close(layer.y[:M].cpu().numpy(), ref)
     layer.close()
+
+
+@pytest.mark.parametrize("b", [8, 4])
+def test_vq_forced_multi_route_experts(mb, b):
+    """VQ + low-rank path with nine experts routed more than once (expert 3
+    six times, eight others twice): more such runs than the kernel shares
+    with extra workgroups, so shared and unshared runs are both checked."""
+    import torch
+    M, k = 12, 2
+    ids = np.array([[3, 5 + t] for t in range(6)] + [[5 + (t - 6), 12 + (t % 4)] for t in range(6, 12)],
+                   dtype=np.int64)
+    assert all(len(set(r)) == k for r in ids)
+    wl = synth.small_workload("vq_multi_%d" % b, H=1024, I=40, E=16, k=k, M=M, seed=131 + b, vq=True, lr_r=16,
+                              block_b=b)
+    say("vq forced", dict(b=b))
+    inp = synth.layer_inputs(wl, 0)
+    inp["h"] = synth.hidden(wl, 0, 0, M=M)
+    layer = make_layer(mb, wl, inp, M)
+    dids = torch.from_numpy(ids.astype(np.int32)).cuda()
+    w = np.tile(np.array([[0.6, 0.4]], dtype=np.float32), (M, 1))
+    dw = torch.from_numpy(w).cuda()
+    layer.align(M, ids=dids)
+    layer.forward(to_dev(inp["h"]), M, ids=dids, w=dw)
+    torch.cuda.synchronize()
+    assert mb.moe_read_device_error(layer.ctx) == 0
+    ref = O.vqlr_forward(inp["h"], ids, w.astype(np.float64), inp, inp["w_down"])
+    check_close(layer.y[:M].cpu().numpy(), ref)
+    layer.close()
