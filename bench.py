@@ -47,7 +47,7 @@ def kernel_algorithmic_bytes(wl, kernel: str, n_experts: int, M: int, K: int = 0
     """Bytes a kernel must move by definition (weights it streams once plus
     its small activation inputs/outputs)."""
     H, I = wl.H, wl.I
-    if kernel == "expert_fused":
+    if kernel in ("expert_fused", "decode_fused"):
         return n_experts * 3 * I * H * 2
     if kernel == "gateup":
         return n_experts * 2 * I * H * 2
@@ -68,7 +68,10 @@ def source_digest(files) -> str:
 
 
 KERNEL_SOURCES = {
-    "expert_fused": ["memory_bound_routed_amd/csrc/dense.hip", "memory_bound_routed_amd/csrc/device_common.h"],
+    "expert_fused": ["memory_bound_routed_amd/csrc/dense.hip", "memory_bound_routed_amd/csrc/device_common.h",
+                     "memory_bound_routed_amd/csrc/topk_device.h"],
+    "decode_fused": ["memory_bound_routed_amd/csrc/dense.hip", "memory_bound_routed_amd/csrc/device_common.h",
+                     "memory_bound_routed_amd/csrc/topk_device.h"],
     "gateup": ["memory_bound_routed_amd/csrc/dense.hip", "memory_bound_routed_amd/csrc/device_common.h"],
     "down": ["memory_bound_routed_amd/csrc/dense.hip", "memory_bound_routed_amd/csrc/device_common.h"],
     "gateup_vqlr": ["memory_bound_routed_amd/csrc/vqlr.hip", "memory_bound_routed_amd/csrc/device_common.h"],
@@ -99,7 +102,14 @@ def _pmc_rows(path, counter):
     return out
 
 
-def traffic_from_counters(fetch_csv, write_csv, workload, kernel="expert_fused"):
+# rocprofv3 kernel-name fragment of each library kernel whose traffic is taken
+# (decode_fused is the routing instance of the fused expert kernel).
+ROCPROF_NAME = {"expert_fused": "expert_fused_kernel", "decode_fused": "expert_fused_kernel",
+                "gateup": "gateup_dense_kernel", "down": "down_kernel", "gateup_vqlr": "gateup_vqlr_kernel",
+                "chan_gather": "chan_gather_kernel"}
+
+
+def traffic_from_counters(fetch_csv, write_csv, workload, kernel="decode_fused"):
     """HBM bytes per launch of `kernel` from two rocprofv3 --pmc runs of
     `bench.py --counter-pass` (FETCH_SIZE, then WRITE_SIZE; KiB per dispatch).
     Each counter is scaled by what it reads for the calibration copy (a
@@ -111,7 +121,7 @@ def traffic_from_counters(fetch_csv, write_csv, workload, kernel="expert_fused")
     for name, path in (("FETCH_SIZE", fetch_csv), ("WRITE_SIZE", write_csv)):
         rows = _pmc_rows(path, name)
         cal = [v for k, v in rows if "neg" in k and "elementwise" in k]
-        ker = [v for k, v in rows if kernel + "_kernel" in k]
+        ker = [v for k, v in rows if ROCPROF_NAME[kernel] in k]
         if not cal or not ker:
             raise SystemExit("%s: no calibration (%d) or %s (%d) dispatches" % (path, len(cal), kernel, len(ker)))
         cal_kib = float(np.median(cal))
@@ -183,7 +193,7 @@ def build_layers(wl, n_layers, M, keep=0):
 def run_steps(layers, hs, M, keep, order):
     for i in order:
         L = layers[i % len(layers)]
-        L.step(hs[i % len(hs)], M, keep=keep)
+        L.decode_step(hs[i % len(hs)], M, keep=keep)
 
 
 def cpu_baseline(wl, budget_s=15.0, max_steps=40):
@@ -346,7 +356,7 @@ def main():
     alg = kernel_algorithmic_bytes(wl, dominant, round(avg_ex), M, keep * M)
     dur_s = kernels[dominant]["avg_us"] / 1e6
     achieved = alg / dur_s / 1e9 if alg else None
-    expert_kernels = [k for k in kern if k not in ("router", "align", "router_align")]
+    expert_kernels = [k for k in kern if k not in ("router", "align", "router_align", "router_gemv")]
     expert_us = sum(kernels[k]["avg_us"] * kernels[k]["launches"] for k in expert_kernels) / K
 
     us_step = ms_per_step * 1e3

@@ -224,6 +224,27 @@ moe_status moe_expert_forward(moe_ctx *ctx, const float *h, int32_t M,
                               const int32_t *counts, int32_t keep_channels,
                               int32_t *kept_out, float *y, void *stream);
 
+/*
+ * One decode step in one call: moe_route_align (moe_route_topk when
+ * keep_channels > 0) followed by moe_expert_forward, with the same arguments
+ * and the same outputs bit for bit (pages "A Multi-Engine Dataflow ...",
+ * MoE-block background: routing then the routed experts; "Route-Block
+ * Membership ...", Sec. 2.1 and Sec. 3.1: the id array and its canonical
+ * plan).  With keep_channels > 0 the plan arguments are ignored (may be NULL).
+ *
+ * For one token with dense weights (H <= 4096, E <= 512) the step is three
+ * launches with no hand-off between workgroups: the router GEMV writes its
+ * row-slice partials; every workgroup of the fused expert kernel adds them,
+ * takes the top-k and softmax and finds its own expert (one block per
+ * selected expert); the combine adds the partials.  Otherwise the calls above
+ * are made as they are.
+ *  h, y: fp32 [M][H]; topk_ids, topk_w: [M][k] out; logits_out: [M][E] out
+ *  or NULL; sorted_routes, block_expert, counts: as moe_align_blocks.
+ */
+moe_status moe_decode_step(moe_ctx *ctx, const float *h, int32_t M, int32_t *topk_ids, float *topk_w,
+                           float *logits_out, int32_t *sorted_routes, int32_t *block_expert, int32_t *counts,
+                           int32_t keep_channels, int32_t *kept_out, float *y, void *stream);
+
 /* ---------------------------------------------------------------- helpers */
 
 /* Rows moe_align_blocks may write: M*k + min(E, M*k)*(b-1); -1 on bad args. */
@@ -282,7 +303,9 @@ enum {
     MOE_KERNEL_CHAN_COMBINE = 9,
     MOE_KERNEL_EXPERT_FUSED = 10, /* dense gate/up + SiLU + down partials (one route per block) */
     MOE_KERNEL_ROUTER_ALIGN = 11, /* router + top-k + softmax + alignment (one launch) */
-    MOE_KERNEL_COUNT = 12
+    MOE_KERNEL_ROUTER_GEMV = 12,  /* router GEMV slice partials only (batch-1 decode step) */
+    MOE_KERNEL_DECODE_FUSED = 13, /* per-workgroup top-k + softmax + plan, then as EXPERT_FUSED */
+    MOE_KERNEL_COUNT = 14
 };
 
 /*

@@ -27,11 +27,13 @@ MOE_OK, MOE_ERR_INVALID_ARG, MOE_ERR_UNSUPPORTED, MOE_ERR_CAPACITY, MOE_ERR_HIP,
 MOE_WFORMAT_DENSE, MOE_WFORMAT_VQLR = 0, 1
 DEVERR_BAD_ROUTE_ID, DEVERR_BAD_PLAN, DEVERR_BAD_BLOCK_EXPERT, DEVERR_BAD_COUNTS = 1, 2, 4, 8
 KERNELS = ["router", "vq_shared", "align", "gateup", "gateup_vqlr", "down", "combine",
-           "chan_select", "chan_gather", "chan_combine", "expert_fused", "router_align"]
+           "chan_select", "chan_gather", "chan_combine", "expert_fused", "router_align", "router_gemv",
+           "decode_fused"]
 MOE_KERNEL_COUNT = len(KERNELS)
 
 # Every symbol include/moe.h declares (checked by the CPU test suite).
 EXPORTS = ["moe_create", "moe_destroy", "moe_route_topk", "moe_route_align", "moe_align_blocks", "moe_expert_forward",
+           "moe_decode_step",
            "moe_align_capacity", "moe_status_string", "moe_read_device_error", "moe_channel_norms",
            "moe_validate_plan", "moe_profile_enable", "moe_profile_read", "moe_kernel_name"]
 
@@ -58,6 +60,7 @@ _sig = {
     "moe_align_blocks": (_i32, [_vp, _vp, _i32, _vp, _vp, _vp, _vp]),
     "moe_route_align": (_i32, [_vp, _vp, _i32, _vp, _vp, _vp, _vp, _vp, _vp, _vp]),
     "moe_expert_forward": (_i32, [_vp, _vp, _i32, _vp, _vp, _vp, _vp, _vp, _i32, _vp, _vp, _vp]),
+    "moe_decode_step": (_i32, [_vp, _vp, _i32, _vp, _vp, _vp, _vp, _vp, _vp, _i32, _vp, _vp, _vp]),
     "moe_align_capacity": (_i32, [_i32, _i32, _i32, _i32]),
     "moe_status_string": (ctypes.c_char_p, [_i32]),
     "moe_read_device_error": (_i32, [_vp, _pi32, _i32]),
@@ -175,6 +178,13 @@ def moe_expert_forward(ctx, h, M, topk_ids, topk_w, sorted_routes, block_expert,
                                    _stream(stream)), "moe_expert_forward")
 
 
+def moe_decode_step(ctx, h, M, topk_ids, topk_w, logits_out, sorted_routes, block_expert, counts, keep_channels,
+                    kept_out, y, stream=None) -> None:
+    _check(_lib.moe_decode_step(ctx, _ptr(h), M, _ptr(topk_ids), _ptr(topk_w), _ptr(logits_out), _ptr(sorted_routes),
+                                _ptr(block_expert), _ptr(counts), keep_channels, _ptr(kept_out), _ptr(y),
+                                _stream(stream)), "moe_decode_step")
+
+
 def moe_read_device_error(ctx, clear: bool = True) -> int:
     flags = _i32(0)
     st = _lib.moe_read_device_error(ctx, ctypes.byref(flags), 1 if clear else 0)
@@ -259,9 +269,15 @@ class Layer:
         moe_route_align(self.ctx, h, M, self.ids, self.w, self.logits if logits else None, self.sorted_routes,
                         self.block_expert, self.counts, stream)
 
+    def decode_step(self, h, M, keep=0, logits=False, stream=None):
+        """One decode step in one call (moe_decode_step)."""
+        moe_decode_step(self.ctx, h, M, self.ids, self.w, self.logits if logits else None, self.sorted_routes,
+                        self.block_expert, self.counts, keep, self.kept if keep else None, self.y, stream)
+        return self.y[:M]
+
     def step(self, h, M, keep=0, stream=None, fused_route_align=True):
         """One decode step: routing, alignment (not needed by the channel-sparse
-        mode) and the experts."""
+        mode) and the experts, as separate calls."""
         if keep:
             self.route(h, M, stream=stream)
         elif fused_route_align:

@@ -31,6 +31,7 @@
 
 #include "device_common.h"
 #include "launch.h"
+#include "topk_device.h"
 
 namespace moe {
 
@@ -86,12 +87,26 @@ __device__ __forceinline__ int plan_route(const PlanArgs& plan, int bb, int q, i
 // chunks are requested right after the plan rows arrive; the route checks,
 // affinities and h (whose addresses depend on the same rows) are issued just
 // before them, since a load queued behind the stream would wait for it.
-template <int Q, int CQ, int NW, int CPW, int NCH, bool FULL>
+//
+// ROUTE (one token, the decode step): there is no plan to read.  Each
+// workgroup adds the router's slice partials itself, takes the top-k by rank
+// counting and the renormalised softmax -- the same arithmetic as the router
+// kernel, so the same ids and affinities bit for bit -- and finds its block's
+// expert in the canonical plan of the token (one block per selected expert,
+// in ascending expert order).  Workgroup (0, 0) writes the ids, affinities,
+// logits and plan.  This replaces the router's last-workgroup hand-off (a
+// store, a ticket and a reload across the device) by 4 KiB of redundant
+// loads per workgroup.
+constexpr int kRouteSlices = 16;  // router row slices a routing workgroup adds
+constexpr int kRouteMaxE = 512;   // experts (one per thread of the workgroup)
+
+template <int Q, int CQ, int NW, int CPW, int NCH, bool FULL, int XG>
 __global__ void __launch_bounds__(NW * MOE_WAVE)
-expert_fused_kernel(PlanArgs plan, const float* __restrict__ h, const float* __restrict__ topk_w, int H, int I,
-                    const uint16_t* __restrict__ Wg, const uint16_t* __restrict__ Wu,
+expert_fused_kernel(PlanArgs plan, RouteArgs route, const float* __restrict__ h, const float* __restrict__ topk_w,
+                    int H, int I, const uint16_t* __restrict__ Wg, const uint16_t* __restrict__ Wu,
                     const uint16_t* __restrict__ Wd, float* __restrict__ part, int nrange,
                     int32_t* __restrict__ err) {
+    constexpr bool ROUTE = XG > 0;        // experts in XG groups of 64
     constexpr int NT = NW * MOE_WAVE;     // threads
     constexpr int CH = NW * CPW;          // channels per chunk
     constexpr int RG = NT / kThreads;     // down row groups (256 column threads each)
@@ -100,6 +115,20 @@ expert_fused_kernel(PlanArgs plan, const float* __restrict__ h, const float* __r
     __shared__ float sp[CH];
     __shared__ float4 hs[Q * MOE_WAVE * 2];
     __shared__ float4 red[RG > 1 ? (RG - 1) * kThreads * CQ * 2 : 1];
+    __shared__ __align__(16) uint64_t rkey[ROUTE ? kRouteMaxE : 2];
+    __shared__ int4 rrank4[ROUTE ? XG * MOE_WAVE : 1];  // per expert: the P partial ranks, 0-padded
+    __shared__ int rsel_e[ROUTE ? MOE_WAVE : 1];
+    __shared__ float rsel_l[ROUTE ? MOE_WAVE : 1];
+    __shared__ int rsel_p[ROUTE ? MOE_WAVE : 1];
+    static_assert(!ROUTE || NT >= XG * MOE_WAVE, "one thread per expert");
+    if constexpr (ROUTE) {
+        // Every argument is read from the kernel-argument segment at entry:
+        // a late read would be a memory round trip before the weight stream.
+        pin_arg(route.part); pin_arg(route.bias); pin_arg(route.nslices); pin_arg(route.ids);
+        pin_arg(route.wts); pin_arg(route.logits); pin_arg(route.sorted_routes); pin_arg(route.block_expert);
+        pin_arg(route.counts); pin_arg(plan.E); pin_arg(plan.k); pin_arg(plan.b); pin_arg(h); pin_arg(Wg);
+        pin_arg(Wu); pin_arg(Wd); pin_arg(part); pin_arg(nrange); pin_arg(H); pin_arg(I);
+    }
     const int blk = blockIdx.x;
     const int range = blockIdx.y;
     const int b = plan.b;
@@ -109,12 +138,89 @@ expert_fused_kernel(PlanArgs plan, const float* __restrict__ h, const float* __r
     const int ct = tid % kThreads;        // down column thread
     const int rgp = tid / kThreads;       // down row group
 
+    constexpr int HPT = (Q * MOE_WAVE * 2 + NT - 1) / NT;  // float4 of h per thread
+    float4 hreg[HPT];  // h of the first route, for the LDS stage
+    int e, r0, nb, rv;
+    float av;
+    bool spec;
+    uint64_t todo;
+    int rk[ROUTE ? XG : 1], below[ROUTE ? XG : 1];  // ROUTE: ranks and plan positions of experts 64 g + lane
+    float lg = 0.f;                                  // ROUTE: logit of expert tid
+    if constexpr (ROUTE) {
+        // The workgroup routes the (single) token itself.  Round 1: h and the
+        // router's slice partials of logit tid, none of which depends on the
+        // routing.  Every workgroup adds the slices in the same order, so all
+        // hold the same logits, top-k and affinities.
+#pragma unroll
+        for (int u = 0; u < HPT; ++u)
+            hreg[u] = *reinterpret_cast<const float4*>(h + min((tid + NT * u) * 4, H - 4));
+        const int E = plan.E, k = plan.k;
+        const int ex = min(tid, E - 1);
+        float xs[kRouteSlices];
+#pragma unroll
+        for (int u = 0; u < kRouteSlices; ++u) xs[u] = route.part[(size_t)min(u, route.nslices - 1) * E + ex];
+        const float bv = route.bias ? route.bias[ex] : 0.f;
+#pragma unroll
+        for (int u = 0; u < kRouteSlices; ++u) lg += u < route.nslices ? xs[u] : 0.f;  // slice order
+        if (route.bias) lg += bv;
+        if (tid < E) {
+            rkey[tid] = order_key((lg != lg) ? -INFINITY : lg, tid);  // NaN ranks as -inf
+            if (route.logits && blk == 0 && range == 0) route.logits[tid] = lg;
+        }
+        __syncthreads();
+        // rank(x) = # keys above x's key, counted in P parts of E/P keys
+        const int lp = 4 * E <= NT ? 2 : (2 * E <= NT ? 1 : 0);
+        const int P = 1 << lp;
+        const int n = E >> lp;
+        if (tid < P * E) {
+            const int pt = (tid >= E) + (tid >= 2 * E) + (tid >= 3 * E);
+            const int x = tid - pt * E;
+            int* dst = reinterpret_cast<int*>(rrank4 + x);
+            dst[pt] = count_greater(rkey, pt * n, n, rkey[x]);
+            if (pt == 0)
+                for (int j = P; j < 4; ++j) dst[j] = 0;
+        }
+        __syncthreads();
+        // Every wave: lane l looks at experts l + 64 g.  The canonical plan of
+        // one token has one block per selected expert, in ascending expert
+        // order, so block blk belongs to the (blk+1)-th selected expert in id
+        // order; its slot (route id) is its rank.  That is all the weight
+        // stream needs; the affinities follow once it is in flight.
+#pragma unroll
+        for (int g = 0; g < XG; ++g) {
+            const int4 v = rrank4[min(lane + MOE_WAVE * g, E - 1)];
+            rk[g] = lane + MOE_WAVE * g < E ? (v.x + v.y) + (v.z + v.w) : k;
+        }
+        int before = 0;
+        e = -1;
+        r0 = 0;
+#pragma unroll
+        for (int g = 0; g < XG; ++g) {
+            const bool sel = rk[g] < k;
+            const uint64_t m = __ballot(sel);
+            below[g] = before + (int)__builtin_amdgcn_mbcnt_hi((uint32_t)(m >> 32),
+                                                               __builtin_amdgcn_mbcnt_lo((uint32_t)m, 0));
+            const uint64_t hit = __ballot(sel && below[g] == blk);
+            if (hit) {
+                const int q = __builtin_ctzll(hit);
+                e = q + MOE_WAVE * g;
+                r0 = __builtin_amdgcn_readlane(rk[g], q);
+            }
+            before += __popcll(m);
+        }
+        if (e < 0) return;  // no such block (uniform)
+        av = 0.f;  // set once the selected logits are in LDS
+        rv = -1;
+        nb = 0;
+        spec = true;
+        todo = 1;
+    } else {
     // First round of independent loads: counts, this and the previous block's
     // expert, and the block's rows (lane q holds row q; b <= 64).
-    int nb = plan.counts[0];
-    const int e = plan.block_expert[blk];
+    nb = plan.counts[0];
+    e = plan.block_expert[blk];
     const int eprev = blk > 0 ? plan.block_expert[blk - 1] : -1;
-    int rv = plan.sorted_routes[(size_t)blk * b + min(lane, b - 1)];
+    rv = plan.sorted_routes[(size_t)blk * b + min(lane, b - 1)];
     if (lane >= b) rv = plan.R;
     if (nb < 0 || nb > plan.max_blocks) {
         if (blk == 0 && range == 0 && tid == 0) atomicOr(err, DEVERR_BAD_COUNTS);
@@ -126,6 +232,7 @@ expert_fused_kernel(PlanArgs plan, const float* __restrict__ h, const float* __r
         return;
     }
     if (eprev == e) return;  // not the first block of the expert's run (uniform)
+    }
 
     const int cbase = range * NCH * CH;
     const size_t ebase = (size_t)e * I * H;
@@ -169,6 +276,26 @@ expert_fused_kernel(PlanArgs plan, const float* __restrict__ h, const float* __r
         }
     };
 
+    if constexpr (ROUTE) {
+        // The weight stream of the token's route starts now, two chunks deep.
+        issue_gu(0, 0);
+        issue_d(0, 0);
+        if (NCH > 1) {
+            issue_gu(1, 1);
+            issue_d(1, 1);
+        }
+        // Slot rank of each selected expert: its id, logit and plan position
+        // (wave g holds the logits of experts 64 g + lane).
+        const int k = plan.k;
+#pragma unroll
+        for (int g = 0; g < XG; ++g) {
+            if (wave == g && rk[g] < k) {
+                rsel_e[rk[g]] = tid;
+                rsel_l[rk[g]] = (lg != lg) ? -INFINITY : lg + 0.0f;  // the logit of the order key
+                rsel_p[rk[g]] = below[g];
+            }
+        }
+    } else {
     // Second round, issued before any weight: every row's id check and
     // affinity (unconditional loads, the row is in range) and h of row 0,
     // which is the expert's first route whenever the plan is well formed.
@@ -179,10 +306,8 @@ expert_fused_kernel(PlanArgs plan, const float* __restrict__ h, const float* __r
     const int rc = min(max(rv, 0), plan.R - 1);
     const int idv0 = plan.topk_ids[rc];
     const float avv0 = topk_w[rc];
-    const int r0 = __builtin_amdgcn_readfirstlane(rv);
-    const bool spec = r0 >= 0 && r0 < plan.R;  // uniform
-    constexpr int HPT = (Q * MOE_WAVE * 2 + NT - 1) / NT;  // float4 of h per thread
-    float4 hreg[HPT];
+    r0 = __builtin_amdgcn_readfirstlane(rv);
+    spec = r0 >= 0 && r0 < plan.R;  // uniform
     const float* h0row = h + (size_t)(min(max(r0, 0), plan.R - 1) / plan.k) * H;
 #pragma unroll
     for (int u = 0; u < HPT; ++u)
@@ -197,8 +322,9 @@ expert_fused_kernel(PlanArgs plan, const float* __restrict__ h, const float* __r
     const bool ok = inr && idv0 == e;
     if (!ok && rv != plan.R && range == 0 && tid < MOE_WAVE) atomicOr(err, DEVERR_BAD_PLAN);
     if (!ok) rv = -1;
-    const float av = ok ? avv0 : 0.f;
-    uint64_t todo = __ballot(rv >= 0);  // valid rows of the first block (wave-uniform)
+    av = ok ? avv0 : 0.f;
+    todo = __ballot(rv >= 0);  // valid rows of the first block (wave-uniform)
+    }
 
     // Gate/up of one chunk from h in LDS: sp[c] = a * SiLU(g_j) * u_j.
     auto gateup = [&](int ci, int buf, float a) {
@@ -288,7 +414,6 @@ expert_fused_kernel(PlanArgs plan, const float* __restrict__ h, const float* __r
         // flight.  Chunk ci+2 refills buffer ci&1 as soon as chunk ci's gate/up
         // (then down) rows have been consumed.
         todo &= ~1ull;
-        const float a = __int_as_float(__builtin_amdgcn_readfirstlane(__float_as_int(av)));
 #pragma unroll
         for (int u = 0; u < HPT; ++u) {
             const int i = tid + NT * u;
@@ -299,7 +424,34 @@ expert_fused_kernel(PlanArgs plan, const float* __restrict__ h, const float* __r
         for (int cq = 0; cq < CQ; ++cq)
 #pragma unroll
             for (int x = 0; x < 8; ++x) acc[cq][x] = 0.f;
-        __syncthreads();  // hs ready
+        __syncthreads();  // hs ready (ROUTE: and the selected experts)
+        if constexpr (ROUTE) {
+            // Lane s: slot s.  The renormalised softmax over the selected
+            // logits (as the router computes it); workgroup (0, 0) writes the
+            // token's ids, affinities and plan, as the router and the
+            // alignment would.
+            const int k = plan.k;
+            const int s = min(lane, k - 1);
+            const int se = rsel_e[s];
+            const float sw = topk_softmax(rsel_l[s], lane, k);
+            av = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(sw), r0));
+            if (blk == 0 && range == 0 && wave == 0) {
+                const int pos = rsel_p[s];
+                if (lane < k) {
+                    route.ids[lane] = se;
+                    route.wts[lane] = sw;
+                    route.block_expert[pos] = se;
+                    route.sorted_routes[pos * b] = lane;
+                }
+                for (int i = lane; i < k * b; i += MOE_WAVE)
+                    if (i % b) route.sorted_routes[i] = k;  // pad sentinel M*k
+                if (lane == 0) {
+                    route.counts[0] = k;
+                    route.counts[1] = k * b;
+                }
+            }
+        }
+        const float a = __int_as_float(__builtin_amdgcn_readfirstlane(__float_as_int(av)));
 #pragma unroll
         for (int ci = 0; ci < NCH; ++ci) {
             const int buf = ci & 1;
@@ -796,19 +948,20 @@ constexpr int kFusedCPW = 1;
 constexpr int fused_nch(int Q) { return Q <= 4 ? 3 : 1; }
 constexpr int fused_range(int Q) { return kFusedNW * kFusedCPW * fused_nch(Q); }
 
-template <int Q, int CQ>
-hipError_t fused_q(const PlanArgs& plan, const float* h, const float* topk_w, int H, int I, const uint16_t* Wg,
-                   const uint16_t* Wu, const uint16_t* Wd, float* part, int32_t* err, hipStream_t stream) {
+template <int Q, int CQ, int XG>
+hipError_t fused_q(const PlanArgs& plan, const RouteArgs& route, const float* h, const float* topk_w, int H, int I,
+                   const uint16_t* Wg, const uint16_t* Wu, const uint16_t* Wd, float* part, int32_t* err,
+                   hipStream_t stream) {
     constexpr int NCH = fused_nch(Q);
     const int nrange = (I + fused_range(Q) - 1) / fused_range(Q);
     const dim3 grid(plan.max_blocks, nrange);
     const dim3 block(kFusedNW * MOE_WAVE);
     if (H == 512 * Q && H == 2048 * CQ)
-        MOE_LAUNCH((expert_fused_kernel<Q, CQ, kFusedNW, kFusedCPW, NCH, true>), grid, block, 0, stream, plan,
-                           h, topk_w, H, I, Wg, Wu, Wd, part, nrange, err);
+        MOE_LAUNCH((expert_fused_kernel<Q, CQ, kFusedNW, kFusedCPW, NCH, true, XG>), grid, block, 0, stream,
+                   plan, route, h, topk_w, H, I, Wg, Wu, Wd, part, nrange, err);
     else
-        MOE_LAUNCH((expert_fused_kernel<Q, CQ, kFusedNW, kFusedCPW, NCH, false>), grid, block, 0, stream, plan,
-                           h, topk_w, H, I, Wg, Wu, Wd, part, nrange, err);
+        MOE_LAUNCH((expert_fused_kernel<Q, CQ, kFusedNW, kFusedCPW, NCH, false, XG>), grid, block, 0, stream,
+                   plan, route, h, topk_w, H, I, Wg, Wu, Wd, part, nrange, err);
     return hipGetLastError();
 }
 
@@ -830,10 +983,28 @@ hipError_t launch_expert_fused(const PlanArgs& plan, const float* h, const float
                                const uint16_t* Wg, const uint16_t* Wu, const uint16_t* Wd, float* part, int32_t* err,
                                hipStream_t stream) {
     const int Q = (H + 511) / 512;
-    const int CQ = (H + 2047) / 2048;
-    if (Q <= 4) return fused_q<4, 1>(plan, h, topk_w, H, I, Wg, Wu, Wd, part, err, stream);
-    if (Q <= 8) return fused_q<8, 2>(plan, h, topk_w, H, I, Wg, Wu, Wd, part, err, stream);
+    const RouteArgs none{};
+    if (Q <= 4) return fused_q<4, 1, 0>(plan, none, h, topk_w, H, I, Wg, Wu, Wd, part, err, stream);
+    if (Q <= 8) return fused_q<8, 2, 0>(plan, none, h, topk_w, H, I, Wg, Wu, Wd, part, err, stream);
     return hipErrorInvalidValue;  // H > 4096: the register tile would spill; the split schedule is used
+}
+
+bool decode_fused_ok(int H, int E, int k, int nslices) {
+    return dense_uses_fused(1, H) && E <= kRouteMaxE && k <= MOE_WAVE && nslices >= 1 && nslices <= kRouteSlices;
+}
+
+hipError_t launch_decode_fused(const PlanArgs& plan, const RouteArgs& route, const float* h, int H, int I,
+                               const uint16_t* Wg, const uint16_t* Wu, const uint16_t* Wd, float* part, int32_t* err,
+                               hipStream_t stream) {
+    if (!decode_fused_ok(H, plan.E, plan.k, route.nslices) || plan.R != plan.k || plan.max_blocks != plan.k)
+        return hipErrorInvalidValue;
+    const int Q = (H + 511) / 512;
+    // experts in groups of 64: 2 groups up to 128 experts, else 8
+    if (plan.E <= 2 * MOE_WAVE)
+        return Q <= 4 ? fused_q<4, 1, 2>(plan, route, h, nullptr, H, I, Wg, Wu, Wd, part, err, stream)
+                      : fused_q<8, 2, 2>(plan, route, h, nullptr, H, I, Wg, Wu, Wd, part, err, stream);
+    return Q <= 4 ? fused_q<4, 1, 8>(plan, route, h, nullptr, H, I, Wg, Wu, Wd, part, err, stream)
+                  : fused_q<8, 2, 8>(plan, route, h, nullptr, H, I, Wg, Wu, Wd, part, err, stream);
 }
 
 hipError_t launch_gateup_dense(const PlanArgs& plan, const float* h, int H, int I, const uint16_t* Wg,

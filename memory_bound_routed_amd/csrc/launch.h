@@ -54,6 +54,12 @@ hipError_t launch_router_align(const float* h, int M, int H, const uint16_t* Wr,
                                int32_t* sorted_routes, int32_t* block_expert, int32_t* counts, int32_t* err,
                                hipStream_t stream);
 
+// Router GEMV of one token without the top-k: part fp32 [router_slices(H, E)][E]
+// (row-slice partials; logit e = 0 + part[0][e] + part[1][e] + ... in slice
+// order, then + bias[e]).
+int router_slices(int H, int E);
+hipError_t launch_router_partials(const float* h, int H, const uint16_t* Wr, int E, float* part, hipStream_t stream);
+
 // ---- align.hip
 size_t align_lds_bytes(int R, int E);
 hipError_t launch_align(const int32_t* topk_ids, int R, int E, int b, int32_t* sorted_routes,
@@ -78,6 +84,25 @@ bool dense_uses_fused(int M, int H);
 int dense_chunks(int M, int H, int I);
 int down_chunks(int I);
 hipError_t launch_expert_fused(const PlanArgs& plan, const float* h, const float* topk_w, int H, int I,
+                               const uint16_t* Wg, const uint16_t* Wu, const uint16_t* Wd, float* part, int32_t* err,
+                               hipStream_t stream);
+// The fused schedule for one token that routes the token itself from the
+// router's slice partials (see router_slices) and writes the routing and the
+// plan as moe_route_align would.  plan: R = k, max_blocks = k, E, k, b; its
+// arrays are not read.
+struct RouteArgs {
+    const float* part;       // fp32 [nslices][E] router slice partials
+    const float* bias;       // fp32 [E] or null
+    int nslices;
+    int32_t* ids;            // int32 [k] out
+    float* wts;              // fp32 [k] out
+    float* logits;           // fp32 [E] out, or null
+    int32_t* sorted_routes;  // int32 [k*b] out
+    int32_t* block_expert;   // int32 [k] out
+    int32_t* counts;         // int32 [2] out
+};
+bool decode_fused_ok(int H, int E, int k, int nslices);
+hipError_t launch_decode_fused(const PlanArgs& plan, const RouteArgs& route, const float* h, int H, int I,
                                const uint16_t* Wg, const uint16_t* Wu, const uint16_t* Wd, float* part, int32_t* err,
                                hipStream_t stream);
 hipError_t launch_gateup_dense(const PlanArgs& plan, const float* h, int H, int I, const uint16_t* Wg,

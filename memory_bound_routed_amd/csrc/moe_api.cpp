@@ -160,7 +160,8 @@ const char* moe_status_string(moe_status s) {
 const char* moe_kernel_name(int32_t k) {
     static const char* names[MOE_KERNEL_COUNT] = {"router",      "vq_shared",   "align",        "gateup",
                                                   "gateup_vqlr", "down",        "combine",      "chan_select",
-                                                  "chan_gather", "chan_combine", "expert_fused", "router_align"};
+                                                  "chan_gather", "chan_combine", "expert_fused", "router_align",
+                                                  "router_gemv", "decode_fused"};
     return (k >= 0 && k < MOE_KERNEL_COUNT) ? names[k] : nullptr;
 }
 
@@ -386,6 +387,69 @@ moe_status moe_expert_forward(moe_ctx* ctx, const float* h, int32_t M, const int
     }
     Launch l(ctx, MOE_KERNEL_COMBINE, s);
     e = moe::launch_combine(topk_ids, M, c.top_k, c.E, c.H, nchunk, ctx->down_part, y, s);
+    l.done();
+    return hip_status(e);
+}
+
+moe_status moe_decode_step(moe_ctx* ctx, const float* h, int32_t M, int32_t* topk_ids, float* topk_w,
+                           float* logits_out, int32_t* sorted_routes, int32_t* block_expert, int32_t* counts,
+                           int32_t keep_channels, int32_t* kept_out, float* y, void* stream) {
+    if (!ctx || M < 0 || keep_channels < 0) return MOE_ERR_INVALID_ARG;
+    const moe_config& c = ctx->cfg;
+    if (M > c.max_tokens) return MOE_ERR_CAPACITY;
+    if (keep_channels > 0) {
+        if (c.max_keep == 0 || c.wformat != MOE_WFORMAT_DENSE) return MOE_ERR_UNSUPPORTED;
+        if (keep_channels > c.max_keep) return MOE_ERR_CAPACITY;
+        moe_status st = moe_route_topk(ctx, h, M, topk_ids, topk_w, logits_out, stream);
+        if (st != MOE_OK) return st;
+        return moe_expert_forward(ctx, h, M, topk_ids, topk_w, nullptr, nullptr, nullptr, keep_channels, kept_out, y,
+                                  stream);
+    }
+    const int nsl = moe::router_slices(c.H, c.E);
+    if (M != 1 || c.wformat != MOE_WFORMAT_DENSE || !moe::decode_fused_ok(c.H, c.E, c.top_k, nsl)) {
+        moe_status st = moe_route_align(ctx, h, M, topk_ids, topk_w, logits_out, sorted_routes, block_expert, counts,
+                                        stream);
+        if (st != MOE_OK) return st;
+        return moe_expert_forward(ctx, h, M, topk_ids, topk_w, sorted_routes, block_expert, counts, 0, nullptr, y,
+                                  stream);
+    }
+    if (!h || !topk_ids || !topk_w || !sorted_routes || !block_expert || !counts || !y || !aligned(h, 16) ||
+        !aligned(y, 16))
+        return MOE_ERR_INVALID_ARG;
+    hipStream_t s = static_cast<hipStream_t>(stream);
+    hipError_t e;
+    {
+        Launch l(ctx, MOE_KERNEL_ROUTER_GEMV, s);
+        e = moe::launch_router_partials(h, c.H, ctx->w.router_w, c.E, ctx->router_part, s);
+        l.done();
+        if (e != hipSuccess) return MOE_ERR_HIP;
+    }
+    moe::PlanArgs plan{};
+    plan.R = c.top_k;
+    plan.k = c.top_k;
+    plan.fk = FastDiv((uint32_t)c.top_k);
+    plan.b = c.block_b;
+    plan.max_blocks = c.top_k;
+    plan.E = c.E;
+    moe::RouteArgs route{};
+    route.part = ctx->router_part;
+    route.bias = ctx->w.router_bias;
+    route.nslices = nsl;
+    route.ids = topk_ids;
+    route.wts = topk_w;
+    route.logits = logits_out;
+    route.sorted_routes = sorted_routes;
+    route.block_expert = block_expert;
+    route.counts = counts;
+    {
+        Launch l(ctx, MOE_KERNEL_DECODE_FUSED, s);
+        e = moe::launch_decode_fused(plan, route, h, c.H, c.I, ctx->w.w_gate, ctx->w.w_up, ctx->w.w_down,
+                                     ctx->down_part, ctx->err, s);
+        l.done();
+        if (e != hipSuccess) return MOE_ERR_HIP;
+    }
+    Launch l(ctx, MOE_KERNEL_COMBINE, s);
+    e = moe::launch_combine(topk_ids, 1, c.top_k, c.E, c.H, moe::dense_chunks(1, c.H, c.I), ctx->down_part, y, s);
     l.done();
     return hip_status(e);
 }

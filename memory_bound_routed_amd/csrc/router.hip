@@ -11,6 +11,7 @@
 #include "align_device.h"
 #include "device_common.h"
 #include "launch.h"
+#include "topk_device.h"
 
 namespace moe {
 
@@ -257,35 +258,6 @@ struct TopkLds {
     float l[kTokTile][32];
 };
 
-// Total-order key of (logit, expert): a larger key ranks first.  The high
-// word maps the fp32 logit monotonically onto uint32 (-0 is first turned into
-// +0, so equal logits give equal words), the low word is ~e, so that equal
-// logits order by ascending expert id.  Keys are distinct within a token.
-__device__ __forceinline__ uint64_t order_key(float l, int e) {
-    uint32_t u = __float_as_uint(l + 0.0f);
-    u = (u & 0x80000000u) ? ~u : (u | 0x80000000u);
-    return ((uint64_t)u << 32) | (uint32_t)~(uint32_t)e;
-}
-
-// # keys in row[j0 .. j0+n) greater than kv (n % 4 == 0, 16-byte aligned).
-__device__ __forceinline__ int count_greater(const uint64_t* row, int j0, int n, uint64_t kv) {
-    const ulonglong2* r2 = reinterpret_cast<const ulonglong2*>(row + j0);
-    int c = 0;
-    int q = 0;
-    for (; q + 8 <= n / 2; q += 8) {  // eight 16-byte reads in flight
-        ulonglong2 o[8];
-#pragma unroll
-        for (int u = 0; u < 8; ++u) o[u] = r2[q + u];
-#pragma unroll
-        for (int u = 0; u < 8; ++u) c += (o[u].x > kv ? 1 : 0) + (o[u].y > kv ? 1 : 0);
-    }
-    for (; q < n / 2; ++q) {
-        const ulonglong2 o = r2[q];
-        c += (o.x > kv ? 1 : 0) + (o.y > kv ? 1 : 0);
-    }
-    return c;
-}
-
 // Slice sum, top-k and softmax of the nt tokens t0 .. t0+nt-1 (nt <= kTokTile)
 // by one workgroup.  LDS: keys [nt][E], then the half-row rank counts
 // [2][nt][E].  COHERENT: the slice partials were written by other workgroups
@@ -334,25 +306,21 @@ __device__ __forceinline__ void topk_pass(int t0, int nt, int M, int E, int k, i
         if (rank < k) {
             const int tl = fE.div(pr);
             const uint64_t key = skey[pr];
-            const uint32_t hi = (uint32_t)(key >> 32);
-            sel.e[tl][rank] = (int)~(uint32_t)key;
-            sel.l[tl][rank] = __uint_as_float((hi & 0x80000000u) ? (hi & 0x7FFFFFFFu) : ~hi);
+            sel.e[tl][rank] = key_expert(key);
+            sel.l[tl][rank] = key_logit(key);
         }
     }
     __syncthreads();
     if (wave < nt) {  // wave w: token t0 + w; lane s: slot s
         const int t = t0 + wave;
-        const float l0 = sel.l[wave][0];
-        const float x = lane < k ? expf(sel.l[wave][lane] - l0) : 0.f;
-        float den = 0.f;
-        for (int s = 0; s < k; ++s) den += __int_as_float(__builtin_amdgcn_readlane(__float_as_int(x), s));
+        const float w = topk_softmax(sel.l[wave][min(lane, k - 1)], lane, k);
         if (lane < k) {
             if (COHERENT_IDS) {
                 store_agent(ids + (size_t)t * k + lane, sel.e[wave][lane]);
-                store_agent(wts + (size_t)t * k + lane, x / den);
+                store_agent(wts + (size_t)t * k + lane, w);
             } else {
                 ids[(size_t)t * k + lane] = sel.e[wave][lane];
-                wts[(size_t)t * k + lane] = x / den;
+                wts[(size_t)t * k + lane] = w;
             }
         }
     }
@@ -464,6 +432,17 @@ router_align_kernel(const float* __restrict__ h, int M, int H, const uint16_t* _
     rearm_ticket(ticket);
 }
 
+// Router GEMV only (one token): the tiles' slice partials part[slice][e],
+// stored for a later launch.  The expert kernel of the batch-1 decode step
+// adds them and takes the top-k itself.
+__global__ void __launch_bounds__(kThreads)
+router_partials_kernel(const float* __restrict__ h, int H, const uint16_t* __restrict__ Wr, int E,
+                       float* __restrict__ part) {
+    extern __shared__ __align__(16) float red[];
+    const RouterTiles tl(H, E);
+    router_tile<1>(h, 1, 0, H, Wr, E, tl, blockIdx.x % tl.nrs, blockIdx.x / tl.nrs, part, red);
+}
+
 size_t lds_bytes(int N) { return (size_t)(kThreads / (N / 8)) * kTokTile * N * sizeof(float); }
 
 // LDS of the one-launch router: the tile's row-group sums, or the keys and
@@ -501,6 +480,16 @@ hipError_t launch_gemv_partials(const float* h, int M, int H, const GemvJob* job
         grid = gemv_slices(H, jobs[i].N) > grid ? gemv_slices(H, jobs[i].N) : grid;
     }
     MOE_LAUNCH(gemv_partials_kernel, dim3(grid, njobs), dim3(kThreads), lds, stream, h, M, H, js);
+    return hipGetLastError();
+}
+
+int router_slices(int H, int E) { return RouterTiles(H, E).nrs; }
+
+hipError_t launch_router_partials(const float* h, int H, const uint16_t* Wr, int E, float* part, hipStream_t stream) {
+    if (E % 8 != 0) return hipErrorInvalidValue;
+    const RouterTiles tl(H, E);
+    const size_t lds = (size_t)tl.rpt * tl.cgw * sizeof(float);
+    MOE_LAUNCH(router_partials_kernel, dim3(router_grid(H, E)), dim3(kThreads), lds, stream, h, H, Wr, E, part);
     return hipGetLastError();
 }
 

@@ -596,3 +596,71 @@ def test_vq_forced_multi_route_experts(mb, b):
     ref = O.vqlr_forward(inp["h"], ids, w.astype(np.float64), inp, inp["w_down"])
     check_close(layer.y[:M].cpu().numpy(), ref)
     layer.close()
+
+
+def _step_outputs(layer, M):
+    n = int(layer.counts[1]) if M else 0
+    return {"ids": layer.ids[:M].clone(), "w": layer.w[:M].clone(), "logits": layer.logits[:M].clone(),
+            "rows": layer.sorted_routes[:n].clone(), "blocks": layer.block_expert[: n // layer.cfg.block_b].clone(),
+            "counts": layer.counts.clone(), "y": layer.y[:M].clone()}
+
+
+@pytest.mark.parametrize("case", [
+    "tiny",          # H=256: one router slice, E=16 (16-expert column groups)
+    "full",          # the batch-1 Qwen3-30B-A3B-shaped layer, two tokens
+    "ragged",        # H=1000 (hidden tail), I=72, E=24, k=3, block size 4
+    "e512_bias",     # E=512 (one rank part per thread), additive router bias on 4 experts
+    "h4096_e256",    # 16 router slices, 16-load register tile, E=256 (two rank parts)
+    "k_eq_e",        # k = E = 16: every expert selected
+    "ties",          # zero router weights + tied bias: the order is decided by the expert ids
+    "m3_fallback",   # three tokens: the separate launches
+])
+def test_decode_step_matches_separate_calls(mb, case):
+    """moe_decode_step gives bit for bit the outputs of moe_route_align +
+    moe_expert_forward (ids, affinities, logits, plan, y), and both match the
+    oracle."""
+    import torch
+    specs = {
+        "tiny": dict(wl=synth.WORKLOADS["tiny_h256_i128_e16_k2"]),
+        "full": dict(wl=synth.WORKLOADS["dense_h2048_i768_e128_k8_m1"], steps=2),
+        "ragged": dict(wl=synth.small_workload("ds_ragged", H=1000, I=72, E=24, k=3, M=1, seed=41, block_b=4)),
+        "e512_bias": dict(wl=synth.small_workload("ds_e512", H=512, I=40, E=512, k=8, M=1, seed=42, hot_experts=4)),
+        "h4096_e256": dict(wl=synth.small_workload("ds_h4096", H=4096, I=24, E=256, k=5, M=1, seed=43)),
+        "k_eq_e": dict(wl=synth.small_workload("ds_keqe", H=256, I=16, E=16, k=16, M=1, seed=44)),
+        "ties": dict(wl=synth.small_workload("ds_ties", H=256, I=16, E=16, k=4, M=1, seed=45)),
+        "m3_fallback": dict(wl=synth.small_workload("ds_m3", H=256, I=24, E=32, k=4, M=3, seed=46)),
+    }[case]
+    wl = specs["wl"]
+    say("decode step vs separate calls:", case, dict(H=wl.H, I=wl.I, E=wl.E, k=wl.k, M=wl.M, b=wl.block_b))
+    inp = synth.layer_inputs(wl, 0)
+    if case == "ties":
+        inp["router_w"] = np.zeros_like(inp["router_w"])
+        inp["router_bias"] = np.array([0.5, 1.0, 1.0, 0.25, 1.0, 0.5] + [0.25] * 10, np.float32)
+    layer = make_layer(mb, wl, inp, wl.M)
+    for step in range(specs.get("steps", 1)):
+        h_np = synth.hidden(wl, 0, step, M=wl.M)
+        h = to_dev(h_np)
+        layer.route_align(h, wl.M, logits=True)
+        layer.forward(h, wl.M)
+        torch.cuda.synchronize()
+        a = _step_outputs(layer, wl.M)
+        for t in (layer.ids, layer.w, layer.logits, layer.sorted_routes, layer.block_expert, layer.counts, layer.y):
+            t.fill_(-3)
+        layer.decode_step(h, wl.M, logits=True)
+        torch.cuda.synchronize()
+        b = _step_outputs(layer, wl.M)
+        for what in a:
+            assert torch.equal(a[what].view(torch.int32), b[what].view(torch.int32)), what
+        assert mb.moe_read_device_error(layer.ctx) == 0
+        g = {"ids": b["ids"].cpu().numpy().astype(np.int64), "w": b["w"].cpu().numpy(),
+             "logits": b["logits"].cpu().numpy(), "num_blocks": int(b["counts"][0]),
+             "num_padded": int(b["counts"][1]), "sorted_routes": b["rows"].cpu().numpy().astype(np.int64),
+             "block_expert": b["blocks"].cpu().numpy().astype(np.int64)}
+        stage_inp = dict(inp, h=h_np)
+        check_router(g, stage_inp, wl.k, wl.H)
+        if case == "ties":
+            np.testing.assert_array_equal(g["ids"], [[1, 2, 4, 0]])
+        check_plan(g, wl.E, wl.block_b)
+        ref = O.dense_forward(h_np, g["ids"], g["w"].astype(np.float64), inp["w_gate"], inp["w_up"], inp["w_down"])
+        say("  step", step, check_close(b["y"].cpu().numpy(), ref))
+    layer.close()
