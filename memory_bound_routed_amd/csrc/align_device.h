@@ -20,7 +20,8 @@ constexpr int kAlignThreads = 256;
 // LDS bytes align_workgroup needs for R routes and E experts.
 __host__ __device__ inline size_t align_lds_bytes_inline(int R, int E) {
     const int nchunk = (R + MOE_WAVE - 1) / MOE_WAVE;
-    return sizeof(int) * ((size_t)2 * R + (size_t)nchunk * E + 2 * (size_t)E + 1);
+    const size_t wg = sizeof(int) * ((size_t)2 * R + (size_t)nchunk * E + 2 * (size_t)E + 1);
+    return wg > sizeof(int) * 2 * MOE_WAVE ? wg : sizeof(int) * 2 * MOE_WAVE;
 }
 
 // Run by all 256 threads of one workgroup; smem holds align_lds_bytes(R, E) bytes.
@@ -108,40 +109,69 @@ __device__ inline void align_workgroup(IdOf id_of, int R, int E, int b,
     }
 }
 
-// The same alignment for R <= 64 routes by one wave, in registers: lane r
-// holds route r.  With id the lane's expert (-1 if invalid),
+// The same alignment for R <= 64 routes by one wave: lane r holds route r.
+// With id the lane's expert (-1 if invalid),
 //   cnt(r)  = # routes with the same expert,   rank(r) = # of them below r,
 //   first   = the lowest route of its expert (rank 0),
 //   off(e)  = sum of the padded counts ceil(cnt/b)*b of the experts below e
 //             (summed over the first routes of those experts),
 // route r goes to off(e) + rank(r); each expert's first route writes its
 // padding rows and its blocks.  The output equals align_workgroup's: the same
-// (expert id, route id) order, the same padding, the same counts.
-// id_of(r) returns route r's id; every lane of the calling wave must call.
+// (expert id, route id) order, the same padding, the same counts.  The sums
+// over routes read the ids and padded counts from the wave's own LDS scratch
+// (2 * 64 ints; a wave's LDS accesses execute in order), four routes per
+// read.  id_of(r) returns route r's id; every lane of the calling wave must
+// call.
 template <typename IdOf>
 __device__ inline void align_wave(IdOf id_of, int R, int E, FastDiv fb, int32_t* __restrict__ sorted_routes,
                                   int32_t* __restrict__ block_expert, int32_t* __restrict__ counts,
-                                  int32_t* __restrict__ err) {
+                                  int32_t* __restrict__ err, int* scratch) {
     const int lane = threadIdx.x % MOE_WAVE;
     const int raw = lane < R ? id_of(lane) : 0;
     const bool ok = lane < R && raw >= 0 && raw < E;
     const int id = ok ? raw : -1;
     if (__ballot(lane < R && !ok) != 0 && lane == 0) atomicOr(err, DEVERR_BAD_ROUTE_ID);
+    int* sid = scratch;               // [64] expert of each route; -2 past R (equal to no id)
+    int* spad = scratch + MOE_WAVE;   // [64] padded count on an expert's first route, else 0
+    sid[lane] = lane < R ? id : -2;
+    __builtin_amdgcn_wave_barrier();
+    const int nq = (R + 3) / 4;       // groups of four routes (uniform)
+    const int4* sid4 = reinterpret_cast<const int4*>(sid);
     int cnt = 0, rank = 0;
-    for (int r2 = 0; r2 < R; ++r2) {
-        const int o = __builtin_amdgcn_readlane(id, r2);
-        cnt += o == id ? 1 : 0;
-        rank += (o == id && r2 < lane) ? 1 : 0;
+    for (int q0 = 0; q0 < nq; q0 += 8) {
+        int4 o[8];
+#pragma unroll
+        for (int u = 0; u < 8; ++u) o[u] = sid4[min(q0 + u, MOE_WAVE / 4 - 1)];
+#pragma unroll
+        for (int u = 0; u < 8; ++u) {
+            if (q0 + u >= nq) break;  // uniform
+            const int r2 = 4 * (q0 + u);
+            cnt += (o[u].x == id) + (o[u].y == id) + (o[u].z == id) + (o[u].w == id);
+            rank += (o[u].x == id && r2 < lane) + (o[u].y == id && r2 + 1 < lane) + (o[u].z == id && r2 + 2 < lane) +
+                    (o[u].w == id && r2 + 3 < lane);
+        }
     }
     const int b = (int)fb.d;
     const int padded = fb.div(cnt + b - 1) * b;
     const int first_pad = (ok && rank == 0) ? padded : 0;  // padded count, on the expert's first route only
+    spad[lane] = first_pad;
+    __builtin_amdgcn_wave_barrier();
+    const int4* spad4 = reinterpret_cast<const int4*>(spad);
     int off = 0, total = 0;
-    for (int r2 = 0; r2 < R; ++r2) {
-        const int o = __builtin_amdgcn_readlane(id, r2);
-        const int pd = __builtin_amdgcn_readlane(first_pad, r2);
-        off += o < id ? pd : 0;
-        total += pd;
+    for (int q0 = 0; q0 < nq; q0 += 8) {
+        int4 o[8], p[8];
+#pragma unroll
+        for (int u = 0; u < 8; ++u) {
+            o[u] = sid4[min(q0 + u, MOE_WAVE / 4 - 1)];
+            p[u] = spad4[min(q0 + u, MOE_WAVE / 4 - 1)];
+        }
+#pragma unroll
+        for (int u = 0; u < 8; ++u) {
+            if (q0 + u >= nq) break;  // uniform
+            off += (o[u].x < id ? p[u].x : 0) + (o[u].y < id ? p[u].y : 0) + (o[u].z < id ? p[u].z : 0) +
+                   (o[u].w < id ? p[u].w : 0);
+            total += (p[u].x + p[u].y) + (p[u].z + p[u].w);
+        }
     }
     if (ok) sorted_routes[off + rank] = lane;
     if (first_pad) {

@@ -148,7 +148,7 @@ gemv_partials_kernel(const float* __restrict__ h, int M, int H, GemvJobs jobs) {
 // tpr = cgw/8 threads cover a row of the group with one 16-byte load each,
 // rpt = 256/tpr rows per pass, kRowsPerThread passes per slice.  The rpt row
 // groups of an output are added by 8 lanes (rpt/8 groups each, in order),
-// then by a fixed xor butterfly over the 8 lanes.  A slice partial is then
+// then by a fixed butterfly over the 8 lanes (pairs, pairs of pairs, quads).  A slice partial is then
 // part[slice][t][e] as for slice_partial, but there are cgw/E times fewer
 // slices for the last workgroup to add.
 constexpr int kRouterCG = 32;
@@ -225,9 +225,11 @@ __device__ __forceinline__ void router_tile(const float* __restrict__ h, int M, 
             const float* src = red + ((size_t)sub * gpl * TT + t) * tl.cgw + c;
             for (int g = 0; g < gpl; ++g) v += src[(size_t)g * TT * tl.cgw];
         }
-        v += __shfl_xor(v, 1, MOE_WAVE);
-        v += __shfl_xor(v, 2, MOE_WAVE);
-        v += __shfl_xor(v, 4, MOE_WAVE);
+        // xor 1, xor 2, then the two quads of the 8 lanes (half-row mirror):
+        // DPP moves, no LDS round trip
+        v += dpp<MOE_DPP_QUAD_XOR1>(v);
+        v += dpp<MOE_DPP_QUAD_XOR2>(v);
+        v += dpp<MOE_DPP_ROW_HALF_MIRROR>(v);
         const int e = cg * tl.cgw + c;
         if (sub == 0 && o < nout && e < E) store_agent(part + ((size_t)rs * M + t0 + t) * E + e, v);
     }
@@ -235,8 +237,10 @@ __device__ __forceinline__ void router_tile(const float* __restrict__ h, int M, 
 
 // Router: tiles as above; per group of tokens, the last tile workgroup to
 // finish (integer ticket) adds the slices in slice order (+ bias) -- every
-// partial load is issued before the first add.  The top-k is
-// taken by rank counting under the total order (logit desc, expert id asc):
+// partial load is issued before the first add.  The top-k is taken per token
+// by one wave from the few keys above a threshold (wave_topk), else by rank
+// counting over all keys; either way under the total order (logit desc,
+// expert id asc):
 // rank(e) = #{e' : l[e'] > l[e] or (l[e'] == l[e] and e' < e)}, and the
 // expert of rank s < k goes to slot s.  The ranks are exact, so the result
 // does not depend on how the work is split.  NaN logits count as -inf.  The
@@ -293,24 +297,36 @@ __device__ __forceinline__ void topk_pass(int t0, int nt, int M, int E, int k, i
         if (logits_out) logits_out[(size_t)t * E + e] = s;
         skey[pr] = order_key((s != s) ? -INFINITY : s, e);
     }
+    __shared__ int s_slow;
+    __shared__ uint64_t wk[kTokTile][MOE_WAVE];
+    __shared__ int wi[kTokTile][MOE_WAVE];
+    if (tid == 0) s_slow = E > 4 * MOE_WAVE;
     __syncthreads();
-    // rank = # keys of the token above the expert's key, counted in two halves
-    for (int it = tid; it < 2 * nt * E; it += kThreads) {
-        const int half = it >= nt * E ? 1 : 0, pr = it - half * nt * E;
-        const int tl = fE.div(pr);
-        prank[it] = count_greater(skey + tl * E, half * halfE, halfE, skey[pr]);
-    }
+    // Wave w selects token t0 + w by itself (see wave_topk); a token with too
+    // many candidates sends the workgroup to the count of every key.
+    if (E <= 4 * MOE_WAVE && wave < nt && !wave_topk<4>(skey + wave * E, E, k, sel.e[wave], sel.l[wave], wk[wave],
+                                                         wi[wave]))
+        s_slow = 1;
     __syncthreads();
-    for (int pr = tid; pr < nt * E; pr += kThreads) {
-        const int rank = prank[pr] + prank[nt * E + pr];
-        if (rank < k) {
+    if (s_slow) {
+        // rank = # keys of the token above the expert's key, counted in two halves
+        for (int it = tid; it < 2 * nt * E; it += kThreads) {
+            const int half = it >= nt * E ? 1 : 0, pr = it - half * nt * E;
             const int tl = fE.div(pr);
-            const uint64_t key = skey[pr];
-            sel.e[tl][rank] = key_expert(key);
-            sel.l[tl][rank] = key_logit(key);
+            prank[it] = count_greater(skey + tl * E, half * halfE, halfE, skey[pr]);
         }
+        __syncthreads();
+        for (int pr = tid; pr < nt * E; pr += kThreads) {
+            const int rank = prank[pr] + prank[nt * E + pr];
+            if (rank < k) {
+                const int tl = fE.div(pr);
+                const uint64_t key = skey[pr];
+                sel.e[tl][rank] = key_expert(key);
+                sel.l[tl][rank] = key_logit(key);
+            }
+        }
+        __syncthreads();
     }
-    __syncthreads();
     if (wave < nt) {  // wave w: token t0 + w; lane s: slot s
         const int t = t0 + wave;
         const float w = topk_softmax(sel.l[wave][min(lane, k - 1)], lane, k);
@@ -407,7 +423,7 @@ router_align_kernel(const float* __restrict__ h, int M, int H, const uint16_t* _
             const int aw = min(M, kThreads / MOE_WAVE - 1);
             if ((int)threadIdx.x / MOE_WAVE == aw)
                 align_wave([&](int r) { const int t = fk.div(r); return sel.e[t][r - t * k]; }, R, E, fb,
-                           sorted_routes, block_expert, counts, err);
+                           sorted_routes, block_expert, counts, err, reinterpret_cast<int*>(red));
         } else {
             __syncthreads();
             align_workgroup([&](int r) { return ids[r]; }, R, E, b, sorted_routes, block_expert, counts, err,
@@ -424,7 +440,8 @@ router_align_kernel(const float* __restrict__ h, int M, int H, const uint16_t* _
     if (!s_last) return;
     if (R <= MOE_WAVE) {
         if (threadIdx.x < MOE_WAVE)
-            align_wave([&](int r) { return load_agent(ids + r); }, R, E, fb, sorted_routes, block_expert, counts, err);
+            align_wave([&](int r) { return load_agent(ids + r); }, R, E, fb, sorted_routes, block_expert, counts, err,
+                       reinterpret_cast<int*>(red));
     } else {
         align_workgroup([&](int r) { return load_agent(ids + r); }, R, E, b, sorted_routes, block_expert, counts, err,
                         reinterpret_cast<int*>(red));

@@ -7,6 +7,8 @@
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
+#include "device_common.h"
+
 namespace moe {
 
 // Total-order key of (logit, expert): a larger key ranks first.  The high
@@ -58,6 +60,99 @@ __device__ __forceinline__ int count_greater(const uint64_t* row, int j0, int n,
         c = add_if_less(add_if_less(c, kv, o.x), kv, o.y);
     }
     return c;
+}
+
+__device__ __forceinline__ uint64_t minmax64(uint64_t a, uint64_t b, bool take_max) {
+    return take_max ? (a > b ? a : b) : (a < b ? a : b);
+}
+
+__device__ __forceinline__ uint64_t readlane64(uint64_t v, int lane) {
+    const uint32_t lo = __builtin_amdgcn_readlane((uint32_t)v, lane);
+    const uint32_t hi = __builtin_amdgcn_readlane((uint32_t)(v >> 32), lane);
+    return ((uint64_t)hi << 32) | lo;
+}
+
+// # set bits of m below this lane.
+__device__ __forceinline__ int mbcnt64(uint64_t m) {
+    return (int)__builtin_amdgcn_mbcnt_hi((uint32_t)(m >> 32), __builtin_amdgcn_mbcnt_lo((uint32_t)m, 0));
+}
+
+// One butterfly step over a DPP lane pairing: the larger (take_max) or the
+// smaller of a lane's key and its partner's.
+template <int CTRL>
+__device__ __forceinline__ uint64_t bfly_step(uint64_t v, bool take_max) {
+    const uint32_t lo = __builtin_amdgcn_update_dpp(0u, (uint32_t)v, CTRL, 0xF, 0xF, false);
+    const uint32_t hi = __builtin_amdgcn_update_dpp(0u, (uint32_t)(v >> 32), CTRL, 0xF, 0xF, false);
+    return minmax64(v, ((uint64_t)hi << 32) | lo, take_max);
+}
+
+// Top-k of one token's E <= 64*G keys (keys[x], x < E, in LDS) by one wave,
+// without the other waves.  T = the least of the maxima of k' >= k aligned
+// groups of 64/k' lanes (k' the power of two >= k; lane l holds keys
+// l + 64 g): at least k keys are >= T, so every key of the top k is >= T (a
+// candidate), and a candidate's rank among all keys is its rank among the
+// candidates.  With at most 64 candidates they are ranked in the wave's LDS
+// list wk/wi (64 entries each; a wave's LDS accesses execute in order), the
+// expert and logit of slot s go to sel_e[s] / sel_l[s] (s < k) and the
+// function returns true; else it writes nothing and returns false (uniform).
+template <int G>
+__device__ __forceinline__ bool wave_topk(const uint64_t* keys, int E, int k, int* sel_e, float* sel_l, uint64_t* wk,
+                                          int* wi) {
+    const int lane = threadIdx.x % MOE_WAVE;
+    uint64_t kk[G];
+#pragma unroll
+    for (int g = 0; g < G; ++g) {
+        const uint64_t kv = keys[min(lane + MOE_WAVE * g, E - 1)];
+        kk[g] = lane + MOE_WAVE * g < E ? kv : 0ull;  // 0: no expert
+    }
+    uint64_t v = kk[0];
+#pragma unroll
+    for (int g = 1; g < G; ++g) v = v > kk[g] ? v : kk[g];
+    const int gb = 6 - (k <= 1 ? 0 : 32 - __builtin_clz((unsigned)(k - 1)));  // steps taking the maximum
+    v = bfly_step<MOE_DPP_QUAD_XOR1>(v, 0 < gb);
+    v = bfly_step<MOE_DPP_QUAD_XOR2>(v, 1 < gb);
+    v = bfly_step<MOE_DPP_ROW_HALF_MIRROR>(v, 2 < gb);
+    v = bfly_step<MOE_DPP_ROW_MIRROR>(v, 3 < gb);
+    const uint64_t T = minmax64(minmax64(readlane64(v, 0), readlane64(v, 16), 4 < gb),
+                                minmax64(readlane64(v, 32), readlane64(v, 48), 4 < gb), 5 < gb);
+    uint64_t m[G];
+    int C = 0;
+#pragma unroll
+    for (int g = 0; g < G; ++g) {
+        m[g] = __ballot(lane + MOE_WAVE * g < E && kk[g] >= T);
+        C += __popcll(m[g]);
+    }
+    if (C > MOE_WAVE) return false;
+    int base = 0;
+#pragma unroll
+    for (int g = 0; g < G; ++g) {
+        if ((m[g] >> lane) & 1ull) {
+            const int pos = base + mbcnt64(m[g]);
+            wk[pos] = kk[g];
+            wi[pos] = lane + MOE_WAVE * g;
+        }
+        base += __popcll(m[g]);
+    }
+    if (lane >= C) wk[lane] = 0ull;  // pad: ranks no one
+    __builtin_amdgcn_wave_barrier();
+    if (lane < C) {
+        const uint64_t ck = wk[lane];
+        const ulonglong2* w2 = reinterpret_cast<const ulonglong2*>(wk);
+        int c = 0;
+        for (int j0 = 0; j0 < (C + 1) / 2; j0 += 8) {  // eight pairs in flight; entries past C are 0
+            ulonglong2 o[8];
+#pragma unroll
+            for (int u = 0; u < 8; ++u) o[u] = w2[j0 + u];  // j0 + u < 32
+#pragma unroll
+            for (int u = 0; u < 8; ++u) c = add_if_less(add_if_less(c, ck, o[u].x), ck, o[u].y);
+        }
+        if (c < k) {
+            sel_e[c] = wi[lane];
+            sel_l[c] = key_logit(ck);
+        }
+    }
+    __builtin_amdgcn_wave_barrier();
+    return true;
 }
 
 // Renormalised softmax over the selected logits of one token, on one wave:
