@@ -664,3 +664,42 @@ def test_decode_step_matches_separate_calls(mb, case):
         ref = O.dense_forward(h_np, g["ids"], g["w"].astype(np.float64), inp["w_gate"], inp["w_up"], inp["w_down"])
         say("  step", step, check_close(b["y"].cpu().numpy(), ref))
     layer.close()
+
+
+@pytest.mark.parametrize("E,k,M", [
+    (256, 32, 4),   # k' = 32 lane groups: most tokens have more than 64 keys above the threshold (all-keys count)
+    (256, 2, 4),    # four keys per lane, few candidates
+    (64, 16, 3),    # one key per lane
+    (8, 8, 2),      # k = E: every key selected, lanes past E hold no expert
+    (1024, 4, 1),   # E > 256: the count of every key
+])
+def test_router_threshold_and_count_paths(mb, E, k, M):
+    """The router's top-k (one wave per token from the keys above a
+    threshold, or every key counted) and the one-wave alignment: ids exact
+    for the kernel's own fp32 logits, affinities and plan as the oracle's."""
+    import torch
+    wl = synth.small_workload("router_%d_%d_%d" % (E, k, M), H=512, I=1, E=E, k=k, M=M, seed=E + k + M)
+    say("router paths", dict(E=E, k=k, M=M))
+    inp = synth.layer_inputs(wl, 0, experts=[])
+    inp["h"] = synth.hidden(wl, 0, 0, M=M)
+    inp["w_gate"] = inp["w_up"] = inp["w_down"] = np.zeros((E, 1, wl.H), np.uint16)
+    layer = mb.Layer(mb.make_config(wl.H, 1, E, k, wl.block_b, M), upload_layer(inp))
+    h = to_dev(inp["h"])
+    for call in ("route", "route_align"):
+        for t in (layer.ids, layer.w, layer.logits, layer.sorted_routes, layer.block_expert, layer.counts):
+            t.fill_(-3)
+        if call == "route":
+            layer.route(h, M, logits=True)
+            layer.align(M)
+        else:
+            layer.route_align(h, M, logits=True)
+        torch.cuda.synchronize()
+        cnt = layer.counts.cpu().numpy()
+        g = {"ids": layer.ids[:M].cpu().numpy().astype(np.int64), "w": layer.w[:M].cpu().numpy(),
+             "logits": layer.logits[:M].cpu().numpy(), "num_blocks": int(cnt[0]), "num_padded": int(cnt[1]),
+             "sorted_routes": layer.sorted_routes[: cnt[1]].cpu().numpy().astype(np.int64),
+             "block_expert": layer.block_expert[: cnt[0]].cpu().numpy().astype(np.int64)}
+        check_router(g, inp, k, wl.H)
+        check_plan(g, E, wl.block_b)
+    assert mb.moe_read_device_error(layer.ctx) == 0
+    layer.close()
