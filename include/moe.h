@@ -236,8 +236,11 @@ moe_status moe_expert_forward(moe_ctx *ctx, const float *h, int32_t M,
  * launches with no hand-off between workgroups: the router GEMV writes its
  * row-slice partials; every workgroup of the fused expert kernel adds them,
  * takes the top-k and softmax and finds its own expert (one block per
- * selected expert); the combine adds the partials.  Otherwise the calls above
- * are made as they are.
+ * selected expert); the combine adds the partials.  In channel-sparse mode
+ * (keep_channels > 0) the router GEMV writes the partials of all M tokens
+ * and each workgroup of the channel selection (one per token) takes its
+ * token's top-k and softmax before selecting.  Otherwise the calls above are
+ * made as they are.
  *  h, y: fp32 [M][H]; topk_ids, topk_w: [M][k] out; logits_out: [M][E] out
  *  or NULL; sorted_routes, block_expert, counts: as moe_align_blocks.
  */
@@ -303,7 +306,7 @@ enum {
     MOE_KERNEL_CHAN_COMBINE = 9,
     MOE_KERNEL_EXPERT_FUSED = 10, /* dense gate/up + SiLU + down partials (one route per block) */
     MOE_KERNEL_ROUTER_ALIGN = 11, /* router + top-k + softmax + alignment (one launch) */
-    MOE_KERNEL_ROUTER_GEMV = 12,  /* router GEMV slice partials only (batch-1 decode step) */
+    MOE_KERNEL_ROUTER_GEMV = 12,  /* router GEMV slice partials only (decode step) */
     MOE_KERNEL_DECODE_FUSED = 13, /* per-workgroup top-k + softmax + plan, then as EXPERT_FUSED */
     MOE_KERNEL_COUNT = 14
 };

@@ -10,6 +10,7 @@
 // the score; ties at the threshold go to the lower expert id, then channel.
 #include "device_common.h"
 #include "launch.h"
+#include "topk_device.h"
 
 namespace moe {
 
@@ -18,8 +19,8 @@ namespace {
 constexpr int kThreads = 256;
 constexpr int kWaves = kThreads / MOE_WAVE;
 
-// Order-preserving map of a double to uint64 (larger double -> larger key).
-__device__ __forceinline__ unsigned long long order_key(double x) {
+// Order-preserving map of a double score to uint64 (larger score -> larger key).
+__device__ __forceinline__ unsigned long long score_key(double x) {
     const unsigned long long u = (unsigned long long)__double_as_longlong(x);
     return (u >> 63) ? ~u : (u | 0x8000000000000000ull);
 }
@@ -83,10 +84,17 @@ __device__ __forceinline__ void wave_hist_add(int* hist, bool act, int d) {
 constexpr int kSelThreads = 1024;
 constexpr int kSelPer = 8;
 
+//
+// ROUTE: the workgroup first routes its token from the router's slice
+// partials -- the logits added in slice order (+ bias), the top-k (one wave
+// from the keys above a threshold, else every key counted) and the
+// renormalised softmax, with the router's arithmetic -- and writes the ids
+// and affinities (and logits) as the router would.
+template <bool ROUTE>
 __global__ void __launch_bounds__(kSelThreads)
 chan_select_kernel(const int32_t* __restrict__ topk_ids, const float* __restrict__ topk_w,
                    const float* __restrict__ norms, int k, int I, int E, int K, FastDiv fI,
-                   int32_t* __restrict__ kept) {
+                   int32_t* __restrict__ kept, SelRoute route) {
     extern __shared__ unsigned char lds[];
     const int n = k * I;
     unsigned char* tie = lds;            // [n], indexed in (expert, channel) order
@@ -105,10 +113,58 @@ chan_select_kernel(const int32_t* __restrict__ topk_ids, const float* __restrict
     const int per = (n + kSelThreads - 1) / kSelThreads;  // <= kSelPer (n <= 8192)
     const int i0 = tid * per;
 
-    if (tid < k) {
-        const int e = topk_ids[(size_t)t * k + tid];
-        se[tid] = (e >= 0 && e < E) ? e : -1;
-        sa[tid] = (double)topk_w[(size_t)t * k + tid];
+    if constexpr (ROUTE) {
+        // keys in the histogram's LDS (not used before the radix passes)
+        uint64_t* skey = reinterpret_cast<uint64_t*>(&hist[0][0][0]);
+        __shared__ int sel_e[32];
+        __shared__ float sel_l[32];
+        __shared__ uint64_t wk[MOE_WAVE];
+        __shared__ int wi[MOE_WAVE];
+        __shared__ int s_slow;
+        float lg = 0.f;
+        if (tid < E) {
+            const float bv = route.bias ? route.bias[tid] : 0.f;
+            for (int sl0 = 0; sl0 < route.nslices; sl0 += 8) {  // eight slices in flight
+                float x[8];
+#pragma unroll
+                for (int u = 0; u < 8; ++u)
+                    x[u] = route.part[((size_t)min(sl0 + u, route.nslices - 1) * route.M + t) * E + tid];
+#pragma unroll
+                for (int u = 0; u < 8; ++u) lg += sl0 + u < route.nslices ? x[u] : 0.f;  // slice order
+            }
+            if (route.bias) lg += bv;
+            if (route.logits) route.logits[(size_t)t * E + tid] = lg;
+            skey[tid] = order_key((lg != lg) ? -INFINITY : lg, tid);  // NaN ranks as -inf
+        }
+        if (tid == 0) s_slow = E > 4 * MOE_WAVE;
+        __syncthreads();
+        if (tid < MOE_WAVE && E <= 4 * MOE_WAVE && !wave_topk<4>(skey, E, k, sel_e, sel_l, wk, wi)) s_slow = 1;
+        __syncthreads();
+        if (s_slow) {  // every key counted (E <= 1024 threads)
+            if (tid < E) {
+                const int rank = count_greater(skey, 0, E, skey[tid]);
+                if (rank < k) {
+                    sel_e[rank] = tid;
+                    sel_l[rank] = key_logit(skey[tid]);
+                }
+            }
+            __syncthreads();
+        }
+        if (tid < MOE_WAVE) {  // lane s: slot s
+            const float w = topk_softmax(sel_l[min(tid, k - 1)], tid, k);
+            if (tid < k) {
+                route.ids[(size_t)t * k + tid] = sel_e[tid];
+                route.wts[(size_t)t * k + tid] = w;
+                se[tid] = sel_e[tid];
+                sa[tid] = (double)w;
+            }
+        }
+    } else {
+        if (tid < k) {
+            const int e = topk_ids[(size_t)t * k + tid];
+            se[tid] = (e >= 0 && e < E) ? e : -1;
+            sa[tid] = (double)topk_w[(size_t)t * k + tid];
+        }
     }
     __syncthreads();
     if (tid < k) {  // slots ordered by expert id (ids of one token are distinct; invalid slots last)
@@ -136,7 +192,7 @@ chan_select_kernel(const int32_t* __restrict__ topk_ids, const float* __restrict
     for (int u = 0; u < kSelPer; ++u) {
         const int idx = min(i0 + u, n - 1);
         const int sl = fI.div(idx), j = idx - sl * I;
-        key[u] = se[sl] < 0 ? 0ull : order_key(sa[sl] * (double)nv[u]);
+        key[u] = se[sl] < 0 ? 0ull : score_key(sa[sl] * (double)nv[u]);
         tpos[u] = spos[sl] * I + j;
     }
 
@@ -488,8 +544,16 @@ size_t chan_select_lds_bytes(int n) { return (size_t)n; }
 hipError_t launch_chan_select(const int32_t* topk_ids, const float* topk_w, const float* norms, int M, int k, int I,
                               int E, int K, int32_t* kept, hipStream_t stream) {
     if (k * I > kSelThreads * kSelPer) return hipErrorInvalidValue;
-    MOE_LAUNCH(chan_select_kernel, dim3(M), dim3(kSelThreads), chan_select_lds_bytes(k * I), stream, topk_ids,
-                       topk_w, norms, k, I, E, K, FastDiv((uint32_t)I), kept);
+    MOE_LAUNCH(chan_select_kernel<false>, dim3(M), dim3(kSelThreads), chan_select_lds_bytes(k * I), stream, topk_ids,
+               topk_w, norms, k, I, E, K, FastDiv((uint32_t)I), kept, SelRoute{});
+    return hipGetLastError();
+}
+
+hipError_t launch_chan_select_routed(const SelRoute& route, const float* norms, int M, int k, int I, int E, int K,
+                                     int32_t* kept, hipStream_t stream) {
+    if (k * I > kSelThreads * kSelPer || E > kSelThreads || k > 32 || route.M != M) return hipErrorInvalidValue;
+    MOE_LAUNCH(chan_select_kernel<true>, dim3(M), dim3(kSelThreads), chan_select_lds_bytes(k * I), stream, nullptr,
+               nullptr, norms, k, I, E, K, FastDiv((uint32_t)I), kept, route);
     return hipGetLastError();
 }
 

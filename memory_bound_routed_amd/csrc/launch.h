@@ -54,11 +54,12 @@ hipError_t launch_router_align(const float* h, int M, int H, const uint16_t* Wr,
                                int32_t* sorted_routes, int32_t* block_expert, int32_t* counts, int32_t* err,
                                hipStream_t stream);
 
-// Router GEMV of one token without the top-k: part fp32 [router_slices(H, E)][E]
-// (row-slice partials; logit e = 0 + part[0][e] + part[1][e] + ... in slice
-// order, then + bias[e]).
+// Router GEMV without the top-k: part fp32 [router_slices(H, E)][M][E]
+// (row-slice partials; logit of (t, e) = 0 + part[0][t][e] + part[1][t][e]
+// + ... in slice order, then + bias[e]).
 int router_slices(int H, int E);
-hipError_t launch_router_partials(const float* h, int H, const uint16_t* Wr, int E, float* part, hipStream_t stream);
+hipError_t launch_router_partials(const float* h, int M, int H, const uint16_t* Wr, int E, float* part,
+                                  hipStream_t stream);
 
 // ---- align.hip
 size_t align_lds_bytes(int R, int E);
@@ -133,6 +134,20 @@ hipError_t launch_gateup_vqlr(const PlanArgs& plan, const VqArgs& vq, const floa
 size_t chan_select_lds_bytes(int n);
 hipError_t launch_chan_select(const int32_t* topk_ids, const float* topk_w, const float* norms, int M, int k,
                               int I, int E, int K, int32_t* kept, hipStream_t stream);
+// The same selection, each workgroup first routing its token from the
+// router's slice partials (launch_router_partials) and writing ids,
+// affinities (and logits) as moe_route_topk would.
+struct SelRoute {
+    const float* part;   // fp32 [nslices][M][E] router slice partials
+    const float* bias;   // fp32 [E] or null
+    int nslices;
+    int M;
+    int32_t* ids;        // int32 [M][k] out
+    float* wts;          // fp32 [M][k] out
+    float* logits;       // fp32 [M][E] out, or null
+};
+hipError_t launch_chan_select_routed(const SelRoute& route, const float* norms, int M, int k, int I, int E, int K,
+                                     int32_t* kept, hipStream_t stream);
 hipError_t launch_chan_gather(const int32_t* topk_ids, const float* topk_w, const int32_t* kept, int M, int k,
                               int I, int E, int H, int K, int chunk, const float* h, const uint16_t* Wg,
                               const uint16_t* Wu, const uint16_t* Wd, float* part, hipStream_t stream);

@@ -135,6 +135,25 @@ struct Launch {
 
 moe_status hip_status(hipError_t e) { return e == hipSuccess ? MOE_OK : MOE_ERR_HIP; }
 
+// Channel-sparse mode after the selection: kept-channel gather, then combine.
+moe_status chan_gather_combine(moe_ctx* ctx, const float* h, int M, const int32_t* topk_ids, const float* topk_w,
+                               int K, const int32_t* kept, float* y, hipStream_t s) {
+    const moe_config& c = ctx->cfg;
+    const int nchunks = (K + kChanChunk - 1) / kChanChunk;
+    hipError_t e;
+    {
+        Launch l(ctx, MOE_KERNEL_CHAN_GATHER, s);
+        e = moe::launch_chan_gather(topk_ids, topk_w, kept, M, c.top_k, c.I, c.E, c.H, K, kChanChunk, h,
+                                    ctx->w.w_gate, ctx->w.w_up, ctx->w.w_down, ctx->chan_part, s);
+        l.done();
+        if (e != hipSuccess) return MOE_ERR_HIP;
+    }
+    Launch l(ctx, MOE_KERNEL_CHAN_COMBINE, s);
+    e = moe::launch_chan_combine(M, c.H, nchunks, ctx->chan_part, y, s);
+    l.done();
+    return hip_status(e);
+}
+
 }  // namespace
 
 extern "C" {
@@ -305,26 +324,15 @@ moe_status moe_expert_forward(moe_ctx* ctx, const float* h, int32_t M, const int
     if (keep_channels > 0) {
         if (c.max_keep == 0 || c.wformat != MOE_WFORMAT_DENSE) return MOE_ERR_UNSUPPORTED;
         if (keep_channels > c.max_keep) return MOE_ERR_CAPACITY;
-        const int K = keep_channels;
         int32_t* kept = kept_out ? kept_out : ctx->kept_ws;
         {
             Launch l(ctx, MOE_KERNEL_CHAN_SELECT, s);
-            e = moe::launch_chan_select(topk_ids, topk_w, ctx->w.chan_norm, M, c.top_k, c.I, c.E, K, kept, s);
+            e = moe::launch_chan_select(topk_ids, topk_w, ctx->w.chan_norm, M, c.top_k, c.I, c.E, keep_channels,
+                                        kept, s);
             l.done();
             if (e != hipSuccess) return MOE_ERR_HIP;
         }
-        const int nchunks = (K + kChanChunk - 1) / kChanChunk;
-        {
-            Launch l(ctx, MOE_KERNEL_CHAN_GATHER, s);
-            e = moe::launch_chan_gather(topk_ids, topk_w, kept, M, c.top_k, c.I, c.E, c.H, K, kChanChunk, h,
-                                        ctx->w.w_gate, ctx->w.w_up, ctx->w.w_down, ctx->chan_part, s);
-            l.done();
-            if (e != hipSuccess) return MOE_ERR_HIP;
-        }
-        Launch l(ctx, MOE_KERNEL_CHAN_COMBINE, s);
-        e = moe::launch_chan_combine(M, c.H, nchunks, ctx->chan_part, y, s);
-        l.done();
-        return hip_status(e);
+        return chan_gather_combine(ctx, h, M, topk_ids, topk_w, keep_channels, kept, y, s);
     }
 
     if (!sorted_routes || !block_expert || !counts) return MOE_ERR_INVALID_ARG;
@@ -398,12 +406,36 @@ moe_status moe_decode_step(moe_ctx* ctx, const float* h, int32_t M, int32_t* top
     const moe_config& c = ctx->cfg;
     if (M > c.max_tokens) return MOE_ERR_CAPACITY;
     if (keep_channels > 0) {
+        // router GEMV partials, then a channel selection whose workgroups
+        // route their tokens, then gather and combine
         if (c.max_keep == 0 || c.wformat != MOE_WFORMAT_DENSE) return MOE_ERR_UNSUPPORTED;
         if (keep_channels > c.max_keep) return MOE_ERR_CAPACITY;
-        moe_status st = moe_route_topk(ctx, h, M, topk_ids, topk_w, logits_out, stream);
-        if (st != MOE_OK) return st;
-        return moe_expert_forward(ctx, h, M, topk_ids, topk_w, nullptr, nullptr, nullptr, keep_channels, kept_out, y,
-                                  stream);
+        if (M == 0) return MOE_OK;
+        if (!h || !topk_ids || !topk_w || !y || !aligned(h, 16) || !aligned(y, 16)) return MOE_ERR_INVALID_ARG;
+        hipStream_t s = static_cast<hipStream_t>(stream);
+        hipError_t e;
+        {
+            Launch l(ctx, MOE_KERNEL_ROUTER_GEMV, s);
+            e = moe::launch_router_partials(h, M, c.H, ctx->w.router_w, c.E, ctx->router_part, s);
+            l.done();
+            if (e != hipSuccess) return MOE_ERR_HIP;
+        }
+        moe::SelRoute route{};
+        route.part = ctx->router_part;
+        route.bias = ctx->w.router_bias;
+        route.nslices = moe::router_slices(c.H, c.E);
+        route.M = M;
+        route.ids = topk_ids;
+        route.wts = topk_w;
+        route.logits = logits_out;
+        int32_t* kept = kept_out ? kept_out : ctx->kept_ws;
+        {
+            Launch l(ctx, MOE_KERNEL_CHAN_SELECT, s);
+            e = moe::launch_chan_select_routed(route, ctx->w.chan_norm, M, c.top_k, c.I, c.E, keep_channels, kept, s);
+            l.done();
+            if (e != hipSuccess) return MOE_ERR_HIP;
+        }
+        return chan_gather_combine(ctx, h, M, topk_ids, topk_w, keep_channels, kept, y, s);
     }
     const int nsl = moe::router_slices(c.H, c.E);
     if (M != 1 || c.wformat != MOE_WFORMAT_DENSE || !moe::decode_fused_ok(c.H, c.E, c.top_k, nsl)) {
@@ -420,7 +452,7 @@ moe_status moe_decode_step(moe_ctx* ctx, const float* h, int32_t M, int32_t* top
     hipError_t e;
     {
         Launch l(ctx, MOE_KERNEL_ROUTER_GEMV, s);
-        e = moe::launch_router_partials(h, c.H, ctx->w.router_w, c.E, ctx->router_part, s);
+        e = moe::launch_router_partials(h, 1, c.H, ctx->w.router_w, c.E, ctx->router_part, s);
         l.done();
         if (e != hipSuccess) return MOE_ERR_HIP;
     }

@@ -449,15 +449,19 @@ router_align_kernel(const float* __restrict__ h, int M, int H, const uint16_t* _
     rearm_ticket(ticket);
 }
 
-// Router GEMV only (one token): the tiles' slice partials part[slice][e],
-// stored for a later launch.  The expert kernel of the batch-1 decode step
-// adds them and takes the top-k itself.
+// Router GEMV only: the tiles' slice partials part[slice][t][e], stored for
+// a later launch, whose workgroups add them and take the top-k themselves
+// (the expert kernel of the batch-1 decode step, the channel selection).
 __global__ void __launch_bounds__(kThreads)
-router_partials_kernel(const float* __restrict__ h, int H, const uint16_t* __restrict__ Wr, int E,
+router_partials_kernel(const float* __restrict__ h, int M, int H, const uint16_t* __restrict__ Wr, int E,
                        float* __restrict__ part) {
     extern __shared__ __align__(16) float red[];
     const RouterTiles tl(H, E);
-    router_tile<1>(h, 1, 0, H, Wr, E, tl, blockIdx.x % tl.nrs, blockIdx.x / tl.nrs, part, red);
+    if (M == 1)
+        router_tile<1>(h, M, 0, H, Wr, E, tl, blockIdx.x % tl.nrs, blockIdx.x / tl.nrs, part, red);
+    else
+        router_tile<kTokTile>(h, M, blockIdx.y * kTokTile, H, Wr, E, tl, blockIdx.x % tl.nrs, blockIdx.x / tl.nrs,
+                              part, red);
 }
 
 size_t lds_bytes(int N) { return (size_t)(kThreads / (N / 8)) * kTokTile * N * sizeof(float); }
@@ -502,11 +506,13 @@ hipError_t launch_gemv_partials(const float* h, int M, int H, const GemvJob* job
 
 int router_slices(int H, int E) { return RouterTiles(H, E).nrs; }
 
-hipError_t launch_router_partials(const float* h, int H, const uint16_t* Wr, int E, float* part, hipStream_t stream) {
-    if (E % 8 != 0) return hipErrorInvalidValue;
+hipError_t launch_router_partials(const float* h, int M, int H, const uint16_t* Wr, int E, float* part,
+                                  hipStream_t stream) {
+    if (M < 1 || E % 8 != 0) return hipErrorInvalidValue;
     const RouterTiles tl(H, E);
-    const size_t lds = (size_t)tl.rpt * tl.cgw * sizeof(float);
-    MOE_LAUNCH(router_partials_kernel, dim3(router_grid(H, E)), dim3(kThreads), lds, stream, h, H, Wr, E, part);
+    const size_t lds = (size_t)tl.rpt * (M == 1 ? 1 : kTokTile) * tl.cgw * sizeof(float);
+    MOE_LAUNCH(router_partials_kernel, dim3(router_grid(H, E), router_groups(M)), dim3(kThreads), lds, stream, h, M,
+               H, Wr, E, part);
     return hipGetLastError();
 }
 

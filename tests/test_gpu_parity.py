@@ -703,3 +703,61 @@ def test_router_threshold_and_count_paths(mb, E, k, M):
         check_plan(g, E, wl.block_b)
     assert mb.moe_read_device_error(layer.ctx) == 0
     layer.close()
+
+
+@pytest.mark.parametrize("case", [
+    "full",      # the batch-1 channel-sparse workload: top 799 of 8 x 768 candidates
+    "m3",        # three tokens (one selection workgroup each, partials of a 4-token router group)
+    "e512",      # E > 256: the top-k counts every key
+])
+def test_decode_step_channel_sparse(mb, case):
+    """moe_decode_step with keep > 0 (router partials, then a selection whose
+    workgroups route their tokens) gives bit for bit the ids, affinities,
+    logits, kept list and y of moe_route_topk + moe_expert_forward, and the
+    oracle's selection and output."""
+    import torch
+    if case == "full":
+        wl = synth.WORKLOADS["chansparse_h2048_i768_e128_k8_m1_keep799"]
+        keep = wl.keep
+    elif case == "m3":
+        wl = synth.small_workload("cs_m3", H=512, I=40, E=64, k=4, M=3, seed=51)
+        keep = 50
+    else:
+        wl = synth.small_workload("cs_e512", H=256, I=24, E=512, k=6, M=2, seed=52, hot_experts=4)
+        keep = 31
+    M = wl.M
+    say("channel-sparse decode step vs separate calls:", case, dict(H=wl.H, I=wl.I, E=wl.E, k=wl.k, M=M, keep=keep))
+    inp = synth.layer_inputs(wl, 0)
+    dev = upload_layer(inp)
+    norms = torch.empty((wl.E, wl.I), dtype=torch.float32, device="cuda")
+    cfg = mb.make_config(wl.H, wl.I, wl.E, wl.k, wl.block_b, M, max_keep=keep)
+    mb.moe_channel_norms(cfg, dev["w_gate"], dev["w_up"], dev["w_down"], norms)
+    dev["chan_norm"] = norms
+    layer = mb.Layer(cfg, dev)
+    h_np = synth.hidden(wl, 0, 1, M=M)
+    h = to_dev(h_np)
+    outs = []
+    for one_call in (False, True):
+        for t in (layer.ids, layer.w, layer.logits, layer.kept, layer.y):
+            t.fill_(-3)
+        if one_call:
+            layer.decode_step(h, M, keep=keep, logits=True)
+        else:
+            layer.route(h, M, logits=True)
+            layer.forward(h, M, keep=keep)
+        torch.cuda.synchronize()
+        outs.append([layer.ids[:M].clone(), layer.w[:M].clone(), layer.logits[:M].clone(),
+                     layer.kept.view(-1)[: M * keep].clone(), layer.y[:M].clone()])
+    for a, b, what in zip(outs[0], outs[1], ("ids", "w", "logits", "kept", "y")):
+        assert torch.equal(a.view(torch.int32), b.view(torch.int32)), what
+    assert mb.moe_read_device_error(layer.ctx) == 0
+    g = {"ids": outs[1][0].cpu().numpy().astype(np.int64), "w": outs[1][1].cpu().numpy(),
+         "logits": outs[1][2].cpu().numpy()}
+    check_router(g, dict(inp, h=h_np), wl.k, wl.H)
+    kept = outs[1][3].view(M, keep).cpu().numpy().astype(np.int64)
+    kept_ref = O.channel_select(g["w"], g["ids"], norms.cpu().numpy(), keep)
+    np.testing.assert_array_equal(kept, kept_ref)
+    ref = O.channel_sparse_forward(h_np, g["ids"], g["w"].astype(np.float64), inp["w_gate"], inp["w_up"],
+                                   inp["w_down"], kept_ref)
+    say("  ", check_close(outs[1][4].cpu().numpy(), ref))
+    layer.close()
