@@ -183,8 +183,10 @@ def build_layers(wl, n_layers, M, keep=0):
             cfg = mb.make_config(wl.H, wl.I, wl.E, wl.k, wl.block_b, M, max_keep=keep)
         if keep:
             norms = torch.empty((wl.E, wl.I), dtype=torch.float32, device="cuda")
+            ranks = torch.empty((wl.E, wl.I), dtype=torch.int32, device="cuda")
             mb.moe_channel_norms(cfg, t["w_gate"], t["w_up"], t["w_down"], norms)
-            t["chan_norm"] = norms
+            mb.moe_channel_ranks(cfg, norms, ranks)
+            t["chan_norm"], t["chan_rank"] = norms, ranks
         layers.append(mb.Layer(cfg, t))
     torch.cuda.synchronize()
     return layers

@@ -108,6 +108,12 @@ typedef struct {
  *               Stage 2)                        required
  *  chan_norm    fp32 [E][I], static channel scores n[e][j] for the
  *               channel-sparse mode (see moe_channel_norms); or NULL
+ *  chan_rank    int32 [E][I], each channel's position in its expert's
+ *               channels ordered by decreasing chan_norm, ties to the lower
+ *               channel (see moe_channel_ranks); required with chan_norm in
+ *               the channel-sparse mode, else may be NULL.  It only speeds up
+ *               the selection: ranks that do not match the norms (or
+ *               affinities that are not positive) still give the exact top K.
  *  For MOE_WFORMAT_VQLR, index [0] is the gate projection and [1] the up
  *  projection (page "A Multi-Engine Dataflow ...", Sec. 3.1 Eq. 1 and Sec. 2.3):
  *  lr_basis[P]  bf16 [H][lr_r]   shared basis D_P
@@ -125,6 +131,7 @@ typedef struct {
     const uint16_t *w_up;
     const uint16_t *w_down;
     const float *chan_norm;
+    const int32_t *chan_rank;
     const uint16_t *lr_basis[2];
     const uint16_t *lr_coef[2];
     const uint16_t *vq_book[2];
@@ -205,7 +212,7 @@ moe_status moe_route_align(moe_ctx *ctx, const float *h, int32_t M, int32_t *top
  * bitwise the same y.  A plan that omits a valid route leaves that route's
  * contribution undefined.
  *
- * Channel-sparse mode (keep_channels = K > 0; needs chan_norm, dense format):
+ * Channel-sparse mode (keep_channels = K > 0; needs chan_norm and chan_rank, dense format):
  * page "Channel Selection for Mixture-of-Experts Decoding Needs No
  * Calibration Data", Background and Stage 2.  Per token, candidate (s, j)
  * scores a_s * n[e_s][j] (exact fp64 product of two fp32 values); the K best
@@ -272,6 +279,21 @@ moe_status moe_read_device_error(moe_ctx *ctx, int32_t *flags, int32_t clear);
  */
 moe_status moe_channel_norms(const moe_config *cfg, const uint16_t *w_gate, const uint16_t *w_up,
                              const uint16_t *w_down, float *norms, void *stream);
+
+/*
+ * Load-time list positions for the channel-sparse selection:
+ *     ranks[e][j] = #{ j2 : norms[e][j2] > norms[e][j]
+ *                          or (norms[e][j2] == norms[e][j] and j2 < j) }
+ * (values compared in float order, -0 equal to +0), i.e. channel j's position
+ * when expert e's channels are ordered by decreasing norm.  With positive
+ * affinities the top K of the affinity-weighted scores
+ * (page "Channel Selection for Mixture-of-Experts Decoding Needs No
+ * Calibration Data", Stage 2) is then a prefix of each routed expert's
+ * order, which the selection searches instead of sorting.  Inputs fp32
+ * [E][I] (device), output int32 [E][I] (device).  Needs only cfg->I
+ * (1..8192) and cfg->E.  Asynchronous on `stream`.
+ */
+moe_status moe_channel_ranks(const moe_config *cfg, const float *norms, int32_t *ranks, void *stream);
 
 /*
  * Host-side check of an alignment plan against its routes (all host

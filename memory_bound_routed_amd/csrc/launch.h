@@ -132,8 +132,12 @@ hipError_t launch_gateup_vqlr(const PlanArgs& plan, const VqArgs& vq, const floa
 
 // ---- chansparse.hip
 size_t chan_select_lds_bytes(int n);
-hipError_t launch_chan_select(const int32_t* topk_ids, const float* topk_w, const float* norms, int M, int k,
-                              int I, int E, int K, int32_t* kept, hipStream_t stream);
+// Channel top-K per token, one workgroup per (slot, token): per slot the
+// kept channels in ascending order, slot_kept int32 [M][k][I], and their
+// number, slot_cnt int32 [M][k] (summing to K per token).
+hipError_t launch_chan_select(const int32_t* topk_ids, const float* topk_w, const float* norms, const int32_t* ranks,
+                              int M, int k, int I, int E, int K, int32_t* slot_cnt, int32_t* slot_kept,
+                              hipStream_t stream);
 // The same selection, each workgroup first routing its token from the
 // router's slice partials (launch_router_partials) and writing ids,
 // affinities (and logits) as moe_route_topk would.
@@ -146,12 +150,15 @@ struct SelRoute {
     float* wts;          // fp32 [M][k] out
     float* logits;       // fp32 [M][E] out, or null
 };
-hipError_t launch_chan_select_routed(const SelRoute& route, const float* norms, int M, int k, int I, int E, int K,
-                                     int32_t* kept, hipStream_t stream);
-hipError_t launch_chan_gather(const int32_t* topk_ids, const float* topk_w, const int32_t* kept, int M, int k,
-                              int I, int E, int H, int K, int chunk, const float* h, const uint16_t* Wg,
-                              const uint16_t* Wu, const uint16_t* Wd, float* part, hipStream_t stream);
+hipError_t launch_chan_select_routed(const SelRoute& route, const float* norms, const int32_t* ranks, int M, int k,
+                                     int I, int E, int K, int32_t* slot_cnt, int32_t* slot_kept, hipStream_t stream);
+// kept_out (nullable): int32 [M][K], the kept set as s * I + j ascending.
+hipError_t launch_chan_gather(const int32_t* topk_ids, const float* topk_w, const int32_t* slot_cnt,
+                              const int32_t* slot_kept, int32_t* kept_out, int M, int k, int I, int E, int H, int K,
+                              int chunk, const float* h, const uint16_t* Wg, const uint16_t* Wu, const uint16_t* Wd,
+                              float* part, hipStream_t stream);
 hipError_t launch_chan_combine(int M, int H, int nchunks, const float* part, float* y, hipStream_t stream);
+hipError_t launch_channel_ranks(int E, int I, const float* norms, int32_t* ranks, hipStream_t stream);
 hipError_t launch_channel_norms(int E, int I, int H, const uint16_t* Wg, const uint16_t* Wu, const uint16_t* Wd,
                                 float* norms, hipStream_t stream);
 

@@ -34,7 +34,8 @@ struct moe_ctx {
     float* zpart[2] = {nullptr, nullptr};
     float* p = nullptr;
     float* down_part = nullptr;
-    int32_t* kept_ws = nullptr;
+    int32_t* slot_cnt = nullptr;   // channel-sparse: kept channels per (token, slot), int32 [MT][k]
+    int32_t* slot_kept = nullptr;  // ... and their channels, int32 [MT][k][I]
     float* chan_part = nullptr;
     bool prof = false;
     std::vector<Rec> recs;
@@ -96,7 +97,8 @@ moe_status check_weights(const moe_config* c, const moe_weights* w) {
                 return MOE_ERR_INVALID_ARG;
         }
     }
-    if (c->max_keep > 0 && (!w->chan_norm || !aligned(w->chan_norm, 4))) return MOE_ERR_INVALID_ARG;
+    if (c->max_keep > 0 && (!w->chan_norm || !aligned(w->chan_norm, 4) || !w->chan_rank || !aligned(w->chan_rank, 4)))
+        return MOE_ERR_INVALID_ARG;
     return MOE_OK;
 }
 
@@ -137,14 +139,15 @@ moe_status hip_status(hipError_t e) { return e == hipSuccess ? MOE_OK : MOE_ERR_
 
 // Channel-sparse mode after the selection: kept-channel gather, then combine.
 moe_status chan_gather_combine(moe_ctx* ctx, const float* h, int M, const int32_t* topk_ids, const float* topk_w,
-                               int K, const int32_t* kept, float* y, hipStream_t s) {
+                               int K, int32_t* kept_out, float* y, hipStream_t s) {
     const moe_config& c = ctx->cfg;
     const int nchunks = (K + kChanChunk - 1) / kChanChunk;
     hipError_t e;
     {
         Launch l(ctx, MOE_KERNEL_CHAN_GATHER, s);
-        e = moe::launch_chan_gather(topk_ids, topk_w, kept, M, c.top_k, c.I, c.E, c.H, K, kChanChunk, h,
-                                    ctx->w.w_gate, ctx->w.w_up, ctx->w.w_down, ctx->chan_part, s);
+        e = moe::launch_chan_gather(topk_ids, topk_w, ctx->slot_cnt, ctx->slot_kept, kept_out, M, c.top_k, c.I, c.E,
+                                    c.H, K, kChanChunk, h, ctx->w.w_gate, ctx->w.w_up, ctx->w.w_down,
+                                    ctx->chan_part, s);
         l.done();
         if (e != hipSuccess) return MOE_ERR_HIP;
     }
@@ -217,7 +220,7 @@ moe_status moe_create(const moe_config* cfg, const moe_weights* w, moe_ctx** out
         sizeof(float) * zsl * MT * c.lr_r,                              // z partials (up)
         sizeof(float) * R * c.I,                                        // p
         sizeof(float) * R * nchunk * c.H,                               // down partials
-        sizeof(int32_t) * MT * c.max_keep,                              // kept list
+        c.max_keep > 0 ? sizeof(int32_t) * MT * c.top_k * (1 + (size_t)c.I) : 0,  // per-slot kept lists
         sizeof(float) * MT * nchan * c.H,                               // channel partials
     };
     size_t off[8], total = 0;
@@ -238,7 +241,8 @@ moe_status moe_create(const moe_config* cfg, const moe_weights* w, moe_ctx** out
     ctx->zpart[1] = reinterpret_cast<float*>(base + off[3]);
     ctx->p = reinterpret_cast<float*>(base + off[4]);
     ctx->down_part = reinterpret_cast<float*>(base + off[5]);
-    ctx->kept_ws = reinterpret_cast<int32_t*>(base + off[6]);
+    ctx->slot_cnt = reinterpret_cast<int32_t*>(base + off[6]);
+    ctx->slot_kept = ctx->slot_cnt + MT * c.top_k;
     ctx->chan_part = reinterpret_cast<float*>(base + off[7]);
     if (hipMemset(ctx->err, 0, sizes[0]) != hipSuccess || hipDeviceSynchronize() != hipSuccess) {
         hipFree(ctx->ws);
@@ -324,15 +328,14 @@ moe_status moe_expert_forward(moe_ctx* ctx, const float* h, int32_t M, const int
     if (keep_channels > 0) {
         if (c.max_keep == 0 || c.wformat != MOE_WFORMAT_DENSE) return MOE_ERR_UNSUPPORTED;
         if (keep_channels > c.max_keep) return MOE_ERR_CAPACITY;
-        int32_t* kept = kept_out ? kept_out : ctx->kept_ws;
         {
             Launch l(ctx, MOE_KERNEL_CHAN_SELECT, s);
-            e = moe::launch_chan_select(topk_ids, topk_w, ctx->w.chan_norm, M, c.top_k, c.I, c.E, keep_channels,
-                                        kept, s);
+            e = moe::launch_chan_select(topk_ids, topk_w, ctx->w.chan_norm, ctx->w.chan_rank, M, c.top_k, c.I, c.E,
+                                        keep_channels, ctx->slot_cnt, ctx->slot_kept, s);
             l.done();
             if (e != hipSuccess) return MOE_ERR_HIP;
         }
-        return chan_gather_combine(ctx, h, M, topk_ids, topk_w, keep_channels, kept, y, s);
+        return chan_gather_combine(ctx, h, M, topk_ids, topk_w, keep_channels, kept_out, y, s);
     }
 
     if (!sorted_routes || !block_expert || !counts) return MOE_ERR_INVALID_ARG;
@@ -428,14 +431,14 @@ moe_status moe_decode_step(moe_ctx* ctx, const float* h, int32_t M, int32_t* top
         route.ids = topk_ids;
         route.wts = topk_w;
         route.logits = logits_out;
-        int32_t* kept = kept_out ? kept_out : ctx->kept_ws;
         {
             Launch l(ctx, MOE_KERNEL_CHAN_SELECT, s);
-            e = moe::launch_chan_select_routed(route, ctx->w.chan_norm, M, c.top_k, c.I, c.E, keep_channels, kept, s);
+            e = moe::launch_chan_select_routed(route, ctx->w.chan_norm, ctx->w.chan_rank, M, c.top_k, c.I, c.E,
+                                               keep_channels, ctx->slot_cnt, ctx->slot_kept, s);
             l.done();
             if (e != hipSuccess) return MOE_ERR_HIP;
         }
-        return chan_gather_combine(ctx, h, M, topk_ids, topk_w, keep_channels, kept, y, s);
+        return chan_gather_combine(ctx, h, M, topk_ids, topk_w, keep_channels, kept_out, y, s);
     }
     const int nsl = moe::router_slices(c.H, c.E);
     if (M != 1 || c.wformat != MOE_WFORMAT_DENSE || !moe::decode_fused_ok(c.H, c.E, c.top_k, nsl)) {
@@ -505,6 +508,14 @@ moe_status moe_channel_norms(const moe_config* cfg, const uint16_t* w_gate, cons
         return MOE_ERR_INVALID_ARG;
     return hip_status(moe::launch_channel_norms(cfg->E, cfg->I, cfg->H, w_gate, w_up, w_down, norms,
                                                 static_cast<hipStream_t>(stream)));
+}
+
+moe_status moe_channel_ranks(const moe_config* cfg, const float* norms, int32_t* ranks, void* stream) {
+    if (!cfg || !norms || !ranks) return MOE_ERR_INVALID_ARG;
+    if (cfg->I <= 0 || cfg->E <= 0) return MOE_ERR_INVALID_ARG;
+    if (cfg->I > 8192 || (int64_t)cfg->E * cfg->I > INT32_MAX) return MOE_ERR_UNSUPPORTED;
+    if (!aligned(norms, 4) || !aligned(ranks, 4)) return MOE_ERR_INVALID_ARG;
+    return hip_status(moe::launch_channel_ranks(cfg->E, cfg->I, norms, ranks, static_cast<hipStream_t>(stream)));
 }
 
 moe_status moe_validate_plan(const int32_t* ids, int32_t M, int32_t k, int32_t E, int32_t b, const int32_t* rows,

@@ -93,6 +93,7 @@ def test_create_rejects_missing_or_misaligned_weights(mb):
     assert mb.moe_create_status(vq, mb.make_weights(FAKE, FAKE, **bad))[0] == 1
     keep = base_cfg(mb, max_keep=799)
     assert mb.moe_create_status(keep, mb.make_weights(FAKE, FAKE, w_gate=FAKE, w_up=FAKE))[0] == 1  # no norms
+    assert mb.moe_create_status(keep, mb.make_weights(FAKE, FAKE, w_gate=FAKE, w_up=FAKE, chan_norm=FAKE))[0] == 1
     assert mb.moe_create_status(None, mb.make_weights(FAKE, FAKE))[0] == 1
 
 
@@ -109,6 +110,10 @@ def test_calls_on_null_context_fail_closed(mb):
     assert lib.moe_channel_norms(ctypes.byref(cfg), None, FAKE, FAKE, FAKE, None) == 1
     bad = base_cfg(mb, H=2044)
     assert lib.moe_channel_norms(ctypes.byref(bad), FAKE, FAKE, FAKE, FAKE, None) == 2
+    assert lib.moe_channel_ranks(ctypes.byref(cfg), None, FAKE, None) == 1
+    assert lib.moe_channel_ranks(ctypes.byref(cfg), FAKE, None, None) == 1
+    assert lib.moe_channel_ranks(None, FAKE, FAKE, None) == 1
+    assert lib.moe_channel_ranks(ctypes.byref(base_cfg(mb, I=8193)), FAKE, FAKE, None) == 2
 
 
 # ---------------------------------------------------------------- plan validator

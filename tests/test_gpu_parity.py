@@ -37,10 +37,20 @@ def say(*a):
     print(*a, flush=True)
 
 
-def make_layer(mb, wl, inp, max_tokens, norms_dev=None, max_keep=0):
+def channel_tables(mb, cfg, dev):
+    """Load-time tables of the channel-sparse mode, computed on the device:
+    the static channel norms and each channel's rank in its expert."""
+    import torch
+    norms = torch.empty((cfg.E, cfg.I), dtype=torch.float32, device="cuda")
+    ranks = torch.empty((cfg.E, cfg.I), dtype=torch.int32, device="cuda")
+    mb.moe_channel_norms(cfg, dev["w_gate"], dev["w_up"], dev["w_down"], norms)
+    mb.moe_channel_ranks(cfg, norms, ranks)
+    dev["chan_norm"], dev["chan_rank"] = norms, ranks
+    return norms
+
+
+def make_layer(mb, wl, inp, max_tokens, max_keep=0):
     dev = upload_layer(inp)
-    if norms_dev is not None:
-        dev["chan_norm"] = norms_dev
     if wl.vq:
         cfg = mb.make_config(wl.H, wl.I, wl.E, wl.k, wl.block_b, max_tokens, mb.MOE_WFORMAT_VQLR, wl.vq_d, wl.vq_K,
                              wl.lr_r, max_keep)
@@ -208,16 +218,15 @@ def test_chansparse_keep799(mb):
     say("chansparse_h2048_i768_e128_k8_m1_keep799 layer 0 (full size)")
     inp = synth.layer_inputs(wl, 0)
     dev = upload_layer(inp)
-    norms = torch.empty((wl.E, wl.I), dtype=torch.float32, device="cuda")
     cfg = mb.make_config(wl.H, wl.I, wl.E, wl.k, wl.block_b, 1, max_keep=wl.keep)
-    mb.moe_channel_norms(cfg, dev["w_gate"], dev["w_up"], dev["w_down"], norms)
+    norms = channel_tables(mb, cfg, dev)
     torch.cuda.synchronize()
     gn = norms.cpu().numpy()
     ref_n = O.channel_norms(inp["w_gate"], inp["w_up"], inp["w_down"], experts=range(0, wl.E, 9))
     sel = list(range(0, wl.E, 9))
     ulp = np.abs(gn[sel].view(np.int32).astype(np.int64) - ref_n[sel].view(np.int32).astype(np.int64))
     assert ulp.max() <= 1, "norms differ by %d ulp" % ulp.max()
-    dev["chan_norm"] = norms
+    np.testing.assert_array_equal(dev["chan_rank"].cpu().numpy(), ref_ranks(gn))
     layer = mb.Layer(cfg, dev)
     for step in range(2):
         h = synth.hidden(wl, 0, step)
@@ -234,16 +243,103 @@ def test_chansparse_keep799(mb):
     layer.close()
 
 
+def ref_ranks(norms: np.ndarray) -> np.ndarray:
+    """Each channel's position when its expert's channels are ordered by
+    decreasing norm, ties to the lower channel (test-side reference)."""
+    E, I = norms.shape
+    out = np.empty((E, I), np.int64)
+    for e in range(E):
+        order = np.lexsort((np.arange(I), -norms[e].astype(np.float64)))
+        out[e, order] = np.arange(I)
+    return out
+
+
+def test_channel_ranks_and_exact_selection(mb):
+    """moe_channel_ranks against a reference ordering; the selection against the
+    oracle's top K with correct ranks, with ranks that do not match the norms
+    (zeros, reversed, a random permutation, out of range), with caller
+    affinities that are zero, negative or equal, with tied norms and with one
+    expert in two slots."""
+    import torch
+    wl = synth.small_workload("cs_ranks", H=256, I=96, E=16, k=4, M=3, seed=61)
+    M, I, k = wl.M, wl.I, wl.k
+    inp = synth.layer_inputs(wl, 0)
+    h_np = synth.hidden(wl, 0, 0, M=M)
+    h = to_dev(h_np)
+    dev = upload_layer(inp)
+    cfg = mb.make_config(wl.H, I, wl.E, k, 8, M, max_keep=k * I)
+    norms = channel_tables(mb, cfg, dev)
+    torch.cuda.synchronize()
+    np.testing.assert_array_equal(dev["chan_rank"].cpu().numpy(), ref_ranks(norms.cpu().numpy()))
+    layer = mb.Layer(cfg, dev)
+    layer.route(h, M)
+    torch.cuda.synchronize()
+    ids = layer.ids[:M].cpu().numpy().astype(np.int64)
+    w = layer.w[:M].cpu().numpy()
+
+    def select(keep, ids_np=ids, w_np=w):
+        layer.kept.fill_(-5)
+        layer.forward(h, M, keep=keep, ids=to_dev(ids_np.astype(np.int32)), w=to_dev(w_np.astype(np.float32)))
+        torch.cuda.synchronize()
+        assert mb.moe_read_device_error(layer.ctx) == 0
+        got = layer.kept.view(-1)[: M * keep].view(M, keep).cpu().numpy().astype(np.int64)
+        ref = O.channel_select(w_np, ids_np, norms.cpu().numpy(), keep)
+        np.testing.assert_array_equal(got, ref)
+        return got
+
+    for keep in (1, 37, 200, k * I):
+        select(keep)
+    kept = select(150)
+    ref_y = O.channel_sparse_forward(h_np, ids, w.astype(np.float64), inp["w_gate"], inp["w_up"], inp["w_down"], kept)
+    say("  keep 150:", check_close(layer.y[:M].cpu().numpy(), ref_y))
+
+    good = dev["chan_rank"].clone()
+    rng = np.random.default_rng(5)
+    for what, bad in (("zeros", torch.zeros_like(good)), ("reversed", I - 1 - good),
+                      ("random permutation", torch.from_numpy(np.stack([rng.permutation(I) for _ in range(wl.E)])
+                                                              .astype(np.int32)).cuda()),
+                      ("out of range", torch.where(good % 3 == 0, good + 5000, good - 7))):
+        say("  ranks:", what)
+        dev["chan_rank"].copy_(bad)
+        select(150)
+    dev["chan_rank"].copy_(good)
+
+    w2 = w.copy()
+    w2[0, 1] = 0.0
+    w2[1, 0] = -w2[1, 0]
+    w2[2, :] = 0.25
+    say("  caller affinities: zero, negative, equal")
+    select(150, w_np=w2)
+    select(k * I - 3, w_np=w2)
+
+    ids2 = ids.copy()
+    ids2[1, 2] = ids2[1, 0]
+    w3 = w.copy()
+    w3[1, 2] = w3[1, 0]
+    say("  one expert in two slots")
+    select(150, ids_np=ids2, w_np=w3)
+
+    say("  tied norms")
+    tied = norms.clone()
+    tied[int(ids[0, 0])] = 0.5
+    tied[int(ids[0, 1]), 1::2] = tied[int(ids[0, 1]), 0::2]
+    norms.copy_(tied)
+    mb.moe_channel_ranks(cfg, norms, dev["chan_rank"])
+    torch.cuda.synchronize()
+    np.testing.assert_array_equal(dev["chan_rank"].cpu().numpy(), ref_ranks(norms.cpu().numpy()))
+    for keep in (60, 150, 300):
+        select(keep)
+    layer.close()
+
+
 def test_chansparse_all_channels_equals_dense(mb):
     import torch
     wl = synth.small_workload("sparse_all", H=264, I=40, E=16, k=3, M=2, seed=77)
     inp = synth.layer_inputs(wl, 0)
     inp["h"] = synth.hidden(wl, 0, 0, M=2)
     dev = upload_layer(inp)
-    norms = torch.empty((wl.E, wl.I), dtype=torch.float32, device="cuda")
     cfg = mb.make_config(wl.H, wl.I, wl.E, wl.k, 8, 2, max_keep=wl.k * wl.I)
-    mb.moe_channel_norms(cfg, dev["w_gate"], dev["w_up"], dev["w_down"], norms)
-    dev["chan_norm"] = norms
+    norms = channel_tables(mb, cfg, dev)
     layer = mb.Layer(cfg, dev)
     gs = run_step(mb, layer, inp["h"], keep=wl.k * wl.I)
     np.testing.assert_array_equal(gs["kept"], np.tile(np.arange(wl.k * wl.I), (2, 1)))
@@ -729,10 +825,8 @@ def test_decode_step_channel_sparse(mb, case):
     say("channel-sparse decode step vs separate calls:", case, dict(H=wl.H, I=wl.I, E=wl.E, k=wl.k, M=M, keep=keep))
     inp = synth.layer_inputs(wl, 0)
     dev = upload_layer(inp)
-    norms = torch.empty((wl.E, wl.I), dtype=torch.float32, device="cuda")
     cfg = mb.make_config(wl.H, wl.I, wl.E, wl.k, wl.block_b, M, max_keep=keep)
-    mb.moe_channel_norms(cfg, dev["w_gate"], dev["w_up"], dev["w_down"], norms)
-    dev["chan_norm"] = norms
+    norms = channel_tables(mb, cfg, dev)
     layer = mb.Layer(cfg, dev)
     h_np = synth.hidden(wl, 0, 1, M=M)
     h = to_dev(h_np)
