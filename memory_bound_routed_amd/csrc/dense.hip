@@ -112,7 +112,7 @@ expert_fused_kernel(PlanArgs plan, RouteArgs route, const float* __restrict__ h,
     constexpr int RG = NT / kThreads;     // down row groups (256 column threads each)
     constexpr int RPG = CH / RG;          // down rows per row group and chunk
     static_assert(NT % kThreads == 0 && CH % RG == 0, "tile");
-    __shared__ float sp[CH];
+    __shared__ float sp[2][CH];  // alternating per chunk: one barrier per chunk
     __shared__ float4 hs[Q * MOE_WAVE * 2];
     __shared__ float4 red[RG > 1 ? (RG - 1) * kThreads * CQ * 2 : 1];
     __shared__ __align__(16) uint64_t rkey[ROUTE ? kRouteMaxE : 2];
@@ -328,6 +328,7 @@ expert_fused_kernel(PlanArgs plan, RouteArgs route, const float* __restrict__ h,
 
     // Gate/up of one chunk from h in LDS: sp[c] = a * SiLU(g_j) * u_j.
     auto gateup = [&](int ci, int buf, float a) {
+        float* spc = sp[ci & 1];
         const int j0 = cbase + ci * CH;
         float ag[CPW], au[CPW];
 #pragma unroll
@@ -355,18 +356,19 @@ expert_fused_kernel(PlanArgs plan, RouteArgs route, const float* __restrict__ h,
             const float g = wave_sum(ag[c]);
             const float u = wave_sum(au[c]);
             const int j = j0 + wave * CPW + c;
-            if (lane == 0) sp[wave * CPW + c] = j < I ? a * silu_mul(g, u) : 0.f;
+            if (lane == 0) spc[wave * CPW + c] = j < I ? a * silu_mul(g, u) : 0.f;
         }
     };
     // Down rows of one chunk scaled by sp, accumulated per column thread.
-    auto down = [&](int buf, float (&acc)[CQ][8]) {
+    auto down = [&](int ci, int buf, float (&acc)[CQ][8]) {
+        const float* spc = sp[ci & 1];
 #pragma unroll
         for (int cq = 0; cq < CQ; ++cq)
 #pragma unroll
             for (int rr = 0; rr < RPG; ++rr) {
                 float wf[8];
                 unpack8(wd[buf][rr][cq], wf);
-                const float s = sp[rgp * RPG + rr];
+                const float s = spc[rgp * RPG + rr];
 #pragma unroll
                 for (int x = 0; x < 8; ++x) acc[cq][x] = fmaf(s, wf[x], acc[cq][x]);
             }
@@ -452,15 +454,16 @@ expert_fused_kernel(PlanArgs plan, RouteArgs route, const float* __restrict__ h,
             }
         }
         const float a = __int_as_float(__builtin_amdgcn_readfirstlane(__float_as_int(av)));
+        // sp alternates per chunk, so the barrier of chunk ci+1 already
+        // orders chunk ci's reads before chunk ci+2 overwrites them.
 #pragma unroll
         for (int ci = 0; ci < NCH; ++ci) {
             const int buf = ci & 1;
             gateup(ci, buf, a);
             if (ci + 2 < NCH) issue_gu(ci + 2, buf);
             __syncthreads();
-            down(buf, acc);
+            down(ci, buf, acc);
             if (ci + 2 < NCH) issue_d(ci + 2, buf);
-            __syncthreads();
         }
         finish(r0, acc);
     }
@@ -500,8 +503,7 @@ expert_fused_kernel(PlanArgs plan, RouteArgs route, const float* __restrict__ h,
             issue_d(ci, 0);
             gateup(ci, 0, a);
             __syncthreads();
-            down(0, acc);
-            __syncthreads();
+            down(ci, 0, acc);
         }
         finish(r, acc);
     }
