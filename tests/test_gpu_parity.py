@@ -332,6 +332,49 @@ def test_channel_ranks_and_exact_selection(mb):
     layer.close()
 
 
+@pytest.mark.parametrize("case", ["n8192_k8", "k1", "k32", "k3_i700"])
+def test_channel_selection_shapes(mb, case):
+    """The selection at its size limits: k * I = 8192 candidates (the largest
+    list LDS), one slot, 32 slots (rank sums over 32-lane groups) and a slot
+    count that is not a power of two (rank sums through LDS); kept lists
+    against the oracle's, y within tolerance, both entry points."""
+    import torch
+    shape = {"n8192_k8": dict(H=256, I=1024, E=16, k=8, M=2, keep=1100),
+             "k1": dict(H=264, I=200, E=8, k=1, M=3, keep=37),
+             "k32": dict(H=256, I=256, E=64, k=32, M=2, keep=2000),
+             "k3_i700": dict(H=512, I=700, E=24, k=3, M=2, keep=701)}[case]
+    keep = shape.pop("keep")
+    wl = synth.small_workload("cs_" + case, seed=71, **shape)
+    M = wl.M
+    say("channel selection shape", case, shape, "keep", keep)
+    inp = synth.layer_inputs(wl, 0)
+    h_np = synth.hidden(wl, 0, 0, M=M)
+    h = to_dev(h_np)
+    dev = upload_layer(inp)
+    cfg = mb.make_config(wl.H, wl.I, wl.E, wl.k, 8, M, max_keep=keep)
+    norms = channel_tables(mb, cfg, dev)
+    layer = mb.Layer(cfg, dev)
+    layer.decode_step(h, M, keep=keep, logits=True)
+    torch.cuda.synchronize()
+    assert mb.moe_read_device_error(layer.ctx) == 0
+    ids = layer.ids[:M].cpu().numpy().astype(np.int64)
+    w = layer.w[:M].cpu().numpy()
+    check_router({"ids": ids, "w": w, "logits": layer.logits[:M].cpu().numpy()}, dict(inp, h=h_np), wl.k, wl.H)
+    kept = layer.kept.view(-1)[: M * keep].view(M, keep).cpu().numpy().astype(np.int64)
+    ref_kept = O.channel_select(w, ids, norms.cpu().numpy(), keep)
+    np.testing.assert_array_equal(kept, ref_kept)
+    y1 = layer.y[:M].cpu().numpy()
+    ref = O.channel_sparse_forward(h_np, ids, w.astype(np.float64), inp["w_gate"], inp["w_up"], inp["w_down"], ref_kept)
+    say("  ", check_close(y1, ref))
+    # the separate selection entry point on the same routing: same kept list, same y bits
+    layer.kept.fill_(-5)
+    layer.forward(h, M, keep=keep)
+    torch.cuda.synchronize()
+    np.testing.assert_array_equal(layer.kept.view(-1)[: M * keep].view(M, keep).cpu().numpy(), ref_kept)
+    assert np.array_equal(layer.y[:M].cpu().numpy().view(np.int32), y1.view(np.int32))
+    layer.close()
+
+
 def test_chansparse_all_channels_equals_dense(mb):
     import torch
     wl = synth.small_workload("sparse_all", H=264, I=40, E=16, k=3, M=2, seed=77)
