@@ -34,7 +34,7 @@ the design notes):
     expert with no route, and skips route ids outside [0, E);
   * the channel-sparse score is the exact product of the fp32 affinity and a
     static fp32 channel norm ||g_j||*||v_j||*||d_j||, top-K across all routed
-    experts, ties broken by (expert id, channel) ascending;
+    experts, ties broken by (expert id, channel, slot) ascending;
   * VQ blocks run along the hidden dimension inside each channel's column of
     W_e (length d), and gate and up each have their own basis and code book.
 
@@ -343,6 +343,22 @@ def vqlr_forward(h, ids, aff, vq: Dict[str, np.ndarray], w_down) -> np.ndarray:
 # ----------------------------------------------------------------------------
 # One whole step
 # ----------------------------------------------------------------------------
+
+def vq_storage_bits_per_weight(d: int, r: int, K: int, H: int, I: int, E: int) -> float:
+    """Bits stored per original gate or up weight by the VQ + low-rank format
+    ([CARDAN] Sec. 5.4; the formula is lost in the page's text, so this is the
+    count of the format's own parts): an 8-bit code index per block of d
+    weights, an expert-private bf16 coefficient matrix C_e of I x r entries
+    over the I x H weights of one expert, and the layer-shared bf16 basis D
+    (H x r) and code book B (K x d) amortised over the E experts."""
+    return 8.0 / d + 16.0 * r / H + (16.0 * H * r + 16.0 * K * d) / (E * H * I)
+
+
+def vq_private_bytes_per_projection(d: int, r: int, H: int, I: int) -> int:
+    """Expert-private bytes of one projection: the uint8 index map J_e
+    (I x H/d) and the bf16 coefficients C_e (I x r)."""
+    return I * (H // d) + I * r * 2
+
 
 def moe_step(inp: Dict[str, np.ndarray], k: int, keep: int = 0, b: int = 8,
              aff_f32_for_selection: Optional[np.ndarray] = None,
