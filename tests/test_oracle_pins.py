@@ -542,6 +542,7 @@ def test_storage_rate_reading_reproduces_the_pages_rate_pairs():
     assert abs(q[0] - q[1]) <= g["match_within_bits"] + 1e-9
     private = {O.vq_private_bytes_per_projection(d, r, sh["H"], sh["I"]) for d, r in g["four_bit_pairs"]}
     assert len(private) == 1
+    import synth  # the workload table (sizes only)
     wl = synth.WORKLOADS["vqlr_h2048_i768_e128_k8_m4_d8_K256_r64"]
     assert wl.routed_bytes_per_expert == 2 * O.vq_private_bytes_per_projection(wl.vq_d, wl.lr_r, wl.H, wl.I) \
         + wl.I * wl.H * 2 == 3735552
