@@ -83,8 +83,9 @@ enum {
  *              workgroup's LDS).
  *  wformat     MOE_WFORMAT_DENSE or MOE_WFORMAT_VQLR.
  *  vq_d, vq_K, lr_r   VQ block length, code book size and low-rank rank for
- *              MOE_WFORMAT_VQLR: vq_d == 8, 1 <= vq_K <= 256, H % (8*vq_d)
- *              == 0, lr_r % 8 == 0 and 8 <= lr_r <= 512.  Ignored for dense.
+ *              MOE_WFORMAT_VQLR: vq_d in {2, 4, 8}, 1 <= vq_K <= 256,
+ *              H % (8*vq_d) == 0, H/vq_d <= 1024, lr_r % 8 == 0 and
+ *              8 <= lr_r <= 512.  Ignored for dense.
  *  max_keep    largest channel top-K moe_expert_forward will be asked for
  *              (0 = channel-sparse mode unused); <= top_k*I, top_k*I <= 8192,
  *              dense format only.
@@ -121,6 +122,8 @@ typedef struct {
  *  vq_book[P]   bf16 [vq_K][vq_d] shared weight code book B_P
  *  vq_idx[P]    uint8 [E][I][H/vq_d] private index map: entry [e][j][b] picks
  *               the code word of rows vq_d*b .. vq_d*b+vq_d-1 of channel j
+ *               (entries >= vq_K select a zero code word; nothing is read
+ *               past the code book)
  *  The reconstructed gate/up weight of channel j, row i is
  *      sum_rho D_P[i][rho] C_P,e[j][rho] + B_P[J_P,e[j][i / vq_d]][i % vq_d].
  */

@@ -72,7 +72,8 @@ moe_status check_config(const moe_config* c) {
     if (nchunk * c->E > 6144) return MOE_ERR_UNSUPPORTED;
     if (c->wformat != MOE_WFORMAT_DENSE && c->wformat != MOE_WFORMAT_VQLR) return MOE_ERR_UNSUPPORTED;
     if (c->wformat == MOE_WFORMAT_VQLR) {
-        if (c->vq_d != 8 || c->vq_K < 1 || c->vq_K > 256 || c->H % (8 * c->vq_d)) return MOE_ERR_UNSUPPORTED;
+        if (c->vq_d != 2 && c->vq_d != 4 && c->vq_d != 8) return MOE_ERR_UNSUPPORTED;
+        if (c->vq_K < 1 || c->vq_K > 256 || c->H % (8 * c->vq_d) || c->H / c->vq_d > 1024) return MOE_ERR_UNSUPPORTED;
         if (c->lr_r % 8 || c->lr_r < 8 || c->lr_r > 512) return MOE_ERR_UNSUPPORTED;
     }
     if (c->max_keep > 0) {

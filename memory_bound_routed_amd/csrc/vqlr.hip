@@ -25,8 +25,22 @@ namespace {
 constexpr int kThreads = 256;
 constexpr int kWaves = kThreads / MOE_WAVE;
 constexpr int kRT = 4;    // routes staged together
-constexpr int kD = 8;     // VQ block length supported by this kernel
 constexpr int kZBatch = 16;
+
+// A code word of D bf16 values (D = 2, 4 or 8), loaded and kept in LDS as one
+// 4-, 8- or 16-byte word.
+template <int D> struct CodeWord;
+template <> struct CodeWord<8> { typedef uint4 T; };
+template <> struct CodeWord<4> { typedef uint2 T; };
+template <> struct CodeWord<2> { typedef uint32_t T; };
+__device__ __forceinline__ void unpack_cw(const uint4 v, float (&f)[8]) { unpack8(v, f); }
+__device__ __forceinline__ void unpack_cw(const uint2 v, float (&f)[4]) {
+    f[0] = bf16_lo(v.x); f[1] = bf16_hi(v.x); f[2] = bf16_lo(v.y); f[3] = bf16_hi(v.y);
+}
+__device__ __forceinline__ void unpack_cw(const uint32_t v, float (&f)[2]) { f[0] = bf16_lo(v); f[1] = bf16_hi(v); }
+__device__ __forceinline__ uint4 zero_cw(uint4) { return make_uint4(0u, 0u, 0u, 0u); }
+__device__ __forceinline__ uint2 zero_cw(uint2) { return make_uint2(0u, 0u); }
+__device__ __forceinline__ uint32_t zero_cw(uint32_t) { return 0u; }
 
 // Overflow workgroups: runs of two or more routes (in block order, the first
 // kOverflow of them) share their routes with one more workgroup, which takes
@@ -50,8 +64,9 @@ __device__ __forceinline__ bool starts_multi_run(const PlanArgs& plan, int bb, i
 
 // Grid (plan blocks, ceil(I / (4*CPW))): workgroup (blk, cy) owns 4*CPW
 // channels of the expert whose run of blocks starts at blk; wave w owns CPW
-// of them.  Lane l owns VQ blocks 4*(l + 64*qb) .. +3 (one 4-byte index load
-// per channel) and low-rank coordinates rho = l + 64*m.  The index maps and
+// of them.  Lane l owns VQ blocks 4*(l + 64*qb) .. +3 of length D (one 4-byte
+// index load per channel; h elements 4*D*(l + 64*qb) .. +4D-1) and low-rank
+// coordinates rho = l + 64*m.  The index maps and
 // coefficients are kept in registers for every route of the expert; the two
 // code books go to LDS.  A route needs its h row and its finished z vectors
 // (the slice partials added in slice order) in LDS.
@@ -61,13 +76,14 @@ __device__ __forceinline__ bool starts_multi_run(const PlanArgs& plan, int bb, i
 // well-formed plan, and at small batch usually its only one), since a load
 // queued behind the stream would wait for all of it.  Further routes are
 // staged rvq at a time.
-template <int QB, int RM, int CPW>
+template <int D, int QB, int RM, int CPW>
 __global__ void __launch_bounds__(kThreads)
 gateup_vqlr_kernel(PlanArgs plan, VqArgs vq, const float* __restrict__ h, int H, int I, int rvq, float* __restrict__ p,
                    int32_t* __restrict__ err) {
-    constexpr int HPT = QB * 2;                // float4 of one h row per thread (H <= QB * 2048)
+    typedef typename CodeWord<D>::T CW;
+    constexpr int HPT = (QB * 64 * D + kThreads - 1) / kThreads;  // float4 of one h row per thread (H <= QB * 256 * D)
     constexpr int ZPT = RM > 2 ? RM / 2 : 1;   // (projection, rho) items of one route per thread
-    __shared__ uint4 book[2][256];
+    __shared__ CW book[2][256];
     extern __shared__ __align__(16) float dyn[];
     float* hsm = dyn;                       // [rvq][H]
     float* zsm = dyn + (size_t)rvq * H;     // [kRT][2][r]
@@ -124,7 +140,7 @@ gateup_vqlr_kernel(PlanArgs plan, VqArgs vq, const float* __restrict__ h, int H,
             rank += __popcll(__ballot(c0 + lane < blk && starts_multi_run(plan, c0 + lane, nb)));
         split = rank < kOverflow;
     }
-    const int nbk = H / kD;  // VQ blocks per channel
+    const int nbk = H / D;  // VQ blocks per channel
     const int r = vq.r;
     const int H4 = H / 4;
     const int j0 = (blockIdx.y * kWaves + wave) * CPW;
@@ -137,11 +153,11 @@ gateup_vqlr_kernel(PlanArgs plan, VqArgs vq, const float* __restrict__ h, int H,
     // kernel-argument segment with a vector load)
     const int r0 = __builtin_amdgcn_readlane(rv, min(sp, MOE_WAVE - 1));  // row sp: the run's route sp if rows 0..sp are routes
     const int t0 = plan.fk.div(min(max(r0, 0), plan.R - 1));
-    uint4 bk[2];
+    CW bk[2];
 #pragma unroll
     for (int u = 0; u < 2; ++u) {
         const int i = tid + kThreads * u;
-        bk[u] = load16(vq.B[i >> 8] + (size_t)min(i & 255, vq.K - 1) * kD);
+        bk[u] = *reinterpret_cast<const CW*>(vq.B[i >> 8] + (size_t)min(i & 255, vq.K - 1) * D);
     }
     float4 h0[HPT];
 #pragma unroll
@@ -190,7 +206,7 @@ gateup_vqlr_kernel(PlanArgs plan, VqArgs vq, const float* __restrict__ h, int H,
 #pragma unroll
     for (int u = 0; u < 2; ++u) {
         const int i = tid + kThreads * u;
-        book[i >> 8][i & 255] = (i & 255) < vq.K ? bk[u] : make_uint4(0, 0, 0, 0);
+        book[i >> 8][i & 255] = (i & 255) < vq.K ? bk[u] : zero_cw(bk[u]);
     }
 #pragma unroll
     for (int v = 0; v < HPT; ++v)  // unconditional (clamped duplicates store the same value)
@@ -237,10 +253,10 @@ gateup_vqlr_kernel(PlanArgs plan, VqArgs vq, const float* __restrict__ h, int H,
         for (int qb = 0; qb < QB; ++qb) {
             const int b4 = 4 * (lane + MOE_WAVE * qb);
             if (b4 >= nbk) continue;
-            const float4* hr = reinterpret_cast<const float4*>(hsm + (size_t)i * H + b4 * kD);
-            float hv[32];
+            const float4* hr = reinterpret_cast<const float4*>(hsm + (size_t)i * H + b4 * D);
+            float hv[4 * D];
 #pragma unroll
-            for (int v = 0; v < 8; ++v) {
+            for (int v = 0; v < D; ++v) {
                 const float4 x = hr[v];
                 hv[4 * v] = x.x; hv[4 * v + 1] = x.y; hv[4 * v + 2] = x.z; hv[4 * v + 3] = x.w;
             }
@@ -250,10 +266,10 @@ gateup_vqlr_kernel(PlanArgs plan, VqArgs vq, const float* __restrict__ h, int H,
                 for (int c = 0; c < CPW; ++c)
 #pragma unroll
                     for (int x = 0; x < 4; ++x) {
-                        float cw[8];
-                        unpack8(book[P][(jw[P][c][qb] >> (8 * x)) & 255u], cw);
+                        float cw[D];
+                        unpack_cw(book[P][(jw[P][c][qb] >> (8 * x)) & 255u], cw);
 #pragma unroll
-                        for (int y = 0; y < 8; ++y) acc[P][c] = fmaf(cw[y], hv[8 * x + y], acc[P][c]);
+                        for (int y = 0; y < D; ++y) acc[P][c] = fmaf(cw[y], hv[D * x + y], acc[P][c]);
                     }
         }
 #pragma unroll
@@ -343,27 +359,38 @@ gateup_vqlr_kernel(PlanArgs plan, VqArgs vq, const float* __restrict__ h, int H,
     }
 }
 
-template <int QB, int RM, int CPW>
+template <int D, int QB, int RM, int CPW>
 hipError_t vq_launch(const PlanArgs& plan, const VqArgs& vq, const float* h, int H, int I, float* p, int32_t* err,
                      hipStream_t stream) {
     // x: the plan blocks, then the overflow workgroups
     const dim3 grid(plan.max_blocks + kOverflow, (I + kWaves * CPW - 1) / (kWaves * CPW));
     const int rvq = H <= 4096 ? kRT : 2;  // staged h rows: <= 64 KiB
     const size_t lds = ((size_t)rvq * H + (size_t)kRT * 2 * vq.r) * sizeof(float);
-    MOE_LAUNCH((gateup_vqlr_kernel<QB, RM, CPW>), grid, dim3(kThreads), lds, stream, plan, vq, h, H, I, rvq, p, err);
+    MOE_LAUNCH((gateup_vqlr_kernel<D, QB, RM, CPW>), grid, dim3(kThreads), lds, stream, plan, vq, h, H, I, rvq, p, err);
     return hipGetLastError();
 }
 
 // Channels per wave: 8 for the smallest register tile (H <= 2048, r <= 64),
 // else 4.
-template <int QB>
+template <int D, int QB>
 hipError_t vq_rm(const PlanArgs& plan, const VqArgs& vq, const float* h, int H, int I, float* p, int32_t* err,
                  hipStream_t stream) {
     const int RM = (vq.r + 63) / 64;
-    if (RM <= 1) return vq_launch<QB, 1, QB == 1 ? 8 : 4>(plan, vq, h, H, I, p, err, stream);
-    if (RM <= 2) return vq_launch<QB, 2, 4>(plan, vq, h, H, I, p, err, stream);
-    if (RM <= 4) return vq_launch<QB, 4, 4>(plan, vq, h, H, I, p, err, stream);
-    if (RM <= 8) return vq_launch<QB, 8, 4>(plan, vq, h, H, I, p, err, stream);
+    if (RM <= 1) return vq_launch<D, QB, 1, QB == 1 ? 8 : 4>(plan, vq, h, H, I, p, err, stream);
+    if (RM <= 2) return vq_launch<D, QB, 2, 4>(plan, vq, h, H, I, p, err, stream);
+    if (RM <= 4) return vq_launch<D, QB, 4, 4>(plan, vq, h, H, I, p, err, stream);
+    if (RM <= 8) return vq_launch<D, QB, 8, 4>(plan, vq, h, H, I, p, err, stream);
+    return hipErrorInvalidValue;
+}
+
+// Lane blocks: QB = ceil(H / D / 256) groups of four VQ blocks per lane.
+template <int D>
+hipError_t vq_qb(const PlanArgs& plan, const VqArgs& vq, const float* h, int H, int I, float* p, int32_t* err,
+                 hipStream_t stream) {
+    const int QB = (H / D + 255) / 256;
+    if (QB <= 1) return vq_rm<D, 1>(plan, vq, h, H, I, p, err, stream);
+    if (QB <= 2) return vq_rm<D, 2>(plan, vq, h, H, I, p, err, stream);
+    if (QB <= 4) return vq_rm<D, 4>(plan, vq, h, H, I, p, err, stream);
     return hipErrorInvalidValue;
 }
 
@@ -371,11 +398,10 @@ hipError_t vq_rm(const PlanArgs& plan, const VqArgs& vq, const float* h, int H, 
 
 hipError_t launch_gateup_vqlr(const PlanArgs& plan, const VqArgs& vq, const float* h, int H, int I, float* p,
                               int32_t* err, hipStream_t stream) {
-    if (vq.d != kD || vq.K < 1 || vq.K > 256) return hipErrorInvalidValue;
-    const int QB = (H / kD + 255) / 256;
-    if (QB <= 1) return vq_rm<1>(plan, vq, h, H, I, p, err, stream);
-    if (QB <= 2) return vq_rm<2>(plan, vq, h, H, I, p, err, stream);
-    if (QB <= 4) return vq_rm<4>(plan, vq, h, H, I, p, err, stream);
+    if (vq.K < 1 || vq.K > 256 || H % (8 * vq.d)) return hipErrorInvalidValue;
+    if (vq.d == 8) return vq_qb<8>(plan, vq, h, H, I, p, err, stream);
+    if (vq.d == 4) return vq_qb<4>(plan, vq, h, H, I, p, err, stream);
+    if (vq.d == 2) return vq_qb<2>(plan, vq, h, H, I, p, err, stream);
     return hipErrorInvalidValue;
 }
 

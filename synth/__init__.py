@@ -17,6 +17,8 @@ experts with top-8 routing and 8-row alignment blocks; synthetic values):
   aligned_h2048_i768_e128_k8_m21  21 tokens, 4 hot experts biased to ~20% of routes
   chansparse_h2048_i768_e128_k8_m1_keep799   channel top-K, K = 799 of 6144
   vqlr_h2048_i768_e128_k8_m4_d8_K256_r64     VQ + low-rank gate/up, 4 tokens
+  vqlr_..._d4_K256_r256, _d8_K256_r384, _d2_K256_r8   the same at the 4-bit
+                                             storage rate, block lengths 4, 8, 2
 
 Distributions: every weight ~ N(0, 0.02) rounded to bf16; hidden states
 ~ N(0, 1) in fp32; VQ index maps uniform over [0, 256).
@@ -158,6 +160,14 @@ WORKLOADS: Dict[str, Workload] = {w.name: w for w in [
     Workload("chansparse_h2048_i768_e128_k8_m1_keep799", H=2048, I=768, E=128, k=8, M=1, seed=1004,
              keep=(13 * 8 * 768 + 50) // 100),
     Workload("vqlr_h2048_i768_e128_k8_m4_d8_K256_r64", H=2048, I=768, E=128, k=8, M=4, seed=1005, vq=True),
+    # block-length sweep at the 4-bit storage rate, same router, hidden states
+    # and routing as the workload above (same seed)
+    Workload("vqlr_h2048_i768_e128_k8_m4_d4_K256_r256", H=2048, I=768, E=128, k=8, M=4, seed=1005, vq=True,
+             vq_d=4, lr_r=256),
+    Workload("vqlr_h2048_i768_e128_k8_m4_d8_K256_r384", H=2048, I=768, E=128, k=8, M=4, seed=1005, vq=True,
+             vq_d=8, lr_r=384),
+    Workload("vqlr_h2048_i768_e128_k8_m4_d2_K256_r8", H=2048, I=768, E=128, k=8, M=4, seed=1005, vq=True,
+             vq_d=2, lr_r=8),
 ]}
 
 
@@ -202,7 +212,7 @@ def expert_matrix(wl: Workload, layer: int, which: str, experts: Optional[Iterab
 def vq_tensors(wl: Workload, layer: int, experts: Optional[Iterable[int]] = None) -> Dict[str, np.ndarray]:
     """VQ + low-rank gate/up inputs: per projection P in (gate, up)
     basis D_P bf16 [H][r], coefficients C_P bf16 [E][I][r],
-    code book B_P bf16 [K][d], index map J_P uint8 [E][I][H/d]."""
+    code book B_P bf16 [K][d], index map J_P uint8 [E][I][H/d] with entries < K."""
     s = wl.layer_seed(layer)
     ex = range(wl.E) if experts is None else sorted(set(int(e) for e in experts))
     out = {}
@@ -214,6 +224,8 @@ def vq_tensors(wl: Workload, layer: int, experts: Optional[Iterable[int]] = None
         for e in ex:
             normal_bf16(s, "lr_coef/%s/e%d" % (P, e), (wl.I, wl.lr_r), SIGMA_W, out=C[e])
             uniform_u8(s, "vq_idx/%s/e%d" % (P, e), (wl.I, wl.H // wl.vq_d), out=J[e])
+            if wl.vq_K < 256:  # indices into a smaller code book (identity at K = 256)
+                np.remainder(J[e], wl.vq_K, out=J[e])
         out["lr_coef_" + P] = C
         out["vq_idx_" + P] = J
     return out

@@ -69,7 +69,8 @@ FAKE = 0x10000  # 16-byte aligned fake address: never dereferenced by host check
     (dict(H=0), 1), (dict(I=-1), 1), (dict(top_k=0), 1), (dict(max_tokens=0), 1), (dict(max_keep=-1), 1),
     (dict(H=2044), 2), (dict(H=8200), 2), (dict(E=20), 2), (dict(E=2048), 2), (dict(top_k=33, E=64), 2),
     (dict(top_k=9, E=8), 2), (dict(block_b=65), 2), (dict(max_tokens=4097), 2), (dict(max_tokens=600), 2),
-    (dict(wformat=7), 2), (dict(wformat=1, vq_d=4, vq_K=256, lr_r=64), 2),
+    (dict(wformat=7), 2), (dict(wformat=1, vq_d=16, vq_K=256, lr_r=64), 2),
+    (dict(wformat=1, vq_d=3, vq_K=256, lr_r=64), 2), (dict(wformat=1, H=4096, vq_d=2, vq_K=256, lr_r=64), 2),
     (dict(wformat=1, vq_d=8, vq_K=257, lr_r=64), 2), (dict(wformat=1, vq_d=8, vq_K=256, lr_r=60), 2),
     (dict(max_keep=8 * 768 + 1), 2), (dict(wformat=1, vq_d=8, vq_K=256, lr_r=64, max_keep=10), 2),
 ])

@@ -414,11 +414,48 @@ def test_vqlr_b4(mb):
     layer.close()
 
 
-def test_vq_exact_codebook_equals_dense_path(mb):
+@pytest.mark.parametrize("name", ["vqlr_h2048_i768_e128_k8_m4_d4_K256_r256", "vqlr_h2048_i768_e128_k8_m4_d2_K256_r8"])
+def test_vqlr_block_length_full_size(mb, name):
+    """The 4-bit-rate block-length sweep at full size (d = 4, r = 256 and
+    d = 2, r = 8), stage-isolated against the oracle."""
+    wl = synth.WORKLOADS[name]
+    say(name, "layer 0 (full size)")
+    inp = synth.layer_inputs(wl, 0)
+    layer = make_layer(mb, wl, inp, wl.M)
+    g = run_step(mb, layer, inp["h"])
+    assert g["err"] == 0
+    check_router(g, inp, wl.k, wl.H)
+    check_plan(g, wl.E, wl.block_b)
+    ref = O.vqlr_forward(inp["h"], g["ids"], g["w"].astype(np.float64), inp, inp["w_down"])
+    say("  stage-isolated", check_close(g["y"], ref))
+    layer.close()
+
+
+@pytest.mark.parametrize("d,H,I,r,K", [(4, 544, 37, 8, 256), (2, 528, 29, 24, 100), (4, 1024, 64, 136, 17),
+                                       (2, 2048, 40, 64, 256), (8, 1088, 33, 72, 200)])
+def test_vq_block_lengths_ragged(mb, d, H, I, r, K):
+    """Block lengths 2, 4 and 8 on hidden sizes off the lane grid, odd channel
+    counts, ranks that are not multiples of 64 and code books smaller than 256,
+    against the oracle (three tokens, the split path)."""
+    say("vq ragged", dict(d=d, H=H, I=I, r=r, K=K))
+    wl = synth.small_workload("vq_d%d_%d_%d" % (d, H, I), H=H, I=I, E=16, k=4, M=3, seed=H + I + d, vq=True,
+                              vq_d=d, lr_r=r, vq_K=K)
+    inp = synth.layer_inputs(wl, 0)
+    inp["h"] = synth.hidden(wl, 0, 0, M=3)
+    layer = make_layer(mb, wl, inp, 3)
+    g = run_step(mb, layer, inp["h"])
+    assert g["err"] == 0
+    ref = O.vqlr_forward(inp["h"], g["ids"], g["w"].astype(np.float64), inp, inp["w_down"])
+    say("  ", check_close(g["y"], ref))
+    layer.close()
+
+
+@pytest.mark.parametrize("d", [8, 4, 2])
+def test_vq_exact_codebook_equals_dense_path(mb, d):
     """With C = 0 the VQ weights are exactly bf16 (a code-book lookup), so the
     GPU VQ path and the GPU dense path on the materialised weights must both
     meet the tolerance against one oracle output."""
-    wl = synth.small_workload("vq_exact", H=512, I=48, E=16, k=4, M=3, seed=91, vq=True, lr_r=16)
+    wl = synth.small_workload("vq_exact_d%d" % d, H=512, I=48, E=16, k=4, M=3, seed=91, vq=True, lr_r=16, vq_d=d)
     inp = synth.layer_inputs(wl, 0)
     inp["h"] = synth.hidden(wl, 0, 0, M=3)
     for P in ("gate", "up"):
