@@ -126,6 +126,8 @@ typedef struct {
  *               past the code book)
  *  The reconstructed gate/up weight of channel j, row i is
  *      sum_rho D_P[i][rho] C_P,e[j][rho] + B_P[J_P,e[j][i / vq_d]][i % vq_d].
+ *  Alignment (checked by moe_create, MOE_ERR_INVALID_ARG otherwise): the bf16
+ *  arrays 16 bytes, vq_idx and the fp32 / int32 arrays 4 bytes.
  */
 typedef struct {
     const uint16_t *router_w;

@@ -34,7 +34,7 @@ LaunchEvents& launch_events();
 // for up to three matrices W_m (bf16 [H][N_m]) in one launch.
 struct GemvJob {
     const uint16_t* W;   // bf16 [H][N]
-    int N;               // columns, N % 8 == 0, N <= 2048
+    int N;               // columns, N % 8 == 0, 8 <= N <= 1024
     float* part;         // fp32 [gemv_slices(H, N)][M][N]
 };
 int gemv_slices(int H, int N);

@@ -93,7 +93,7 @@ moe_status check_weights(const moe_config* c, const moe_weights* w) {
     } else {
         for (int P = 0; P < 2; ++P) {
             if (!w->lr_basis[P] || !w->lr_coef[P] || !w->vq_book[P] || !w->vq_idx[P]) return MOE_ERR_INVALID_ARG;
-            if (!aligned(w->lr_basis[P], 16) || !aligned(w->lr_coef[P], 2) || !aligned(w->vq_book[P], 16) ||
+            if (!aligned(w->lr_basis[P], 16) || !aligned(w->lr_coef[P], 16) || !aligned(w->vq_book[P], 16) ||
                 !aligned(w->vq_idx[P], 4))
                 return MOE_ERR_INVALID_ARG;
         }

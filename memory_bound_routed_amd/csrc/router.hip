@@ -19,7 +19,6 @@ namespace {
 
 constexpr int kThreads = 256;
 constexpr int kTokTile = 4;
-constexpr int kHStage = 2048;  // floats of h staged in LDS per token stage (batches of several tokens)
 constexpr int kRowsPerThread = 4;
 constexpr int kMaxJobs = 3;
 constexpr int kMaxExpertsPerLane = 16;  // E <= 1024
@@ -27,120 +26,6 @@ constexpr int kMaxExpertsPerLane = 16;  // E <= 1024
 struct GemvJobs {
     GemvJob job[kMaxJobs];
 };
-
-// Slice partial of one matrix: part[slice][t][n] = sum_{i in slice} h[t][i] W[i][n].
-// N/8 threads cover a row with one 16-byte load each; rpp = 256/(N/8) row
-// groups; each thread handles kRowsPerThread rows of the slice (all loads
-// issued together), then one thread per output adds the row groups in group
-// order from LDS.  Summation depth per partial: kRowsPerThread + rpp - 1.
-// COHERENT: the partials are read by another workgroup of the same launch,
-// so they are stored device-coherently.
-template <int TT, bool COHERENT>
-__device__ __forceinline__ void slice_partial(const float* __restrict__ h, int M, int H,
-                                              const uint16_t* __restrict__ W, int N, int slice, float* __restrict__ part,
-                                              float* red) {
-    const int tpr = N >> 3;
-    const int rpp = kThreads / tpr;
-    const int tid = threadIdx.x;
-    const int col8 = tid % tpr;
-    const int rg = tid / tpr;
-    const bool active = rg < rpp;
-    const int slice_rows = rpp * kRowsPerThread;
-    const int r0 = slice * slice_rows;
-
-    // The thread's weight rows are loaded once and reused for every token
-    // pass.  Every load is issued before the first use: rows past H read row
-    // H-1 and tokens past M read token M-1, and both are zeroed by a select
-    // afterwards (no load sits in a branch, which would make the compiler
-    // wait for it before the next one).
-    uint4 wv[kRowsPerThread];
-    if (active) {
-#pragma unroll
-        for (int u = 0; u < kRowsPerThread; ++u) {
-            const int i = min(r0 + rg + u * rpp, H - 1);
-            wv[u] = load_stream16(W + (size_t)i * N + col8 * 8);
-        }
-    }
-    // Several tokens: the slice's rows of h for a stage of tokens go to LDS
-    // in one round (one memory round trip per stage instead of one per pass).
-    __shared__ float hst[kHStage];
-    const int stage_tokens = TT == 1 ? 1 : max(1, kHStage / slice_rows);
-    for (int tc = 0; tc < M; tc += stage_tokens) {
-      const int ntc = min(stage_tokens, M - tc);
-      if (TT > 1) {
-        __syncthreads();  // the previous stage is no longer read
-        for (int idx = tid; idx < ntc * slice_rows; idx += kThreads) {
-            const int t = idx / slice_rows, i = idx - t * slice_rows;
-            hst[idx] = r0 + i < H ? h[(size_t)(tc + t) * H + r0 + i] : 0.f;
-        }
-        __syncthreads();
-      }
-      for (int t0 = tc; t0 < tc + ntc; t0 += TT) {
-        const int nt = min(TT, tc + ntc - t0);
-        if (active) {
-            float hv[kRowsPerThread][TT];
-#pragma unroll
-            for (int u = 0; u < kRowsPerThread; ++u) {
-                const int i = min(r0 + rg + u * rpp, H - 1);
-#pragma unroll
-                for (int t = 0; t < TT; ++t)
-                    hv[u][t] = TT == 1 ? h[(size_t)t0 * H + i]
-                                       : hst[(t0 - tc + min(t, nt - 1)) * slice_rows + min(rg + u * rpp, slice_rows - 1)];
-            }
-#pragma unroll
-            for (int u = 0; u < kRowsPerThread; ++u) {
-                const bool row_ok = r0 + rg + u * rpp < H;
-#pragma unroll
-                for (int t = 0; t < TT; ++t) hv[u][t] = (row_ok && t < nt) ? hv[u][t] : 0.f;
-            }
-            float acc[TT][8];
-#pragma unroll
-            for (int t = 0; t < TT; ++t)
-#pragma unroll
-                for (int c = 0; c < 8; ++c) acc[t][c] = 0.f;
-#pragma unroll
-            for (int u = 0; u < kRowsPerThread; ++u) {
-                float wf[8];
-                unpack8(wv[u], wf);
-#pragma unroll
-                for (int t = 0; t < TT; ++t)
-#pragma unroll
-                    for (int c = 0; c < 8; ++c) acc[t][c] = fmaf(hv[u][t], wf[c], acc[t][c]);
-            }
-#pragma unroll
-            for (int t = 0; t < TT; ++t)
-#pragma unroll
-                for (int c = 0; c < 8; ++c) red[(rg * TT + t) * N + col8 * 8 + c] = acc[t][c];
-        }
-        __syncthreads();
-        // row groups added in group order: thread idx = t*N + n sums red[g][t][n]
-        for (int idx = tid; idx < nt * N; idx += kThreads) {
-            float s = red[idx];
-#pragma unroll 8
-            for (int g = 1; g < rpp; ++g) s += red[g * TT * N + idx];
-            float* dst = part + ((size_t)slice * M + t0) * N + idx;
-            if (COHERENT)
-                store_agent(dst, s);
-            else
-                *dst = s;
-        }
-        __syncthreads();
-      }
-    }
-}
-
-__global__ void __launch_bounds__(kThreads)
-gemv_partials_kernel(const float* __restrict__ h, int M, int H, GemvJobs jobs) {
-    extern __shared__ __align__(16) float red[];
-    const GemvJob& jb = jobs.job[blockIdx.y];
-    const int rpp = kThreads / (jb.N >> 3);
-    const int nslices = (H + rpp * kRowsPerThread - 1) / (rpp * kRowsPerThread);
-    if ((int)blockIdx.x >= nslices) return;
-    if (M == 1)
-        slice_partial<1, false>(h, M, H, jb.W, jb.N, blockIdx.x, jb.part, red);
-    else
-        slice_partial<kTokTile, false>(h, M, H, jb.W, jb.N, blockIdx.x, jb.part, red);
-}
 
 // Router GEMV tiles: the grid covers row slices x column groups of cgw
 // experts (32, or 16 / 8 for small E) along x, groups of kTokTile tokens
@@ -464,7 +349,28 @@ router_partials_kernel(const float* __restrict__ h, int M, int H, const uint16_t
                               part, red);
 }
 
-size_t lds_bytes(int N) { return (size_t)(kThreads / (N / 8)) * kTokTile * N * sizeof(float); }
+// Slice partials of up to kMaxJobs skinny GEMVs (the VQ + low-rank format's
+// z = D^T h of the gate and the up basis), one matrix per grid z, tiled as
+// the router: part[slice][t][n] = sum_{i in slice} h[t][i] W[i][n] with
+// RouterTiles(H, N).nrs slices (8 at H = 2048 for N >= 32), so a consumer
+// adds few slices whatever N is.
+__global__ void __launch_bounds__(kThreads)
+gemv_partials_kernel(const float* __restrict__ h, int M, int H, GemvJobs jobs) {
+    extern __shared__ __align__(16) float red[];
+    const GemvJob& jb = jobs.job[blockIdx.z];
+    const RouterTiles tl(H, jb.N);
+    if ((int)blockIdx.x >= tl.nrs * tl.ncg) return;
+    if (M == 1)
+        router_tile<1>(h, M, 0, H, jb.W, jb.N, tl, blockIdx.x % tl.nrs, blockIdx.x / tl.nrs, jb.part, red);
+    else
+        router_tile<kTokTile>(h, M, blockIdx.y * kTokTile, H, jb.W, jb.N, tl, blockIdx.x % tl.nrs,
+                              blockIdx.x / tl.nrs, jb.part, red);
+}
+
+size_t tile_lds_bytes(int H, int N) {
+    const RouterTiles tl(H, N);
+    return (size_t)tl.rpt * kTokTile * tl.cgw * sizeof(float);
+}
 
 // LDS of the one-launch router: the tile's row-group sums, or the keys and
 // rank counts of the top-k (8 + 2*4 bytes per token and expert), whichever
@@ -485,22 +391,20 @@ int router_grid(int H, int E) {
 
 int router_groups(int M) { return M == 1 ? 1 : (M + kTokTile - 1) / kTokTile; }
 
-int gemv_slices(int H, int N) {
-    const int rpp = kThreads / (N / 8);
-    return (H + rpp * kRowsPerThread - 1) / (rpp * kRowsPerThread);
-}
+int gemv_slices(int H, int N) { return RouterTiles(H, N).nrs; }
 
 hipError_t launch_gemv_partials(const float* h, int M, int H, const GemvJob* jobs, int njobs, hipStream_t stream) {
-    if (njobs < 1 || njobs > kMaxJobs) return hipErrorInvalidValue;
+    if (njobs < 1 || njobs > kMaxJobs || M < 1) return hipErrorInvalidValue;
     GemvJobs js{};
     size_t lds = 0;
     int grid = 0;
     for (int i = 0; i < njobs; ++i) {
+        if (jobs[i].N < 8 || jobs[i].N % 8) return hipErrorInvalidValue;
         js.job[i] = jobs[i];
-        lds = lds_bytes(jobs[i].N) > lds ? lds_bytes(jobs[i].N) : lds;
-        grid = gemv_slices(H, jobs[i].N) > grid ? gemv_slices(H, jobs[i].N) : grid;
+        lds = tile_lds_bytes(H, jobs[i].N) > lds ? tile_lds_bytes(H, jobs[i].N) : lds;
+        grid = router_grid(H, jobs[i].N) > grid ? router_grid(H, jobs[i].N) : grid;
     }
-    MOE_LAUNCH(gemv_partials_kernel, dim3(grid, njobs), dim3(kThreads), lds, stream, h, M, H, js);
+    MOE_LAUNCH(gemv_partials_kernel, dim3(grid, router_groups(M), njobs), dim3(kThreads), lds, stream, h, M, H, js);
     return hipGetLastError();
 }
 

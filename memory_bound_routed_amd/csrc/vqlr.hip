@@ -39,6 +39,28 @@ __device__ __forceinline__ void unpack_cw(const uint2 v, float (&f)[4]) {
 }
 __device__ __forceinline__ void unpack_cw(const uint32_t v, float (&f)[2]) { f[0] = bf16_lo(v); f[1] = bf16_hi(v); }
 __device__ __forceinline__ uint4 zero_cw(uint4) { return make_uint4(0u, 0u, 0u, 0u); }
+
+// RM consecutive low-rank coefficients (bf16) of one lane in (RM + 1) / 2
+// 32-bit words, loaded as one 2-, 4-, 8- or 16-byte word.
+template <int RM>
+struct Coef {
+    uint32_t w[(RM + 1) / 2];
+    __device__ __forceinline__ void load(const uint16_t* p) {
+        if constexpr (RM == 1) {
+            w[0] = __builtin_nontemporal_load(p);
+        } else if constexpr (RM == 2) {
+            w[0] = __builtin_nontemporal_load(reinterpret_cast<const uint32_t*>(p));
+        } else if constexpr (RM == 4) {
+            typedef unsigned int u32x2_t __attribute__((ext_vector_type(2)));
+            const u32x2_t v = __builtin_nontemporal_load(reinterpret_cast<const u32x2_t*>(p));
+            w[0] = v.x; w[1] = v.y;
+        } else {
+            const uint4 v = load_stream16(p);
+            w[0] = v.x; w[1] = v.y; w[2] = v.z; w[3] = v.w;
+        }
+    }
+    __device__ __forceinline__ float get(int m) const { return (m & 1) ? bf16_hi(w[m >> 1]) : bf16_lo(w[m >> 1]); }
+};
 __device__ __forceinline__ uint2 zero_cw(uint2) { return make_uint2(0u, 0u); }
 __device__ __forceinline__ uint32_t zero_cw(uint32_t) { return 0u; }
 
@@ -66,7 +88,8 @@ __device__ __forceinline__ bool starts_multi_run(const PlanArgs& plan, int bb, i
 // channels of the expert whose run of blocks starts at blk; wave w owns CPW
 // of them.  Lane l owns VQ blocks 4*(l + 64*qb) .. +3 of length D (one 4-byte
 // index load per channel; h elements 4*D*(l + 64*qb) .. +4D-1) and low-rank
-// coordinates rho = l + 64*m.  The index maps and
+// coordinates rho = RM*l .. RM*l + RM-1 (one load of RM bf16 per channel;
+// r % 8 == 0 makes a lane's coordinates all valid or all past r).  The index maps and
 // coefficients are kept in registers for every route of the expert; the two
 // code books go to LDS.  A route needs its h row and its finished z vectors
 // (the slice partials added in slice order) in LDS.
@@ -177,7 +200,8 @@ gateup_vqlr_kernel(PlanArgs plan, VqArgs vq, const float* __restrict__ h, int H,
 
     // The index and coefficient stream.
     uint32_t jw[2][CPW][QB];
-    uint32_t cw16[2][CPW][RM];  // bf16 patterns, converted (and masked) where used
+    Coef<RM> cw[2][CPW];  // bf16 patterns, converted (and masked) where used
+    const int rl = r / RM;  // lanes holding coefficients (r % 8 == 0, RM <= 8)
 #pragma unroll
     for (int P = 0; P < 2; ++P)
 #pragma unroll
@@ -194,11 +218,7 @@ gateup_vqlr_kernel(PlanArgs plan, VqArgs vq, const float* __restrict__ h, int H,
                 const int b4 = 4 * (lane + MOE_WAVE * qb);
                 jw[P][c][qb] = __builtin_nontemporal_load(reinterpret_cast<const uint32_t*>(jrow + min(b4, nbk - 4)));
             }
-#pragma unroll
-            for (int m = 0; m < RM; ++m) {
-                const int rho = lane + MOE_WAVE * m;
-                cw16[P][c][m] = __builtin_nontemporal_load(crow + min(rho, r - 1));
-            }
+            cw[P][c].load(crow + RM * min(lane, rl - 1));
         }
 
     // Round 2 into LDS (in the stream's basic block, so that nothing moves
@@ -239,16 +259,19 @@ gateup_vqlr_kernel(PlanArgs plan, VqArgs vq, const float* __restrict__ h, int H,
         for (int P = 0; P < 2; ++P)
 #pragma unroll
             for (int c = 0; c < CPW; ++c) acc[P][c] = 0.f;
+        if (lane < rl) {
 #pragma unroll
-        for (int P = 0; P < 2; ++P)
+            for (int P = 0; P < 2; ++P) {
+                float z[RM];
+                const float* zr = zsm + (i * 2 + P) * r + RM * lane;
 #pragma unroll
-            for (int m = 0; m < RM; ++m) {
-                const int rho = lane + MOE_WAVE * m;
-                const float z = rho < r ? zsm[(i * 2 + P) * r + rho] : 0.f;
+                for (int m = 0; m < RM; ++m) z[m] = zr[m];
 #pragma unroll
                 for (int c = 0; c < CPW; ++c)
-                    acc[P][c] = fmaf(rho < r ? bf16_lo(cw16[P][c][m]) : 0.f, z, acc[P][c]);
+#pragma unroll
+                    for (int m = 0; m < RM; ++m) acc[P][c] = fmaf(cw[P][c].get(m), z[m], acc[P][c]);
             }
+        }
 #pragma unroll
         for (int qb = 0; qb < QB; ++qb) {
             const int b4 = 4 * (lane + MOE_WAVE * qb);
