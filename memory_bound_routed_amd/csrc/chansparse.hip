@@ -133,7 +133,7 @@ chan_select_kernel(const int32_t* __restrict__ topk_ids, const float* __restrict
     const int n = k * I;
     unsigned long long* keys = reinterpret_cast<unsigned long long*>(lds);  // [k][I] key at list position
     uint16_t* jsrt = reinterpret_cast<uint16_t*>(lds + 8 * (size_t)n);     // [k][I] channel at list position
-    unsigned char* flag = lds;  // [n] kept, candidate order (over the keys, after the search)
+    unsigned char* flag = lds;  // [I] kept channels of the own list (over the keys, after the search)
     __shared__ double sa[32];
     __shared__ int se[32];
     __shared__ int seo[32];  // tie order of slot s: its expert id, invalid last
