@@ -450,6 +450,34 @@ def test_vq_block_lengths_ragged(mb, d, H, I, r, K):
     layer.close()
 
 
+@pytest.mark.parametrize("name", ["dense_h2048_i768_e128_k8_m8", "dense_h2048_i768_e128_k8_m16",
+                                  "vqlr_h2048_i768_e128_k8_m8_d8_K256_r64", "vqlr_h2048_i768_e128_k8_m16_d8_K256_r64"])
+def test_batch_8_16_full_size(mb, name):
+    """Batch 8 and 16 decode at full size (dense bf16 and VQ + low rank): the
+    plan, the router (certified ids) and y against the oracle, stage-isolated,
+    through the one-call decode step and the separate calls, bit for bit."""
+    import torch
+    wl = synth.WORKLOADS[name]
+    say(name, "layer 0 (full size)")
+    inp = synth.layer_inputs(wl, 0)
+    layer = make_layer(mb, wl, inp, wl.M)
+    g = run_step(mb, layer, inp["h"])
+    assert g["err"] == 0
+    check_router(g, inp, wl.k, wl.H)
+    check_plan(g, wl.E, wl.block_b)
+    say("  distinct experts", len(set(g["ids"].ravel())))
+    if wl.vq:
+        ref = O.vqlr_forward(inp["h"], g["ids"], g["w"].astype(np.float64), inp, inp["w_down"])
+    else:
+        ref = O.dense_forward(inp["h"], g["ids"], g["w"].astype(np.float64), inp["w_gate"], inp["w_up"],
+                              inp["w_down"])
+    say("  stage-isolated", check_close(g["y"], ref))
+    y1 = layer.decode_step(to_dev(inp["h"]), wl.M).cpu().numpy()
+    torch.cuda.synchronize()
+    assert np.array_equal(y1.view(np.int32), np.asarray(g["y"], np.float32).view(np.int32))
+    layer.close()
+
+
 @pytest.mark.parametrize("d", [8, 4, 2])
 def test_vq_exact_codebook_equals_dense_path(mb, d):
     """With C = 0 the VQ weights are exactly bf16 (a code-book lookup), so the
