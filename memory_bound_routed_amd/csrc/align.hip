@@ -20,10 +20,10 @@ align_kernel(const int32_t* __restrict__ topk_ids, int R, int E, int b, int32_t*
     extern __shared__ int smem[];
     if (R <= MOE_WAVE) {
         if (threadIdx.x < MOE_WAVE)
-            align_wave([&](int r) { return topk_ids[r]; }, R, E, fb, sorted_routes, block_expert, counts, err, smem);
+            align_wave([&](int r) { return topk_ids[r]; }, R, E, fb, sorted_routes, block_expert, counts, err);
         return;
     }
-    align_workgroup([&](int r) { return topk_ids[r]; }, R, E, b, sorted_routes, block_expert, counts, err, smem);
+    align_workgroup([&](int r) { return topk_ids[r]; }, R, E, fb, sorted_routes, block_expert, counts, err, smem);
 }
 
 }  // namespace

@@ -97,26 +97,47 @@ __device__ __forceinline__ void router_tile(const float* __restrict__ h, int M, 
 #pragma unroll
         for (int c = 0; c < 8; ++c) red[(rg * TT + t) * tl.cgw + c8 * 8 + c] = acc[t][c];
     __syncthreads();
-    // output o = t*cgw + c: lanes 8o' .. 8o'+7 of a pass (every lane takes part
-    // in the butterfly)
+    // output o = t*cgw + c: lanes 8o' .. 8o'+7 of pass p (o = 32p + o'; every
+    // lane takes part in the butterfly).  The row groups of a lane (gpl = 8,
+    // 16 or 32) are read 8 at a time for every pass at once, and added in
+    // row-group order.
     const int sub = tid % 8;
-    const int gpl = tl.rpt / 8;  // row groups per lane
+    const int gpl = tl.rpt / 8;  // row groups per lane, a multiple of 8
     const int nout = Mg * tl.cgw;
-    for (int o0 = 0; o0 < nout; o0 += kThreads / 8) {
-        const int o = o0 + tid / 8;
+    constexpr int kOutPerPass = kThreads / 8;
+    constexpr int NP = (TT * kRouterCG + kOutPerPass - 1) / kOutPerPass;  // passes, nout <= TT * cgw
+    float v[NP];
+    const float* src[NP];
+#pragma unroll
+    for (int p = 0; p < NP; ++p) {
+        v[p] = 0.f;
+        const int o = min(p * kOutPerPass + tid / 8, nout - 1);  // clamped reads are dropped below
         const int t = o / tl.cgw, c = o - t * tl.cgw;
-        float v = 0.f;
-        if (o < nout) {
-            const float* src = red + ((size_t)sub * gpl * TT + t) * tl.cgw + c;
-            for (int g = 0; g < gpl; ++g) v += src[(size_t)g * TT * tl.cgw];
-        }
+        src[p] = red + ((size_t)sub * gpl * TT + t) * tl.cgw + c;
+    }
+    for (int g0 = 0; g0 < gpl; g0 += 8) {
+        float x[NP][8];
+#pragma unroll
+        for (int p = 0; p < NP; ++p)
+#pragma unroll
+            for (int u = 0; u < 8; ++u) x[p][u] = src[p][(size_t)(g0 + u) * TT * tl.cgw];
+#pragma unroll
+        for (int p = 0; p < NP; ++p)
+#pragma unroll
+            for (int u = 0; u < 8; ++u) v[p] += x[p][u];
+    }
+#pragma unroll
+    for (int p = 0; p < NP; ++p) {
         // xor 1, xor 2, then the two quads of the 8 lanes (half-row mirror):
         // DPP moves, no LDS round trip
-        v += dpp<MOE_DPP_QUAD_XOR1>(v);
-        v += dpp<MOE_DPP_QUAD_XOR2>(v);
-        v += dpp<MOE_DPP_ROW_HALF_MIRROR>(v);
+        float w = v[p];
+        w += dpp<MOE_DPP_QUAD_XOR1>(w);
+        w += dpp<MOE_DPP_QUAD_XOR2>(w);
+        w += dpp<MOE_DPP_ROW_HALF_MIRROR>(w);
+        const int o = p * kOutPerPass + tid / 8;
+        const int t = o / tl.cgw, c = o - t * tl.cgw;
         const int e = cg * tl.cgw + c;
-        if (sub == 0 && o < nout && e < E) store_agent(part + ((size_t)rs * M + t0 + t) * E + e, v);
+        if (sub == 0 && o < nout && e < E) store_agent(part + ((size_t)rs * M + t0 + t) * E + e, w);
     }
 }
 
@@ -163,24 +184,42 @@ __device__ __forceinline__ void topk_pass(int t0, int nt, int M, int E, int k, i
     uint64_t* skey = reinterpret_cast<uint64_t*>(red);
     int* prank = reinterpret_cast<int*>(skey + nt * E);
     const int halfE = E / 2;  // E % 8 == 0: each half is a whole number of 16-byte key pairs
-    for (int pr = tid; pr < nt * E; pr += kThreads) {
-        const int tq = fE.div(pr);
-        const int t = t0 + tq, e = pr - tq * E;
-        const float bv = bias ? bias[e] : 0.f;  // issued with the slice loads
-        float s = 0.f;
-        for (int sl0 = 0; sl0 < nslices; sl0 += SB) {
-            float x[SB];
+    // Two (token, expert) entries per thread and round: the slice loads of
+    // both are in flight together.
+    for (int pr0 = tid; pr0 < nt * E; pr0 += 2 * kThreads) {
+        int pe[2], te[2], ee[2];
+        float bv[2], s[2];
 #pragma unroll
-            for (int u = 0; u < SB; ++u) {
-                const float* q = part + ((size_t)min(sl0 + u, nslices - 1) * M + t) * E + e;
-                x[u] = COHERENT ? load_agent(q) : *q;
-            }
-#pragma unroll
-            for (int u = 0; u < SB; ++u) s += sl0 + u < nslices ? x[u] : 0.f;  // slice order
+        for (int i = 0; i < 2; ++i) {
+            pe[i] = pr0 + i * kThreads;
+            const int prc = min(pe[i], nt * E - 1);  // a clamped entry is computed and not stored
+            const int tq = fE.div(prc);
+            te[i] = t0 + tq;
+            ee[i] = prc - tq * E;
+            bv[i] = bias ? bias[ee[i]] : 0.f;  // issued with the slice loads
+            s[i] = 0.f;
         }
-        if (bias) s += bv;
-        if (logits_out) logits_out[(size_t)t * E + e] = s;
-        skey[pr] = order_key((s != s) ? -INFINITY : s, e);
+        for (int sl0 = 0; sl0 < nslices; sl0 += SB) {
+            float x[2][SB];
+#pragma unroll
+            for (int i = 0; i < 2; ++i)
+#pragma unroll
+                for (int u = 0; u < SB; ++u) {
+                    const float* q = part + ((size_t)min(sl0 + u, nslices - 1) * M + te[i]) * E + ee[i];
+                    x[i][u] = COHERENT ? load_agent(q) : *q;
+                }
+#pragma unroll
+            for (int i = 0; i < 2; ++i)
+#pragma unroll
+                for (int u = 0; u < SB; ++u) s[i] += sl0 + u < nslices ? x[i][u] : 0.f;  // slice order
+        }
+#pragma unroll
+        for (int i = 0; i < 2; ++i) {
+            if (pe[i] >= nt * E) continue;
+            if (bias) s[i] += bv[i];
+            if (logits_out) logits_out[(size_t)te[i] * E + ee[i]] = s[i];
+            skey[pe[i]] = order_key((s[i] != s[i]) ? -INFINITY : s[i], ee[i]);
+        }
     }
     __shared__ int s_slow;
     __shared__ uint64_t wk[kTokTile][MOE_WAVE];
@@ -308,10 +347,10 @@ router_align_kernel(const float* __restrict__ h, int M, int H, const uint16_t* _
             const int aw = min(M, kThreads / MOE_WAVE - 1);
             if ((int)threadIdx.x / MOE_WAVE == aw)
                 align_wave([&](int r) { const int t = fk.div(r); return sel.e[t][r - t * k]; }, R, E, fb,
-                           sorted_routes, block_expert, counts, err, reinterpret_cast<int*>(red));
+                           sorted_routes, block_expert, counts, err);
         } else {
             __syncthreads();
-            align_workgroup([&](int r) { return ids[r]; }, R, E, b, sorted_routes, block_expert, counts, err,
+            align_workgroup([&](int r) { return ids[r]; }, R, E, fb, sorted_routes, block_expert, counts, err,
                             reinterpret_cast<int*>(red));
         }
         rearm_ticket(ticket + 1);
@@ -325,10 +364,9 @@ router_align_kernel(const float* __restrict__ h, int M, int H, const uint16_t* _
     if (!s_last) return;
     if (R <= MOE_WAVE) {
         if (threadIdx.x < MOE_WAVE)
-            align_wave([&](int r) { return load_agent(ids + r); }, R, E, fb, sorted_routes, block_expert, counts, err,
-                       reinterpret_cast<int*>(red));
+            align_wave([&](int r) { return load_agent(ids + r); }, R, E, fb, sorted_routes, block_expert, counts, err);
     } else {
-        align_workgroup([&](int r) { return load_agent(ids + r); }, R, E, b, sorted_routes, block_expert, counts, err,
+        align_workgroup([&](int r) { return load_agent(ids + r); }, R, E, fb, sorted_routes, block_expert, counts, err,
                         reinterpret_cast<int*>(red));
     }
     rearm_ticket(ticket);

@@ -72,11 +72,6 @@ __device__ __forceinline__ uint64_t readlane64(uint64_t v, int lane) {
     return ((uint64_t)hi << 32) | lo;
 }
 
-// # set bits of m below this lane.
-__device__ __forceinline__ int mbcnt64(uint64_t m) {
-    return (int)__builtin_amdgcn_mbcnt_hi((uint32_t)(m >> 32), __builtin_amdgcn_mbcnt_lo((uint32_t)m, 0));
-}
-
 // One butterfly step over a DPP lane pairing: the larger (take_max) or the
 // smaller of a lane's key and its partner's.
 template <int CTRL>
