@@ -571,6 +571,49 @@ def test_alignment_randomised_stage_isolated(mb):
     layer.close()
 
 
+@pytest.mark.parametrize("E,k,b,maxM", [(1024, 8, 1, 48), (1024, 6, 3, 40), (8, 8, 64, 16), (8, 8, 1, 512),
+                                         (136, 8, 5, 96)])
+def test_alignment_extremes(mb, E, k, b, maxM):
+    """Alignment at the limits of its bit arithmetic: 10-bit expert ids
+    (E = 1024, four experts per thread in the block-count scan), E = 8,
+    b = 1 (an expert can need 64 blocks), b = 64, and 4096 routes (64
+    chunks).  Bit-exact against the oracle's alignment (page "Route-Block
+    Membership Selects Packed-AWQ Arithmetic", Sec. 2.1 and Sec. 5.3)."""
+    import torch
+    rng = np.random.default_rng(7 + E + b)
+    wl = synth.small_workload("align_ext", H=64, I=8, E=E, k=k, M=1, seed=11, block_b=b)
+    inp = synth.layer_inputs(wl, 0)
+    layer = make_layer(mb, wl, inp, maxM)
+    cap = mb.moe_align_capacity(maxM, k, E, b)
+    for trial in range(24):
+        M = [1, maxM, 64 // k, 64 // k + 1][trial] if trial < 4 else int(rng.integers(1, maxM + 1))
+        kind = trial % 4
+        if kind == 0:
+            ids = rng.integers(0, E, size=(M, k))
+        elif kind == 1:
+            ids = np.full((M, k), E - 1 - int(rng.integers(min(E, 4))))
+        elif kind == 2:
+            ids = rng.integers(-2, E + 2, size=(M, k))
+        else:
+            p = np.ones(E); p[-3:] = 40.0
+            ids = rng.choice(E, size=(M, k), p=p / p.sum())
+        dids = torch.from_numpy(ids.astype(np.int32)).cuda()
+        sr = torch.full((cap,), -7, dtype=torch.int32, device="cuda")
+        be = torch.full((max(cap // b, 1),), -7, dtype=torch.int32, device="cuda")
+        ct = torch.zeros(2, dtype=torch.int32, device="cuda")
+        mb.moe_align_blocks(layer.ctx, dids, M, sr, be, ct)
+        torch.cuda.synchronize()
+        flags = mb.moe_read_device_error(layer.ctx)
+        al = O.align_blocks(ids, E, b)
+        c = ct.cpu().numpy()
+        assert int(c[0]) == al["num_blocks"] and int(c[1]) == al["num_padded"], (trial, M)
+        np.testing.assert_array_equal(sr[: c[1]].cpu().numpy(), al["sorted_routes"])
+        np.testing.assert_array_equal(be[: c[0]].cpu().numpy(), al["block_expert"])
+        assert np.all(sr[c[1]:].cpu().numpy() == -7), "wrote past num_padded"
+        assert (flags == mb.DEVERR_BAD_ROUTE_ID) == (al["invalid_routes"] > 0)
+    layer.close()
+
+
 def test_empty_batch_and_max_tokens(mb):
     import torch
     wl = synth.small_workload("edge", H=256, I=32, E=16, k=2, M=6, seed=5)
