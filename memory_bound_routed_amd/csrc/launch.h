@@ -52,7 +52,7 @@ hipError_t launch_router(const float* h, int M, int H, const uint16_t* Wr, int E
 hipError_t launch_router_align(const float* h, int M, int H, const uint16_t* Wr, int E, const float* bias, int k,
                                float* part, unsigned* ticket, int32_t* ids, float* wts, float* logits_out, int b,
                                int32_t* sorted_routes, int32_t* block_expert, int32_t* counts, int32_t* err,
-                               hipStream_t stream);
+                               hipStream_t stream, const GemvJob* jobs = nullptr, int njobs = 0);
 
 // Router GEMV without the top-k: part fp32 [router_slices(H, E)][M][E]
 // (row-slice partials; logit of (t, e) = 0 + part[0][t][e] + part[1][t][e]

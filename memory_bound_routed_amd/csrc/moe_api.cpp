@@ -281,7 +281,8 @@ moe_status moe_route_topk(moe_ctx* ctx, const float* h, int32_t M, int32_t* topk
     return hip_status(e);
 }
 
-moe_status moe_route_align(moe_ctx* ctx, const float* h, int32_t M, int32_t* topk_ids, float* topk_w,
+static moe_status route_align_impl(bool with_z, moe_ctx* ctx, const float* h, int32_t M, int32_t* topk_ids,
+                                   float* topk_w,
                            float* logits_out, int32_t* sorted_routes, int32_t* block_expert, int32_t* counts,
                            void* stream) {
     if (!ctx || M < 0) return MOE_ERR_INVALID_ARG;
@@ -291,12 +292,24 @@ moe_status moe_route_align(moe_ctx* ctx, const float* h, int32_t M, int32_t* top
     if (!h || !topk_ids || !topk_w || !sorted_routes || !block_expert || !aligned(h, 16)) return MOE_ERR_INVALID_ARG;
     const moe_config& c = ctx->cfg;
     hipStream_t s = static_cast<hipStream_t>(stream);
+    // with_z: the VQ + low-rank shared projections z = D^T h ride along as
+    // extra workgroups of the same launch
+    const moe::GemvJob jobs[2] = {{ctx->w.lr_basis[0], c.lr_r, ctx->zpart[0]},
+                                  {ctx->w.lr_basis[1], c.lr_r, ctx->zpart[1]}};
     Launch l(ctx, MOE_KERNEL_ROUTER_ALIGN, s);
     hipError_t e = moe::launch_router_align(h, M, c.H, ctx->w.router_w, c.E, ctx->w.router_bias, c.top_k,
                                             ctx->router_part, ctx->ticket, topk_ids, topk_w, logits_out, c.block_b,
-                                            sorted_routes, block_expert, counts, ctx->err, s);
+                                            sorted_routes, block_expert, counts, ctx->err, s, with_z ? jobs : nullptr,
+                                            with_z ? 2 : 0);
     l.done();
     return hip_status(e);
+}
+
+moe_status moe_route_align(moe_ctx* ctx, const float* h, int32_t M, int32_t* topk_ids, float* topk_w,
+                           float* logits_out, int32_t* sorted_routes, int32_t* block_expert, int32_t* counts,
+                           void* stream) {
+    return route_align_impl(false, ctx, h, M, topk_ids, topk_w, logits_out, sorted_routes, block_expert, counts,
+                            stream);
 }
 
 moe_status moe_align_blocks(moe_ctx* ctx, const int32_t* topk_ids, int32_t M, int32_t* sorted_routes,
@@ -315,7 +328,8 @@ moe_status moe_align_blocks(moe_ctx* ctx, const int32_t* topk_ids, int32_t M, in
     return hip_status(e);
 }
 
-moe_status moe_expert_forward(moe_ctx* ctx, const float* h, int32_t M, const int32_t* topk_ids, const float* topk_w,
+static moe_status expert_forward_impl(bool z_ready, moe_ctx* ctx, const float* h, int32_t M,
+                                      const int32_t* topk_ids, const float* topk_w,
                               const int32_t* sorted_routes, const int32_t* block_expert, const int32_t* counts,
                               int32_t keep_channels, int32_t* kept_out, float* y, void* stream) {
     if (!ctx || M < 0 || keep_channels < 0) return MOE_ERR_INVALID_ARG;
@@ -369,7 +383,7 @@ moe_status moe_expert_forward(moe_ctx* ctx, const float* h, int32_t M, const int
         } else {
             moe::GemvJob jobs[2] = {{ctx->w.lr_basis[0], c.lr_r, ctx->zpart[0]},
                                     {ctx->w.lr_basis[1], c.lr_r, ctx->zpart[1]}};
-            {
+            if (!z_ready) {  // else computed by the routing launch of this step
                 Launch l(ctx, MOE_KERNEL_VQ_SHARED, s);
                 e = moe::launch_gemv_partials(h, M, c.H, jobs, 2, s);
                 l.done();
@@ -401,6 +415,13 @@ moe_status moe_expert_forward(moe_ctx* ctx, const float* h, int32_t M, const int
     e = moe::launch_combine(topk_ids, M, c.top_k, c.E, c.H, nchunk, ctx->down_part, y, s);
     l.done();
     return hip_status(e);
+}
+
+moe_status moe_expert_forward(moe_ctx* ctx, const float* h, int32_t M, const int32_t* topk_ids, const float* topk_w,
+                              const int32_t* sorted_routes, const int32_t* block_expert, const int32_t* counts,
+                              int32_t keep_channels, int32_t* kept_out, float* y, void* stream) {
+    return expert_forward_impl(false, ctx, h, M, topk_ids, topk_w, sorted_routes, block_expert, counts, keep_channels,
+                               kept_out, y, stream);
 }
 
 moe_status moe_decode_step(moe_ctx* ctx, const float* h, int32_t M, int32_t* topk_ids, float* topk_w,
@@ -443,11 +464,12 @@ moe_status moe_decode_step(moe_ctx* ctx, const float* h, int32_t M, int32_t* top
     }
     const int nsl = moe::router_slices(c.H, c.E);
     if (M != 1 || c.wformat != MOE_WFORMAT_DENSE || !moe::decode_fused_ok(c.H, c.E, c.top_k, nsl)) {
-        moe_status st = moe_route_align(ctx, h, M, topk_ids, topk_w, logits_out, sorted_routes, block_expert, counts,
-                                        stream);
+        const bool vq = c.wformat == MOE_WFORMAT_VQLR;  // z = D^T h in the routing launch
+        moe_status st = route_align_impl(vq, ctx, h, M, topk_ids, topk_w, logits_out, sorted_routes, block_expert,
+                                         counts, stream);
         if (st != MOE_OK) return st;
-        return moe_expert_forward(ctx, h, M, topk_ids, topk_w, sorted_routes, block_expert, counts, 0, nullptr, y,
-                                  stream);
+        return expert_forward_impl(vq, ctx, h, M, topk_ids, topk_w, sorted_routes, block_expert, counts, 0, nullptr,
+                                   y, stream);
     }
     if (!h || !topk_ids || !topk_w || !sorted_routes || !block_expert || !counts || !y || !aligned(h, 16) ||
         !aligned(y, 16))

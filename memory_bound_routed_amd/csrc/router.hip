@@ -284,7 +284,7 @@ __device__ __forceinline__ bool router_body(const float* __restrict__ h, int M, 
     router_tile<TT>(h, M, t0, H, Wr, E, tl, blockIdx.x % tl.nrs, blockIdx.x / tl.nrs, part, red);
     __builtin_amdgcn_s_waitcnt(0);  // this wave's partial stores have completed
     __syncthreads();
-    if (threadIdx.x == 0) s_last = atomicAdd(ticket + 1 + blockIdx.y, 1u) == (unsigned)(gridDim.x - 1);
+    if (threadIdx.x == 0) s_last = atomicAdd(ticket + 1 + blockIdx.y, 1u) == (unsigned)(tl.nrs * tl.ncg - 1);
     __syncthreads();
     if (!s_last) return false;
     topk_pass<true, COHERENT_IDS, kSliceBatchTiles>(t0, min(TT, M - t0), M, E, k, tl.nrs, part, bias, logits_out, ids,
@@ -321,15 +321,40 @@ router_kernel(const float* __restrict__ h, int M, int H, const uint16_t* __restr
 // group's last workgroup publishes its ids device-coherently and, once its
 // stores have completed, takes the alignment ticket; the last one aligns,
 // reading the ids device-coherently.
+//
+// Workgroups past the router's tiles (x >= its tile count) compute the
+// tiles of up to kMaxJobs skinny GEMVs on the same h instead (the VQ +
+// low-rank format's z = D^T h, as gemv_partials_kernel) and take no ticket.
 __global__ void __launch_bounds__(kThreads)
 router_align_kernel(const float* __restrict__ h, int M, int H, const uint16_t* __restrict__ Wr, int E,
                     const float* __restrict__ bias, int k, float* __restrict__ part, unsigned* __restrict__ ticket,
                     int32_t* __restrict__ ids, float* __restrict__ wts, float* __restrict__ logits_out, int b,
                     int32_t* __restrict__ sorted_routes, int32_t* __restrict__ block_expert,
-                    int32_t* __restrict__ counts, int32_t* __restrict__ err, FastDiv fE, FastDiv fk, FastDiv fb) {
+                    int32_t* __restrict__ counts, int32_t* __restrict__ err, FastDiv fE, FastDiv fk, FastDiv fb,
+                    GemvJobs jobs, int njobs) {
     extern __shared__ __align__(16) float red[];
     __shared__ TopkLds sel;
     __shared__ int s_last;
+    {
+        const RouterTiles rt(H, E);
+        int x = (int)blockIdx.x - rt.nrs * rt.ncg;
+        if (x >= 0) {
+            for (int j = 0; j < njobs; ++j) {  // uniform
+                const GemvJob& jb = jobs.job[j];
+                const RouterTiles tj(H, jb.N);
+                if (x < tj.nrs * tj.ncg) {
+                    if (M == 1)
+                        router_tile<1>(h, M, 0, H, jb.W, jb.N, tj, x % tj.nrs, x / tj.nrs, jb.part, red);
+                    else
+                        router_tile<kTokTile>(h, M, blockIdx.y * kTokTile, H, jb.W, jb.N, tj, x % tj.nrs,
+                                              x / tj.nrs, jb.part, red);
+                    return;
+                }
+                x -= tj.nrs * tj.ncg;
+            }
+            return;
+        }
+    }
     pin_arg(bias); pin_arg(k); pin_arg(E); pin_arg(M); pin_arg(ids); pin_arg(wts); pin_arg(logits_out);
     pin_arg(ticket); pin_arg(part); pin_arg(b); pin_arg(sorted_routes); pin_arg(block_expert); pin_arg(counts);
     pin_arg(err); pin_arg(fE.m); pin_arg(fE.s); pin_arg(fk.m); pin_arg(fk.s); pin_arg(fb.m); pin_arg(fb.s);
@@ -461,14 +486,21 @@ hipError_t launch_router_partials(const float* h, int M, int H, const uint16_t* 
 hipError_t launch_router_align(const float* h, int M, int H, const uint16_t* Wr, int E, const float* bias, int k,
                                float* part, unsigned* ticket, int32_t* ids, float* wts, float* logits_out, int b,
                                int32_t* sorted_routes, int32_t* block_expert, int32_t* counts, int32_t* err,
-                               hipStream_t stream) {
-    if (M < 1 || E % 8 != 0) return hipErrorInvalidValue;
+                               hipStream_t stream, const GemvJob* jobs, int njobs) {
+    if (M < 1 || E % 8 != 0 || njobs < 0 || njobs > kMaxJobs || (njobs > 0 && !jobs)) return hipErrorInvalidValue;
     const size_t la = align_lds_bytes(M * k, E);
-    const size_t lds = router_lds_bytes(H, E) > la ? router_lds_bytes(H, E) : la;
-    MOE_LAUNCH(router_align_kernel, dim3(router_grid(H, E), router_groups(M)), dim3(kThreads), lds, stream, h, M, H,
-               Wr, E, bias,
-                       k, part, ticket, ids, wts, logits_out, b, sorted_routes, block_expert, counts, err,
-                       FastDiv((uint32_t)E), FastDiv((uint32_t)k), FastDiv((uint32_t)b));
+    size_t lds = router_lds_bytes(H, E) > la ? router_lds_bytes(H, E) : la;
+    GemvJobs js{};
+    int grid = router_grid(H, E);
+    for (int i = 0; i < njobs; ++i) {
+        if (jobs[i].N < 8 || jobs[i].N % 8) return hipErrorInvalidValue;
+        js.job[i] = jobs[i];
+        lds = tile_lds_bytes(H, jobs[i].N) > lds ? tile_lds_bytes(H, jobs[i].N) : lds;
+        grid += router_grid(H, jobs[i].N);
+    }
+    MOE_LAUNCH(router_align_kernel, dim3(grid, router_groups(M)), dim3(kThreads), lds, stream, h, M, H, Wr, E, bias,
+               k, part, ticket, ids, wts, logits_out, b, sorted_routes, block_expert, counts, err,
+               FastDiv((uint32_t)E), FastDiv((uint32_t)k), FastDiv((uint32_t)b), js, njobs);
     return hipGetLastError();
 }
 
