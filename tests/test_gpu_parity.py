@@ -451,7 +451,8 @@ def test_vq_block_lengths_ragged(mb, d, H, I, r, K):
 
 
 @pytest.mark.parametrize("name", ["dense_h2048_i768_e128_k8_m8", "dense_h2048_i768_e128_k8_m16",
-                                  "vqlr_h2048_i768_e128_k8_m8_d8_K256_r64", "vqlr_h2048_i768_e128_k8_m16_d8_K256_r64"])
+                                  "vqlr_h2048_i768_e128_k8_m8_d8_K256_r64", "vqlr_h2048_i768_e128_k8_m16_d8_K256_r64",
+                                  "vqlr_h2048_i768_e128_k8_m4_d8_K256_r64"])
 def test_batch_8_16_full_size(mb, name):
     """Batch 8 and 16 decode at full size (dense bf16 and VQ + low rank): the
     plan, the router (certified ids) and y against the oracle, stage-isolated,
