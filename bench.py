@@ -3,15 +3,22 @@
 
     python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload NAME]
 
-A step is one pass of the whole hot path over one token batch:
-moe_route_topk + moe_align_blocks + moe_expert_forward on one layer.  The
-default workload is the Qwen3-30B-A3B-shaped batch-1 layer (H=2048, I=768,
-E=128, top-8): 48 independent layers are resident in HBM and step i runs on
-layer i mod 48, so every step streams its routed weights cold from HBM
-(47 x 75.5 MB are read between two visits of a layer, far beyond the 256 MB
-Infinity Cache).  The steps of one 48-layer cycle are captured in a HIP graph
-(the library never allocates or synchronises inside a call) and the graph is
-replayed; eager (uncaptured) timing is reported beside it.
+A step is one moe_decode_step call on one layer: for the default batch-1
+dense workload that is three kernels (the router GEMV's row-slice partials,
+the routing expert kernel that takes the top-k itself and streams the
+experts' gate/up/down rows, and the fixed-order combine).  The default
+workload is the Qwen3-30B-A3B-shaped batch-1 layer (H=2048, I=768, E=128,
+top-8): 48 independent layers are resident in HBM and step i runs on layer
+i mod 48, so every step streams its routed weights cold from HBM (47 x 75.5 MB
+are read between two visits of a layer, far beyond the 256 MB Infinity
+Cache).
+
+Timing: the steps are captured in HIP graphs (the library never allocates or
+synchronises inside a call) of at most one 48-layer cycle each; the timed
+region is exactly K steps after W warm-up steps, every graph replay bracketed
+by HIP events.  A statistics pass then replays the 48-step cycle at least 7
+times and reports the median and min-max of the per-step time; eager
+(uncaptured) timing is reported beside it.
 
 Printed: one JSON line with the metric, the per-kernel roofline of the
 dominant kernel (durations from HIP events recorded by the library on its
@@ -198,18 +205,47 @@ def run_steps(layers, hs, M, keep, order):
         L.decode_step(hs[i % len(hs)], M, keep=keep)
 
 
-def cpu_baseline(wl, budget_s=15.0, max_steps=40):
-    """The fp64 oracle timed on the host (single BLAS thread) on a bounded
-    sample: steps over the first 4 layers, each layer's routed experts drawn
-    from the seeded generator beforehand (generation is not timed)."""
+def host_info():
+    """Host CPU model and the cores this process may use."""
+    model = "unknown"
+    try:
+        for line in open("/proc/cpuinfo"):
+            if line.startswith("model name"):
+                model = line.split(":", 1)[1].strip()
+                break
+    except OSError:
+        pass
+    cores = len(os.sched_getaffinity(0)) if hasattr(os, "sched_getaffinity") else os.cpu_count()
+    cores = int(cores or 1)
+    omp = os.environ.get("OMP_NUM_THREADS", "")
+    if omp.isdigit() and int(omp) > 0:  # the host share this process is given
+        cores = min(cores, int(omp))
+    return model, cores
+
+
+def cpu_baseline(wl, budget_s=10.0, max_steps=40):
+    """The fp64 oracle timed on the host on a bounded sample: steps over the
+    first 4 layers, each layer's routed experts drawn from the seeded
+    generator beforehand (generation is not timed); once with one BLAS
+    thread, once with a thread per usable host core."""
     import synth
     import oracle as O
     from threadpoolctl import threadpool_limits
+    model, cores = host_info()
+    sample = _cpu_sample(wl, synth, O)
     with threadpool_limits(limits=1):
-        return _cpu_baseline(wl, budget_s, max_steps, synth, O)
+        one = _cpu_time(wl, sample, budget_s, max_steps, O)
+    with threadpool_limits(limits=cores):
+        allc = _cpu_time(wl, sample, budget_s, max_steps, O)
+    return {"value": allc["value"], "unit": "GB/s", "us_per_step": allc["us_per_step"], "cores": cores,
+            "kind": "oracle", "cpu_model": model, "nproc": cores,
+            "single_core": {"value": one["value"], "unit": "GB/s", "us_per_step": one["us_per_step"], "cores": 1,
+                            "steps": one["steps"]},
+            "sample": "%d steps of %s cycling over %d host-resident layers (only routed experts drawn); fp64 numpy, "
+                      "BLAS threads = %d (single_core: 1)" % (allc["steps"], wl.name, len(sample), cores)}
 
 
-def _cpu_baseline(wl, budget_s, max_steps, synth, O):
+def _cpu_sample(wl, synth, O):
     keep = wl.keep
     layers = []
     for L in range(min(4, wl.layers)):
@@ -220,18 +256,20 @@ def _cpu_baseline(wl, budget_s, max_steps, synth, O):
         full = synth.layer_inputs(wl, L, experts=ex)
         norms = O.channel_norms(full["w_gate"], full["w_up"], full["w_down"], experts=ex) if keep else None
         layers.append((full, norms, len(ex)))
+    return layers
+
+
+def _cpu_time(wl, layers, budget_s, max_steps, O):
+    keep = wl.keep
     t_total, n, bytes_total = 0.0, 0, 0
     while n < max_steps and t_total < budget_s:
         full, norms, nex = layers[n % len(layers)]
         t0 = time.perf_counter()
         O.moe_step(full, wl.k, keep=keep, norms=norms)
         t_total += time.perf_counter() - t0
-        bytes_total += (keep * 3 * wl.H * 2) if keep else routed_bytes_per_step(wl, nex)
+        bytes_total += (keep * 3 * wl.H * 2 * wl.M) if keep else routed_bytes_per_step(wl, nex)
         n += 1
-    return {"value": round(bytes_total / t_total / 1e9, 4), "unit": "GB/s",
-            "us_per_step": round(t_total / n * 1e6, 1), "cores": 1, "kind": "oracle",
-            "sample": "%d steps of %s cycling over %d host-resident layers (only routed experts drawn); "
-                      "fp64 numpy, one BLAS thread" % (n, wl.name, len(layers))}
+    return {"value": round(bytes_total / t_total / 1e9, 4), "us_per_step": round(t_total / n * 1e6, 1), "steps": n}
 
 
 def main():
@@ -283,10 +321,8 @@ def main():
         return
 
     cycle = list(range(n_h))
-    reps = max(1, round(args.steps / len(cycle)))
-    wreps = max(1, round(args.warmup / len(cycle)))
-    K = reps * len(cycle)
-    W = wreps * len(cycle)
+    K = max(1, args.steps)
+    W = max(0, args.warmup)
 
     # distinct routed experts per layer for the byte count: route every layer once (eager)
     n_ex = []
@@ -295,31 +331,65 @@ def main():
         L.route(hs[i], M)
         n_ex.append(len(set(L.ids[:M].flatten().tolist())))
     torch.cuda.synchronize()
-    bytes_per_cycle = sum((keep * 3 * wl.H * 2 * M) if keep else routed_bytes_per_step(wl, n) for n in n_ex)
+    step_bytes = [(keep * 3 * wl.H * 2 * M) if keep else routed_bytes_per_step(wl, n) for n in n_ex]
 
-    # ---- graph-captured steps
+    # ---- graph-captured steps: graphs of one 48-step cycle (and a shorter
+    # one for a remainder), step i of a run on layer i mod 48
     s = torch.cuda.Stream()
     s.wait_stream(torch.cuda.current_stream())
     with torch.cuda.stream(s):
         run_steps(layers, hs, M, keep, cycle)  # eager warm-up on the capture stream
     torch.cuda.current_stream().wait_stream(s)
     torch.cuda.synchronize()
-    g = torch.cuda.CUDAGraph()
-    with torch.cuda.graph(g):
-        run_steps(layers, hs, M, keep, cycle)
-    torch.cuda.synchronize()
-    for _ in range(wreps):
-        g.replay()
+    graphs = {}
+
+    def graph_of(n):
+        if n not in graphs:
+            g = torch.cuda.CUDAGraph()
+            with torch.cuda.graph(g):
+                run_steps(layers, hs, M, keep, range(n))
+            torch.cuda.synchronize()
+            graphs[n] = g
+        return graphs[n]
+
+    def blocks_of(n):
+        return [len(cycle)] * (n // len(cycle)) + ([n % len(cycle)] if n % len(cycle) else [])
+
+    def timed_replays(sizes):
+        ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in sizes]
+        gs = [graph_of(n) for n in sizes]
+        torch.cuda.synchronize()
+        for (a, b), g in zip(ev, gs):
+            a.record()
+            g.replay()
+            b.record()
+        torch.cuda.synchronize()
+        return [a.elapsed_time(b) for a, b in ev]
+
+    for n in blocks_of(W):
+        graph_of(n).replay()
     torch.cuda.synchronize()
     t0 = torch.cuda.Event(enable_timing=True)
     t1 = torch.cuda.Event(enable_timing=True)
+    sizes = blocks_of(K)
+    gs = [graph_of(n) for n in sizes]
+    torch.cuda.synchronize()
     t0.record()
-    for _ in range(reps):
+    for g in gs:
         g.replay()
     t1.record()
     torch.cuda.synchronize()
     ms_graph = t0.elapsed_time(t1)
     ms_per_step = ms_graph / K
+    bytes_timed = sum(step_bytes[i % len(cycle)] for i in range(K))
+
+    # statistics: at least 7 replays of the 48-step cycle, each timed
+    n_stat = max(7, K // len(cycle))
+    per_step = sorted(t / len(cycle) * 1e3 for t in timed_replays([len(cycle)] * n_stat))
+    stats = {"replays": n_stat, "steps_per_replay": len(cycle),
+             "median_us_per_step": round(float(np.median(per_step)), 3),
+             "min_us_per_step": round(per_step[0], 3), "max_us_per_step": round(per_step[-1], 3)}
+    reps = max(1, round(K / len(cycle)))
 
     # ---- eager steps (no graph)
     run_steps(layers, hs, M, keep, cycle)
@@ -362,7 +432,7 @@ def main():
     expert_us = sum(kernels[k]["avg_us"] * kernels[k]["launches"] for k in expert_kernels) / K
 
     us_step = ms_per_step * 1e3
-    gbs = bytes_per_cycle * reps / (ms_graph / 1e3) / 1e9
+    gbs = bytes_timed / (ms_graph / 1e3) / 1e9
     out = {
         "metric": METRIC,
         "value": round(gbs, 2),
@@ -383,9 +453,10 @@ def main():
                 "N(0,0.02) bf16 weights, N(0,1) fp32 hidden states" % (n_layers - 1),
         "config": {"workload": wl.name, "H": wl.H, "I": wl.I, "E": wl.E, "top_k": wl.k, "tokens": M,
                    "block_b": wl.block_b, "layers_rotated": n_layers, "keep_channels": keep or None,
-                   "routed_bytes_per_step": int(bytes_per_cycle / len(cycle)),
-                   "avg_distinct_experts": round(avg_ex, 2), "timing": "HIP graph of one 48-step layer cycle, "
-                   "replayed %d times; HIP events around all replays" % reps},
+                   "routed_bytes_per_step": int(sum(step_bytes) / len(cycle)),
+                   "avg_distinct_experts": round(avg_ex, 2), "timing": "exactly %d steps as HIP-graph replays of <= %d steps "
+                   "between two HIP events after %d warm-up steps" % (K, len(cycle), W)},
+        "timing_stats": stats,
         "kernels": kernels,
         "roofline": {
             "kernel": dominant,

@@ -265,6 +265,15 @@ moe_status moe_decode_step(moe_ctx *ctx, const float *h, int32_t M, int32_t *top
 /* Rows moe_align_blocks may write: M*k + min(E, M*k)*(b-1); -1 on bad args. */
 int32_t moe_align_capacity(int32_t M, int32_t k, int32_t E, int32_t b);
 
+/*
+ * Bytes of device workspace a context of `cfg` with max_tokens = max_tokens
+ * allocates (router and VQ partials, the p buffer of the split schedule, down
+ * partials, channel-selection lists and partials, tickets); host only, no GPU
+ * needed.  -1 when cfg is NULL or the configuration (with that max_tokens)
+ * would be rejected by moe_create.
+ */
+int64_t moe_workspace_bytes(const moe_config *cfg, int32_t max_tokens);
+
 /* Static text for a status code. */
 const char *moe_status_string(moe_status s);
 

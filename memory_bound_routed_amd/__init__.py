@@ -10,305 +10,19 @@ Build the library in-tree first:  python -m memory_bound_routed_amd._build
 """
 from __future__ import annotations
 
-import ctypes
 import os
-from typing import Dict, Optional, Sequence, Tuple
+import sys
 
 _PKG = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(_PKG, "libmoe.so")
 
-if not os.path.exists(LIB_PATH):
+# While `python -m memory_bound_routed_amd._build` locates its target, the
+# interpreter imports this package with sys.argv == ['-m'] (argv[0] becomes
+# the script path only once the module is found).  That is the one import
+# allowed without the library: it is the command that builds it.
+_BUILDING = not os.path.exists(LIB_PATH) and sys.argv[:1] == ["-m"]
+if not os.path.exists(LIB_PATH) and not _BUILDING:
     raise ImportError("libmoe.so is not built at %s; run `python -m memory_bound_routed_amd._build`" % LIB_PATH)
-# torch first: it loads its own HIP runtime, which libmoe.so must then bind to
-# (the same soname); loaded the other way round, the process would hold two
-# HIP runtimes and torch's device memory would be foreign to the library's.
-try:
-    import torch  # noqa: F401
-except ImportError:  # the library can still be loaded (host-side checks)
-    pass
-_lib = ctypes.CDLL(LIB_PATH)
-
-# ---------------------------------------------------------------- C types
-
-MOE_OK, MOE_ERR_INVALID_ARG, MOE_ERR_UNSUPPORTED, MOE_ERR_CAPACITY, MOE_ERR_HIP, MOE_ERR_DEVICE = range(6)
-MOE_WFORMAT_DENSE, MOE_WFORMAT_VQLR = 0, 1
-DEVERR_BAD_ROUTE_ID, DEVERR_BAD_PLAN, DEVERR_BAD_BLOCK_EXPERT, DEVERR_BAD_COUNTS = 1, 2, 4, 8
-KERNELS = ["router", "vq_shared", "align", "gateup", "gateup_vqlr", "down", "combine",
-           "chan_select", "chan_gather", "chan_combine", "expert_fused", "router_align", "router_gemv",
-           "decode_fused"]
-MOE_KERNEL_COUNT = len(KERNELS)
-
-# Every symbol include/moe.h declares (checked by the CPU test suite).
-EXPORTS = ["moe_create", "moe_destroy", "moe_route_topk", "moe_route_align", "moe_align_blocks", "moe_expert_forward",
-           "moe_decode_step",
-           "moe_align_capacity", "moe_status_string", "moe_read_device_error", "moe_channel_norms", "moe_channel_ranks",
-           "moe_validate_plan", "moe_profile_enable", "moe_profile_read", "moe_kernel_name"]
-
-
-class moe_config(ctypes.Structure):
-    _fields_ = [(n, ctypes.c_int32) for n in
-                ("H", "I", "E", "top_k", "block_b", "max_tokens", "wformat", "vq_d", "vq_K", "lr_r", "max_keep")]
-
-
-_vp = ctypes.c_void_p
-
-
-class moe_weights(ctypes.Structure):
-    _fields_ = [("router_w", _vp), ("router_bias", _vp), ("w_gate", _vp), ("w_up", _vp), ("w_down", _vp),
-                ("chan_norm", _vp), ("chan_rank", _vp), ("lr_basis", _vp * 2), ("lr_coef", _vp * 2), ("vq_book", _vp * 2),
-                ("vq_idx", _vp * 2)]
-
-
-_i32, _pi32 = ctypes.c_int32, ctypes.POINTER(ctypes.c_int32)
-_sig = {
-    "moe_create": (_i32, [ctypes.POINTER(moe_config), ctypes.POINTER(moe_weights), ctypes.POINTER(_vp)]),
-    "moe_destroy": (None, [_vp]),
-    "moe_route_topk": (_i32, [_vp, _vp, _i32, _vp, _vp, _vp, _vp]),
-    "moe_align_blocks": (_i32, [_vp, _vp, _i32, _vp, _vp, _vp, _vp]),
-    "moe_route_align": (_i32, [_vp, _vp, _i32, _vp, _vp, _vp, _vp, _vp, _vp, _vp]),
-    "moe_expert_forward": (_i32, [_vp, _vp, _i32, _vp, _vp, _vp, _vp, _vp, _i32, _vp, _vp, _vp]),
-    "moe_decode_step": (_i32, [_vp, _vp, _i32, _vp, _vp, _vp, _vp, _vp, _vp, _i32, _vp, _vp, _vp]),
-    "moe_align_capacity": (_i32, [_i32, _i32, _i32, _i32]),
-    "moe_status_string": (ctypes.c_char_p, [_i32]),
-    "moe_read_device_error": (_i32, [_vp, _pi32, _i32]),
-    "moe_channel_norms": (_i32, [ctypes.POINTER(moe_config), _vp, _vp, _vp, _vp, _vp]),
-    "moe_channel_ranks": (_i32, [ctypes.POINTER(moe_config), _vp, _vp, _vp]),
-    "moe_validate_plan": (_i32, [_vp, _i32, _i32, _i32, _i32, _vp, _vp, _vp, _pi32]),
-    "moe_profile_enable": (_i32, [_vp, _i32]),
-    "moe_profile_read": (_i32, [_vp, ctypes.POINTER(ctypes.c_double), ctypes.POINTER(ctypes.c_int64)]),
-    "moe_kernel_name": (ctypes.c_char_p, [_i32]),
-}
-for _name, (_res, _args) in _sig.items():
-    _f = getattr(_lib, _name)
-    _f.restype = _res
-    _f.argtypes = _args
-
-
-class MoeError(RuntimeError):
-    def __init__(self, status: int, where: str):
-        self.status = status
-        super().__init__("%s: %s (status %d)" % (where, moe_status_string(status), status))
-
-
-def _check(status: int, where: str) -> None:
-    if status != MOE_OK:
-        raise MoeError(status, where)
-
-
-def _ptr(t) -> Optional[int]:
-    """Device or host address of a tensor / array (None stays NULL)."""
-    if t is None:
-        return None
-    if hasattr(t, "data_ptr"):
-        return t.data_ptr()
-    if hasattr(t, "ctypes"):
-        return t.ctypes.data
-    return int(t)
-
-
-def _stream(stream) -> Optional[int]:
-    if stream is None:
-        import torch
-        return torch.cuda.current_stream().cuda_stream
-    if hasattr(stream, "cuda_stream"):
-        return stream.cuda_stream
-    return int(stream)
-
-
-# ---------------------------------------------------------------- entry points
-
-def moe_status_string(status: int) -> str:
-    return _lib.moe_status_string(status).decode()
-
-
-def moe_kernel_name(kernel: int) -> Optional[str]:
-    s = _lib.moe_kernel_name(kernel)
-    return s.decode() if s else None
-
-
-def moe_align_capacity(M: int, k: int, E: int, b: int) -> int:
-    return _lib.moe_align_capacity(M, k, E, b)
-
-
-def make_config(H, I, E, top_k, block_b=8, max_tokens=1, wformat=MOE_WFORMAT_DENSE, vq_d=0, vq_K=0, lr_r=0,
-                max_keep=0) -> moe_config:
-    return moe_config(H, I, E, top_k, block_b, max_tokens, wformat, vq_d, vq_K, lr_r, max_keep)
-
-
-def make_weights(router_w, w_down, router_bias=None, w_gate=None, w_up=None, chan_norm=None, chan_rank=None,
-                 lr_basis=(None, None), lr_coef=(None, None), vq_book=(None, None),
-                 vq_idx=(None, None)) -> moe_weights:
-    w = moe_weights()
-    w.router_w, w.router_bias, w.w_gate, w.w_up, w.w_down, w.chan_norm, w.chan_rank = (
-        _ptr(router_w), _ptr(router_bias), _ptr(w_gate), _ptr(w_up), _ptr(w_down), _ptr(chan_norm),
-        _ptr(chan_rank))
-    for P in range(2):
-        w.lr_basis[P], w.lr_coef[P] = _ptr(lr_basis[P]), _ptr(lr_coef[P])
-        w.vq_book[P], w.vq_idx[P] = _ptr(vq_book[P]), _ptr(vq_idx[P])
-    return w
-
-
-def moe_create(cfg: moe_config, weights: moe_weights) -> int:
-    out = _vp()
-    _check(_lib.moe_create(ctypes.byref(cfg), ctypes.byref(weights), ctypes.byref(out)), "moe_create")
-    return out.value
-
-
-def moe_create_status(cfg: Optional[moe_config], weights: Optional[moe_weights]) -> Tuple[int, Optional[int]]:
-    """Raw status variant (for tests of the failure paths)."""
-    out = _vp()
-    st = _lib.moe_create(ctypes.byref(cfg) if cfg is not None else None,
-                         ctypes.byref(weights) if weights is not None else None, ctypes.byref(out))
-    return st, out.value
-
-
-def moe_destroy(ctx: Optional[int]) -> None:
-    _lib.moe_destroy(ctx)
-
-
-def moe_route_topk(ctx, h, M, topk_ids, topk_w, logits_out=None, stream=None) -> None:
-    _check(_lib.moe_route_topk(ctx, _ptr(h), M, _ptr(topk_ids), _ptr(topk_w), _ptr(logits_out), _stream(stream)),
-           "moe_route_topk")
-
-
-def moe_route_align(ctx, h, M, topk_ids, topk_w, logits_out, sorted_routes, block_expert, counts, stream=None) -> None:
-    _check(_lib.moe_route_align(ctx, _ptr(h), M, _ptr(topk_ids), _ptr(topk_w), _ptr(logits_out), _ptr(sorted_routes),
-                                _ptr(block_expert), _ptr(counts), _stream(stream)), "moe_route_align")
-
-
-def moe_align_blocks(ctx, topk_ids, M, sorted_routes, block_expert, counts, stream=None) -> None:
-    _check(_lib.moe_align_blocks(ctx, _ptr(topk_ids), M, _ptr(sorted_routes), _ptr(block_expert), _ptr(counts),
-                                 _stream(stream)), "moe_align_blocks")
-
-
-def moe_expert_forward(ctx, h, M, topk_ids, topk_w, sorted_routes, block_expert, counts, keep_channels, kept_out, y,
-                       stream=None) -> None:
-    _check(_lib.moe_expert_forward(ctx, _ptr(h), M, _ptr(topk_ids), _ptr(topk_w), _ptr(sorted_routes),
-                                   _ptr(block_expert), _ptr(counts), keep_channels, _ptr(kept_out), _ptr(y),
-                                   _stream(stream)), "moe_expert_forward")
-
-
-def moe_decode_step(ctx, h, M, topk_ids, topk_w, logits_out, sorted_routes, block_expert, counts, keep_channels,
-                    kept_out, y, stream=None) -> None:
-    _check(_lib.moe_decode_step(ctx, _ptr(h), M, _ptr(topk_ids), _ptr(topk_w), _ptr(logits_out), _ptr(sorted_routes),
-                                _ptr(block_expert), _ptr(counts), keep_channels, _ptr(kept_out), _ptr(y),
-                                _stream(stream)), "moe_decode_step")
-
-
-def moe_read_device_error(ctx, clear: bool = True) -> int:
-    flags = _i32(0)
-    st = _lib.moe_read_device_error(ctx, ctypes.byref(flags), 1 if clear else 0)
-    if st not in (MOE_OK, MOE_ERR_DEVICE):
-        raise MoeError(st, "moe_read_device_error")
-    return flags.value
-
-
-def moe_channel_norms(cfg: moe_config, w_gate, w_up, w_down, norms, stream=None) -> None:
-    _check(_lib.moe_channel_norms(ctypes.byref(cfg), _ptr(w_gate), _ptr(w_up), _ptr(w_down), _ptr(norms),
-                                  _stream(stream)), "moe_channel_norms")
-
-
-def moe_channel_ranks(cfg: moe_config, norms, ranks, stream=None) -> None:
-    _check(_lib.moe_channel_ranks(ctypes.byref(cfg), _ptr(norms), _ptr(ranks), _stream(stream)), "moe_channel_ranks")
-
-
-def moe_validate_plan(topk_ids, M, k, E, b, sorted_routes, block_expert, counts) -> Tuple[int, int]:
-    """Host check of a plan (numpy int32 arrays).  Returns (status, reason)."""
-    import numpy as np
-    arrs = [np.ascontiguousarray(a, dtype=np.int32) if a is not None else None
-            for a in (topk_ids, sorted_routes, block_expert, counts)]
-    reason = _i32(0)
-    st = _lib.moe_validate_plan(_ptr(arrs[0]), M, k, E, b, _ptr(arrs[1]), _ptr(arrs[2]), _ptr(arrs[3]),
-                                ctypes.byref(reason))
-    return st, reason.value
-
-
-def moe_profile_enable(ctx, enable: bool = True) -> None:
-    _check(_lib.moe_profile_enable(ctx, 1 if enable else 0), "moe_profile_enable")
-
-
-def moe_profile_read(ctx) -> Dict[str, Tuple[float, int]]:
-    """{kernel name: (total ms, launches)} of the recorded launches (synchronises)."""
-    ms = (ctypes.c_double * MOE_KERNEL_COUNT)()
-    n = (ctypes.c_int64 * MOE_KERNEL_COUNT)()
-    _check(_lib.moe_profile_read(ctx, ms, n), "moe_profile_read")
-    return {KERNELS[i]: (ms[i], n[i]) for i in range(MOE_KERNEL_COUNT) if n[i]}
-
-
-# ---------------------------------------------------------------- convenience
-
-class Layer:
-    """One MoE layer bound to device tensors: owns a context and the per-call
-    buffers, and runs the three calls of a step on the current stream."""
-
-    def __init__(self, cfg: moe_config, tensors: Dict[str, object]):
-        import torch
-        self.cfg = cfg
-        self.tensors = tensors  # keeps the borrowed weights alive
-        t = tensors
-        self.weights = make_weights(
-            t["router_w"], t["w_down"], router_bias=t.get("router_bias"), w_gate=t.get("w_gate"),
-            w_up=t.get("w_up"), chan_norm=t.get("chan_norm"), chan_rank=t.get("chan_rank"),
-            lr_basis=(t.get("lr_basis_gate"), t.get("lr_basis_up")),
-            lr_coef=(t.get("lr_coef_gate"), t.get("lr_coef_up")),
-            vq_book=(t.get("vq_book_gate"), t.get("vq_book_up")),
-            vq_idx=(t.get("vq_idx_gate"), t.get("vq_idx_up")))
-        self.ctx = moe_create(cfg, self.weights)
-        dev = t["router_w"].device
-        M, k = cfg.max_tokens, cfg.top_k
-        cap = moe_align_capacity(M, k, cfg.E, cfg.block_b)
-        i32 = torch.int32
-        self.ids = torch.empty((M, k), dtype=i32, device=dev)
-        self.w = torch.empty((M, k), dtype=torch.float32, device=dev)
-        self.logits = torch.empty((M, cfg.E), dtype=torch.float32, device=dev)
-        self.sorted_routes = torch.full((max(cap, 1),), -7, dtype=i32, device=dev)
-        self.block_expert = torch.full((max(cap // cfg.block_b, 1),), -7, dtype=i32, device=dev)
-        self.counts = torch.zeros(2, dtype=i32, device=dev)
-        self.y = torch.empty((M, cfg.H), dtype=torch.float32, device=dev)
-        self.kept = torch.empty((M, max(cfg.max_keep, 1)), dtype=i32, device=dev)
-
-    def route(self, h, M, logits=False, stream=None):
-        moe_route_topk(self.ctx, h, M, self.ids, self.w, self.logits if logits else None, stream)
-
-    def align(self, M, ids=None, stream=None):
-        moe_align_blocks(self.ctx, self.ids if ids is None else ids, M, self.sorted_routes, self.block_expert,
-                         self.counts, stream)
-
-    def forward(self, h, M, keep=0, ids=None, w=None, plan=None, stream=None, y=None):
-        sr, be, ct = plan if plan is not None else (self.sorted_routes, self.block_expert, self.counts)
-        moe_expert_forward(self.ctx, h, M, self.ids if ids is None else ids, self.w if w is None else w,
-                           sr, be, ct, keep, self.kept if keep else None, self.y if y is None else y, stream)
-
-    def route_align(self, h, M, logits=False, stream=None):
-        moe_route_align(self.ctx, h, M, self.ids, self.w, self.logits if logits else None, self.sorted_routes,
-                        self.block_expert, self.counts, stream)
-
-    def decode_step(self, h, M, keep=0, logits=False, stream=None):
-        """One decode step in one call (moe_decode_step)."""
-        moe_decode_step(self.ctx, h, M, self.ids, self.w, self.logits if logits else None, self.sorted_routes,
-                        self.block_expert, self.counts, keep, self.kept if keep else None, self.y, stream)
-        return self.y[:M]
-
-    def step(self, h, M, keep=0, stream=None, fused_route_align=True):
-        """One decode step: routing, alignment (not needed by the channel-sparse
-        mode) and the experts, as separate calls."""
-        if keep:
-            self.route(h, M, stream=stream)
-        elif fused_route_align:
-            self.route_align(h, M, stream=stream)
-        else:
-            self.route(h, M, stream=stream)
-            self.align(M, stream=stream)
-        self.forward(h, M, keep=keep, stream=stream)
-        return self.y[:M]
-
-    def close(self):
-        if self.ctx:
-            moe_destroy(self.ctx)
-            self.ctx = None
-
-    def __del__(self):
-        try:
-            self.close()
-        except Exception:
-            pass
+if not _BUILDING:
+    from ._binding import *  # noqa: F401,F403  (the entry points, Layer, constants)
+    from ._binding import _lib  # noqa: F401  (the loaded library, for the ABI tests)

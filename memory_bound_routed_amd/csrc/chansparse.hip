@@ -6,8 +6,11 @@
 //
 // The score of candidate (slot s, channel j) is a_s * n[e_s][j]: the exact
 // fp64 product of two fp32 values, so selection needs no rounding decision.
-// The K best are found with an MSD radix select on the 64-bit order key of
-// the score; ties at the threshold go to the lower expert id, then channel.
+// With positive affinities the K best form a prefix of each routed expert's
+// channels ordered by decreasing norm (an order computed once per layer), so
+// each (slot, token) workgroup finds its own prefix length by binary searches
+// over the k orders instead of sorting; ties go to the lower expert id, then
+// channel, then slot.
 #include <algorithm>
 #include <climits>
 

@@ -22,14 +22,12 @@ struct Rec {
 
 }  // namespace
 
-struct moe_ctx {
-    moe_config cfg;
-    moe_weights w;
-    int device = 0;
-    void* ws = nullptr;
-    size_t ws_bytes = 0;
-    int32_t* err = nullptr;
-    unsigned* ticket = nullptr;        // router last-workgroup ticket (zero between calls)
+// Device buffers of one call sequence (partials, tickets, lists); every
+// kernel takes them as arguments.  A context owns one, laid out for its
+// max_tokens by workspace_layout.
+struct Workspace {
+    int32_t* err = nullptr;            // sticky device error flags
+    unsigned* ticket = nullptr;        // router last-workgroup tickets (zero between calls)
     float* router_part = nullptr;
     float* zpart[2] = {nullptr, nullptr};
     float* p = nullptr;
@@ -37,6 +35,15 @@ struct moe_ctx {
     int32_t* slot_cnt = nullptr;   // channel-sparse: kept channels per (token, slot), int32 [MT][k]
     int32_t* slot_kept = nullptr;  // ... and their channels, int32 [MT][k][I]
     float* chan_part = nullptr;
+};
+
+struct moe_ctx {
+    moe_config cfg;
+    moe_weights w;
+    int device = 0;
+    void* ws_mem = nullptr;
+    size_t ws_bytes = 0;
+    Workspace ws;
     bool prof = false;
     std::vector<Rec> recs;
     std::vector<hipEvent_t> pool;
@@ -103,6 +110,53 @@ moe_status check_weights(const moe_config* c, const moe_weights* w) {
     return MOE_OK;
 }
 
+// Byte size of the workspace of `c` for calls of up to MT tokens; with a
+// base address, also the buffer addresses inside it (256-byte aligned).
+size_t workspace_layout(const moe_config& c, size_t MT, char* base, Workspace* ws) {
+    const size_t R = MT * c.top_k;
+    const size_t zsl = c.wformat == MOE_WFORMAT_VQLR ? moe::gemv_slices(c.H, c.lr_r) : 0;
+    // down partials: one chunk per route on the split path; the fused path
+    // (one token) writes dense_chunks of them for each of its top_k routes
+    size_t down = R * (size_t)moe::down_chunks(c.I) * c.H;
+    if (moe::dense_uses_fused(1, c.H)) {
+        const size_t f = (size_t)c.top_k * moe::dense_chunks(1, c.H, c.I) * c.H;
+        down = f > down ? f : down;
+    }
+    const size_t nchan = c.max_keep > 0 ? (c.max_keep + kChanChunk - 1) / kChanChunk : 0;
+    const size_t sizes[8] = {
+        64 + sizeof(unsigned) * (1 + (size_t)moe::router_groups((int)MT)),  // err flag, router tickets
+        sizeof(float) * moe::gemv_slices(c.H, c.E) * MT * c.E,          // router partials
+        sizeof(float) * zsl * MT * c.lr_r,                              // z = D^T h partials (gate)
+        sizeof(float) * zsl * MT * c.lr_r,                              // z partials (up)
+        sizeof(float) * R * c.I,                                        // p
+        sizeof(float) * down,                                           // down partials
+        c.max_keep > 0 ? sizeof(int32_t) * MT * c.top_k * (1 + (size_t)c.I) : 0,  // per-slot kept lists
+        sizeof(float) * MT * nchan * c.H,                               // channel partials
+    };
+    size_t off[8], total = 0;
+    for (int i = 0; i < 8; ++i) {
+        off[i] = total;
+        total += (sizes[i] + 255) & ~(size_t)255;
+    }
+    if (base && ws) {
+        ws->err = reinterpret_cast<int32_t*>(base + off[0]);
+        ws->ticket = reinterpret_cast<unsigned*>(base + off[0] + 64);
+        ws->router_part = reinterpret_cast<float*>(base + off[1]);
+        ws->zpart[0] = reinterpret_cast<float*>(base + off[2]);
+        ws->zpart[1] = reinterpret_cast<float*>(base + off[3]);
+        ws->p = reinterpret_cast<float*>(base + off[4]);
+        ws->down_part = reinterpret_cast<float*>(base + off[5]);
+        ws->slot_cnt = reinterpret_cast<int32_t*>(base + off[6]);
+        ws->slot_kept = ws->slot_cnt + MT * c.top_k;
+        ws->chan_part = reinterpret_cast<float*>(base + off[7]);
+    }
+    return total;
+}
+
+// Header bytes of the workspace that must be zero before the first call
+// (error word and tickets).
+size_t workspace_header_bytes(size_t MT) { return 64 + sizeof(unsigned) * (1 + (size_t)moe::router_groups((int)MT)); }
+
 hipEvent_t take_event(moe_ctx* ctx) {
     if (!ctx->pool.empty()) {
         hipEvent_t e = ctx->pool.back();
@@ -115,13 +169,14 @@ hipEvent_t take_event(moe_ctx* ctx) {
 }
 
 // While profiling, hands a start/stop event pair to the next launch, which
-// stamps them from its own dispatch (see MOE_LAUNCH).
+// stamps them from its own dispatch (see MOE_LAUNCH).  Without a context
+// (or with profiling off) it does nothing.
 struct Launch {
     moe_ctx* ctx;
     Rec rec{};
     bool on = false;
-    Launch(moe_ctx* c, int kernel, hipStream_t) : ctx(c) {
-        if (ctx->prof) {
+    Launch(moe_ctx* c, int kernel) : ctx(c) {
+        if (ctx && ctx->prof) {
             rec.kernel = kernel;
             rec.a = take_event(ctx);
             rec.b = take_event(ctx);
@@ -136,27 +191,252 @@ struct Launch {
     }
 };
 
+// What one call runs on: the layer (config, weights), the workspace its
+// kernels use, and the context that records profiling events (or null).
+struct Exec {
+    const moe_config& c;
+    const moe_weights& w;
+    const Workspace& ws;
+    moe_ctx* prof;
+};
+
 moe_status hip_status(hipError_t e) { return e == hipSuccess ? MOE_OK : MOE_ERR_HIP; }
 
 // Channel-sparse mode after the selection: kept-channel gather, then combine.
-moe_status chan_gather_combine(moe_ctx* ctx, const float* h, int M, const int32_t* topk_ids, const float* topk_w,
+moe_status chan_gather_combine(const Exec& x, const float* h, int M, const int32_t* topk_ids, const float* topk_w,
                                int K, int32_t* kept_out, float* y, hipStream_t s) {
-    const moe_config& c = ctx->cfg;
+    const moe_config& c = x.c;
     const int nchunks = (K + kChanChunk - 1) / kChanChunk;
     hipError_t e;
     {
-        Launch l(ctx, MOE_KERNEL_CHAN_GATHER, s);
-        e = moe::launch_chan_gather(topk_ids, topk_w, ctx->slot_cnt, ctx->slot_kept, kept_out, M, c.top_k, c.I, c.E,
-                                    c.H, K, kChanChunk, h, ctx->w.w_gate, ctx->w.w_up, ctx->w.w_down,
-                                    ctx->chan_part, s);
+        Launch l(x.prof, MOE_KERNEL_CHAN_GATHER);
+        e = moe::launch_chan_gather(topk_ids, topk_w, x.ws.slot_cnt, x.ws.slot_kept, kept_out, M, c.top_k, c.I, c.E,
+                                    c.H, K, kChanChunk, h, x.w.w_gate, x.w.w_up, x.w.w_down, x.ws.chan_part, s);
         l.done();
         if (e != hipSuccess) return MOE_ERR_HIP;
     }
-    Launch l(ctx, MOE_KERNEL_CHAN_COMBINE, s);
-    e = moe::launch_chan_combine(M, c.H, nchunks, ctx->chan_part, y, s);
+    Launch l(x.prof, MOE_KERNEL_CHAN_COMBINE);
+    e = moe::launch_chan_combine(M, c.H, nchunks, x.ws.chan_part, y, s);
     l.done();
     return hip_status(e);
 }
+
+moe_status route_topk_impl(const Exec& x, const float* h, int32_t M, int32_t* topk_ids, float* topk_w,
+                           float* logits_out, hipStream_t s) {
+    if (M == 0) return MOE_OK;
+    if (!h || !topk_ids || !topk_w || !aligned(h, 16)) return MOE_ERR_INVALID_ARG;
+    const moe_config& c = x.c;
+    Launch l(x.prof, MOE_KERNEL_ROUTER);
+    hipError_t e = moe::launch_router(h, M, c.H, x.w.router_w, c.E, x.w.router_bias, c.top_k, x.ws.router_part,
+                                      x.ws.ticket, topk_ids, topk_w, logits_out, s);
+    l.done();
+    return hip_status(e);
+}
+
+moe_status align_impl(const Exec& x, const int32_t* topk_ids, int32_t M, int32_t* sorted_routes,
+                      int32_t* block_expert, int32_t* counts, hipStream_t s) {
+    if (!counts) return MOE_ERR_INVALID_ARG;
+    // M == 0: the kernel runs with no routes and only writes counts = {0, 0}
+    if (M > 0 && (!topk_ids || !sorted_routes || !block_expert)) return MOE_ERR_INVALID_ARG;
+    const moe_config& c = x.c;
+    Launch l(x.prof, MOE_KERNEL_ALIGN);
+    hipError_t e = moe::launch_align(topk_ids, M * c.top_k, c.E, c.block_b, sorted_routes, block_expert, counts,
+                                     x.ws.err, s);
+    l.done();
+    return hip_status(e);
+}
+
+moe_status route_align_impl(const Exec& x, bool with_z, const float* h, int32_t M, int32_t* topk_ids,
+                            float* topk_w, float* logits_out, int32_t* sorted_routes, int32_t* block_expert,
+                            int32_t* counts, hipStream_t s) {
+    if (!counts) return MOE_ERR_INVALID_ARG;
+    if (M == 0) return align_impl(x, nullptr, 0, nullptr, nullptr, counts, s);
+    if (!h || !topk_ids || !topk_w || !sorted_routes || !block_expert || !aligned(h, 16)) return MOE_ERR_INVALID_ARG;
+    const moe_config& c = x.c;
+    // with_z: the VQ + low-rank shared projections z = D^T h ride along as
+    // extra workgroups of the same launch
+    const moe::GemvJob jobs[2] = {{x.w.lr_basis[0], c.lr_r, x.ws.zpart[0]},
+                                  {x.w.lr_basis[1], c.lr_r, x.ws.zpart[1]}};
+    Launch l(x.prof, MOE_KERNEL_ROUTER_ALIGN);
+    hipError_t e = moe::launch_router_align(h, M, c.H, x.w.router_w, c.E, x.w.router_bias, c.top_k,
+                                            x.ws.router_part, x.ws.ticket, topk_ids, topk_w, logits_out, c.block_b,
+                                            sorted_routes, block_expert, counts, x.ws.err, s,
+                                            with_z ? jobs : nullptr, with_z ? 2 : 0);
+    l.done();
+    return hip_status(e);
+}
+
+moe_status expert_forward_impl(const Exec& x, bool z_ready, const float* h, int32_t M, const int32_t* topk_ids,
+                               const float* topk_w, const int32_t* sorted_routes, const int32_t* block_expert,
+                               const int32_t* counts, int32_t keep_channels, int32_t* kept_out, float* y,
+                               hipStream_t s) {
+    const moe_config& c = x.c;
+    if (M == 0) return MOE_OK;
+    if (!h || !topk_ids || !topk_w || !y || !aligned(h, 16) || !aligned(y, 16)) return MOE_ERR_INVALID_ARG;
+    hipError_t e;
+
+    if (keep_channels > 0) {
+        if (c.max_keep == 0 || c.wformat != MOE_WFORMAT_DENSE) return MOE_ERR_UNSUPPORTED;
+        if (keep_channels > c.max_keep) return MOE_ERR_CAPACITY;
+        {
+            Launch l(x.prof, MOE_KERNEL_CHAN_SELECT);
+            e = moe::launch_chan_select(topk_ids, topk_w, x.w.chan_norm, x.w.chan_rank, M, c.top_k, c.I, c.E,
+                                        keep_channels, x.ws.slot_cnt, x.ws.slot_kept, s);
+            l.done();
+            if (e != hipSuccess) return MOE_ERR_HIP;
+        }
+        return chan_gather_combine(x, h, M, topk_ids, topk_w, keep_channels, kept_out, y, s);
+    }
+
+    if (!sorted_routes || !block_expert || !counts) return MOE_ERR_INVALID_ARG;
+    moe::PlanArgs plan{};
+    plan.topk_ids = topk_ids;
+    plan.sorted_routes = sorted_routes;
+    plan.block_expert = block_expert;
+    plan.counts = counts;
+    plan.R = M * c.top_k;
+    plan.k = c.top_k;
+    plan.fk = FastDiv((uint32_t)c.top_k);
+    plan.b = c.block_b;
+    plan.max_blocks = (int)(align_capacity64(M, c.top_k, c.E, c.block_b) / c.block_b);
+    plan.E = c.E;
+
+    int nchunk = moe::down_chunks(c.I);
+    if (c.wformat == MOE_WFORMAT_DENSE && moe::dense_uses_fused(M, c.H)) {
+        nchunk = moe::dense_chunks(M, c.H, c.I);
+        Launch l(x.prof, MOE_KERNEL_EXPERT_FUSED);
+        e = moe::launch_expert_fused(plan, h, topk_w, c.H, c.I, x.w.w_gate, x.w.w_up, x.w.w_down, x.ws.down_part,
+                                     x.ws.err, s);
+        l.done();
+        if (e != hipSuccess) return MOE_ERR_HIP;
+    } else {
+        if (c.wformat == MOE_WFORMAT_DENSE) {
+            Launch l(x.prof, MOE_KERNEL_GATEUP);
+            e = moe::launch_gateup_dense(plan, h, c.H, c.I, x.w.w_gate, x.w.w_up, x.ws.p, x.ws.err, s);
+            l.done();
+            if (e != hipSuccess) return MOE_ERR_HIP;
+        } else {
+            moe::GemvJob jobs[2] = {{x.w.lr_basis[0], c.lr_r, x.ws.zpart[0]},
+                                    {x.w.lr_basis[1], c.lr_r, x.ws.zpart[1]}};
+            if (!z_ready) {  // else computed by the routing launch of this step
+                Launch l(x.prof, MOE_KERNEL_VQ_SHARED);
+                e = moe::launch_gemv_partials(h, M, c.H, jobs, 2, s);
+                l.done();
+                if (e != hipSuccess) return MOE_ERR_HIP;
+            }
+            moe::VqArgs vq{};
+            for (int P = 0; P < 2; ++P) {
+                vq.C[P] = x.w.lr_coef[P];
+                vq.B[P] = x.w.vq_book[P];
+                vq.J[P] = x.w.vq_idx[P];
+                vq.zpart[P] = x.ws.zpart[P];
+            }
+            vq.zslices = moe::gemv_slices(c.H, c.lr_r);
+            vq.M = M;
+            vq.r = c.lr_r;
+            vq.K = c.vq_K;
+            vq.d = c.vq_d;
+            Launch l(x.prof, MOE_KERNEL_GATEUP_VQLR);
+            e = moe::launch_gateup_vqlr(plan, vq, h, c.H, c.I, x.ws.p, x.ws.err, s);
+            l.done();
+            if (e != hipSuccess) return MOE_ERR_HIP;
+        }
+        Launch l(x.prof, MOE_KERNEL_DOWN);
+        e = moe::launch_down(plan, c.H, c.I, x.w.w_down, x.ws.p, topk_w, x.ws.down_part, x.ws.err, s);
+        l.done();
+        if (e != hipSuccess) return MOE_ERR_HIP;
+    }
+    Launch l(x.prof, MOE_KERNEL_COMBINE);
+    e = moe::launch_combine(topk_ids, M, c.top_k, c.E, c.H, nchunk, x.ws.down_part, y, s);
+    l.done();
+    return hip_status(e);
+}
+
+moe_status decode_step_impl(const Exec& x, const float* h, int32_t M, int32_t* topk_ids, float* topk_w,
+                            float* logits_out, int32_t* sorted_routes, int32_t* block_expert, int32_t* counts,
+                            int32_t keep_channels, int32_t* kept_out, float* y, hipStream_t s) {
+    const moe_config& c = x.c;
+    if (keep_channels > 0) {
+        // router GEMV partials, then a channel selection whose workgroups
+        // route their tokens, then gather and combine
+        if (c.max_keep == 0 || c.wformat != MOE_WFORMAT_DENSE) return MOE_ERR_UNSUPPORTED;
+        if (keep_channels > c.max_keep) return MOE_ERR_CAPACITY;
+        if (M == 0) return MOE_OK;
+        if (!h || !topk_ids || !topk_w || !y || !aligned(h, 16) || !aligned(y, 16)) return MOE_ERR_INVALID_ARG;
+        hipError_t e;
+        {
+            Launch l(x.prof, MOE_KERNEL_ROUTER_GEMV);
+            e = moe::launch_router_partials(h, M, c.H, x.w.router_w, c.E, x.ws.router_part, s);
+            l.done();
+            if (e != hipSuccess) return MOE_ERR_HIP;
+        }
+        moe::SelRoute route{};
+        route.part = x.ws.router_part;
+        route.bias = x.w.router_bias;
+        route.nslices = moe::router_slices(c.H, c.E);
+        route.M = M;
+        route.ids = topk_ids;
+        route.wts = topk_w;
+        route.logits = logits_out;
+        {
+            Launch l(x.prof, MOE_KERNEL_CHAN_SELECT);
+            e = moe::launch_chan_select_routed(route, x.w.chan_norm, x.w.chan_rank, M, c.top_k, c.I, c.E,
+                                               keep_channels, x.ws.slot_cnt, x.ws.slot_kept, s);
+            l.done();
+            if (e != hipSuccess) return MOE_ERR_HIP;
+        }
+        return chan_gather_combine(x, h, M, topk_ids, topk_w, keep_channels, kept_out, y, s);
+    }
+    const int nsl = moe::router_slices(c.H, c.E);
+    if (M != 1 || c.wformat != MOE_WFORMAT_DENSE || !moe::decode_fused_ok(c.H, c.E, c.top_k, nsl)) {
+        const bool vq = c.wformat == MOE_WFORMAT_VQLR;  // z = D^T h in the routing launch
+        moe_status st = route_align_impl(x, vq, h, M, topk_ids, topk_w, logits_out, sorted_routes, block_expert,
+                                         counts, s);
+        if (st != MOE_OK) return st;
+        return expert_forward_impl(x, vq, h, M, topk_ids, topk_w, sorted_routes, block_expert, counts, 0, nullptr,
+                                   y, s);
+    }
+    if (!h || !topk_ids || !topk_w || !sorted_routes || !block_expert || !counts || !y || !aligned(h, 16) ||
+        !aligned(y, 16))
+        return MOE_ERR_INVALID_ARG;
+    hipError_t e;
+    {
+        Launch l(x.prof, MOE_KERNEL_ROUTER_GEMV);
+        e = moe::launch_router_partials(h, 1, c.H, x.w.router_w, c.E, x.ws.router_part, s);
+        l.done();
+        if (e != hipSuccess) return MOE_ERR_HIP;
+    }
+    moe::PlanArgs plan{};
+    plan.R = c.top_k;
+    plan.k = c.top_k;
+    plan.fk = FastDiv((uint32_t)c.top_k);
+    plan.b = c.block_b;
+    plan.max_blocks = c.top_k;
+    plan.E = c.E;
+    moe::RouteArgs route{};
+    route.part = x.ws.router_part;
+    route.bias = x.w.router_bias;
+    route.nslices = nsl;
+    route.ids = topk_ids;
+    route.wts = topk_w;
+    route.logits = logits_out;
+    route.sorted_routes = sorted_routes;
+    route.block_expert = block_expert;
+    route.counts = counts;
+    {
+        Launch l(x.prof, MOE_KERNEL_DECODE_FUSED);
+        e = moe::launch_decode_fused(plan, route, h, c.H, c.I, x.w.w_gate, x.w.w_up, x.w.w_down, x.ws.down_part,
+                                     x.ws.err, s);
+        l.done();
+        if (e != hipSuccess) return MOE_ERR_HIP;
+    }
+    Launch l(x.prof, MOE_KERNEL_COMBINE);
+    e = moe::launch_combine(topk_ids, 1, c.top_k, c.E, c.H, moe::dense_chunks(1, c.H, c.I), x.ws.down_part, y, s);
+    l.done();
+    return hip_status(e);
+}
+
+Exec exec_of(moe_ctx* ctx) { return Exec{ctx->cfg, ctx->w, ctx->ws, ctx}; }
 
 }  // namespace
 
@@ -166,6 +446,14 @@ int32_t moe_align_capacity(int32_t M, int32_t k, int32_t E, int32_t b) {
     if (M < 0 || k <= 0 || E <= 0 || b <= 0) return -1;
     const int64_t c = align_capacity64(M, k, E, b);
     return c > INT32_MAX ? -1 : (int32_t)c;
+}
+
+int64_t moe_workspace_bytes(const moe_config* cfg, int32_t max_tokens) {
+    if (!cfg || max_tokens < 1) return -1;
+    moe_config c = *cfg;
+    c.max_tokens = max_tokens;
+    if (check_config(&c) != MOE_OK) return -1;
+    return (int64_t)workspace_layout(c, (size_t)max_tokens, nullptr, nullptr);
 }
 
 const char* moe_status_string(moe_status s) {
@@ -205,48 +493,16 @@ moe_status moe_create(const moe_config* cfg, const moe_weights* w, moe_ctx** out
         delete ctx;
         return MOE_ERR_HIP;
     }
-    const moe_config& c = *cfg;
-    const size_t MT = c.max_tokens, R = MT * c.top_k;
-    const size_t zsl = c.wformat == MOE_WFORMAT_VQLR ? moe::gemv_slices(c.H, c.lr_r) : 0;
-    size_t nchunk = moe::down_chunks(c.I);
-    if (moe::dense_uses_fused(1, c.H)) {
-        const size_t f = moe::dense_chunks(1, c.H, c.I);
-        nchunk = f > nchunk ? f : nchunk;
-    }
-    const size_t nchan = c.max_keep > 0 ? (c.max_keep + kChanChunk - 1) / kChanChunk : 0;
-    size_t sizes[8] = {
-        64 + sizeof(unsigned) * (1 + (size_t)moe::router_groups((int)MT)),  // err flag, router tickets
-        sizeof(float) * moe::gemv_slices(c.H, c.E) * MT * c.E,          // router partials
-        sizeof(float) * zsl * MT * c.lr_r,                              // z = D^T h partials (gate)
-        sizeof(float) * zsl * MT * c.lr_r,                              // z partials (up)
-        sizeof(float) * R * c.I,                                        // p
-        sizeof(float) * R * nchunk * c.H,                               // down partials
-        c.max_keep > 0 ? sizeof(int32_t) * MT * c.top_k * (1 + (size_t)c.I) : 0,  // per-slot kept lists
-        sizeof(float) * MT * nchan * c.H,                               // channel partials
-    };
-    size_t off[8], total = 0;
-    for (int i = 0; i < 8; ++i) {
-        off[i] = total;
-        total += (sizes[i] + 255) & ~(size_t)255;
-    }
-    if (hipMalloc(&ctx->ws, total) != hipSuccess) {
+    const size_t MT = cfg->max_tokens;
+    const size_t total = workspace_layout(*cfg, MT, nullptr, nullptr);
+    if (hipMalloc(&ctx->ws_mem, total) != hipSuccess) {
         delete ctx;
         return MOE_ERR_HIP;
     }
     ctx->ws_bytes = total;
-    char* base = static_cast<char*>(ctx->ws);
-    ctx->err = reinterpret_cast<int32_t*>(base + off[0]);
-    ctx->ticket = reinterpret_cast<unsigned*>(base + off[0] + 64);
-    ctx->router_part = reinterpret_cast<float*>(base + off[1]);
-    ctx->zpart[0] = reinterpret_cast<float*>(base + off[2]);
-    ctx->zpart[1] = reinterpret_cast<float*>(base + off[3]);
-    ctx->p = reinterpret_cast<float*>(base + off[4]);
-    ctx->down_part = reinterpret_cast<float*>(base + off[5]);
-    ctx->slot_cnt = reinterpret_cast<int32_t*>(base + off[6]);
-    ctx->slot_kept = ctx->slot_cnt + MT * c.top_k;
-    ctx->chan_part = reinterpret_cast<float*>(base + off[7]);
-    if (hipMemset(ctx->err, 0, sizes[0]) != hipSuccess || hipDeviceSynchronize() != hipSuccess) {
-        hipFree(ctx->ws);
+    workspace_layout(*cfg, MT, static_cast<char*>(ctx->ws_mem), &ctx->ws);
+    if (hipMemset(ctx->ws_mem, 0, workspace_header_bytes(MT)) != hipSuccess || hipDeviceSynchronize() != hipSuccess) {
+        hipFree(ctx->ws_mem);
         delete ctx;
         return MOE_ERR_HIP;
     }
@@ -262,7 +518,7 @@ void moe_destroy(moe_ctx* ctx) {
         hipEventDestroy(r.b);
     }
     for (auto e : ctx->pool) hipEventDestroy(e);
-    if (ctx->ws) hipFree(ctx->ws);
+    if (ctx->ws_mem) hipFree(ctx->ws_mem);
     delete ctx;
 }
 
@@ -270,254 +526,50 @@ moe_status moe_route_topk(moe_ctx* ctx, const float* h, int32_t M, int32_t* topk
                           float* logits_out, void* stream) {
     if (!ctx || M < 0) return MOE_ERR_INVALID_ARG;
     if (M > ctx->cfg.max_tokens) return MOE_ERR_CAPACITY;
-    if (M == 0) return MOE_OK;
-    if (!h || !topk_ids || !topk_w || !aligned(h, 16)) return MOE_ERR_INVALID_ARG;
-    const moe_config& c = ctx->cfg;
-    hipStream_t s = static_cast<hipStream_t>(stream);
-    Launch l(ctx, MOE_KERNEL_ROUTER, s);
-    hipError_t e = moe::launch_router(h, M, c.H, ctx->w.router_w, c.E, ctx->w.router_bias, c.top_k, ctx->router_part,
-                                      ctx->ticket, topk_ids, topk_w, logits_out, s);
-    l.done();
-    return hip_status(e);
-}
-
-static moe_status route_align_impl(bool with_z, moe_ctx* ctx, const float* h, int32_t M, int32_t* topk_ids,
-                                   float* topk_w,
-                           float* logits_out, int32_t* sorted_routes, int32_t* block_expert, int32_t* counts,
-                           void* stream) {
-    if (!ctx || M < 0) return MOE_ERR_INVALID_ARG;
-    if (M > ctx->cfg.max_tokens) return MOE_ERR_CAPACITY;
-    if (!counts) return MOE_ERR_INVALID_ARG;
-    if (M == 0) return moe_align_blocks(ctx, nullptr, 0, nullptr, nullptr, counts, stream);
-    if (!h || !topk_ids || !topk_w || !sorted_routes || !block_expert || !aligned(h, 16)) return MOE_ERR_INVALID_ARG;
-    const moe_config& c = ctx->cfg;
-    hipStream_t s = static_cast<hipStream_t>(stream);
-    // with_z: the VQ + low-rank shared projections z = D^T h ride along as
-    // extra workgroups of the same launch
-    const moe::GemvJob jobs[2] = {{ctx->w.lr_basis[0], c.lr_r, ctx->zpart[0]},
-                                  {ctx->w.lr_basis[1], c.lr_r, ctx->zpart[1]}};
-    Launch l(ctx, MOE_KERNEL_ROUTER_ALIGN, s);
-    hipError_t e = moe::launch_router_align(h, M, c.H, ctx->w.router_w, c.E, ctx->w.router_bias, c.top_k,
-                                            ctx->router_part, ctx->ticket, topk_ids, topk_w, logits_out, c.block_b,
-                                            sorted_routes, block_expert, counts, ctx->err, s, with_z ? jobs : nullptr,
-                                            with_z ? 2 : 0);
-    l.done();
-    return hip_status(e);
+    return route_topk_impl(exec_of(ctx), h, M, topk_ids, topk_w, logits_out, static_cast<hipStream_t>(stream));
 }
 
 moe_status moe_route_align(moe_ctx* ctx, const float* h, int32_t M, int32_t* topk_ids, float* topk_w,
                            float* logits_out, int32_t* sorted_routes, int32_t* block_expert, int32_t* counts,
                            void* stream) {
-    return route_align_impl(false, ctx, h, M, topk_ids, topk_w, logits_out, sorted_routes, block_expert, counts,
-                            stream);
+    if (!ctx || M < 0) return MOE_ERR_INVALID_ARG;
+    if (M > ctx->cfg.max_tokens) return MOE_ERR_CAPACITY;
+    return route_align_impl(exec_of(ctx), false, h, M, topk_ids, topk_w, logits_out, sorted_routes, block_expert,
+                            counts, static_cast<hipStream_t>(stream));
 }
 
 moe_status moe_align_blocks(moe_ctx* ctx, const int32_t* topk_ids, int32_t M, int32_t* sorted_routes,
                             int32_t* block_expert, int32_t* counts, void* stream) {
     if (!ctx || M < 0) return MOE_ERR_INVALID_ARG;
     if (M > ctx->cfg.max_tokens) return MOE_ERR_CAPACITY;
-    if (!counts) return MOE_ERR_INVALID_ARG;
-    const moe_config& c = ctx->cfg;
-    hipStream_t s = static_cast<hipStream_t>(stream);
-    // M == 0: the kernel runs with no routes and only writes counts = {0, 0}
-    if (M > 0 && (!topk_ids || !sorted_routes || !block_expert)) return MOE_ERR_INVALID_ARG;
-    Launch l(ctx, MOE_KERNEL_ALIGN, s);
-    hipError_t e = moe::launch_align(topk_ids, M * c.top_k, c.E, c.block_b, sorted_routes, block_expert, counts,
-                                     ctx->err, s);
-    l.done();
-    return hip_status(e);
-}
-
-static moe_status expert_forward_impl(bool z_ready, moe_ctx* ctx, const float* h, int32_t M,
-                                      const int32_t* topk_ids, const float* topk_w,
-                              const int32_t* sorted_routes, const int32_t* block_expert, const int32_t* counts,
-                              int32_t keep_channels, int32_t* kept_out, float* y, void* stream) {
-    if (!ctx || M < 0 || keep_channels < 0) return MOE_ERR_INVALID_ARG;
-    const moe_config& c = ctx->cfg;
-    if (M > c.max_tokens) return MOE_ERR_CAPACITY;
-    if (M == 0) return MOE_OK;
-    if (!h || !topk_ids || !topk_w || !y || !aligned(h, 16) || !aligned(y, 16)) return MOE_ERR_INVALID_ARG;
-    hipStream_t s = static_cast<hipStream_t>(stream);
-    hipError_t e;
-
-    if (keep_channels > 0) {
-        if (c.max_keep == 0 || c.wformat != MOE_WFORMAT_DENSE) return MOE_ERR_UNSUPPORTED;
-        if (keep_channels > c.max_keep) return MOE_ERR_CAPACITY;
-        {
-            Launch l(ctx, MOE_KERNEL_CHAN_SELECT, s);
-            e = moe::launch_chan_select(topk_ids, topk_w, ctx->w.chan_norm, ctx->w.chan_rank, M, c.top_k, c.I, c.E,
-                                        keep_channels, ctx->slot_cnt, ctx->slot_kept, s);
-            l.done();
-            if (e != hipSuccess) return MOE_ERR_HIP;
-        }
-        return chan_gather_combine(ctx, h, M, topk_ids, topk_w, keep_channels, kept_out, y, s);
-    }
-
-    if (!sorted_routes || !block_expert || !counts) return MOE_ERR_INVALID_ARG;
-    moe::PlanArgs plan{};
-    plan.topk_ids = topk_ids;
-    plan.sorted_routes = sorted_routes;
-    plan.block_expert = block_expert;
-    plan.counts = counts;
-    plan.R = M * c.top_k;
-    plan.k = c.top_k;
-    plan.fk = FastDiv((uint32_t)c.top_k);
-    plan.b = c.block_b;
-    plan.max_blocks = (int)(align_capacity64(M, c.top_k, c.E, c.block_b) / c.block_b);
-    plan.E = c.E;
-
-    int nchunk = moe::down_chunks(c.I);
-    if (c.wformat == MOE_WFORMAT_DENSE && moe::dense_uses_fused(M, c.H)) {
-        nchunk = moe::dense_chunks(M, c.H, c.I);
-        Launch l(ctx, MOE_KERNEL_EXPERT_FUSED, s);
-        e = moe::launch_expert_fused(plan, h, topk_w, c.H, c.I, ctx->w.w_gate, ctx->w.w_up, ctx->w.w_down,
-                                     ctx->down_part, ctx->err, s);
-        l.done();
-        if (e != hipSuccess) return MOE_ERR_HIP;
-    } else {
-        if (c.wformat == MOE_WFORMAT_DENSE) {
-            Launch l(ctx, MOE_KERNEL_GATEUP, s);
-            e = moe::launch_gateup_dense(plan, h, c.H, c.I, ctx->w.w_gate, ctx->w.w_up, ctx->p, ctx->err, s);
-            l.done();
-            if (e != hipSuccess) return MOE_ERR_HIP;
-        } else {
-            moe::GemvJob jobs[2] = {{ctx->w.lr_basis[0], c.lr_r, ctx->zpart[0]},
-                                    {ctx->w.lr_basis[1], c.lr_r, ctx->zpart[1]}};
-            if (!z_ready) {  // else computed by the routing launch of this step
-                Launch l(ctx, MOE_KERNEL_VQ_SHARED, s);
-                e = moe::launch_gemv_partials(h, M, c.H, jobs, 2, s);
-                l.done();
-                if (e != hipSuccess) return MOE_ERR_HIP;
-            }
-            moe::VqArgs vq{};
-            for (int P = 0; P < 2; ++P) {
-                vq.C[P] = ctx->w.lr_coef[P];
-                vq.B[P] = ctx->w.vq_book[P];
-                vq.J[P] = ctx->w.vq_idx[P];
-                vq.zpart[P] = ctx->zpart[P];
-            }
-            vq.zslices = moe::gemv_slices(c.H, c.lr_r);
-            vq.M = M;
-            vq.r = c.lr_r;
-            vq.K = c.vq_K;
-            vq.d = c.vq_d;
-            Launch l(ctx, MOE_KERNEL_GATEUP_VQLR, s);
-            e = moe::launch_gateup_vqlr(plan, vq, h, c.H, c.I, ctx->p, ctx->err, s);
-            l.done();
-            if (e != hipSuccess) return MOE_ERR_HIP;
-        }
-        Launch l(ctx, MOE_KERNEL_DOWN, s);
-        e = moe::launch_down(plan, c.H, c.I, ctx->w.w_down, ctx->p, topk_w, ctx->down_part, ctx->err, s);
-        l.done();
-        if (e != hipSuccess) return MOE_ERR_HIP;
-    }
-    Launch l(ctx, MOE_KERNEL_COMBINE, s);
-    e = moe::launch_combine(topk_ids, M, c.top_k, c.E, c.H, nchunk, ctx->down_part, y, s);
-    l.done();
-    return hip_status(e);
+    return align_impl(exec_of(ctx), topk_ids, M, sorted_routes, block_expert, counts,
+                      static_cast<hipStream_t>(stream));
 }
 
 moe_status moe_expert_forward(moe_ctx* ctx, const float* h, int32_t M, const int32_t* topk_ids, const float* topk_w,
                               const int32_t* sorted_routes, const int32_t* block_expert, const int32_t* counts,
                               int32_t keep_channels, int32_t* kept_out, float* y, void* stream) {
-    return expert_forward_impl(false, ctx, h, M, topk_ids, topk_w, sorted_routes, block_expert, counts, keep_channels,
-                               kept_out, y, stream);
+    if (!ctx || M < 0 || keep_channels < 0) return MOE_ERR_INVALID_ARG;
+    if (M > ctx->cfg.max_tokens) return MOE_ERR_CAPACITY;
+    return expert_forward_impl(exec_of(ctx), false, h, M, topk_ids, topk_w, sorted_routes, block_expert, counts,
+                               keep_channels, kept_out, y, static_cast<hipStream_t>(stream));
 }
 
 moe_status moe_decode_step(moe_ctx* ctx, const float* h, int32_t M, int32_t* topk_ids, float* topk_w,
                            float* logits_out, int32_t* sorted_routes, int32_t* block_expert, int32_t* counts,
                            int32_t keep_channels, int32_t* kept_out, float* y, void* stream) {
     if (!ctx || M < 0 || keep_channels < 0) return MOE_ERR_INVALID_ARG;
-    const moe_config& c = ctx->cfg;
-    if (M > c.max_tokens) return MOE_ERR_CAPACITY;
-    if (keep_channels > 0) {
-        // router GEMV partials, then a channel selection whose workgroups
-        // route their tokens, then gather and combine
-        if (c.max_keep == 0 || c.wformat != MOE_WFORMAT_DENSE) return MOE_ERR_UNSUPPORTED;
-        if (keep_channels > c.max_keep) return MOE_ERR_CAPACITY;
-        if (M == 0) return MOE_OK;
-        if (!h || !topk_ids || !topk_w || !y || !aligned(h, 16) || !aligned(y, 16)) return MOE_ERR_INVALID_ARG;
-        hipStream_t s = static_cast<hipStream_t>(stream);
-        hipError_t e;
-        {
-            Launch l(ctx, MOE_KERNEL_ROUTER_GEMV, s);
-            e = moe::launch_router_partials(h, M, c.H, ctx->w.router_w, c.E, ctx->router_part, s);
-            l.done();
-            if (e != hipSuccess) return MOE_ERR_HIP;
-        }
-        moe::SelRoute route{};
-        route.part = ctx->router_part;
-        route.bias = ctx->w.router_bias;
-        route.nslices = moe::router_slices(c.H, c.E);
-        route.M = M;
-        route.ids = topk_ids;
-        route.wts = topk_w;
-        route.logits = logits_out;
-        {
-            Launch l(ctx, MOE_KERNEL_CHAN_SELECT, s);
-            e = moe::launch_chan_select_routed(route, ctx->w.chan_norm, ctx->w.chan_rank, M, c.top_k, c.I, c.E,
-                                               keep_channels, ctx->slot_cnt, ctx->slot_kept, s);
-            l.done();
-            if (e != hipSuccess) return MOE_ERR_HIP;
-        }
-        return chan_gather_combine(ctx, h, M, topk_ids, topk_w, keep_channels, kept_out, y, s);
-    }
-    const int nsl = moe::router_slices(c.H, c.E);
-    if (M != 1 || c.wformat != MOE_WFORMAT_DENSE || !moe::decode_fused_ok(c.H, c.E, c.top_k, nsl)) {
-        const bool vq = c.wformat == MOE_WFORMAT_VQLR;  // z = D^T h in the routing launch
-        moe_status st = route_align_impl(vq, ctx, h, M, topk_ids, topk_w, logits_out, sorted_routes, block_expert,
-                                         counts, stream);
-        if (st != MOE_OK) return st;
-        return expert_forward_impl(vq, ctx, h, M, topk_ids, topk_w, sorted_routes, block_expert, counts, 0, nullptr,
-                                   y, stream);
-    }
-    if (!h || !topk_ids || !topk_w || !sorted_routes || !block_expert || !counts || !y || !aligned(h, 16) ||
-        !aligned(y, 16))
-        return MOE_ERR_INVALID_ARG;
-    hipStream_t s = static_cast<hipStream_t>(stream);
-    hipError_t e;
-    {
-        Launch l(ctx, MOE_KERNEL_ROUTER_GEMV, s);
-        e = moe::launch_router_partials(h, 1, c.H, ctx->w.router_w, c.E, ctx->router_part, s);
-        l.done();
-        if (e != hipSuccess) return MOE_ERR_HIP;
-    }
-    moe::PlanArgs plan{};
-    plan.R = c.top_k;
-    plan.k = c.top_k;
-    plan.fk = FastDiv((uint32_t)c.top_k);
-    plan.b = c.block_b;
-    plan.max_blocks = c.top_k;
-    plan.E = c.E;
-    moe::RouteArgs route{};
-    route.part = ctx->router_part;
-    route.bias = ctx->w.router_bias;
-    route.nslices = nsl;
-    route.ids = topk_ids;
-    route.wts = topk_w;
-    route.logits = logits_out;
-    route.sorted_routes = sorted_routes;
-    route.block_expert = block_expert;
-    route.counts = counts;
-    {
-        Launch l(ctx, MOE_KERNEL_DECODE_FUSED, s);
-        e = moe::launch_decode_fused(plan, route, h, c.H, c.I, ctx->w.w_gate, ctx->w.w_up, ctx->w.w_down,
-                                     ctx->down_part, ctx->err, s);
-        l.done();
-        if (e != hipSuccess) return MOE_ERR_HIP;
-    }
-    Launch l(ctx, MOE_KERNEL_COMBINE, s);
-    e = moe::launch_combine(topk_ids, 1, c.top_k, c.E, c.H, moe::dense_chunks(1, c.H, c.I), ctx->down_part, y, s);
-    l.done();
-    return hip_status(e);
+    if (M > ctx->cfg.max_tokens) return MOE_ERR_CAPACITY;
+    return decode_step_impl(exec_of(ctx), h, M, topk_ids, topk_w, logits_out, sorted_routes, block_expert, counts,
+                            keep_channels, kept_out, y, static_cast<hipStream_t>(stream));
 }
 
 moe_status moe_read_device_error(moe_ctx* ctx, int32_t* flags, int32_t clear) {
     if (!ctx || !flags) return MOE_ERR_INVALID_ARG;
     if (hipDeviceSynchronize() != hipSuccess) return MOE_ERR_HIP;
     int32_t v = 0;
-    if (hipMemcpy(&v, ctx->err, sizeof(v), hipMemcpyDeviceToHost) != hipSuccess) return MOE_ERR_HIP;
-    if (clear && v && hipMemset(ctx->err, 0, sizeof(int32_t)) != hipSuccess) return MOE_ERR_HIP;
+    if (hipMemcpy(&v, ctx->ws.err, sizeof(v), hipMemcpyDeviceToHost) != hipSuccess) return MOE_ERR_HIP;
+    if (clear && v && hipMemset(ctx->ws.err, 0, sizeof(int32_t)) != hipSuccess) return MOE_ERR_HIP;
     *flags = v;
     return v ? MOE_ERR_DEVICE : MOE_OK;
 }

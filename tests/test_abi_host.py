@@ -229,3 +229,24 @@ def test_multiply_high_division_identity():
         assert m < (1 << 32)
         q = (((xs * m) >> 32) + xs) >> s
         assert np.array_equal(q, xs // d), d
+
+
+def test_workspace_bytes_at_the_accepted_limits():
+    """The context workspace holds, per route, I floats of SiLU(gate)*up and one
+    H-float down partial (the split schedule), plus the fused schedule's
+    chunked partials of a single token's top_k routes; it never scales with
+    max_tokens * top_k * (fused chunks).  Checked where check_config's limits
+    bind (4096 routes, H = 4096, I = 16384) and on the 21-token workload."""
+    import memory_bound_routed_amd as mb
+    for (H, I, E, k, MT) in [(4096, 16384, 96, 8, 512), (8192, 16384, 32, 32, 128), (2048, 768, 128, 8, 21),
+                             (2048, 768, 128, 8, 1)]:
+        cfg = mb.make_config(H, I, E, k, 8, MT)
+        ws = mb.moe_workspace_bytes(cfg, MT)
+        R = MT * k
+        fused_chunks = -(-I // 24) if H <= 2048 else -(-I // 8)
+        fused = k * fused_chunks * H * 4 if H <= 4096 else 0
+        main = R * I * 4 + max(R * H * 4, fused)
+        assert main <= ws <= main + 8 * 2 ** 20, (H, I, E, k, MT, ws, main)
+    # rejected configurations report -1
+    assert mb.moe_workspace_bytes(mb.make_config(4096, 16384, 1024, 8, 8, 512), 512) == -1
+    assert mb.moe_workspace_bytes(mb.make_config(2048, 768, 128, 8, 8, 1), 0) == -1

@@ -233,6 +233,10 @@ def test_chansparse_keep799(mb):
         g = run_step(mb, layer, h, keep=wl.keep)
         assert g["err"] == 0
         _, ok = check_router(g, dict(inp, h=h), wl.k, wl.H)
+        routed = sorted(set(g["ids"].ravel().tolist()))
+        ref_r = O.channel_norms(inp["w_gate"], inp["w_up"], inp["w_down"], experts=routed)
+        ulp_r = np.abs(gn[routed].view(np.int32).astype(np.int64) - ref_r[routed].view(np.int32).astype(np.int64))
+        assert ulp_r.max() <= 1, "norms of the routed experts differ by %d ulp" % ulp_r.max()
         kept_ref = O.channel_select(g["w"], g["ids"], gn, wl.keep)
         np.testing.assert_array_equal(g["kept"], kept_ref)
         per_slot = np.bincount(g["kept"][0] // wl.I, minlength=wl.k)
@@ -642,7 +646,7 @@ def test_empty_batch_and_max_tokens(mb):
 @pytest.mark.parametrize("name", ["aligned_h2048_i768_e128_k8_m21", "fused_h2048_i768_e16_k8_m1"])
 def test_bitwise_reproducible_over_repeated_calls(mb, name):
     import torch
-    if name.startswith("fused"):   # one token: the fused kernel, whose last workgroups sum y
+    if name.startswith("fused"):   # one token: the plan-reading fused kernel, then the combine kernel
         wl = synth.small_workload(name, H=2048, I=768, E=16, k=8, M=1, seed=41)
     else:
         wl = synth.WORKLOADS[name]
@@ -668,27 +672,97 @@ def test_bitwise_reproducible_over_repeated_calls(mb, name):
     layer.close()
 
 
+# The five workloads of the decode step, run through moe_decode_step (the
+# benchmarked call): name -> channel top-K (0 = dense / VQ).
+FIVE = [("tiny_h256_i128_e16_k2", 0), ("dense_h2048_i768_e128_k8_m1", 0), ("aligned_h2048_i768_e128_k8_m21", 0),
+        ("chansparse_h2048_i768_e128_k8_m1_keep799", 799), ("vqlr_h2048_i768_e128_k8_m4_d8_K256_r64", 0)]
+
+
+def _decode_outputs(layer, M, keep):
+    """Every output of one moe_decode_step as int32 tensors (fp32 by bits)."""
+    import torch
+    out = [layer.y[:M].view(torch.int32), layer.ids[:M], layer.w[:M].view(torch.int32)]
+    if keep:
+        out.append(layer.kept.view(-1)[: M * keep])
+    else:
+        out.append(layer.counts)
+        n = int(layer.counts[1].item())
+        out.append(layer.sorted_routes[:n])
+        out.append(layer.block_expert[: int(layer.counts[0].item())])
+    return [t.clone() for t in out]
+
+
+@pytest.mark.parametrize("name,keep", FIVE)
+def test_decode_step_bitwise_reproducible_five_workloads(mb, name, keep):
+    """100 calls of the one-call decode step on the same inputs give the same
+    bits in every output (y, ids, affinities, plan or kept list)."""
+    import torch
+    wl = synth.WORKLOADS[name]
+    say("100 repeated decode steps,", name)
+    inp = synth.layer_inputs(wl, 0)
+    if keep:
+        dev = upload_layer(inp)
+        cfg = mb.make_config(wl.H, wl.I, wl.E, wl.k, wl.block_b, wl.M, max_keep=keep)
+        channel_tables(mb, cfg, dev)
+        layer = mb.Layer(cfg, dev)
+    else:
+        layer = make_layer(mb, wl, inp, wl.M)
+    h = to_dev(inp["h"])
+    first = None
+    for i in range(100):
+        layer.decode_step(h, wl.M, keep=keep)
+        outs = _decode_outputs(layer, wl.M, keep)
+        if first is None:
+            first = outs
+        else:
+            for a, b in zip(first, outs):
+                assert torch.equal(a, b), "call %d differs" % i
+    torch.cuda.synchronize()
+    assert mb.moe_read_device_error(layer.ctx) == 0
+    layer.close()
+
+
 _HISTORY_SCRIPT = r"""
 import hashlib, sys, numpy as np, torch
 sys.path.insert(0, sys.argv[1]); sys.path.insert(0, sys.argv[1] + '/tests')
 import synth, memory_bound_routed_amd as mb
 from helpers import upload_layer, to_dev
-keep = []
-if sys.argv[2] == 'H1':   # allocate and keep extra tensors before building the layer
+keep_alive = []
+if sys.argv[2] == 'H1':   # allocate and keep extra tensors before building the layers
     for n in (3, 777, 12345):
-        keep.append(torch.randn(n, device='cuda'))
+        keep_alive.append(torch.randn(n, device='cuda'))
     torch.cuda.synchronize()
-wl = synth.WORKLOADS['aligned_h2048_i768_e128_k8_m21']
-inp = synth.layer_inputs(wl, 0)
-cfg = mb.make_config(wl.H, wl.I, wl.E, wl.k, wl.block_b, wl.M)
-layer = mb.Layer(cfg, upload_layer(inp))
-y = layer.step(to_dev(inp['h']), wl.M)
-torch.cuda.synchronize()
-print(hashlib.sha256(y.cpu().numpy().tobytes()).hexdigest())
+for name, keep in [("tiny_h256_i128_e16_k2", 0), ("dense_h2048_i768_e128_k8_m1", 0),
+                   ("aligned_h2048_i768_e128_k8_m21", 0), ("chansparse_h2048_i768_e128_k8_m1_keep799", 799),
+                   ("vqlr_h2048_i768_e128_k8_m4_d8_K256_r64", 0)]:
+    wl = synth.WORKLOADS[name]
+    inp = synth.layer_inputs(wl, 0)
+    dev = upload_layer(inp)
+    if wl.vq:
+        cfg = mb.make_config(wl.H, wl.I, wl.E, wl.k, wl.block_b, wl.M, mb.MOE_WFORMAT_VQLR, wl.vq_d, wl.vq_K, wl.lr_r)
+    else:
+        cfg = mb.make_config(wl.H, wl.I, wl.E, wl.k, wl.block_b, wl.M, max_keep=keep)
+    if keep:
+        dev['chan_norm'] = torch.empty((wl.E, wl.I), dtype=torch.float32, device='cuda')
+        dev['chan_rank'] = torch.empty((wl.E, wl.I), dtype=torch.int32, device='cuda')
+        mb.moe_channel_norms(cfg, dev['w_gate'], dev['w_up'], dev['w_down'], dev['chan_norm'])
+        mb.moe_channel_ranks(cfg, dev['chan_norm'], dev['chan_rank'])
+    layer = mb.Layer(cfg, dev)
+    y = layer.decode_step(to_dev(inp['h']), wl.M, keep=keep)
+    torch.cuda.synchronize()
+    hsh = hashlib.sha256(y.cpu().numpy().tobytes())
+    hsh.update(layer.ids[:wl.M].cpu().numpy().tobytes())
+    if keep:
+        hsh.update(layer.kept.view(-1)[:wl.M * keep].cpu().numpy().tobytes())
+    print(name, hsh.hexdigest(), flush=True)
+    layer.close()
+    del dev, layer
 """
 
 
 def test_bitwise_identical_across_process_histories(mb):
+    """Two fresh processes with different allocation histories give the same
+    bits for the decode step of all five workloads."""
     root = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
     hashes = {}
     for hist in ("H0", "H1"):
@@ -696,8 +770,10 @@ def test_bitwise_identical_across_process_histories(mb):
         r = subprocess.run([sys.executable, "-c", _HISTORY_SCRIPT, root, hist], capture_output=True, text=True,
                            timeout=300)
         assert r.returncode == 0, r.stderr[-2000:]
-        hashes[hist] = r.stdout.strip().splitlines()[-1]
-    say("  ", hashes)
+        lines = [ln.split() for ln in r.stdout.strip().splitlines() if len(ln.split()) == 2]
+        hashes[hist] = dict(lines)
+    say("  ", hashes["H0"])
+    assert len(hashes["H0"]) == 5
     assert hashes["H0"] == hashes["H1"]
 
 
