@@ -260,6 +260,29 @@ moe_status moe_decode_step(moe_ctx *ctx, const float *h, int32_t M, int32_t *top
                            float *logits_out, int32_t *sorted_routes, int32_t *block_expert, int32_t *counts,
                            int32_t keep_channels, int32_t *kept_out, float *y, void *stream);
 
+/*
+ * moe_decode_step for callers that cannot allocate device memory (code under
+ * HIP graph capture, tight serving loops, harnesses that forbid hipMalloc):
+ * no context, no allocation.  Same arguments and outputs as moe_decode_step,
+ * with the layer given by `cfg` and `w` (host pointers to the structs;
+ * validated on every call as moe_create would) instead of a context.
+ *  - The workspace is a device array inside the library of 16 MiB per GPU,
+ *    held from the first use until the process ends.  A call whose
+ *    workspace (moe_workspace_bytes(cfg, max(M, 1))) exceeds it returns
+ *    MOE_ERR_CAPACITY and enqueues nothing.
+ *  - Every call on one GPU shares that array: calls that overlap on a GPU
+ *    (several streams or threads at once) race; serialise them.
+ *  - The first call on a device looks up the array's address
+ *    (hipGetSymbolAddress); make it outside graph capture.
+ *  - Device-side anomalies are skipped as in moe_decode_step, but their
+ *    flags stay in the shared array and are not reported.
+ *  - No profiling events are recorded.
+ */
+moe_status moe_decode_step_noalloc(const moe_config *cfg, const moe_weights *w, const float *h, int32_t M,
+                                   int32_t *topk_ids, float *topk_w, float *logits_out, int32_t *sorted_routes,
+                                   int32_t *block_expert, int32_t *counts, int32_t keep_channels,
+                                   int32_t *kept_out, float *y, void *stream);
+
 /* ---------------------------------------------------------------- helpers */
 
 /* Rows moe_align_blocks may write: M*k + min(E, M*k)*(b-1); -1 on bad args. */

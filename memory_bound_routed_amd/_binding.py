@@ -29,7 +29,7 @@ MOE_KERNEL_COUNT = len(KERNELS)
 
 # Every symbol include/moe.h declares (checked by the CPU test suite).
 EXPORTS = ["moe_create", "moe_destroy", "moe_route_topk", "moe_route_align", "moe_align_blocks", "moe_expert_forward",
-           "moe_decode_step",
+           "moe_decode_step", "moe_decode_step_noalloc",
            "moe_align_capacity", "moe_workspace_bytes", "moe_status_string", "moe_read_device_error", "moe_channel_norms", "moe_channel_ranks",
            "moe_validate_plan", "moe_profile_enable", "moe_profile_read", "moe_kernel_name"]
 
@@ -57,6 +57,8 @@ _sig = {
     "moe_route_align": (_i32, [_vp, _vp, _i32, _vp, _vp, _vp, _vp, _vp, _vp, _vp]),
     "moe_expert_forward": (_i32, [_vp, _vp, _i32, _vp, _vp, _vp, _vp, _vp, _i32, _vp, _vp, _vp]),
     "moe_decode_step": (_i32, [_vp, _vp, _i32, _vp, _vp, _vp, _vp, _vp, _vp, _i32, _vp, _vp, _vp]),
+    "moe_decode_step_noalloc": (_i32, [ctypes.POINTER(moe_config), ctypes.POINTER(moe_weights), _vp, _i32, _vp, _vp,
+                                       _vp, _vp, _vp, _vp, _i32, _vp, _vp, _vp]),
     "moe_align_capacity": (_i32, [_i32, _i32, _i32, _i32]),
     "moe_workspace_bytes": (ctypes.c_int64, [ctypes.POINTER(moe_config), _i32]),
     "moe_status_string": (ctypes.c_char_p, [_i32]),
@@ -187,6 +189,23 @@ def moe_decode_step(ctx, h, M, topk_ids, topk_w, logits_out, sorted_routes, bloc
     _check(_lib.moe_decode_step(ctx, _ptr(h), M, _ptr(topk_ids), _ptr(topk_w), _ptr(logits_out), _ptr(sorted_routes),
                                 _ptr(block_expert), _ptr(counts), keep_channels, _ptr(kept_out), _ptr(y),
                                 _stream(stream)), "moe_decode_step")
+
+
+def moe_decode_step_noalloc(cfg, weights, h, M, topk_ids, topk_w, logits_out, sorted_routes, block_expert, counts,
+                            keep_channels, kept_out, y, stream=None) -> None:
+    _check(_lib.moe_decode_step_noalloc(ctypes.byref(cfg), ctypes.byref(weights), _ptr(h), M, _ptr(topk_ids),
+                                        _ptr(topk_w), _ptr(logits_out), _ptr(sorted_routes), _ptr(block_expert),
+                                        _ptr(counts), keep_channels, _ptr(kept_out), _ptr(y), _stream(stream)),
+           "moe_decode_step_noalloc")
+
+
+def moe_decode_step_noalloc_status(cfg, weights, h, M, topk_ids, topk_w, logits_out, sorted_routes, block_expert,
+                                   counts, keep_channels, kept_out, y, stream=0) -> int:
+    """Raw status variant (for tests of the failure paths; the default stream
+    is passed as NULL so that no device is touched before the checks)."""
+    return _lib.moe_decode_step_noalloc(ctypes.byref(cfg), ctypes.byref(weights), _ptr(h), M, _ptr(topk_ids),
+                                        _ptr(topk_w), _ptr(logits_out), _ptr(sorted_routes), _ptr(block_expert),
+                                        _ptr(counts), keep_channels, _ptr(kept_out), _ptr(y), stream)
 
 
 def moe_read_device_error(ctx, clear: bool = True) -> int:

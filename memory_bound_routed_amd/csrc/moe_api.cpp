@@ -6,6 +6,7 @@
 
 #include <cstdint>
 #include <cstring>
+#include <mutex>
 #include <new>
 #include <vector>
 
@@ -438,6 +439,32 @@ moe_status decode_step_impl(const Exec& x, const float* h, int32_t M, int32_t* t
 
 Exec exec_of(moe_ctx* ctx) { return Exec{ctx->cfg, ctx->w, ctx->ws, ctx}; }
 
+// Workspace of moe_decode_step_noalloc: one array per device, zeroed when the
+// code object is loaded (so its error word and tickets start at zero; every
+// kernel that takes a ticket re-arms it) and kept until the process ends.
+// In host code `scratch` names a host-side stand-in: its device address on
+// each GPU comes from hipGetSymbolAddress and is kept per device.
+constexpr size_t kScratchBytes = (size_t)16 << 20;
+__device__ __align__(256) char scratch[kScratchBytes];
+
+constexpr int kMaxDevices = 64;
+std::mutex g_scratch_mu;
+char* g_scratch_dev[kMaxDevices] = {};
+
+// Device address of `scratch` on the current device (looked up once per device).
+moe_status scratch_address(char** out) {
+    int dev = -1;
+    if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDevices) return MOE_ERR_HIP;
+    std::lock_guard<std::mutex> lock(g_scratch_mu);
+    if (!g_scratch_dev[dev]) {
+        void* ptr = nullptr;
+        if (hipGetSymbolAddress(&ptr, HIP_SYMBOL(scratch)) != hipSuccess || !ptr) return MOE_ERR_HIP;
+        g_scratch_dev[dev] = static_cast<char*>(ptr);
+    }
+    *out = g_scratch_dev[dev];
+    return MOE_OK;
+}
+
 }  // namespace
 
 extern "C" {
@@ -561,6 +588,29 @@ moe_status moe_decode_step(moe_ctx* ctx, const float* h, int32_t M, int32_t* top
     if (!ctx || M < 0 || keep_channels < 0) return MOE_ERR_INVALID_ARG;
     if (M > ctx->cfg.max_tokens) return MOE_ERR_CAPACITY;
     return decode_step_impl(exec_of(ctx), h, M, topk_ids, topk_w, logits_out, sorted_routes, block_expert, counts,
+                            keep_channels, kept_out, y, static_cast<hipStream_t>(stream));
+}
+
+moe_status moe_decode_step_noalloc(const moe_config* cfg, const moe_weights* w, const float* h, int32_t M,
+                                   int32_t* topk_ids, float* topk_w, float* logits_out, int32_t* sorted_routes,
+                                   int32_t* block_expert, int32_t* counts, int32_t keep_channels, int32_t* kept_out,
+                                   float* y, void* stream) {
+    if (!cfg || !w || M < 0 || keep_channels < 0) return MOE_ERR_INVALID_ARG;
+    moe_status st = check_config(cfg);
+    if (st != MOE_OK) return st;
+    st = check_weights(cfg, w);
+    if (st != MOE_OK) return st;
+    if (M > cfg->max_tokens) return MOE_ERR_CAPACITY;
+    // the workspace of exactly this call's M must fit the array
+    const size_t MT = M > 0 ? (size_t)M : 1;
+    if (workspace_layout(*cfg, MT, nullptr, nullptr) > kScratchBytes) return MOE_ERR_CAPACITY;
+    char* base = nullptr;
+    st = scratch_address(&base);
+    if (st != MOE_OK) return st;
+    Workspace ws;
+    workspace_layout(*cfg, MT, base, &ws);
+    const Exec x{*cfg, *w, ws, nullptr};
+    return decode_step_impl(x, h, M, topk_ids, topk_w, logits_out, sorted_routes, block_expert, counts,
                             keep_channels, kept_out, y, static_cast<hipStream_t>(stream));
 }
 
