@@ -237,12 +237,16 @@ def cpu_baseline(wl, budget_s=10.0, max_steps=40):
         one = _cpu_time(wl, sample, budget_s, max_steps, O)
     with threadpool_limits(limits=cores):
         allc = _cpu_time(wl, sample, budget_s, max_steps, O)
-    return {"value": allc["value"], "unit": "GB/s", "us_per_step": allc["us_per_step"], "cores": cores,
+    # the faster of the two thread counts is the reported value (small GEMVs
+    # can run slower on many BLAS threads than on one)
+    best, nthreads = (allc, cores) if allc["value"] >= one["value"] else (one, 1)
+    return {"value": best["value"], "unit": "GB/s", "us_per_step": best["us_per_step"], "cores": nthreads,
             "kind": "oracle", "cpu_model": model, "nproc": cores,
-            "single_core": {"value": one["value"], "unit": "GB/s", "us_per_step": one["us_per_step"], "cores": 1,
-                            "steps": one["steps"]},
+            "single_core": {"value": one["value"], "us_per_step": one["us_per_step"], "steps": one["steps"]},
+            "all_cores": {"value": allc["value"], "us_per_step": allc["us_per_step"], "steps": allc["steps"],
+                          "threads": cores},
             "sample": "%d steps of %s cycling over %d host-resident layers (only routed experts drawn); fp64 numpy, "
-                      "BLAS threads = %d (single_core: 1)" % (allc["steps"], wl.name, len(sample), cores)}
+                      "timed with 1 and with %d BLAS threads" % (best["steps"], wl.name, len(sample), cores)}
 
 
 def _cpu_sample(wl, synth, O):
