@@ -127,7 +127,7 @@ typedef struct {
  *  The reconstructed gate/up weight of channel j, row i is
  *      sum_rho D_P[i][rho] C_P,e[j][rho] + B_P[J_P,e[j][i / vq_d]][i % vq_d].
  *  Alignment (checked by moe_create, MOE_ERR_INVALID_ARG otherwise): the bf16
- *  arrays 16 bytes, vq_idx and the fp32 / int32 arrays 4 bytes.
+ *  arrays and vq_idx 16 bytes, the fp32 / int32 arrays 4 bytes.
  */
 typedef struct {
     const uint16_t *router_w;
@@ -367,7 +367,8 @@ enum {
     MOE_KERNEL_ROUTER_ALIGN = 11, /* router + top-k + softmax + alignment (one launch) */
     MOE_KERNEL_ROUTER_GEMV = 12,  /* router GEMV slice partials only (decode step) */
     MOE_KERNEL_DECODE_FUSED = 13, /* per-workgroup top-k + softmax + plan, then as EXPERT_FUSED */
-    MOE_KERNEL_COUNT = 14
+    MOE_KERNEL_VQ_FINISH = 14,    /* VQ + low rank: slice partials -> SiLU(gate) * up */
+    MOE_KERNEL_COUNT = 15
 };
 
 /*

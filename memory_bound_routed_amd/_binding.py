@@ -24,7 +24,7 @@ MOE_WFORMAT_DENSE, MOE_WFORMAT_VQLR = 0, 1
 DEVERR_BAD_ROUTE_ID, DEVERR_BAD_PLAN, DEVERR_BAD_BLOCK_EXPERT, DEVERR_BAD_COUNTS = 1, 2, 4, 8
 KERNELS = ["router", "vq_shared", "align", "gateup", "gateup_vqlr", "down", "combine",
            "chan_select", "chan_gather", "chan_combine", "expert_fused", "router_align", "router_gemv",
-           "decode_fused"]
+           "decode_fused", "vq_finish"]
 MOE_KERNEL_COUNT = len(KERNELS)
 
 # Every symbol include/moe.h declares (checked by the CPU test suite).

@@ -127,8 +127,16 @@ struct VqArgs {
     int K;
     int d;
 };
-hipError_t launch_gateup_vqlr(const PlanArgs& plan, const VqArgs& vq, const float* h, int H, int I, float* p,
-                              int32_t* err, hipStream_t stream);
+// T slices per channel: ceil((H / d) / 64).
+int vq_slices(int H, int d);
+// One workgroup set per route r < R (token r / k, expert topk_ids[r]; ids
+// outside [0, E) have no output): vp fp32 [R][vq_slices][2][I] slice
+// partials of o_gate and o_up.
+hipError_t launch_gateup_vqlr(const int32_t* topk_ids, int R, int k, int E, const VqArgs& vq, const float* h, int H,
+                              int I, float* vp, int32_t* err, hipStream_t stream);
+// p[r][j] = SiLU(sum_s vp[r][s][0][j]) * (sum_s vp[r][s][1][j]), sums in
+// slice order, for the R routes.
+hipError_t launch_vq_finish(const float* vp, int R, int I, int nslice, float* p, hipStream_t stream);
 
 // ---- chansparse.hip
 size_t chan_select_lds_bytes(int n);

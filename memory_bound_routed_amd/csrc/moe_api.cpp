@@ -102,7 +102,7 @@ moe_status check_weights(const moe_config* c, const moe_weights* w) {
         for (int P = 0; P < 2; ++P) {
             if (!w->lr_basis[P] || !w->lr_coef[P] || !w->vq_book[P] || !w->vq_idx[P]) return MOE_ERR_INVALID_ARG;
             if (!aligned(w->lr_basis[P], 16) || !aligned(w->lr_coef[P], 16) || !aligned(w->vq_book[P], 16) ||
-                !aligned(w->vq_idx[P], 4))
+                !aligned(w->vq_idx[P], 16))
                 return MOE_ERR_INVALID_ARG;
         }
     }
@@ -129,7 +129,7 @@ size_t workspace_layout(const moe_config& c, size_t MT, char* base, Workspace* w
         sizeof(float) * moe::gemv_slices(c.H, c.E) * MT * c.E,          // router partials
         sizeof(float) * zsl * MT * c.lr_r,                              // z = D^T h partials (gate)
         sizeof(float) * zsl * MT * c.lr_r,                              // z partials (up)
-        sizeof(float) * R * c.I,                                        // p
+        sizeof(float) * R * c.I * (c.wformat == MOE_WFORMAT_VQLR ? 1 + 2 * (size_t)moe::vq_slices(c.H, c.vq_d) : 1),  // p (+ VQ slice partials)
         sizeof(float) * down,                                           // down partials
         c.max_keep > 0 ? sizeof(int32_t) * MT * c.top_k * (1 + (size_t)c.I) : 0,  // per-slot kept lists
         sizeof(float) * MT * nchan * c.H,                               // channel partials
@@ -337,8 +337,17 @@ moe_status expert_forward_impl(const Exec& x, bool z_ready, const float* h, int3
             vq.r = c.lr_r;
             vq.K = c.vq_K;
             vq.d = c.vq_d;
-            Launch l(x.prof, MOE_KERNEL_GATEUP_VQLR);
-            e = moe::launch_gateup_vqlr(plan, vq, h, c.H, c.I, x.ws.p, x.ws.err, s);
+            // slice partials after p in the same buffer
+            float* vp = x.ws.p + (size_t)plan.R * c.I;
+            const int nsl = moe::vq_slices(c.H, c.vq_d);
+            {
+                Launch l(x.prof, MOE_KERNEL_GATEUP_VQLR);
+                e = moe::launch_gateup_vqlr(topk_ids, plan.R, c.top_k, c.E, vq, h, c.H, c.I, vp, x.ws.err, s);
+                l.done();
+                if (e != hipSuccess) return MOE_ERR_HIP;
+            }
+            Launch l(x.prof, MOE_KERNEL_VQ_FINISH);
+            e = moe::launch_vq_finish(vp, plan.R, c.I, nsl, x.ws.p, s);
             l.done();
             if (e != hipSuccess) return MOE_ERR_HIP;
         }
@@ -499,7 +508,7 @@ const char* moe_kernel_name(int32_t k) {
     static const char* names[MOE_KERNEL_COUNT] = {"router",      "vq_shared",   "align",        "gateup",
                                                   "gateup_vqlr", "down",        "combine",      "chan_select",
                                                   "chan_gather", "chan_combine", "expert_fused", "router_align",
-                                                  "router_gemv", "decode_fused"};
+                                                  "router_gemv", "decode_fused", "vq_finish"};
     return (k >= 0 && k < MOE_KERNEL_COUNT) ? names[k] : nullptr;
 }
 

@@ -4,17 +4,29 @@
 // cross-expert gather batching and joint accumulation).
 //
 // For projection P of channel j of expert e and token t:
-//     o_P[j] = sum_rho C_P,e[j][rho] z_P[t][rho]  +  sum_b h_b . B_P[J_P,e[j][b]]
-// where z_P = D_P^T h (computed once per token by the GEMV-partials kernel,
-// summed here over its row slices in slice order) and h_b is the b-th
-// length-8 block of h.  The page materialises the projection code book
-// T[b][c] = h_b . B_c; an fp32 T is 256 KiB per token and projection, larger
-// than a CU's LDS, so here the two 4 KiB weight code books stay resident in
-// LDS and each selected code word is applied to h_b on the fly (8 FMAs per
-// index).  Both terms accumulate into one fp32 register per lane before a
-// single wave reduction (the joint accumulation), then p = SiLU(o_gate)*o_up.
-// One launch covers every routed expert (the gather batching); each expert's
-// J and C are read once per step for all of its routes.
+//     o_P[j] = sum_rho C_P,e[j][rho] z_P[t][rho]  +  sum_b T_P[t][b][J_P,e[j][b]]
+// with z_P = D_P^T h (computed once per token by the GEMV-partials tiles,
+// summed here over their row slices in slice order) and the projection code
+// book T_P[t][b][c] = h_b . B_P[c] of the page, h_b the b-th length-d block
+// of h.  An fp32 T is 256 KiB per token and projection at H = 2048, more than
+// a CU's LDS, and a bf16 T is not accurate enough; so T is cut into slices of
+// 64 blocks (64 KiB) and one workgroup owns one (route, projection, slice):
+// it forms its slice of T on the matrix cores and then adds, for every
+// channel of the route's expert, T[b][J[j][b]] over its 64 blocks -- one
+// 4-byte LDS read and one add per index byte, where applying each code word
+// to h directly takes a 4d-byte read and d FMAs.  Each slice workgroup also
+// adds the low-rank term of a share of the channels (16-channel chunks dealt
+// out over the slices) and stores one partial per (route, slice, projection,
+// channel).  A finishing kernel adds a route's slice partials in slice order
+// and forms p = SiLU(o_gate) * o_up for the down projection (the joint
+// accumulation of the page, split across the two kernels).
+//
+// The grid is route-major (one token's use of an expert per workgroup set):
+// a route never waits for another route of its expert, and an expert routed
+// by two tokens is read twice, the second time mostly from the caches.  All
+// slices of one (route, projection) run on one XCD (grid x padded to a
+// multiple of 8; workgroups are dealt to the XCDs round robin by linear id),
+// so the 128-byte lines of J they share are fetched into one L2.
 #include "device_common.h"
 #include "launch.h"
 
@@ -23,408 +35,417 @@ namespace moe {
 namespace {
 
 constexpr int kThreads = 256;
-constexpr int kWaves = kThreads / MOE_WAVE;
-constexpr int kRT = 4;    // routes staged together
-constexpr int kZBatch = 16;
+constexpr int kSlice = 64;      // VQ blocks per slice of T
+constexpr int kCodes = 256;     // code words addressable by a uint8 index (entries >= K are zero)
+constexpr int kMaxR = 512;      // largest low-rank rank
+constexpr int kZBatch = 8;      // z slice partials loaded ahead of the stream
 
-// A code word of D bf16 values (D = 2, 4 or 8), loaded and kept in LDS as one
-// 4-, 8- or 16-byte word.
-template <int D> struct CodeWord;
-template <> struct CodeWord<8> { typedef uint4 T; };
-template <> struct CodeWord<4> { typedef uint2 T; };
-template <> struct CodeWord<2> { typedef uint32_t T; };
-__device__ __forceinline__ void unpack_cw(const uint4 v, float (&f)[8]) { unpack8(v, f); }
-__device__ __forceinline__ void unpack_cw(const uint2 v, float (&f)[4]) {
-    f[0] = bf16_lo(v.x); f[1] = bf16_hi(v.x); f[2] = bf16_lo(v.y); f[3] = bf16_hi(v.y);
+typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
+typedef float f32x4_t __attribute__((ext_vector_type(4)));
+
+// fp32 -> bf16 pattern, round to nearest even (finite inputs).
+__device__ __forceinline__ uint32_t bf16_rne(float x) {
+    const uint32_t u = __float_as_uint(x);
+    return (u + 0x7FFFu + ((u >> 16) & 1u)) >> 16;
 }
-__device__ __forceinline__ void unpack_cw(const uint32_t v, float (&f)[2]) { f[0] = bf16_lo(v); f[1] = bf16_hi(v); }
-__device__ __forceinline__ uint4 zero_cw(uint4) { return make_uint4(0u, 0u, 0u, 0u); }
+// x = hi + lo + O(2^-18 |x|), hi and lo bf16 patterns.
+__device__ __forceinline__ void split_bf16(float x, uint32_t& hi, uint32_t& lo) {
+    hi = bf16_rne(x);
+    lo = bf16_rne(x - __uint_as_float(hi << 16));
+}
 
-// RM consecutive low-rank coefficients (bf16) of one lane in (RM + 1) / 2
-// 32-bit words, loaded as one 2-, 4-, 8- or 16-byte word.
-template <int RM>
-struct Coef {
-    uint32_t w[(RM + 1) / 2];
-    __device__ __forceinline__ void load(const uint16_t* p) {
-        if constexpr (RM == 1) {
-            w[0] = __builtin_nontemporal_load(p);
-        } else if constexpr (RM == 2) {
-            w[0] = __builtin_nontemporal_load(reinterpret_cast<const uint32_t*>(p));
-        } else if constexpr (RM == 4) {
-            typedef unsigned int u32x2_t __attribute__((ext_vector_type(2)));
-            const u32x2_t v = __builtin_nontemporal_load(reinterpret_cast<const u32x2_t*>(p));
-            w[0] = v.x; w[1] = v.y;
-        } else {
-            const uint4 v = load_stream16(p);
-            w[0] = v.x; w[1] = v.y; w[2] = v.z; w[3] = v.w;
-        }
+// One lane's quarter of a channel's slice segment: 16 index bytes (blocks
+// 16 q .. 16 q + 15 of the slice) as 4 words.  `row` is the channel's index
+// row, `o` the quarter's byte offset in it, `last` the offset of the row's
+// last 16 (JW = 16) or 8 (JW = 8) valid bytes of the slice, `vb` the valid
+// bytes of the quarter (0, 8 or 16; the rest read as index 0 of a zero row
+// of T).  The loads always go out, from clamped addresses, and the value is
+// selected afterwards: a load inside a branch makes the compiler wait for
+// every load in flight at the branch's end.
+template <int JW>
+__device__ __forceinline__ uint4 load_quarter(const uint8_t* row, int o, int last, int vb) {
+    if constexpr (JW == 16) {
+        const u32x4_t x = __builtin_nontemporal_load(reinterpret_cast<const u32x4_t*>(row + min(o, last)));
+        return vb >= 16 ? make_uint4(x.x, x.y, x.z, x.w) : make_uint4(0u, 0u, 0u, 0u);
+    } else {
+        typedef unsigned int u32x2_t __attribute__((ext_vector_type(2)));
+        const u32x2_t a = __builtin_nontemporal_load(reinterpret_cast<const u32x2_t*>(row + min(o, last)));
+        const u32x2_t b = __builtin_nontemporal_load(reinterpret_cast<const u32x2_t*>(row + min(o + 8, last)));
+        return make_uint4(vb >= 8 ? a.x : 0u, vb >= 8 ? a.y : 0u, vb >= 16 ? b.x : 0u, vb >= 16 ? b.y : 0u);
     }
-    __device__ __forceinline__ float get(int m) const { return (m & 1) ? bf16_hi(w[m >> 1]) : bf16_lo(w[m >> 1]); }
-};
-__device__ __forceinline__ uint2 zero_cw(uint2) { return make_uint2(0u, 0u); }
-__device__ __forceinline__ uint32_t zero_cw(uint32_t) { return 0u; }
-
-// Overflow workgroups: runs of two or more routes (in block order, the first
-// kOverflow of them) share their routes with one more workgroup, which takes
-// the odd-numbered routes of the run while the run's own workgroup takes the
-// even-numbered ones, so that an expert routed twice ends with the others.
-constexpr int kOverflow = 4;
-
-// Per lane: whether plan block bb (< nb) starts a run of at least two routes.
-// A well-formed plan fills a run's first block first, so its row 1 is a route
-// exactly then (one-row blocks: the next block has the same expert).  Both
-// workgroups of a run evaluate this on the same plan, so they agree.
-__device__ __forceinline__ bool starts_multi_run(const PlanArgs& plan, int bb, int nb) {
-    const int bc = min(max(bb, 0), plan.max_blocks - 1);
-    const int e = plan.block_expert[bc];
-    const int ep = plan.block_expert[max(bc - 1, 0)];
-    const int en = plan.block_expert[min(bc + 1, plan.max_blocks - 1)];
-    const int r1 = plan.sorted_routes[(size_t)bc * plan.b + min(1, plan.b - 1)];
-    const bool two = plan.b > 1 ? r1 != plan.R : (bc + 1 < nb && en == e);
-    return bb >= 0 && bb < nb && (bc == 0 || ep != e) && e >= 0 && e < plan.E && two;
 }
 
-// Grid (plan blocks, ceil(I / (4*CPW))): workgroup (blk, cy) owns 4*CPW
-// channels of the expert whose run of blocks starts at blk; wave w owns CPW
-// of them.  Lane l owns VQ blocks 4*(l + 64*qb) .. +3 of length D (one 4-byte
-// index load per channel; h elements 4*D*(l + 64*qb) .. +4D-1) and low-rank
-// coordinates rho = RM*l .. RM*l + RM-1 (one load of RM bf16 per channel;
-// r % 8 == 0 makes a lane's coordinates all valid or all past r).  The index maps and
-// coefficients are kept in registers for every route of the expert; the two
-// code books go to LDS.  A route needs its h row and its finished z vectors
-// (the slice partials added in slice order) in LDS.
-// Loads are ordered by what they wait for: the plan rows come first; then,
-// before the index and coefficient stream, the row checks, the code books
-// and h and the z partials of row 0 (the expert's first route in a
-// well-formed plan, and at small batch usually its only one), since a load
-// queued behind the stream would wait for all of it.  Further routes are
-// staged rvq at a time.
-template <int D, int QB, int RM, int CPW>
+// sum over the lane's 16 blocks of T[16 q + i][byte i], in block order.  The
+// words pass through an empty asm so that the addresses are formed here, next
+// to their reads (else the compiler forms all of them early and holds them in
+// registers, leaving none for reads in flight).
+__device__ __forceinline__ float gather_quarter(const float* T, uint4 win, int q) {
+    uint32_t w[4] = {win.x, win.y, win.z, win.w};
+#pragma unroll
+    for (int k = 0; k < 4; ++k) asm volatile("" : "+v"(w[k]));
+    const float* Tq = T + q * 16 * kCodes;
+    float v[16];
+#pragma unroll
+    for (int i = 0; i < 16; ++i) v[i] = Tq[i * kCodes + ((w[i >> 2] >> (8 * (i & 3))) & 255u)];
+    float acc = 0.f;
+#pragma unroll
+    for (int i = 0; i < 16; ++i) acc += v[i];
+    return acc;
+}
+
+// Slice workgroup owning the low-rank term of the 16-channel chunk c.
+__device__ __forceinline__ int lr_owner(int c, int nslice) { return (c + c / nslice) % nslice; }
+
+constexpr int kPassCh = 64;                    // channels per pass (16 per wave, 4 lanes each)
+constexpr int kRegPasses = 12;                 // passes whose index quarters are requested up front
+constexpr int kLrPre = 4;                      // owned low-rank chunks whose coefficients are requested up front
+
+// Grid (x = 2 * route + projection, padded to a multiple of 8; y = T
+// slice).  Workgroup (r, P, s) computes slice s of projection P for route r:
+//  * T[b][c] = h_b . B_P[c] for the slice's 64 blocks b and the 256 code
+//    words c, on the matrix cores: [blocks x (h_hi | h_lo)] times
+//    [(B | B) x codes] with bf16 operands (h = h_hi + h_lo to 2^-18, B is
+//    bf16), fp32 accumulation; wave w forms codes 64 w .. 64 w + 63;
+//  * lane l of wave w, in pass p, takes channel 64 p + 16 w + l / 4 and the
+//    16 blocks 16 (l % 4) .. +15 of the slice (its 16 index bytes, one load),
+//    sums T over them, and (if the slice owns the channel's chunk) adds its
+//    quarter of the low-rank term; the quad's four sums are then added in a
+//    fixed order.
+// Everything that does not depend on the route's expert (h, z, the code
+// book) is requested together with its id; the index and coefficient
+// stream follows as soon as the id has arrived.
+template <int D, int JW>
 __global__ void __launch_bounds__(kThreads)
-gateup_vqlr_kernel(PlanArgs plan, VqArgs vq, const float* __restrict__ h, int H, int I, int rvq, float* __restrict__ p,
-                   int32_t* __restrict__ err) {
-    typedef typename CodeWord<D>::T CW;
-    constexpr int HPT = (QB * 64 * D + kThreads - 1) / kThreads;  // float4 of one h row per thread (H <= QB * 256 * D)
-    constexpr int ZPT = RM > 2 ? RM / 2 : 1;   // (projection, rho) items of one route per thread
-    __shared__ CW book[2][256];
-    extern __shared__ __align__(16) float dyn[];
-    float* hsm = dyn;                       // [rvq][H]
-    float* zsm = dyn + (size_t)rvq * H;     // [kRT][2][r]
-    const int b = plan.b;
+gateup_vqt_kernel(const int32_t* __restrict__ topk_ids, int R, FastDiv fk, int E, VqArgs vq,
+                  const float* __restrict__ h, int H, int I, float* __restrict__ vp, int32_t* __restrict__ err) {
+    static_assert(kThreads == 4 * MOE_WAVE, "four waves");
+    __shared__ float T[kSlice * kCodes];
+    __shared__ float zsm[kMaxR];
+    const int r = blockIdx.x >> 1;
+    const int P = blockIdx.x & 1;
+    const int s = blockIdx.y;
+    const int nslice = gridDim.y;
     const int tid = threadIdx.x;
     const int wave = tid / MOE_WAVE;
     const int lane = tid % MOE_WAVE;
-    const bool ovf = (int)blockIdx.x >= plan.max_blocks;  // an overflow workgroup
-    int blk = blockIdx.x;
-    if (ovf) {  // find the run: the (x - max_blocks)-th block starting a run of two or more routes
-        int nbo = plan.counts[0];
-        nbo = nbo < 0 ? 0 : min(nbo, plan.max_blocks);
-        int o = (int)blockIdx.x - plan.max_blocks;
-        blk = -1;
-        for (int c0 = 0; c0 < nbo; c0 += MOE_WAVE) {  // uniform
-            const uint64_t m = __ballot(starts_multi_run(plan, c0 + lane, nbo));
-            const int c = __popcll(m);
-            if (o < c) {
-                uint64_t mm = m;
-                for (int i = 0; i < o; ++i) mm &= mm - 1;
-                blk = c0 + __builtin_ctzll(mm);
-                break;
-            }
-            o -= c;
-        }
-        if (blk < 0) return;  // fewer such runs than overflow workgroups (uniform)
-    }
-    const int sp = ovf ? 1 : 0;  // this workgroup's first route of the run
+    const int g = lane / 16;   // MFMA K group / operand row group
+    const int q = lane % 4;    // gather quarter
+    if (r >= R) return;  // grid padding
 
-    // Round 1: counts, the previous, this and the next block's expert, the
-    // block's rows.
-    int nb = plan.counts[0];
-    const int e = plan.block_expert[blk];
-    const int eprev = blk > 0 ? plan.block_expert[blk - 1] : -1;
-    const int enext = plan.block_expert[min(blk + 1, plan.max_blocks - 1)];  // checked against nb below
-    int rv = plan.sorted_routes[(size_t)blk * b + min(lane, b - 1)];
-    if (lane >= b) rv = plan.R;
-    if (nb < 0 || nb > plan.max_blocks) {
-        if (blockIdx.x == 0 && blockIdx.y == 0 && tid == 0) atomicOr(err, DEVERR_BAD_COUNTS);
-        nb = nb < 0 ? 0 : plan.max_blocks;
+    const int nbk = H / D;                        // VQ blocks per channel
+    const int L = min(kSlice, nbk - s * kSlice);  // valid blocks of this slice (> 0)
+    const int rr = vq.r;
+    const int t = fk.div(r);
+    const uint16_t* Cb = P ? vq.C[1] : vq.C[0];
+    const uint16_t* Bb = P ? vq.B[1] : vq.B[0];
+    const uint8_t* Jb = P ? vq.J[1] : vq.J[0];
+    const float* zp = P ? vq.zpart[1] : vq.zpart[0];
+
+    // Round 1: the route's expert; code-book operands; h operands; z partials.
+    const int e = topk_ids[r];
+    uint4 bw[4];  // B operand words of N tiles 4 wave + u (code 16 (4 wave + u) + lane % 16)
+#pragma unroll
+    for (int u = 0; u < 4; ++u) {
+        const int c = 16 * (4 * wave + u) + lane % 16;
+        const uint16_t* cw = Bb + (size_t)min(c, vq.K - 1) * D;
+        uint4 v = make_uint4(0u, 0u, 0u, 0u);
+        if (c < vq.K) {
+            if constexpr (D == 8) {
+                if (g < 2) v = load16(cw);
+            } else if constexpr (D == 4) {
+                if (g == 0) {
+                    const uint2 a = *reinterpret_cast<const uint2*>(cw);
+                    v = make_uint4(a.x, a.y, a.x, a.y);
+                }
+            } else {
+                if (g == 0) {
+                    const uint32_t a = *reinterpret_cast<const uint32_t*>(cw);
+                    v = make_uint4(a, a, 0u, 0u);
+                }
+            }
+        }
+        bw[u] = v;
     }
-    if (blk >= nb) return;
-    if (e < 0 || e >= plan.E) {
-        if (!ovf && blockIdx.y == 0 && tid == 0) atomicOr(err, DEVERR_BAD_BLOCK_EXPERT);
+    float hx[4][D];  // h of block 16 m + lane % 16 of the slice (zero past the channel's blocks)
+#pragma unroll
+    for (int m = 0; m < 4; ++m) {
+        const int b = 16 * m + lane % 16;
+        const bool in = b < L && (D == 8 ? g < 2 : g == 0);
+        const float* src = h + (size_t)t * H + (size_t)(s * kSlice + min(b, L - 1)) * D;
+        if constexpr (D == 2) {
+            const float2 a = *reinterpret_cast<const float2*>(src);
+            hx[m][0] = in ? a.x : 0.f;
+            hx[m][1] = in ? a.y : 0.f;
+        } else {
+#pragma unroll
+            for (int x = 0; x < D; x += 4) {
+                const float4 a = *reinterpret_cast<const float4*>(src + x);
+                hx[m][x] = in ? a.x : 0.f; hx[m][x + 1] = in ? a.y : 0.f;
+                hx[m][x + 2] = in ? a.z : 0.f; hx[m][x + 3] = in ? a.w : 0.f;
+            }
+        }
+    }
+    // z partials of coordinate rho = tid (the first kZBatch slices; threads
+    // past r load nothing)
+    float zx[kZBatch];
+#pragma unroll
+    for (int u = 0; u < kZBatch; ++u)
+        zx[u] = zp[((size_t)min(u, vq.zslices - 1) * vq.M + t) * rr + min(tid, rr - 1)];
+    if (e < 0 || e >= E) {  // an invalid route has no output (uniform)
+        if (P == 0 && s == 0 && tid == 0) atomicOr(err, DEVERR_BAD_ROUTE_ID);
         return;
     }
-    if (eprev == e) return;  // not the first block of the expert's run (uniform)
-    // A run's own workgroup shares it if it is among the first kOverflow runs
-    // of two or more routes (rank over the blocks before it).
-    bool split = ovf;
-    if (!ovf && starts_multi_run(plan, blk, min(max(nb, 0), plan.max_blocks))) {
-        int rank = 0;
-        for (int c0 = 0; c0 < blk; c0 += MOE_WAVE)  // uniform
-            rank += __popcll(__ballot(c0 + lane < blk && starts_multi_run(plan, c0 + lane, nb)));
-        split = rank < kOverflow;
-    }
-    const int nbk = H / D;  // VQ blocks per channel
-    const int r = vq.r;
-    const int H4 = H / 4;
-    const int j0 = (blockIdx.y * kWaves + wave) * CPW;
-    const bool active = j0 < I;  // inactive waves still take part in the barriers
-
-    // Round 2 (clamped, always-valid addresses).
-    const int idv = plan.topk_ids[min(max(rv, 0), plan.R - 1)];
-    // (the argument struct's arrays are indexed by compile-time constants or
-    // through a select: a run-time index would load the pointer from the
-    // kernel-argument segment with a vector load)
-    const int r0 = __builtin_amdgcn_readlane(rv, min(sp, MOE_WAVE - 1));  // row sp: the run's route sp if rows 0..sp are routes
-    const int t0 = plan.fk.div(min(max(r0, 0), plan.R - 1));
-    CW bk[2];
-#pragma unroll
-    for (int u = 0; u < 2; ++u) {
-        const int i = tid + kThreads * u;
-        bk[u] = *reinterpret_cast<const CW*>(vq.B[i >> 8] + (size_t)min(i & 255, vq.K - 1) * D);
-    }
-    float4 h0[HPT];
-#pragma unroll
-    for (int v = 0; v < HPT; ++v)
-        h0[v] = reinterpret_cast<const float4*>(h + (size_t)t0 * H)[min(tid + kThreads * v, H4 - 1)];
-    float zx[ZPT][kZBatch];
-#pragma unroll
-    for (int w = 0; w < ZPT; ++w) {
-        const int it = min(tid + kThreads * w, 2 * r - 1);
-        const int P = it >= r ? 1 : 0, rho = it - P * r;
-#pragma unroll
-        for (int u = 0; u < kZBatch; ++u)
-            zx[w][u] = (P ? vq.zpart[1] : vq.zpart[0])[((size_t)min(u, vq.zslices - 1) * vq.M + t0) * r + rho];
-    }
-
     __builtin_amdgcn_sched_barrier(0);  // keeps the loads above ahead of the stream below
 
-    // The index and coefficient stream.
-    uint32_t jw[2][CPW][QB];
-    Coef<RM> cw[2][CPW];  // bf16 patterns, converted (and masked) where used
-    const int rl = r / RM;  // lanes holding coefficients (r % 8 == 0, RM <= 8)
+    // The index stream: pass p, lane quarter q of channel 64 p + 16 wave + lane / 4.
+    const int npass = (I + kPassCh - 1) / kPassCh;
+    const int vb = min(max(L - 16 * q, 0), 16);
+    const int jlast = s * kSlice + L - JW;  // offset of the slice's last JW valid bytes in a row
+    uint4 jq[kRegPasses];
 #pragma unroll
-    for (int P = 0; P < 2; ++P)
-#pragma unroll
-        for (int c = 0; c < CPW; ++c) {
-            const int j = min(j0 + c, I - 1);
-            const uint8_t* jrow = vq.J[P] + ((size_t)e * I + j) * nbk;
-            const uint16_t* crow = vq.C[P] + ((size_t)e * I + j) * r;
-            // Unconditional loads of clamped addresses, used as loaded: a
-            // select here would let the compiler put the load in a branch,
-            // which is waited for at the branch's end, one load at a time.
-            // Lanes past the last block or coordinate are masked where used.
-#pragma unroll
-            for (int qb = 0; qb < QB; ++qb) {
-                const int b4 = 4 * (lane + MOE_WAVE * qb);
-                jw[P][c][qb] = __builtin_nontemporal_load(reinterpret_cast<const uint32_t*>(jrow + min(b4, nbk - 4)));
-            }
-            cw[P][c].load(crow + RM * min(lane, rl - 1));
-        }
-
-    // Round 2 into LDS (in the stream's basic block, so that nothing moves
-    // these loads behind it): the code books, and slot 0 with row 0's h and z.
-#pragma unroll
-    for (int u = 0; u < 2; ++u) {
-        const int i = tid + kThreads * u;
-        book[i >> 8][i & 255] = (i & 255) < vq.K ? bk[u] : zero_cw(bk[u]);
+    for (int p = 0; p < kRegPasses; ++p) {
+        const int j = min(kPassCh * p + 16 * wave + lane / 4, I - 1);
+        jq[p] = load_quarter<JW>(Jb + ((size_t)e * I + j) * nbk, s * kSlice + 16 * q, jlast, p < npass ? vb : 0);
     }
+    // The passes whose 16-channel chunk this slice owns for the low-rank term
+    // (wave-uniform), and the coefficients of the first kLrPre of them: the
+    // lane's 16 of the first 64 coordinates, rho = 16 q .. 16 q + 15.
+    int po[kLrPre];
+    int nown = 0;
 #pragma unroll
-    for (int v = 0; v < HPT; ++v)  // unconditional (clamped duplicates store the same value)
-        reinterpret_cast<float4*>(hsm)[min(tid + kThreads * v, H4 - 1)] = h0[v];
+    for (int u = 0; u < kLrPre; ++u) po[u] = -1;
+    for (int p = 0; p < npass; ++p) {
+        if (lr_owner(4 * p + wave, nslice) != s) continue;
 #pragma unroll
-    for (int w = 0; w < ZPT; ++w) {
-        const int it = tid + kThreads * w;
+        for (int u = 0; u < kLrPre; ++u)
+            if (u == nown) po[u] = p;
+        ++nown;
+    }
+    uint4 cpre[kLrPre][2];
+#pragma unroll
+    for (int u = 0; u < kLrPre; ++u) {
+        const int j = min(kPassCh * max(po[u], 0) + 16 * wave + lane / 4, I - 1);
+        const uint16_t* crow = Cb + ((size_t)e * I + j) * rr;
+        const uint4 a = load_stream16(crow + min(16 * q, rr - 8));
+        const uint4 b = load_stream16(crow + min(16 * q + 8, rr - 8));
+        const bool use = po[u] >= 0;
+        cpre[u][0] = use && 16 * q < rr ? a : make_uint4(0u, 0u, 0u, 0u);
+        cpre[u][1] = use && 16 * q + 8 < rr ? b : make_uint4(0u, 0u, 0u, 0u);
+    }
+
+    // T on the matrix cores (its operands arrived before the stream).
+    {
+        uint4 aw[4];  // A operand words of M tile m: 8 bf16 of K group g
+#pragma unroll
+        for (int m = 0; m < 4; ++m) {
+            uint32_t hi[D], lo[D];
+#pragma unroll
+            for (int x = 0; x < D; ++x) split_bf16(hx[m][x], hi[x], lo[x]);
+            uint32_t k8[8];  // K slots 8 g .. 8 g + 7 (zero past 2 D)
+            if constexpr (D == 8) {
+#pragma unroll
+                for (int x = 0; x < 8; ++x) k8[x] = g == 0 ? hi[x] : lo[x];
+            } else if constexpr (D == 4) {
+#pragma unroll
+                for (int x = 0; x < 4; ++x) { k8[x] = hi[x]; k8[4 + x] = lo[x]; }
+            } else {
+                k8[0] = hi[0]; k8[1] = hi[1]; k8[2] = lo[0]; k8[3] = lo[1];
+                k8[4] = k8[5] = k8[6] = k8[7] = 0u;
+            }
+            aw[m] = make_uint4(k8[0] | (k8[1] << 16), k8[2] | (k8[3] << 16), k8[4] | (k8[5] << 16),
+                               k8[6] | (k8[7] << 16));
+        }
+#pragma unroll
+        for (int m = 0; m < 4; ++m)
+#pragma unroll
+            for (int u = 0; u < 4; ++u) {
+                const f32x4_t zero = {0.f, 0.f, 0.f, 0.f};
+                const f32x4_t d4 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(
+                    __builtin_bit_cast(bf16x8_t, aw[m]), __builtin_bit_cast(bf16x8_t, bw[u]), zero, 0, 0, 0);
+                // lane holds T[16 m + 4 g + i][16 (4 wave + u) + lane % 16]
+                float* dst = T + (16 * m + 4 * g) * kCodes + 16 * (4 * wave + u) + lane % 16;
+#pragma unroll
+                for (int i = 0; i < 4; ++i) dst[i * kCodes] = d4[i];
+            }
+    }
+    // z (slice partials in slice order) into LDS; coordinates past 256 and
+    // slices past kZBatch are loaded here.
+    if (tid < rr) {
         float z = 0.f;
 #pragma unroll
-        for (int u = 0; u < kZBatch; ++u) z += u < vq.zslices ? zx[w][u] : 0.f;  // slice order
-        if (it < 2 * r) {
-            const int P = it >= r ? 1 : 0, rho = it - P * r;
-            for (int sl = kZBatch; sl < vq.zslices; ++sl) z += (P ? vq.zpart[1] : vq.zpart[0])[((size_t)sl * vq.M + t0) * r + rho];
-            zsm[it] = z;
-        }
+        for (int u = 0; u < kZBatch; ++u) z += u < vq.zslices ? zx[u] : 0.f;
+        for (int sl = kZBatch; sl < vq.zslices; ++sl) z += zp[((size_t)sl * vq.M + t) * rr + tid];
+        zsm[tid] = z;
     }
-    auto rows_ok = [&](int rvx, int idx) {
-        const bool ok = rvx >= 0 && rvx < plan.R && idx == e;
-        if (!ok && rvx != plan.R && wave == 0 && !ovf && blockIdx.y == 0) atomicOr(err, DEVERR_BAD_PLAN);
-        return __ballot(ok);
-    };
-    uint64_t todo = rows_ok(rv, idv);
+    for (int rho = tid + kThreads; rho < rr; rho += kThreads) {
+        float z = 0.f;
+        for (int sl = 0; sl < vq.zslices; ++sl) z += zp[((size_t)sl * vq.M + t) * rr + rho];
+        zsm[rho] = z;
+    }
+    for (int rho = rr + tid; rho < kMaxR; rho += kThreads) zsm[rho] = 0.f;  // read against zero coefficients
     __syncthreads();
 
-    // One route from LDS slot i: o_P[j] = C_e[j] . z + sum over blocks of the
-    // selected code words applied to h's blocks, then p = SiLU(o_gate) * o_up.
-    auto compute = [&](int i, int route) {
-        float acc[2][CPW];
+    // Low-rank quarter of the lane's channel in an owned pass: coordinates
+    // 64 c0 + 16 q + x, in rho order; the first 64 from the prefetched
+    // coefficients, further ones loaded here.
+    auto lr_dot = [&](const uint4 (&c)[2], int rho0, float acc) {
 #pragma unroll
-        for (int P = 0; P < 2; ++P)
+        for (int u = 0; u < 2; ++u) {
+            float f[8];
+            unpack8(c[u], f);
+            const int rb = min(rho0 + 8 * u, kMaxR - 8);  // coefficients past r are zero
 #pragma unroll
-            for (int c = 0; c < CPW; ++c) acc[P][c] = 0.f;
-        if (lane < rl) {
-#pragma unroll
-            for (int P = 0; P < 2; ++P) {
-                float z[RM];
-                const float* zr = zsm + (i * 2 + P) * r + RM * lane;
-#pragma unroll
-                for (int m = 0; m < RM; ++m) z[m] = zr[m];
-#pragma unroll
-                for (int c = 0; c < CPW; ++c)
-#pragma unroll
-                    for (int m = 0; m < RM; ++m) acc[P][c] = fmaf(cw[P][c].get(m), z[m], acc[P][c]);
-            }
+            for (int x = 0; x < 8; ++x) acc = fmaf(f[x], zsm[rb + x], acc);
         }
-#pragma unroll
-        for (int qb = 0; qb < QB; ++qb) {
-            const int b4 = 4 * (lane + MOE_WAVE * qb);
-            if (b4 >= nbk) continue;
-            const float4* hr = reinterpret_cast<const float4*>(hsm + (size_t)i * H + b4 * D);
-            float hv[4 * D];
-#pragma unroll
-            for (int v = 0; v < D; ++v) {
-                const float4 x = hr[v];
-                hv[4 * v] = x.x; hv[4 * v + 1] = x.y; hv[4 * v + 2] = x.z; hv[4 * v + 3] = x.w;
-            }
-#pragma unroll
-            for (int P = 0; P < 2; ++P)
-#pragma unroll
-                for (int c = 0; c < CPW; ++c)
-#pragma unroll
-                    for (int x = 0; x < 4; ++x) {
-                        float cw[D];
-                        unpack_cw(book[P][(jw[P][c][qb] >> (8 * x)) & 255u], cw);
-#pragma unroll
-                        for (int y = 0; y < D; ++y) acc[P][c] = fmaf(cw[y], hv[D * x + y], acc[P][c]);
-                    }
+        return acc;
+    };
+    auto lr_rest = [&](int p, float acc) {  // coordinates 64 .. r - 1
+        const int j = min(kPassCh * p + 16 * wave + lane / 4, I - 1);
+        const uint16_t* crow = Cb + ((size_t)e * I + j) * rr;
+        for (int c0 = 64; c0 < rr; c0 += 64) {
+            uint4 c[2];
+            const int rho0 = c0 + 16 * q;
+            const uint4 a = load_stream16(crow + min(rho0, rr - 8));
+            const uint4 b = load_stream16(crow + min(rho0 + 8, rr - 8));
+            c[0] = rho0 < rr ? a : make_uint4(0u, 0u, 0u, 0u);
+            c[1] = rho0 + 8 < rr ? b : make_uint4(0u, 0u, 0u, 0u);
+            acc = lr_dot(c, rho0, acc);
         }
-#pragma unroll
-        for (int c = 0; c < CPW; ++c) {
-            const float og = wave_sum(acc[0][c]);
-            const float ou = wave_sum(acc[1][c]);
-            if (lane == 0 && j0 + c < I) p[(size_t)route * I + j0 + c] = silu_mul(og, ou);
-        }
+        return acc;
     };
 
-    // The routes of the run in order (the first block's valid rows, then the
-    // following blocks'): all of them, or -- for a shared run -- every other
-    // one from sp.  Row sp's h and z are in slot 0 already if rows 0..sp of
-    // the first block are routes; other routes are staged rvq at a time.
-    const uint64_t lowmask = (2ull << sp) - 1;
-    bool pre = sp < b && (todo & lowmask) == lowmask;
-    int bb = blk, n = 0;
-    for (;;) {
-        if (!todo) {
-            if (++bb >= nb || (bb == blk + 1 ? enext : plan.block_expert[bb]) != e) break;
-            int rv2 = plan.sorted_routes[(size_t)bb * b + min(lane, b - 1)];
-            if (lane >= b) rv2 = plan.R;
-            todo = rows_ok(rv2, plan.topk_ids[min(max(rv2, 0), plan.R - 1)]);
-            rv = rv2;
-            continue;
+    // The gathers, pass by pass as the index words arrive (they were
+    // requested before the coefficients).
+    float acc[kRegPasses];
+#pragma unroll
+    for (int p = 0; p < kRegPasses; ++p) acc[p] = p < npass ? gather_quarter(T, jq[p], q) : 0.f;
+    // The low-rank quarters of the owned passes, added where they belong by
+    // compile-time selects (a run-time index would move the array to scratch
+    // memory).
+#pragma unroll
+    for (int u = 0; u < kLrPre; ++u) {
+        const int p = po[u];  // wave-uniform
+        if (p < 0) continue;
+        float v = lr_dot(cpre[u], 16 * q, 0.f);
+        if (rr > 64) v = lr_rest(p, v);
+#pragma unroll
+        for (int pp = 0; pp < kRegPasses; ++pp)
+            if (pp == p) acc[pp] += v;
+    }
+    for (int p = 0, n = 0; p < min(npass, kRegPasses); ++p) {  // owned passes beyond the prefetched ones
+        if (lr_owner(4 * p + wave, nslice) != s || n++ < kLrPre) continue;
+        const uint4 z0 = make_uint4(0u, 0u, 0u, 0u);
+        const uint4 cz[2] = {z0, z0};
+        const int j = min(kPassCh * p + 16 * wave + lane / 4, I - 1);
+        const uint16_t* crow = Cb + ((size_t)e * I + j) * rr;
+        uint4 c[2] = {cz[0], cz[1]};
+        const uint4 a = load_stream16(crow + min(16 * q, rr - 8));
+        const uint4 b = load_stream16(crow + min(16 * q + 8, rr - 8));
+        c[0] = 16 * q < rr ? a : z0;
+        c[1] = 16 * q + 8 < rr ? b : z0;
+        float v = lr_dot(c, 16 * q, 0.f);
+        if (rr > 64) v = lr_rest(p, v);
+#pragma unroll
+        for (int pp = 0; pp < kRegPasses; ++pp)
+            if (pp == p) acc[pp] += v;
+    }
+    // quad sums (q0 + q1) + (q2 + q3), in every lane of the quad; lane q of a
+    // quad stores passes 4 m + q
+#pragma unroll
+    for (int p = 0; p < kRegPasses; ++p) {
+        acc[p] += dpp<MOE_DPP_QUAD_XOR1>(acc[p]);
+        acc[p] += dpp<MOE_DPP_QUAD_XOR2>(acc[p]);
+    }
+    float* dst = vp + ((size_t)(r * nslice + s) * 2 + P) * I + 16 * wave + lane / 4;
+#pragma unroll
+    for (int m = 0; m < kRegPasses / 4; ++m) {
+        float v = acc[4 * m];
+#pragma unroll
+        for (int x = 1; x < 4; ++x) v = q == x ? acc[4 * m + x] : v;
+        const int p = 4 * m + q;
+        if (p < npass && kPassCh * p + 16 * wave + lane / 4 < I) dst[kPassCh * p] = v;
+    }
+    for (int p = kRegPasses; p < npass; ++p) {  // further passes: indices loaded here
+        const int j = kPassCh * p + 16 * wave + lane / 4;
+        const uint4 w = load_quarter<JW>(Jb + ((size_t)e * I + min(j, I - 1)) * nbk, s * kSlice + 16 * q, jlast, vb);
+        float a = gather_quarter(T, w, q);
+        if (lr_owner(4 * p + wave, nslice) == s) {
+            const uint4 z0 = make_uint4(0u, 0u, 0u, 0u);
+            const uint16_t* crow = Cb + ((size_t)e * I + min(j, I - 1)) * rr;
+            uint4 c[2];
+            const uint4 ca = load_stream16(crow + min(16 * q, rr - 8));
+            const uint4 cb = load_stream16(crow + min(16 * q + 8, rr - 8));
+            c[0] = 16 * q < rr ? ca : z0;
+            c[1] = 16 * q + 8 < rr ? cb : z0;
+            float v = lr_dot(c, 16 * q, 0.f);
+            if (rr > 64) v = lr_rest(p, v);
+            a += v;
         }
-        // the next routes of this workgroup, at most rvq, the first possibly in slot 0
-        int rt[kRT], rq[kRT];
-        int nr = 0;
-#pragma unroll
-        for (int i = 0; i < kRT; ++i) {
-            rt[i] = -1;
-            rq[i] = -1;
-        }
-        while (todo && nr < rvq) {  // uniform
-            const int q = __builtin_ctzll(todo);
-            todo &= todo - 1;
-            const bool mine = !split || (n & 1) == sp;
-            ++n;
-            if (!mine) continue;
-#pragma unroll
-            for (int i = 0; i < kRT; ++i)
-                if (i == nr) {
-                    rt[i] = __builtin_amdgcn_readlane(rv, q);
-                    rq[i] = q;
-                }
-            ++nr;
-        }
-        if (nr == 0) continue;
-        const bool have0 = pre && bb == blk && rq[0] == sp;  // slot 0 already holds the first
-        pre = false;
-        if (!have0 || nr > 1) {
-            __syncthreads();  // the previous routes' slots are no longer read
-#pragma unroll
-            for (int i = 0; i < kRT; ++i) {
-                if (i >= nr || (i == 0 && have0)) continue;
-                const float4* src = reinterpret_cast<const float4*>(h + (size_t)plan.fk.div(rt[i]) * H);
-                float4* dst = reinterpret_cast<float4*>(hsm + (size_t)i * H);
-                for (int c4 = tid; c4 < H4; c4 += kThreads) dst[c4] = src[c4];
-            }
-            for (int it = tid; it < nr * 2 * r; it += kThreads) {
-                const int i = it / (2 * r), rem = it - i * 2 * r, P = rem / r, rho = rem - P * r;
-                if (i == 0 && have0) continue;
-                int ti = 0;
-#pragma unroll
-                for (int ii = 0; ii < kRT; ++ii)
-                    if (ii == i) ti = plan.fk.div(rt[ii]);
-                float z = 0.f;
-                for (int sl0 = 0; sl0 < vq.zslices; sl0 += kZBatch) {
-                    float x[kZBatch];
-#pragma unroll
-                    for (int u = 0; u < kZBatch; ++u)
-                        x[u] = (P ? vq.zpart[1] : vq.zpart[0])[((size_t)min(sl0 + u, vq.zslices - 1) * vq.M + ti) * r + rho];
-#pragma unroll
-                    for (int u = 0; u < kZBatch; ++u) z += sl0 + u < vq.zslices ? x[u] : 0.f;  // slice order
-                }
-                zsm[it] = z;
-            }
-            __syncthreads();
-        }
-        if (!active) continue;
-#pragma unroll
-        for (int i = 0; i < kRT; ++i) {
-            if (i >= nr) break;
-            compute(i, rt[i]);
-        }
+        a += dpp<MOE_DPP_QUAD_XOR1>(a);
+        a += dpp<MOE_DPP_QUAD_XOR2>(a);
+        if (q == 0 && j < I) vp[((size_t)(r * nslice + s) * 2 + P) * I + j] = a;
     }
 }
 
-template <int D, int QB, int RM, int CPW>
-hipError_t vq_launch(const PlanArgs& plan, const VqArgs& vq, const float* h, int H, int I, float* p, int32_t* err,
-                     hipStream_t stream) {
-    // x: the plan blocks, then the overflow workgroups
-    const dim3 grid(plan.max_blocks + kOverflow, (I + kWaves * CPW - 1) / (kWaves * CPW));
-    const int rvq = H <= 4096 ? kRT : 2;  // staged h rows: <= 64 KiB
-    const size_t lds = ((size_t)rvq * H + (size_t)kRT * 2 * vq.r) * sizeof(float);
-    MOE_LAUNCH((gateup_vqlr_kernel<D, QB, RM, CPW>), grid, dim3(kThreads), lds, stream, plan, vq, h, H, I, rvq, p, err);
+template <int D>
+hipError_t vqt_d(const int32_t* ids, int R, int k, int E, const VqArgs& vq, const float* h, int H, int I, float* vp,
+                 int32_t* err, hipStream_t stream) {
+    const int nslice = (H / D + kSlice - 1) / kSlice;
+    const dim3 grid((2 * R + 7) / 8 * 8, nslice);
+    // 16-byte index loads when every quarter segment is 16-byte aligned
+    if ((H / D) % 16 == 0)
+        MOE_LAUNCH((gateup_vqt_kernel<D, 16>), grid, dim3(kThreads), 0, stream, ids, R, FastDiv((uint32_t)k), E, vq,
+                   h, H, I, vp, err);
+    else
+        MOE_LAUNCH((gateup_vqt_kernel<D, 8>), grid, dim3(kThreads), 0, stream, ids, R, FastDiv((uint32_t)k), E, vq,
+                   h, H, I, vp, err);
     return hipGetLastError();
 }
 
-// Channels per wave: 8 for the smallest register tile (H <= 2048, r <= 64),
-// else 4.
-template <int D, int QB>
-hipError_t vq_rm(const PlanArgs& plan, const VqArgs& vq, const float* h, int H, int I, float* p, int32_t* err,
-                 hipStream_t stream) {
-    const int RM = (vq.r + 63) / 64;
-    if (RM <= 1) return vq_launch<D, QB, 1, QB == 1 ? 8 : 4>(plan, vq, h, H, I, p, err, stream);
-    if (RM <= 2) return vq_launch<D, QB, 2, 4>(plan, vq, h, H, I, p, err, stream);
-    if (RM <= 4) return vq_launch<D, QB, 4, 4>(plan, vq, h, H, I, p, err, stream);
-    if (RM <= 8) return vq_launch<D, QB, 8, 4>(plan, vq, h, H, I, p, err, stream);
-    return hipErrorInvalidValue;
-}
+// One thread per (route, channel): the slice partials of both projections,
+// all loads issued together, added in slice order.
+constexpr int kMaxSlices = 16;
 
-// Lane blocks: QB = ceil(H / D / 256) groups of four VQ blocks per lane.
-template <int D>
-hipError_t vq_qb(const PlanArgs& plan, const VqArgs& vq, const float* h, int H, int I, float* p, int32_t* err,
-                 hipStream_t stream) {
-    const int QB = (H / D + 255) / 256;
-    if (QB <= 1) return vq_rm<D, 1>(plan, vq, h, H, I, p, err, stream);
-    if (QB <= 2) return vq_rm<D, 2>(plan, vq, h, H, I, p, err, stream);
-    if (QB <= 4) return vq_rm<D, 4>(plan, vq, h, H, I, p, err, stream);
-    return hipErrorInvalidValue;
+__global__ void __launch_bounds__(kThreads)
+vq_finish_kernel(const float* __restrict__ vp, int R, int I, int nslice, float* __restrict__ p) {
+    const int j = blockIdx.x * kThreads + threadIdx.x;
+    const int r = blockIdx.y;
+    if (j >= I) return;
+    const float* src = vp + (size_t)r * nslice * 2 * I + j;
+    float g[kMaxSlices], u[kMaxSlices];
+#pragma unroll
+    for (int sl = 0; sl < kMaxSlices; ++sl) {
+        const int sc = min(sl, nslice - 1);
+        g[sl] = src[(size_t)(2 * sc) * I];
+        u[sl] = src[(size_t)(2 * sc + 1) * I];
+    }
+    float og = 0.f, ou = 0.f;
+#pragma unroll
+    for (int sl = 0; sl < kMaxSlices; ++sl) {
+        og += sl < nslice ? g[sl] : 0.f;
+        ou += sl < nslice ? u[sl] : 0.f;
+    }
+    p[(size_t)r * I + j] = silu_mul(og, ou);
 }
 
 }  // namespace
 
-hipError_t launch_gateup_vqlr(const PlanArgs& plan, const VqArgs& vq, const float* h, int H, int I, float* p,
-                              int32_t* err, hipStream_t stream) {
-    if (vq.K < 1 || vq.K > 256 || H % (8 * vq.d)) return hipErrorInvalidValue;
-    if (vq.d == 8) return vq_qb<8>(plan, vq, h, H, I, p, err, stream);
-    if (vq.d == 4) return vq_qb<4>(plan, vq, h, H, I, p, err, stream);
-    if (vq.d == 2) return vq_qb<2>(plan, vq, h, H, I, p, err, stream);
+hipError_t launch_vq_finish(const float* vp, int R, int I, int nslice, float* p, hipStream_t stream) {
+    if (nslice < 1 || nslice > kMaxSlices || R < 1) return hipErrorInvalidValue;
+    MOE_LAUNCH(vq_finish_kernel, dim3((I + kThreads - 1) / kThreads, R), dim3(kThreads), 0, stream, vp, R, I,
+               nslice, p);
+    return hipGetLastError();
+}
+
+int vq_slices(int H, int d) { return (H / d + kSlice - 1) / kSlice; }
+
+hipError_t launch_gateup_vqlr(const int32_t* topk_ids, int R, int k, int E, const VqArgs& vq, const float* h, int H,
+                              int I, float* vp, int32_t* err, hipStream_t stream) {
+    if (vq.K < 1 || vq.K > kCodes || H % (8 * vq.d) || vq.r < 8 || vq.r > kMaxR || vq.r % 8 || R < 1 || k < 1)
+        return hipErrorInvalidValue;
+    if (vq.d == 8) return vqt_d<8>(topk_ids, R, k, E, vq, h, H, I, vp, err, stream);
+    if (vq.d == 4) return vqt_d<4>(topk_ids, R, k, E, vq, h, H, I, vp, err, stream);
+    if (vq.d == 2) return vqt_d<2>(topk_ids, R, k, E, vq, h, H, I, vp, err, stream);
     return hipErrorInvalidValue;
 }
 
