@@ -85,7 +85,8 @@ enum {
  *  vq_d, vq_K, lr_r   VQ block length, code book size and low-rank rank for
  *              MOE_WFORMAT_VQLR: vq_d in {2, 4, 8}, 1 <= vq_K <= 256,
  *              H % (8*vq_d) == 0, H/vq_d <= 1024, lr_r % 8 == 0 and
- *              8 <= lr_r <= 512.  Ignored for dense.
+ *              0 <= lr_r <= 512 (0: VQ only, no low-rank term; lr_basis
+ *              and lr_coef may then be NULL).  Ignored for dense.
  *  max_keep    largest channel top-K moe_expert_forward will be asked for
  *              (0 = channel-sparse mode unused); <= top_k*I, top_k*I <= 8192,
  *              dense format only.

@@ -82,7 +82,7 @@ moe_status check_config(const moe_config* c) {
     if (c->wformat == MOE_WFORMAT_VQLR) {
         if (c->vq_d != 2 && c->vq_d != 4 && c->vq_d != 8) return MOE_ERR_UNSUPPORTED;
         if (c->vq_K < 1 || c->vq_K > 256 || c->H % (8 * c->vq_d) || c->H / c->vq_d > 1024) return MOE_ERR_UNSUPPORTED;
-        if (c->lr_r % 8 || c->lr_r < 8 || c->lr_r > 512) return MOE_ERR_UNSUPPORTED;
+        if (c->lr_r % 8 || c->lr_r < 0 || c->lr_r > 512) return MOE_ERR_UNSUPPORTED;  // 0: VQ only
     }
     if (c->max_keep > 0) {
         if (c->wformat != MOE_WFORMAT_DENSE) return MOE_ERR_UNSUPPORTED;
@@ -100,9 +100,10 @@ moe_status check_weights(const moe_config* c, const moe_weights* w) {
         if (!aligned(w->w_gate, 16) || !aligned(w->w_up, 16)) return MOE_ERR_INVALID_ARG;
     } else {
         for (int P = 0; P < 2; ++P) {
-            if (!w->lr_basis[P] || !w->lr_coef[P] || !w->vq_book[P] || !w->vq_idx[P]) return MOE_ERR_INVALID_ARG;
-            if (!aligned(w->lr_basis[P], 16) || !aligned(w->lr_coef[P], 16) || !aligned(w->vq_book[P], 16) ||
-                !aligned(w->vq_idx[P], 16))
+            if (!w->vq_book[P] || !w->vq_idx[P] || !aligned(w->vq_book[P], 16) || !aligned(w->vq_idx[P], 16))
+                return MOE_ERR_INVALID_ARG;
+            if (c->lr_r == 0) continue;  // VQ only: no low-rank term
+            if (!w->lr_basis[P] || !w->lr_coef[P] || !aligned(w->lr_basis[P], 16) || !aligned(w->lr_coef[P], 16))
                 return MOE_ERR_INVALID_ARG;
         }
     }
@@ -115,7 +116,7 @@ moe_status check_weights(const moe_config* c, const moe_weights* w) {
 // base address, also the buffer addresses inside it (256-byte aligned).
 size_t workspace_layout(const moe_config& c, size_t MT, char* base, Workspace* ws) {
     const size_t R = MT * c.top_k;
-    const size_t zsl = c.wformat == MOE_WFORMAT_VQLR ? moe::gemv_slices(c.H, c.lr_r) : 0;
+    const size_t zsl = c.wformat == MOE_WFORMAT_VQLR && c.lr_r > 0 ? moe::gemv_slices(c.H, c.lr_r) : 0;
     // down partials: one chunk per route on the split path; the fused path
     // (one token) writes dense_chunks of them for each of its top_k routes
     size_t down = R * (size_t)moe::down_chunks(c.I) * c.H;
@@ -319,7 +320,7 @@ moe_status expert_forward_impl(const Exec& x, bool z_ready, const float* h, int3
         } else {
             moe::GemvJob jobs[2] = {{x.w.lr_basis[0], c.lr_r, x.ws.zpart[0]},
                                     {x.w.lr_basis[1], c.lr_r, x.ws.zpart[1]}};
-            if (!z_ready) {  // else computed by the routing launch of this step
+            if (!z_ready && c.lr_r > 0) {  // else computed by the routing launch of this step (or no low rank)
                 Launch l(x.prof, MOE_KERNEL_VQ_SHARED);
                 e = moe::launch_gemv_partials(h, M, c.H, jobs, 2, s);
                 l.done();
@@ -332,7 +333,7 @@ moe_status expert_forward_impl(const Exec& x, bool z_ready, const float* h, int3
                 vq.J[P] = x.w.vq_idx[P];
                 vq.zpart[P] = x.ws.zpart[P];
             }
-            vq.zslices = moe::gemv_slices(c.H, c.lr_r);
+            vq.zslices = c.lr_r > 0 ? moe::gemv_slices(c.H, c.lr_r) : 0;
             vq.M = M;
             vq.r = c.lr_r;
             vq.K = c.vq_K;
@@ -400,8 +401,8 @@ moe_status decode_step_impl(const Exec& x, const float* h, int32_t M, int32_t* t
     const int nsl = moe::router_slices(c.H, c.E);
     if (M != 1 || c.wformat != MOE_WFORMAT_DENSE || !moe::decode_fused_ok(c.H, c.E, c.top_k, nsl)) {
         const bool vq = c.wformat == MOE_WFORMAT_VQLR;  // z = D^T h in the routing launch
-        moe_status st = route_align_impl(x, vq, h, M, topk_ids, topk_w, logits_out, sorted_routes, block_expert,
-                                         counts, s);
+        moe_status st = route_align_impl(x, vq && c.lr_r > 0, h, M, topk_ids, topk_w, logits_out, sorted_routes,
+                                         block_expert, counts, s);
         if (st != MOE_OK) return st;
         return expert_forward_impl(x, vq, h, M, topk_ids, topk_w, sorted_routes, block_expert, counts, 0, nullptr,
                                    y, s);

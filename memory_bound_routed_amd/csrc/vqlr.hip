@@ -114,7 +114,7 @@ constexpr int kLrPre = 4;                      // owned low-rank chunks whose co
 // Everything that does not depend on the route's expert (h, z, the code
 // book) is requested together with its id; the index and coefficient
 // stream follows as soon as the id has arrived.
-template <int D, int JW>
+template <int D, int JW, bool LR>
 __global__ void __launch_bounds__(kThreads)
 gateup_vqt_kernel(const int32_t* __restrict__ topk_ids, int R, FastDiv fk, int E, VqArgs vq,
                   const float* __restrict__ h, int H, int I, float* __restrict__ vp, int32_t* __restrict__ err) {
@@ -190,7 +190,7 @@ gateup_vqt_kernel(const int32_t* __restrict__ topk_ids, int R, FastDiv fk, int E
     float zx[kZBatch];
 #pragma unroll
     for (int u = 0; u < kZBatch; ++u)
-        zx[u] = zp[((size_t)min(u, vq.zslices - 1) * vq.M + t) * rr + min(tid, rr - 1)];
+        zx[u] = LR ? zp[((size_t)min(u, vq.zslices - 1) * vq.M + t) * rr + min(tid, rr - 1)] : 0.f;
     if (e < 0 || e >= E) {  // an invalid route has no output (uniform)
         if (P == 0 && s == 0 && tid == 0) atomicOr(err, DEVERR_BAD_ROUTE_ID);
         return;
@@ -214,7 +214,7 @@ gateup_vqt_kernel(const int32_t* __restrict__ topk_ids, int R, FastDiv fk, int E
     int nown = 0;
 #pragma unroll
     for (int u = 0; u < kLrPre; ++u) po[u] = -1;
-    for (int p = 0; p < npass; ++p) {
+    for (int p = 0; LR && p < npass; ++p) {
         if (lr_owner(4 * p + wave, nslice) != s) continue;
 #pragma unroll
         for (int u = 0; u < kLrPre; ++u)
@@ -224,6 +224,10 @@ gateup_vqt_kernel(const int32_t* __restrict__ topk_ids, int R, FastDiv fk, int E
     uint4 cpre[kLrPre][2];
 #pragma unroll
     for (int u = 0; u < kLrPre; ++u) {
+        if constexpr (!LR) {
+            cpre[u][0] = cpre[u][1] = make_uint4(0u, 0u, 0u, 0u);
+            continue;
+        }
         const int j = min(kPassCh * max(po[u], 0) + 16 * wave + lane / 4, I - 1);
         const uint16_t* crow = Cb + ((size_t)e * I + j) * rr;
         const uint4 a = load_stream16(crow + min(16 * q, rr - 8));
@@ -270,14 +274,14 @@ gateup_vqt_kernel(const int32_t* __restrict__ topk_ids, int R, FastDiv fk, int E
     }
     // z (slice partials in slice order) into LDS; coordinates past 256 and
     // slices past kZBatch are loaded here.
-    if (tid < rr) {
+    if (LR && tid < rr) {
         float z = 0.f;
 #pragma unroll
         for (int u = 0; u < kZBatch; ++u) z += u < vq.zslices ? zx[u] : 0.f;
         for (int sl = kZBatch; sl < vq.zslices; ++sl) z += zp[((size_t)sl * vq.M + t) * rr + tid];
         zsm[tid] = z;
     }
-    for (int rho = tid + kThreads; rho < rr; rho += kThreads) {
+    for (int rho = tid + kThreads; LR && rho < rr; rho += kThreads) {
         float z = 0.f;
         for (int sl = 0; sl < vq.zslices; ++sl) z += zp[((size_t)sl * vq.M + t) * rr + rho];
         zsm[rho] = z;
@@ -332,7 +336,7 @@ gateup_vqt_kernel(const int32_t* __restrict__ topk_ids, int R, FastDiv fk, int E
         for (int pp = 0; pp < kRegPasses; ++pp)
             if (pp == p) acc[pp] += v;
     }
-    for (int p = 0, n = 0; p < min(npass, kRegPasses); ++p) {  // owned passes beyond the prefetched ones
+    for (int p = 0, n = 0; LR && p < min(npass, kRegPasses); ++p) {  // owned passes beyond the prefetched ones
         if (lr_owner(4 * p + wave, nslice) != s || n++ < kLrPre) continue;
         const uint4 z0 = make_uint4(0u, 0u, 0u, 0u);
         const uint4 cz[2] = {z0, z0};
@@ -369,7 +373,7 @@ gateup_vqt_kernel(const int32_t* __restrict__ topk_ids, int R, FastDiv fk, int E
         const int j = kPassCh * p + 16 * wave + lane / 4;
         const uint4 w = load_quarter<JW>(Jb + ((size_t)e * I + min(j, I - 1)) * nbk, s * kSlice + 16 * q, jlast, vb);
         float a = gather_quarter(T, w, q);
-        if (lr_owner(4 * p + wave, nslice) == s) {
+        if (LR && lr_owner(4 * p + wave, nslice) == s) {
             const uint4 z0 = make_uint4(0u, 0u, 0u, 0u);
             const uint16_t* crow = Cb + ((size_t)e * I + min(j, I - 1)) * rr;
             uint4 c[2];
@@ -387,19 +391,26 @@ gateup_vqt_kernel(const int32_t* __restrict__ topk_ids, int R, FastDiv fk, int E
     }
 }
 
-template <int D>
-hipError_t vqt_d(const int32_t* ids, int R, int k, int E, const VqArgs& vq, const float* h, int H, int I, float* vp,
-                 int32_t* err, hipStream_t stream) {
+template <int D, bool LR>
+hipError_t vqt_lr(const int32_t* ids, int R, int k, int E, const VqArgs& vq, const float* h, int H, int I, float* vp,
+                  int32_t* err, hipStream_t stream) {
     const int nslice = (H / D + kSlice - 1) / kSlice;
     const dim3 grid((2 * R + 7) / 8 * 8, nslice);
     // 16-byte index loads when every quarter segment is 16-byte aligned
     if ((H / D) % 16 == 0)
-        MOE_LAUNCH((gateup_vqt_kernel<D, 16>), grid, dim3(kThreads), 0, stream, ids, R, FastDiv((uint32_t)k), E, vq,
-                   h, H, I, vp, err);
+        MOE_LAUNCH((gateup_vqt_kernel<D, 16, LR>), grid, dim3(kThreads), 0, stream, ids, R, FastDiv((uint32_t)k), E,
+                   vq, h, H, I, vp, err);
     else
-        MOE_LAUNCH((gateup_vqt_kernel<D, 8>), grid, dim3(kThreads), 0, stream, ids, R, FastDiv((uint32_t)k), E, vq,
-                   h, H, I, vp, err);
+        MOE_LAUNCH((gateup_vqt_kernel<D, 8, LR>), grid, dim3(kThreads), 0, stream, ids, R, FastDiv((uint32_t)k), E,
+                   vq, h, H, I, vp, err);
     return hipGetLastError();
+}
+
+template <int D>
+hipError_t vqt_d(const int32_t* ids, int R, int k, int E, const VqArgs& vq, const float* h, int H, int I, float* vp,
+                 int32_t* err, hipStream_t stream) {
+    if (vq.r > 0) return vqt_lr<D, true>(ids, R, k, E, vq, h, H, I, vp, err, stream);
+    return vqt_lr<D, false>(ids, R, k, E, vq, h, H, I, vp, err, stream);
 }
 
 // One thread per (route, channel): the slice partials of both projections,
@@ -441,7 +452,7 @@ int vq_slices(int H, int d) { return (H / d + kSlice - 1) / kSlice; }
 
 hipError_t launch_gateup_vqlr(const int32_t* topk_ids, int R, int k, int E, const VqArgs& vq, const float* h, int H,
                               int I, float* vp, int32_t* err, hipStream_t stream) {
-    if (vq.K < 1 || vq.K > kCodes || H % (8 * vq.d) || vq.r < 8 || vq.r > kMaxR || vq.r % 8 || R < 1 || k < 1)
+    if (vq.K < 1 || vq.K > kCodes || H % (8 * vq.d) || vq.r < 0 || vq.r > kMaxR || vq.r % 8 || R < 1 || k < 1)
         return hipErrorInvalidValue;
     if (vq.d == 8) return vqt_d<8>(topk_ids, R, k, E, vq, h, H, I, vp, err, stream);
     if (vq.d == 4) return vqt_d<4>(topk_ids, R, k, E, vq, h, H, I, vp, err, stream);

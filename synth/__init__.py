@@ -17,8 +17,9 @@ experts with top-8 routing and 8-row alignment blocks; synthetic values):
   aligned_h2048_i768_e128_k8_m21  21 tokens, 4 hot experts biased to ~20% of routes
   chansparse_h2048_i768_e128_k8_m1_keep799   channel top-K, K = 799 of 6144
   vqlr_h2048_i768_e128_k8_m4_d8_K256_r64     VQ + low-rank gate/up, 4 tokens
-  vqlr_..._d4_K256_r256, _d8_K256_r384, _d2_K256_r8   the same at the 4-bit
-                                             storage rate, block lengths 4, 8, 2
+  vqlr_..._d4_K256_r256, _d8_K256_r384, _d2_K256_r8, _d2_K256_r0   the same at
+                                             the 4-bit storage rate, block lengths 4, 8, 2
+                                             (r = 0: VQ only)
   dense_..._m8, _m16; vqlr_..._m8_..., _m16_...   batch 8 and 16 decode
 
 Distributions: every weight ~ N(0, 0.02) rounded to bf16; hidden states
@@ -169,6 +170,9 @@ WORKLOADS: Dict[str, Workload] = {w.name: w for w in [
              vq_d=8, lr_r=384),
     Workload("vqlr_h2048_i768_e128_k8_m4_d2_K256_r8", H=2048, I=768, E=128, k=8, M=4, seed=1005, vq=True,
              vq_d=2, lr_r=8),
+    # the page's VQ-only point (d, r) = (2, 0): no low-rank term
+    Workload("vqlr_h2048_i768_e128_k8_m4_d2_K256_r0", H=2048, I=768, E=128, k=8, M=4, seed=1005, vq=True,
+             vq_d=2, lr_r=0),
     # batch 8 and 16 decode (no hot experts): dense bf16 and VQ + low rank
     Workload("dense_h2048_i768_e128_k8_m8", H=2048, I=768, E=128, k=8, M=8, seed=1006),
     Workload("dense_h2048_i768_e128_k8_m16", H=2048, I=768, E=128, k=8, M=16, seed=1007),

@@ -418,10 +418,12 @@ def test_vqlr_b4(mb):
     layer.close()
 
 
-@pytest.mark.parametrize("name", ["vqlr_h2048_i768_e128_k8_m4_d4_K256_r256", "vqlr_h2048_i768_e128_k8_m4_d2_K256_r8"])
+@pytest.mark.parametrize("name", ["vqlr_h2048_i768_e128_k8_m4_d4_K256_r256", "vqlr_h2048_i768_e128_k8_m4_d2_K256_r8",
+                                  "vqlr_h2048_i768_e128_k8_m4_d2_K256_r0"])
 def test_vqlr_block_length_full_size(mb, name):
-    """The 4-bit-rate block-length sweep at full size (d = 4, r = 256 and
-    d = 2, r = 8), stage-isolated against the oracle."""
+    """The 4-bit-rate block-length sweep at full size (d = 4, r = 256;
+    d = 2, r = 8; and the page's VQ-only d = 2, r = 0), stage-isolated against
+    the oracle; the one-call decode step gives the same bits."""
     wl = synth.WORKLOADS[name]
     say(name, "layer 0 (full size)")
     inp = synth.layer_inputs(wl, 0)
@@ -432,6 +434,8 @@ def test_vqlr_block_length_full_size(mb, name):
     check_plan(g, wl.E, wl.block_b)
     ref = O.vqlr_forward(inp["h"], g["ids"], g["w"].astype(np.float64), inp, inp["w_down"])
     say("  stage-isolated", check_close(g["y"], ref))
+    y2 = layer.decode_step(to_dev(inp["h"]), wl.M).cpu().numpy()
+    assert np.array_equal(y2.view(np.int32), g["y"].view(np.int32)), "decode step differs from the separate calls"
     layer.close()
 
 
