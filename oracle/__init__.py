@@ -5,3 +5,4 @@ this package; the product path never does.  See moe_oracle.py.
 """
 from .moe_oracle import *  # noqa: F401,F403
 from .moe_oracle import bf16_to_f64, silu  # noqa: F401
+from . import reader_oracle as reader  # noqa: F401  (the channel-selection reader)

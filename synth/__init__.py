@@ -205,6 +205,13 @@ def router_bias(wl: Workload, layer: int) -> Optional[np.ndarray]:
     return b
 
 
+def rotation_signs(wl: Workload, layer: int, block: int = 128) -> np.ndarray:
+    """Random signs +-1 (int8 [H / block][block]) of the channel-selection
+    reader's randomized Hadamard rotation: bit 0 of one stream word each."""
+    w = words(wl.layer_seed(layer), "rotation_signs", wl.H)
+    return np.where((w & np.uint64(1)) != 0, 1, -1).astype(np.int8).reshape(wl.H // block, block)
+
+
 def expert_matrix(wl: Workload, layer: int, which: str, experts: Optional[Iterable[int]] = None,
                   out: Optional[np.ndarray] = None) -> np.ndarray:
     """Dense bf16 expert weights [E][I][H] (row j = channel j) for which in
