@@ -26,7 +26,8 @@ extracted text.  Readings taken here (each restated where it is used):
   * ternary code of a rotated block u: the threshold rule of Ternary Weight
     Networks (Li and Liu, 2016): Delta = 0.7 * mean |u_i|, c_i = sign(u_i) if
     |u_i| > Delta else 0, scale = mean of |u_i| over the nonzero codes (0 if
-    none); stored as fp32(scale / 128);
+    none), both sums taken by pairwise halving; stored as
+    fp32(scale / 128);
   * storage: codes in base 3, five channels per byte (digit c + 1, channel
     5 g + m weighted by 3^m), coordinate-major -- for every (expert,
     projection, block, coordinate) one row of ceil(I / 5) bytes over the
@@ -115,19 +116,29 @@ def rotate(v: np.ndarray, signs: np.ndarray) -> np.ndarray:
 # Ternary sketch (Stage 1; storage format lost -- reading in the header)
 # ----------------------------------------------------------------------------
 
+def pair_sum(a: np.ndarray) -> np.ndarray:
+    """Sum along the last axis (a power of two) by pairwise halving: adjacent
+    elements first, then adjacent pairs, and so on (a fixed order, so the
+    ternary threshold below is the same in any implementation of it)."""
+    a = np.asarray(a, F64)
+    while a.shape[-1] > 1:
+        a = a[..., 0::2] + a[..., 1::2]
+    return a[..., 0]
+
+
 def ternary_code(u: np.ndarray) -> Tuple[np.ndarray, np.ndarray]:
     """Ternary Weight Networks code of each rotated block (last axis, 128):
-    Delta = 0.7 * (sum |u_i|) / 128 with the sum taken left to right,
-    c_i = sign(u_i) for |u_i| > Delta else 0, scale = (sum of |u_i| over the
-    nonzero codes, left to right) / (their count), 0 if none.  Returns codes
-    int8 and the stored scale fp32(scale / 128)."""
+    Delta = 0.7 * (sum |u_i|) / 128, c_i = sign(u_i) for |u_i| > Delta else
+    0, scale = (sum of |u_i| over the nonzero codes) / (their count), 0 if
+    none; sums by pairwise halving.  Returns codes int8 and the stored scale
+    fp32(scale / 128)."""
     a = np.abs(np.asarray(u, F64))
-    total = np.cumsum(a, axis=-1)[..., -1]        # sequential sum
+    total = pair_sum(a)
     delta = TWN_RATIO * (total / BLOCK)
     nz = a > delta[..., None]
     codes = np.where(nz, np.sign(u), 0).astype(np.int8)
     cnt = nz.sum(axis=-1)
-    snz = np.cumsum(np.where(nz, a, 0.0), axis=-1)[..., -1]
+    snz = pair_sum(np.where(nz, a, 0.0))
     scale = np.where(cnt > 0, snz / np.maximum(cnt, 1), 0.0)
     return codes, (scale / BLOCK).astype(np.float32)
 

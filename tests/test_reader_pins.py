@@ -78,6 +78,16 @@ def test_ternary_code_hand_derived():
     assert s == np.float32(0.75 / 128)
 
 
+def test_pair_sum_order_and_value():
+    rng = np.random.default_rng(12)
+    v = rng.integers(-10 ** 6, 10 ** 6, (4, 128)).astype(np.float64)  # exact in any order
+    np.testing.assert_array_equal(Rd.pair_sum(v), v.sum(axis=-1))
+    # the order is ((x0 + x1) + (x2 + x3)): for 2^53, 1, 1, -2^53 that gives 1, left to right 0
+    w = np.array([2.0 ** 53, 1.0, 1.0, -(2.0 ** 53)])
+    assert Rd.pair_sum(w) == 1.0
+    assert ((w[0] + w[1]) + w[2]) + w[3] == 0.0
+
+
 def test_ternary_code_scale_invariance():
     rng = np.random.default_rng(2)
     u = rng.standard_normal((6, 128))
