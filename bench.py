@@ -50,10 +50,39 @@ def routed_bytes_per_step(wl, n_experts: int) -> int:
     return n_experts * wl.routed_bytes_per_expert + shared
 
 
+def reader_screen_bytes(wl, M: int) -> int:
+    """Sketch bytes the screening reads per step: for every routed (token,
+    slot) and projection, the rows of the 80 scanned coordinates of every
+    128-block (ceil(I/5) padded to 16 bytes each) and the blocks' scales,
+    plus the routed experts' down-column norms."""
+    nb = wl.H // 128
+    rowb = ((wl.I + 4) // 5 + 15) // 16 * 16
+    return M * wl.k * (2 * nb * (80 * rowb + 4 * wl.I) + 4 * wl.I)
+
+
+def reader_bytes_per_step(wl, M: int) -> int:
+    """Weight bytes of one reader step: screening, the kept channels' gate,
+    up and down rows, and the recovery map's coefficients and basis."""
+    rec = M * wl.k * wl.I * wl.rec_rank * 2 + wl.H * wl.rec_rank * 4 if wl.rec_rank else 0
+    return reader_screen_bytes(wl, M) + wl.keep * M * 3 * wl.H * 2 + rec
+
+
+def step_weight_bytes(wl, n_experts: int, M: int) -> int:
+    if wl.reader:
+        return reader_bytes_per_step(wl, M)
+    if wl.keep:
+        return wl.keep * 3 * wl.H * 2 * M
+    return routed_bytes_per_step(wl, n_experts)
+
+
 def kernel_algorithmic_bytes(wl, kernel: str, n_experts: int, M: int, K: int = 0) -> int:
     """Bytes a kernel must move by definition (weights it streams once plus
     its small activation inputs/outputs)."""
     H, I = wl.H, wl.I
+    if kernel == "reader_screen":
+        return reader_screen_bytes(wl, M)
+    if kernel == "reader_recover":
+        return M * wl.k * I * wl.rec_rank * 2
     if kernel in ("expert_fused", "decode_fused"):
         return n_experts * 3 * I * H * 2
     if kernel == "gateup":
@@ -83,6 +112,8 @@ KERNEL_SOURCES = {
     "down": ["memory_bound_routed_amd/csrc/dense.hip", "memory_bound_routed_amd/csrc/device_common.h"],
     "gateup_vqlr": ["memory_bound_routed_amd/csrc/vqlr.hip", "memory_bound_routed_amd/csrc/device_common.h"],
     "chan_gather": ["memory_bound_routed_amd/csrc/chansparse.hip", "memory_bound_routed_amd/csrc/device_common.h"],
+    "reader_screen": ["memory_bound_routed_amd/csrc/reader.hip", "memory_bound_routed_amd/csrc/device_common.h",
+                      "memory_bound_routed_amd/csrc/topk_device.h"],
 }
 
 
@@ -113,7 +144,7 @@ def _pmc_rows(path, counter):
 # (decode_fused is the routing instance of the fused expert kernel).
 ROCPROF_NAME = {"expert_fused": "expert_fused_kernel", "decode_fused": "expert_fused_kernel",
                 "gateup": "gateup_dense_kernel", "down": "down_kernel", "gateup_vqlr": "gateup_vqlr_kernel",
-                "chan_gather": "chan_gather_kernel"}
+                "chan_gather": "chan_gather_kernel", "reader_screen": "reader_screen_kernel"}
 
 
 def traffic_from_counters(fetch_csv, write_csv, workload, kernel="decode_fused"):
@@ -187,8 +218,11 @@ def build_layers(wl, n_layers, M, keep=0):
             cfg = mb.make_config(wl.H, wl.I, wl.E, wl.k, wl.block_b, M, mb.MOE_WFORMAT_VQLR, wl.vq_d, wl.vq_K,
                                  wl.lr_r)
         else:
-            cfg = mb.make_config(wl.H, wl.I, wl.E, wl.k, wl.block_b, M, max_keep=keep)
-        if keep:
+            cfg = mb.make_config(wl.H, wl.I, wl.E, wl.k, wl.block_b, M, max_keep=keep, reader=int(wl.reader),
+                                 rec_rank=wl.rec_rank)
+        if wl.reader:
+            reader_tables(mb, cfg, t, synth.rotation_signs(wl, L))
+        elif keep:
             norms = torch.empty((wl.E, wl.I), dtype=torch.float32, device="cuda")
             ranks = torch.empty((wl.E, wl.I), dtype=torch.int32, device="cuda")
             mb.moe_channel_norms(cfg, t["w_gate"], t["w_up"], t["w_down"], norms)
@@ -197,6 +231,23 @@ def build_layers(wl, n_layers, M, keep=0):
         layers.append(mb.Layer(cfg, t))
     torch.cuda.synchronize()
     return layers
+
+
+def reader_tables(mb, cfg, t, signs, iters=8):
+    """The reader's load-time arrays of one layer, built on the device."""
+    import torch
+    E, I, H = cfg.E, cfg.I, cfg.H
+    t["rot_signs"] = torch.from_numpy(np.ascontiguousarray(signs, np.int8).reshape(-1)).cuda()
+    t["sketch"] = torch.empty(E * 2 * H * mb.moe_sketch_row_bytes(I), dtype=torch.uint8, device="cuda")
+    t["sketch_scale"] = torch.empty((E, 2, H // 128, I), dtype=torch.float32, device="cuda")
+    t["down_norm"] = torch.empty((E, I), dtype=torch.float32, device="cuda")
+    mb.moe_reader_sketch(cfg, t["w_gate"], t["w_up"], t["rot_signs"], t["sketch"], t["sketch_scale"])
+    mb.moe_down_norms(cfg, t["w_down"], t["down_norm"])
+    if cfg.rec_rank:
+        t["rec_basis"] = torch.empty((H, cfg.rec_rank), dtype=torch.float32, device="cuda")
+        t["rec_coef"] = torch.empty((E, I, cfg.rec_rank), dtype=torch.int16, device="cuda")
+        mb.moe_recovery_basis(cfg, t["w_down"], cfg.rec_rank, iters, t["rec_basis"])
+        mb.moe_recovery_coefs(cfg, t["rec_basis"], cfg.rec_rank, t["w_down"], t["rec_coef"])
 
 
 def run_steps(layers, hs, M, keep, order):
@@ -245,21 +296,45 @@ def cpu_baseline(wl, budget_s=10.0, max_steps=40):
             "single_core": {"value": one["value"], "us_per_step": one["us_per_step"], "steps": one["steps"]},
             "all_cores": {"value": allc["value"], "us_per_step": allc["us_per_step"], "steps": allc["steps"],
                           "threads": cores},
-            "sample": "%d steps of %s cycling over %d host-resident layers (only routed experts drawn); fp64 numpy, "
-                      "timed with 1 and with %d BLAS threads" % (best["steps"], wl.name, len(sample), cores)}
+            "sample": "%d steps of %s cycling over %d host-resident layers (only routed experts drawn%s); fp64 numpy, "
+                      "timed with 1 and with %d BLAS threads"
+                      % (best["steps"], wl.name, len(sample),
+                         "; sketches precomputed, recovery basis of the routed experts' down columns"
+                         if wl.reader else "", cores)}
 
 
 def _cpu_sample(wl, synth, O):
     keep = wl.keep
     layers = []
-    for L in range(min(4, wl.layers)):
+    for L in range(min(4, wl.layers if not wl.reader else 4)):
         inp = {"h": synth.hidden(wl, L), "router_w": synth.router_weight(wl, L),
                "router_bias": synth.router_bias(wl, L)}
         ids, _, _ = O.route_topk(inp["h"], inp["router_w"], wl.k, inp["router_bias"])
         ex = sorted(set(ids.ravel().tolist()))
         full = synth.layer_inputs(wl, L, experts=ex)
-        norms = O.channel_norms(full["w_gate"], full["w_up"], full["w_down"], experts=ex) if keep else None
-        layers.append((full, norms, len(ex)))
+        extra = None
+        if wl.reader:
+            # load-time arrays of the routed experts (not timed): sketches,
+            # down norms and -- standing in for the whole layer's -- a recovery
+            # basis of the routed experts' down columns
+            signs = synth.rotation_signs(wl, L)
+            sk = {}
+            for e in ex:
+                cg, sg = O.reader.sketch_expert(full["w_gate"][e], signs)
+                cu, su = O.reader.sketch_expert(full["w_up"][e], signs)
+                sk[e] = (cg, sg, cu, su, O.reader.down_norms(full["w_down"][e]))
+            rec = None
+            if wl.rec_rank:
+                U = O.reader.recovery_basis(full["w_down"][ex], wl.rec_rank)
+                b = np.zeros((wl.E, wl.I, wl.rec_rank), np.uint16)
+                for e in ex:
+                    b[e] = O.reader.recovery_coefs(U, full["w_down"][e])
+                rec = (U, b)
+            extra = (signs, sk, rec)
+            norms = None
+        else:
+            norms = O.channel_norms(full["w_gate"], full["w_up"], full["w_down"], experts=ex) if keep else None
+        layers.append((full, norms, len(ex), extra))
     return layers
 
 
@@ -267,11 +342,18 @@ def _cpu_time(wl, layers, budget_s, max_steps, O):
     keep = wl.keep
     t_total, n, bytes_total = 0.0, 0, 0
     while n < max_steps and t_total < budget_s:
-        full, norms, nex = layers[n % len(layers)]
+        full, norms, nex, extra = layers[n % len(layers)]
         t0 = time.perf_counter()
-        O.moe_step(full, wl.k, keep=keep, norms=norms)
+        if wl.reader:
+            signs, sk, rec = extra
+            ids, aff, _ = O.route_topk(full["h"], full["router_w"], wl.k, full.get("router_bias"))
+            for t in range(wl.M):
+                O.reader.reader_step(full["h"][t], ids[t], aff[t].astype(np.float32), full["w_gate"], full["w_up"],
+                                     full["w_down"], signs, keep, recovery=rec, sketches=sk)
+        else:
+            O.moe_step(full, wl.k, keep=keep, norms=norms)
         t_total += time.perf_counter() - t0
-        bytes_total += (keep * 3 * wl.H * 2 * wl.M) if keep else routed_bytes_per_step(wl, nex)
+        bytes_total += step_weight_bytes(wl, nex, wl.M)
         n += 1
     return {"value": round(bytes_total / t_total / 1e9, 4), "us_per_step": round(t_total / n * 1e6, 1), "steps": n}
 
@@ -335,7 +417,7 @@ def main():
         L.route(hs[i], M)
         n_ex.append(len(set(L.ids[:M].flatten().tolist())))
     torch.cuda.synchronize()
-    step_bytes = [(keep * 3 * wl.H * 2 * M) if keep else routed_bytes_per_step(wl, n) for n in n_ex]
+    step_bytes = [step_weight_bytes(wl, n, M) for n in n_ex]
 
     # ---- graph-captured steps: graphs of one 48-step cycle (and a shorter
     # one for a remainder), step i of a run on layer i mod 48
@@ -457,6 +539,9 @@ def main():
                 "N(0,0.02) bf16 weights, N(0,1) fp32 hidden states" % (n_layers - 1),
         "config": {"workload": wl.name, "H": wl.H, "I": wl.I, "E": wl.E, "top_k": wl.k, "tokens": M,
                    "block_b": wl.block_b, "layers_rotated": n_layers, "keep_channels": keep or None,
+                   "selection": ("ternary-sketch reader" + (", rank-%d recovery map" % wl.rec_rank
+                                                           if wl.rec_rank else "")) if wl.reader else
+                   ("static channel norms" if keep else None),
                    "routed_bytes_per_step": int(sum(step_bytes) / len(cycle)),
                    "avg_distinct_experts": round(avg_ex, 2), "timing": "exactly %d steps as HIP-graph replays of <= %d steps "
                    "between two HIP events after %d warm-up steps" % (K, len(cycle), W)},

@@ -90,12 +90,21 @@ enum {
  *  max_keep    largest channel top-K moe_expert_forward will be asked for
  *              (0 = channel-sparse mode unused); <= top_k*I, top_k*I <= 8192,
  *              dense format only.
+ *  reader      channel scores of the channel-sparse mode: 0 = the static
+ *              scores chan_norm, 1 = the ternary-sketch reader (page "Channel
+ *              Selection for Mixture-of-Experts Decoding Needs No Calibration
+ *              Data", Stages 1 and 2): needs max_keep > 0, H % 128 == 0, and
+ *              the weights rot_signs, sketch, sketch_scale, down_norm.
+ *  rec_rank    with reader = 1: 0 (no recovery) or the rank of the recovery
+ *              map of the discarded channels (Stage 3), 8..32, % 8 == 0;
+ *              needs rec_basis and rec_coef.
  */
 typedef struct {
     int32_t H, I, E, top_k, block_b, max_tokens;
     int32_t wformat;
     int32_t vq_d, vq_K, lr_r;
     int32_t max_keep;
+    int32_t reader, rec_rank;
 } moe_config;
 
 /*
@@ -127,8 +136,20 @@ typedef struct {
  *               past the code book)
  *  The reconstructed gate/up weight of channel j, row i is
  *      sum_rho D_P[i][rho] C_P,e[j][rho] + B_P[J_P,e[j][i / vq_d]][i % vq_d].
+ *  For the reader (cfg->reader = 1; nblk = H / 128, rowb =
+ *  moe_sketch_row_bytes(I)), all made at load time from the weights alone:
+ *  rot_signs    int8 [nblk][128] of +-1: the random signs sigma of the
+ *               rotation R = H_128 diag(sigma) / sqrt(128) of every 128-block
+ *               (the same for every row and for h)
+ *  sketch       uint8 [E][2][nblk][128][rowb] (moe_reader_sketch): ternary
+ *               codes of the rotated gate ([.][0]) and up ([.][1]) rows, base
+ *               3, five channels per byte, one row per rotated coordinate
+ *  sketch_scale fp32 [E][2][nblk][I] (moe_reader_sketch)
+ *  down_norm    fp32 [E][I] ||down column|| (moe_down_norms)
+ *  rec_basis    fp32 [H][rec_rank] (moe_recovery_basis), with rec_rank > 0
+ *  rec_coef     bf16 [E][I][rec_rank] (moe_recovery_coefs), with rec_rank > 0
  *  Alignment (checked by moe_create, MOE_ERR_INVALID_ARG otherwise): the bf16
- *  arrays and vq_idx 16 bytes, the fp32 / int32 arrays 4 bytes.
+ *  arrays, vq_idx and sketch 16 bytes, the fp32 / int32 arrays 4 bytes.
  */
 typedef struct {
     const uint16_t *router_w;
@@ -142,6 +163,12 @@ typedef struct {
     const uint16_t *lr_coef[2];
     const uint16_t *vq_book[2];
     const uint8_t *vq_idx[2];
+    const int8_t *rot_signs;
+    const uint8_t *sketch;
+    const float *sketch_scale;
+    const float *down_norm;
+    const float *rec_basis;
+    const uint16_t *rec_coef;
 } moe_weights;
 
 /*
@@ -228,6 +255,21 @@ moe_status moe_route_align(moe_ctx *ctx, const float *h, int32_t M, int32_t *top
  * The plan arguments are ignored (may be NULL).  kept_out (int32 [M][K], may
  * be NULL) receives the kept set as s*I + j in ascending order.
  *
+ * Reader mode (cfg->reader = 1, keep_channels = K > 0): the same exact
+ * compute of the kept channels, but the scores come from the ternary sketch
+ * (page "Channel Selection ...", Stages 1 to 3):
+ *  1. per 128-block of h, x'' = H_128 diag(sigma) h_blk (fp64, exact for
+ *     ordinary fp32 input) and the 80 coordinates of largest |x''| (ties to
+ *     the lower coordinate);
+ *  2. g_hat_j = sum over blocks of scale_j,blk * sum over the 80 coordinates
+ *     of code_j,i * x''_i, likewise v_hat_j from the up sketch (fp32);
+ *  3. score (s, j) = (a_s * ||d_j||) * |SiLU(g_hat_j) * v_hat_j| (fp32; NaN
+ *     scores as 0), the K best kept, ties to the lower expert id, channel,
+ *     then slot -- an exact selection of these fp32 scores;
+ *  4. with rec_rank > 0, y[t] += U * sum over the dropped (s, j) of
+ *     a_s * p_hat_j * b_j with p_hat_j = SiLU(g_hat_j) * v_hat_j, U =
+ *     rec_basis, b_j = rec_coef row j (fp32 sums in a fixed order).
+ *
  *  h        fp32 [M][H];  topk_ids int32 [M][k];  topk_w fp32 [M][k]
  *  y        fp32 [M][H] out (fully overwritten)
  */
@@ -252,8 +294,11 @@ moe_status moe_expert_forward(moe_ctx *ctx, const float *h, int32_t M,
  * selected expert); the combine adds the partials.  In channel-sparse mode
  * (keep_channels > 0) the router GEMV writes the partials of all M tokens
  * and each workgroup of the channel selection (one per token) takes its
- * token's top-k and softmax before selecting.  Otherwise the calls above are
- * made as they are.
+ * token's top-k and softmax before selecting.  In reader mode the router
+ * GEMV launch also rotates and scans h in workgroups of its own, and every
+ * screening workgroup routes its token before reading the sketch (E <= 256;
+ * above, the routing is moe_route_topk's and the rotation a launch of its
+ * own).  Otherwise the calls above are made as they are.
  *  h, y: fp32 [M][H]; topk_ids, topk_w: [M][k] out; logits_out: [M][E] out
  *  or NULL; sorted_routes, block_expert, counts: as moe_align_blocks.
  */
@@ -283,6 +328,22 @@ moe_status moe_decode_step_noalloc(const moe_config *cfg, const moe_weights *w, 
                                    int32_t *topk_ids, float *topk_w, float *logits_out, int32_t *sorted_routes,
                                    int32_t *block_expert, int32_t *counts, int32_t keep_channels,
                                    int32_t *kept_out, float *y, void *stream);
+
+/*
+ * Diagnostic readout of the reader's stages 1 to 3 (cfg->reader = 1) for
+ * given routes: the rotation and scan of h, the screening estimates, the
+ * scores and the K-best selection, exactly as moe_expert_forward computes
+ * them, copied to caller buffers (device; each may be NULL):
+ *  xsel   uint8 [M][H/128][80] scanned coordinates of each block, ascending
+ *  xval   fp32 [M][H/128][80]  x'' of those coordinates (rounded to fp32)
+ *  est    fp32 [M][k][2][I]    g_hat ([.][0]) and v_hat ([.][1])
+ *  score  fp32 [M][k][I]       output-level scores
+ *  kept   int32 [M][K]         the kept set as s*I + j, ascending
+ * 1 <= K <= max_keep.  Asynchronous on `stream`.
+ */
+moe_status moe_reader_inspect(moe_ctx *ctx, const float *h, int32_t M, const int32_t *topk_ids,
+                              const float *topk_w, int32_t K, uint8_t *xsel, float *xval, float *est,
+                              float *score, int32_t *kept, void *stream);
 
 /* ---------------------------------------------------------------- helpers */
 
@@ -334,6 +395,51 @@ moe_status moe_channel_norms(const moe_config *cfg, const uint16_t *w_gate, cons
 moe_status moe_channel_ranks(const moe_config *cfg, const float *norms, int32_t *ranks, void *stream);
 
 /*
+ * Load-time arrays of the reader (page "Channel Selection for
+ * Mixture-of-Experts Decoding Needs No Calibration Data", "A Reader Built
+ * from Weights Alone": built from the weights alone, no calibration data).
+ * Each needs only cfg->H (% 128 == 0 for the sketch), I, E; inputs and
+ * outputs are device arrays in the layouts of moe_weights.
+ *
+ * moe_sketch_row_bytes: bytes of one coordinate row of the sketch,
+ * ceil(I / 5) padded to a multiple of 16; -1 when I is out of range.
+ *
+ * moe_reader_sketch: for every expert, projection (gate, up), block and
+ * channel j, the rotated row u = H_128 diag(sigma) w_j,blk (fp64) is coded
+ * by the Ternary Weight Networks rule (Li and Liu, 2016): Delta = 0.7 *
+ * mean |u_i|, code sign(u_i) where |u_i| > Delta else 0, scale = mean |u_i|
+ * over the nonzero codes (0 if none), both sums by pairwise halving
+ * (adjacent pairs, then pairs of pairs, ...); sketch_scale = fp32(scale /
+ * 128).  Codes are stored base 3 (digit code + 1; channel 5g + m of byte g
+ * weighted 3^m; channels past I as code 0; padding bytes zero).  Clears the
+ * sketch with hipMemsetAsync first: not for graph capture.
+ *
+ * moe_down_norms: down_norm[e][j] = fp32(||w_down[e][j]||), the sum of
+ * squares in fp64.
+ *
+ * moe_recovery_basis: U [H][rank] fp32 (1 <= rank <= 32, H % 64 == 0): the
+ * eigenvectors of G = sum over all experts and channels of d_j d_j^T for its
+ * rank largest eigenvalues, in decreasing order, each column's entry of
+ * largest magnitude made positive.  G is formed in fp32; the eigenvectors by
+ * `iters` rounds (>= 1) of subspace iteration from a fixed start with
+ * Cholesky QR, then a Rayleigh-Ritz step (Jacobi rotations in fp64): an
+ * approximation whose accuracy grows with iters and the eigenvalue gaps.
+ * Allocates and frees a scratch of about 4 H^2 bytes and synchronises the
+ * stream.
+ *
+ * moe_recovery_coefs: b[e][j] = U^T d_j (fp32 sums), rounded to bf16
+ * (nearest even): bf16 [E][I][rank], 8 <= rank <= 32, rank % 8 == 0.
+ */
+int32_t moe_sketch_row_bytes(int32_t I);
+moe_status moe_reader_sketch(const moe_config *cfg, const uint16_t *w_gate, const uint16_t *w_up,
+                             const int8_t *rot_signs, uint8_t *sketch, float *sketch_scale, void *stream);
+moe_status moe_down_norms(const moe_config *cfg, const uint16_t *w_down, float *down_norm, void *stream);
+moe_status moe_recovery_basis(const moe_config *cfg, const uint16_t *w_down, int32_t rank, int32_t iters,
+                              float *basis, void *stream);
+moe_status moe_recovery_coefs(const moe_config *cfg, const float *basis, int32_t rank, const uint16_t *w_down,
+                              uint16_t *coef, void *stream);
+
+/*
  * Host-side check of an alignment plan against its routes (all host
  * pointers; no GPU needed).  Checks: counts in range; every valid route
  * exactly once; rows of a block belong to its expert; pads only at a block's
@@ -369,7 +475,12 @@ enum {
     MOE_KERNEL_ROUTER_GEMV = 12,  /* router GEMV slice partials only (decode step) */
     MOE_KERNEL_DECODE_FUSED = 13, /* per-workgroup top-k + softmax + plan, then as EXPERT_FUSED */
     MOE_KERNEL_VQ_FINISH = 14,    /* VQ + low rank: slice partials -> SiLU(gate) * up */
-    MOE_KERNEL_COUNT = 15
+    MOE_KERNEL_READER_ROTATE = 15,  /* reader: rotation and scan of h (own launch) */
+    MOE_KERNEL_READER_SCREEN = 16,  /* reader: sketch estimates (routing first in the decode step) */
+    MOE_KERNEL_READER_SELECT = 17,  /* reader: output-level scores, exact top K */
+    MOE_KERNEL_READER_RECOVER = 18, /* reader: recovery partials of the dropped channels */
+    MOE_KERNEL_READER_COMBINE = 19, /* reader: combine + recovery map */
+    MOE_KERNEL_COUNT = 20
 };
 
 /*

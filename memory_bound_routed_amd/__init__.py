@@ -18,9 +18,10 @@ LIB_PATH = os.path.join(_PKG, "libmoe.so")
 
 # While `python -m memory_bound_routed_amd._build` locates its target, the
 # interpreter imports this package with sys.argv == ['-m'] (argv[0] becomes
-# the script path only once the module is found).  That is the one import
-# allowed without the library: it is the command that builds it.
-_BUILDING = not os.path.exists(LIB_PATH) and sys.argv[:1] == ["-m"]
+# the script path only once the module is found).  That import loads nothing:
+# the command builds the library, which may be missing or older than the
+# binding.
+_BUILDING = sys.argv[:1] == ["-m"]
 if not os.path.exists(LIB_PATH) and not _BUILDING:
     raise ImportError("libmoe.so is not built at %s; run `python -m memory_bound_routed_amd._build`" % LIB_PATH)
 if not _BUILDING:

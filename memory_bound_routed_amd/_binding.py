@@ -24,19 +24,22 @@ MOE_WFORMAT_DENSE, MOE_WFORMAT_VQLR = 0, 1
 DEVERR_BAD_ROUTE_ID, DEVERR_BAD_PLAN, DEVERR_BAD_BLOCK_EXPERT, DEVERR_BAD_COUNTS = 1, 2, 4, 8
 KERNELS = ["router", "vq_shared", "align", "gateup", "gateup_vqlr", "down", "combine",
            "chan_select", "chan_gather", "chan_combine", "expert_fused", "router_align", "router_gemv",
-           "decode_fused", "vq_finish"]
+           "decode_fused", "vq_finish", "reader_rotate", "reader_screen", "reader_select", "reader_recover",
+           "reader_combine"]
 MOE_KERNEL_COUNT = len(KERNELS)
 
 # Every symbol include/moe.h declares (checked by the CPU test suite).
 EXPORTS = ["moe_create", "moe_destroy", "moe_route_topk", "moe_route_align", "moe_align_blocks", "moe_expert_forward",
            "moe_decode_step", "moe_decode_step_noalloc",
            "moe_align_capacity", "moe_workspace_bytes", "moe_status_string", "moe_read_device_error", "moe_channel_norms", "moe_channel_ranks",
-           "moe_validate_plan", "moe_profile_enable", "moe_profile_read", "moe_kernel_name"]
+           "moe_validate_plan", "moe_profile_enable", "moe_profile_read", "moe_kernel_name", "moe_reader_inspect",
+           "moe_sketch_row_bytes", "moe_reader_sketch", "moe_down_norms", "moe_recovery_basis", "moe_recovery_coefs"]
 
 
 class moe_config(ctypes.Structure):
     _fields_ = [(n, ctypes.c_int32) for n in
-                ("H", "I", "E", "top_k", "block_b", "max_tokens", "wformat", "vq_d", "vq_K", "lr_r", "max_keep")]
+                ("H", "I", "E", "top_k", "block_b", "max_tokens", "wformat", "vq_d", "vq_K", "lr_r", "max_keep",
+                 "reader", "rec_rank")]
 
 
 _vp = ctypes.c_void_p
@@ -45,7 +48,8 @@ _vp = ctypes.c_void_p
 class moe_weights(ctypes.Structure):
     _fields_ = [("router_w", _vp), ("router_bias", _vp), ("w_gate", _vp), ("w_up", _vp), ("w_down", _vp),
                 ("chan_norm", _vp), ("chan_rank", _vp), ("lr_basis", _vp * 2), ("lr_coef", _vp * 2), ("vq_book", _vp * 2),
-                ("vq_idx", _vp * 2)]
+                ("vq_idx", _vp * 2), ("rot_signs", _vp), ("sketch", _vp), ("sketch_scale", _vp), ("down_norm", _vp),
+                ("rec_basis", _vp), ("rec_coef", _vp)]
 
 
 _i32, _pi32 = ctypes.c_int32, ctypes.POINTER(ctypes.c_int32)
@@ -69,6 +73,12 @@ _sig = {
     "moe_profile_enable": (_i32, [_vp, _i32]),
     "moe_profile_read": (_i32, [_vp, ctypes.POINTER(ctypes.c_double), ctypes.POINTER(ctypes.c_int64)]),
     "moe_kernel_name": (ctypes.c_char_p, [_i32]),
+    "moe_reader_inspect": (_i32, [_vp, _vp, _i32, _vp, _vp, _i32, _vp, _vp, _vp, _vp, _vp, _vp]),
+    "moe_sketch_row_bytes": (_i32, [_i32]),
+    "moe_reader_sketch": (_i32, [ctypes.POINTER(moe_config), _vp, _vp, _vp, _vp, _vp, _vp]),
+    "moe_down_norms": (_i32, [ctypes.POINTER(moe_config), _vp, _vp, _vp]),
+    "moe_recovery_basis": (_i32, [ctypes.POINTER(moe_config), _vp, _i32, _i32, _vp, _vp]),
+    "moe_recovery_coefs": (_i32, [ctypes.POINTER(moe_config), _vp, _i32, _vp, _vp, _vp]),
 }
 for _name, (_res, _args) in _sig.items():
     _f = getattr(_lib, _name)
@@ -127,13 +137,14 @@ def moe_workspace_bytes(cfg: "moe_config", max_tokens: int) -> int:
 
 
 def make_config(H, I, E, top_k, block_b=8, max_tokens=1, wformat=MOE_WFORMAT_DENSE, vq_d=0, vq_K=0, lr_r=0,
-                max_keep=0) -> moe_config:
-    return moe_config(H, I, E, top_k, block_b, max_tokens, wformat, vq_d, vq_K, lr_r, max_keep)
+                max_keep=0, reader=0, rec_rank=0) -> moe_config:
+    return moe_config(H, I, E, top_k, block_b, max_tokens, wformat, vq_d, vq_K, lr_r, max_keep, reader, rec_rank)
 
 
 def make_weights(router_w, w_down, router_bias=None, w_gate=None, w_up=None, chan_norm=None, chan_rank=None,
                  lr_basis=(None, None), lr_coef=(None, None), vq_book=(None, None),
-                 vq_idx=(None, None)) -> moe_weights:
+                 vq_idx=(None, None), rot_signs=None, sketch=None, sketch_scale=None, down_norm=None,
+                 rec_basis=None, rec_coef=None) -> moe_weights:
     w = moe_weights()
     w.router_w, w.router_bias, w.w_gate, w.w_up, w.w_down, w.chan_norm, w.chan_rank = (
         _ptr(router_w), _ptr(router_bias), _ptr(w_gate), _ptr(w_up), _ptr(w_down), _ptr(chan_norm),
@@ -141,6 +152,9 @@ def make_weights(router_w, w_down, router_bias=None, w_gate=None, w_up=None, cha
     for P in range(2):
         w.lr_basis[P], w.lr_coef[P] = _ptr(lr_basis[P]), _ptr(lr_coef[P])
         w.vq_book[P], w.vq_idx[P] = _ptr(vq_book[P]), _ptr(vq_idx[P])
+    w.rot_signs, w.sketch, w.sketch_scale, w.down_norm = _ptr(rot_signs), _ptr(sketch), _ptr(sketch_scale), \
+        _ptr(down_norm)
+    w.rec_basis, w.rec_coef = _ptr(rec_basis), _ptr(rec_coef)
     return w
 
 
@@ -225,6 +239,35 @@ def moe_channel_ranks(cfg: moe_config, norms, ranks, stream=None) -> None:
     _check(_lib.moe_channel_ranks(ctypes.byref(cfg), _ptr(norms), _ptr(ranks), _stream(stream)), "moe_channel_ranks")
 
 
+def moe_reader_inspect(ctx, h, M, topk_ids, topk_w, K, xsel=None, xval=None, est=None, score=None, kept=None,
+                       stream=None) -> None:
+    _check(_lib.moe_reader_inspect(ctx, _ptr(h), M, _ptr(topk_ids), _ptr(topk_w), K, _ptr(xsel), _ptr(xval),
+                                   _ptr(est), _ptr(score), _ptr(kept), _stream(stream)), "moe_reader_inspect")
+
+
+def moe_sketch_row_bytes(I: int) -> int:
+    return _lib.moe_sketch_row_bytes(I)
+
+
+def moe_reader_sketch(cfg: moe_config, w_gate, w_up, rot_signs, sketch, sketch_scale, stream=None) -> None:
+    _check(_lib.moe_reader_sketch(ctypes.byref(cfg), _ptr(w_gate), _ptr(w_up), _ptr(rot_signs), _ptr(sketch),
+                                  _ptr(sketch_scale), _stream(stream)), "moe_reader_sketch")
+
+
+def moe_down_norms(cfg: moe_config, w_down, down_norm, stream=None) -> None:
+    _check(_lib.moe_down_norms(ctypes.byref(cfg), _ptr(w_down), _ptr(down_norm), _stream(stream)), "moe_down_norms")
+
+
+def moe_recovery_basis(cfg: moe_config, w_down, rank, iters, basis, stream=None) -> None:
+    _check(_lib.moe_recovery_basis(ctypes.byref(cfg), _ptr(w_down), rank, iters, _ptr(basis), _stream(stream)),
+           "moe_recovery_basis")
+
+
+def moe_recovery_coefs(cfg: moe_config, basis, rank, w_down, coef, stream=None) -> None:
+    _check(_lib.moe_recovery_coefs(ctypes.byref(cfg), _ptr(basis), rank, _ptr(w_down), _ptr(coef), _stream(stream)),
+           "moe_recovery_coefs")
+
+
 def moe_validate_plan(topk_ids, M, k, E, b, sorted_routes, block_expert, counts) -> Tuple[int, int]:
     """Host check of a plan (numpy int32 arrays).  Returns (status, reason)."""
     import numpy as np
@@ -265,7 +308,9 @@ class Layer:
             lr_basis=(t.get("lr_basis_gate"), t.get("lr_basis_up")),
             lr_coef=(t.get("lr_coef_gate"), t.get("lr_coef_up")),
             vq_book=(t.get("vq_book_gate"), t.get("vq_book_up")),
-            vq_idx=(t.get("vq_idx_gate"), t.get("vq_idx_up")))
+            vq_idx=(t.get("vq_idx_gate"), t.get("vq_idx_up")), rot_signs=t.get("rot_signs"),
+            sketch=t.get("sketch"), sketch_scale=t.get("sketch_scale"), down_norm=t.get("down_norm"),
+            rec_basis=t.get("rec_basis"), rec_coef=t.get("rec_coef"))
         self.ctx = moe_create(cfg, self.weights)
         dev = t["router_w"].device
         M, k = cfg.max_tokens, cfg.top_k

@@ -20,7 +20,7 @@ BUILD = os.path.join(PKG, "_build")
 LIB = os.path.join(PKG, "libmoe.so")
 ARCH = "gfx950"
 
-SOURCES = ["moe_api.cpp", "router.hip", "align.hip", "dense.hip", "vqlr.hip", "chansparse.hip"]
+SOURCES = ["moe_api.cpp", "router.hip", "align.hip", "dense.hip", "vqlr.hip", "chansparse.hip", "reader.hip"]
 
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 

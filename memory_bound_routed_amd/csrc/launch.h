@@ -58,8 +58,16 @@ hipError_t launch_router_align(const float* h, int M, int H, const uint16_t* Wr,
 // (row-slice partials; logit of (t, e) = 0 + part[0][t][e] + part[1][t][e]
 // + ... in slice order, then + bias[e]).
 int router_slices(int H, int E);
+// Optional rotation job of the channel-selection reader riding along
+// (reader_device.h: per token and 128-block, the scanned coordinates
+// xsel u8 [M][H/128][80] and values xval fp32 [M][H/128][80]).
+struct RotJob {
+    const int8_t* signs;  // int8 [H] (+-1)
+    uint8_t* xsel;
+    float* xval;
+};
 hipError_t launch_router_partials(const float* h, int M, int H, const uint16_t* Wr, int E, float* part,
-                                  hipStream_t stream);
+                                  hipStream_t stream, const RotJob* rot = nullptr);
 
 // ---- align.hip
 size_t align_lds_bytes(int R, int E);
@@ -169,5 +177,62 @@ hipError_t launch_chan_combine(int M, int H, int nchunks, const float* part, flo
 hipError_t launch_channel_ranks(int E, int I, const float* norms, int32_t* ranks, hipStream_t stream);
 hipError_t launch_channel_norms(int E, int I, int H, const uint16_t* Wg, const uint16_t* Wu, const uint16_t* Wd,
                                 float* norms, hipStream_t stream);
+
+// ---- reader.hip (channel selection by the ternary-sketch reader)
+// Per-call buffers and load-time arrays of the reader.  Layouts:
+//  sketch    u8 [E][2][nblk][128][rowb]  base-3 codes, coordinate-major rows
+//  scale     fp32 [E][2][nblk][I]        per (block, channel) scale / 128
+//  xsel/xval u8 / fp32 [M][nblk][80]     scanned coordinates (ascending), x''
+//  est       fp32 [M][k][2][I]           g_hat (P = 0), v_hat (P = 1)
+//  phat, score fp32 [M][k][I];  kept_flag u8 [M][k][I]
+//  dnorm     fp32 [E][I];  rec_coef bf16 [E][I][rank];  rpart fp32 [M][k][chunks][rank]
+struct ReaderArgs {
+    const uint8_t* sketch;
+    const float* scale;
+    const uint8_t* xsel;
+    const float* xval;
+    float* est;
+    float* phat;
+    float* score;
+    const float* dnorm;
+    uint8_t* kept_flag;
+    const uint16_t* rec_coef;
+    float* rpart;
+    int rank;
+    int nblk;
+    int rowb;
+    int I;
+    int k;
+    int E;
+};
+// Bytes of one coordinate row of the sketch: ceil(I / 5) padded to 16.
+int reader_row_bytes(int I);
+// Rotation + partial scan of each 128-block of h (M tokens) in its own launch.
+hipError_t launch_reader_rotate(const float* h, int M, int H, const int8_t* signs, uint8_t* xsel, float* xval,
+                                hipStream_t stream);
+// Screening: est for every routed (token, slot) from topk_ids, or (route
+// non-null) routing each token first from the router's slice partials.
+hipError_t launch_reader_screen(const ReaderArgs& ra, const SelRoute* route, const int32_t* topk_ids, int M,
+                                hipStream_t stream);
+// Output-level scores and the exact top K per token: slot_cnt / slot_kept as
+// launch_chan_select, phat, score and kept_flag in ra.
+hipError_t launch_reader_select(const ReaderArgs& ra, const int32_t* topk_ids, const float* topk_w, int M, int K,
+                                int32_t* slot_cnt, int32_t* slot_kept, int32_t* kept_out, hipStream_t stream);
+int reader_recover_chunks(int I);
+// Recovery partials rpart of the dropped candidates (ra.rank in 8..32, % 8).
+hipError_t launch_reader_recover(const ReaderArgs& ra, const int32_t* topk_ids, const float* topk_w, int M,
+                                 hipStream_t stream);
+// y = sum of the gather's chunk partials + U (sum of the nrp recovery partials).
+hipError_t launch_reader_combine(int M, int H, int nchunks, const float* part, const float* rpart, int nrp, int rank,
+                                 const float* U, float* y, hipStream_t stream);
+// Load time.
+hipError_t launch_reader_sketch(int E, int I, int H, const uint16_t* Wg, const uint16_t* Wu, const int8_t* signs,
+                                uint8_t* sketch, float* scale, hipStream_t stream);
+hipError_t launch_down_norms(int E, int I, int H, const uint16_t* Wd, float* dn, hipStream_t stream);
+size_t recovery_basis_scratch(int H, int rank);
+hipError_t launch_recovery_basis(int E, int I, int H, const uint16_t* Wd, int rank, int iters, float* U, void* scratch,
+                                 hipStream_t stream);
+hipError_t launch_recovery_coefs(int E, int I, int H, const float* U, int rank, const uint16_t* Wd, uint16_t* b,
+                                 hipStream_t stream);
 
 }  // namespace moe

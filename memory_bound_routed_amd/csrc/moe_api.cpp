@@ -36,6 +36,16 @@ struct Workspace {
     int32_t* slot_cnt = nullptr;   // channel-sparse: kept channels per (token, slot), int32 [MT][k]
     int32_t* slot_kept = nullptr;  // ... and their channels, int32 [MT][k][I]
     float* chan_part = nullptr;
+    // reader: scanned coordinates and values [MT][H/128][80], estimates
+    // [MT][k][2][I], p_hat, scores and kept flags [MT][k][I], recovery
+    // partials [MT][k][chunks][rec_rank]
+    uint8_t* xsel = nullptr;
+    float* xval = nullptr;
+    float* est = nullptr;
+    float* phat = nullptr;
+    float* score = nullptr;
+    uint8_t* kept_flag = nullptr;
+    float* rpart = nullptr;
 };
 
 struct moe_ctx {
@@ -88,6 +98,14 @@ moe_status check_config(const moe_config* c) {
         if (c->wformat != MOE_WFORMAT_DENSE) return MOE_ERR_UNSUPPORTED;
         if (c->max_keep > c->top_k * c->I || c->top_k * c->I > 8192) return MOE_ERR_UNSUPPORTED;
     }
+    if (c->reader != 0 && c->reader != 1) return MOE_ERR_INVALID_ARG;
+    if (c->rec_rank < 0) return MOE_ERR_INVALID_ARG;
+    if (c->reader) {
+        if (c->max_keep == 0 || c->H % 128) return MOE_ERR_UNSUPPORTED;
+        if (c->rec_rank && (c->rec_rank < 8 || c->rec_rank > 32 || c->rec_rank % 8)) return MOE_ERR_UNSUPPORTED;
+    } else if (c->rec_rank) {
+        return MOE_ERR_UNSUPPORTED;  // the recovery map belongs to the reader
+    }
     return MOE_OK;
 }
 
@@ -107,8 +125,17 @@ moe_status check_weights(const moe_config* c, const moe_weights* w) {
                 return MOE_ERR_INVALID_ARG;
         }
     }
-    if (c->max_keep > 0 && (!w->chan_norm || !aligned(w->chan_norm, 4) || !w->chan_rank || !aligned(w->chan_rank, 4)))
+    if (c->max_keep > 0 && !c->reader &&
+        (!w->chan_norm || !aligned(w->chan_norm, 4) || !w->chan_rank || !aligned(w->chan_rank, 4)))
         return MOE_ERR_INVALID_ARG;
+    if (c->reader) {
+        if (!w->rot_signs || !w->sketch || !aligned(w->sketch, 16) || !w->sketch_scale ||
+            !aligned(w->sketch_scale, 4) || !w->down_norm || !aligned(w->down_norm, 4))
+            return MOE_ERR_INVALID_ARG;
+        if (c->rec_rank &&
+            (!w->rec_basis || !aligned(w->rec_basis, 4) || !w->rec_coef || !aligned(w->rec_coef, 16)))
+            return MOE_ERR_INVALID_ARG;
+    }
     return MOE_OK;
 }
 
@@ -125,7 +152,11 @@ size_t workspace_layout(const moe_config& c, size_t MT, char* base, Workspace* w
         down = f > down ? f : down;
     }
     const size_t nchan = c.max_keep > 0 ? (c.max_keep + kChanChunk - 1) / kChanChunk : 0;
-    const size_t sizes[8] = {
+    const size_t rd = c.reader ? 1 : 0;
+    const size_t nscan = rd * MT * (c.H / 128) * 80;  // scanned coordinates of all blocks
+    const size_t nkc = rd * R * c.I;                    // candidates
+    constexpr int kBufs = 15;
+    const size_t sizes[kBufs] = {
         64 + sizeof(unsigned) * (1 + (size_t)moe::router_groups((int)MT)),  // err flag, router tickets
         sizeof(float) * moe::gemv_slices(c.H, c.E) * MT * c.E,          // router partials
         sizeof(float) * zsl * MT * c.lr_r,                              // z = D^T h partials (gate)
@@ -134,9 +165,16 @@ size_t workspace_layout(const moe_config& c, size_t MT, char* base, Workspace* w
         sizeof(float) * down,                                           // down partials
         c.max_keep > 0 ? sizeof(int32_t) * MT * c.top_k * (1 + (size_t)c.I) : 0,  // per-slot kept lists
         sizeof(float) * MT * nchan * c.H,                               // channel partials
+        nscan,                                                          // reader: scanned coordinates
+        sizeof(float) * nscan,                                          // ... and their values
+        sizeof(float) * 2 * nkc,                                        // estimates
+        sizeof(float) * nkc,                                            // p_hat
+        sizeof(float) * nkc,                                            // scores
+        nkc,                                                            // kept flags
+        sizeof(float) * R * (c.rec_rank ? (size_t)moe::reader_recover_chunks(c.I) * c.rec_rank : 0),  // recovery
     };
-    size_t off[8], total = 0;
-    for (int i = 0; i < 8; ++i) {
+    size_t off[kBufs], total = 0;
+    for (int i = 0; i < kBufs; ++i) {
         off[i] = total;
         total += (sizes[i] + 255) & ~(size_t)255;
     }
@@ -151,6 +189,13 @@ size_t workspace_layout(const moe_config& c, size_t MT, char* base, Workspace* w
         ws->slot_cnt = reinterpret_cast<int32_t*>(base + off[6]);
         ws->slot_kept = ws->slot_cnt + MT * c.top_k;
         ws->chan_part = reinterpret_cast<float*>(base + off[7]);
+        ws->xsel = reinterpret_cast<uint8_t*>(base + off[8]);
+        ws->xval = reinterpret_cast<float*>(base + off[9]);
+        ws->est = reinterpret_cast<float*>(base + off[10]);
+        ws->phat = reinterpret_cast<float*>(base + off[11]);
+        ws->score = reinterpret_cast<float*>(base + off[12]);
+        ws->kept_flag = reinterpret_cast<uint8_t*>(base + off[13]);
+        ws->rpart = reinterpret_cast<float*>(base + off[14]);
     }
     return total;
 }
@@ -223,6 +268,76 @@ moe_status chan_gather_combine(const Exec& x, const float* h, int M, const int32
     return hip_status(e);
 }
 
+moe::ReaderArgs reader_args(const Exec& x) {
+    moe::ReaderArgs ra{};
+    ra.sketch = x.w.sketch;
+    ra.scale = x.w.sketch_scale;
+    ra.xsel = x.ws.xsel;
+    ra.xval = x.ws.xval;
+    ra.est = x.ws.est;
+    ra.phat = x.ws.phat;
+    ra.score = x.ws.score;
+    ra.dnorm = x.w.down_norm;
+    ra.kept_flag = x.ws.kept_flag;
+    ra.rec_coef = x.w.rec_coef;
+    ra.rpart = x.ws.rpart;
+    ra.rank = x.c.rec_rank;
+    ra.nblk = x.c.H / 128;
+    ra.rowb = moe::reader_row_bytes(x.c.I);
+    ra.I = x.c.I;
+    ra.k = x.c.top_k;
+    ra.E = x.c.E;
+    return ra;
+}
+
+// Reader, from the routes on: rotation (unless already done), screening,
+// selection, gather, then the combine (with the recovery map when rec_rank > 0).
+moe_status reader_forward(const Exec& x, bool rotated, const moe::SelRoute* route, const float* h, int M,
+                          const int32_t* topk_ids, const float* topk_w, int K, int32_t* kept_out, float* y,
+                          hipStream_t s) {
+    const moe_config& c = x.c;
+    const moe::ReaderArgs ra = reader_args(x);
+    hipError_t e;
+    if (!rotated) {
+        Launch l(x.prof, MOE_KERNEL_READER_ROTATE);
+        e = moe::launch_reader_rotate(h, M, c.H, x.w.rot_signs, x.ws.xsel, x.ws.xval, s);
+        l.done();
+        if (e != hipSuccess) return MOE_ERR_HIP;
+    }
+    {
+        Launch l(x.prof, MOE_KERNEL_READER_SCREEN);
+        e = moe::launch_reader_screen(ra, route, topk_ids, M, s);
+        l.done();
+        if (e != hipSuccess) return MOE_ERR_HIP;
+    }
+    {
+        Launch l(x.prof, MOE_KERNEL_READER_SELECT);
+        e = moe::launch_reader_select(ra, topk_ids, topk_w, M, K, x.ws.slot_cnt, x.ws.slot_kept, nullptr, s);
+        l.done();
+        if (e != hipSuccess) return MOE_ERR_HIP;
+    }
+    if (!c.rec_rank) return chan_gather_combine(x, h, M, topk_ids, topk_w, K, kept_out, y, s);
+    const int nchunks = (K + kChanChunk - 1) / kChanChunk;
+    {
+        Launch l(x.prof, MOE_KERNEL_CHAN_GATHER);
+        e = moe::launch_chan_gather(topk_ids, topk_w, x.ws.slot_cnt, x.ws.slot_kept, kept_out, M, c.top_k, c.I, c.E,
+                                    c.H, K, kChanChunk, h, x.w.w_gate, x.w.w_up, x.w.w_down, x.ws.chan_part, s);
+        l.done();
+        if (e != hipSuccess) return MOE_ERR_HIP;
+    }
+    {
+        Launch l(x.prof, MOE_KERNEL_READER_RECOVER);
+        e = moe::launch_reader_recover(ra, topk_ids, topk_w, M, s);
+        l.done();
+        if (e != hipSuccess) return MOE_ERR_HIP;
+    }
+    Launch l(x.prof, MOE_KERNEL_READER_COMBINE);
+    e = moe::launch_reader_combine(M, c.H, nchunks, x.ws.chan_part, x.ws.rpart,
+                                   c.top_k * moe::reader_recover_chunks(c.I), c.rec_rank, x.w.rec_basis, y, s);
+    l.done();
+    return hip_status(e);
+}
+
 moe_status route_topk_impl(const Exec& x, const float* h, int32_t M, int32_t* topk_ids, float* topk_w,
                            float* logits_out, hipStream_t s) {
     if (M == 0) return MOE_OK;
@@ -280,6 +395,7 @@ moe_status expert_forward_impl(const Exec& x, bool z_ready, const float* h, int3
     if (keep_channels > 0) {
         if (c.max_keep == 0 || c.wformat != MOE_WFORMAT_DENSE) return MOE_ERR_UNSUPPORTED;
         if (keep_channels > c.max_keep) return MOE_ERR_CAPACITY;
+        if (c.reader) return reader_forward(x, false, nullptr, h, M, topk_ids, topk_w, keep_channels, kept_out, y, s);
         {
             Launch l(x.prof, MOE_KERNEL_CHAN_SELECT);
             e = moe::launch_chan_select(topk_ids, topk_w, x.w.chan_norm, x.w.chan_rank, M, c.top_k, c.I, c.E,
@@ -375,9 +491,17 @@ moe_status decode_step_impl(const Exec& x, const float* h, int32_t M, int32_t* t
         if (M == 0) return MOE_OK;
         if (!h || !topk_ids || !topk_w || !y || !aligned(h, 16) || !aligned(y, 16)) return MOE_ERR_INVALID_ARG;
         hipError_t e;
+        if (c.reader && c.E > 256) {  // routing as moe_route_topk, then the reader from the routes
+            moe_status st = route_topk_impl(x, h, M, topk_ids, topk_w, logits_out, s);
+            if (st != MOE_OK) return st;
+            return reader_forward(x, false, nullptr, h, M, topk_ids, topk_w, keep_channels, kept_out, y, s);
+        }
         {
+            // the reader's rotation rides along in workgroups of its own
+            const moe::RotJob rot{x.w.rot_signs, x.ws.xsel, x.ws.xval};
             Launch l(x.prof, MOE_KERNEL_ROUTER_GEMV);
-            e = moe::launch_router_partials(h, M, c.H, x.w.router_w, c.E, x.ws.router_part, s);
+            e = moe::launch_router_partials(h, M, c.H, x.w.router_w, c.E, x.ws.router_part, s,
+                                            c.reader ? &rot : nullptr);
             l.done();
             if (e != hipSuccess) return MOE_ERR_HIP;
         }
@@ -389,6 +513,7 @@ moe_status decode_step_impl(const Exec& x, const float* h, int32_t M, int32_t* t
         route.ids = topk_ids;
         route.wts = topk_w;
         route.logits = logits_out;
+        if (c.reader) return reader_forward(x, true, &route, h, M, topk_ids, topk_w, keep_channels, kept_out, y, s);
         {
             Launch l(x.prof, MOE_KERNEL_CHAN_SELECT);
             e = moe::launch_chan_select_routed(route, x.w.chan_norm, x.w.chan_rank, M, c.top_k, c.I, c.E,
@@ -509,7 +634,9 @@ const char* moe_kernel_name(int32_t k) {
     static const char* names[MOE_KERNEL_COUNT] = {"router",      "vq_shared",   "align",        "gateup",
                                                   "gateup_vqlr", "down",        "combine",      "chan_select",
                                                   "chan_gather", "chan_combine", "expert_fused", "router_align",
-                                                  "router_gemv", "decode_fused", "vq_finish"};
+                                                  "router_gemv", "decode_fused", "vq_finish",   "reader_rotate",
+                                                  "reader_screen", "reader_select", "reader_recover",
+                                                  "reader_combine"};
     return (k >= 0 && k < MOE_KERNEL_COUNT) ? names[k] : nullptr;
 }
 
@@ -622,6 +749,94 @@ moe_status moe_decode_step_noalloc(const moe_config* cfg, const moe_weights* w, 
     const Exec x{*cfg, *w, ws, nullptr};
     return decode_step_impl(x, h, M, topk_ids, topk_w, logits_out, sorted_routes, block_expert, counts,
                             keep_channels, kept_out, y, static_cast<hipStream_t>(stream));
+}
+
+moe_status moe_reader_inspect(moe_ctx* ctx, const float* h, int32_t M, const int32_t* topk_ids,
+                              const float* topk_w, int32_t K, uint8_t* xsel, float* xval, float* est, float* score,
+                              int32_t* kept, void* stream) {
+    if (!ctx || M < 0) return MOE_ERR_INVALID_ARG;
+    const moe_config& c = ctx->cfg;
+    if (!c.reader) return MOE_ERR_UNSUPPORTED;
+    if (M > c.max_tokens || K > c.max_keep) return MOE_ERR_CAPACITY;
+    if (K < 1) return MOE_ERR_INVALID_ARG;
+    if (M == 0) return MOE_OK;
+    if (!h || !topk_ids || !topk_w || !aligned(h, 16)) return MOE_ERR_INVALID_ARG;
+    const hipStream_t s = static_cast<hipStream_t>(stream);
+    const Exec x = exec_of(ctx);
+    const moe::ReaderArgs ra = reader_args(x);
+    hipError_t e = moe::launch_reader_rotate(h, M, c.H, x.w.rot_signs, x.ws.xsel, x.ws.xval, s);
+    if (e == hipSuccess) e = moe::launch_reader_screen(ra, nullptr, topk_ids, M, s);
+    if (e == hipSuccess)
+        e = moe::launch_reader_select(ra, topk_ids, topk_w, M, K, x.ws.slot_cnt, x.ws.slot_kept, kept, s);
+    const size_t nscan = (size_t)M * (c.H / 128) * 80;
+    const size_t nkc = (size_t)M * c.top_k * c.I;
+    if (e == hipSuccess && xsel) e = hipMemcpyAsync(xsel, x.ws.xsel, nscan, hipMemcpyDeviceToDevice, s);
+    if (e == hipSuccess && xval) e = hipMemcpyAsync(xval, x.ws.xval, 4 * nscan, hipMemcpyDeviceToDevice, s);
+    if (e == hipSuccess && est) e = hipMemcpyAsync(est, x.ws.est, 8 * nkc, hipMemcpyDeviceToDevice, s);
+    if (e == hipSuccess && score) e = hipMemcpyAsync(score, x.ws.score, 4 * nkc, hipMemcpyDeviceToDevice, s);
+    return hip_status(e);
+}
+
+int32_t moe_sketch_row_bytes(int32_t I) {
+    if (I < 1 || I > 16384) return -1;
+    return moe::reader_row_bytes(I);
+}
+
+namespace {
+moe_status check_load_shape(const moe_config* cfg) {
+    if (!cfg || cfg->H <= 0 || cfg->I <= 0 || cfg->E <= 0) return MOE_ERR_INVALID_ARG;
+    if (cfg->H % 8 || cfg->H > 8192 || cfg->I > 16384 || cfg->E > 8192) return MOE_ERR_UNSUPPORTED;
+    return MOE_OK;
+}
+}  // namespace
+
+moe_status moe_reader_sketch(const moe_config* cfg, const uint16_t* w_gate, const uint16_t* w_up,
+                             const int8_t* rot_signs, uint8_t* sketch, float* sketch_scale, void* stream) {
+    moe_status st = check_load_shape(cfg);
+    if (st != MOE_OK) return st;
+    if (cfg->H % 128) return MOE_ERR_UNSUPPORTED;
+    if (!w_gate || !w_up || !rot_signs || !sketch || !sketch_scale) return MOE_ERR_INVALID_ARG;
+    if (!aligned(w_gate, 16) || !aligned(w_up, 16) || !aligned(sketch_scale, 4)) return MOE_ERR_INVALID_ARG;
+    const hipStream_t s = static_cast<hipStream_t>(stream);
+    const size_t bytes = (size_t)cfg->E * 2 * cfg->H * moe::reader_row_bytes(cfg->I);
+    if (hipMemsetAsync(sketch, 0, bytes, s) != hipSuccess) return MOE_ERR_HIP;
+    return hip_status(
+        moe::launch_reader_sketch(cfg->E, cfg->I, cfg->H, w_gate, w_up, rot_signs, sketch, sketch_scale, s));
+}
+
+moe_status moe_down_norms(const moe_config* cfg, const uint16_t* w_down, float* down_norm, void* stream) {
+    moe_status st = check_load_shape(cfg);
+    if (st != MOE_OK) return st;
+    if (!w_down || !down_norm || !aligned(w_down, 16) || !aligned(down_norm, 4)) return MOE_ERR_INVALID_ARG;
+    return hip_status(
+        moe::launch_down_norms(cfg->E, cfg->I, cfg->H, w_down, down_norm, static_cast<hipStream_t>(stream)));
+}
+
+moe_status moe_recovery_basis(const moe_config* cfg, const uint16_t* w_down, int32_t rank, int32_t iters,
+                              float* basis, void* stream) {
+    moe_status st = check_load_shape(cfg);
+    if (st != MOE_OK) return st;
+    if (rank < 1 || rank > 32 || iters < 1 || iters > 1000) return MOE_ERR_INVALID_ARG;
+    if (cfg->H % 64) return MOE_ERR_UNSUPPORTED;
+    if (!w_down || !basis || !aligned(w_down, 16) || !aligned(basis, 4)) return MOE_ERR_INVALID_ARG;
+    const hipStream_t s = static_cast<hipStream_t>(stream);
+    void* scratch_mem = nullptr;
+    if (hipMalloc(&scratch_mem, moe::recovery_basis_scratch(cfg->H, rank)) != hipSuccess) return MOE_ERR_HIP;
+    hipError_t e = moe::launch_recovery_basis(cfg->E, cfg->I, cfg->H, w_down, rank, iters, basis, scratch_mem, s);
+    const hipError_t e2 = hipStreamSynchronize(s);
+    hipFree(scratch_mem);
+    return hip_status(e != hipSuccess ? e : e2);
+}
+
+moe_status moe_recovery_coefs(const moe_config* cfg, const float* basis, int32_t rank, const uint16_t* w_down,
+                              uint16_t* coef, void* stream) {
+    moe_status st = check_load_shape(cfg);
+    if (st != MOE_OK) return st;
+    if (rank < 8 || rank > 32 || rank % 8) return MOE_ERR_INVALID_ARG;
+    if (!basis || !w_down || !coef || !aligned(basis, 4) || !aligned(w_down, 16) || !aligned(coef, 16))
+        return MOE_ERR_INVALID_ARG;
+    return hip_status(moe::launch_recovery_coefs(cfg->E, cfg->I, cfg->H, basis, rank, w_down, coef,
+                                                 static_cast<hipStream_t>(stream)));
 }
 
 moe_status moe_read_device_error(moe_ctx* ctx, int32_t* flags, int32_t clear) {

@@ -1,0 +1,947 @@
+// The channel-selection reader (page "Channel Selection for Mixture-of-
+// Experts Decoding Needs No Calibration Data": "A Reader Built from Weights
+// Alone", Stage 1 "Screen with a Ternary Sketch", Stage 2 "Compute the Top k
+// Exactly with Output-Level Scores", Stage 3 "Recover Discarded Channels with
+// a rank-32 Map"; the sketch format, Eq. 1 and Eq. 2 are lost in the page's
+// text -- the readings are stated where they are used).
+//
+// Decode time, per token:
+//  1. rotation and partial scan of h (reader_device.h): per 128-block the 80
+//     coordinates of largest |x''|, x'' = H_128 diag(sigma) h exact in fp64;
+//  2. screening (reader_screen_kernel): for every routed expert, gate and up,
+//     g_hat_j = sum over blocks of scale_j,blk * sum over the scanned
+//     coordinates of c_j,i x''_i, from the base-3 sketch rows of the scanned
+//     coordinates only;
+//  3. selection (reader_select_kernel): score w_s ||d_j|| |SiLU(g_hat) v_hat|,
+//     the K best of the token's k * I candidates by an exact radix select
+//     over a total order (score, then expert id, channel, slot), the kept
+//     lists per slot for the gather of chansparse.hip;
+//  4. with the recovery map: (reader_recover_kernel) r = sum over the dropped
+//     candidates of w_s p_hat_j b_j, p_hat_j = SiLU(g_hat_j) v_hat_j, then
+//     (reader_combine_kernel) y = sum of the gather's chunk partials + U r.
+// Load time: the sketch (reader_sketch_kernel), the down-column norms, the
+// recovery basis U (top-32 eigenvectors of the Gram matrix of the stacked down
+// columns, by subspace iteration with a Rayleigh-Ritz step) and b_j = U^T d_j.
+//
+// Every reduction has a fixed order, so results are bitwise reproducible.
+#include "device_common.h"
+#include "launch.h"
+#include "reader_device.h"
+#include "topk_device.h"
+
+namespace moe {
+
+namespace {
+
+constexpr int kThreads = 256;
+constexpr int kWaves = kThreads / MOE_WAVE;
+constexpr int kRowGroups = 64;   // screening: row groups of a workgroup (4 lanes each)
+constexpr int kRangeCh = 80;     // screening: channels per workgroup (16 bytes of a row)
+constexpr int kSelThreads = 1024;
+constexpr int kSelPer = 8;       // selection: candidates per thread (k * I <= 8192)
+constexpr int kMaxRank = 32;
+
+// ---------------------------------------------------------------------------
+// Rotation jobs of a launch of their own (the separate-calls path; the
+// one-call decode step does them in the router launch's spare workgroups).
+__global__ void __launch_bounds__(kThreads)
+reader_rotate_kernel(const float* __restrict__ h, int M, int H, const int8_t* __restrict__ signs,
+                     uint8_t* __restrict__ xsel, float* __restrict__ xval) {
+    __shared__ double key[kWaves][kReaderBlock];
+    const int nblk = H / kReaderBlock;
+    const int job = blockIdx.x * kWaves + threadIdx.x / MOE_WAVE;
+    if (job >= M * nblk) return;  // whole waves
+    const int t = job / nblk, b = job - t * nblk;
+    rotate_scan_wave(h + (size_t)t * H + b * kReaderBlock, signs + b * kReaderBlock,
+                     xsel + (size_t)job * kReaderScan, xval + (size_t)job * kReaderScan, key[threadIdx.x / MOE_WAVE]);
+}
+
+// ---------------------------------------------------------------------------
+// Screening.  Workgroup (pair, c) of token t estimates projection P of slot
+// s's expert (pair = 2 s + P) for the 80 channels 80 c .. 80 c + 79, i.e.
+// bytes 16 c .. 16 c + 15 of every scanned coordinate row.  The grid's x
+// runs over groups of 8 pairs times the nseg channel ranges with the pair
+// varying fastest (x = pair % 8 + 8 (c + nseg (pair / 8))): workgroups are
+// dealt to the 8 XCDs round-robin by their linear id, so all ranges of one
+// pair -- which read the same cache lines of the same rows -- share one
+// XCD's L2, while the pairs spread over the XCDs.
+//
+// Thread (row group rg = tid / 4, word w = tid % 4): block b = rg % nblk,
+// the scanned coordinates n = q, q + Pb, ... with q = rg / nblk and Pb =
+// 64 / nblk groups per block; bytes 16 c + 4 w .. + 3 of each such row
+// (channels 80 c + 20 w .. + 19).  Each row's 4 bytes are decoded with a
+// 243-entry table of codes in LDS and accumulated against x''; the sum of a
+// row group is scaled by its block's scale, and the 64 row groups are added
+// in order.  The scanned coordinates of all blocks are staged in LDS (their
+// loads issued before the routing).  ROUTE: every workgroup first routes its
+// token from the router's slice partials with the router's arithmetic
+// (E <= 256).
+constexpr int kStage = kRowGroups * kReaderScan / kThreads;  // staged (coordinate, value) per thread, nblk <= 64
+
+template <bool ROUTE>
+__global__ void __launch_bounds__(kThreads)
+reader_screen_kernel(ReaderArgs ra, SelRoute route, const int32_t* __restrict__ topk_ids, int nseg) {
+    __shared__ float4 lut4[243];
+    __shared__ float lut1[243];
+    __shared__ float red[kRowGroups][kRangeCh + 1];
+    __shared__ uint8_t s_sel[kRowGroups * kReaderScan];
+    __shared__ float s_val[kRowGroups * kReaderScan];
+    __shared__ int s_e;
+    const int x = blockIdx.x;
+    const int pair = x % 8 + 8 * (x / (8 * nseg));
+    const int c = (x / 8) % nseg;
+    const int t = blockIdx.y;
+    const int k = ra.k;
+    if (pair >= 2 * k) return;  // whole workgroup, before any barrier
+    const int s = pair >> 1;
+    const int P = pair & 1;
+    const int tid = threadIdx.x;
+    const int w = tid % 4;
+    const int rg = tid / 4;
+    const int nblk = ra.nblk;
+    const int I = ra.I;
+
+    // scanned coordinates and values of the token's blocks (independent of the routing)
+    const int nst = nblk * kReaderScan;
+    uint32_t st_sel[kStage];
+    float st_val[kStage];
+    {
+        const uint8_t* gs = ra.xsel + (size_t)t * nst;
+        const float* gv = ra.xval + (size_t)t * nst;
+#pragma unroll
+        for (int u = 0; u < kStage; ++u) {
+            const int i = min(tid + kThreads * u, nst - 1);
+            st_sel[u] = gs[i];
+            st_val[u] = gv[i];
+        }
+    }
+    // the code table: digit m of byte v (base 3) minus 1
+    if (tid < 243) {
+        int v = tid;
+        float d[5];
+#pragma unroll
+        for (int m = 0; m < 5; ++m) {
+            d[m] = (float)(v % 3 - 1);
+            v /= 3;
+        }
+        lut4[tid] = make_float4(d[0], d[1], d[2], d[3]);
+        lut1[tid] = d[4];
+    }
+
+    if constexpr (ROUTE) {
+        __shared__ uint64_t skey[kThreads];
+        __shared__ int sel_e[32];
+        __shared__ float sel_l[32];
+        __shared__ uint64_t wk[MOE_WAVE];
+        __shared__ int wi[MOE_WAVE];
+        __shared__ int s_slow;
+        const int E = ra.E;
+        const bool writer = x == 0;  // pair 0, range 0 writes the routing
+        float lg = 0.f;
+        if (tid < E) {
+            const float bv = route.bias ? route.bias[tid] : 0.f;
+            for (int sl0 = 0; sl0 < route.nslices; sl0 += 8) {  // eight slices in flight
+                float xs[8];
+#pragma unroll
+                for (int u = 0; u < 8; ++u)
+                    xs[u] = route.part[((size_t)min(sl0 + u, route.nslices - 1) * route.M + t) * E + tid];
+#pragma unroll
+                for (int u = 0; u < 8; ++u) lg += sl0 + u < route.nslices ? xs[u] : 0.f;  // slice order
+            }
+            if (route.bias) lg += bv;
+            if (route.logits && writer) route.logits[(size_t)t * E + tid] = lg;
+            skey[tid] = order_key((lg != lg) ? -INFINITY : lg, tid);  // NaN ranks as -inf
+        }
+        if (tid == 0) s_slow = 0;
+        __syncthreads();
+        if (tid < MOE_WAVE && !wave_topk<4>(skey, E, k, sel_e, sel_l, wk, wi)) s_slow = 1;
+        __syncthreads();
+        if (s_slow) {  // every key counted
+            if (tid < E) {
+                const int rank = count_greater(skey, 0, E, skey[tid]);
+                if (rank < k) {
+                    sel_e[rank] = tid;
+                    sel_l[rank] = key_logit(skey[tid]);
+                }
+            }
+            __syncthreads();
+        }
+        if (tid < MOE_WAVE) {  // lane s: slot s
+            const float wv = topk_softmax(sel_l[min(tid, k - 1)], tid, k);
+            if (tid < k && writer) {
+                route.ids[(size_t)t * k + tid] = sel_e[tid];
+                route.wts[(size_t)t * k + tid] = wv;
+            }
+            if (tid == 0) s_e = sel_e[s];
+        }
+    } else {
+        if (tid == 0) s_e = topk_ids[(size_t)t * k + s];
+    }
+#pragma unroll
+    for (int u = 0; u < kStage; ++u) {
+        const int i = tid + kThreads * u;
+        if (i < nst) {
+            s_sel[i] = (uint8_t)st_sel[u];
+            s_val[i] = st_val[u];
+        }
+    }
+    __syncthreads();
+    const int e = s_e;
+    const bool valid = e >= 0 && e < ra.E;
+    const int ec = valid ? e : 0;
+
+    // this thread's rows: block b, scanned coordinates q, q + Pb, ... (< 80)
+    const int Pb = kRowGroups / nblk;
+    const int b = rg % nblk;
+    const int q = rg / nblk;
+    const bool active = rg < nblk * Pb;
+    const int nrows = active ? (kReaderScan - q + Pb - 1) / Pb : 0;  // rows of this group
+    const uint8_t* rows = ra.sketch + (((size_t)ec * 2 + P) * nblk + b) * kReaderBlock * ra.rowb + 16 * c + 4 * w;
+    const uint8_t* ssel = s_sel + b * kReaderScan;
+    const float* sval = s_val + b * kReaderScan;
+    float acc[20];
+#pragma unroll
+    for (int m = 0; m < 20; ++m) acc[m] = 0.f;
+    constexpr int kBatch = 20;
+    for (int n0 = 0; n0 < nrows; n0 += kBatch) {  // uniform per row group
+        uint32_t wd[kBatch];
+        float xv[kBatch];
+#pragma unroll
+        for (int u = 0; u < kBatch; ++u) {
+            const int n = min(q + (n0 + u) * Pb, kReaderScan - 1);
+            wd[u] = *reinterpret_cast<const uint32_t*>(rows + (size_t)ssel[n] * ra.rowb);
+            xv[u] = n0 + u < nrows ? sval[n] : 0.f;
+        }
+#pragma unroll
+        for (int u = 0; u < kBatch; ++u) {
+#pragma unroll
+            for (int y = 0; y < 4; ++y) {
+                const uint32_t v = (wd[u] >> (8 * y)) & 255u;
+                const uint32_t vc = v < 243u ? v : 121u;  // bytes past the codes read as code 0
+                const float4 d4 = lut4[vc];
+                const float d1 = lut1[vc];
+                acc[5 * y] = fmaf(d4.x, xv[u], acc[5 * y]);
+                acc[5 * y + 1] = fmaf(d4.y, xv[u], acc[5 * y + 1]);
+                acc[5 * y + 2] = fmaf(d4.z, xv[u], acc[5 * y + 2]);
+                acc[5 * y + 3] = fmaf(d4.w, xv[u], acc[5 * y + 3]);
+                acc[5 * y + 4] = fmaf(d1, xv[u], acc[5 * y + 4]);
+            }
+        }
+    }
+    // the block's scale per channel, then the row groups in order
+    const int ch0 = kRangeCh * c + 20 * w;
+    const float* scl = ra.scale + (((size_t)ec * 2 + P) * nblk + b) * I;
+#pragma unroll
+    for (int m = 0; m < 20; ++m) {
+        const float sv = scl[min(ch0 + m, I - 1)];
+        red[rg][20 * w + m] = (active && ch0 + m < I) ? sv * acc[m] : 0.f;
+    }
+    __syncthreads();
+    if (tid < kRangeCh && kRangeCh * c + tid < I) {
+        float g = 0.f;
+        for (int r2 = 0; r2 < kRowGroups; ++r2) g += red[r2][tid];
+        ra.est[(((size_t)t * k + s) * 2 + P) * I + kRangeCh * c + tid] = valid ? g : 0.f;
+    }
+}
+
+// ---------------------------------------------------------------------------
+// Selection, one workgroup per token.  Candidate idx = s * I + j, thread tid
+// owning idx = 8 tid .. 8 tid + 7 (a contiguous run, for the scan of the kept
+// flags).  Key: the score's bits (non-negative fp32, so order-preserving) in
+// the high word, the complement of (e << 19 | j << 5 | s) in the low word, so
+// that equal scores order by expert id, channel, then slot; keys are
+// distinct.  The K-th largest key is found digit by digit from the top (8
+// bits per pass, a histogram in LDS, stopping as soon as the remaining
+// demand is a whole digit bucket); the kept candidates are the keys at or
+// above it.
+__device__ __forceinline__ uint64_t cand_key(float score, int e, int j, int s) {
+    const uint32_t tb = ((uint32_t)e << 19) | ((uint32_t)j << 5) | (uint32_t)s;
+    return ((uint64_t)__float_as_uint(score) << 32) | (uint32_t)(0xFFFFFFFFu - tb);
+}
+
+__global__ void __launch_bounds__(kSelThreads)
+reader_select_kernel(ReaderArgs ra, const int32_t* __restrict__ topk_ids, const float* __restrict__ topk_w, int K,
+                     FastDiv fI, int32_t* __restrict__ slot_cnt, int32_t* __restrict__ slot_kept,
+                     int32_t* __restrict__ kept_out) {
+    __shared__ int se[32];
+    __shared__ float sw[32];
+    __shared__ int hist[256];
+    __shared__ uint64_t s_pref;
+    __shared__ int s_need, s_done;
+    __shared__ int wsum[kSelThreads / MOE_WAVE];
+    __shared__ int slot_off[33];
+    const int t = blockIdx.x;
+    const int tid = threadIdx.x;
+    const int I = ra.I, k = ra.k, E = ra.E;
+    const int n = k * I;
+    if (tid < k) {
+        const int e = topk_ids[(size_t)t * k + tid];
+        se[tid] = (e >= 0 && e < E) ? e : -1;
+        sw[tid] = topk_w[(size_t)t * k + tid];
+    }
+    if (tid < 256) hist[tid] = 0;
+    __syncthreads();
+    uint64_t key[kSelPer];
+#pragma unroll
+    for (int u = 0; u < kSelPer; ++u) {
+        const int idx = kSelPer * tid + u;
+        const int ic = min(idx, n - 1);
+        const int s = fI.div(ic), j = ic - s * I;
+        const int e = se[s];
+        const float g = ra.est[(((size_t)t * k + s) * 2 + 0) * I + j];
+        const float v = ra.est[(((size_t)t * k + s) * 2 + 1) * I + j];
+        const float dn = ra.dnorm[(size_t)max(e, 0) * I + j];
+        const float ph = silu_mul(g, v);
+        float sc = (sw[s] * dn) * fabsf(ph);
+        if (!(sc >= 0.f) || e < 0) sc = 0.f;  // NaN, invalid slot
+        if (idx < n) {
+            ra.phat[((size_t)t * k + s) * I + j] = ph;
+            ra.score[((size_t)t * k + s) * I + j] = sc;
+        }
+        key[u] = idx < n ? cand_key(sc, e < 0 ? 8191 : e, j, s) : 0ull;
+    }
+    // digit-by-digit search of the K-th largest key (K < n; K >= n keeps all)
+    if (tid == 0) {
+        s_pref = 0ull;
+        s_need = K;
+        s_done = K >= n || K <= 0;
+    }
+    __syncthreads();
+    for (int shift = 56; shift >= 0 && !s_done; shift -= 8) {  // uniform
+        const uint64_t pref = s_pref;
+        const int above = shift + 8;  // bits above the digit fixed by pref
+#pragma unroll
+        for (int u = 0; u < kSelPer; ++u) {
+            const bool match = kSelPer * tid + u < n && (above == 64 ? true : (key[u] >> above) == (pref >> above));
+            if (match) atomicAdd(&hist[(int)((key[u] >> shift) & 255u)], 1);
+        }
+        __syncthreads();
+        if (tid < MOE_WAVE) {  // the digit where the demand falls, from the top
+            const int lane = tid;
+            int cnt[4];
+            int sum = 0;
+#pragma unroll
+            for (int x = 0; x < 4; ++x) {
+                cnt[x] = hist[255 - (4 * lane + x)];  // bins in descending order
+                sum += cnt[x];
+            }
+            int incl = sum;  // inclusive prefix over lanes (descending bins)
+#pragma unroll
+            for (int d = 1; d < MOE_WAVE; d <<= 1) {
+                const int y = __shfl_up(incl, d, MOE_WAVE);
+                if (lane >= d) incl += y;
+            }
+            const int need = s_need;
+            int before = incl - sum;
+            int found = -1, nb = 0, nc = 0;
+#pragma unroll
+            for (int x = 0; x < 4; ++x) {
+                if (found < 0 && before < need && need <= before + cnt[x]) {
+                    found = 255 - (4 * lane + x);
+                    nb = before;
+                    nc = cnt[x];
+                }
+                before += cnt[x];
+            }
+            const uint64_t m = __ballot(found >= 0);
+            const int src = __builtin_ctzll(m);  // exactly one lane (need <= total)
+            const int dig = __shfl(found, src, MOE_WAVE);
+            const int nbv = __shfl(nb, src, MOE_WAVE);
+            const int ncv = __shfl(nc, src, MOE_WAVE);
+            if (lane == 0) {
+                s_pref = pref | ((uint64_t)dig << shift);
+                s_need = need - nbv;
+                if (need - nbv == ncv) s_done = 1;  // the whole bucket is kept
+            }
+        }
+        __syncthreads();
+        if (tid < 256) hist[tid] = 0;
+        __syncthreads();
+    }
+    // kept: keys at or above the threshold (the bucket prefix with zero low bits)
+    const uint64_t thr = s_pref;
+    const bool all = K >= n;
+    const bool none = K <= 0;
+    unsigned kmask = 0;
+#pragma unroll
+    for (int u = 0; u < kSelPer; ++u) {
+        const bool kept = kSelPer * tid + u < n && !none && (all || key[u] >= thr);
+        kmask |= kept ? (1u << u) : 0u;
+    }
+    // positions in candidate order: exclusive scan of the counts
+    const int cntk = __builtin_popcount(kmask);
+    const int lane = tid % MOE_WAVE, wave = tid / MOE_WAVE;
+    int incl = cntk;
+#pragma unroll
+    for (int d = 1; d < MOE_WAVE; d <<= 1) {
+        const int y = __shfl_up(incl, d, MOE_WAVE);
+        if (lane >= d) incl += y;
+    }
+    if (lane == MOE_WAVE - 1) wsum[wave] = incl;
+    __syncthreads();
+    int base = 0;
+    for (int x = 0; x < wave; ++x) base += wsum[x];
+    int pos = base + incl - cntk;
+    // the first kept position of every slot: the slot's first candidate's owner
+#pragma unroll
+    for (int u = 0; u < kSelPer; ++u) {
+        const int idx = kSelPer * tid + u;
+        if (idx < n && fI.mod(idx) == 0) slot_off[fI.div(idx)] = pos + __builtin_popcount(kmask & ((1u << u) - 1u));
+    }
+    if (tid == 0) slot_off[k] = all ? n : (none ? 0 : K);
+    __syncthreads();
+#pragma unroll
+    for (int u = 0; u < kSelPer; ++u) {
+        const int idx = kSelPer * tid + u;
+        if (idx >= n) continue;
+        const int s = fI.div(idx), j = idx - s * I;
+        const bool kept = (kmask >> u) & 1u;
+        ra.kept_flag[((size_t)t * k + s) * I + j] = kept ? 1 : 0;
+        if (kept) {
+            if (kept_out) kept_out[(size_t)t * K + pos] = idx;
+            slot_kept[((size_t)t * k + s) * I + (pos - slot_off[s])] = j;
+            ++pos;
+        }
+    }
+    if (tid < k) slot_cnt[(size_t)t * k + tid] = slot_off[tid + 1] - slot_off[tid];
+}
+
+// ---------------------------------------------------------------------------
+// Recovery partials.  Grid (channel chunks of 256, k, M): thread j of slot s
+// adds, for a dropped candidate, (w_s p_hat_j) b_j[r] for r < rank; the 256
+// threads are added by a fixed butterfly per wave, then the waves in order:
+// rpart[t][s][chunk][r].
+__global__ void __launch_bounds__(kThreads)
+reader_recover_kernel(ReaderArgs ra, const int32_t* __restrict__ topk_ids, const float* __restrict__ topk_w) {
+    __shared__ float wpart[kWaves][kMaxRank];
+    const int chunk = blockIdx.x, s = blockIdx.y, t = blockIdx.z;
+    const int tid = threadIdx.x, lane = tid % MOE_WAVE, wave = tid / MOE_WAVE;
+    const int I = ra.I, k = ra.k, rank = ra.rank;
+    const int j = chunk * kThreads + tid;
+    const int e = topk_ids[(size_t)t * k + s];
+    const float a = topk_w[(size_t)t * k + s];
+    const bool ev = e >= 0 && e < ra.E;
+    const int jc = min(j, I - 1);
+    const bool use = ev && j < I && !ra.kept_flag[((size_t)t * k + s) * I + jc];
+    const float coef = use ? a * ra.phat[((size_t)t * k + s) * I + jc] : 0.f;
+    const uint16_t* brow = ra.rec_coef + ((size_t)(ev ? e : 0) * I + jc) * rank;
+    float contrib[kMaxRank];
+#pragma unroll
+    for (int r8 = 0; r8 < kMaxRank / 8; ++r8) {
+        float f[8];
+        unpack8(8 * r8 < rank ? load16(brow + 8 * r8) : make_uint4(0u, 0u, 0u, 0u), f);
+#pragma unroll
+        for (int x = 0; x < 8; ++x) contrib[8 * r8 + x] = use ? coef * f[x] : 0.f;
+    }
+#pragma unroll
+    for (int r = 0; r < kMaxRank; ++r) {
+        const float v = wave_sum(contrib[r]);
+        if (lane == 0) wpart[wave][r] = v;
+    }
+    __syncthreads();
+    if (tid < rank)
+        ra.rpart[(((size_t)t * k + s) * gridDim.x + chunk) * rank + tid] =
+            (wpart[0][tid] + wpart[1][tid]) + (wpart[2][tid] + wpart[3][tid]);
+}
+
+// y[t][col] = sum over the gather chunks of part[t][chunk][col] (as the
+// channel-sparse combine), then + sum_r U[col][r] R[r] with R[r] the sum of
+// the token's recovery partials in order.  One wave per workgroup.
+constexpr int kCombCG = 4;
+constexpr int kCombRG = MOE_WAVE / kCombCG;
+constexpr int kCombBatch = 8;
+
+__global__ void __launch_bounds__(MOE_WAVE)
+reader_combine_kernel(int H, int nchunks, const float* __restrict__ part, const float* __restrict__ rpart, int nrp,
+                      int rank, const float* __restrict__ U, float* __restrict__ y) {
+    const int t = blockIdx.y;
+    const int lane = threadIdx.x;
+    const int cg = lane % kCombCG;
+    const int rg = lane / kCombCG;
+    const int col = (blockIdx.x * kCombCG + cg) * 4;
+    float4 acc = make_float4(0.f, 0.f, 0.f, 0.f);
+    const float* src = part + (size_t)t * nchunks * H + min(col, H - 4);
+    for (int c0 = rg; c0 < nchunks; c0 += kCombBatch * kCombRG) {
+        float4 v[kCombBatch];
+#pragma unroll
+        for (int u = 0; u < kCombBatch; ++u)
+            v[u] = *reinterpret_cast<const float4*>(src + (size_t)min(c0 + u * kCombRG, nchunks - 1) * H);
+#pragma unroll
+        for (int u = 0; u < kCombBatch; ++u) {
+            const bool use = c0 + u * kCombRG < nchunks;
+            acc.x += use ? v[u].x : 0.f;
+            acc.y += use ? v[u].y : 0.f;
+            acc.z += use ? v[u].z : 0.f;
+            acc.w += use ? v[u].w : 0.f;
+        }
+    }
+#pragma unroll
+    for (int m = kCombCG; m < MOE_WAVE; m <<= 1) {
+        acc.x += __shfl_xor(acc.x, m, MOE_WAVE);
+        acc.y += __shfl_xor(acc.y, m, MOE_WAVE);
+        acc.z += __shfl_xor(acc.z, m, MOE_WAVE);
+        acc.w += __shfl_xor(acc.w, m, MOE_WAVE);
+    }
+    // R: lane r < rank adds the nrp partials of coordinate r in order
+    float R = 0.f;
+    for (int i = 0; i < nrp; ++i) R += lane < rank ? rpart[((size_t)t * nrp + i) * rank + min(lane, rank - 1)] : 0.f;
+    float rec[4] = {0.f, 0.f, 0.f, 0.f};
+    for (int r = 0; r < rank; ++r) {
+        const float Rr = __shfl(R, r, MOE_WAVE);
+#pragma unroll
+        for (int x = 0; x < 4; ++x) rec[x] = fmaf(U[(size_t)min(col + x, H - 1) * rank + r], Rr, rec[x]);
+    }
+    if (rg == 0 && col < H)
+        *reinterpret_cast<float4*>(y + (size_t)t * H + col) =
+            make_float4(acc.x + rec[0], acc.y + rec[1], acc.z + rec[2], acc.w + rec[3]);
+}
+
+// ---------------------------------------------------------------------------
+// Load time: the sketch.  Grid (ceil(I / 20), nblk, 2 E): workgroup (cg, b,
+// 2 e + P) sketches block b of projection P's rows j = 20 cg .. 20 cg + 19 of
+// expert e, five rows per wave: each row's block is rotated as in
+// rotate_scan_wave (fp64 butterflies), the ternary threshold
+// 0.7 * (sum |u|) / 128 and the scale (sum of the kept |u|) / (their number)
+// are taken with the sums by pairwise halving (in-lane pair, then lane
+// distances 1, 2, ..., 32) -- the order of their definition -- and the codes
+// go to LDS; then the 128 coordinate rows get their 4 bytes (20 channels,
+// base 3) each.  Rows past I are code 0; bytes past ceil(I / 5) are left as
+// they are (zero).
+__global__ void __launch_bounds__(kThreads)
+reader_sketch_kernel(const uint16_t* __restrict__ Wg, const uint16_t* __restrict__ Wu,
+                     const int8_t* __restrict__ signs, int H, int I, int rowb, uint8_t* __restrict__ sketch,
+                     float* __restrict__ scale) {
+    __shared__ int8_t codes[20][kReaderBlock];
+    const int cg = blockIdx.x, b = blockIdx.y;
+    const int e = blockIdx.z >> 1, P = blockIdx.z & 1;
+    const int nblk = H / kReaderBlock;
+    const int tid = threadIdx.x, lane = tid % MOE_WAVE, wave = tid / MOE_WAVE;
+    const uint16_t* W = P ? Wu : Wg;
+    const int s0 = signs[b * kReaderBlock + 2 * lane], s1 = signs[b * kReaderBlock + 2 * lane + 1];
+    for (int rr = 0; rr < 5; ++rr) {
+        const int r = wave * 5 + rr;
+        const int j = 20 * cg + r;
+        if (j >= I) {  // past the channels: code 0 (uniform per wave)
+            codes[r][2 * lane] = 0;
+            codes[r][2 * lane + 1] = 0;
+            continue;
+        }
+        const uint32_t hv = *reinterpret_cast<const uint32_t*>(W + ((size_t)e * I + j) * H + b * kReaderBlock + 2 * lane);
+        double a = (double)bf16_lo(hv) * (double)s0;
+        double c = (double)bf16_hi(hv) * (double)s1;
+        {
+            const double x = a + c, y = a - c;
+            a = x;
+            c = y;
+        }
+#pragma unroll
+        for (int d = 1; d < MOE_WAVE; d <<= 1) {
+            const double pa = __shfl_xor(a, d, MOE_WAVE);
+            const double pc = __shfl_xor(c, d, MOE_WAVE);
+            if (lane & d) {
+                a = pa - a;
+                c = pc - c;
+            } else {
+                a = a + pa;
+                c = c + pc;
+            }
+        }
+        const double ma = fabs(a), mc = fabs(c);
+        double tot = ma + mc;  // pairwise halving: the lane's pair, then lanes 1, 2, ..., 32 apart
+#pragma unroll
+        for (int d = 1; d < MOE_WAVE; d <<= 1) tot = tot + __shfl_xor(tot, d, MOE_WAVE);
+        const double delta = 0.7 * (tot / 128.0);
+        const bool na = ma > delta, nc = mc > delta;
+        double snz = (na ? ma : 0.0) + (nc ? mc : 0.0);
+#pragma unroll
+        for (int d = 1; d < MOE_WAVE; d <<= 1) snz = snz + __shfl_xor(snz, d, MOE_WAVE);
+        const int cnt = __popcll(__ballot(na)) + __popcll(__ballot(nc));
+        const double sc = cnt > 0 ? snz / (double)cnt : 0.0;
+        codes[r][2 * lane] = na ? (a > 0.0 ? 1 : -1) : 0;
+        codes[r][2 * lane + 1] = nc ? (c > 0.0 ? 1 : -1) : 0;
+        if (lane == 0) scale[(((size_t)e * 2 + P) * nblk + b) * I + j] = (float)(sc / 128.0);
+    }
+    __syncthreads();
+    const int ng = (I + 4) / 5;  // code bytes of a row
+    for (int x = tid; x < kReaderBlock * 4; x += kThreads) {
+        const int i = x >> 2, by = x & 3;
+        const int g = 4 * cg + by;
+        if (g >= ng) continue;
+        int v = 0, p3 = 1;
+#pragma unroll
+        for (int m = 0; m < 5; ++m) {
+            v += (codes[5 * by + m][i] + 1) * p3;
+            p3 *= 3;
+        }
+        sketch[((((size_t)e * 2 + P) * nblk + b) * kReaderBlock + i) * rowb + g] = (uint8_t)v;
+    }
+}
+
+// ||d_j|| of every channel: one wave per channel, fp64 sum of squares (fixed
+// butterfly), rounded once.
+__global__ void __launch_bounds__(kThreads)
+down_norms_kernel(int EI, int H, const uint16_t* __restrict__ Wd, float* __restrict__ dn) {
+    const int ch = blockIdx.x * kWaves + threadIdx.x / MOE_WAVE;
+    const int lane = threadIdx.x % MOE_WAVE;
+    if (ch >= EI) return;
+    double sd = 0.0;
+    for (int col = lane * 8; col < H; col += MOE_WAVE * 8) {
+        float c[8];
+        unpack8(load16(Wd + (size_t)ch * H + col), c);
+#pragma unroll
+        for (int x = 0; x < 8; ++x) sd += (double)c[x] * (double)c[x];
+    }
+    sd = wave_sum_f64(sd);
+    if (lane == 0) dn[ch] = (float)sqrt(sd);
+}
+
+// ---------------------------------------------------------------------------
+// Load time: the recovery basis.  G = sum over all channels of d d^T (fp32,
+// [H][H]), tiles of 64 x 64 (upper triangle, mirrored), each thread a 4 x 4
+// block, the channels walked in order 16 at a time through LDS.
+__global__ void __launch_bounds__(kThreads)
+gram_kernel(const uint16_t* __restrict__ Wd, int N, int H, float* __restrict__ G) {
+    __shared__ float As[16][64];
+    __shared__ float Bs[16][64];
+    const int ta = blockIdx.x, tb = blockIdx.y;
+    if (ta > tb) return;
+    const int tid = threadIdx.x;
+    const int ti = tid / 16, tj = tid % 16;  // 16 x 16 threads, 4 x 4 each
+    float acc[4][4];
+#pragma unroll
+    for (int x = 0; x < 4; ++x)
+#pragma unroll
+        for (int z = 0; z < 4; ++z) acc[x][z] = 0.f;
+    for (int n0 = 0; n0 < N; n0 += 16) {
+        // 16 rows x 64 columns of each tile: thread loads 4 + 4 bf16 values
+        {
+            const int r = tid / 16, cq = (tid % 16) * 4;
+            const int nn = min(n0 + r, N - 1);
+            const bool in = n0 + r < N;
+            const uint2 va = *reinterpret_cast<const uint2*>(Wd + (size_t)nn * H + 64 * ta + cq);
+            const uint2 vb = *reinterpret_cast<const uint2*>(Wd + (size_t)nn * H + 64 * tb + cq);
+            As[r][cq] = in ? bf16_lo(va.x) : 0.f; As[r][cq + 1] = in ? bf16_hi(va.x) : 0.f;
+            As[r][cq + 2] = in ? bf16_lo(va.y) : 0.f; As[r][cq + 3] = in ? bf16_hi(va.y) : 0.f;
+            Bs[r][cq] = in ? bf16_lo(vb.x) : 0.f; Bs[r][cq + 1] = in ? bf16_hi(vb.x) : 0.f;
+            Bs[r][cq + 2] = in ? bf16_lo(vb.y) : 0.f; Bs[r][cq + 3] = in ? bf16_hi(vb.y) : 0.f;
+        }
+        __syncthreads();
+#pragma unroll 4
+        for (int r = 0; r < 16; ++r) {
+            const float4 av = *reinterpret_cast<const float4*>(&As[r][4 * ti]);
+            const float4 bv = *reinterpret_cast<const float4*>(&Bs[r][4 * tj]);
+            const float a4[4] = {av.x, av.y, av.z, av.w};
+            const float b4[4] = {bv.x, bv.y, bv.z, bv.w};
+#pragma unroll
+            for (int x = 0; x < 4; ++x)
+#pragma unroll
+                for (int z = 0; z < 4; ++z) acc[x][z] = fmaf(a4[x], b4[z], acc[x][z]);
+        }
+        __syncthreads();
+    }
+#pragma unroll
+    for (int x = 0; x < 4; ++x)
+#pragma unroll
+        for (int z = 0; z < 4; ++z) {
+            const int i = 64 * ta + 4 * ti + x, jj = 64 * tb + 4 * tj + z;
+            G[(size_t)i * H + jj] = acc[x][z];
+            G[(size_t)jj * H + i] = acc[x][z];
+        }
+}
+
+// Z = A Q, A fp32 [H][H], Q [H][rank] (rank <= 32): one thread per (row,
+// column), the row of A walked in order.
+__global__ void __launch_bounds__(kThreads)
+gemm_aq_kernel(const float* __restrict__ A, const float* __restrict__ Q, int H, int rank, float* __restrict__ Z) {
+    const int idx = blockIdx.x * kThreads + threadIdx.x;
+    if (idx >= H * rank) return;
+    const int i = idx / rank, r = idx - i * rank;
+    float acc = 0.f;
+    for (int a = 0; a < H; ++a) acc = fmaf(A[(size_t)i * H + a], Q[(size_t)a * rank + r], acc);
+    Z[idx] = acc;
+}
+
+// S = X^T Y (rank x rank, fp64), X and Y [H][rank]: one workgroup, thread
+// (r, c) of the first rank^2 threads walks the rows in order.
+__global__ void __launch_bounds__(1024)
+xty_kernel(const float* __restrict__ X, const float* __restrict__ Y, int H, int rank, double* __restrict__ S) {
+    const int tid = threadIdx.x;
+    if (tid >= rank * rank) return;
+    const int r = tid / rank, c = tid - r * rank;
+    double acc = 0.0;
+    for (int i = 0; i < H; ++i) acc += (double)X[(size_t)i * rank + r] * (double)Y[(size_t)i * rank + c];
+    S[tid] = acc;
+}
+
+// Orthonormalise the columns of Z by Cholesky QR: S = Z^T Z = L L^T, Q =
+// Z L^{-T}.  One workgroup; the factorisation by thread 0 (rank <= 32), the
+// rows of Q by all threads.
+__global__ void __launch_bounds__(1024)
+cholqr_kernel(const float* __restrict__ Z, const double* __restrict__ S, int H, int rank, float* __restrict__ Q) {
+    __shared__ double L[kMaxRank][kMaxRank];
+    __shared__ double Li[kMaxRank][kMaxRank];  // L^{-1}
+    const int tid = threadIdx.x;
+    if (tid == 0) {
+        for (int c = 0; c < rank; ++c) {
+            for (int r = 0; r < rank; ++r) L[r][c] = 0.0;
+        }
+        for (int c = 0; c < rank; ++c) {
+            double d = S[c * rank + c];
+            for (int m = 0; m < c; ++m) d -= L[c][m] * L[c][m];
+            d = d > 0.0 ? sqrt(d) : 1e-300;
+            L[c][c] = d;
+            for (int r = c + 1; r < rank; ++r) {
+                double v = S[r * rank + c];
+                for (int m = 0; m < c; ++m) v -= L[r][m] * L[c][m];
+                L[r][c] = v / d;
+            }
+        }
+        for (int c = 0; c < rank; ++c) {  // forward substitution, column by column
+            for (int r = 0; r < rank; ++r) {
+                double v = (r == c) ? 1.0 : 0.0;
+                for (int m = 0; m < r; ++m) v -= L[r][m] * Li[m][c];
+                Li[r][c] = r < c ? 0.0 : v / L[r][r];
+            }
+        }
+    }
+    __syncthreads();
+    for (int i = tid; i < H; i += 1024) {
+        double z[kMaxRank];
+        for (int m = 0; m < rank; ++m) z[m] = Z[(size_t)i * rank + m];
+        for (int c = 0; c < rank; ++c) {  // (Z L^{-T})[i][c] = sum_m z[m] Li[c][m]
+            double v = 0.0;
+            for (int m = 0; m <= c; ++m) v += z[m] * Li[c][m];
+            Q[(size_t)i * rank + c] = (float)v;
+        }
+    }
+}
+
+// Rayleigh-Ritz: B = Q^T G Q (symmetric, rank x rank) -> eigenvectors V by
+// cyclic Jacobi rotations (fp64, one thread), U = Q V with the columns in
+// decreasing eigenvalue order and each column's entry of largest magnitude
+// made positive.
+__global__ void __launch_bounds__(1024)
+ritz_kernel(const float* __restrict__ Q, const double* __restrict__ B, int H, int rank, float* __restrict__ U) {
+    __shared__ double A[kMaxRank][kMaxRank];
+    __shared__ double V[kMaxRank][kMaxRank];
+    __shared__ int ord[kMaxRank];
+    __shared__ float cmax[kMaxRank];
+    __shared__ int csgn[kMaxRank];
+    const int tid = threadIdx.x;
+    if (tid == 0) {
+        for (int r = 0; r < rank; ++r)
+            for (int c = 0; c < rank; ++c) {
+                A[r][c] = 0.5 * (B[r * rank + c] + B[c * rank + r]);
+                V[r][c] = r == c ? 1.0 : 0.0;
+            }
+        for (int sweep = 0; sweep < 60; ++sweep) {
+            double off = 0.0;
+            for (int p = 0; p < rank; ++p)
+                for (int q = p + 1; q < rank; ++q) off += A[p][q] * A[p][q];
+            if (off < 1e-30) break;
+            for (int p = 0; p < rank; ++p)
+                for (int q = p + 1; q < rank; ++q) {
+                    if (A[p][q] == 0.0) continue;
+                    const double th = (A[q][q] - A[p][p]) / (2.0 * A[p][q]);
+                    const double tt = (th >= 0 ? 1.0 : -1.0) / (fabs(th) + sqrt(th * th + 1.0));
+                    const double cs = 1.0 / sqrt(tt * tt + 1.0), sn = tt * cs;
+                    for (int m = 0; m < rank; ++m) {  // A <- J^T A J
+                        const double amp = A[m][p], amq = A[m][q];
+                        A[m][p] = cs * amp - sn * amq;
+                        A[m][q] = sn * amp + cs * amq;
+                    }
+                    for (int m = 0; m < rank; ++m) {
+                        const double apm = A[p][m], aqm = A[q][m];
+                        A[p][m] = cs * apm - sn * aqm;
+                        A[q][m] = sn * apm + cs * aqm;
+                    }
+                    for (int m = 0; m < rank; ++m) {
+                        const double vmp = V[m][p], vmq = V[m][q];
+                        V[m][p] = cs * vmp - sn * vmq;
+                        V[m][q] = sn * vmp + cs * vmq;
+                    }
+                }
+        }
+        for (int r = 0; r < rank; ++r) ord[r] = r;  // decreasing eigenvalue (stable)
+        for (int r = 1; r < rank; ++r)
+            for (int x = r; x > 0 && A[ord[x]][ord[x]] > A[ord[x - 1]][ord[x - 1]]; --x) {
+                const int tmp = ord[x];
+                ord[x] = ord[x - 1];
+                ord[x - 1] = tmp;
+            }
+        for (int c = 0; c < rank; ++c) {
+            cmax[c] = -1.f;
+            csgn[c] = 1;
+        }
+    }
+    __syncthreads();
+    // U = Q V[:, ord]; the sign of each column from its largest-magnitude entry
+    // (first such row in row order)
+    if (tid < rank) {
+        const int c = tid, vc = ord[c];
+        float best = -1.f;
+        int sg = 1;
+        for (int i = 0; i < H; ++i) {
+            double v = 0.0;
+            for (int m = 0; m < rank; ++m) v += (double)Q[(size_t)i * rank + m] * V[m][vc];
+            const float fv = (float)v;
+            if (fabsf(fv) > best) {
+                best = fabsf(fv);
+                sg = fv < 0.f ? -1 : 1;
+            }
+        }
+        csgn[c] = sg;
+    }
+    __syncthreads();
+    for (int i = tid; i < H; i += 1024) {
+        for (int c = 0; c < rank; ++c) {
+            const int vc = ord[c];
+            double v = 0.0;
+            for (int m = 0; m < rank; ++m) v += (double)Q[(size_t)i * rank + m] * V[m][vc];
+            U[(size_t)i * rank + c] = (float)(csgn[c] * v);
+        }
+    }
+}
+
+// Deterministic start of the subspace iteration: a hash of (row, column)
+// mapped to [-1, 1).
+__global__ void __launch_bounds__(kThreads) init_q_kernel(int H, int rank, float* __restrict__ Q) {
+    const int idx = blockIdx.x * kThreads + threadIdx.x;
+    if (idx >= H * rank) return;
+    uint32_t x = (uint32_t)idx * 0x9E3779B9u + 0x7F4A7C15u;
+    x ^= x >> 16;
+    x *= 0x85EBCA6Bu;
+    x ^= x >> 13;
+    x *= 0xC2B2AE35u;
+    x ^= x >> 16;
+    Q[idx] = (float)((double)x / 2147483648.0 - 1.0);
+}
+
+// b_j = U^T d_j for every channel, rounded to bf16: thread (channel, r)
+// walks the column in order in fp32.
+__global__ void __launch_bounds__(kThreads)
+recovery_coefs_kernel(const float* __restrict__ U, const uint16_t* __restrict__ Wd, int EI, int H, int rank,
+                      uint16_t* __restrict__ b) {
+    const size_t idx = (size_t)blockIdx.x * kThreads + threadIdx.x;
+    if (idx >= (size_t)EI * rank) return;
+    const size_t ch = idx / rank;
+    const int r = (int)(idx - ch * rank);
+    float acc = 0.f;
+    for (int i = 0; i < H; i += 8) {
+        float f[8];
+        unpack8(load16(Wd + ch * H + i), f);
+#pragma unroll
+        for (int x = 0; x < 8; ++x) acc = fmaf(f[x], U[(size_t)(i + x) * rank + r], acc);
+    }
+    const uint32_t u = __float_as_uint(acc);
+    b[idx] = (uint16_t)((u + 0x7FFFu + ((u >> 16) & 1u)) >> 16);
+}
+
+}  // namespace
+
+// ---------------------------------------------------------------------------
+
+int reader_row_bytes(int I) { return ((I + 4) / 5 + 15) / 16 * 16; }
+
+hipError_t launch_reader_rotate(const float* h, int M, int H, const int8_t* signs, uint8_t* xsel, float* xval,
+                                hipStream_t stream) {
+    if (H % kReaderBlock || M < 1) return hipErrorInvalidValue;
+    const int jobs = M * (H / kReaderBlock);
+    MOE_LAUNCH(reader_rotate_kernel, dim3((jobs + kWaves - 1) / kWaves), dim3(kThreads), 0, stream, h, M, H, signs,
+               xsel, xval);
+    return hipGetLastError();
+}
+
+hipError_t launch_reader_screen(const ReaderArgs& ra, const SelRoute* route, const int32_t* topk_ids, int M,
+                                hipStream_t stream) {
+    if (ra.nblk < 1 || ra.nblk > kRowGroups || ra.k < 1 || ra.k > 32 || ra.rowb != reader_row_bytes(ra.I) || M < 1)
+        return hipErrorInvalidValue;
+    const int nseg = ra.rowb / 16;
+    const dim3 grid((2 * ra.k + 7) / 8 * 8 * nseg, M);
+    if (route) {
+        if (ra.E > kThreads || route->M != M) return hipErrorInvalidValue;
+        MOE_LAUNCH(reader_screen_kernel<true>, grid, dim3(kThreads), 0, stream, ra, *route, nullptr, nseg);
+    } else {
+        MOE_LAUNCH(reader_screen_kernel<false>, grid, dim3(kThreads), 0, stream, ra, SelRoute{}, topk_ids, nseg);
+    }
+    return hipGetLastError();
+}
+
+hipError_t launch_reader_select(const ReaderArgs& ra, const int32_t* topk_ids, const float* topk_w, int M, int K,
+                                int32_t* slot_cnt, int32_t* slot_kept, int32_t* kept_out, hipStream_t stream) {
+    if (ra.k * ra.I > kSelThreads * kSelPer || ra.k > 32 || ra.E > 8192 || ra.I > 16384) return hipErrorInvalidValue;
+    MOE_LAUNCH(reader_select_kernel, dim3(M), dim3(kSelThreads), 0, stream, ra, topk_ids, topk_w, K,
+               FastDiv((uint32_t)ra.I), slot_cnt, slot_kept, kept_out);
+    return hipGetLastError();
+}
+
+int reader_recover_chunks(int I) { return (I + kThreads - 1) / kThreads; }
+
+hipError_t launch_reader_recover(const ReaderArgs& ra, const int32_t* topk_ids, const float* topk_w, int M,
+                                 hipStream_t stream) {
+    if (ra.rank < 1 || ra.rank > kMaxRank || ra.rank % 8) return hipErrorInvalidValue;
+    MOE_LAUNCH(reader_recover_kernel, dim3(reader_recover_chunks(ra.I), ra.k, M), dim3(kThreads), 0, stream, ra,
+               topk_ids, topk_w);
+    return hipGetLastError();
+}
+
+hipError_t launch_reader_combine(int M, int H, int nchunks, const float* part, const float* rpart, int nrp, int rank,
+                                 const float* U, float* y, hipStream_t stream) {
+    const dim3 grid((H / 4 + kCombCG - 1) / kCombCG, M);
+    MOE_LAUNCH(reader_combine_kernel, grid, dim3(MOE_WAVE), 0, stream, H, nchunks, part, rpart, nrp, rank, U, y);
+    return hipGetLastError();
+}
+
+hipError_t launch_reader_sketch(int E, int I, int H, const uint16_t* Wg, const uint16_t* Wu, const int8_t* signs,
+                                uint8_t* sketch, float* scale, hipStream_t stream) {
+    if (H % kReaderBlock) return hipErrorInvalidValue;
+    const dim3 grid((I + 19) / 20, H / kReaderBlock, 2 * E);
+    hipLaunchKernelGGL(reader_sketch_kernel, grid, dim3(kThreads), 0, stream, Wg, Wu, signs, H, I, reader_row_bytes(I),
+                       sketch, scale);
+    return hipGetLastError();
+}
+
+hipError_t launch_down_norms(int E, int I, int H, const uint16_t* Wd, float* dn, hipStream_t stream) {
+    const int EI = E * I;
+    hipLaunchKernelGGL(down_norms_kernel, dim3((EI + kWaves - 1) / kWaves), dim3(kThreads), 0, stream, EI, H, Wd, dn);
+    return hipGetLastError();
+}
+
+// Workspace of launch_recovery_basis: G [H][H] fp32, Q, Z [H][rank] fp32, S [rank][rank] fp64.
+size_t recovery_basis_scratch(int H, int rank) {
+    return (size_t)H * H * 4 + 2 * (size_t)H * rank * 4 + (size_t)rank * rank * 8 + 1024;
+}
+
+hipError_t launch_recovery_basis(int E, int I, int H, const uint16_t* Wd, int rank, int iters, float* U, void* scratch,
+                                 hipStream_t stream) {
+    if (rank < 1 || rank > kMaxRank || H % 64 || iters < 1) return hipErrorInvalidValue;
+    char* p = static_cast<char*>(scratch);
+    float* G = reinterpret_cast<float*>(p);
+    float* Q = reinterpret_cast<float*>(p + (size_t)H * H * 4);
+    float* Z = Q + (size_t)H * rank;
+    double* S = reinterpret_cast<double*>(reinterpret_cast<char*>(Z + (size_t)H * rank) + 256 -
+                                          (reinterpret_cast<uintptr_t>(Z + (size_t)H * rank) % 256));
+    const int nt = H / 64;
+    hipLaunchKernelGGL(gram_kernel, dim3(nt, nt), dim3(kThreads), 0, stream, Wd, E * I, H, G);
+    const int gq = (H * rank + kThreads - 1) / kThreads;
+    hipLaunchKernelGGL(init_q_kernel, dim3(gq), dim3(kThreads), 0, stream, H, rank, Q);
+    for (int it = 0; it < iters; ++it) {
+        hipLaunchKernelGGL(gemm_aq_kernel, dim3(gq), dim3(kThreads), 0, stream, G, Q, H, rank, Z);
+        hipLaunchKernelGGL(xty_kernel, dim3(1), dim3(1024), 0, stream, Z, Z, H, rank, S);
+        hipLaunchKernelGGL(cholqr_kernel, dim3(1), dim3(1024), 0, stream, Z, S, H, rank, Q);
+    }
+    hipLaunchKernelGGL(gemm_aq_kernel, dim3(gq), dim3(kThreads), 0, stream, G, Q, H, rank, Z);
+    hipLaunchKernelGGL(xty_kernel, dim3(1), dim3(1024), 0, stream, Q, Z, H, rank, S);
+    hipLaunchKernelGGL(ritz_kernel, dim3(1), dim3(1024), 0, stream, Q, S, H, rank, U);
+    return hipGetLastError();
+}
+
+hipError_t launch_recovery_coefs(int E, int I, int H, const float* U, int rank, const uint16_t* Wd, uint16_t* b,
+                                 hipStream_t stream) {
+    const size_t n = (size_t)E * I * rank;
+    hipLaunchKernelGGL(recovery_coefs_kernel, dim3((unsigned)((n + kThreads - 1) / kThreads)), dim3(kThreads), 0,
+                       stream, U, Wd, E * I, H, rank, b);
+    return hipGetLastError();
+}
+
+}  // namespace moe

@@ -11,6 +11,7 @@
 #include "align_device.h"
 #include "device_common.h"
 #include "launch.h"
+#include "reader_device.h"
 #include "topk_device.h"
 
 namespace moe {
@@ -400,11 +401,28 @@ router_align_kernel(const float* __restrict__ h, int M, int H, const uint16_t* _
 // Router GEMV only: the tiles' slice partials part[slice][t][e], stored for
 // a later launch, whose workgroups add them and take the top-k themselves
 // (the expert kernel of the batch-1 decode step, the channel selection).
+// With a rotation job (rot.signs non-null), workgroups past the router's
+// tiles rotate and scan the 128-blocks of the group's tokens for the
+// channel-selection reader instead, one block per wave.
 __global__ void __launch_bounds__(kThreads)
 router_partials_kernel(const float* __restrict__ h, int M, int H, const uint16_t* __restrict__ Wr, int E,
-                       float* __restrict__ part) {
+                       float* __restrict__ part, RotJob rot) {
     extern __shared__ __align__(16) float red[];
     const RouterTiles tl(H, E);
+    const int x = (int)blockIdx.x - tl.nrs * tl.ncg;
+    if (x >= 0) {
+        const int nblk = H / kReaderBlock;
+        const int TT = M == 1 ? 1 : kTokTile;
+        const int t0 = blockIdx.y * TT;
+        const int job = x * (kThreads / MOE_WAVE) + (int)threadIdx.x / MOE_WAVE;  // (token in group, block)
+        const int tt = job / nblk, b = job - tt * nblk;
+        if (tt >= TT || t0 + tt >= M) return;  // whole waves; no barrier follows
+        const size_t jb = (size_t)(t0 + tt) * nblk + b;
+        double* key = reinterpret_cast<double*>(red) + ((int)threadIdx.x / MOE_WAVE) * kReaderBlock;
+        rotate_scan_wave(h + (size_t)(t0 + tt) * H + b * kReaderBlock, rot.signs + b * kReaderBlock,
+                         rot.xsel + jb * kReaderScan, rot.xval + jb * kReaderScan, key);
+        return;
+    }
     if (M == 1)
         router_tile<1>(h, M, 0, H, Wr, E, tl, blockIdx.x % tl.nrs, blockIdx.x / tl.nrs, part, red);
     else
@@ -474,12 +492,22 @@ hipError_t launch_gemv_partials(const float* h, int M, int H, const GemvJob* job
 int router_slices(int H, int E) { return RouterTiles(H, E).nrs; }
 
 hipError_t launch_router_partials(const float* h, int M, int H, const uint16_t* Wr, int E, float* part,
-                                  hipStream_t stream) {
+                                  hipStream_t stream, const RotJob* rot) {
     if (M < 1 || E % 8 != 0) return hipErrorInvalidValue;
     const RouterTiles tl(H, E);
-    const size_t lds = (size_t)tl.rpt * (M == 1 ? 1 : kTokTile) * tl.cgw * sizeof(float);
-    MOE_LAUNCH(router_partials_kernel, dim3(router_grid(H, E), router_groups(M)), dim3(kThreads), lds, stream, h, M,
-               H, Wr, E, part);
+    size_t lds = (size_t)tl.rpt * (M == 1 ? 1 : kTokTile) * tl.cgw * sizeof(float);
+    int grid = router_grid(H, E);
+    RotJob rj{};
+    if (rot) {
+        if (H % kReaderBlock || !rot->signs || !rot->xsel || !rot->xval) return hipErrorInvalidValue;
+        const int jobs = (M == 1 ? 1 : kTokTile) * (H / kReaderBlock);
+        grid += (jobs + kThreads / MOE_WAVE - 1) / (kThreads / MOE_WAVE);
+        const size_t kl = (size_t)kThreads / MOE_WAVE * kReaderBlock * sizeof(double);
+        lds = lds > kl ? lds : kl;
+        rj = *rot;
+    }
+    MOE_LAUNCH(router_partials_kernel, dim3(grid, router_groups(M)), dim3(kThreads), lds, stream, h, M, H, Wr, E,
+               part, rj);
     return hipGetLastError();
 }
 

@@ -144,6 +144,8 @@ class Workload:
     vq_d: int = 8
     vq_K: int = 256
     lr_r: int = 64
+    reader: bool = False          # channel scores from the ternary-sketch reader
+    rec_rank: int = 0             # rank of the reader's recovery map (0 = none)
 
     def layer_seed(self, layer: int) -> int:
         return self.seed * 1000 + layer
@@ -161,6 +163,12 @@ WORKLOADS: Dict[str, Workload] = {w.name: w for w in [
     Workload("aligned_h2048_i768_e128_k8_m21", H=2048, I=768, E=128, k=8, M=21, seed=1003, hot_experts=4),
     Workload("chansparse_h2048_i768_e128_k8_m1_keep799", H=2048, I=768, E=128, k=8, M=1, seed=1004,
              keep=(13 * 8 * 768 + 50) // 100),
+    # the sketch reader at the page's exact-channel budget: 12.3% of the
+    # 8 * 768 candidates computed exactly, without and with the rank-32 map
+    Workload("reader_h2048_i768_e128_k8_m1_keep756", H=2048, I=768, E=128, k=8, M=1, seed=1008, keep=756,
+             reader=True),
+    Workload("reader_h2048_i768_e128_k8_m1_keep756_r32", H=2048, I=768, E=128, k=8, M=1, seed=1008, keep=756,
+             reader=True, rec_rank=32),
     Workload("vqlr_h2048_i768_e128_k8_m4_d8_K256_r64", H=2048, I=768, E=128, k=8, M=4, seed=1005, vq=True),
     # block-length sweep at the 4-bit storage rate, same router, hidden states
     # and routing as the workload above (same seed)
