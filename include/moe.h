@@ -149,7 +149,8 @@ typedef struct {
  *  rec_basis    fp32 [H][rec_rank] (moe_recovery_basis), with rec_rank > 0
  *  rec_coef     bf16 [E][I][rec_rank] (moe_recovery_coefs), with rec_rank > 0
  *  Alignment (checked by moe_create, MOE_ERR_INVALID_ARG otherwise): the bf16
- *  arrays, vq_idx and sketch 16 bytes, the fp32 / int32 arrays 4 bytes.
+ *  arrays, vq_idx, sketch and down_norm 16 bytes, the other fp32 / int32
+ *  arrays 4 bytes.
  */
 typedef struct {
     const uint16_t *router_w;

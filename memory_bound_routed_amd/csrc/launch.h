@@ -183,8 +183,9 @@ hipError_t launch_channel_norms(int E, int I, int H, const uint16_t* Wg, const u
 //  sketch    u8 [E][2][nblk][128][rowb]  base-3 codes, coordinate-major rows
 //  scale     fp32 [E][2][nblk][I]        per (block, channel) scale / 128
 //  xsel/xval u8 / fp32 [M][nblk][80]     scanned coordinates (ascending), x''
-//  est       fp32 [M][k][2][I]           g_hat (P = 0), v_hat (P = 1)
-//  phat, score fp32 [M][k][I];  kept_flag u8 [M][k][I]
+//  est       fp32 [M][k][2][nbq][I]      partial g_hat (P = 0), v_hat (P = 1) of
+//                                        each group of bpw blocks (reader_groups)
+//  kept_flag u8 [M][k][I]
 //  dnorm     fp32 [E][I];  rec_coef bf16 [E][I][rank];  rpart fp32 [M][k][chunks][rank]
 struct ReaderArgs {
     const uint8_t* sketch;
@@ -192,14 +193,14 @@ struct ReaderArgs {
     const uint8_t* xsel;
     const float* xval;
     float* est;
-    float* phat;
-    float* score;
     const float* dnorm;
     uint8_t* kept_flag;
     const uint16_t* rec_coef;
     float* rpart;
     int rank;
     int nblk;
+    int nbq;
+    int bpw;
     int rowb;
     int I;
     int k;
@@ -207,6 +208,9 @@ struct ReaderArgs {
 };
 // Bytes of one coordinate row of the sketch: ceil(I / 5) padded to 16.
 int reader_row_bytes(int I);
+// Block groups of the screening: bpw = ceil(nblk / 2) blocks each; returns
+// their number nbq (<= 2).
+int reader_groups(int nblk, int* bpw);
 // Rotation + partial scan of each 128-block of h (M tokens) in its own launch.
 hipError_t launch_reader_rotate(const float* h, int M, int H, const int8_t* signs, uint8_t* xsel, float* xval,
                                 hipStream_t stream);
@@ -215,9 +219,12 @@ hipError_t launch_reader_rotate(const float* h, int M, int H, const int8_t* sign
 hipError_t launch_reader_screen(const ReaderArgs& ra, const SelRoute* route, const int32_t* topk_ids, int M,
                                 hipStream_t stream);
 // Output-level scores and the exact top K per token: slot_cnt / slot_kept as
-// launch_chan_select, phat, score and kept_flag in ra.
+// launch_chan_select and kept_flag in ra; optionally (non-null) the kept set
+// kept_out [M][K], the summed estimates est_out [M][k][2][I] and the scores
+// score_out [M][k][I].
 hipError_t launch_reader_select(const ReaderArgs& ra, const int32_t* topk_ids, const float* topk_w, int M, int K,
-                                int32_t* slot_cnt, int32_t* slot_kept, int32_t* kept_out, hipStream_t stream);
+                                int32_t* slot_cnt, int32_t* slot_kept, int32_t* kept_out, float* est_out,
+                                float* score_out, hipStream_t stream);
 int reader_recover_chunks(int I);
 // Recovery partials rpart of the dropped candidates (ra.rank in 8..32, % 8).
 hipError_t launch_reader_recover(const ReaderArgs& ra, const int32_t* topk_ids, const float* topk_w, int M,

@@ -36,14 +36,12 @@ struct Workspace {
     int32_t* slot_cnt = nullptr;   // channel-sparse: kept channels per (token, slot), int32 [MT][k]
     int32_t* slot_kept = nullptr;  // ... and their channels, int32 [MT][k][I]
     float* chan_part = nullptr;
-    // reader: scanned coordinates and values [MT][H/128][80], estimates
-    // [MT][k][2][I], p_hat, scores and kept flags [MT][k][I], recovery
+    // reader: scanned coordinates and values [MT][H/128][80], estimates of
+    // the block groups [MT][k][2][nbq][I], kept flags [MT][k][I], recovery
     // partials [MT][k][chunks][rec_rank]
     uint8_t* xsel = nullptr;
     float* xval = nullptr;
     float* est = nullptr;
-    float* phat = nullptr;
-    float* score = nullptr;
     uint8_t* kept_flag = nullptr;
     float* rpart = nullptr;
 };
@@ -130,7 +128,7 @@ moe_status check_weights(const moe_config* c, const moe_weights* w) {
         return MOE_ERR_INVALID_ARG;
     if (c->reader) {
         if (!w->rot_signs || !w->sketch || !aligned(w->sketch, 16) || !w->sketch_scale ||
-            !aligned(w->sketch_scale, 4) || !w->down_norm || !aligned(w->down_norm, 4))
+            !aligned(w->sketch_scale, 4) || !w->down_norm || !aligned(w->down_norm, 16))
             return MOE_ERR_INVALID_ARG;
         if (c->rec_rank &&
             (!w->rec_basis || !aligned(w->rec_basis, 4) || !w->rec_coef || !aligned(w->rec_coef, 16)))
@@ -155,7 +153,8 @@ size_t workspace_layout(const moe_config& c, size_t MT, char* base, Workspace* w
     const size_t rd = c.reader ? 1 : 0;
     const size_t nscan = rd * MT * (c.H / 128) * 80;  // scanned coordinates of all blocks
     const size_t nkc = rd * R * c.I;                    // candidates
-    constexpr int kBufs = 15;
+    const size_t nbq = c.reader ? (size_t)moe::reader_groups(c.H / 128, nullptr) : 0;
+    constexpr int kBufs = 13;
     const size_t sizes[kBufs] = {
         64 + sizeof(unsigned) * (1 + (size_t)moe::router_groups((int)MT)),  // err flag, router tickets
         sizeof(float) * moe::gemv_slices(c.H, c.E) * MT * c.E,          // router partials
@@ -167,9 +166,7 @@ size_t workspace_layout(const moe_config& c, size_t MT, char* base, Workspace* w
         sizeof(float) * MT * nchan * c.H,                               // channel partials
         nscan,                                                          // reader: scanned coordinates
         sizeof(float) * nscan,                                          // ... and their values
-        sizeof(float) * 2 * nkc,                                        // estimates
-        sizeof(float) * nkc,                                            // p_hat
-        sizeof(float) * nkc,                                            // scores
+        sizeof(float) * 2 * nbq * nkc,                                  // group estimates
         nkc,                                                            // kept flags
         sizeof(float) * R * (c.rec_rank ? (size_t)moe::reader_recover_chunks(c.I) * c.rec_rank : 0),  // recovery
     };
@@ -192,10 +189,8 @@ size_t workspace_layout(const moe_config& c, size_t MT, char* base, Workspace* w
         ws->xsel = reinterpret_cast<uint8_t*>(base + off[8]);
         ws->xval = reinterpret_cast<float*>(base + off[9]);
         ws->est = reinterpret_cast<float*>(base + off[10]);
-        ws->phat = reinterpret_cast<float*>(base + off[11]);
-        ws->score = reinterpret_cast<float*>(base + off[12]);
-        ws->kept_flag = reinterpret_cast<uint8_t*>(base + off[13]);
-        ws->rpart = reinterpret_cast<float*>(base + off[14]);
+        ws->kept_flag = reinterpret_cast<uint8_t*>(base + off[11]);
+        ws->rpart = reinterpret_cast<float*>(base + off[12]);
     }
     return total;
 }
@@ -275,14 +270,13 @@ moe::ReaderArgs reader_args(const Exec& x) {
     ra.xsel = x.ws.xsel;
     ra.xval = x.ws.xval;
     ra.est = x.ws.est;
-    ra.phat = x.ws.phat;
-    ra.score = x.ws.score;
     ra.dnorm = x.w.down_norm;
     ra.kept_flag = x.ws.kept_flag;
     ra.rec_coef = x.w.rec_coef;
     ra.rpart = x.ws.rpart;
     ra.rank = x.c.rec_rank;
     ra.nblk = x.c.H / 128;
+    ra.nbq = moe::reader_groups(ra.nblk, &ra.bpw);
     ra.rowb = moe::reader_row_bytes(x.c.I);
     ra.I = x.c.I;
     ra.k = x.c.top_k;
@@ -312,7 +306,8 @@ moe_status reader_forward(const Exec& x, bool rotated, const moe::SelRoute* rout
     }
     {
         Launch l(x.prof, MOE_KERNEL_READER_SELECT);
-        e = moe::launch_reader_select(ra, topk_ids, topk_w, M, K, x.ws.slot_cnt, x.ws.slot_kept, nullptr, s);
+        e = moe::launch_reader_select(ra, topk_ids, topk_w, M, K, x.ws.slot_cnt, x.ws.slot_kept, nullptr, nullptr,
+                                      nullptr, s);
         l.done();
         if (e != hipSuccess) return MOE_ERR_HIP;
     }
@@ -767,13 +762,10 @@ moe_status moe_reader_inspect(moe_ctx* ctx, const float* h, int32_t M, const int
     hipError_t e = moe::launch_reader_rotate(h, M, c.H, x.w.rot_signs, x.ws.xsel, x.ws.xval, s);
     if (e == hipSuccess) e = moe::launch_reader_screen(ra, nullptr, topk_ids, M, s);
     if (e == hipSuccess)
-        e = moe::launch_reader_select(ra, topk_ids, topk_w, M, K, x.ws.slot_cnt, x.ws.slot_kept, kept, s);
+        e = moe::launch_reader_select(ra, topk_ids, topk_w, M, K, x.ws.slot_cnt, x.ws.slot_kept, kept, est, score, s);
     const size_t nscan = (size_t)M * (c.H / 128) * 80;
-    const size_t nkc = (size_t)M * c.top_k * c.I;
     if (e == hipSuccess && xsel) e = hipMemcpyAsync(xsel, x.ws.xsel, nscan, hipMemcpyDeviceToDevice, s);
     if (e == hipSuccess && xval) e = hipMemcpyAsync(xval, x.ws.xval, 4 * nscan, hipMemcpyDeviceToDevice, s);
-    if (e == hipSuccess && est) e = hipMemcpyAsync(est, x.ws.est, 8 * nkc, hipMemcpyDeviceToDevice, s);
-    if (e == hipSuccess && score) e = hipMemcpyAsync(score, x.ws.score, 4 * nkc, hipMemcpyDeviceToDevice, s);
     return hip_status(e);
 }
 

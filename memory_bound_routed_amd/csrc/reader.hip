@@ -47,36 +47,42 @@ constexpr int kMaxRank = 32;
 __global__ void __launch_bounds__(kThreads)
 reader_rotate_kernel(const float* __restrict__ h, int M, int H, const int8_t* __restrict__ signs,
                      uint8_t* __restrict__ xsel, float* __restrict__ xval) {
-    __shared__ double key[kWaves][kReaderBlock];
     const int nblk = H / kReaderBlock;
     const int job = blockIdx.x * kWaves + threadIdx.x / MOE_WAVE;
     if (job >= M * nblk) return;  // whole waves
     const int t = job / nblk, b = job - t * nblk;
     rotate_scan_wave(h + (size_t)t * H + b * kReaderBlock, signs + b * kReaderBlock,
-                     xsel + (size_t)job * kReaderScan, xval + (size_t)job * kReaderScan, key[threadIdx.x / MOE_WAVE]);
+                     xsel + (size_t)job * kReaderScan, xval + (size_t)job * kReaderScan);
 }
 
 // ---------------------------------------------------------------------------
-// Screening.  Workgroup (pair, c) of token t estimates projection P of slot
-// s's expert (pair = 2 s + P) for the 80 channels 80 c .. 80 c + 79, i.e.
-// bytes 16 c .. 16 c + 15 of every scanned coordinate row.  The grid's x
-// runs over groups of 8 pairs times the nseg channel ranges with the pair
-// varying fastest (x = pair % 8 + 8 (c + nseg (pair / 8))): workgroups are
-// dealt to the 8 XCDs round-robin by their linear id, so all ranges of one
-// pair -- which read the same cache lines of the same rows -- share one
-// XCD's L2, while the pairs spread over the XCDs.
+// Screening.  The work of one token is cut into units (pair, c, bq): pair =
+// 2 s + P (projection P of slot s's expert), c the range of 80 channels
+// 80 c .. 80 c + 79 (bytes 16 c .. 16 c + 15 of every coordinate row) and bq
+// the group of bpw consecutive 128-blocks bq * bpw .. (nbq = ceil(nblk /
+// bpw) groups, bpw = ceil(nblk / 2)).  A workgroup per unit writes the
+// group's partial estimate est[t][s][P][bq][j]; the selection adds the nbq
+// partials in order.  The grid's x runs over groups of 8 pairs times the
+// (c, bq) units with the pair varying fastest (x = pair % 8 + 8 (u + nu
+// (pair / 8)), u = c + nseg bq): workgroups are dealt to the 8 XCDs
+// round-robin by their linear id, so all units of one pair -- which read the
+// same cache lines of the same rows -- share one XCD's L2, while the pairs
+// spread over the XCDs.
 //
-// Thread (row group rg = tid / 4, word w = tid % 4): block b = rg % nblk,
-// the scanned coordinates n = q, q + Pb, ... with q = rg / nblk and Pb =
-// 64 / nblk groups per block; bytes 16 c + 4 w .. + 3 of each such row
+// Thread (row group rg = tid / 4, word w = tid % 4): local block bl = rg %
+// bpw, the scanned coordinates n = q, q + Pb, ... with q = rg / bpw and Pb =
+// 64 / bpw groups per block; bytes 16 c + 4 w .. + 3 of each such row
 // (channels 80 c + 20 w .. + 19).  Each row's 4 bytes are decoded with a
 // 243-entry table of codes in LDS and accumulated against x''; the sum of a
 // row group is scaled by its block's scale, and the 64 row groups are added
-// in order.  The scanned coordinates of all blocks are staged in LDS (their
-// loads issued before the routing).  ROUTE: every workgroup first routes its
-// token from the router's slice partials with the router's arithmetic
-// (E <= 256).
-constexpr int kStage = kRowGroups * kReaderScan / kThreads;  // staged (coordinate, value) per thread, nblk <= 64
+// in order.  The group's scanned coordinates are staged in LDS (their loads
+// issued before the routing); the scales are loaded with the rows.  ROUTE:
+// every workgroup first routes its token from the router's slice partials
+// with the router's arithmetic (E <= 256).
+constexpr int kMaxBpw = 32;                                      // nblk <= 64
+constexpr int kMaxGroups = 2;
+constexpr int kStage = kMaxBpw * kReaderScan / kThreads;         // staged (coordinate, value) per thread
+constexpr int kRowBatch = 10;                                    // rows in flight per thread
 
 template <bool ROUTE>
 __global__ void __launch_bounds__(kThreads)
@@ -84,12 +90,16 @@ reader_screen_kernel(ReaderArgs ra, SelRoute route, const int32_t* __restrict__ 
     __shared__ float4 lut4[243];
     __shared__ float lut1[243];
     __shared__ float red[kRowGroups][kRangeCh + 1];
-    __shared__ uint8_t s_sel[kRowGroups * kReaderScan];
-    __shared__ float s_val[kRowGroups * kReaderScan];
+    __shared__ uint8_t s_sel[kMaxBpw * kReaderScan];
+    __shared__ float s_val[kMaxBpw * kReaderScan];
     __shared__ int s_e;
     const int x = blockIdx.x;
-    const int pair = x % 8 + 8 * (x / (8 * nseg));
-    const int c = (x / 8) % nseg;
+    const int nbq = ra.nbq, bpw = ra.bpw;
+    const int nu = nseg * nbq;
+    const int pair = x % 8 + 8 * (x / (8 * nu));
+    const int u0 = (x / 8) % nu;
+    const int c = u0 % nseg;
+    const int bq = u0 / nseg;
     const int t = blockIdx.y;
     const int k = ra.k;
     if (pair >= 2 * k) return;  // whole workgroup, before any barrier
@@ -100,14 +110,16 @@ reader_screen_kernel(ReaderArgs ra, SelRoute route, const int32_t* __restrict__ 
     const int rg = tid / 4;
     const int nblk = ra.nblk;
     const int I = ra.I;
+    const int b0 = bq * bpw;
+    const int nbh = min(bpw, nblk - b0);  // blocks of this group
 
-    // scanned coordinates and values of the token's blocks (independent of the routing)
-    const int nst = nblk * kReaderScan;
+    // scanned coordinates and values of the group's blocks (independent of the routing)
+    const int nst = nbh * kReaderScan;
     uint32_t st_sel[kStage];
     float st_val[kStage];
     {
-        const uint8_t* gs = ra.xsel + (size_t)t * nst;
-        const float* gv = ra.xval + (size_t)t * nst;
+        const uint8_t* gs = ra.xsel + ((size_t)t * nblk + b0) * kReaderScan;
+        const float* gv = ra.xval + ((size_t)t * nblk + b0) * kReaderScan;
 #pragma unroll
         for (int u = 0; u < kStage; ++u) {
             const int i = min(tid + kThreads * u, nst - 1);
@@ -136,7 +148,7 @@ reader_screen_kernel(ReaderArgs ra, SelRoute route, const int32_t* __restrict__ 
         __shared__ int wi[MOE_WAVE];
         __shared__ int s_slow;
         const int E = ra.E;
-        const bool writer = x == 0;  // pair 0, range 0 writes the routing
+        const bool writer = x == 0;  // pair 0, unit 0 writes the routing
         float lg = 0.f;
         if (tid < E) {
             const float bv = route.bias ? route.bias[tid] : 0.f;
@@ -190,30 +202,36 @@ reader_screen_kernel(ReaderArgs ra, SelRoute route, const int32_t* __restrict__ 
     const bool valid = e >= 0 && e < ra.E;
     const int ec = valid ? e : 0;
 
-    // this thread's rows: block b, scanned coordinates q, q + Pb, ... (< 80)
-    const int Pb = kRowGroups / nblk;
-    const int b = rg % nblk;
-    const int q = rg / nblk;
-    const bool active = rg < nblk * Pb;
+    // this thread's rows: local block bl, scanned coordinates q, q + Pb, ... (< 80)
+    const int Pb = kRowGroups / bpw;
+    const int bl = rg % bpw;
+    const int q = rg / bpw;
+    const bool active = q < Pb && bl < nbh;
+    const int b = b0 + min(bl, nbh - 1);
     const int nrows = active ? (kReaderScan - q + Pb - 1) / Pb : 0;  // rows of this group
     const uint8_t* rows = ra.sketch + (((size_t)ec * 2 + P) * nblk + b) * kReaderBlock * ra.rowb + 16 * c + 4 * w;
-    const uint8_t* ssel = s_sel + b * kReaderScan;
-    const float* sval = s_val + b * kReaderScan;
+    const uint8_t* ssel = s_sel + min(bl, nbh - 1) * kReaderScan;
+    const float* sval = s_val + min(bl, nbh - 1) * kReaderScan;
+    // the block's scales of this thread's 20 channels, loaded with the first rows
+    const int ch0 = kRangeCh * c + 20 * w;
+    const float* scl = ra.scale + (((size_t)ec * 2 + P) * nblk + b) * I;
+    float sv[20];
+#pragma unroll
+    for (int m = 0; m < 20; ++m) sv[m] = scl[min(ch0 + m, I - 1)];
     float acc[20];
 #pragma unroll
     for (int m = 0; m < 20; ++m) acc[m] = 0.f;
-    constexpr int kBatch = 20;
-    for (int n0 = 0; n0 < nrows; n0 += kBatch) {  // uniform per row group
-        uint32_t wd[kBatch];
-        float xv[kBatch];
+    for (int n0 = 0; n0 < nrows; n0 += kRowBatch) {  // uniform per row group
+        uint32_t wd[kRowBatch];
+        float xv[kRowBatch];
 #pragma unroll
-        for (int u = 0; u < kBatch; ++u) {
+        for (int u = 0; u < kRowBatch; ++u) {
             const int n = min(q + (n0 + u) * Pb, kReaderScan - 1);
             wd[u] = *reinterpret_cast<const uint32_t*>(rows + (size_t)ssel[n] * ra.rowb);
             xv[u] = n0 + u < nrows ? sval[n] : 0.f;
         }
 #pragma unroll
-        for (int u = 0; u < kBatch; ++u) {
+        for (int u = 0; u < kRowBatch; ++u) {
 #pragma unroll
             for (int y = 0; y < 4; ++y) {
                 const uint32_t v = (wd[u] >> (8 * y)) & 255u;
@@ -229,143 +247,318 @@ reader_screen_kernel(ReaderArgs ra, SelRoute route, const int32_t* __restrict__ 
         }
     }
     // the block's scale per channel, then the row groups in order
-    const int ch0 = kRangeCh * c + 20 * w;
-    const float* scl = ra.scale + (((size_t)ec * 2 + P) * nblk + b) * I;
 #pragma unroll
-    for (int m = 0; m < 20; ++m) {
-        const float sv = scl[min(ch0 + m, I - 1)];
-        red[rg][20 * w + m] = (active && ch0 + m < I) ? sv * acc[m] : 0.f;
-    }
+    for (int m = 0; m < 20; ++m) red[rg][20 * w + m] = (active && ch0 + m < I) ? sv[m] * acc[m] : 0.f;
     __syncthreads();
     if (tid < kRangeCh && kRangeCh * c + tid < I) {
         float g = 0.f;
         for (int r2 = 0; r2 < kRowGroups; ++r2) g += red[r2][tid];
-        ra.est[(((size_t)t * k + s) * 2 + P) * I + kRangeCh * c + tid] = valid ? g : 0.f;
+        ra.est[((((size_t)t * k + s) * 2 + P) * nbq + bq) * I + kRangeCh * c + tid] = valid ? g : 0.f;
     }
 }
 
 // ---------------------------------------------------------------------------
 // Selection, one workgroup per token.  Candidate idx = s * I + j, thread tid
 // owning idx = 8 tid .. 8 tid + 7 (a contiguous run, for the scan of the kept
-// flags).  Key: the score's bits (non-negative fp32, so order-preserving) in
-// the high word, the complement of (e << 19 | j << 5 | s) in the low word, so
-// that equal scores order by expert id, channel, then slot; keys are
-// distinct.  The K-th largest key is found digit by digit from the top (8
-// bits per pass, a histogram in LDS, stopping as soon as the remaining
-// demand is a whole digit bucket); the kept candidates are the keys at or
-// above it.
-__device__ __forceinline__ uint64_t cand_key(float score, int e, int j, int s) {
-    const uint32_t tb = ((uint32_t)e << 19) | ((uint32_t)j << 5) | (uint32_t)s;
-    return ((uint64_t)__float_as_uint(score) << 32) | (uint32_t)(0xFFFFFFFFu - tb);
+// flags).  g_hat and v_hat are the screening's group partials added in
+// order; the score (w_s * ||d_j||) * |SiLU(g_hat) v_hat| is a non-negative
+// fp32 (NaN and invalid slots score 0) whose bit pattern orders like its
+// value.
+//
+// The K-th largest score is found by a radix select over the 32-bit pattern
+// in three digit passes (bits 31..21, 20..10, 9..0): each pass histograms the
+// digit of the candidates that share the digits found so far (LDS atomics),
+// and a suffix scan over the bins finds the bin where the count of larger
+// candidates reaches the demand.  When the demand is that whole bin the kept
+// set is every score at or above the bin's prefix; otherwise, after the last
+// pass, the K-th score T is exact and the candidates scoring exactly T are
+// taken in the order (expert id, channel, slot): the same select over the
+// complement of the 32-bit tie key e << 19 | j << 5 | s (invalid slots as
+// expert 8191) picks the ones needed.
+constexpr int kSelWaves = kSelThreads / MOE_WAVE;
+constexpr int kRadixBins = 2048;
+
+struct RadixLds {
+    int hist[kRadixBins];
+    int wsum[kSelWaves];
+    uint32_t wmax[kSelWaves], wmin[kSelWaves];
+    int digit, above, cnt;
+};
+
+// After the histogram L.hist[0 .. nb) is complete (and a barrier): the bin
+// where the candidates in larger bins first reach `need` -- its index, the
+// count in larger bins and its own count, the same in every thread.
+__device__ __forceinline__ void find_bin(int nb, int need, RadixLds& L, int* digit, int* above, int* cnt) {
+    const int tid = threadIdx.x;
+    const int lane = tid % MOE_WAVE, wave = tid / MOE_WAVE;
+    const int nbt = nb / 2;  // thread tid owns the bins nb-1-2 tid and nb-2-2 tid (descending)
+    const int b1 = nb - 1 - 2 * tid, b2 = nb - 2 - 2 * tid;
+    const int h1 = tid < nbt ? L.hist[b1] : 0;
+    const int h2 = tid < nbt ? L.hist[b2] : 0;
+    const int loc = h1 + h2;
+    int incl = loc;
+#pragma unroll
+    for (int d = 1; d < MOE_WAVE; d <<= 1) {
+        const int y = __shfl_up(incl, d, MOE_WAVE);
+        if (lane >= d) incl += y;
+    }
+    if (lane == MOE_WAVE - 1) L.wsum[wave] = incl;
+    __syncthreads();
+    int base = 0;
+    for (int x = 0; x < wave; ++x) base += L.wsum[x];
+    const int before = base + incl - loc;  // candidates in larger bins
+    if (tid < nbt) {
+        if (before < need && need <= before + h1) {
+            L.digit = b1;
+            L.above = before;
+            L.cnt = h1;
+        } else if (before + h1 < need && need <= before + loc) {
+            L.digit = b2;
+            L.above = before + h1;
+            L.cnt = h2;
+        }
+    }
+    __syncthreads();
+    *digit = L.digit;
+    *above = L.above;
+    *cnt = L.cnt;
+    __syncthreads();  // L is reused next
+}
+
+// Among the candidates u with (vmask >> u) & 1 (at least `need` of them),
+// the value X such that `need` keys are >= X: returns X and sets *whole when
+// the keys >= X are exactly `need` (else the keys equal to X exceed the
+// demand: ties).  Three digit passes (bits 31..21, 20..10, 9..0), each a
+// histogram of the candidates sharing the digits found so far.  1024 threads.
+__device__ uint32_t radix_kth_largest(const uint32_t (&key)[kSelPer], unsigned vmask, int need, RadixLds& L,
+                                      bool* whole) {
+    const int tid = threadIdx.x;
+    uint32_t prefix = 0, pmask = 0;
+    *whole = false;
+    for (int pass = 0; pass < 3; ++pass) {  // uniform
+        const int shift = pass == 0 ? 21 : (pass == 1 ? 10 : 0);
+        const int nb = pass == 2 ? 1024 : 2048;
+        for (int i = tid; i < nb; i += kSelThreads) L.hist[i] = 0;
+        __syncthreads();
+#pragma unroll
+        for (int u = 0; u < kSelPer; ++u)
+            if (((vmask >> u) & 1u) && (key[u] & pmask) == prefix) atomicAdd(&L.hist[(key[u] >> shift) & (nb - 1)], 1);
+        __syncthreads();
+        int dg, ab, ct;
+        find_bin(nb, need, L, &dg, &ab, &ct);
+        prefix |= (uint32_t)dg << shift;
+        pmask |= (uint32_t)(nb - 1) << shift;
+        need -= ab;
+        if (need == ct) {  // the whole bin is kept (uniform)
+            *whole = true;
+            return prefix;
+        }
+    }
+    return prefix;  // exact value; its keys exceed the demand
+}
+
+template <int CTRL>
+__device__ __forceinline__ uint32_t dpp_u32(uint32_t v) {
+    return (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, CTRL, 0xF, 0xF, false);
+}
+
+// Workgroup maximum and minimum of one value per thread.
+__device__ __forceinline__ void block_max_min(uint32_t mx, uint32_t mn, RadixLds& L, uint32_t* omx, uint32_t* omn) {
+    mx = max(mx, dpp_u32<MOE_DPP_QUAD_XOR1>(mx));
+    mn = min(mn, dpp_u32<MOE_DPP_QUAD_XOR1>(mn));
+    mx = max(mx, dpp_u32<MOE_DPP_QUAD_XOR2>(mx));
+    mn = min(mn, dpp_u32<MOE_DPP_QUAD_XOR2>(mn));
+    mx = max(mx, dpp_u32<MOE_DPP_ROW_HALF_MIRROR>(mx));
+    mn = min(mn, dpp_u32<MOE_DPP_ROW_HALF_MIRROR>(mn));
+    mx = max(mx, dpp_u32<MOE_DPP_ROW_MIRROR>(mx));
+    mn = min(mn, dpp_u32<MOE_DPP_ROW_MIRROR>(mn));
+    uint32_t wmx = 0, wmn = 0xFFFFFFFFu;
+#pragma unroll
+    for (int r = 0; r < 4; ++r) {
+        wmx = max(wmx, (uint32_t)__builtin_amdgcn_readlane((int)mx, 16 * r));
+        wmn = min(wmn, (uint32_t)__builtin_amdgcn_readlane((int)mn, 16 * r));
+    }
+    const int wave = threadIdx.x / MOE_WAVE;
+    if (threadIdx.x % MOE_WAVE == 0) {
+        L.wmax[wave] = wmx;
+        L.wmin[wave] = wmn;
+    }
+    __syncthreads();
+    uint32_t a = 0, b = 0xFFFFFFFFu;
+    for (int x = 0; x < kSelWaves; ++x) {
+        a = max(a, L.wmax[x]);
+        b = min(b, L.wmin[x]);
+    }
+    *omx = a;
+    *omn = b;
 }
 
 __global__ void __launch_bounds__(kSelThreads)
 reader_select_kernel(ReaderArgs ra, const int32_t* __restrict__ topk_ids, const float* __restrict__ topk_w, int K,
                      FastDiv fI, int32_t* __restrict__ slot_cnt, int32_t* __restrict__ slot_kept,
-                     int32_t* __restrict__ kept_out) {
+                     int32_t* __restrict__ kept_out, float* __restrict__ est_out, float* __restrict__ score_out) {
     __shared__ int se[32];
     __shared__ float sw[32];
-    __shared__ int hist[256];
-    __shared__ uint64_t s_pref;
-    __shared__ int s_need, s_done;
-    __shared__ int wsum[kSelThreads / MOE_WAVE];
+    __shared__ RadixLds rl;
+    __shared__ int wsum[kSelWaves];
     __shared__ int slot_off[33];
     const int t = blockIdx.x;
     const int tid = threadIdx.x;
-    const int I = ra.I, k = ra.k, E = ra.E;
+    const int I = ra.I, k = ra.k, E = ra.E, nbq = ra.nbq;
     const int n = k * I;
+    const float* __restrict__ est = ra.est;
+    const float* __restrict__ dnorm = ra.dnorm;
     if (tid < k) {
         const int e = topk_ids[(size_t)t * k + tid];
         se[tid] = (e >= 0 && e < E) ? e : -1;
         sw[tid] = topk_w[(size_t)t * k + tid];
     }
-    if (tid < 256) hist[tid] = 0;
     __syncthreads();
-    uint64_t key[kSelPer];
+    // every load first: the group partials of g and v and the norm of each
+    // candidate -- as 16-byte loads when a thread's 8 candidates are 8
+    // consecutive channels of one slot (I % 8 == 0), else one by one
+    float g[kSelPer], v[kSelPer], dn[kSelPer];
+    if (I % kSelPer == 0) {  // uniform
+        const int ic = min(kSelPer * tid, n - kSelPer);
+        const int s = fI.div(ic), j = ic - s * I;
+        const float* eg = est + (((size_t)t * k + s) * 2 * nbq) * I + j;
+        float4 gq[kMaxGroups][2], vq[kMaxGroups][2], dq[2];
+#pragma unroll
+        for (int q = 0; q < kMaxGroups; ++q) {
+#pragma unroll
+            for (int h2 = 0; h2 < 2; ++h2) {
+                gq[q][h2] = *reinterpret_cast<const float4*>(eg + (size_t)min(q, nbq - 1) * I + 4 * h2);
+                vq[q][h2] = *reinterpret_cast<const float4*>(eg + (size_t)(nbq + min(q, nbq - 1)) * I + 4 * h2);
+            }
+        }
+#pragma unroll
+        for (int h2 = 0; h2 < 2; ++h2)
+            dq[h2] = *reinterpret_cast<const float4*>(dnorm + (size_t)max(se[s], 0) * I + j + 4 * h2);
+#pragma unroll
+        for (int u = 0; u < kSelPer; ++u) {
+            const int h2 = u / 4, c4 = u % 4;
+            auto comp = [&](const float4& f) { return c4 == 0 ? f.x : (c4 == 1 ? f.y : (c4 == 2 ? f.z : f.w)); };
+            g[u] = comp(gq[0][h2]);
+            v[u] = comp(vq[0][h2]);
+#pragma unroll
+            for (int q = 1; q < kMaxGroups; ++q) {
+                g[u] += q < nbq ? comp(gq[q][h2]) : 0.f;
+                v[u] += q < nbq ? comp(vq[q][h2]) : 0.f;
+            }
+            dn[u] = comp(dq[h2]);
+        }
+    } else {
+        float gp[kSelPer][kMaxGroups], vp[kSelPer][kMaxGroups];
+#pragma unroll
+        for (int u = 0; u < kSelPer; ++u) {
+            const int ic = min(kSelPer * tid + u, n - 1);
+            const int s = fI.div(ic), j = ic - s * I;
+            const float* eg = est + (((size_t)t * k + s) * 2 * nbq) * I + j;
+#pragma unroll
+            for (int q = 0; q < kMaxGroups; ++q) {
+                gp[u][q] = eg[(size_t)min(q, nbq - 1) * I];
+                vp[u][q] = eg[(size_t)(nbq + min(q, nbq - 1)) * I];
+            }
+            dn[u] = dnorm[(size_t)max(se[s], 0) * I + j];
+        }
+#pragma unroll
+        for (int u = 0; u < kSelPer; ++u) {
+            g[u] = gp[u][0];
+            v[u] = vp[u][0];
+#pragma unroll
+            for (int q = 1; q < kMaxGroups; ++q) {
+                g[u] += q < nbq ? gp[u][q] : 0.f;
+                v[u] += q < nbq ? vp[u][q] : 0.f;
+            }
+        }
+    }
+    uint32_t sb[kSelPer];  // score bits
+    uint32_t tb[kSelPer];  // tie keys
+    unsigned vmask = 0;    // real candidates
+    uint32_t smax = 0, smin = 0xFFFFFFFFu;
 #pragma unroll
     for (int u = 0; u < kSelPer; ++u) {
         const int idx = kSelPer * tid + u;
         const int ic = min(idx, n - 1);
         const int s = fI.div(ic), j = ic - s * I;
         const int e = se[s];
-        const float g = ra.est[(((size_t)t * k + s) * 2 + 0) * I + j];
-        const float v = ra.est[(((size_t)t * k + s) * 2 + 1) * I + j];
-        const float dn = ra.dnorm[(size_t)max(e, 0) * I + j];
-        const float ph = silu_mul(g, v);
-        float sc = (sw[s] * dn) * fabsf(ph);
+        float sc = (sw[s] * dn[u]) * fabsf(silu_mul(g[u], v[u]));
         if (!(sc >= 0.f) || e < 0) sc = 0.f;  // NaN, invalid slot
+        sc += 0.f;                          // -0 as +0
         if (idx < n) {
-            ra.phat[((size_t)t * k + s) * I + j] = ph;
-            ra.score[((size_t)t * k + s) * I + j] = sc;
+            if (est_out) {
+                est_out[(((size_t)t * k + s) * 2 + 0) * I + j] = g[u];
+                est_out[(((size_t)t * k + s) * 2 + 1) * I + j] = v[u];
+            }
+            if (score_out) score_out[((size_t)t * k + s) * I + j] = sc;
         }
-        key[u] = idx < n ? cand_key(sc, e < 0 ? 8191 : e, j, s) : 0ull;
+        sb[u] = idx < n ? __float_as_uint(sc) : 0u;
+        tb[u] = ((uint32_t)(e < 0 ? 8191 : e) << 19) | ((uint32_t)j << 5) | (uint32_t)s;
+        vmask |= idx < n ? (1u << u) : 0u;
+        if (idx < n) {
+            smax = max(smax, sb[u]);
+            smin = min(smin, sb[u]);
+        }
     }
-    // digit-by-digit search of the K-th largest key (K < n; K >= n keeps all)
-    if (tid == 0) {
-        s_pref = 0ull;
-        s_need = K;
-        s_done = K >= n || K <= 0;
-    }
-    __syncthreads();
-    for (int shift = 56; shift >= 0 && !s_done; shift -= 8) {  // uniform
-        const uint64_t pref = s_pref;
-        const int above = shift + 8;  // bits above the digit fixed by pref
+    const bool all = K >= n;
+    // First pass over 2048 bins linear in the score between the minimum and
+    // the maximum (monotone in the score, and spread where the bit patterns
+    // would crowd into a few exponents); then the exact select among the
+    // candidates of the threshold bin only.
+    int bin[kSelPer] = {0, 0, 0, 0, 0, 0, 0, 0};
+    int B = 0;                     // threshold bin: bins above are kept, below dropped
+    uint32_t T = 0, M = 0xFFFFFFFFu;  // inside bin B: score threshold, largest tie key kept
+    bool exact = true;
+    if (!all) {
+        uint32_t mx, mn;
+        block_max_min(smax, smin, rl, &mx, &mn);
+        const float fmn = __uint_as_float(mn), d = __uint_as_float(mx) - fmn;
+        float scl = d > 0.f ? (float)kRadixBins / d : 0.f;
+        if (!(scl < INFINITY)) scl = 0.f;  // a range too small (or infinite): one bin
+        for (int i = tid; i < kRadixBins; i += kSelThreads) rl.hist[i] = 0;
+        __syncthreads();
 #pragma unroll
         for (int u = 0; u < kSelPer; ++u) {
-            const bool match = kSelPer * tid + u < n && (above == 64 ? true : (key[u] >> above) == (pref >> above));
-            if (match) atomicAdd(&hist[(int)((key[u] >> shift) & 255u)], 1);
+            const float f = (__uint_as_float(sb[u]) - fmn) * scl;
+            bin[u] = f < (float)(kRadixBins - 1) ? (int)f : kRadixBins - 1;
+            if ((vmask >> u) & 1u) atomicAdd(&rl.hist[bin[u]], 1);
         }
         __syncthreads();
-        if (tid < MOE_WAVE) {  // the digit where the demand falls, from the top
-            const int lane = tid;
-            int cnt[4];
-            int sum = 0;
+        int ab, ct;
+        find_bin(kRadixBins, K, rl, &B, &ab, &ct);
+        const int need = K - ab;
+        if (need != ct) {
+            unsigned bmask = 0;
 #pragma unroll
-            for (int x = 0; x < 4; ++x) {
-                cnt[x] = hist[255 - (4 * lane + x)];  // bins in descending order
-                sum += cnt[x];
-            }
-            int incl = sum;  // inclusive prefix over lanes (descending bins)
+            for (int u = 0; u < kSelPer; ++u) bmask |= (((vmask >> u) & 1u) && bin[u] == B) ? (1u << u) : 0u;
+            T = radix_kth_largest(sb, bmask, need, rl, &exact);
+            if (!exact) {  // the scores equal to T: their ties in tie-key order
+                int gtc = 0;
+                unsigned eqmask = 0;
+                uint32_t ntb[kSelPer];
 #pragma unroll
-            for (int d = 1; d < MOE_WAVE; d <<= 1) {
-                const int y = __shfl_up(incl, d, MOE_WAVE);
-                if (lane >= d) incl += y;
-            }
-            const int need = s_need;
-            int before = incl - sum;
-            int found = -1, nb = 0, nc = 0;
-#pragma unroll
-            for (int x = 0; x < 4; ++x) {
-                if (found < 0 && before < need && need <= before + cnt[x]) {
-                    found = 255 - (4 * lane + x);
-                    nb = before;
-                    nc = cnt[x];
+                for (int u = 0; u < kSelPer; ++u) {
+                    gtc += ((bmask >> u) & 1u) && sb[u] > T ? 1 : 0;
+                    eqmask |= (((bmask >> u) & 1u) && sb[u] == T) ? (1u << u) : 0u;
+                    ntb[u] = ~tb[u];
                 }
-                before += cnt[x];
-            }
-            const uint64_t m = __ballot(found >= 0);
-            const int src = __builtin_ctzll(m);  // exactly one lane (need <= total)
-            const int dig = __shfl(found, src, MOE_WAVE);
-            const int nbv = __shfl(nb, src, MOE_WAVE);
-            const int ncv = __shfl(nc, src, MOE_WAVE);
-            if (lane == 0) {
-                s_pref = pref | ((uint64_t)dig << shift);
-                s_need = need - nbv;
-                if (need - nbv == ncv) s_done = 1;  // the whole bucket is kept
+                if (tid == 0) rl.cnt = 0;
+                __syncthreads();
+                if (gtc) atomicAdd(&rl.cnt, gtc);
+                __syncthreads();
+                const int need2 = need - rl.cnt;
+                __syncthreads();
+                bool w2;
+                M = ~radix_kth_largest(ntb, eqmask, need2, rl, &w2);  // the need2-th smallest tie key
             }
         }
-        __syncthreads();
-        if (tid < 256) hist[tid] = 0;
-        __syncthreads();
     }
-    // kept: keys at or above the threshold (the bucket prefix with zero low bits)
-    const uint64_t thr = s_pref;
-    const bool all = K >= n;
-    const bool none = K <= 0;
     unsigned kmask = 0;
 #pragma unroll
     for (int u = 0; u < kSelPer; ++u) {
-        const bool kept = kSelPer * tid + u < n && !none && (all || key[u] >= thr);
+        const bool kept = ((vmask >> u) & 1u) &&
+                          (all || bin[u] > B ||
+                           (bin[u] == B && (sb[u] > T || (sb[u] == T && (exact || tb[u] <= M)))));
         kmask |= kept ? (1u << u) : 0u;
     }
     // positions in candidate order: exclusive scan of the counts
@@ -388,7 +581,7 @@ reader_select_kernel(ReaderArgs ra, const int32_t* __restrict__ topk_ids, const 
         const int idx = kSelPer * tid + u;
         if (idx < n && fI.mod(idx) == 0) slot_off[fI.div(idx)] = pos + __builtin_popcount(kmask & ((1u << u) - 1u));
     }
-    if (tid == 0) slot_off[k] = all ? n : (none ? 0 : K);
+    if (tid == 0) slot_off[k] = all ? n : K;
     __syncthreads();
 #pragma unroll
     for (int u = 0; u < kSelPer; ++u) {
@@ -408,35 +601,53 @@ reader_select_kernel(ReaderArgs ra, const int32_t* __restrict__ topk_ids, const 
 
 // ---------------------------------------------------------------------------
 // Recovery partials.  Grid (channel chunks of 256, k, M): thread j of slot s
-// adds, for a dropped candidate, (w_s p_hat_j) b_j[r] for r < rank; the 256
-// threads are added by a fixed butterfly per wave, then the waves in order:
-// rpart[t][s][chunk][r].
+// adds, for a dropped candidate, (w_s p_hat_j) b_j[r] for r < rank, with
+// p_hat_j = SiLU(g_hat_j) v_hat_j from the screening's group partials added
+// as the selection adds them; the 256 threads are added by a fixed butterfly
+// per wave, then the waves in order: rpart[t][s][chunk][r].
 __global__ void __launch_bounds__(kThreads)
 reader_recover_kernel(ReaderArgs ra, const int32_t* __restrict__ topk_ids, const float* __restrict__ topk_w) {
     __shared__ float wpart[kWaves][kMaxRank];
     const int chunk = blockIdx.x, s = blockIdx.y, t = blockIdx.z;
     const int tid = threadIdx.x, lane = tid % MOE_WAVE, wave = tid / MOE_WAVE;
-    const int I = ra.I, k = ra.k, rank = ra.rank;
+    const int I = ra.I, k = ra.k, rank = ra.rank, nbq = ra.nbq;
     const int j = chunk * kThreads + tid;
     const int e = topk_ids[(size_t)t * k + s];
     const float a = topk_w[(size_t)t * k + s];
     const bool ev = e >= 0 && e < ra.E;
     const int jc = min(j, I - 1);
+    const float* eg = ra.est + (((size_t)t * k + s) * 2 * nbq) * I + jc;
+    float gp[kMaxGroups], vp[kMaxGroups];
+#pragma unroll
+    for (int q = 0; q < kMaxGroups; ++q) {
+        gp[q] = eg[(size_t)min(q, nbq - 1) * I];
+        vp[q] = eg[(size_t)(nbq + min(q, nbq - 1)) * I];
+    }
     const bool use = ev && j < I && !ra.kept_flag[((size_t)t * k + s) * I + jc];
-    const float coef = use ? a * ra.phat[((size_t)t * k + s) * I + jc] : 0.f;
     const uint16_t* brow = ra.rec_coef + ((size_t)(ev ? e : 0) * I + jc) * rank;
+    uint4 bw[kMaxRank / 8];
+#pragma unroll
+    for (int r8 = 0; r8 < kMaxRank / 8; ++r8)
+        bw[r8] = 8 * r8 < rank ? load16(brow + 8 * r8) : make_uint4(0u, 0u, 0u, 0u);
+    float g = gp[0], v = vp[0];
+#pragma unroll
+    for (int q = 1; q < kMaxGroups; ++q) {
+        g += q < nbq ? gp[q] : 0.f;
+        v += q < nbq ? vp[q] : 0.f;
+    }
+    const float coef = use ? a * silu_mul(g, v) : 0.f;
     float contrib[kMaxRank];
 #pragma unroll
     for (int r8 = 0; r8 < kMaxRank / 8; ++r8) {
         float f[8];
-        unpack8(8 * r8 < rank ? load16(brow + 8 * r8) : make_uint4(0u, 0u, 0u, 0u), f);
+        unpack8(bw[r8], f);
 #pragma unroll
         for (int x = 0; x < 8; ++x) contrib[8 * r8 + x] = use ? coef * f[x] : 0.f;
     }
 #pragma unroll
     for (int r = 0; r < kMaxRank; ++r) {
-        const float v = wave_sum(contrib[r]);
-        if (lane == 0) wpart[wave][r] = v;
+        const float v2 = wave_sum(contrib[r]);
+        if (lane == 0) wpart[wave][r] = v2;
     }
     __syncthreads();
     if (tid < rank)
@@ -444,12 +655,16 @@ reader_recover_kernel(ReaderArgs ra, const int32_t* __restrict__ topk_ids, const
             (wpart[0][tid] + wpart[1][tid]) + (wpart[2][tid] + wpart[3][tid]);
 }
 
-// y[t][col] = sum over the gather chunks of part[t][chunk][col] (as the
-// channel-sparse combine), then + sum_r U[col][r] R[r] with R[r] the sum of
-// the token's recovery partials in order.  One wave per workgroup.
+// y[t][col] = sum over the gather chunks of part[t][chunk][col] plus the
+// recovery map's sum_r U[col][r] R[r], R[r] = the token's nrp recovery
+// partials added in order.  One wave per workgroup, 16 columns: lane (row
+// group g, float4 column c4) adds chunks g, g + 16, ... in order and the
+// map's ranks 2g and 2g + 1; the 16 row groups are then combined by a
+// butterfly over the lane bits above the column bits (a fixed order).
 constexpr int kCombCG = 4;
 constexpr int kCombRG = MOE_WAVE / kCombCG;
 constexpr int kCombBatch = 8;
+constexpr int kRecBatch = 32;
 
 __global__ void __launch_bounds__(MOE_WAVE)
 reader_combine_kernel(int H, int nchunks, const float* __restrict__ part, const float* __restrict__ rpart, int nrp,
@@ -459,6 +674,26 @@ reader_combine_kernel(int H, int nchunks, const float* __restrict__ part, const 
     const int cg = lane % kCombCG;
     const int rg = lane / kCombCG;
     const int col = (blockIdx.x * kCombCG + cg) * 4;
+    const int r0 = 2 * rg;
+    const bool rin = r0 < rank;  // rank is even
+    const int rc = rin ? r0 : 0;
+    // the map's inputs first: this lane's two ranks of the partials and of U
+    float R0 = 0.f, R1 = 0.f;
+    const float* rp = rpart + (size_t)t * nrp * rank + rc;
+    for (int i0 = 0; i0 < nrp; i0 += kRecBatch) {
+        float2 v[kRecBatch];
+#pragma unroll
+        for (int u = 0; u < kRecBatch; ++u)
+            v[u] = *reinterpret_cast<const float2*>(rp + (size_t)min(i0 + u, nrp - 1) * rank);
+#pragma unroll
+        for (int u = 0; u < kRecBatch; ++u) {
+            R0 += i0 + u < nrp ? v[u].x : 0.f;
+            R1 += i0 + u < nrp ? v[u].y : 0.f;
+        }
+    }
+    float2 uu[4];
+#pragma unroll
+    for (int x = 0; x < 4; ++x) uu[x] = *reinterpret_cast<const float2*>(U + (size_t)min(col + x, H - 1) * rank + rc);
     float4 acc = make_float4(0.f, 0.f, 0.f, 0.f);
     const float* src = part + (size_t)t * nchunks * H + min(col, H - 4);
     for (int c0 = rg; c0 < nchunks; c0 += kCombBatch * kCombRG) {
@@ -475,6 +710,12 @@ reader_combine_kernel(int H, int nchunks, const float* __restrict__ part, const 
             acc.w += use ? v[u].w : 0.f;
         }
     }
+    if (rin) {
+        acc.x += uu[0].x * R0 + uu[0].y * R1;
+        acc.y += uu[1].x * R0 + uu[1].y * R1;
+        acc.z += uu[2].x * R0 + uu[2].y * R1;
+        acc.w += uu[3].x * R0 + uu[3].y * R1;
+    }
 #pragma unroll
     for (int m = kCombCG; m < MOE_WAVE; m <<= 1) {
         acc.x += __shfl_xor(acc.x, m, MOE_WAVE);
@@ -482,18 +723,7 @@ reader_combine_kernel(int H, int nchunks, const float* __restrict__ part, const 
         acc.z += __shfl_xor(acc.z, m, MOE_WAVE);
         acc.w += __shfl_xor(acc.w, m, MOE_WAVE);
     }
-    // R: lane r < rank adds the nrp partials of coordinate r in order
-    float R = 0.f;
-    for (int i = 0; i < nrp; ++i) R += lane < rank ? rpart[((size_t)t * nrp + i) * rank + min(lane, rank - 1)] : 0.f;
-    float rec[4] = {0.f, 0.f, 0.f, 0.f};
-    for (int r = 0; r < rank; ++r) {
-        const float Rr = __shfl(R, r, MOE_WAVE);
-#pragma unroll
-        for (int x = 0; x < 4; ++x) rec[x] = fmaf(U[(size_t)min(col + x, H - 1) * rank + r], Rr, rec[x]);
-    }
-    if (rg == 0 && col < H)
-        *reinterpret_cast<float4*>(y + (size_t)t * H + col) =
-            make_float4(acc.x + rec[0], acc.y + rec[1], acc.z + rec[2], acc.w + rec[3]);
+    if (rg == 0 && col < H) *reinterpret_cast<float4*>(y + (size_t)t * H + col) = acc;
 }
 
 // ---------------------------------------------------------------------------
@@ -852,12 +1082,21 @@ hipError_t launch_reader_rotate(const float* h, int M, int H, const int8_t* sign
     return hipGetLastError();
 }
 
+int reader_groups(int nblk, int* bpw) {
+    const int b = (nblk + kMaxGroups - 1) / kMaxGroups;
+    if (bpw) *bpw = b;
+    return (nblk + b - 1) / b;
+}
+
 hipError_t launch_reader_screen(const ReaderArgs& ra, const SelRoute* route, const int32_t* topk_ids, int M,
                                 hipStream_t stream) {
-    if (ra.nblk < 1 || ra.nblk > kRowGroups || ra.k < 1 || ra.k > 32 || ra.rowb != reader_row_bytes(ra.I) || M < 1)
+    int bpw = 0;
+    const int nbq = ra.nblk >= 1 ? reader_groups(ra.nblk, &bpw) : 0;
+    if (ra.nblk < 1 || ra.nblk > kRowGroups || ra.k < 1 || ra.k > 32 || ra.rowb != reader_row_bytes(ra.I) || M < 1 ||
+        ra.nbq != nbq || ra.bpw != bpw || bpw > kMaxBpw)
         return hipErrorInvalidValue;
     const int nseg = ra.rowb / 16;
-    const dim3 grid((2 * ra.k + 7) / 8 * 8 * nseg, M);
+    const dim3 grid((2 * ra.k + 7) / 8 * 8 * nseg * nbq, M);
     if (route) {
         if (ra.E > kThreads || route->M != M) return hipErrorInvalidValue;
         MOE_LAUNCH(reader_screen_kernel<true>, grid, dim3(kThreads), 0, stream, ra, *route, nullptr, nseg);
@@ -868,10 +1107,13 @@ hipError_t launch_reader_screen(const ReaderArgs& ra, const SelRoute* route, con
 }
 
 hipError_t launch_reader_select(const ReaderArgs& ra, const int32_t* topk_ids, const float* topk_w, int M, int K,
-                                int32_t* slot_cnt, int32_t* slot_kept, int32_t* kept_out, hipStream_t stream) {
-    if (ra.k * ra.I > kSelThreads * kSelPer || ra.k > 32 || ra.E > 8192 || ra.I > 16384) return hipErrorInvalidValue;
+                                int32_t* slot_cnt, int32_t* slot_kept, int32_t* kept_out, float* est_out,
+                                float* score_out, hipStream_t stream) {
+    if (ra.k * ra.I > kSelThreads * kSelPer || ra.k > 32 || ra.E > 8192 || ra.I > 16384 || ra.nbq < 1 ||
+        ra.nbq > kMaxGroups || K < 1)
+        return hipErrorInvalidValue;
     MOE_LAUNCH(reader_select_kernel, dim3(M), dim3(kSelThreads), 0, stream, ra, topk_ids, topk_w, K,
-               FastDiv((uint32_t)ra.I), slot_cnt, slot_kept, kept_out);
+               FastDiv((uint32_t)ra.I), slot_cnt, slot_kept, kept_out, est_out, score_out);
     return hipGetLastError();
 }
 

@@ -418,9 +418,8 @@ router_partials_kernel(const float* __restrict__ h, int M, int H, const uint16_t
         const int tt = job / nblk, b = job - tt * nblk;
         if (tt >= TT || t0 + tt >= M) return;  // whole waves; no barrier follows
         const size_t jb = (size_t)(t0 + tt) * nblk + b;
-        double* key = reinterpret_cast<double*>(red) + ((int)threadIdx.x / MOE_WAVE) * kReaderBlock;
         rotate_scan_wave(h + (size_t)(t0 + tt) * H + b * kReaderBlock, rot.signs + b * kReaderBlock,
-                         rot.xsel + jb * kReaderScan, rot.xval + jb * kReaderScan, key);
+                         rot.xsel + jb * kReaderScan, rot.xval + jb * kReaderScan);
         return;
     }
     if (M == 1)
@@ -502,8 +501,6 @@ hipError_t launch_router_partials(const float* h, int M, int H, const uint16_t* 
         if (H % kReaderBlock || !rot->signs || !rot->xsel || !rot->xval) return hipErrorInvalidValue;
         const int jobs = (M == 1 ? 1 : kTokTile) * (H / kReaderBlock);
         grid += (jobs + kThreads / MOE_WAVE - 1) / (kThreads / MOE_WAVE);
-        const size_t kl = (size_t)kThreads / MOE_WAVE * kReaderBlock * sizeof(double);
-        lds = lds > kl ? lds : kl;
         rj = *rot;
     }
     MOE_LAUNCH(router_partials_kernel, dim3(grid, router_groups(M)), dim3(kThreads), lds, stream, h, M, H, Wr, E,

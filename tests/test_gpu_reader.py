@@ -7,7 +7,8 @@ Comparison rules
     values: bit-exact (both sides take the same fp64 operations in the same
     order, then round once);
   * estimates g_hat, v_hat: within the rigorous fp32 bound of their sums
-    (summation depth <= 80 rows + 64 row groups + 1 scale product);
+    (summation depth <= 80 rows + 64 row groups + 1 scale product + 2 block
+    groups);
   * kept list: bit-exact against the oracle's selection applied to the GPU's
     own fp32 scores (the decision taken in the kernel's precision); against
     the oracle's fp64 scores, every difference must lie within the scores'
@@ -109,8 +110,8 @@ def inspect(mb, layer, cfg, h_np, ids_np, w_np, K):
 
 def est_bound(codes_scale, xr, mask, ids_t, I):
     """Rigorous bound on |fp32 estimate - exact| per (slot, P, channel):
-    gamma_145 * sum over blocks of |scale| * sum over scanned |x''|."""
-    n = 80 + 64 + 1
+    gamma_147 * sum over blocks of |scale| * sum over scanned |x''|."""
+    n = 80 + 64 + 1 + 2
     gam = n * U32 / (1 - n * U32)
     ax = np.where(mask, np.abs(xr), 0.0).sum(axis=1)   # [nb]
     out = np.zeros((len(ids_t), 2, I))
