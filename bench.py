@@ -224,10 +224,8 @@ def build_layers(wl, n_layers, M, keep=0):
             reader_tables(mb, cfg, t, synth.rotation_signs(wl, L))
         elif keep:
             norms = torch.empty((wl.E, wl.I), dtype=torch.float32, device="cuda")
-            ranks = torch.empty((wl.E, wl.I), dtype=torch.int32, device="cuda")
             mb.moe_channel_norms(cfg, t["w_gate"], t["w_up"], t["w_down"], norms)
-            mb.moe_channel_ranks(cfg, norms, ranks)
-            t["chan_norm"], t["chan_rank"] = norms, ranks
+            t["chan_norm"] = norms
         layers.append(mb.Layer(cfg, t))
     torch.cuda.synchronize()
     return layers

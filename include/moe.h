@@ -119,12 +119,6 @@ typedef struct {
  *               Stage 2)                        required
  *  chan_norm    fp32 [E][I], static channel scores n[e][j] for the
  *               channel-sparse mode (see moe_channel_norms); or NULL
- *  chan_rank    int32 [E][I], each channel's position in its expert's
- *               channels ordered by decreasing chan_norm, ties to the lower
- *               channel (see moe_channel_ranks); required with chan_norm in
- *               the channel-sparse mode, else may be NULL.  It only speeds up
- *               the selection: ranks that do not match the norms (or
- *               affinities that are not positive) still give the exact top K.
  *  For MOE_WFORMAT_VQLR, index [0] is the gate projection and [1] the up
  *  projection (page "A Multi-Engine Dataflow ...", Sec. 3.1 Eq. 1 and Sec. 2.3):
  *  lr_basis[P]  bf16 [H][lr_r]   shared basis D_P
@@ -149,8 +143,8 @@ typedef struct {
  *  rec_basis    fp32 [H][rec_rank] (moe_recovery_basis), with rec_rank > 0
  *  rec_coef     bf16 [E][I][rec_rank] (moe_recovery_coefs), with rec_rank > 0
  *  Alignment (checked by moe_create, MOE_ERR_INVALID_ARG otherwise): the bf16
- *  arrays, vq_idx, sketch and down_norm 16 bytes, the other fp32 / int32
- *  arrays 4 bytes.
+ *  arrays, vq_idx, sketch, chan_norm and down_norm 16 bytes, the other
+ *  fp32 / int32 arrays 4 bytes.
  */
 typedef struct {
     const uint16_t *router_w;
@@ -159,7 +153,6 @@ typedef struct {
     const uint16_t *w_up;
     const uint16_t *w_down;
     const float *chan_norm;
-    const int32_t *chan_rank;
     const uint16_t *lr_basis[2];
     const uint16_t *lr_coef[2];
     const uint16_t *vq_book[2];
@@ -246,11 +239,12 @@ moe_status moe_route_align(moe_ctx *ctx, const float *h, int32_t M, int32_t *top
  * bitwise the same y.  A plan that omits a valid route leaves that route's
  * contribution undefined.
  *
- * Channel-sparse mode (keep_channels = K > 0; needs chan_norm and chan_rank, dense format):
+ * Channel-sparse mode (keep_channels = K > 0; needs chan_norm, dense format):
  * page "Channel Selection for Mixture-of-Experts Decoding Needs No
  * Calibration Data", Background and Stage 2.  Per token, candidate (s, j)
  * scores a_s * n[e_s][j] (exact fp64 product of two fp32 values); the K best
- * across all k experts are kept (ties: lower expert id, then lower channel);
+ * across all k experts are kept (ties: lower expert id, then lower channel,
+ * then lower slot), exactly, by one workgroup per token;
  * only the kept gate rows, up rows and down rows are read, and
  *     y[t] = sum over kept (s, j) of a_s * SiLU(g_j.h_t)(v_j.h_t) * d_j.
  * The plan arguments are ignored (may be NULL).  kept_out (int32 [M][K], may
@@ -294,8 +288,8 @@ moe_status moe_expert_forward(moe_ctx *ctx, const float *h, int32_t M,
  * takes the top-k and softmax and finds its own expert (one block per
  * selected expert); the combine adds the partials.  In channel-sparse mode
  * (keep_channels > 0) the router GEMV writes the partials of all M tokens
- * and each workgroup of the channel selection (one per token) takes its
- * token's top-k and softmax before selecting.  In reader mode the router
+ * and each workgroup of the selection-and-gather launch takes its token's
+ * top-k and softmax before selecting.  In reader mode the router
  * GEMV launch also rotates and scans h in workgroups of its own, and every
  * screening workgroup routes its token before reading the sketch (E <= 256;
  * above, the routing is moe_route_topk's and the rotation a launch of its
@@ -380,20 +374,6 @@ moe_status moe_read_device_error(moe_ctx *ctx, int32_t *flags, int32_t clear);
 moe_status moe_channel_norms(const moe_config *cfg, const uint16_t *w_gate, const uint16_t *w_up,
                              const uint16_t *w_down, float *norms, void *stream);
 
-/*
- * Load-time list positions for the channel-sparse selection:
- *     ranks[e][j] = #{ j2 : norms[e][j2] > norms[e][j]
- *                          or (norms[e][j2] == norms[e][j] and j2 < j) }
- * (values compared in float order, -0 equal to +0), i.e. channel j's position
- * when expert e's channels are ordered by decreasing norm.  With positive
- * affinities the top K of the affinity-weighted scores
- * (page "Channel Selection for Mixture-of-Experts Decoding Needs No
- * Calibration Data", Stage 2) is then a prefix of each routed expert's
- * order, which the selection searches instead of sorting.  Inputs fp32
- * [E][I] (device), output int32 [E][I] (device).  Needs only cfg->I
- * (1..8192) and cfg->E.  Asynchronous on `stream`.
- */
-moe_status moe_channel_ranks(const moe_config *cfg, const float *norms, int32_t *ranks, void *stream);
 
 /*
  * Load-time arrays of the reader (page "Channel Selection for
@@ -468,8 +448,8 @@ enum {
     MOE_KERNEL_GATEUP_VQLR = 4,   /* VQ + low-rank gate/up + SiLU */
     MOE_KERNEL_DOWN = 5,          /* down GEMV partials */
     MOE_KERNEL_COMBINE = 6,       /* fixed-order weighted combine */
-    MOE_KERNEL_CHAN_SELECT = 7,   /* channel top-K */
-    MOE_KERNEL_CHAN_GATHER = 8,   /* kept-channel gate/up + down partials */
+    MOE_KERNEL_CHAN_SELECT = 7,   /* (no longer launched: the top-K runs inside CHAN_GATHER) */
+    MOE_KERNEL_CHAN_GATHER = 8,   /* channel top-K + kept-channel gate/up + down partials */
     MOE_KERNEL_CHAN_COMBINE = 9,
     MOE_KERNEL_EXPERT_FUSED = 10, /* dense gate/up + SiLU + down partials (one route per block) */
     MOE_KERNEL_ROUTER_ALIGN = 11, /* router + top-k + softmax + alignment (one launch) */
@@ -478,7 +458,8 @@ enum {
     MOE_KERNEL_VQ_FINISH = 14,    /* VQ + low rank: slice partials -> SiLU(gate) * up */
     MOE_KERNEL_READER_ROTATE = 15,  /* reader: rotation and scan of h (own launch) */
     MOE_KERNEL_READER_SCREEN = 16,  /* reader: sketch estimates (routing first in the decode step) */
-    MOE_KERNEL_READER_SELECT = 17,  /* reader: output-level scores, exact top K */
+    MOE_KERNEL_READER_SELECT = 17,  /* reader: output-level scores and top K of moe_reader_inspect (the
+                                       forward path selects inside CHAN_GATHER) */
     MOE_KERNEL_READER_RECOVER = 18, /* reader: recovery partials of the dropped channels */
     MOE_KERNEL_READER_COMBINE = 19, /* reader: combine + recovery map */
     MOE_KERNEL_COUNT = 20

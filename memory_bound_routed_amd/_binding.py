@@ -31,7 +31,7 @@ MOE_KERNEL_COUNT = len(KERNELS)
 # Every symbol include/moe.h declares (checked by the CPU test suite).
 EXPORTS = ["moe_create", "moe_destroy", "moe_route_topk", "moe_route_align", "moe_align_blocks", "moe_expert_forward",
            "moe_decode_step", "moe_decode_step_noalloc",
-           "moe_align_capacity", "moe_workspace_bytes", "moe_status_string", "moe_read_device_error", "moe_channel_norms", "moe_channel_ranks",
+           "moe_align_capacity", "moe_workspace_bytes", "moe_status_string", "moe_read_device_error", "moe_channel_norms",
            "moe_validate_plan", "moe_profile_enable", "moe_profile_read", "moe_kernel_name", "moe_reader_inspect",
            "moe_sketch_row_bytes", "moe_reader_sketch", "moe_down_norms", "moe_recovery_basis", "moe_recovery_coefs"]
 
@@ -47,7 +47,7 @@ _vp = ctypes.c_void_p
 
 class moe_weights(ctypes.Structure):
     _fields_ = [("router_w", _vp), ("router_bias", _vp), ("w_gate", _vp), ("w_up", _vp), ("w_down", _vp),
-                ("chan_norm", _vp), ("chan_rank", _vp), ("lr_basis", _vp * 2), ("lr_coef", _vp * 2), ("vq_book", _vp * 2),
+                ("chan_norm", _vp), ("lr_basis", _vp * 2), ("lr_coef", _vp * 2), ("vq_book", _vp * 2),
                 ("vq_idx", _vp * 2), ("rot_signs", _vp), ("sketch", _vp), ("sketch_scale", _vp), ("down_norm", _vp),
                 ("rec_basis", _vp), ("rec_coef", _vp)]
 
@@ -68,7 +68,6 @@ _sig = {
     "moe_status_string": (ctypes.c_char_p, [_i32]),
     "moe_read_device_error": (_i32, [_vp, _pi32, _i32]),
     "moe_channel_norms": (_i32, [ctypes.POINTER(moe_config), _vp, _vp, _vp, _vp, _vp]),
-    "moe_channel_ranks": (_i32, [ctypes.POINTER(moe_config), _vp, _vp, _vp]),
     "moe_validate_plan": (_i32, [_vp, _i32, _i32, _i32, _i32, _vp, _vp, _vp, _pi32]),
     "moe_profile_enable": (_i32, [_vp, _i32]),
     "moe_profile_read": (_i32, [_vp, ctypes.POINTER(ctypes.c_double), ctypes.POINTER(ctypes.c_int64)]),
@@ -141,14 +140,13 @@ def make_config(H, I, E, top_k, block_b=8, max_tokens=1, wformat=MOE_WFORMAT_DEN
     return moe_config(H, I, E, top_k, block_b, max_tokens, wformat, vq_d, vq_K, lr_r, max_keep, reader, rec_rank)
 
 
-def make_weights(router_w, w_down, router_bias=None, w_gate=None, w_up=None, chan_norm=None, chan_rank=None,
+def make_weights(router_w, w_down, router_bias=None, w_gate=None, w_up=None, chan_norm=None,
                  lr_basis=(None, None), lr_coef=(None, None), vq_book=(None, None),
                  vq_idx=(None, None), rot_signs=None, sketch=None, sketch_scale=None, down_norm=None,
                  rec_basis=None, rec_coef=None) -> moe_weights:
     w = moe_weights()
-    w.router_w, w.router_bias, w.w_gate, w.w_up, w.w_down, w.chan_norm, w.chan_rank = (
-        _ptr(router_w), _ptr(router_bias), _ptr(w_gate), _ptr(w_up), _ptr(w_down), _ptr(chan_norm),
-        _ptr(chan_rank))
+    w.router_w, w.router_bias, w.w_gate, w.w_up, w.w_down, w.chan_norm = (
+        _ptr(router_w), _ptr(router_bias), _ptr(w_gate), _ptr(w_up), _ptr(w_down), _ptr(chan_norm))
     for P in range(2):
         w.lr_basis[P], w.lr_coef[P] = _ptr(lr_basis[P]), _ptr(lr_coef[P])
         w.vq_book[P], w.vq_idx[P] = _ptr(vq_book[P]), _ptr(vq_idx[P])
@@ -235,10 +233,6 @@ def moe_channel_norms(cfg: moe_config, w_gate, w_up, w_down, norms, stream=None)
                                   _stream(stream)), "moe_channel_norms")
 
 
-def moe_channel_ranks(cfg: moe_config, norms, ranks, stream=None) -> None:
-    _check(_lib.moe_channel_ranks(ctypes.byref(cfg), _ptr(norms), _ptr(ranks), _stream(stream)), "moe_channel_ranks")
-
-
 def moe_reader_inspect(ctx, h, M, topk_ids, topk_w, K, xsel=None, xval=None, est=None, score=None, kept=None,
                        stream=None) -> None:
     _check(_lib.moe_reader_inspect(ctx, _ptr(h), M, _ptr(topk_ids), _ptr(topk_w), K, _ptr(xsel), _ptr(xval),
@@ -304,7 +298,7 @@ class Layer:
         t = tensors
         self.weights = make_weights(
             t["router_w"], t["w_down"], router_bias=t.get("router_bias"), w_gate=t.get("w_gate"),
-            w_up=t.get("w_up"), chan_norm=t.get("chan_norm"), chan_rank=t.get("chan_rank"),
+            w_up=t.get("w_up"), chan_norm=t.get("chan_norm"),
             lr_basis=(t.get("lr_basis_gate"), t.get("lr_basis_up")),
             lr_coef=(t.get("lr_coef_gate"), t.get("lr_coef_up")),
             vq_book=(t.get("vq_book_gate"), t.get("vq_book_up")),

@@ -5,17 +5,17 @@
 // d_j is contiguous).
 //
 // The score of candidate (slot s, channel j) is a_s * n[e_s][j]: the exact
-// fp64 product of two fp32 values, so selection needs no rounding decision.
-// With positive affinities the K best form a prefix of each routed expert's
-// channels ordered by decreasing norm (an order computed once per layer), so
-// each (slot, token) workgroup finds its own prefix length by binary searches
-// over the k orders instead of sorting; ties go to the lower expert id, then
-// channel, then slot.
+// fp64 product of two fp32 values, so selection needs no rounding decision;
+// one workgroup per token takes the K best exactly (select_device.h), ties to
+// the lower expert id, then channel, then slot.  The gather computes the kept
+// channels exactly and writes chunk partials that the combine adds in order.
 #include <algorithm>
 #include <climits>
 
 #include "device_common.h"
 #include "launch.h"
+#include "reader_device.h"
+#include "select_device.h"
 #include "topk_device.h"
 
 namespace moe {
@@ -31,489 +31,329 @@ __device__ __forceinline__ unsigned long long score_key(double x) {
     return (u >> 63) ? ~u : (u | 0x8000000000000000ull);
 }
 
-// Exclusive scan of one int per thread over a workgroup of NT threads;
-// returns the exclusive prefix and writes the total to *total.
-template <int NT>
-__device__ __forceinline__ int block_exclusive_scan(int v, int* wsum, int* total) {
-    constexpr int NWV = NT / MOE_WAVE;
-    const int lane = threadIdx.x % MOE_WAVE;
-    const int wave = threadIdx.x / MOE_WAVE;
-    int x = v;
-#pragma unroll
-    for (int d = 1; d < MOE_WAVE; d <<= 1) {
-        const int y = __shfl_up(x, d, MOE_WAVE);
-        if (lane >= d) x += y;
-    }
-    if (lane == MOE_WAVE - 1) wsum[wave] = x;
-    __syncthreads();
-    int base = 0, all = 0;
-#pragma unroll
-    for (int w = 0; w < NWV; ++w) {
-        const int c = wsum[w];
-        base += w < wave ? c : 0;
-        all += c;
-    }
-    __syncthreads();
-    *total = all;
-    return base + x - v;
-}
+// Selection and gather in one launch.  Grid (ceil(K / 8) chunks, M tokens),
+// 1024 threads.  Every workgroup of a token takes the token's K best
+// candidates (slot s, channel j) exactly -- the same arithmetic in each, so
+// the same set -- then computes the kept candidates at positions 8 c ..
+// 8 c + 7 of the candidate order (s * I + j ascending):
+//   part[t][c][col] = sum over those (s, j), in position order, of
+//                     (a_s * SiLU(g_j . h_t) * (v_j . h_t)) * d_j[col].
+// The selection's latency is paid once per workgroup, in parallel, instead of
+// in a launch of its own followed by list reads.
+//
+// MODE 0: candidate (s, j) scores a_s * n[e_s][j], the exact fp64 product of
+// two fp32 values; ranked by that score (descending), then expert id,
+// channel and slot (ascending); a slot whose expert id is invalid contributes
+// candidates below every valid one, in channel order.  select_top takes the
+// K best by bins linear in the score (as fp32) between the token's minimum
+// and maximum -- invalid slots in a bin of their own below them -- and,
+// inside the threshold bin, the 64-bit order key of the fp64 score (high and
+// low words) and the complement of the tie key e << 19 | j << 5 | s.
+// ROUTE (MODE 0): each workgroup first routes its token from the router's
+// slice partials -- the logits added in slice order (+ bias), the top-k (one
+// wave from the keys above a threshold, else every key counted) and the
+// renormalised softmax, with the router's arithmetic; workgroup 0 writes the
+// ids and affinities (and logits) as the router would.
+// MODE 1: the reader's scores (reader_scores: the sketch estimates and
+// (w_s ||d_j||) |SiLU(g_hat) v_hat|), bins linear in the score, then the
+// score bits and the tie key.
+//
+// Gather: wave w computes projection w % 2 (gate, up) of the chunk's kept
+// channel w / 2 -- lane l over hidden columns 8 (l + 64 q), h staged in LDS,
+// the lanes added by wave_sum; threads 0..255 then add the 8 down rows
+// scaled by a_s * SiLU(g) * u, in position order, at columns 8 (tid + 256 cq).
+// Workgroup (0, t) also writes the kept flags (kept_flag[t][s][j], when
+// asked) and every workgroup its positions of kept_out.
+constexpr int kGatherKC = 8;  // kept channels per workgroup (two waves each)
 
-// Order-preserving map of a float to uint32 (larger value -> larger key;
-// -0 and +0 share a key).
-__device__ __forceinline__ uint32_t float_key(float x) {
-    const uint32_t u = __float_as_uint(x + 0.0f);
-    return (u >> 31) ? ~u : (u | 0x80000000u);
-}
-
-// Channel top-K of one token by search over k sorted lists.
-//
-// Candidate (s, j) is ranked by its score (descending), then expert id,
-// channel and slot (ascending): a strict total order.  List s holds
-// slot s's I candidates in decreasing key order; the kept candidates of a
-// slot are then a prefix of its list, and only the k prefix lengths c_s
-// (summing to K) have to be found.
-//
-// Lists.  The load-time ranks (moe_channel_ranks: each channel's position
-// when its expert's channels are ordered by decreasing norm, ties to the
-// lower channel) place every channel in its list with one scatter through
-// LDS.  For a_s > 0 and finite norms that is the list's key order, since the
-// product of two fp32 values is exact in fp64 and therefore strictly
-// increasing in n.  Every list is checked (a permutation, strictly
-// decreasing keys); a list that fails -- a_s = 0 or negative, non-finite
-// norms, ranks that do not belong to these norms -- is sorted in LDS by rank
-// counting instead, so the result is always the exact top K.  A slot whose
-// expert id is invalid contributes candidates of key 0 in channel order,
-// after every valid expert's.
-//
-// Search.  The global rank of list entry (s, r) is r plus, for every other
-// list t, the number of t's entries ranked above it (a binary search).  One
-// workgroup per (slot s0, token) finds c_s0 alone: a window bracketing it
-// starts at [0, I]; each round evaluates the ranks of P evenly spread
-// positions of the window (P * k binary searches, one per thread) and
-// narrows it to the step where the rank crosses K.  At k = 8, I = 768: P =
-// 128, two rounds.  The k workgroups of a token build the same lists, so
-// their prefix lengths add up to exactly K without any exchange.
-//
-// Output: per (token, slot) the kept channels in ascending order,
-// slot_kept[t][s][0 .. c_s), and slot_cnt[t][s] = c_s.  The gather turns the
-// counts into offsets; in candidate order (s * I + j ascending) the kept set
-// is the concatenation of the slots' lists.
-//
-// LDS (dynamic, n = k * I): the 64-bit score key of each list position
-// [n] (computed once; reused for the kept flags), the channel of each list
-// position uint16 [n].
-constexpr int kSelThreads = 1024;
-constexpr int kSelPer = 8;  // candidates per thread (n <= 8192)
-constexpr uint16_t kNoChannel = 0xFFFF;
-
-// ROUTE: the workgroup first routes its token from the router's slice
-// partials -- the logits added in slice order (+ bias), the top-k (one wave
-// from the keys above a threshold, else every key counted) and the
-// renormalised softmax, with the router's arithmetic -- and writes the ids
-// and affinities (and logits) as the router would.
-// Pivots per round (one binary search per thread and list), and the
-// divisors of the search (multiply-high division: a divide by a variable
-// costs tens of instructions otherwise).
-struct SelSearch {
-    int P;
-    FastDiv fk, fP1;  // by k, P + 1
+struct SparseArgs {
+    int32_t* topk_ids;        // [M][k] in (out with ROUTE)
+    float* topk_w;            // [M][k] in (out with ROUTE)
+    const float* norms;       // MODE 0: fp32 [E][I]
+    ReaderArgs ra;            // MODE 1
+    SelRoute route;           // ROUTE
+    int k, I, E, H, K;
+    const float* h;
+    const uint16_t* Wg;
+    const uint16_t* Wu;
+    const uint16_t* Wd;
+    float* part;              // fp32 [M][nchunks][H]
+    int32_t* kept_out;        // int32 [M][K] or null
+    uint8_t* kept_flag;       // u8 [M][k][I] or null
 };
-SelSearch sel_search(int k) {
-    SelSearch q;
-    q.P = std::max(1, kSelThreads / k);  // k <= 32: P * k <= kSelThreads
-    q.fk = FastDiv((uint32_t)k);
-    q.fP1 = FastDiv((uint32_t)(q.P + 1));
-    return q;
-}
 
-template <bool ROUTE>
+template <int MODE, bool ROUTE, int Q, int CQ>
 __global__ void __launch_bounds__(kSelThreads)
-chan_select_kernel(const int32_t* __restrict__ topk_ids, const float* __restrict__ topk_w,
-                   const float* __restrict__ norms, const int32_t* __restrict__ ranks, int k, int I, int E, int K,
-                   FastDiv fI, SelSearch srch_div, int32_t* __restrict__ slot_cnt, int32_t* __restrict__ slot_kept,
-                   SelRoute route) {
-    extern __shared__ __align__(16) unsigned char lds[];
-    const int n = k * I;
-    unsigned long long* keys = reinterpret_cast<unsigned long long*>(lds);  // [k][I] key at list position
-    uint16_t* jsrt = reinterpret_cast<uint16_t*>(lds + 8 * (size_t)n);     // [k][I] channel at list position
-    unsigned char* flag = lds;  // [I] kept channels of the own list (over the keys, after the search)
-    __shared__ double sa[32];
+chan_topk_gather_kernel(SparseArgs A, FastDiv fI) {
+    constexpr int KC = kGatherKC;
     __shared__ int se[32];
-    __shared__ int seo[32];  // tie order of slot s: its expert id, invalid last
-    __shared__ unsigned s_bad;  // bit s: list s fails the order check
-    __shared__ int pcnt[2][kSelThreads];  // per round (alternating), per (pivot, list): entries ranked above
-    __shared__ int wsum[kSelThreads / MOE_WAVE];
-    const int s0 = blockIdx.x;  // own slot
-    const int t = blockIdx.y;
-    const int tid = threadIdx.x;
-    if (tid == 0) s_bad = 0u;
-
-    if constexpr (ROUTE) {
-        __shared__ uint64_t skey[kSelThreads];
-        __shared__ int sel_e[32];
-        __shared__ float sel_l[32];
-        __shared__ uint64_t wk[MOE_WAVE];
-        __shared__ int wi[MOE_WAVE];
-        __shared__ int s_slow;
-        float lg = 0.f;
-        if (tid < E) {
-            const float bv = route.bias ? route.bias[tid] : 0.f;
-            for (int sl0 = 0; sl0 < route.nslices; sl0 += 8) {  // eight slices in flight
-                float x[8];
-#pragma unroll
-                for (int u = 0; u < 8; ++u)
-                    x[u] = route.part[((size_t)min(sl0 + u, route.nslices - 1) * route.M + t) * E + tid];
-#pragma unroll
-                for (int u = 0; u < 8; ++u) lg += sl0 + u < route.nslices ? x[u] : 0.f;  // slice order
-            }
-            if (route.bias) lg += bv;
-            if (route.logits && s0 == 0) route.logits[(size_t)t * E + tid] = lg;
-            skey[tid] = order_key((lg != lg) ? -INFINITY : lg, tid);  // NaN ranks as -inf
-        }
-        if (tid == 0) s_slow = E > 4 * MOE_WAVE;
-        __syncthreads();
-        if (tid < MOE_WAVE && E <= 4 * MOE_WAVE && !wave_topk<4>(skey, E, k, sel_e, sel_l, wk, wi)) s_slow = 1;
-        __syncthreads();
-        if (s_slow) {  // every key counted (E <= 1024 threads)
-            if (tid < E) {
-                const int rank = count_greater(skey, 0, E, skey[tid]);
-                if (rank < k) {
-                    sel_e[rank] = tid;
-                    sel_l[rank] = key_logit(skey[tid]);
-                }
-            }
-            __syncthreads();
-        }
-        if (tid < MOE_WAVE) {  // lane s: slot s
-            const float w = topk_softmax(sel_l[min(tid, k - 1)], tid, k);
-            if (tid < k) {
-                if (s0 == 0) {
-                    route.ids[(size_t)t * k + tid] = sel_e[tid];
-                    route.wts[(size_t)t * k + tid] = w;
-                }
-                se[tid] = sel_e[tid];
-                sa[tid] = (double)w;
-            }
-        }
-    } else {
-        if (tid < k) {
-            const int e = topk_ids[(size_t)t * k + tid];
-            se[tid] = (e >= 0 && e < E) ? e : -1;
-            sa[tid] = (double)topk_w[(size_t)t * k + tid];
-        }
-    }
-    for (int i = tid; i < n; i += kSelThreads) jsrt[i] = kNoChannel;
-    __syncthreads();
-    if (tid < k) seo[tid] = se[tid] < 0 ? INT_MAX : se[tid];
-    // Score key of slot s's channel with norm x (-0 ranks as +0; an invalid
-    // slot's candidates all have key 0).
-    auto cand_key = [&](int s, float x) -> unsigned long long {
-        return se[s] < 0 ? 0ull : score_key(sa[s] * (double)x + 0.0);
-    };
-    // Norm and list position of each candidate idx = s * I + j, thread tid
-    // owning idx = tid + kSelThreads * u (coalesced loads, issued together);
-    // the list position of an invalid slot's candidate is its channel.
-    float nv[kSelPer];
-    int rv[kSelPer];
-#pragma unroll
-    for (int u = 0; u < kSelPer; ++u) {
-        const int idx = min(tid + kSelThreads * u, n - 1);
-        const int sl = fI.div(idx), j = idx - sl * I;
-        const int e = se[sl];
-        const size_t g = (size_t)(e < 0 ? 0 : e) * I + j;
-        nv[u] = norms[g];
-        rv[u] = ranks[g];
-    }
-    unsigned bad = 0u;
-#pragma unroll
-    for (int u = 0; u < kSelPer; ++u) {
-        const int idx = tid + kSelThreads * u;
-        if (idx >= n) break;
-        const int sl = fI.div(idx), j = idx - sl * I;
-        const int r = se[sl] < 0 ? j : rv[u];
-        if (r < 0 || r >= I) {
-            bad |= 1u << sl;
-            continue;
-        }
-        keys[sl * I + r] = cand_key(sl, nv[u]);
-        jsrt[sl * I + r] = (uint16_t)j;
-    }
-    __syncthreads();
-    // Every list position filled and keys strictly decreasing (ties: channel ascending).
-#pragma unroll
-    for (int u = 0; u < kSelPer; ++u) {
-        const int p = tid + kSelThreads * u;
-        if (p >= n) break;
-        const int s = fI.div(p), r = p - s * I;
-        const int jr = jsrt[p];
-        bool ok = jr != kNoChannel;
-        if (ok && r + 1 < I) {
-            const int jn = jsrt[p + 1];
-            const unsigned long long kc = keys[p], kn = keys[p + 1];
-            ok = jn == kNoChannel || kc > kn || (kc == kn && jr < jn);  // an empty next slot fails on its own
-        }
-        if (!ok) bad |= 1u << s;
-    }
-    if (bad) atomicOr(&s_bad, bad);
-    __syncthreads();
-    // Lists that fail: channel order first, then each channel moved to its
-    // rank under the run-time key (counted over the whole list).
-    for (unsigned todo = s_bad; todo; todo &= todo - 1) {  // uniform
-        const int s = __builtin_ctz(todo);
-        const int e = se[s];  // an invalid slot's list is always in order; guarded anyway
-        const int nj = (I + kSelThreads - 1) / kSelThreads;
-        for (int j = tid; j < I; j += kSelThreads) {
-            keys[s * I + j] = cand_key(s, e < 0 ? 0.f : norms[(size_t)e * I + j]);
-            jsrt[s * I + j] = (uint16_t)j;
-        }
-        __syncthreads();
-        int rr[kSelPer];
-        unsigned long long kk[kSelPer];
-        for (int q = 0; q < nj; ++q) {
-            const int j = tid + kSelThreads * q;
-            if (j >= I) break;
-            const unsigned long long x = keys[s * I + j];
-            int c = 0;
-            for (int j2 = 0; j2 < I; ++j2) {
-                const unsigned long long y = keys[s * I + j2];
-                c += (y > x || (y == x && j2 < j)) ? 1 : 0;
-            }
-            rr[q] = c;
-            kk[q] = x;
-        }
-        __syncthreads();
-        for (int q = 0; q < nj; ++q) {
-            const int j = tid + kSelThreads * q;
-            if (j >= I) break;
-            keys[s * I + rr[q]] = kk[q];
-            jsrt[s * I + rr[q]] = (uint16_t)j;
-        }
-        __syncthreads();
-    }
-
-    // Own list s0: a window [lo, hi] around c_s0, narrowed by rounds of P
-    // pivots (P * k binary searches, one per thread: pivot p = tid / k,
-    // list tl = tid % k).  The pivots' ranks increase with their positions,
-    // so the pivots kept form a prefix whose length one block-wide count
-    // gives.  A pivot's count in list tl lies between the counts of the two
-    // pivots of the previous round that bracket the window, [clo, chi], so
-    // later searches only cover that range.
-    const int P = srch_div.P;
-    const FastDiv fk = srch_div.fk, fP1 = srch_div.fP1;
-    const int p = fk.div(tid);
-    const int tl = tid - p * k;
-    const bool act = tid < P * k;
-    // ranks summed over the k lanes of a pivot by shuffles when k is a power
-    // of two (the lanes are consecutive inside one wave), else through LDS
-    const bool pow2 = (k & (k - 1)) == 0;
-    int lo = 0, hi = I, clo = 0, chi = I;
-    for (int round = 0;; ++round) {
-        int* pc = pcnt[round & 1];
-        const int r = lo + fP1.div((p + 1) * (hi - lo));  // in [lo, hi) when act; (p + 1) * (hi - lo) < 2^24
-        const int rc = min(r, I - 1);
-        const unsigned long long kc = keys[s0 * I + rc];
-        const int jc = jsrt[s0 * I + rc], ec = seo[s0];
-        const bool srch = act && tl != s0;
-        int cnt = (act && tl == s0) ? r : clo;  // own list: the entries before r
-        int span = chi - clo;
-        int step = 1;
-        while (step * 2 <= span) step *= 2;
-        // entries of list tl ranked above the candidate (a prefix of the list)
-        for (; step > 0; step >>= 1) {
-            const int np = cnt + step;
-            if (srch && np <= chi) {
-                const unsigned long long y = keys[tl * I + np - 1];
-                bool above = y > kc;
-                if (y == kc) {  // equal scores: expert, channel, slot
-                    const int jy = jsrt[tl * I + np - 1], ey = seo[tl];
-                    above = ey < ec || (ey == ec && (jy < jc || (jy == jc && tl < s0)));
-                }
-                if (above) cnt = np;
-            }
-        }
-        if (act) pc[tid] = cnt;
-        bool kept_pivot = false;
-        if (pow2) {
-            int rank = act ? cnt : 0;
-            for (int m = 1; m < k; m <<= 1) rank += __shfl_xor(rank, m, MOE_WAVE);
-            kept_pivot = act && tl == 0 && rank < K;
-        } else {
-            __syncthreads();
-            if (tid < P) {
-                int rank = 0;
-                for (int x = 0; x < k; ++x) rank += pc[tid * k + x];
-                kept_pivot = rank < K;
-            }
-        }
-        const int c = __syncthreads_count(kept_pivot);  // also orders the pc writes before the reads below
-        const int nlo = c > 0 ? lo + fP1.div(c * (hi - lo)) + 1 : lo;  // past the last kept pivot
-        const int nhi = c < P ? lo + fP1.div((c + 1) * (hi - lo)) : hi;  // the first dropped pivot
-        if (tl < k) {
-            clo = c > 0 ? pc[(c - 1) * k + tl] : clo;
-            chi = c < P ? pc[c * k + tl] : chi;
-        }
-        lo = nlo;
-        hi = nhi;
-        if (lo >= hi) break;  // uniform
-    }
-    // Kept channels of the own list in ascending channel order (flags over
-    // the keys, no longer read), then their count.
-    const int c = lo;
-    for (int i = tid; i < (I + 3) / 4; i += kSelThreads) reinterpret_cast<unsigned*>(flag)[i] = 0u;
-    __syncthreads();
-    for (int r = tid; r < c; r += kSelThreads) flag[jsrt[s0 * I + r]] = 1;
-    __syncthreads();
-    const int pj = (I + kSelThreads - 1) / kSelThreads;  // <= kSelPer
-    const int j0 = tid * pj;
-    unsigned takemask = 0;
-    for (int u = 0; u < pj; ++u)
-        if (j0 + u < I && flag[j0 + u]) takemask |= 1u << u;
-    int total;
-    int pos = block_exclusive_scan<kSelThreads>(__builtin_popcount(takemask), wsum, &total);
-    int32_t* dst = slot_kept + ((size_t)t * k + s0) * I;
-    for (int u = 0; u < pj; ++u)
-        if ((takemask >> u) & 1u) dst[pos++] = j0 + u;
-    if (tid == 0) slot_cnt[(size_t)t * k + s0] = c;
-}
-
-// Gate/up of KC = 4*2 kept channels (two per wave), scaled by the router
-// weight, then their down rows summed over all H in kept order:
-//   part[t][chunk][col] = sum_{q in chunk} (a_{s_q} * p_q) * d_q[col].
-// Kept position q of a token (candidate order) is entry q - C_s of slot s's
-// list, C_s = c_0 + ... + c_{s-1} <= q < C_s + c_s; workgroup (chunk, t)
-// also writes kept_out[t][q] = s * I + j for its positions when asked.
-template <int Q, int CQ>
-__global__ void __launch_bounds__(kThreads)
-chan_gather_kernel(const int32_t* __restrict__ topk_ids, const float* __restrict__ topk_w,
-                   const int32_t* __restrict__ slot_cnt, const int32_t* __restrict__ slot_kept,
-                   int32_t* __restrict__ kept_out, int k, int I, int E, int H, int K, const float* __restrict__ h,
-                   const uint16_t* __restrict__ Wg, const uint16_t* __restrict__ Wu, const uint16_t* __restrict__ Wd,
-                   float* __restrict__ part) {
-    constexpr int KC = kWaves * 2;
+    __shared__ float sa[32];
+    __shared__ RadixLds rl;
+    __shared__ float4 hs[Q * MOE_WAVE * 2];  // h of the token (8 floats per lane and q)
+    __shared__ int ce[KC], cj[KC];
+    __shared__ float ca[KC];
+    __shared__ float gu[KC][2];
     __shared__ float cs[KC];
     const int t = blockIdx.y;
     const int chunk = blockIdx.x;
     const int nchunks = gridDim.x;
     const int tid = threadIdx.x;
-    const int wave = tid / MOE_WAVE;
-    const int lane = tid % MOE_WAVE;
+    const int wave = tid / MOE_WAVE, lane = tid % MOE_WAVE;
+    const int k = A.k, I = A.I, E = A.E, H = A.H, K = A.K;
+    const int n = k * I;
     const int q0 = chunk * KC;
 
-    // h of the token first: it depends on nothing, and a load queued behind
-    // the weight stream would wait for all of it
-    float4 hq[Q][2];
+    // h first: it depends on nothing (staged in LDS once the selection's own
+    // loads are in flight)
+    constexpr int HF4 = Q * MOE_WAVE * 2;  // float4 of h (padded)
+    constexpr int HPT = (HF4 + kSelThreads - 1) / kSelThreads;
+    float4 hreg[HPT];
+#pragma unroll
+    for (int u = 0; u < HPT; ++u) {
+        const int f = min(tid + kSelThreads * u, HF4 - 1);
+        hreg[u] = *reinterpret_cast<const float4*>(A.h + (size_t)t * H + min(4 * f, H - 4));
+    }
+
+    unsigned kmask = 0;
+    bool all = K >= n;
+    if constexpr (MODE == 0) {
+        if constexpr (ROUTE) {
+            const SelRoute& route = A.route;
+            __shared__ uint64_t skey[kSelThreads];
+            __shared__ int sel_e[32];
+            __shared__ float sel_l[32];
+            __shared__ uint64_t wk[MOE_WAVE];
+            __shared__ int wi[MOE_WAVE];
+            __shared__ int s_slow;
+            float lg = 0.f;
+            if (tid < E) {
+                const float bv = route.bias ? route.bias[tid] : 0.f;
+                for (int sl0 = 0; sl0 < route.nslices; sl0 += 8) {  // eight slices in flight
+                    float x[8];
+#pragma unroll
+                    for (int u = 0; u < 8; ++u)
+                        x[u] = route.part[((size_t)min(sl0 + u, route.nslices - 1) * route.M + t) * E + tid];
+#pragma unroll
+                    for (int u = 0; u < 8; ++u) lg += sl0 + u < route.nslices ? x[u] : 0.f;  // slice order
+                }
+                if (route.bias) lg += bv;
+                if (route.logits && chunk == 0) route.logits[(size_t)t * E + tid] = lg;
+                skey[tid] = order_key((lg != lg) ? -INFINITY : lg, tid);  // NaN ranks as -inf
+            }
+            if (tid == 0) s_slow = E > 4 * MOE_WAVE;
+            __syncthreads();
+            if (tid < MOE_WAVE && E <= 4 * MOE_WAVE && !wave_topk<4>(skey, E, k, sel_e, sel_l, wk, wi)) s_slow = 1;
+            __syncthreads();
+            if (s_slow) {  // every key counted (E <= 1024 threads)
+                if (tid < E) {
+                    const int rank = count_greater(skey, 0, E, skey[tid]);
+                    if (rank < k) {
+                        sel_e[rank] = tid;
+                        sel_l[rank] = key_logit(skey[tid]);
+                    }
+                }
+                __syncthreads();
+            }
+            if (tid < MOE_WAVE) {  // lane s: slot s
+                const float w = topk_softmax(sel_l[min(tid, k - 1)], tid, k);
+                if (tid < k) {
+                    if (chunk == 0) {
+                        A.topk_ids[(size_t)t * k + tid] = sel_e[tid];
+                        A.topk_w[(size_t)t * k + tid] = w;
+                    }
+                    se[tid] = sel_e[tid];
+                    sa[tid] = w;
+                }
+            }
+        } else {
+            if (tid < k) {
+                const int e = A.topk_ids[(size_t)t * k + tid];
+                se[tid] = (e >= 0 && e < E) ? e : -1;
+                sa[tid] = A.topk_w[(size_t)t * k + tid];
+            }
+        }
+        __syncthreads();
+        // the norms of the thread's candidates: 16-byte loads when they are 8
+        // consecutive channels of one slot (I % 8 == 0), else one by one
+        float nv[kSelPer];
+        if (I % kSelPer == 0) {  // uniform
+            const int ic = min(kSelPer * tid, n - kSelPer);
+            const int s = fI.div(ic), j = ic - s * I;
+            const float* src = A.norms + (size_t)max(se[s], 0) * I + j;
+            const float4 a = *reinterpret_cast<const float4*>(src);
+            const float4 b = *reinterpret_cast<const float4*>(src + 4);
+            nv[0] = a.x; nv[1] = a.y; nv[2] = a.z; nv[3] = a.w;
+            nv[4] = b.x; nv[5] = b.y; nv[6] = b.z; nv[7] = b.w;
+        } else {
+#pragma unroll
+            for (int u = 0; u < kSelPer; ++u) {
+                const int ic = min(kSelPer * tid + u, n - 1);
+                const int s = fI.div(ic), j = ic - s * I;
+                nv[u] = A.norms[(size_t)max(se[s], 0) * I + j];
+            }
+        }
+#pragma unroll
+        for (int u = 0; u < HPT; ++u)
+            if (tid + kSelThreads * u < HF4) hs[tid + kSelThreads * u] = hreg[u];
+        double sc[kSelPer];
+        uint32_t key[3][kSelPer];
+        unsigned vmask = 0, bmask = 0;  // candidates; candidates of valid slots
+        uint32_t fmax = 0, fmin = 0xFFFFFFFFu;
+#pragma unroll
+        for (int u = 0; u < kSelPer; ++u) {
+            const int idx = kSelPer * tid + u;
+            const int ic = min(idx, n - 1);
+            const int s = fI.div(ic), j = ic - s * I;
+            const int e = se[s];
+            sc[u] = (double)sa[s] * (double)nv[u] + 0.0;  // exact; -0 as +0
+            const unsigned long long kk = e < 0 ? 0ull : score_key(sc[u]);
+            key[0][u] = (uint32_t)(kk >> 32);
+            key[1][u] = (uint32_t)kk;
+            key[2][u] = ~(((uint32_t)(e < 0 ? 8191 : e) << 19) | ((uint32_t)j << 5) | (uint32_t)s);
+            vmask |= idx < n ? (1u << u) : 0u;
+            if (idx < n && e >= 0) {
+                bmask |= 1u << u;
+                const uint32_t fk = float_order_key((float)sc[u]);
+                fmax = max(fmax, fk);
+                fmin = min(fmin, fk);
+            }
+        }
+        kmask = vmask;
+        if (!all) {
+            // bins linear in the score (as fp32) between the token's minimum
+            // and maximum; invalid slots in bin 0, below every valid candidate
+            uint32_t mx, mn;
+            block_max_min(fmax, fmin, rl, &mx, &mn);
+            const float lo = float_of_order_key(mn);
+            const float scl = linear_scale(lo, float_of_order_key(mx), kRadixBins - 1);
+            int bin[kSelPer];
+#pragma unroll
+            for (int u = 0; u < kSelPer; ++u)
+                bin[u] = ((bmask >> u) & 1u) ? 1 + linear_bin((float)sc[u], lo, scl, kRadixBins - 1) : 0;
+            kmask = select_top<3>(bin, key, vmask, K, rl);
+        }
+    } else {
+        if (tid < k) {
+            const int e = A.topk_ids[(size_t)t * k + tid];
+            se[tid] = (e >= 0 && e < E) ? e : -1;
+            sa[tid] = A.topk_w[(size_t)t * k + tid];
+        }
+        __syncthreads();
+        uint32_t sb[kSelPer], tb[kSelPer], smax, smin;
+        unsigned vmask;
+        reader_scores(A.ra, t, fI, se, sa, sb, tb, vmask, smax, smin, nullptr, nullptr);
+#pragma unroll
+        for (int u = 0; u < HPT; ++u)
+            if (tid + kSelThreads * u < HF4) hs[tid + kSelThreads * u] = hreg[u];
+        kmask = vmask;
+        if (!all) {
+            uint32_t mx, mn;
+            block_max_min(smax, smin, rl, &mx, &mn);  // non-negative scores: bits order like values
+            const float lo = __uint_as_float(mn);
+            const float scl = linear_scale(lo, __uint_as_float(mx), kRadixBins);
+            int bin[kSelPer];
+            uint32_t key[2][kSelPer];
+#pragma unroll
+            for (int u = 0; u < kSelPer; ++u) {
+                bin[u] = linear_bin(__uint_as_float(sb[u]), lo, scl, kRadixBins);
+                key[0][u] = sb[u];
+                key[1][u] = ~tb[u];
+            }
+            kmask = select_top<2>(bin, key, vmask, K, rl);
+        }
+    }
+
+    // positions of the kept candidates in candidate order; the chunk's own
+    if (tid < KC) ce[tid] = -1;
+    const int cntk = __builtin_popcount(kmask);
+    int incl = cntk;
+#pragma unroll
+    for (int d = 1; d < MOE_WAVE; d <<= 1) {
+        const int y = __shfl_up(incl, d, MOE_WAVE);
+        if (lane >= d) incl += y;
+    }
+    if (lane == MOE_WAVE - 1) rl.wsum[wave] = incl;
+    __syncthreads();
+    int pos = incl - cntk;
+    for (int x = 0; x < wave; ++x) pos += rl.wsum[x];
+#pragma unroll
+    for (int u = 0; u < kSelPer; ++u) {
+        const int idx = kSelPer * tid + u;
+        if (idx >= n) continue;
+        const bool kept = (kmask >> u) & 1u;
+        const int s = fI.div(idx), j = idx - s * I;
+        if (A.kept_flag && chunk == 0) A.kept_flag[((size_t)t * k + s) * I + j] = kept ? 1 : 0;
+        if (!kept) continue;
+        if (pos >= q0 && pos < q0 + KC) {
+            ce[pos - q0] = se[s];
+            cj[pos - q0] = j;
+            ca[pos - q0] = sa[s];
+            if (A.kept_out) A.kept_out[(size_t)t * K + pos] = idx;
+        }
+        ++pos;
+    }
+    __syncthreads();
+
+    // gather: every load of the chunk first (gate or up row of one channel
+    // per wave, the down rows of all of them in threads 0..255)
+    const int qc = wave >> 1, P = wave & 1;
+    const int ec = ce[qc];
+    const bool okc = ec >= 0;
+    const size_t rowc = okc ? ((size_t)ec * I + cj[qc]) * H : 0;
+    const uint16_t* W = P ? A.Wu : A.Wg;
+    uint4 wv[Q];
 #pragma unroll
     for (int q = 0; q < Q; ++q) {
-        const int col = min((lane + MOE_WAVE * q) * 8, H - 8);
-        hq[q][0] = *reinterpret_cast<const float4*>(h + (size_t)t * H + col);
-        hq[q][1] = *reinterpret_cast<const float4*>(h + (size_t)t * H + col + 4);
+        const int col = (lane + MOE_WAVE * q) * 8;
+        wv[q] = (okc && col < H) ? load_stream16(W + rowc + col) : make_uint4(0u, 0u, 0u, 0u);
     }
-    // Resolve the KC kept channels of the chunk: lane l < k loads slot l's
-    // count, expert and affinity (one round of vector loads), lane q finds
-    // the slot of position q0 + q from the running counts and loads its
-    // channel (a second round), then every lane takes the values by readlane.
-    int ce[KC], cj[KC];
-    float ca[KC];
-    {
-        const int sl = min(lane, k - 1);
-        const int cnt_l = slot_cnt[(size_t)t * k + sl];
-        const int e_l = topk_ids[(size_t)t * k + sl];
-        const float a_l = topk_w[(size_t)t * k + sl];
-        const int q = lane % KC;
-        const int pos = q0 + q;
-        int s = -1, off = 0, run = 0;
-        for (int x = 0; x < k; ++x) {  // k <= 32
-            const int cx = min(max(__builtin_amdgcn_readlane(cnt_l, x), 0), I);
-            if (s < 0 && pos < run + cx) {
-                s = x;
-                off = pos - run;
-            }
-            run += cx;
-        }
-        const bool qin = pos < K && s >= 0;
-        const int sc = qin ? s : 0;
-        const int jv = slot_kept[((size_t)t * k + sc) * I + (qin ? off : 0)];
-        const int e = __builtin_amdgcn_ds_bpermute(sc << 2, e_l);
-        const float a = __int_as_float(__builtin_amdgcn_ds_bpermute(sc << 2, __float_as_int(a_l)));
-        const bool vin = qin && jv >= 0 && jv < I;
-        const int ev = (vin && e >= 0 && e < E) ? e : -1;
-        if (kept_out && lane < KC && wave == 0 && pos < K) kept_out[(size_t)t * K + pos] = vin ? sc * I + jv : -1;
+    uint4 wd[KC];
+    auto load_down = [&](int cq) {
 #pragma unroll
         for (int qq = 0; qq < KC; ++qq) {
-            ce[qq] = __builtin_amdgcn_readlane(ev, qq);
-            cj[qq] = __builtin_amdgcn_readlane(jv, qq);
-            ca[qq] = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(a), qq));
-        }
-    }
-    // issue every load of the chunk: gate/up rows of this wave's two
-    // channels, down rows of all KC channels, the token's h
-    uint4 wg[2][Q], wu[2][Q], wd[KC][CQ];
-#pragma unroll
-    for (int c = 0; c < 2; ++c) {
-        const int qq = wave * 2 + c;
-        const bool ok = ce[qq] >= 0;
-        const size_t row = ok ? ((size_t)ce[qq] * I + cj[qq]) * H : 0;
-#pragma unroll
-        for (int q = 0; q < Q; ++q) {
-            const int col = (lane + MOE_WAVE * q) * 8;
-            const bool in = ok && col < H;
-            wg[c][q] = in ? load_stream16(Wg + row + col) : make_uint4(0, 0, 0, 0);
-            wu[c][q] = in ? load_stream16(Wu + row + col) : make_uint4(0, 0, 0, 0);
-        }
-    }
-#pragma unroll
-    for (int qq = 0; qq < KC; ++qq) {
-        const bool ok = ce[qq] >= 0;
-        const size_t row = ok ? ((size_t)ce[qq] * I + cj[qq]) * H : 0;
-#pragma unroll
-        for (int cq = 0; cq < CQ; ++cq) {
+            const bool ok = ce[qq] >= 0;
+            const size_t row = ok ? ((size_t)ce[qq] * I + cj[qq]) * H : 0;
             const int col = (tid + kThreads * cq) * 8;
-            wd[qq][cq] = (ok && col < H) ? load_stream16(Wd + row + col) : make_uint4(0, 0, 0, 0);
+            wd[qq] = (ok && col < H && tid < kThreads) ? load_stream16(A.Wd + row + col) : make_uint4(0u, 0u, 0u, 0u);
         }
-    }
-    float ag[2] = {0.f, 0.f}, au[2] = {0.f, 0.f};
+    };
+    load_down(0);
+    float acc = 0.f;
 #pragma unroll
     for (int q = 0; q < Q; ++q) {
         const int col = (lane + MOE_WAVE * q) * 8;
         if (col >= H) continue;
-        const float4 h0 = hq[q][0], h1 = hq[q][1];
+        const float4 h0 = hs[2 * (lane + MOE_WAVE * q)], h1 = hs[2 * (lane + MOE_WAVE * q) + 1];
         const float hv[8] = {h0.x, h0.y, h0.z, h0.w, h1.x, h1.y, h1.z, h1.w};
+        float f[8];
+        unpack8(wv[q], f);
 #pragma unroll
-        for (int c = 0; c < 2; ++c) {
-            float gf[8], uf[8];
-            unpack8(wg[c][q], gf);
-            unpack8(wu[c][q], uf);
-#pragma unroll
-            for (int x = 0; x < 8; ++x) {
-                ag[c] = fmaf(gf[x], hv[x], ag[c]);
-                au[c] = fmaf(uf[x], hv[x], au[c]);
-            }
-        }
+        for (int x = 0; x < 8; ++x) acc = fmaf(f[x], hv[x], acc);
     }
-#pragma unroll
-    for (int c = 0; c < 2; ++c) {
-        const float g = wave_sum(ag[c]);
-        const float u = wave_sum(au[c]);
-        const int qq = wave * 2 + c;
-        if (lane == 0) cs[qq] = ce[qq] >= 0 ? ca[qq] * silu_mul(g, u) : 0.f;
-    }
+    const float dot = wave_sum(acc);
+    if (lane == 0) gu[qc][P] = dot;
     __syncthreads();
+    if (tid < KC) cs[tid] = ce[tid] >= 0 ? ca[tid] * silu_mul(gu[tid][0], gu[tid][1]) : 0.f;
+    __syncthreads();
+    if (tid < kThreads) {
 #pragma unroll
-    for (int cq = 0; cq < CQ; ++cq) {
-        const int col = (tid + kThreads * cq) * 8;
-        if (col >= H) continue;
-        float acc[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
+        for (int cq = 0; cq < CQ; ++cq) {
+            if (cq > 0) load_down(cq);
+            const int col = (tid + kThreads * cq) * 8;
+            if (col >= H) continue;
+            float o[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-        for (int qq = 0; qq < KC; ++qq) {
-            float wf[8];
-            unpack8(wd[qq][cq], wf);
-            const float cq_ = cs[qq];
+            for (int qq = 0; qq < KC; ++qq) {
+                float wf[8];
+                unpack8(wd[qq], wf);
+                const float c = cs[qq];
 #pragma unroll
-            for (int x = 0; x < 8; ++x) acc[x] = fmaf(cq_, wf[x], acc[x]);
+                for (int x = 0; x < 8; ++x) o[x] = fmaf(c, wf[x], o[x]);
+            }
+            float* dst = A.part + ((size_t)t * nchunks + chunk) * H + col;
+            *reinterpret_cast<float4*>(dst) = make_float4(o[0], o[1], o[2], o[3]);
+            *reinterpret_cast<float4*>(dst + 4) = make_float4(o[4], o[5], o[6], o[7]);
         }
-        float* dst = part + ((size_t)t * nchunks + chunk) * H + col;
-        *reinterpret_cast<float4*>(dst) = make_float4(acc[0], acc[1], acc[2], acc[3]);
-        *reinterpret_cast<float4*>(dst + 4) = make_float4(acc[4], acc[5], acc[6], acc[7]);
     }
 }
 
@@ -588,100 +428,62 @@ channel_norms_kernel(int EI, int H, const uint16_t* __restrict__ Wg, const uint1
     if (lane == 0) norms[ch] = (float)((sqrt(sg) * sqrt(sv)) * sqrt(sd));
 }
 
-// Load-time list positions of the channel-sparse selection: ranks[e][j] =
-// the number of channels j2 of expert e whose norm is greater (float order)
-// or equal with j2 < j, i.e. channel j's position when the expert's channels
-// are ordered by decreasing norm, ties to the lower channel.  One workgroup
-// per expert, the expert's norms in LDS.
-__global__ void __launch_bounds__(kSelThreads)
-channel_ranks_kernel(int I, const float* __restrict__ norms, int32_t* __restrict__ ranks) {
-    extern __shared__ uint32_t nk[];
-    const int e = blockIdx.x;
-    for (int j = threadIdx.x; j < I; j += kSelThreads) nk[j] = float_key(norms[(size_t)e * I + j]);
-    __syncthreads();
-    for (int j = threadIdx.x; j < I; j += kSelThreads) {
-        const uint32_t x = nk[j];
-        int c = 0;
-        for (int j2 = 0; j2 < I; ++j2) {
-            const uint32_t y = nk[j2];
-            c += (y > x || (y == x && j2 < j)) ? 1 : 0;
-        }
-        ranks[(size_t)e * I + j] = c;
-    }
-}
-
-template <int Q>
-hipError_t gather_q(const int32_t* topk_ids, const float* topk_w, const int32_t* slot_cnt, const int32_t* slot_kept,
-                    int32_t* kept_out, int M, int k, int I, int E, int H, int K, const float* h, const uint16_t* Wg,
-                    const uint16_t* Wu, const uint16_t* Wd, float* part, hipStream_t stream) {
-    constexpr int KC = kWaves * 2;
-    const dim3 grid((K + KC - 1) / KC, M);
-    const int CQ = (H + 2047) / 2048;
-    if (CQ <= 1)
-        MOE_LAUNCH((chan_gather_kernel<Q, 1>), grid, dim3(kThreads), 0, stream, topk_ids, topk_w, slot_cnt,
-                   slot_kept, kept_out, k, I, E, H, K, h, Wg, Wu, Wd, part);
-    else if (CQ <= 2)
-        MOE_LAUNCH((chan_gather_kernel<Q, 2>), grid, dim3(kThreads), 0, stream, topk_ids, topk_w, slot_cnt,
-                   slot_kept, kept_out, k, I, E, H, K, h, Wg, Wu, Wd, part);
-    else if (CQ <= 4)
-        MOE_LAUNCH((chan_gather_kernel<Q, 4>), grid, dim3(kThreads), 0, stream, topk_ids, topk_w, slot_cnt,
-                   slot_kept, kept_out, k, I, E, H, K, h, Wg, Wu, Wd, part);
-    else
-        return hipErrorInvalidValue;
-    return hipGetLastError();
-}
-
 }  // namespace
 
-// list keys uint64 [n] (later the kept flags) + list channels uint16 [n]
-size_t chan_select_lds_bytes(int n) { return (size_t)n * (sizeof(unsigned long long) + sizeof(uint16_t)); }
-
-hipError_t launch_chan_select(const int32_t* topk_ids, const float* topk_w, const float* norms, const int32_t* ranks,
-                              int M, int k, int I, int E, int K, int32_t* slot_cnt, int32_t* slot_kept,
-                              hipStream_t stream) {
-    if (k * I > kSelThreads * kSelPer || k > 32) return hipErrorInvalidValue;
-    MOE_LAUNCH(chan_select_kernel<false>, dim3(k, M), dim3(kSelThreads), chan_select_lds_bytes(k * I), stream,
-               topk_ids, topk_w, norms, ranks, k, I, E, K, FastDiv((uint32_t)I), sel_search(k), slot_cnt, slot_kept,
-               SelRoute{});
+template <int MODE, bool ROUTE>
+hipError_t topk_gather(const SparseArgs& a, int M, hipStream_t stream) {
+    const int Q = (a.H + 511) / 512;
+    const dim3 grid((a.K + kGatherKC - 1) / kGatherKC, M);
+    const FastDiv fI((uint32_t)a.I);
+#define MOE_TG(QQ, CQQ) MOE_LAUNCH((chan_topk_gather_kernel<MODE, ROUTE, QQ, CQQ>), grid, dim3(kSelThreads), 0, stream, \
+                                   a, fI)
+    if (Q <= 4) MOE_TG(4, 1);
+    else if (Q <= 8) MOE_TG(8, 2);
+    else if (Q <= 16) MOE_TG(16, 4);
+    else return hipErrorInvalidValue;
+#undef MOE_TG
     return hipGetLastError();
 }
 
-hipError_t launch_chan_select_routed(const SelRoute& route, const float* norms, const int32_t* ranks, int M, int k,
-                                     int I, int E, int K, int32_t* slot_cnt, int32_t* slot_kept, hipStream_t stream) {
-    if (k * I > kSelThreads * kSelPer || E > kSelThreads || k > 32 || route.M != M) return hipErrorInvalidValue;
-    MOE_LAUNCH(chan_select_kernel<true>, dim3(k, M), dim3(kSelThreads), chan_select_lds_bytes(k * I), stream, nullptr,
-               nullptr, norms, ranks, k, I, E, K, FastDiv((uint32_t)I), sel_search(k), slot_cnt, slot_kept, route);
-    return hipGetLastError();
-}
-
-hipError_t launch_chan_gather(const int32_t* topk_ids, const float* topk_w, const int32_t* slot_cnt,
-                              const int32_t* slot_kept, int32_t* kept_out, int M, int k, int I, int E, int H, int K,
-                              int chunk, const float* h, const uint16_t* Wg, const uint16_t* Wu, const uint16_t* Wd,
-                              float* part, hipStream_t stream) {
-    (void)chunk;
-    if (k > MOE_WAVE) return hipErrorInvalidValue;
-    const int Q = (H + 511) / 512;
-#define MOE_GATHER(QQ) gather_q<QQ>(topk_ids, topk_w, slot_cnt, slot_kept, kept_out, M, k, I, E, H, K, h, Wg, Wu, Wd, \
-                                   part, stream)
-    if (Q <= 1) return MOE_GATHER(1);
-    if (Q <= 2) return MOE_GATHER(2);
-    if (Q <= 4) return MOE_GATHER(4);
-    if (Q <= 8) return MOE_GATHER(8);
-    if (Q <= 16) return MOE_GATHER(16);
-#undef MOE_GATHER
-    return hipErrorInvalidValue;
+hipError_t launch_chan_topk_gather(int mode, const SelRoute* route, int32_t* topk_ids, float* topk_w,
+                                   const float* norms, const ReaderArgs* ra, int M, int k, int I, int E, int H, int K,
+                                   const float* h, const uint16_t* Wg, const uint16_t* Wu, const uint16_t* Wd,
+                                   float* part, int32_t* kept_out, uint8_t* kept_flag, hipStream_t stream) {
+    if (k * I > kSelThreads * kSelPer || k > 32 || E > 8192 || I > 16384 || K < 1 || K > k * I || M < 1 ||
+        H % 8 || H > 8192)
+        return hipErrorInvalidValue;
+    SparseArgs a{};
+    a.topk_ids = topk_ids;
+    a.topk_w = topk_w;
+    a.norms = norms;
+    if (ra) a.ra = *ra;
+    a.k = k;
+    a.I = I;
+    a.E = E;
+    a.H = H;
+    a.K = K;
+    a.h = h;
+    a.Wg = Wg;
+    a.Wu = Wu;
+    a.Wd = Wd;
+    a.part = part;
+    a.kept_out = kept_out;
+    a.kept_flag = kept_flag;
+    if (mode == 1) {
+        if (!ra || route || ra->nbq < 1 || ra->nbq > kReaderMaxGroups || ra->I != I || ra->k != k) return hipErrorInvalidValue;
+        return topk_gather<1, false>(a, M, stream);
+    }
+    if (route) {
+        if (E > kSelThreads || route->M != M) return hipErrorInvalidValue;
+        a.route = *route;
+        return topk_gather<0, true>(a, M, stream);
+    }
+    return topk_gather<0, false>(a, M, stream);
 }
 
 hipError_t launch_chan_combine(int M, int H, int nchunks, const float* part, float* y, hipStream_t stream) {
     const dim3 grid((H / 4 + kCombCG - 1) / kCombCG, M);
     MOE_LAUNCH(chan_combine_kernel, grid, dim3(MOE_WAVE), 0, stream, H, nchunks, part, y);
-    return hipGetLastError();
-}
-
-hipError_t launch_channel_ranks(int E, int I, const float* norms, int32_t* ranks, hipStream_t stream) {
-    if (I < 1 || I > kSelThreads * kSelPer) return hipErrorInvalidValue;
-    hipLaunchKernelGGL(channel_ranks_kernel, dim3(E), dim3(kSelThreads), (size_t)I * sizeof(uint32_t), stream, I,
-                       norms, ranks);
     return hipGetLastError();
 }
 

@@ -147,16 +147,6 @@ hipError_t launch_gateup_vqlr(const int32_t* topk_ids, int R, int k, int E, cons
 hipError_t launch_vq_finish(const float* vp, int R, int I, int nslice, float* p, hipStream_t stream);
 
 // ---- chansparse.hip
-size_t chan_select_lds_bytes(int n);
-// Channel top-K per token, one workgroup per (slot, token): per slot the
-// kept channels in ascending order, slot_kept int32 [M][k][I], and their
-// number, slot_cnt int32 [M][k] (summing to K per token).
-hipError_t launch_chan_select(const int32_t* topk_ids, const float* topk_w, const float* norms, const int32_t* ranks,
-                              int M, int k, int I, int E, int K, int32_t* slot_cnt, int32_t* slot_kept,
-                              hipStream_t stream);
-// The same selection, each workgroup first routing its token from the
-// router's slice partials (launch_router_partials) and writing ids,
-// affinities (and logits) as moe_route_topk would.
 struct SelRoute {
     const float* part;   // fp32 [nslices][M][E] router slice partials
     const float* bias;   // fp32 [E] or null
@@ -166,15 +156,19 @@ struct SelRoute {
     float* wts;          // fp32 [M][k] out
     float* logits;       // fp32 [M][E] out, or null
 };
-hipError_t launch_chan_select_routed(const SelRoute& route, const float* norms, const int32_t* ranks, int M, int k,
-                                     int I, int E, int K, int32_t* slot_cnt, int32_t* slot_kept, hipStream_t stream);
-// kept_out (nullable): int32 [M][K], the kept set as s * I + j ascending.
-hipError_t launch_chan_gather(const int32_t* topk_ids, const float* topk_w, const int32_t* slot_cnt,
-                              const int32_t* slot_kept, int32_t* kept_out, int M, int k, int I, int E, int H, int K,
-                              int chunk, const float* h, const uint16_t* Wg, const uint16_t* Wu, const uint16_t* Wd,
-                              float* part, hipStream_t stream);
+struct ReaderArgs;
+// Channel top-K and the kept channels' gate/up + down partials in one launch
+// (grid ceil(K / 8) x M): mode 0 scores by the static norms (route non-null:
+// each workgroup first routes its token from the router's slice partials and
+// the ids / affinities are written to topk_ids / topk_w), mode 1 by the
+// reader's estimates (ra).  part fp32 [M][ceil(K / 8)][H]; kept_out int32
+// [M][K] (nullable): the kept set as s * I + j ascending; kept_flag u8
+// [M][k][I] (nullable).
+hipError_t launch_chan_topk_gather(int mode, const SelRoute* route, int32_t* topk_ids, float* topk_w,
+                                   const float* norms, const ReaderArgs* ra, int M, int k, int I, int E, int H, int K,
+                                   const float* h, const uint16_t* Wg, const uint16_t* Wu, const uint16_t* Wd,
+                                   float* part, int32_t* kept_out, uint8_t* kept_flag, hipStream_t stream);
 hipError_t launch_chan_combine(int M, int H, int nchunks, const float* part, float* y, hipStream_t stream);
-hipError_t launch_channel_ranks(int E, int I, const float* norms, int32_t* ranks, hipStream_t stream);
 hipError_t launch_channel_norms(int E, int I, int H, const uint16_t* Wg, const uint16_t* Wu, const uint16_t* Wd,
                                 float* norms, hipStream_t stream);
 

@@ -123,8 +123,7 @@ moe_status check_weights(const moe_config* c, const moe_weights* w) {
                 return MOE_ERR_INVALID_ARG;
         }
     }
-    if (c->max_keep > 0 && !c->reader &&
-        (!w->chan_norm || !aligned(w->chan_norm, 4) || !w->chan_rank || !aligned(w->chan_rank, 4)))
+    if (c->max_keep > 0 && !c->reader && (!w->chan_norm || !aligned(w->chan_norm, 16)))
         return MOE_ERR_INVALID_ARG;
     if (c->reader) {
         if (!w->rot_signs || !w->sketch || !aligned(w->sketch, 16) || !w->sketch_scale ||
@@ -244,21 +243,40 @@ struct Exec {
 
 moe_status hip_status(hipError_t e) { return e == hipSuccess ? MOE_OK : MOE_ERR_HIP; }
 
-// Channel-sparse mode after the selection: kept-channel gather, then combine.
-moe_status chan_gather_combine(const Exec& x, const float* h, int M, const int32_t* topk_ids, const float* topk_w,
-                               int K, int32_t* kept_out, float* y, hipStream_t s) {
+// Channel-sparse mode from the routes (or, with `route`, from the router's
+// slice partials): the selection-and-gather launch, then the combine (with
+// the recovery map in reader mode when rec_rank > 0).  mode 0: static norms,
+// 1: the reader's estimates (already screened).
+moe_status sparse_gather_combine(const Exec& x, int mode, const moe::SelRoute* route, const moe::ReaderArgs* ra,
+                                 const float* h, int M, int32_t* topk_ids, float* topk_w, int K, int32_t* kept_out,
+                                 float* y, hipStream_t s) {
     const moe_config& c = x.c;
     const int nchunks = (K + kChanChunk - 1) / kChanChunk;
+    const bool rec = mode == 1 && c.rec_rank > 0;
     hipError_t e;
     {
         Launch l(x.prof, MOE_KERNEL_CHAN_GATHER);
-        e = moe::launch_chan_gather(topk_ids, topk_w, x.ws.slot_cnt, x.ws.slot_kept, kept_out, M, c.top_k, c.I, c.E,
-                                    c.H, K, kChanChunk, h, x.w.w_gate, x.w.w_up, x.w.w_down, x.ws.chan_part, s);
+        e = moe::launch_chan_topk_gather(mode, route, topk_ids, topk_w, x.w.chan_norm, ra, M, c.top_k, c.I, c.E, c.H,
+                                         K, h, x.w.w_gate, x.w.w_up, x.w.w_down, x.ws.chan_part, kept_out,
+                                         rec ? x.ws.kept_flag : nullptr, s);
         l.done();
         if (e != hipSuccess) return MOE_ERR_HIP;
     }
-    Launch l(x.prof, MOE_KERNEL_CHAN_COMBINE);
-    e = moe::launch_chan_combine(M, c.H, nchunks, x.ws.chan_part, y, s);
+    if (!rec) {
+        Launch l(x.prof, MOE_KERNEL_CHAN_COMBINE);
+        e = moe::launch_chan_combine(M, c.H, nchunks, x.ws.chan_part, y, s);
+        l.done();
+        return hip_status(e);
+    }
+    {
+        Launch l(x.prof, MOE_KERNEL_READER_RECOVER);
+        e = moe::launch_reader_recover(*ra, topk_ids, topk_w, M, s);
+        l.done();
+        if (e != hipSuccess) return MOE_ERR_HIP;
+    }
+    Launch l(x.prof, MOE_KERNEL_READER_COMBINE);
+    e = moe::launch_reader_combine(M, c.H, nchunks, x.ws.chan_part, x.ws.rpart,
+                                   c.top_k * moe::reader_recover_chunks(c.I), c.rec_rank, x.w.rec_basis, y, s);
     l.done();
     return hip_status(e);
 }
@@ -285,7 +303,8 @@ moe::ReaderArgs reader_args(const Exec& x) {
 }
 
 // Reader, from the routes on: rotation (unless already done), screening,
-// selection, gather, then the combine (with the recovery map when rec_rank > 0).
+// then selection-and-gather and the combine (with the recovery map when
+// rec_rank > 0).
 moe_status reader_forward(const Exec& x, bool rotated, const moe::SelRoute* route, const float* h, int M,
                           const int32_t* topk_ids, const float* topk_w, int K, int32_t* kept_out, float* y,
                           hipStream_t s) {
@@ -304,33 +323,8 @@ moe_status reader_forward(const Exec& x, bool rotated, const moe::SelRoute* rout
         l.done();
         if (e != hipSuccess) return MOE_ERR_HIP;
     }
-    {
-        Launch l(x.prof, MOE_KERNEL_READER_SELECT);
-        e = moe::launch_reader_select(ra, topk_ids, topk_w, M, K, x.ws.slot_cnt, x.ws.slot_kept, nullptr, nullptr,
-                                      nullptr, s);
-        l.done();
-        if (e != hipSuccess) return MOE_ERR_HIP;
-    }
-    if (!c.rec_rank) return chan_gather_combine(x, h, M, topk_ids, topk_w, K, kept_out, y, s);
-    const int nchunks = (K + kChanChunk - 1) / kChanChunk;
-    {
-        Launch l(x.prof, MOE_KERNEL_CHAN_GATHER);
-        e = moe::launch_chan_gather(topk_ids, topk_w, x.ws.slot_cnt, x.ws.slot_kept, kept_out, M, c.top_k, c.I, c.E,
-                                    c.H, K, kChanChunk, h, x.w.w_gate, x.w.w_up, x.w.w_down, x.ws.chan_part, s);
-        l.done();
-        if (e != hipSuccess) return MOE_ERR_HIP;
-    }
-    {
-        Launch l(x.prof, MOE_KERNEL_READER_RECOVER);
-        e = moe::launch_reader_recover(ra, topk_ids, topk_w, M, s);
-        l.done();
-        if (e != hipSuccess) return MOE_ERR_HIP;
-    }
-    Launch l(x.prof, MOE_KERNEL_READER_COMBINE);
-    e = moe::launch_reader_combine(M, c.H, nchunks, x.ws.chan_part, x.ws.rpart,
-                                   c.top_k * moe::reader_recover_chunks(c.I), c.rec_rank, x.w.rec_basis, y, s);
-    l.done();
-    return hip_status(e);
+    return sparse_gather_combine(x, 1, nullptr, &ra, h, M, const_cast<int32_t*>(topk_ids),
+                                 const_cast<float*>(topk_w), K, kept_out, y, s);
 }
 
 moe_status route_topk_impl(const Exec& x, const float* h, int32_t M, int32_t* topk_ids, float* topk_w,
@@ -391,14 +385,8 @@ moe_status expert_forward_impl(const Exec& x, bool z_ready, const float* h, int3
         if (c.max_keep == 0 || c.wformat != MOE_WFORMAT_DENSE) return MOE_ERR_UNSUPPORTED;
         if (keep_channels > c.max_keep) return MOE_ERR_CAPACITY;
         if (c.reader) return reader_forward(x, false, nullptr, h, M, topk_ids, topk_w, keep_channels, kept_out, y, s);
-        {
-            Launch l(x.prof, MOE_KERNEL_CHAN_SELECT);
-            e = moe::launch_chan_select(topk_ids, topk_w, x.w.chan_norm, x.w.chan_rank, M, c.top_k, c.I, c.E,
-                                        keep_channels, x.ws.slot_cnt, x.ws.slot_kept, s);
-            l.done();
-            if (e != hipSuccess) return MOE_ERR_HIP;
-        }
-        return chan_gather_combine(x, h, M, topk_ids, topk_w, keep_channels, kept_out, y, s);
+        return sparse_gather_combine(x, 0, nullptr, nullptr, h, M, const_cast<int32_t*>(topk_ids),
+                                     const_cast<float*>(topk_w), keep_channels, kept_out, y, s);
     }
 
     if (!sorted_routes || !block_expert || !counts) return MOE_ERR_INVALID_ARG;
@@ -509,14 +497,7 @@ moe_status decode_step_impl(const Exec& x, const float* h, int32_t M, int32_t* t
         route.wts = topk_w;
         route.logits = logits_out;
         if (c.reader) return reader_forward(x, true, &route, h, M, topk_ids, topk_w, keep_channels, kept_out, y, s);
-        {
-            Launch l(x.prof, MOE_KERNEL_CHAN_SELECT);
-            e = moe::launch_chan_select_routed(route, x.w.chan_norm, x.w.chan_rank, M, c.top_k, c.I, c.E,
-                                               keep_channels, x.ws.slot_cnt, x.ws.slot_kept, s);
-            l.done();
-            if (e != hipSuccess) return MOE_ERR_HIP;
-        }
-        return chan_gather_combine(x, h, M, topk_ids, topk_w, keep_channels, kept_out, y, s);
+        return sparse_gather_combine(x, 0, &route, nullptr, h, M, topk_ids, topk_w, keep_channels, kept_out, y, s);
     }
     const int nsl = moe::router_slices(c.H, c.E);
     if (M != 1 || c.wformat != MOE_WFORMAT_DENSE || !moe::decode_fused_ok(c.H, c.E, c.top_k, nsl)) {
@@ -850,14 +831,6 @@ moe_status moe_channel_norms(const moe_config* cfg, const uint16_t* w_gate, cons
         return MOE_ERR_INVALID_ARG;
     return hip_status(moe::launch_channel_norms(cfg->E, cfg->I, cfg->H, w_gate, w_up, w_down, norms,
                                                 static_cast<hipStream_t>(stream)));
-}
-
-moe_status moe_channel_ranks(const moe_config* cfg, const float* norms, int32_t* ranks, void* stream) {
-    if (!cfg || !norms || !ranks) return MOE_ERR_INVALID_ARG;
-    if (cfg->I <= 0 || cfg->E <= 0) return MOE_ERR_INVALID_ARG;
-    if (cfg->I > 8192 || (int64_t)cfg->E * cfg->I > INT32_MAX) return MOE_ERR_UNSUPPORTED;
-    if (!aligned(norms, 4) || !aligned(ranks, 4)) return MOE_ERR_INVALID_ARG;
-    return hip_status(moe::launch_channel_ranks(cfg->E, cfg->I, norms, ranks, static_cast<hipStream_t>(stream)));
 }
 
 moe_status moe_validate_plan(const int32_t* ids, int32_t M, int32_t k, int32_t E, int32_t b, const int32_t* rows,

@@ -27,6 +27,7 @@
 #include "device_common.h"
 #include "launch.h"
 #include "reader_device.h"
+#include "select_device.h"
 #include "topk_device.h"
 
 namespace moe {
@@ -37,8 +38,6 @@ constexpr int kThreads = 256;
 constexpr int kWaves = kThreads / MOE_WAVE;
 constexpr int kRowGroups = 64;   // screening: row groups of a workgroup (4 lanes each)
 constexpr int kRangeCh = 80;     // screening: channels per workgroup (16 bytes of a row)
-constexpr int kSelThreads = 1024;
-constexpr int kSelPer = 8;       // selection: candidates per thread (k * I <= 8192)
 constexpr int kMaxRank = 32;
 
 // ---------------------------------------------------------------------------
@@ -80,7 +79,7 @@ reader_rotate_kernel(const float* __restrict__ h, int M, int H, const int8_t* __
 // every workgroup first routes its token from the router's slice partials
 // with the router's arithmetic (E <= 256).
 constexpr int kMaxBpw = 32;                                      // nblk <= 64
-constexpr int kMaxGroups = 2;
+constexpr int kMaxGroups = kReaderMaxGroups;
 constexpr int kStage = kMaxBpw * kReaderScan / kThreads;         // staged (coordinate, value) per thread
 constexpr int kRowBatch = 10;                                    // rows in flight per thread
 
@@ -265,134 +264,11 @@ reader_screen_kernel(ReaderArgs ra, SelRoute route, const int32_t* __restrict__ 
 // fp32 (NaN and invalid slots score 0) whose bit pattern orders like its
 // value.
 //
-// The K-th largest score is found by a radix select over the 32-bit pattern
-// in three digit passes (bits 31..21, 20..10, 9..0): each pass histograms the
-// digit of the candidates that share the digits found so far (LDS atomics),
-// and a suffix scan over the bins finds the bin where the count of larger
-// candidates reaches the demand.  When the demand is that whole bin the kept
-// set is every score at or above the bin's prefix; otherwise, after the last
-// pass, the K-th score T is exact and the candidates scoring exactly T are
-// taken in the order (expert id, channel, slot): the same select over the
-// complement of the 32-bit tie key e << 19 | j << 5 | s (invalid slots as
-// expert 8191) picks the ones needed.
-constexpr int kSelWaves = kSelThreads / MOE_WAVE;
-constexpr int kRadixBins = 2048;
-
-struct RadixLds {
-    int hist[kRadixBins];
-    int wsum[kSelWaves];
-    uint32_t wmax[kSelWaves], wmin[kSelWaves];
-    int digit, above, cnt;
-};
-
-// After the histogram L.hist[0 .. nb) is complete (and a barrier): the bin
-// where the candidates in larger bins first reach `need` -- its index, the
-// count in larger bins and its own count, the same in every thread.
-__device__ __forceinline__ void find_bin(int nb, int need, RadixLds& L, int* digit, int* above, int* cnt) {
-    const int tid = threadIdx.x;
-    const int lane = tid % MOE_WAVE, wave = tid / MOE_WAVE;
-    const int nbt = nb / 2;  // thread tid owns the bins nb-1-2 tid and nb-2-2 tid (descending)
-    const int b1 = nb - 1 - 2 * tid, b2 = nb - 2 - 2 * tid;
-    const int h1 = tid < nbt ? L.hist[b1] : 0;
-    const int h2 = tid < nbt ? L.hist[b2] : 0;
-    const int loc = h1 + h2;
-    int incl = loc;
-#pragma unroll
-    for (int d = 1; d < MOE_WAVE; d <<= 1) {
-        const int y = __shfl_up(incl, d, MOE_WAVE);
-        if (lane >= d) incl += y;
-    }
-    if (lane == MOE_WAVE - 1) L.wsum[wave] = incl;
-    __syncthreads();
-    int base = 0;
-    for (int x = 0; x < wave; ++x) base += L.wsum[x];
-    const int before = base + incl - loc;  // candidates in larger bins
-    if (tid < nbt) {
-        if (before < need && need <= before + h1) {
-            L.digit = b1;
-            L.above = before;
-            L.cnt = h1;
-        } else if (before + h1 < need && need <= before + loc) {
-            L.digit = b2;
-            L.above = before + h1;
-            L.cnt = h2;
-        }
-    }
-    __syncthreads();
-    *digit = L.digit;
-    *above = L.above;
-    *cnt = L.cnt;
-    __syncthreads();  // L is reused next
-}
-
-// Among the candidates u with (vmask >> u) & 1 (at least `need` of them),
-// the value X such that `need` keys are >= X: returns X and sets *whole when
-// the keys >= X are exactly `need` (else the keys equal to X exceed the
-// demand: ties).  Three digit passes (bits 31..21, 20..10, 9..0), each a
-// histogram of the candidates sharing the digits found so far.  1024 threads.
-__device__ uint32_t radix_kth_largest(const uint32_t (&key)[kSelPer], unsigned vmask, int need, RadixLds& L,
-                                      bool* whole) {
-    const int tid = threadIdx.x;
-    uint32_t prefix = 0, pmask = 0;
-    *whole = false;
-    for (int pass = 0; pass < 3; ++pass) {  // uniform
-        const int shift = pass == 0 ? 21 : (pass == 1 ? 10 : 0);
-        const int nb = pass == 2 ? 1024 : 2048;
-        for (int i = tid; i < nb; i += kSelThreads) L.hist[i] = 0;
-        __syncthreads();
-#pragma unroll
-        for (int u = 0; u < kSelPer; ++u)
-            if (((vmask >> u) & 1u) && (key[u] & pmask) == prefix) atomicAdd(&L.hist[(key[u] >> shift) & (nb - 1)], 1);
-        __syncthreads();
-        int dg, ab, ct;
-        find_bin(nb, need, L, &dg, &ab, &ct);
-        prefix |= (uint32_t)dg << shift;
-        pmask |= (uint32_t)(nb - 1) << shift;
-        need -= ab;
-        if (need == ct) {  // the whole bin is kept (uniform)
-            *whole = true;
-            return prefix;
-        }
-    }
-    return prefix;  // exact value; its keys exceed the demand
-}
-
-template <int CTRL>
-__device__ __forceinline__ uint32_t dpp_u32(uint32_t v) {
-    return (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, CTRL, 0xF, 0xF, false);
-}
-
-// Workgroup maximum and minimum of one value per thread.
-__device__ __forceinline__ void block_max_min(uint32_t mx, uint32_t mn, RadixLds& L, uint32_t* omx, uint32_t* omn) {
-    mx = max(mx, dpp_u32<MOE_DPP_QUAD_XOR1>(mx));
-    mn = min(mn, dpp_u32<MOE_DPP_QUAD_XOR1>(mn));
-    mx = max(mx, dpp_u32<MOE_DPP_QUAD_XOR2>(mx));
-    mn = min(mn, dpp_u32<MOE_DPP_QUAD_XOR2>(mn));
-    mx = max(mx, dpp_u32<MOE_DPP_ROW_HALF_MIRROR>(mx));
-    mn = min(mn, dpp_u32<MOE_DPP_ROW_HALF_MIRROR>(mn));
-    mx = max(mx, dpp_u32<MOE_DPP_ROW_MIRROR>(mx));
-    mn = min(mn, dpp_u32<MOE_DPP_ROW_MIRROR>(mn));
-    uint32_t wmx = 0, wmn = 0xFFFFFFFFu;
-#pragma unroll
-    for (int r = 0; r < 4; ++r) {
-        wmx = max(wmx, (uint32_t)__builtin_amdgcn_readlane((int)mx, 16 * r));
-        wmn = min(wmn, (uint32_t)__builtin_amdgcn_readlane((int)mn, 16 * r));
-    }
-    const int wave = threadIdx.x / MOE_WAVE;
-    if (threadIdx.x % MOE_WAVE == 0) {
-        L.wmax[wave] = wmx;
-        L.wmin[wave] = wmn;
-    }
-    __syncthreads();
-    uint32_t a = 0, b = 0xFFFFFFFFu;
-    for (int x = 0; x < kSelWaves; ++x) {
-        a = max(a, L.wmax[x]);
-        b = min(b, L.wmin[x]);
-    }
-    *omx = a;
-    *omn = b;
-}
-
+// The K best are taken by select_top (select_device.h): bins linear in the
+// score between its minimum and maximum, then inside the threshold bin the
+// score bits and the complement of the tie key e << 19 | j << 5 | s (invalid
+// slots as expert 8191), so that equal scores order by expert id, channel,
+// then slot.
 __global__ void __launch_bounds__(kSelThreads)
 reader_select_kernel(ReaderArgs ra, const int32_t* __restrict__ topk_ids, const float* __restrict__ topk_w, int K,
                      FastDiv fI, int32_t* __restrict__ slot_cnt, int32_t* __restrict__ slot_kept,
@@ -400,203 +276,37 @@ reader_select_kernel(ReaderArgs ra, const int32_t* __restrict__ topk_ids, const 
     __shared__ int se[32];
     __shared__ float sw[32];
     __shared__ RadixLds rl;
-    __shared__ int wsum[kSelWaves];
-    __shared__ int slot_off[33];
     const int t = blockIdx.x;
     const int tid = threadIdx.x;
-    const int I = ra.I, k = ra.k, E = ra.E, nbq = ra.nbq;
+    const int I = ra.I, k = ra.k, E = ra.E;
     const int n = k * I;
-    const float* __restrict__ est = ra.est;
-    const float* __restrict__ dnorm = ra.dnorm;
     if (tid < k) {
         const int e = topk_ids[(size_t)t * k + tid];
         se[tid] = (e >= 0 && e < E) ? e : -1;
         sw[tid] = topk_w[(size_t)t * k + tid];
     }
     __syncthreads();
-    // every load first: the group partials of g and v and the norm of each
-    // candidate -- as 16-byte loads when a thread's 8 candidates are 8
-    // consecutive channels of one slot (I % 8 == 0), else one by one
-    float g[kSelPer], v[kSelPer], dn[kSelPer];
-    if (I % kSelPer == 0) {  // uniform
-        const int ic = min(kSelPer * tid, n - kSelPer);
-        const int s = fI.div(ic), j = ic - s * I;
-        const float* eg = est + (((size_t)t * k + s) * 2 * nbq) * I + j;
-        float4 gq[kMaxGroups][2], vq[kMaxGroups][2], dq[2];
-#pragma unroll
-        for (int q = 0; q < kMaxGroups; ++q) {
-#pragma unroll
-            for (int h2 = 0; h2 < 2; ++h2) {
-                gq[q][h2] = *reinterpret_cast<const float4*>(eg + (size_t)min(q, nbq - 1) * I + 4 * h2);
-                vq[q][h2] = *reinterpret_cast<const float4*>(eg + (size_t)(nbq + min(q, nbq - 1)) * I + 4 * h2);
-            }
-        }
-#pragma unroll
-        for (int h2 = 0; h2 < 2; ++h2)
-            dq[h2] = *reinterpret_cast<const float4*>(dnorm + (size_t)max(se[s], 0) * I + j + 4 * h2);
-#pragma unroll
-        for (int u = 0; u < kSelPer; ++u) {
-            const int h2 = u / 4, c4 = u % 4;
-            auto comp = [&](const float4& f) { return c4 == 0 ? f.x : (c4 == 1 ? f.y : (c4 == 2 ? f.z : f.w)); };
-            g[u] = comp(gq[0][h2]);
-            v[u] = comp(vq[0][h2]);
-#pragma unroll
-            for (int q = 1; q < kMaxGroups; ++q) {
-                g[u] += q < nbq ? comp(gq[q][h2]) : 0.f;
-                v[u] += q < nbq ? comp(vq[q][h2]) : 0.f;
-            }
-            dn[u] = comp(dq[h2]);
-        }
-    } else {
-        float gp[kSelPer][kMaxGroups], vp[kSelPer][kMaxGroups];
-#pragma unroll
-        for (int u = 0; u < kSelPer; ++u) {
-            const int ic = min(kSelPer * tid + u, n - 1);
-            const int s = fI.div(ic), j = ic - s * I;
-            const float* eg = est + (((size_t)t * k + s) * 2 * nbq) * I + j;
-#pragma unroll
-            for (int q = 0; q < kMaxGroups; ++q) {
-                gp[u][q] = eg[(size_t)min(q, nbq - 1) * I];
-                vp[u][q] = eg[(size_t)(nbq + min(q, nbq - 1)) * I];
-            }
-            dn[u] = dnorm[(size_t)max(se[s], 0) * I + j];
-        }
-#pragma unroll
-        for (int u = 0; u < kSelPer; ++u) {
-            g[u] = gp[u][0];
-            v[u] = vp[u][0];
-#pragma unroll
-            for (int q = 1; q < kMaxGroups; ++q) {
-                g[u] += q < nbq ? gp[u][q] : 0.f;
-                v[u] += q < nbq ? vp[u][q] : 0.f;
-            }
-        }
-    }
-    uint32_t sb[kSelPer];  // score bits
-    uint32_t tb[kSelPer];  // tie keys
-    unsigned vmask = 0;    // real candidates
-    uint32_t smax = 0, smin = 0xFFFFFFFFu;
-#pragma unroll
-    for (int u = 0; u < kSelPer; ++u) {
-        const int idx = kSelPer * tid + u;
-        const int ic = min(idx, n - 1);
-        const int s = fI.div(ic), j = ic - s * I;
-        const int e = se[s];
-        float sc = (sw[s] * dn[u]) * fabsf(silu_mul(g[u], v[u]));
-        if (!(sc >= 0.f) || e < 0) sc = 0.f;  // NaN, invalid slot
-        sc += 0.f;                          // -0 as +0
-        if (idx < n) {
-            if (est_out) {
-                est_out[(((size_t)t * k + s) * 2 + 0) * I + j] = g[u];
-                est_out[(((size_t)t * k + s) * 2 + 1) * I + j] = v[u];
-            }
-            if (score_out) score_out[((size_t)t * k + s) * I + j] = sc;
-        }
-        sb[u] = idx < n ? __float_as_uint(sc) : 0u;
-        tb[u] = ((uint32_t)(e < 0 ? 8191 : e) << 19) | ((uint32_t)j << 5) | (uint32_t)s;
-        vmask |= idx < n ? (1u << u) : 0u;
-        if (idx < n) {
-            smax = max(smax, sb[u]);
-            smin = min(smin, sb[u]);
-        }
-    }
+    uint32_t sb[kSelPer], tb[kSelPer], smax, smin;
+    unsigned vmask;
+    reader_scores(ra, t, fI, se, sw, sb, tb, vmask, smax, smin, est_out, score_out);
     const bool all = K >= n;
-    // First pass over 2048 bins linear in the score between the minimum and
-    // the maximum (monotone in the score, and spread where the bit patterns
-    // would crowd into a few exponents); then the exact select among the
-    // candidates of the threshold bin only.
-    int bin[kSelPer] = {0, 0, 0, 0, 0, 0, 0, 0};
-    int B = 0;                     // threshold bin: bins above are kept, below dropped
-    uint32_t T = 0, M = 0xFFFFFFFFu;  // inside bin B: score threshold, largest tie key kept
-    bool exact = true;
+    unsigned kmask = vmask;
     if (!all) {
         uint32_t mx, mn;
-        block_max_min(smax, smin, rl, &mx, &mn);
-        const float fmn = __uint_as_float(mn), d = __uint_as_float(mx) - fmn;
-        float scl = d > 0.f ? (float)kRadixBins / d : 0.f;
-        if (!(scl < INFINITY)) scl = 0.f;  // a range too small (or infinite): one bin
-        for (int i = tid; i < kRadixBins; i += kSelThreads) rl.hist[i] = 0;
-        __syncthreads();
+        block_max_min(smax, smin, rl, &mx, &mn);  // non-negative scores: bits order like values
+        const float lo = __uint_as_float(mn);
+        const float scl = linear_scale(lo, __uint_as_float(mx), kRadixBins);
+        int bin[kSelPer];
+        uint32_t key[2][kSelPer];
 #pragma unroll
         for (int u = 0; u < kSelPer; ++u) {
-            const float f = (__uint_as_float(sb[u]) - fmn) * scl;
-            bin[u] = f < (float)(kRadixBins - 1) ? (int)f : kRadixBins - 1;
-            if ((vmask >> u) & 1u) atomicAdd(&rl.hist[bin[u]], 1);
+            bin[u] = linear_bin(__uint_as_float(sb[u]), lo, scl, kRadixBins);
+            key[0][u] = sb[u];
+            key[1][u] = ~tb[u];
         }
-        __syncthreads();
-        int ab, ct;
-        find_bin(kRadixBins, K, rl, &B, &ab, &ct);
-        const int need = K - ab;
-        if (need != ct) {
-            unsigned bmask = 0;
-#pragma unroll
-            for (int u = 0; u < kSelPer; ++u) bmask |= (((vmask >> u) & 1u) && bin[u] == B) ? (1u << u) : 0u;
-            T = radix_kth_largest(sb, bmask, need, rl, &exact);
-            if (!exact) {  // the scores equal to T: their ties in tie-key order
-                int gtc = 0;
-                unsigned eqmask = 0;
-                uint32_t ntb[kSelPer];
-#pragma unroll
-                for (int u = 0; u < kSelPer; ++u) {
-                    gtc += ((bmask >> u) & 1u) && sb[u] > T ? 1 : 0;
-                    eqmask |= (((bmask >> u) & 1u) && sb[u] == T) ? (1u << u) : 0u;
-                    ntb[u] = ~tb[u];
-                }
-                if (tid == 0) rl.cnt = 0;
-                __syncthreads();
-                if (gtc) atomicAdd(&rl.cnt, gtc);
-                __syncthreads();
-                const int need2 = need - rl.cnt;
-                __syncthreads();
-                bool w2;
-                M = ~radix_kth_largest(ntb, eqmask, need2, rl, &w2);  // the need2-th smallest tie key
-            }
-        }
+        kmask = select_top<2>(bin, key, vmask, K, rl);
     }
-    unsigned kmask = 0;
-#pragma unroll
-    for (int u = 0; u < kSelPer; ++u) {
-        const bool kept = ((vmask >> u) & 1u) &&
-                          (all || bin[u] > B ||
-                           (bin[u] == B && (sb[u] > T || (sb[u] == T && (exact || tb[u] <= M)))));
-        kmask |= kept ? (1u << u) : 0u;
-    }
-    // positions in candidate order: exclusive scan of the counts
-    const int cntk = __builtin_popcount(kmask);
-    const int lane = tid % MOE_WAVE, wave = tid / MOE_WAVE;
-    int incl = cntk;
-#pragma unroll
-    for (int d = 1; d < MOE_WAVE; d <<= 1) {
-        const int y = __shfl_up(incl, d, MOE_WAVE);
-        if (lane >= d) incl += y;
-    }
-    if (lane == MOE_WAVE - 1) wsum[wave] = incl;
-    __syncthreads();
-    int base = 0;
-    for (int x = 0; x < wave; ++x) base += wsum[x];
-    int pos = base + incl - cntk;
-    // the first kept position of every slot: the slot's first candidate's owner
-#pragma unroll
-    for (int u = 0; u < kSelPer; ++u) {
-        const int idx = kSelPer * tid + u;
-        if (idx < n && fI.mod(idx) == 0) slot_off[fI.div(idx)] = pos + __builtin_popcount(kmask & ((1u << u) - 1u));
-    }
-    if (tid == 0) slot_off[k] = all ? n : K;
-    __syncthreads();
-#pragma unroll
-    for (int u = 0; u < kSelPer; ++u) {
-        const int idx = kSelPer * tid + u;
-        if (idx >= n) continue;
-        const int s = fI.div(idx), j = idx - s * I;
-        const bool kept = (kmask >> u) & 1u;
-        ra.kept_flag[((size_t)t * k + s) * I + j] = kept ? 1 : 0;
-        if (kept) {
-            if (kept_out) kept_out[(size_t)t * K + pos] = idx;
-            slot_kept[((size_t)t * k + s) * I + (pos - slot_off[s])] = j;
-            ++pos;
-        }
-    }
-    if (tid < k) slot_cnt[(size_t)t * k + tid] = slot_off[tid + 1] - slot_off[tid];
+    emit_kept(kmask, t, k, I, K, all, fI, rl, slot_cnt, slot_kept, kept_out, ra.kept_flag);
 }
 
 // ---------------------------------------------------------------------------

@@ -5,11 +5,14 @@
 #pragma once
 
 #include "device_common.h"
+#include "launch.h"
+#include "select_device.h"
 
 namespace moe {
 
 constexpr int kReaderBlock = 128;  // rotation block (coordinates)
 constexpr int kReaderScan = 80;    // coordinates scanned per block
+constexpr int kReaderMaxGroups = 2;  // block groups of the screening (partial estimates per channel)
 
 // # of the wave's 128 keys (two per lane) at or above c.
 __device__ __forceinline__ int count_at_least(uint64_t ka, uint64_t kb, uint64_t c) {
@@ -96,6 +99,111 @@ __device__ __forceinline__ void rotate_scan_wave(const float* __restrict__ hb, c
     if (sb) {
         sel[pa + (sa ? 1 : 0)] = (uint8_t)(2 * lane + 1);
         val[pa + (sa ? 1 : 0)] = (float)b;
+    }
+}
+
+// Per-candidate scores of the reader for one token (thread tid, candidates
+// idx = 8 tid .. 8 tid + 7 = s * I + j): g_hat and v_hat as the screening's
+// group partials added in order, then the score (w_s * ||d_j||) *
+// |SiLU(g_hat) v_hat| in fp32 (NaN and invalid slots score 0, -0 as +0) as
+// its bit pattern sb (non-negative: it orders like the value) and the tie
+// key tb = e << 19 | j << 5 | s (invalid slots as expert 8191).  Also the
+// mask of real candidates and the largest and smallest score bits; est_out
+// and score_out (nullable) receive g_hat, v_hat and the score.  se / sw: the
+// token's expert ids (-1 when invalid) and affinities, in LDS.
+__device__ inline void reader_scores(const ReaderArgs& ra, int t, FastDiv fI, const int* se, const float* sw,
+                                     uint32_t (&sb)[kSelPer], uint32_t (&tb)[kSelPer], unsigned& vmask,
+                                     uint32_t& smax, uint32_t& smin, float* __restrict__ est_out,
+                                     float* __restrict__ score_out) {
+    const int tid = threadIdx.x;
+    const int I = ra.I, k = ra.k, nbq = ra.nbq;
+    const int n = k * I;
+    const float* __restrict__ est = ra.est;
+    const float* __restrict__ dnorm = ra.dnorm;
+    // every load first: the group partials of g and v and the norm of each
+    // candidate -- as 16-byte loads when a thread's 8 candidates are 8
+    // consecutive channels of one slot (I % 8 == 0), else one by one
+    float g[kSelPer], v[kSelPer], dn[kSelPer];
+    if (I % kSelPer == 0) {  // uniform
+        const int ic = min(kSelPer * tid, n - kSelPer);
+        const int s = fI.div(ic), j = ic - s * I;
+        const float* eg = est + (((size_t)t * k + s) * 2 * nbq) * I + j;
+        float4 gq[kReaderMaxGroups][2], vq[kReaderMaxGroups][2], dq[2];
+#pragma unroll
+        for (int q = 0; q < kReaderMaxGroups; ++q) {
+#pragma unroll
+            for (int h2 = 0; h2 < 2; ++h2) {
+                gq[q][h2] = *reinterpret_cast<const float4*>(eg + (size_t)min(q, nbq - 1) * I + 4 * h2);
+                vq[q][h2] = *reinterpret_cast<const float4*>(eg + (size_t)(nbq + min(q, nbq - 1)) * I + 4 * h2);
+            }
+        }
+#pragma unroll
+        for (int h2 = 0; h2 < 2; ++h2)
+            dq[h2] = *reinterpret_cast<const float4*>(dnorm + (size_t)max(se[s], 0) * I + j + 4 * h2);
+#pragma unroll
+        for (int u = 0; u < kSelPer; ++u) {
+            const int h2 = u / 4, c4 = u % 4;
+            auto comp = [&](const float4& f) { return c4 == 0 ? f.x : (c4 == 1 ? f.y : (c4 == 2 ? f.z : f.w)); };
+            g[u] = comp(gq[0][h2]);
+            v[u] = comp(vq[0][h2]);
+#pragma unroll
+            for (int q = 1; q < kReaderMaxGroups; ++q) {
+                g[u] += q < nbq ? comp(gq[q][h2]) : 0.f;
+                v[u] += q < nbq ? comp(vq[q][h2]) : 0.f;
+            }
+            dn[u] = comp(dq[h2]);
+        }
+    } else {
+        float gp[kSelPer][kReaderMaxGroups], vp[kSelPer][kReaderMaxGroups];
+#pragma unroll
+        for (int u = 0; u < kSelPer; ++u) {
+            const int ic = min(kSelPer * tid + u, n - 1);
+            const int s = fI.div(ic), j = ic - s * I;
+            const float* eg = est + (((size_t)t * k + s) * 2 * nbq) * I + j;
+#pragma unroll
+            for (int q = 0; q < kReaderMaxGroups; ++q) {
+                gp[u][q] = eg[(size_t)min(q, nbq - 1) * I];
+                vp[u][q] = eg[(size_t)(nbq + min(q, nbq - 1)) * I];
+            }
+            dn[u] = dnorm[(size_t)max(se[s], 0) * I + j];
+        }
+#pragma unroll
+        for (int u = 0; u < kSelPer; ++u) {
+            g[u] = gp[u][0];
+            v[u] = vp[u][0];
+#pragma unroll
+            for (int q = 1; q < kReaderMaxGroups; ++q) {
+                g[u] += q < nbq ? gp[u][q] : 0.f;
+                v[u] += q < nbq ? vp[u][q] : 0.f;
+            }
+        }
+    }
+    vmask = 0;
+    smax = 0;
+    smin = 0xFFFFFFFFu;
+#pragma unroll
+    for (int u = 0; u < kSelPer; ++u) {
+        const int idx = kSelPer * tid + u;
+        const int ic = min(idx, n - 1);
+        const int s = fI.div(ic), j = ic - s * I;
+        const int e = se[s];
+        float sc = (sw[s] * dn[u]) * fabsf(silu_mul(g[u], v[u]));
+        if (!(sc >= 0.f) || e < 0) sc = 0.f;  // NaN, invalid slot
+        sc += 0.f;                          // -0 as +0
+        if (idx < n) {
+            if (est_out) {
+                est_out[(((size_t)t * k + s) * 2 + 0) * I + j] = g[u];
+                est_out[(((size_t)t * k + s) * 2 + 1) * I + j] = v[u];
+            }
+            if (score_out) score_out[((size_t)t * k + s) * I + j] = sc;
+        }
+        sb[u] = idx < n ? __float_as_uint(sc) : 0u;
+        tb[u] = ((uint32_t)(e < 0 ? 8191 : e) << 19) | ((uint32_t)j << 5) | (uint32_t)s;
+        vmask |= idx < n ? (1u << u) : 0u;
+        if (idx < n) {
+            smax = max(smax, sb[u]);
+            smin = min(smin, sb[u]);
+        }
     }
 }
 

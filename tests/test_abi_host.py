@@ -73,6 +73,9 @@ FAKE = 0x10000  # 16-byte aligned fake address: never dereferenced by host check
     (dict(wformat=1, vq_d=3, vq_K=256, lr_r=64), 2), (dict(wformat=1, H=4096, vq_d=2, vq_K=256, lr_r=64), 2),
     (dict(wformat=1, vq_d=8, vq_K=257, lr_r=64), 2), (dict(wformat=1, vq_d=8, vq_K=256, lr_r=60), 2),
     (dict(max_keep=8 * 768 + 1), 2), (dict(wformat=1, vq_d=8, vq_K=256, lr_r=64, max_keep=10), 2),
+    (dict(reader=2, max_keep=10), 1), (dict(rec_rank=-8, reader=1, max_keep=10), 1),
+    (dict(reader=1), 2), (dict(reader=1, max_keep=10, H=2040), 2), (dict(rec_rank=32, max_keep=10), 2),
+    (dict(reader=1, max_keep=10, rec_rank=12), 2), (dict(reader=1, max_keep=10, rec_rank=40), 2),
 ])
 def test_create_rejects_bad_configs_before_any_gpu_call(mb, kw, status):
     cfg = base_cfg(mb, **kw)
@@ -94,7 +97,15 @@ def test_create_rejects_missing_or_misaligned_weights(mb):
     assert mb.moe_create_status(vq, mb.make_weights(FAKE, FAKE, **bad))[0] == 1
     keep = base_cfg(mb, max_keep=799)
     assert mb.moe_create_status(keep, mb.make_weights(FAKE, FAKE, w_gate=FAKE, w_up=FAKE))[0] == 1  # no norms
-    assert mb.moe_create_status(keep, mb.make_weights(FAKE, FAKE, w_gate=FAKE, w_up=FAKE, chan_norm=FAKE))[0] == 1
+    assert mb.moe_create_status(keep, mb.make_weights(FAKE, FAKE, w_gate=FAKE, w_up=FAKE,
+                                                      chan_norm=FAKE + 4))[0] == 1  # norms read 16 bytes at a time
+    rd = base_cfg(mb, max_keep=756, reader=1, rec_rank=32)
+    full = dict(w_gate=FAKE, w_up=FAKE, rot_signs=FAKE, sketch=FAKE, sketch_scale=FAKE, down_norm=FAKE,
+                rec_basis=FAKE, rec_coef=FAKE)
+    for name, val in (("rot_signs", None), ("sketch", None), ("sketch", FAKE + 8), ("sketch_scale", None),
+                      ("down_norm", None), ("down_norm", FAKE + 4), ("rec_basis", None), ("rec_coef", None),
+                      ("rec_coef", FAKE + 2)):
+        assert mb.moe_create_status(rd, mb.make_weights(FAKE, FAKE, **dict(full, **{name: val})))[0] == 1, name
     assert mb.moe_create_status(None, mb.make_weights(FAKE, FAKE))[0] == 1
 
 
@@ -111,10 +122,6 @@ def test_calls_on_null_context_fail_closed(mb):
     assert lib.moe_channel_norms(ctypes.byref(cfg), None, FAKE, FAKE, FAKE, None) == 1
     bad = base_cfg(mb, H=2044)
     assert lib.moe_channel_norms(ctypes.byref(bad), FAKE, FAKE, FAKE, FAKE, None) == 2
-    assert lib.moe_channel_ranks(ctypes.byref(cfg), None, FAKE, None) == 1
-    assert lib.moe_channel_ranks(ctypes.byref(cfg), FAKE, None, None) == 1
-    assert lib.moe_channel_ranks(None, FAKE, FAKE, None) == 1
-    assert lib.moe_channel_ranks(ctypes.byref(base_cfg(mb, I=8193)), FAKE, FAKE, None) == 2
 
 
 # ---------------------------------------------------------------- plan validator
@@ -250,3 +257,22 @@ def test_workspace_bytes_at_the_accepted_limits():
     # rejected configurations report -1
     assert mb.moe_workspace_bytes(mb.make_config(4096, 16384, 1024, 8, 8, 512), 512) == -1
     assert mb.moe_workspace_bytes(mb.make_config(2048, 768, 128, 8, 8, 1), 0) == -1
+
+
+def test_reader_load_time_entry_points_check_arguments(mb):
+    """Host-side checks of the reader's load-time calls (no GPU needed)."""
+    lib = mb._lib
+    assert mb.moe_sketch_row_bytes(768) == 160  # ceil(768 / 5) = 154 bytes, padded to 16
+    assert mb.moe_sketch_row_bytes(5) == 16 and mb.moe_sketch_row_bytes(0) == -1
+    cfg = base_cfg(mb)
+    assert lib.moe_reader_sketch(ctypes.byref(cfg), FAKE, FAKE, None, FAKE, FAKE, None) == 1
+    assert lib.moe_reader_sketch(ctypes.byref(base_cfg(mb, H=2056)), FAKE, FAKE, FAKE, FAKE, FAKE, None) == 2
+    assert lib.moe_reader_sketch(None, FAKE, FAKE, FAKE, FAKE, FAKE, None) == 1
+    assert lib.moe_down_norms(ctypes.byref(cfg), FAKE + 8, FAKE, None) == 1
+    assert lib.moe_recovery_basis(ctypes.byref(cfg), FAKE, 0, 10, FAKE, None) == 1
+    assert lib.moe_recovery_basis(ctypes.byref(cfg), FAKE, 33, 10, FAKE, None) == 1
+    assert lib.moe_recovery_basis(ctypes.byref(cfg), FAKE, 32, 0, FAKE, None) == 1
+    assert lib.moe_recovery_basis(ctypes.byref(base_cfg(mb, H=2056)), FAKE, 32, 10, FAKE, None) == 2
+    assert lib.moe_recovery_coefs(ctypes.byref(cfg), FAKE, 12, FAKE, FAKE, None) == 1
+    assert lib.moe_recovery_coefs(ctypes.byref(cfg), FAKE, 32, FAKE, FAKE + 2, None) == 1
+    assert lib.moe_reader_inspect(None, FAKE, 1, FAKE, FAKE, 10, None, None, None, None, None, None) == 1

@@ -38,14 +38,12 @@ def say(*a):
 
 
 def channel_tables(mb, cfg, dev):
-    """Load-time tables of the channel-sparse mode, computed on the device:
-    the static channel norms and each channel's rank in its expert."""
+    """Load-time table of the channel-sparse mode, computed on the device:
+    the static channel norms."""
     import torch
     norms = torch.empty((cfg.E, cfg.I), dtype=torch.float32, device="cuda")
-    ranks = torch.empty((cfg.E, cfg.I), dtype=torch.int32, device="cuda")
     mb.moe_channel_norms(cfg, dev["w_gate"], dev["w_up"], dev["w_down"], norms)
-    mb.moe_channel_ranks(cfg, norms, ranks)
-    dev["chan_norm"], dev["chan_rank"] = norms, ranks
+    dev["chan_norm"] = norms
     return norms
 
 
@@ -226,7 +224,6 @@ def test_chansparse_keep799(mb):
     sel = list(range(0, wl.E, 9))
     ulp = np.abs(gn[sel].view(np.int32).astype(np.int64) - ref_n[sel].view(np.int32).astype(np.int64))
     assert ulp.max() <= 1, "norms differ by %d ulp" % ulp.max()
-    np.testing.assert_array_equal(dev["chan_rank"].cpu().numpy(), ref_ranks(gn))
     layer = mb.Layer(cfg, dev)
     for step in range(2):
         h = synth.hidden(wl, 0, step)
@@ -247,23 +244,10 @@ def test_chansparse_keep799(mb):
     layer.close()
 
 
-def ref_ranks(norms: np.ndarray) -> np.ndarray:
-    """Each channel's position when its expert's channels are ordered by
-    decreasing norm, ties to the lower channel (test-side reference)."""
-    E, I = norms.shape
-    out = np.empty((E, I), np.int64)
-    for e in range(E):
-        order = np.lexsort((np.arange(I), -norms[e].astype(np.float64)))
-        out[e, order] = np.arange(I)
-    return out
-
-
-def test_channel_ranks_and_exact_selection(mb):
-    """moe_channel_ranks against a reference ordering; the selection against the
-    oracle's top K with correct ranks, with ranks that do not match the norms
-    (zeros, reversed, a random permutation, out of range), with caller
-    affinities that are zero, negative or equal, with tied norms and with one
-    expert in two slots."""
+def test_channel_exact_selection(mb):
+    """The selection against the oracle's top K, with caller affinities that
+    are zero, negative or equal, with tied norms (a whole expert at one value,
+    pairs of equal channels) and with one expert in two slots."""
     import torch
     wl = synth.small_workload("cs_ranks", H=256, I=96, E=16, k=4, M=3, seed=61)
     M, I, k = wl.M, wl.I, wl.k
@@ -274,7 +258,6 @@ def test_channel_ranks_and_exact_selection(mb):
     cfg = mb.make_config(wl.H, I, wl.E, k, 8, M, max_keep=k * I)
     norms = channel_tables(mb, cfg, dev)
     torch.cuda.synchronize()
-    np.testing.assert_array_equal(dev["chan_rank"].cpu().numpy(), ref_ranks(norms.cpu().numpy()))
     layer = mb.Layer(cfg, dev)
     layer.route(h, M)
     torch.cuda.synchronize()
@@ -297,17 +280,6 @@ def test_channel_ranks_and_exact_selection(mb):
     ref_y = O.channel_sparse_forward(h_np, ids, w.astype(np.float64), inp["w_gate"], inp["w_up"], inp["w_down"], kept)
     say("  keep 150:", check_close(layer.y[:M].cpu().numpy(), ref_y))
 
-    good = dev["chan_rank"].clone()
-    rng = np.random.default_rng(5)
-    for what, bad in (("zeros", torch.zeros_like(good)), ("reversed", I - 1 - good),
-                      ("random permutation", torch.from_numpy(np.stack([rng.permutation(I) for _ in range(wl.E)])
-                                                              .astype(np.int32)).cuda()),
-                      ("out of range", torch.where(good % 3 == 0, good + 5000, good - 7))):
-        say("  ranks:", what)
-        dev["chan_rank"].copy_(bad)
-        select(150)
-    dev["chan_rank"].copy_(good)
-
     w2 = w.copy()
     w2[0, 1] = 0.0
     w2[1, 0] = -w2[1, 0]
@@ -328,9 +300,7 @@ def test_channel_ranks_and_exact_selection(mb):
     tied[int(ids[0, 0])] = 0.5
     tied[int(ids[0, 1]), 1::2] = tied[int(ids[0, 1]), 0::2]
     norms.copy_(tied)
-    mb.moe_channel_ranks(cfg, norms, dev["chan_rank"])
     torch.cuda.synchronize()
-    np.testing.assert_array_equal(dev["chan_rank"].cpu().numpy(), ref_ranks(norms.cpu().numpy()))
     for keep in (60, 150, 300):
         select(keep)
     layer.close()
@@ -338,10 +308,10 @@ def test_channel_ranks_and_exact_selection(mb):
 
 @pytest.mark.parametrize("case", ["n8192_k8", "k1", "k32", "k3_i700"])
 def test_channel_selection_shapes(mb, case):
-    """The selection at its size limits: k * I = 8192 candidates (the largest
-    list LDS), one slot, 32 slots (rank sums over 32-lane groups) and a slot
-    count that is not a power of two (rank sums through LDS); kept lists
-    against the oracle's, y within tolerance, both entry points."""
+    """The selection at its size limits: k * I = 8192 candidates (every
+    thread's eight), one slot, 32 slots, and a channel count that is not a
+    multiple of 8 (candidates of one thread in two slots); kept lists against
+    the oracle's, y within tolerance, both entry points."""
     import torch
     shape = {"n8192_k8": dict(H=256, I=1024, E=16, k=8, M=2, keep=1100),
              "k1": dict(H=264, I=200, E=8, k=1, M=3, keep=37),
@@ -748,9 +718,7 @@ for name, keep in [("tiny_h256_i128_e16_k2", 0), ("dense_h2048_i768_e128_k8_m1",
         cfg = mb.make_config(wl.H, wl.I, wl.E, wl.k, wl.block_b, wl.M, max_keep=keep)
     if keep:
         dev['chan_norm'] = torch.empty((wl.E, wl.I), dtype=torch.float32, device='cuda')
-        dev['chan_rank'] = torch.empty((wl.E, wl.I), dtype=torch.int32, device='cuda')
         mb.moe_channel_norms(cfg, dev['w_gate'], dev['w_up'], dev['w_down'], dev['chan_norm'])
-        mb.moe_channel_ranks(cfg, dev['chan_norm'], dev['chan_rank'])
     layer = mb.Layer(cfg, dev)
     y = layer.decode_step(to_dev(inp['h']), wl.M, keep=keep)
     torch.cuda.synchronize()

@@ -81,9 +81,7 @@ def test_noalloc_decode_step_equals_context_call(mb, name, max_tokens, M1, M2, k
     cfg = _cfg(mb, wl, max_tokens, keep)
     if keep:
         dev["chan_norm"] = torch.empty((wl.E, wl.I), dtype=torch.float32, device="cuda")
-        dev["chan_rank"] = torch.empty((wl.E, wl.I), dtype=torch.int32, device="cuda")
         mb.moe_channel_norms(cfg, dev["w_gate"], dev["w_up"], dev["w_down"], dev["chan_norm"])
-        mb.moe_channel_ranks(cfg, dev["chan_norm"], dev["chan_rank"])
     layer = mb.Layer(cfg, dev)
     hs = to_dev(np.concatenate([synth.hidden(wl, 0, step=s, M=1) for s in range(M1)]))
     for M in (M1, M2):
