@@ -111,7 +111,9 @@ KERNEL_SOURCES = {
     "gateup": ["memory_bound_routed_amd/csrc/dense.hip", "memory_bound_routed_amd/csrc/device_common.h"],
     "down": ["memory_bound_routed_amd/csrc/dense.hip", "memory_bound_routed_amd/csrc/device_common.h"],
     "gateup_vqlr": ["memory_bound_routed_amd/csrc/vqlr.hip", "memory_bound_routed_amd/csrc/device_common.h"],
-    "chan_gather": ["memory_bound_routed_amd/csrc/chansparse.hip", "memory_bound_routed_amd/csrc/device_common.h"],
+    "chan_gather": ["memory_bound_routed_amd/csrc/chansparse.hip", "memory_bound_routed_amd/csrc/device_common.h",
+                    "memory_bound_routed_amd/csrc/select_device.h", "memory_bound_routed_amd/csrc/reader_device.h",
+                    "memory_bound_routed_amd/csrc/topk_device.h"],
     "reader_screen": ["memory_bound_routed_amd/csrc/reader.hip", "memory_bound_routed_amd/csrc/device_common.h",
                       "memory_bound_routed_amd/csrc/topk_device.h"],
 }
@@ -143,8 +145,8 @@ def _pmc_rows(path, counter):
 # rocprofv3 kernel-name fragment of each library kernel whose traffic is taken
 # (decode_fused is the routing instance of the fused expert kernel).
 ROCPROF_NAME = {"expert_fused": "expert_fused_kernel", "decode_fused": "expert_fused_kernel",
-                "gateup": "gateup_dense_kernel", "down": "down_kernel", "gateup_vqlr": "gateup_vqlr_kernel",
-                "chan_gather": "chan_gather_kernel", "reader_screen": "reader_screen_kernel"}
+                "gateup": "gateup_dense_kernel", "down": "down_kernel", "gateup_vqlr": "gateup_vqt_kernel",
+                "chan_gather": "chan_topk_gather_kernel", "reader_screen": "reader_screen_kernel"}
 
 
 def traffic_from_counters(fetch_csv, write_csv, workload, kernel="decode_fused"):
@@ -368,10 +370,12 @@ def main():
     ap.add_argument("--traffic-from", nargs=2, metavar=("FETCH_CSV", "WRITE_CSV"),
                     help="host only: turn two rocprofv3 --pmc counter CSVs of --counter-pass into "
                          "profiles/traffic_<kernel>_<workload>.json")
+    ap.add_argument("--traffic-kernel", default="decode_fused", choices=sorted(ROCPROF_NAME),
+                    help="the kernel whose dispatches --traffic-from reads")
     args = ap.parse_args()
 
     if args.traffic_from:
-        traffic_from_counters(args.traffic_from[0], args.traffic_from[1], args.workload)
+        traffic_from_counters(args.traffic_from[0], args.traffic_from[1], args.workload, args.traffic_kernel)
         return
 
     if args.gpus != 1:

@@ -181,6 +181,9 @@ WORKLOADS: Dict[str, Workload] = {w.name: w for w in [
     # the page's VQ-only point (d, r) = (2, 0): no low-rank term
     Workload("vqlr_h2048_i768_e128_k8_m4_d2_K256_r0", H=2048, I=768, E=128, k=8, M=4, seed=1005, vq=True,
              vq_d=2, lr_r=0),
+    # dense bf16 at the VQ workloads' batch of 4: same seed, so the same router,
+    # hidden states and routing as the VQ + low-rank workloads above
+    Workload("dense_h2048_i768_e128_k8_m4", H=2048, I=768, E=128, k=8, M=4, seed=1005),
     # batch 8 and 16 decode (no hot experts): dense bf16 and VQ + low rank
     Workload("dense_h2048_i768_e128_k8_m8", H=2048, I=768, E=128, k=8, M=8, seed=1006),
     Workload("dense_h2048_i768_e128_k8_m16", H=2048, I=768, E=128, k=8, M=16, seed=1007),
