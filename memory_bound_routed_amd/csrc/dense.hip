@@ -25,7 +25,9 @@
 //    transfers during gate/up compute), then writes a down partial
 //    part[route][chunk][:] = sum_{j in chunk} (a_route * p_j) * d_j.
 //  * split (several routes per block): the gate/up kernel writes p, then a
-//    down kernel over 64-row chunks writes the same kind of partial.
+//    down kernel over column blocks writes one full-length partial per route
+//    (256-column blocks on the matrix cores, 128-column blocks on the vector
+//    ALUs).
 // Both feed combine_kernel: y[t] = sum over the token's routes and chunks.
 #include <type_traits>
 
@@ -679,7 +681,8 @@ gateup_dense_kernel(PlanArgs plan, const float* __restrict__ h, int H, int I, co
 // and the RGS row groups are added at the end: by an xor butterfly inside
 // each wave, then the waves in wave order.  Rows that are not routes of the
 // expert (pads) get s = 0 and no output; RT = 2, 4 or 8 accumulators cover
-// the leading rows up to the last route.
+// the leading rows up to the last route.  This is the vector-ALU form; the
+// matrix-core form (down_pass_mfma) computes the same partials.
 constexpr int kDownStage = 1024;  // rows of s staged at a time (32 KiB)
 constexpr int kDownNB = 4;        // weight rows per thread and buffer
 
@@ -818,7 +821,167 @@ __device__ __forceinline__ void down_pass(int e, int H, int I, const uint16_t* _
     __syncthreads();  // dsm is reused by the next pass
 }
 
+// The same product on the matrix cores (bf16 16x16x32, fp32 accumulation)
+// for a pass of up to 8 routes and the CB columns of the workgroup (CB = 128
+// or 256): NCG = CB / 128 column groups of 128, NKG = 4 / NCG channel
+// groups.  Wave w covers columns cb*CB + 128*(w % NCG) + [0, 128) and the K
+// tiles of 32 channels kt = w / NCG, w / NCG + NKG, ... of each stage.  MFMA rows
+// 0..7 are the hi bf16 parts of s = a_i * p[route_i][j] for routes i = 0..7,
+// rows 8..15 their lo parts (s = hi + lo + O(2^-18 |s|)); the weights are
+// exact in bf16.  Lane l loads 16 bytes (8 columns) of each of the 8 rows
+// j0 + 8 (l / 16) + i of the tile at columns 8 (l % 16) .. +7 of the wave's
+// 128; MFMA g (g = 0..7) takes column 8 n + g of lane n = l % 16 from each
+// row -- two rows per register, by byte permutes -- so the 8 products of a
+// tile cover the wave's 128 columns with no transpose in memory.  At the end
+// hi and lo rows are added (lane l + 32 into lane l), then the NKG waves of a
+// column group in wave order, and row i of the result is route i's partial.
+constexpr int kMfmaTile = 32;
+
 template <int CB>
+__device__ __forceinline__ void down_pass_mfma(int e, int H, int I, const uint16_t* __restrict__ Wd,
+                                               const float* __restrict__ p, const int (&rr)[8], const float (&ra)[8],
+                                               uint32_t valid, float* __restrict__ part, float* dsm) {
+    constexpr int NCG = CB / 128, NKG = kWaves / NCG;
+    static_assert((CB == 128 || CB == 256) && kWaves == 4, "column groups of 128 over four waves");
+    typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
+    typedef float f32x4_t __attribute__((ext_vector_type(4)));
+    const int tid = threadIdx.x;
+    const int lane = tid % MOE_WAVE;
+    const int wave = tid / MOE_WAVE;
+    const int chf = wave % NCG, kh = wave / NCG;
+    const int colw = blockIdx.x * CB + 128 * chf;         // the wave's first column
+    const int coll = colw + 8 * (lane % 16);              // this lane's 8 columns
+    const uint16_t* wbase = Wd + (size_t)e * I * H + min(coll, H - 8);
+    const int rsub = 8 * (lane / 16);                     // the lane's 8 rows of a tile
+    // the route this thread stages: s route-major in LDS, dsm[i][j] (i < 8)
+    const int si = tid & 7;
+    int sr = 0;
+    float sa = 0.f;
+#pragma unroll
+    for (int i = 0; i < 8; ++i)
+        if (i == si && ((valid >> i) & 1)) {
+            sr = rr[i];
+            sa = ra[i];
+        }
+    const bool sv = (valid >> si) & 1;
+    f32x4_t acc[8];
+#pragma unroll
+    for (int g = 0; g < 8; ++g) acc[g] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+    uint4 wb[2][8];
+    for (int js = 0; js < I; js += kDownStage) {
+        const int jn = min(kDownStage, I - js);
+        const int nt = (jn + kMfmaTile - 1) / kMfmaTile;  // tiles of the stage
+        auto issue = [&](uint4 (&w)[8], int kt) {
+#pragma unroll
+            for (int i = 0; i < 8; ++i) {
+                const int jl = min(kMfmaTile * kt + rsub + i, jn - 1);
+                w[i] = load_stream16(wbase + (size_t)(js + jl) * H);
+            }
+        };
+        // stage s (the p loads go out before the first weights)
+        constexpr int SPT = kDownStage / (kThreads / 8);
+        float pv[SPT];
+#pragma unroll
+        for (int u = 0; u < SPT; ++u) {
+            const int jj = min((tid >> 3) + (kThreads / 8) * u, jn - 1);
+            pv[u] = p[(size_t)sr * I + js + jj];
+        }
+        if (kh < nt) issue(wb[0], kh);
+        __syncthreads();  // the previous stage's s is no longer read
+#pragma unroll
+        for (int u = 0; u < SPT; ++u) {
+            const int jj = (tid >> 3) + (kThreads / 8) * u;
+            if (jj < nt * kMfmaTile) dsm[si * kDownStage + jj] = (sv && jj < jn) ? sa * pv[u] : 0.f;
+        }
+        __syncthreads();
+        // one tile: A from the staged s of channels kt*32 + rsub .., B from w
+        auto tile = [&](const uint4 (&w)[8], int kt) {
+            // A: row lane % 16 (hi of route m, or lo of route m - 8), channels rsub .. rsub + 7 of the tile
+            const int m = lane % 16;
+            const float4* srow = reinterpret_cast<const float4*>(dsm + (m & 7) * kDownStage + kMfmaTile * kt + rsub);
+            const float4 s0 = srow[0], s1 = srow[1];
+            const float sx[8] = {s0.x, s0.y, s0.z, s0.w, s1.x, s1.y, s1.z, s1.w};
+            uint32_t ak[8];
+#pragma unroll
+            for (int x = 0; x < 8; ++x) {
+                const uint32_t u = __float_as_uint(sx[x]);
+                const uint32_t hi = (u + 0x7FFFu + ((u >> 16) & 1u)) >> 16;  // round to nearest even
+                const float rem = sx[x] - __uint_as_float(hi << 16);
+                const uint32_t ur = __float_as_uint(rem);
+                const uint32_t lo = (ur + 0x7FFFu + ((ur >> 16) & 1u)) >> 16;
+                ak[x] = m < 8 ? hi : lo;
+            }
+            const uint4 aw = make_uint4(ak[0] | (ak[1] << 16), ak[2] | (ak[3] << 16), ak[4] | (ak[5] << 16),
+                                        ak[6] | (ak[7] << 16));
+#pragma unroll
+            for (int g = 0; g < 8; ++g) {
+                // column g of each row: the 16-bit half g % 2 of word g / 2; rows 2t, 2t + 1 into word t
+                const uint32_t sel = (g & 1) ? 0x07060302u : 0x05040100u;
+                auto word = [&](const uint4& v) { return (g >> 1) == 0 ? v.x : ((g >> 1) == 1 ? v.y : ((g >> 1) == 2 ? v.z : v.w)); };
+                const uint4 bw = make_uint4(__builtin_amdgcn_perm(word(w[1]), word(w[0]), sel),
+                                            __builtin_amdgcn_perm(word(w[3]), word(w[2]), sel),
+                                            __builtin_amdgcn_perm(word(w[5]), word(w[4]), sel),
+                                            __builtin_amdgcn_perm(word(w[7]), word(w[6]), sel));
+                acc[g] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8_t, aw),
+                                                                 __builtin_bit_cast(bf16x8_t, bw), acc[g], 0, 0, 0);
+            }
+        };
+        // two register buffers in turn (indices fixed at compile time)
+        for (int kt = kh; kt < nt; kt += 2 * NKG) {  // uniform per wave
+            if (kt + NKG < nt) issue(wb[1], kt + NKG);
+            tile(wb[0], kt);
+            if (kt + NKG < nt) {
+                if (kt + 2 * NKG < nt) issue(wb[0], kt + 2 * NKG);
+                tile(wb[1], kt + NKG);
+            }
+        }
+    }
+    // hi + lo: lane l < 32 holds rows 4 (l / 16) + q (routes), lane l + 32 their lo parts
+#pragma unroll
+    for (int g = 0; g < 8; ++g)
+#pragma unroll
+        for (int q = 0; q < 4; ++q) acc[g][q] += __shfl_xor(acc[g][q], 32, MOE_WAVE);
+    __syncthreads();  // s is no longer read
+    // the other channel groups hand their sums to group 0 (added in wave order)
+    float* red = dsm;  // [NKG - 1][NCG][32 lanes][8 g][4 q]
+    if (kh > 0 && lane < 32) {
+#pragma unroll
+        for (int g = 0; g < 8; ++g)
+            *reinterpret_cast<float4*>(red + ((((kh - 1) * NCG + chf) * 32 + lane) * 8 + g) * 4) =
+                make_float4(acc[g][0], acc[g][1], acc[g][2], acc[g][3]);
+    }
+    __syncthreads();
+    if (kh == 0 && lane < 32 && coll < H) {
+        float o[4][8];
+#pragma unroll
+        for (int g = 0; g < 8; ++g) {
+            o[0][g] = acc[g][0];
+            o[1][g] = acc[g][1];
+            o[2][g] = acc[g][2];
+            o[3][g] = acc[g][3];
+#pragma unroll
+            for (int k2 = 1; k2 < NKG; ++k2) {
+                const float4 v =
+                    *reinterpret_cast<const float4*>(red + ((((k2 - 1) * NCG + chf) * 32 + lane) * 8 + g) * 4);
+                o[0][g] += v.x;
+                o[1][g] += v.y;
+                o[2][g] += v.z;
+                o[3][g] += v.w;
+            }
+        }
+#pragma unroll
+        for (int q = 0; q < 4; ++q) {
+            const int i = 4 * (lane / 16) + q;  // route row
+            if (!((valid >> i) & 1)) continue;
+            float* dst = part + (size_t)rr[i] * H + coll;
+            *reinterpret_cast<float4*>(dst) = make_float4(o[q][0], o[q][1], o[q][2], o[q][3]);
+            *reinterpret_cast<float4*>(dst + 4) = make_float4(o[q][4], o[q][5], o[q][6], o[q][7]);
+        }
+    }
+    __syncthreads();  // dsm is reused by the next pass
+}
+
+template <int CB, bool MFMA>
 __global__ void __launch_bounds__(kThreads)
 down_kernel(PlanArgs plan, int H, int I, const uint16_t* __restrict__ Wd, const float* __restrict__ p,
             const float* __restrict__ topk_w, float* __restrict__ part, int32_t* __restrict__ err) {
@@ -861,7 +1024,9 @@ down_kernel(PlanArgs plan, int H, int I, const uint16_t* __restrict__ Wd, const 
             ra[i] = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(av), q));
         }
         const int nv = 32 - __builtin_clz(valid);  // rows up to the last route
-        if (nv <= 2)
+        if constexpr (MFMA)
+            down_pass_mfma<CB>(e, H, I, Wd, p, rr, ra, valid, part, dsm);
+        else if (nv <= 2)
             down_pass<CB, 2>(e, H, I, Wd, p, rr, ra, valid, part, dsm);
         else if (nv <= 4)
             down_pass<CB, 4>(e, H, I, Wd, p, rr, ra, valid, part, dsm);
@@ -1022,14 +1187,18 @@ hipError_t launch_gateup_dense(const PlanArgs& plan, const float* h, int H, int 
 
 hipError_t launch_down(const PlanArgs& plan, int H, int I, const uint16_t* Wd, const float* p, const float* topk_w,
                        float* part, int32_t* err, hipStream_t stream) {
-    // 256-column blocks when that still gives two workgroups per CU, else 128
+    // 256-column blocks on the matrix cores when that still gives two
+    // workgroups per CU, else 128-column blocks on the vector ALUs (few
+    // experts: there the MFMA pass measured slower, 20.4 vs 19.0 us on four
+    // tokens of top-8 over 128 experts, 2048 x 768, while on 21 tokens the
+    // 256-column MFMA pass took 46.3 us against 54.4 us)
     const size_t lds = (size_t)kDownStage * 8 * sizeof(float);
     if ((size_t)plan.max_blocks * ((H + 255) / 256) >= 512) {
         const dim3 grid((H + 255) / 256, plan.max_blocks);
-        MOE_LAUNCH(down_kernel<256>, grid, dim3(kThreads), lds, stream, plan, H, I, Wd, p, topk_w, part, err);
+        MOE_LAUNCH((down_kernel<256, true>), grid, dim3(kThreads), lds, stream, plan, H, I, Wd, p, topk_w, part, err);
     } else {
         const dim3 grid((H + 127) / 128, plan.max_blocks);
-        MOE_LAUNCH(down_kernel<128>, grid, dim3(kThreads), lds, stream, plan, H, I, Wd, p, topk_w, part, err);
+        MOE_LAUNCH((down_kernel<128, false>), grid, dim3(kThreads), lds, stream, plan, H, I, Wd, p, topk_w, part, err);
     }
     return hipGetLastError();
 }

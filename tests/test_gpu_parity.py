@@ -866,6 +866,38 @@ def test_split_path_forced_hot_expert(mb, b, hot):
     layer.close()
 
 
+@pytest.mark.parametrize("b,hot", [(16, 10), (8, 12), (4, 7)])
+def test_split_down_matrix_cores_forced_hot_expert(mb, b, hot):
+    """The split schedule's 256-column down launch (bf16 MFMA tiles of 32
+    channels, s split into hi and lo bf16 parts) with forced multi-route
+    experts: full 8-route passes, a ragged last channel tile (I = 200) and a
+    partial last column block (H = 2056); checked against the oracle."""
+    import torch
+    M, k, E, H, I = 40, 2, 64, 2056, 200
+    ids = np.zeros((M, k), dtype=np.int64)
+    for t in range(M):
+        ids[t, 0] = 3 if t < hot else 5 + (2 * t) % 9
+        ids[t, 1] = 5 + (2 * t + 1) % 9
+    assert all(len(set(r)) == k for r in ids) and (ids == 3).sum() == hot
+    cap = mb.moe_align_capacity(M, k, E, b)
+    assert (cap // b) * ((H + 255) // 256) >= 512, "shape must take the 256-column launch"
+    wl = synth.small_workload("mfma_hot_%d_%d" % (b, hot), H=H, I=I, E=E, k=k, M=M, seed=131 + b, block_b=b)
+    say("split down matrix cores", dict(b=b, hot=hot, H=H, I=I, E=E, M=M))
+    inp = synth.layer_inputs(wl, 0)
+    inp["h"] = synth.hidden(wl, 0, 0, M=M)
+    layer = make_layer(mb, wl, inp, M)
+    dids = torch.from_numpy(ids.astype(np.int32)).cuda()
+    w = np.tile(np.array([[0.6, 0.4]], dtype=np.float32), (M, 1))
+    dw = torch.from_numpy(w).cuda()
+    layer.align(M, ids=dids)
+    layer.forward(to_dev(inp["h"]), M, ids=dids, w=dw)
+    torch.cuda.synchronize()
+    assert mb.moe_read_device_error(layer.ctx) == 0
+    ref = O.dense_forward(inp["h"], ids, w.astype(np.float64), inp["w_gate"], inp["w_up"], inp["w_down"])
+    check_close(layer.y[:M].cpu().numpy(), ref)
+    layer.close()
+
+
 @pytest.mark.parametrize("b", [8, 4])
 def test_vq_forced_multi_route_experts(mb, b):
     """VQ + low-rank path with nine experts routed more than once (expert 3
