@@ -4,11 +4,14 @@
 // exact compute of the kept channels, down stored transposed so that each
 // d_j is contiguous).
 //
-// The score of candidate (slot s, channel j) is a_s * n[e_s][j]: the exact
-// fp64 product of two fp32 values, so selection needs no rounding decision;
-// one workgroup per token takes the K best exactly (select_device.h), ties to
-// the lower expert id, then channel, then slot.  The gather computes the kept
-// channels exactly and writes chunk partials that the combine adds in order.
+// Two scores.  Static mode: candidate (slot s, channel j) scores a_s *
+// n[e_s][j], the exact fp64 product of two fp32 values, so selection needs no
+// rounding decision.  Reader mode (Stage 2): the output-level score
+// w_s * ||d_j|| * |SiLU(g_hat_j) * v_hat_j| of the sketch estimates, in fp32
+// (reader_device.h).  Every gather workgroup of a token takes the K best
+// exactly (select_device.h), ties to the lower expert id, then channel, then
+// slot, computes its share of the kept channels exactly and writes a chunk
+// partial that the combine adds in order.
 #include <algorithm>
 #include <climits>
 
