@@ -11,11 +11,14 @@
 //   1. a histogram over 2048 bins and a suffix scan: the bin B where the count
 //      of candidates in better bins reaches K (bins above B are kept, bins
 //      below dropped);
-//   2. inside bin B only, a radix select over each key in turn -- digit
-//      passes of up to 11 bits from the highest bit where the candidates'
-//      keys differ (a key on which they all tie is skipped) -- narrowing to
-//      the candidates that tie on the keys so far until the demand is met
-//      exactly.
+//   2. inside bin B only: when B holds at most 256 candidates, they are
+//      listed in LDS and each is kept when fewer than the demand of them
+//      rank above it (keys compared in order); else a radix select over each
+//      key in turn -- digit passes of up to 11 bits from the highest bit
+//      where the candidates' keys differ (a key on which they all tie is
+//      skipped) -- narrowing to the candidates that tie on the keys so far
+//      until the demand is met exactly.  Both keep the same set: the best
+//      `demand` by the keys, the last of which is distinct.
 // The bins (linear_bin between the candidates' minimum and maximum) spread
 // the candidates so that the histogram's LDS atomics seldom meet on one
 // address; the radix passes only see bin B's few candidates.
@@ -29,14 +32,16 @@ constexpr int kSelThreads = 1024;
 constexpr int kSelPer = 8;  // candidates per thread (k * I <= 8192)
 constexpr int kSelWaves = kSelThreads / MOE_WAVE;
 constexpr int kRadixBins = 2048;  // bins of the first pass and of a radix digit pass (11 bits)
+constexpr int kRankList = 256;    // threshold-bin candidates ranked directly (at most)
 
-struct RadixLds {
-    int hist[kRadixBins];
+struct __align__(16) RadixLds {
+    int hist[kRadixBins];  // also the ranked list: [kRankList] x 4 keys, then [kRankList] flags
     int wsum[kSelWaves];
     uint32_t wmax[kSelWaves], wmin[kSelWaves];
-    int digit, above, cnt, total;
+    int digit, above, cnt, total, nlist;
     int slot_off[33];
 };
+static_assert(kRankList * 5 <= kRadixBins, "the ranked list fits in the histogram");
 
 // After the histogram L.hist[0 .. nb) is complete (and a barrier): the bin
 // where the candidates in larger bins first reach `need` -- its index, the
@@ -198,8 +203,10 @@ __device__ __forceinline__ float linear_scale(float lo, float hi, int nbins) {
 template <int NL>
 __device__ unsigned select_top(const int (&bin)[kSelPer], const uint32_t (&key)[NL][kSelPer], unsigned vmask, int K,
                                RadixLds& L) {
+    static_assert(NL >= 1 && NL <= 4, "up to four keys per candidate");
     const int tid = threadIdx.x;
     for (int i = tid; i < kRadixBins; i += kSelThreads) L.hist[i] = 0;
+    if (tid == 0) L.nlist = 0;
     __syncthreads();
 #pragma unroll
     for (int u = 0; u < kSelPer; ++u)
@@ -215,6 +222,60 @@ __device__ unsigned select_top(const int (&bin)[kSelPer], const uint32_t (&key)[
         cand |= (((vmask >> u) & 1u) && bin[u] == B) ? (1u << u) : 0u;
     }
     if (need == ct) return kept | cand;  // the whole bin
+    if (ct <= kRankList) {  // uniform
+        // list bin B's candidates: slots by a wave scan and one LDS atomic
+        // per wave (the order of the list does not matter)
+        uint4* lk = reinterpret_cast<uint4*>(L.hist);  // entry i: its keys
+        int* flag = L.hist + 4 * kRankList;
+        const int lane = tid % MOE_WAVE;
+        int slot0 = 0;
+        if (__ballot(cand != 0u)) {  // uniform per wave
+            const int c = __builtin_popcount(cand);
+            int incl = c;
+#pragma unroll
+            for (int d = 1; d < MOE_WAVE; d <<= 1) {
+                const int y = __shfl_up(incl, d, MOE_WAVE);
+                if (lane >= d) incl += y;
+            }
+            int wbase = 0;
+            if (lane == MOE_WAVE - 1) wbase = atomicAdd(&L.nlist, incl);
+            slot0 = __shfl(wbase, MOE_WAVE - 1, MOE_WAVE) + incl - c;
+#pragma unroll
+            for (int u = 0, sl = slot0; u < kSelPer; ++u) {
+                if (!((cand >> u) & 1u)) continue;
+                uint32_t kk[4] = {0u, 0u, 0u, 0u};
+#pragma unroll
+                for (int lv = 0; lv < NL; ++lv) kk[lv] = key[lv][u];
+                lk[sl++] = make_uint4(kk[0], kk[1], kk[2], kk[3]);
+            }
+        }
+        __syncthreads();
+        if (tid < ct) {  // entry tid: kept when fewer than `need` entries rank above it
+            const uint4 me = lk[tid];
+            const uint32_t mk[4] = {me.x, me.y, me.z, me.w};
+            int rank = 0;
+            for (int j = 0; j < ct; ++j) {
+                const uint4 o = lk[j];
+                const uint32_t ok[4] = {o.x, o.y, o.z, o.w};
+                bool gt = false, eq = true;
+#pragma unroll
+                for (int lv = 0; lv < NL; ++lv) {
+                    gt = gt || (eq && ok[lv] > mk[lv]);
+                    eq = eq && ok[lv] == mk[lv];
+                }
+                rank += gt ? 1 : 0;
+            }
+            flag[tid] = rank < need ? 1 : 0;
+        }
+        __syncthreads();
+#pragma unroll
+        for (int u = 0, sl = slot0; u < kSelPer; ++u) {
+            if (!((cand >> u) & 1u)) continue;
+            kept |= flag[sl++] ? (1u << u) : 0u;
+        }
+        __syncthreads();  // L is reused next
+        return kept;
+    }
 #pragma unroll
     for (int lv = 0; lv < NL; ++lv) {
         // the candidates' range on this key: equal keys need no pass; else
