@@ -215,8 +215,21 @@ reader_screen_kernel(ReaderArgs ra, SelRoute route, const int32_t* __restrict__ 
     const int ch0 = kRangeCh * c + 20 * w;
     const float* scl = ra.scale + (((size_t)ec * 2 + P) * nblk + b) * I;
     float sv[20];
+    if (I % 4 == 0 && ch0 + 20 <= I && (reinterpret_cast<uintptr_t>(ra.scale) & 15u) == 0) {
+        // five 16-byte loads (16-byte aligned: rows of I fp32, offsets of 20 channels); the
+        // screening's time goes into issuing its many small loads, so fewer instructions count
 #pragma unroll
-    for (int m = 0; m < 20; ++m) sv[m] = scl[min(ch0 + m, I - 1)];
+        for (int m4 = 0; m4 < 5; ++m4) {
+            const float4 v = *reinterpret_cast<const float4*>(scl + ch0 + 4 * m4);
+            sv[4 * m4] = v.x;
+            sv[4 * m4 + 1] = v.y;
+            sv[4 * m4 + 2] = v.z;
+            sv[4 * m4 + 3] = v.w;
+        }
+    } else {
+#pragma unroll
+        for (int m = 0; m < 20; ++m) sv[m] = scl[min(ch0 + m, I - 1)];
+    }
     float acc[20];
 #pragma unroll
     for (int m = 0; m < 20; ++m) acc[m] = 0.f;
