@@ -27,6 +27,7 @@ namespace {
 
 constexpr int kThreads = 256;
 constexpr int kWaves = kThreads / MOE_WAVE;
+constexpr int kBufferFlags = 0x00020000;  // fourth word of a raw gfx9 buffer descriptor (32-bit data)
 
 // Order-preserving map of a double score to uint64 (larger score -> larger key).
 __device__ __forceinline__ unsigned long long score_key(double x) {
@@ -182,11 +183,18 @@ chan_topk_gather_kernel(SparseArgs A, FastDiv fI) {
         if (I % kSelPer == 0) {  // uniform
             const int ic = min(kSelPer * tid, n - kSelPer);
             const int s = fI.div(ic), j = ic - s * I;
-            const float* src = A.norms + (size_t)max(se[s], 0) * I + j;
-            const float4 a = *reinterpret_cast<const float4*>(src);
-            const float4 b = *reinterpret_cast<const float4*>(src + 4);
-            nv[0] = a.x; nv[1] = a.y; nv[2] = a.z; nv[3] = a.w;
-            nv[4] = b.x; nv[5] = b.y; nv[6] = b.z; nv[7] = b.w;
+            // two 16-byte buffer loads (plain vector loads here are split
+            // into eight 4-byte loads by the compiler; the load count, not
+            // the bytes, is what this latency-bound phase pays for)
+            const __amdgpu_buffer_rsrc_t nr = __builtin_amdgcn_make_buffer_rsrc(
+                const_cast<float*>(A.norms), (short)0, E * I * 4, kBufferFlags);
+            const int off = (max(se[s], 0) * I + j) * 4;
+            const u32x4_t a = __builtin_amdgcn_raw_buffer_load_b128(nr, off, 0, 0);
+            const u32x4_t b = __builtin_amdgcn_raw_buffer_load_b128(nr, off + 16, 0, 0);
+            nv[0] = __uint_as_float(a.x); nv[1] = __uint_as_float(a.y);
+            nv[2] = __uint_as_float(a.z); nv[3] = __uint_as_float(a.w);
+            nv[4] = __uint_as_float(b.x); nv[5] = __uint_as_float(b.y);
+            nv[6] = __uint_as_float(b.z); nv[7] = __uint_as_float(b.w);
         } else {
 #pragma unroll
             for (int u = 0; u < kSelPer; ++u) {

@@ -127,19 +127,30 @@ __device__ inline void reader_scores(const ReaderArgs& ra, int t, FastDiv fI, co
     if (I % kSelPer == 0) {  // uniform
         const int ic = min(kSelPer * tid, n - kSelPer);
         const int s = fI.div(ic), j = ic - s * I;
-        const float* eg = est + (((size_t)t * k + s) * 2 * nbq) * I + j;
+        // 16-byte buffer loads (plain vector loads here are split into 4-byte
+        // ones by the compiler, and the load count is what this phase pays):
+        // the token's estimates, and the down norms
+        const __amdgpu_buffer_rsrc_t er = __builtin_amdgcn_make_buffer_rsrc(
+            const_cast<float*>(est + (size_t)t * k * 2 * nbq * I), (short)0, k * 2 * nbq * I * 4, 0x00020000);
+        const __amdgpu_buffer_rsrc_t dr = __builtin_amdgcn_make_buffer_rsrc(
+            const_cast<float*>(dnorm), (short)0, ra.E * I * 4, 0x00020000);
+        const int eo = (s * 2 * nbq * I + j) * 4;
+        auto ld4 = [](const __amdgpu_buffer_rsrc_t& r, int off) {
+            const u32x4_t x = __builtin_amdgcn_raw_buffer_load_b128(r, off, 0, 0);
+            return make_float4(__uint_as_float(x.x), __uint_as_float(x.y), __uint_as_float(x.z),
+                               __uint_as_float(x.w));
+        };
         float4 gq[kReaderMaxGroups][2], vq[kReaderMaxGroups][2], dq[2];
 #pragma unroll
         for (int q = 0; q < kReaderMaxGroups; ++q) {
 #pragma unroll
             for (int h2 = 0; h2 < 2; ++h2) {
-                gq[q][h2] = *reinterpret_cast<const float4*>(eg + (size_t)min(q, nbq - 1) * I + 4 * h2);
-                vq[q][h2] = *reinterpret_cast<const float4*>(eg + (size_t)(nbq + min(q, nbq - 1)) * I + 4 * h2);
+                gq[q][h2] = ld4(er, eo + (min(q, nbq - 1) * I + 4 * h2) * 4);
+                vq[q][h2] = ld4(er, eo + ((nbq + min(q, nbq - 1)) * I + 4 * h2) * 4);
             }
         }
 #pragma unroll
-        for (int h2 = 0; h2 < 2; ++h2)
-            dq[h2] = *reinterpret_cast<const float4*>(dnorm + (size_t)max(se[s], 0) * I + j + 4 * h2);
+        for (int h2 = 0; h2 < 2; ++h2) dq[h2] = ld4(dr, ((max(se[s], 0) * I + j) + 4 * h2) * 4);
 #pragma unroll
         for (int u = 0; u < kSelPer; ++u) {
             const int h2 = u / 4, c4 = u % 4;
