@@ -80,7 +80,9 @@ reader_rotate_kernel(const float* __restrict__ h, int M, int H, const int8_t* __
 // with the router's arithmetic (E <= 256).
 constexpr int kMaxBpw = 32;                                      // nblk <= 64
 constexpr int kMaxGroups = kReaderMaxGroups;
-constexpr int kStage = kMaxBpw * kReaderScan / kThreads;         // staged (coordinate, value) per thread
+constexpr int kStageS = (kMaxBpw * kReaderScan / 16 + kThreads - 1) / kThreads;  // 16-byte coordinate chunks per thread
+constexpr int kStageV = (kMaxBpw * kReaderScan / 4 + kThreads - 1) / kThreads;   // 16-byte value chunks per thread
+static_assert(kReaderScan % 16 == 0, "a block's scanned coordinates are whole 16-byte chunks");
 constexpr int kRowBatch = 10;                                    // rows in flight per thread
 
 template <bool ROUTE>
@@ -89,8 +91,8 @@ reader_screen_kernel(ReaderArgs ra, SelRoute route, const int32_t* __restrict__ 
     __shared__ float4 lut4[243];
     __shared__ float lut1[243];
     __shared__ float red[kRowGroups][kRangeCh + 1];
-    __shared__ uint8_t s_sel[kMaxBpw * kReaderScan];
-    __shared__ float s_val[kMaxBpw * kReaderScan];
+    __shared__ __align__(16) uint8_t s_sel[kMaxBpw * kReaderScan];
+    __shared__ __align__(16) float s_val[kMaxBpw * kReaderScan];
     __shared__ int s_e;
     const int x = blockIdx.x;
     const int nbq = ra.nbq, bpw = ra.bpw;
@@ -112,18 +114,25 @@ reader_screen_kernel(ReaderArgs ra, SelRoute route, const int32_t* __restrict__ 
     const int b0 = bq * bpw;
     const int nbh = min(bpw, nblk - b0);  // blocks of this group
 
-    // scanned coordinates and values of the group's blocks (independent of the routing)
+    // scanned coordinates and values of the group's blocks (independent of
+    // the routing), as 16-byte buffer loads: nst is a multiple of 80, so of 16
     const int nst = nbh * kReaderScan;
-    uint32_t st_sel[kStage];
-    float st_val[kStage];
+    uint4 st_sel[kStageS];
+    uint4 st_val[kStageV];
     {
-        const uint8_t* gs = ra.xsel + ((size_t)t * nblk + b0) * kReaderScan;
-        const float* gv = ra.xval + ((size_t)t * nblk + b0) * kReaderScan;
+        const __amdgpu_buffer_rsrc_t gs = __builtin_amdgcn_make_buffer_rsrc(
+            const_cast<uint8_t*>(ra.xsel) + ((size_t)t * nblk + b0) * kReaderScan, (short)0, nst, 0x00020000);
+        const __amdgpu_buffer_rsrc_t gv = __builtin_amdgcn_make_buffer_rsrc(
+            const_cast<float*>(ra.xval) + ((size_t)t * nblk + b0) * kReaderScan, (short)0, nst * 4, 0x00020000);
 #pragma unroll
-        for (int u = 0; u < kStage; ++u) {
-            const int i = min(tid + kThreads * u, nst - 1);
-            st_sel[u] = gs[i];
-            st_val[u] = gv[i];
+        for (int u = 0; u < kStageS; ++u) {
+            const u32x4_t x = __builtin_amdgcn_raw_buffer_load_b128(gs, 16 * (tid + kThreads * u), 0, 0);
+            st_sel[u] = make_uint4(x.x, x.y, x.z, x.w);
+        }
+#pragma unroll
+        for (int u = 0; u < kStageV; ++u) {
+            const u32x4_t x = __builtin_amdgcn_raw_buffer_load_b128(gv, 16 * (tid + kThreads * u), 0, 0);
+            st_val[u] = make_uint4(x.x, x.y, x.z, x.w);
         }
     }
     // the code table: digit m of byte v (base 3) minus 1
@@ -189,12 +198,14 @@ reader_screen_kernel(ReaderArgs ra, SelRoute route, const int32_t* __restrict__ 
         if (tid == 0) s_e = topk_ids[(size_t)t * k + s];
     }
 #pragma unroll
-    for (int u = 0; u < kStage; ++u) {
+    for (int u = 0; u < kStageS; ++u) {
+        const int i = tid + kThreads * u;  // 16-byte chunk
+        if (16 * i < nst) reinterpret_cast<uint4*>(s_sel)[i] = st_sel[u];
+    }
+#pragma unroll
+    for (int u = 0; u < kStageV; ++u) {
         const int i = tid + kThreads * u;
-        if (i < nst) {
-            s_sel[i] = (uint8_t)st_sel[u];
-            s_val[i] = st_val[u];
-        }
+        if (4 * i < nst) reinterpret_cast<uint4*>(s_val)[i] = st_val[u];
     }
     __syncthreads();
     const int e = s_e;
