@@ -158,9 +158,19 @@ expert_fused_kernel(PlanArgs plan, RouteArgs route, const float* __restrict__ h,
             hreg[u] = *reinterpret_cast<const float4*>(h + min((tid + NT * u) * 4, H - 4));
         const int E = plan.E, k = plan.k;
         const int ex = min(tid, E - 1);
+        // only the waves that hold experts load, one 4-byte buffer load per
+        // slice (slices past nslices are out of the buffer's range and read 0)
         float xs[kRouteSlices];
+        if (wave * MOE_WAVE < E) {  // uniform
+            const __amdgpu_buffer_rsrc_t pr = __builtin_amdgcn_make_buffer_rsrc(
+                const_cast<float*>(route.part), (short)0, route.nslices * E * 4, 0x00020000);
 #pragma unroll
-        for (int u = 0; u < kRouteSlices; ++u) xs[u] = route.part[(size_t)min(u, route.nslices - 1) * E + ex];
+            for (int u = 0; u < kRouteSlices; ++u)
+                xs[u] = __uint_as_float(__builtin_amdgcn_raw_buffer_load_b32(pr, (u * E + ex) * 4, 0, 0));
+        } else {
+#pragma unroll
+            for (int u = 0; u < kRouteSlices; ++u) xs[u] = 0.f;
+        }
         const float bv = route.bias ? route.bias[ex] : 0.f;
 #pragma unroll
         for (int u = 0; u < kRouteSlices; ++u) lg += u < route.nslices ? xs[u] : 0.f;  // slice order
