@@ -189,8 +189,12 @@ gateup_vqt_kernel(const int32_t* __restrict__ topk_ids, int R, FastDiv fk, int E
     // past r load nothing)
     float zx[kZBatch];
 #pragma unroll
-    for (int u = 0; u < kZBatch; ++u)
-        zx[u] = LR ? zp[((size_t)min(u, vq.zslices - 1) * vq.M + t) * rr + min(tid, rr - 1)] : 0.f;
+    for (int u = 0; u < kZBatch; ++u) zx[u] = 0.f;
+    if (LR && wave * MOE_WAVE < rr) {  // uniform: only the waves that hold coordinates load
+#pragma unroll
+        for (int u = 0; u < kZBatch; ++u)
+            zx[u] = zp[((size_t)min(u, vq.zslices - 1) * vq.M + t) * rr + min(tid, rr - 1)];
+    }
     if (e < 0 || e >= E) {  // an invalid route has no output (uniform)
         if (P == 0 && s == 0 && tid == 0) atomicOr(err, DEVERR_BAD_ROUTE_ID);
         return;
