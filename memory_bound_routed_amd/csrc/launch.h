@@ -67,7 +67,8 @@ struct RotJob {
     float* xval;
 };
 hipError_t launch_router_partials(const float* h, int M, int H, const uint16_t* Wr, int E, float* part,
-                                  hipStream_t stream, const RotJob* rot = nullptr);
+                                  hipStream_t stream, const RotJob* rot = nullptr, const GemvJob* jobs = nullptr,
+                                  int njobs = 0);
 
 // ---- align.hip
 size_t align_lds_bytes(int R, int E);
@@ -139,12 +140,27 @@ struct VqArgs {
 int vq_slices(int H, int d);
 // One workgroup set per route r < R (token r / k, expert topk_ids[r]; ids
 // outside [0, E) have no output): vp fp32 [R][vq_slices][2][I] slice
-// partials of o_gate and o_up.
+// partials of o_gate and o_up.  With route (the decode step; needs
+// vq_routes_ok): no ids are read -- every workgroup routes its token from the
+// router's slice partials, and the token's ids, weights and logits are
+// stored to route->ids / wts / logits.
+struct SelRoute;
+bool vq_routes_ok(int E, int k);
 hipError_t launch_gateup_vqlr(const int32_t* topk_ids, int R, int k, int E, const VqArgs& vq, const float* h, int H,
-                              int I, float* vp, int32_t* err, hipStream_t stream);
+                              int I, float* vp, int32_t* err, hipStream_t stream, const SelRoute* route = nullptr);
 // p[r][j] = SiLU(sum_s vp[r][s][0][j]) * (sum_s vp[r][s][1][j]), sums in
-// slice order, for the R routes.
-hipError_t launch_vq_finish(const float* vp, int R, int I, int nslice, float* p, hipStream_t stream);
+// slice order, for the R routes.  With plan: also the canonical alignment of
+// the R routes from ids (written by the previous launch), by workgroup (0, 0).
+struct VqPlanJob {
+    const int32_t* ids;  // [R]
+    int E, b;
+    int32_t* sorted_routes;
+    int32_t* block_expert;
+    int32_t* counts;
+    int32_t* err;
+};
+hipError_t launch_vq_finish(const float* vp, int R, int I, int nslice, float* p, hipStream_t stream,
+                            const VqPlanJob* plan = nullptr);
 
 // ---- chansparse.hip
 struct SelRoute {

@@ -372,10 +372,14 @@ moe_status route_align_impl(const Exec& x, bool with_z, const float* h, int32_t 
     return hip_status(e);
 }
 
+// vq_route / vq_plan (VQ + low rank, the decode step): the gate/up launch
+// routes the tokens itself (storing ids, weights and logits) and the finish
+// launch aligns the routes into sorted_routes / block_expert / counts.
 moe_status expert_forward_impl(const Exec& x, bool z_ready, const float* h, int32_t M, const int32_t* topk_ids,
                                const float* topk_w, const int32_t* sorted_routes, const int32_t* block_expert,
                                const int32_t* counts, int32_t keep_channels, int32_t* kept_out, float* y,
-                               hipStream_t s) {
+                               hipStream_t s, const moe::SelRoute* vq_route = nullptr,
+                               const moe::VqPlanJob* vq_plan = nullptr) {
     const moe_config& c = x.c;
     if (M == 0) return MOE_OK;
     if (!h || !topk_ids || !topk_w || !y || !aligned(h, 16) || !aligned(y, 16)) return MOE_ERR_INVALID_ARG;
@@ -442,12 +446,13 @@ moe_status expert_forward_impl(const Exec& x, bool z_ready, const float* h, int3
             const int nsl = moe::vq_slices(c.H, c.vq_d);
             {
                 Launch l(x.prof, MOE_KERNEL_GATEUP_VQLR);
-                e = moe::launch_gateup_vqlr(topk_ids, plan.R, c.top_k, c.E, vq, h, c.H, c.I, vp, x.ws.err, s);
+                e = moe::launch_gateup_vqlr(topk_ids, plan.R, c.top_k, c.E, vq, h, c.H, c.I, vp, x.ws.err, s,
+                                            vq_route);
                 l.done();
                 if (e != hipSuccess) return MOE_ERR_HIP;
             }
             Launch l(x.prof, MOE_KERNEL_VQ_FINISH);
-            e = moe::launch_vq_finish(vp, plan.R, c.I, nsl, x.ws.p, s);
+            e = moe::launch_vq_finish(vp, plan.R, c.I, nsl, x.ws.p, s, vq_plan);
             l.done();
             if (e != hipSuccess) return MOE_ERR_HIP;
         }
@@ -500,6 +505,35 @@ moe_status decode_step_impl(const Exec& x, const float* h, int32_t M, int32_t* t
         return sparse_gather_combine(x, 0, &route, nullptr, h, M, topk_ids, topk_w, keep_channels, kept_out, y, s);
     }
     const int nsl = moe::router_slices(c.H, c.E);
+    if (c.wformat == MOE_WFORMAT_VQLR && M > 0 && moe::vq_routes_ok(c.E, c.top_k)) {
+        // router GEMV partials (and z = D^T h in workgroups of their own),
+        // then a gate/up launch whose workgroups route their tokens, a finish
+        // launch that also aligns, down and combine
+        if (!h || !topk_ids || !topk_w || !sorted_routes || !block_expert || !counts || !y || !aligned(h, 16) ||
+            !aligned(y, 16))
+            return MOE_ERR_INVALID_ARG;
+        const moe::GemvJob jobs[2] = {{x.w.lr_basis[0], c.lr_r, x.ws.zpart[0]},
+                                      {x.w.lr_basis[1], c.lr_r, x.ws.zpart[1]}};
+        {
+            Launch l(x.prof, MOE_KERNEL_ROUTER_GEMV);
+            const hipError_t e = moe::launch_router_partials(h, M, c.H, x.w.router_w, c.E, x.ws.router_part, s,
+                                                             nullptr, c.lr_r > 0 ? jobs : nullptr,
+                                                             c.lr_r > 0 ? 2 : 0);
+            l.done();
+            if (e != hipSuccess) return MOE_ERR_HIP;
+        }
+        moe::SelRoute route{};
+        route.part = x.ws.router_part;
+        route.bias = x.w.router_bias;
+        route.nslices = nsl;
+        route.M = M;
+        route.ids = topk_ids;
+        route.wts = topk_w;
+        route.logits = logits_out;
+        const moe::VqPlanJob pj{topk_ids, c.E, c.block_b, sorted_routes, block_expert, counts, x.ws.err};
+        return expert_forward_impl(x, true, h, M, topk_ids, topk_w, sorted_routes, block_expert, counts, 0, nullptr,
+                                   y, s, &route, &pj);
+    }
     if (M != 1 || c.wformat != MOE_WFORMAT_DENSE || !moe::decode_fused_ok(c.H, c.E, c.top_k, nsl)) {
         const bool vq = c.wformat == MOE_WFORMAT_VQLR;  // z = D^T h in the routing launch
         moe_status st = route_align_impl(x, vq && c.lr_r > 0, h, M, topk_ids, topk_w, logits_out, sorted_routes,

@@ -400,16 +400,31 @@ router_align_kernel(const float* __restrict__ h, int M, int H, const uint16_t* _
 
 // Router GEMV only: the tiles' slice partials part[slice][t][e], stored for
 // a later launch, whose workgroups add them and take the top-k themselves
-// (the expert kernel of the batch-1 decode step, the channel selection).
-// With a rotation job (rot.signs non-null), workgroups past the router's
-// tiles rotate and scan the 128-blocks of the group's tokens for the
-// channel-selection reader instead, one block per wave.
+// (the expert kernel of the batch-1 decode step, the channel selection, the
+// VQ gate/up of the decode step).  Workgroups past the router's tiles compute
+// the tiles of up to kMaxJobs skinny GEMVs on the same h first (the VQ +
+// low-rank format's z = D^T h, as gemv_partials_kernel), then, with a
+// rotation job (rot.signs non-null), rotate and scan the 128-blocks of the
+// group's tokens for the channel-selection reader, one block per wave.
 __global__ void __launch_bounds__(kThreads)
 router_partials_kernel(const float* __restrict__ h, int M, int H, const uint16_t* __restrict__ Wr, int E,
-                       float* __restrict__ part, RotJob rot) {
+                       float* __restrict__ part, RotJob rot, GemvJobs jobs, int njobs) {
     extern __shared__ __align__(16) float red[];
     const RouterTiles tl(H, E);
-    const int x = (int)blockIdx.x - tl.nrs * tl.ncg;
+    int x = (int)blockIdx.x - tl.nrs * tl.ncg;
+    for (int j = 0; x >= 0 && j < njobs; ++j) {  // uniform
+        const GemvJob& jb = jobs.job[j];
+        const RouterTiles tj(H, jb.N);
+        if (x < tj.nrs * tj.ncg) {
+            if (M == 1)
+                router_tile<1>(h, M, 0, H, jb.W, jb.N, tj, x % tj.nrs, x / tj.nrs, jb.part, red);
+            else
+                router_tile<kTokTile>(h, M, blockIdx.y * kTokTile, H, jb.W, jb.N, tj, x % tj.nrs, x / tj.nrs,
+                                      jb.part, red);
+            return;
+        }
+        x -= tj.nrs * tj.ncg;
+    }
     if (x >= 0) {
         const int nblk = H / kReaderBlock;
         const int TT = M == 1 ? 1 : kTokTile;
@@ -491,11 +506,18 @@ hipError_t launch_gemv_partials(const float* h, int M, int H, const GemvJob* job
 int router_slices(int H, int E) { return RouterTiles(H, E).nrs; }
 
 hipError_t launch_router_partials(const float* h, int M, int H, const uint16_t* Wr, int E, float* part,
-                                  hipStream_t stream, const RotJob* rot) {
-    if (M < 1 || E % 8 != 0) return hipErrorInvalidValue;
+                                  hipStream_t stream, const RotJob* rot, const GemvJob* jobs, int njobs) {
+    if (M < 1 || E % 8 != 0 || njobs < 0 || njobs > kMaxJobs || (njobs > 0 && !jobs)) return hipErrorInvalidValue;
     const RouterTiles tl(H, E);
     size_t lds = (size_t)tl.rpt * (M == 1 ? 1 : kTokTile) * tl.cgw * sizeof(float);
     int grid = router_grid(H, E);
+    GemvJobs js{};
+    for (int i = 0; i < njobs; ++i) {
+        if (jobs[i].N < 8 || jobs[i].N % 8) return hipErrorInvalidValue;
+        js.job[i] = jobs[i];
+        lds = tile_lds_bytes(H, jobs[i].N) > lds ? tile_lds_bytes(H, jobs[i].N) : lds;
+        grid += router_grid(H, jobs[i].N);
+    }
     RotJob rj{};
     if (rot) {
         if (H % kReaderBlock || !rot->signs || !rot->xsel || !rot->xval) return hipErrorInvalidValue;
@@ -504,7 +526,7 @@ hipError_t launch_router_partials(const float* h, int M, int H, const uint16_t* 
         rj = *rot;
     }
     MOE_LAUNCH(router_partials_kernel, dim3(grid, router_groups(M)), dim3(kThreads), lds, stream, h, M, H, Wr, E,
-               part, rj);
+               part, rj, js, njobs);
     return hipGetLastError();
 }
 

@@ -162,4 +162,74 @@ __device__ __forceinline__ float topk_softmax(float l, int lane, int k) {
     return x / den;
 }
 
+// LDS of route_token in a workgroup of NT threads.
+template <int NT>
+struct __align__(16) RouteLds {
+    uint64_t skey[NT];
+    uint64_t wk[MOE_WAVE];
+    int wi[MOE_WAVE];
+    int sel_e[32];
+    float sel_l[32];
+    float sel_w[32];
+    int slow;
+};
+
+// One token's routing inside a workgroup of NT threads (E <= NT, k <= 32):
+// the router's slice partials part[slice][t][e] of M tokens added in slice
+// order (+ bias), the top-k by (logit, expert) -- by one wave (wave_topk)
+// when E <= 256 and the keys at or above its threshold fit in a wave, else
+// by counting every key -- and the renormalised softmax.  The arithmetic is
+// the router's, so the ids and weights are its own bit for bit.  Leaves
+// L.sel_e, sel_l[0 .. k) readable by every thread, and with `weights` (or in
+// the writer) sel_w[0 .. k) too (each path ends with a barrier); the writer
+// (uniform) also stores the token's logits (when logits is not null), ids
+// and weights.
+template <int NT>
+__device__ inline void route_token(const float* __restrict__ part, const float* __restrict__ bias, int nslices,
+                                   int M, int t, int E, int k, bool writer, float* __restrict__ logits,
+                                   int32_t* __restrict__ ids, float* __restrict__ wts, RouteLds<NT>& L,
+                                   bool weights = true) {
+    const int tid = threadIdx.x;
+    if (tid < E) {
+        float lg = 0.f;
+        const float bv = bias ? bias[tid] : 0.f;
+        for (int sl0 = 0; sl0 < nslices; sl0 += 8) {  // eight slices in flight
+            float xs[8];
+#pragma unroll
+            for (int u = 0; u < 8; ++u) xs[u] = part[((size_t)min(sl0 + u, nslices - 1) * M + t) * E + tid];
+#pragma unroll
+            for (int u = 0; u < 8; ++u) lg += sl0 + u < nslices ? xs[u] : 0.f;  // slice order
+        }
+        if (bias) lg += bv;
+        if (logits && writer) logits[(size_t)t * E + tid] = lg;
+        L.skey[tid] = order_key((lg != lg) ? -INFINITY : lg, tid);  // NaN ranks as -inf
+    }
+    if (tid == 0) L.slow = E > 4 * MOE_WAVE;
+    __syncthreads();
+    if (tid < MOE_WAVE && E <= 4 * MOE_WAVE && !wave_topk<4>(L.skey, E, k, L.sel_e, L.sel_l, L.wk, L.wi)) L.slow = 1;
+    __syncthreads();
+    if (L.slow) {  // every key counted
+        if (tid < E) {
+            const int rank = count_greater(L.skey, 0, E, L.skey[tid]);
+            if (rank < k) {
+                L.sel_e[rank] = tid;
+                L.sel_l[rank] = key_logit(L.skey[tid]);
+            }
+        }
+        __syncthreads();
+    }
+    if (!weights && !writer) return;  // uniform: the selection is readable
+    if (tid < MOE_WAVE) {  // lane s: slot s
+        const float w = topk_softmax(L.sel_l[min(tid, k - 1)], tid, k);
+        if (tid < k) {
+            L.sel_w[tid] = w;
+            if (writer) {
+                ids[(size_t)t * k + tid] = L.sel_e[tid];
+                wts[(size_t)t * k + tid] = w;
+            }
+        }
+    }
+    __syncthreads();
+}
+
 }  // namespace moe

@@ -27,8 +27,10 @@
 // slices of one (route, projection) run on one XCD (grid x padded to a
 // multiple of 8; workgroups are dealt to the XCDs round robin by linear id),
 // so the 128-byte lines of J they share are fetched into one L2.
+#include "align_device.h"
 #include "device_common.h"
 #include "launch.h"
+#include "topk_device.h"
 
 namespace moe {
 
@@ -113,11 +115,16 @@ constexpr int kLrPre = 4;                      // owned low-rank chunks whose co
 //    fixed order.
 // Everything that does not depend on the route's expert (h, z, the code
 // book) is requested together with its id; the index and coefficient
-// stream follows as soon as the id has arrived.
-template <int D, int JW, bool LR>
+// stream follows as soon as the id has arrived.  ROUTE (the decode step):
+// there is no id to read; the workgroup routes its token itself from the
+// router's slice partials (route_token: the router's arithmetic, so the
+// router's ids bit for bit), and the workgroup of the token's first route,
+// gate, slice 0 stores the token's ids, weights and logits.
+template <int D, int JW, bool LR, bool ROUTE>
 __global__ void __launch_bounds__(kThreads)
-gateup_vqt_kernel(const int32_t* __restrict__ topk_ids, int R, FastDiv fk, int E, VqArgs vq,
-                  const float* __restrict__ h, int H, int I, float* __restrict__ vp, int32_t* __restrict__ err) {
+gateup_vqt_kernel(const int32_t* __restrict__ topk_ids, int R, int k, FastDiv fk, int E, VqArgs vq,
+                  const float* __restrict__ h, int H, int I, float* __restrict__ vp, int32_t* __restrict__ err,
+                  SelRoute route) {
     static_assert(kThreads == 4 * MOE_WAVE, "four waves");
     __shared__ float T[kSlice * kCodes];
     __shared__ float zsm[kMaxR];
@@ -142,7 +149,7 @@ gateup_vqt_kernel(const int32_t* __restrict__ topk_ids, int R, FastDiv fk, int E
     const float* zp = P ? vq.zpart[1] : vq.zpart[0];
 
     // Round 1: the route's expert; code-book operands; h operands; z partials.
-    const int e = topk_ids[r];
+    int e = ROUTE ? 0 : topk_ids[r];
     uint4 bw[4];  // B operand words of N tiles 4 wave + u (code 16 (4 wave + u) + lane % 16)
 #pragma unroll
     for (int u = 0; u < 4; ++u) {
@@ -194,6 +201,13 @@ gateup_vqt_kernel(const int32_t* __restrict__ topk_ids, int R, FastDiv fk, int E
 #pragma unroll
         for (int u = 0; u < kZBatch; ++u)
             zx[u] = zp[((size_t)min(u, vq.zslices - 1) * vq.M + t) * rr + min(tid, rr - 1)];
+    }
+    if constexpr (ROUTE) {
+        __shared__ RouteLds<kThreads> rl;
+        const int slot = r - t * k;
+        route_token<kThreads>(route.part, route.bias, route.nslices, route.M, t, E, k, P == 0 && s == 0 && slot == 0,
+                              route.logits, route.ids, route.wts, rl, false);
+        e = rl.sel_e[slot];
     }
     if (e < 0 || e >= E) {  // an invalid route has no output (uniform)
         if (P == 0 && s == 0 && tid == 0) atomicOr(err, DEVERR_BAD_ROUTE_ID);
@@ -395,37 +409,56 @@ gateup_vqt_kernel(const int32_t* __restrict__ topk_ids, int R, FastDiv fk, int E
     }
 }
 
-template <int D, bool LR>
+template <int D, bool LR, bool ROUTE>
 hipError_t vqt_lr(const int32_t* ids, int R, int k, int E, const VqArgs& vq, const float* h, int H, int I, float* vp,
-                  int32_t* err, hipStream_t stream) {
+                  int32_t* err, const SelRoute& route, hipStream_t stream) {
     const int nslice = (H / D + kSlice - 1) / kSlice;
     const dim3 grid((2 * R + 7) / 8 * 8, nslice);
     // 16-byte index loads when every quarter segment is 16-byte aligned
     if ((H / D) % 16 == 0)
-        MOE_LAUNCH((gateup_vqt_kernel<D, 16, LR>), grid, dim3(kThreads), 0, stream, ids, R, FastDiv((uint32_t)k), E,
-                   vq, h, H, I, vp, err);
+        MOE_LAUNCH((gateup_vqt_kernel<D, 16, LR, ROUTE>), grid, dim3(kThreads), 0, stream, ids, R, k,
+                   FastDiv((uint32_t)k), E, vq, h, H, I, vp, err, route);
     else
-        MOE_LAUNCH((gateup_vqt_kernel<D, 8, LR>), grid, dim3(kThreads), 0, stream, ids, R, FastDiv((uint32_t)k), E,
-                   vq, h, H, I, vp, err);
+        MOE_LAUNCH((gateup_vqt_kernel<D, 8, LR, ROUTE>), grid, dim3(kThreads), 0, stream, ids, R, k,
+                   FastDiv((uint32_t)k), E, vq, h, H, I, vp, err, route);
     return hipGetLastError();
 }
 
 template <int D>
 hipError_t vqt_d(const int32_t* ids, int R, int k, int E, const VqArgs& vq, const float* h, int H, int I, float* vp,
-                 int32_t* err, hipStream_t stream) {
-    if (vq.r > 0) return vqt_lr<D, true>(ids, R, k, E, vq, h, H, I, vp, err, stream);
-    return vqt_lr<D, false>(ids, R, k, E, vq, h, H, I, vp, err, stream);
+                 int32_t* err, const SelRoute* route, hipStream_t stream) {
+    const SelRoute none{};
+    if (route) {
+        if (vq.r > 0) return vqt_lr<D, true, true>(ids, R, k, E, vq, h, H, I, vp, err, *route, stream);
+        return vqt_lr<D, false, true>(ids, R, k, E, vq, h, H, I, vp, err, *route, stream);
+    }
+    if (vq.r > 0) return vqt_lr<D, true, false>(ids, R, k, E, vq, h, H, I, vp, err, none, stream);
+    return vqt_lr<D, false, false>(ids, R, k, E, vq, h, H, I, vp, err, none, stream);
 }
 
 // One thread per (route, channel): the slice partials of both projections,
-// all loads issued together, added in slice order.
+// all loads issued together, added in slice order.  With an alignment job
+// (the decode step, whose gate/up launch routed the tokens itself),
+// workgroup (0, 0) then aligns the routes from the ids that launch stored:
+// the canonical plan of the down projection.
 constexpr int kMaxSlices = 16;
 
+struct AlignJob {
+    const int32_t* ids;  // [R] route ids (null: no alignment)
+    int E;
+    FastDiv fb;          // division by the block size
+    int32_t* sorted_routes;
+    int32_t* block_expert;
+    int32_t* counts;
+    int32_t* err;
+};
+
 __global__ void __launch_bounds__(kThreads)
-vq_finish_kernel(const float* __restrict__ vp, int R, int I, int nslice, float* __restrict__ p) {
+vq_finish_kernel(const float* __restrict__ vp, int R, int I, int nslice, float* __restrict__ p, AlignJob aj) {
+    extern __shared__ __align__(16) int asm_lds[];
     const int j = blockIdx.x * kThreads + threadIdx.x;
     const int r = blockIdx.y;
-    if (j >= I) return;
+    if (j < I) {
     const float* src = vp + (size_t)r * nslice * 2 * I + j;
     float g[kMaxSlices], u[kMaxSlices];
 #pragma unroll
@@ -441,26 +474,51 @@ vq_finish_kernel(const float* __restrict__ vp, int R, int I, int nslice, float* 
         ou += sl < nslice ? u[sl] : 0.f;
     }
     p[(size_t)r * I + j] = silu_mul(og, ou);
+    }
+    if (aj.ids && blockIdx.x == 0 && blockIdx.y == 0) {  // uniform
+        if (R <= MOE_WAVE) {
+            if (threadIdx.x < MOE_WAVE)
+                align_wave([&](int q) { return aj.ids[q]; }, R, aj.E, aj.fb, aj.sorted_routes, aj.block_expert,
+                           aj.counts, aj.err);
+        } else {
+            align_workgroup([&](int q) { return aj.ids[q]; }, R, aj.E, aj.fb, aj.sorted_routes, aj.block_expert,
+                            aj.counts, aj.err, asm_lds);
+        }
+    }
 }
 
 }  // namespace
 
-hipError_t launch_vq_finish(const float* vp, int R, int I, int nslice, float* p, hipStream_t stream) {
+hipError_t launch_vq_finish(const float* vp, int R, int I, int nslice, float* p, hipStream_t stream,
+                            const VqPlanJob* plan) {
     if (nslice < 1 || nslice > kMaxSlices || R < 1) return hipErrorInvalidValue;
-    MOE_LAUNCH(vq_finish_kernel, dim3((I + kThreads - 1) / kThreads, R), dim3(kThreads), 0, stream, vp, R, I,
-               nslice, p);
+    AlignJob aj{};
+    size_t lds = 0;
+    if (plan) {
+        static_assert(kThreads == kAlignThreads, "the alignment runs on the finish workgroup's threads");
+        if (!plan->ids || plan->E < 1 || plan->b < 1) return hipErrorInvalidValue;
+        aj = AlignJob{plan->ids, plan->E, FastDiv((uint32_t)plan->b), plan->sorted_routes, plan->block_expert,
+                      plan->counts, plan->err};
+        lds = R > MOE_WAVE ? align_lds_bytes(R, plan->E) : 0;
+    }
+    MOE_LAUNCH(vq_finish_kernel, dim3((I + kThreads - 1) / kThreads, R), dim3(kThreads), lds, stream, vp, R, I,
+               nslice, p, aj);
     return hipGetLastError();
 }
 
 int vq_slices(int H, int d) { return (H / d + kSlice - 1) / kSlice; }
 
+bool vq_routes_ok(int E, int k) { return E <= kThreads && k <= 32; }
+
 hipError_t launch_gateup_vqlr(const int32_t* topk_ids, int R, int k, int E, const VqArgs& vq, const float* h, int H,
-                              int I, float* vp, int32_t* err, hipStream_t stream) {
+                              int I, float* vp, int32_t* err, hipStream_t stream, const SelRoute* route) {
     if (vq.K < 1 || vq.K > kCodes || H % (8 * vq.d) || vq.r < 0 || vq.r > kMaxR || vq.r % 8 || R < 1 || k < 1)
         return hipErrorInvalidValue;
-    if (vq.d == 8) return vqt_d<8>(topk_ids, R, k, E, vq, h, H, I, vp, err, stream);
-    if (vq.d == 4) return vqt_d<4>(topk_ids, R, k, E, vq, h, H, I, vp, err, stream);
-    if (vq.d == 2) return vqt_d<2>(topk_ids, R, k, E, vq, h, H, I, vp, err, stream);
+    if (route && (!vq_routes_ok(E, k) || !route->part || !route->ids || !route->wts || route->M * k != R))
+        return hipErrorInvalidValue;
+    if (vq.d == 8) return vqt_d<8>(topk_ids, R, k, E, vq, h, H, I, vp, err, route, stream);
+    if (vq.d == 4) return vqt_d<4>(topk_ids, R, k, E, vq, h, H, I, vp, err, route, stream);
+    if (vq.d == 2) return vqt_d<2>(topk_ids, R, k, E, vq, h, H, I, vp, err, route, stream);
     return hipErrorInvalidValue;
 }
 

@@ -994,6 +994,59 @@ def test_decode_step_matches_separate_calls(mb, case):
     layer.close()
 
 
+@pytest.mark.parametrize("case", [
+    "m4",         # the 4-token VQ + low-rank step (d 8, K 256, r 64): 32 routes, one-wave alignment
+    "m16",        # 16 tokens: 128 routes, the workgroup alignment; four router token groups
+    "r0_d2",      # the VQ-only point (no z tiles, no coefficient stream)
+    "ragged",     # H 544, I 37, d 4, K 100, r 8, E 40, k 3, block size 4, 5 tokens, router bias
+    "k_eq_e",     # k = E = 16 with three tokens: every expert routed by every token
+    "e264",       # E > 256: the routing launch + separate launches
+])
+def test_vq_decode_step_matches_separate_calls(mb, case):
+    """The VQ decode step, whose gate/up workgroups route their tokens from
+    the router's slice partials and whose finish launch aligns the routes,
+    gives bit for bit the ids, affinities, logits, plan and y of
+    moe_route_align + moe_expert_forward; y matches the oracle."""
+    import torch
+    sw = synth.small_workload
+    wl = {
+        "m4": synth.WORKLOADS["vqlr_h2048_i768_e128_k8_m4_d8_K256_r64"],
+        "m16": synth.WORKLOADS["vqlr_h2048_i768_e128_k8_m16_d8_K256_r64"],
+        "r0_d2": synth.WORKLOADS["vqlr_h2048_i768_e128_k8_m4_d2_K256_r0"],
+        "ragged": sw("vqds_ragged", H=544, I=37, E=40, k=3, M=5, seed=61, block_b=4, vq=True, vq_d=4, vq_K=100,
+                     lr_r=8, hot_experts=3),
+        "k_eq_e": sw("vqds_keqe", H=256, I=24, E=16, k=16, M=3, seed=62, vq=True, vq_d=8, vq_K=64, lr_r=16),
+        "e264": sw("vqds_e264", H=512, I=40, E=264, k=4, M=2, seed=63, vq=True, vq_d=8, vq_K=256, lr_r=8),
+    }[case]
+    say("VQ decode step vs separate calls:", case, dict(H=wl.H, I=wl.I, E=wl.E, k=wl.k, M=wl.M, d=wl.vq_d,
+                                                       r=wl.lr_r, b=wl.block_b))
+    inp = synth.layer_inputs(wl, 0)
+    layer = make_layer(mb, wl, inp, wl.M)
+    h_np = inp["h"]
+    h = to_dev(h_np)
+    layer.route_align(h, wl.M, logits=True)
+    layer.forward(h, wl.M)
+    torch.cuda.synchronize()
+    a = _step_outputs(layer, wl.M)
+    for t in (layer.ids, layer.w, layer.logits, layer.sorted_routes, layer.block_expert, layer.counts, layer.y):
+        t.fill_(-3)
+    layer.decode_step(h, wl.M, logits=True)
+    torch.cuda.synchronize()
+    b = _step_outputs(layer, wl.M)
+    for what in a:
+        assert torch.equal(a[what].view(torch.int32), b[what].view(torch.int32)), what
+    assert mb.moe_read_device_error(layer.ctx) == 0
+    g = {"ids": b["ids"].cpu().numpy().astype(np.int64), "w": b["w"].cpu().numpy(),
+         "logits": b["logits"].cpu().numpy(), "num_blocks": int(b["counts"][0]),
+         "num_padded": int(b["counts"][1]), "sorted_routes": b["rows"].cpu().numpy().astype(np.int64),
+         "block_expert": b["blocks"].cpu().numpy().astype(np.int64)}
+    check_router(g, inp, wl.k, wl.H)
+    check_plan(g, wl.E, wl.block_b)
+    ref = O.vqlr_forward(h_np, g["ids"], g["w"].astype(np.float64), inp, inp["w_down"])
+    say("  decode step", check_close(b["y"].cpu().numpy(), ref))
+    layer.close()
+
+
 @pytest.mark.parametrize("E,k,M", [
     (256, 32, 4),   # k' = 32 lane groups: most tokens have more than 64 keys above the threshold (all-keys count)
     (256, 2, 4),    # four keys per lane, few candidates
