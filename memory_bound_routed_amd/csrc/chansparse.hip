@@ -122,52 +122,15 @@ chan_topk_gather_kernel(SparseArgs A, FastDiv fI) {
     bool all = K >= n;
     if constexpr (MODE == 0) {
         if constexpr (ROUTE) {
+            // the token's routing (the router's arithmetic); chunk 0 stores
+            // the ids, weights and logits
             const SelRoute& route = A.route;
-            __shared__ uint64_t skey[kSelThreads];
-            __shared__ int sel_e[32];
-            __shared__ float sel_l[32];
-            __shared__ uint64_t wk[MOE_WAVE];
-            __shared__ int wi[MOE_WAVE];
-            __shared__ int s_slow;
-            float lg = 0.f;
-            if (tid < E) {
-                const float bv = route.bias ? route.bias[tid] : 0.f;
-                for (int sl0 = 0; sl0 < route.nslices; sl0 += 8) {  // eight slices in flight
-                    float x[8];
-#pragma unroll
-                    for (int u = 0; u < 8; ++u)
-                        x[u] = route.part[((size_t)min(sl0 + u, route.nslices - 1) * route.M + t) * E + tid];
-#pragma unroll
-                    for (int u = 0; u < 8; ++u) lg += sl0 + u < route.nslices ? x[u] : 0.f;  // slice order
-                }
-                if (route.bias) lg += bv;
-                if (route.logits && chunk == 0) route.logits[(size_t)t * E + tid] = lg;
-                skey[tid] = order_key((lg != lg) ? -INFINITY : lg, tid);  // NaN ranks as -inf
-            }
-            if (tid == 0) s_slow = E > 4 * MOE_WAVE;
-            __syncthreads();
-            if (tid < MOE_WAVE && E <= 4 * MOE_WAVE && !wave_topk<4>(skey, E, k, sel_e, sel_l, wk, wi)) s_slow = 1;
-            __syncthreads();
-            if (s_slow) {  // every key counted (E <= 1024 threads)
-                if (tid < E) {
-                    const int rank = count_greater(skey, 0, E, skey[tid]);
-                    if (rank < k) {
-                        sel_e[rank] = tid;
-                        sel_l[rank] = key_logit(skey[tid]);
-                    }
-                }
-                __syncthreads();
-            }
-            if (tid < MOE_WAVE) {  // lane s: slot s
-                const float w = topk_softmax(sel_l[min(tid, k - 1)], tid, k);
-                if (tid < k) {
-                    if (chunk == 0) {
-                        A.topk_ids[(size_t)t * k + tid] = sel_e[tid];
-                        A.topk_w[(size_t)t * k + tid] = w;
-                    }
-                    se[tid] = sel_e[tid];
-                    sa[tid] = w;
-                }
+            __shared__ RouteLds<kSelThreads> rlt;
+            route_token<kSelThreads>(route.part, route.bias, route.nslices, route.M, t, E, k, chunk == 0,
+                                     route.logits, A.topk_ids, A.topk_w, rlt);
+            if (tid < k) {
+                se[tid] = rlt.sel_e[tid];
+                sa[tid] = rlt.sel_w[tid];
             }
         } else {
             if (tid < k) {

@@ -149,51 +149,12 @@ reader_screen_kernel(ReaderArgs ra, SelRoute route, const int32_t* __restrict__ 
     }
 
     if constexpr (ROUTE) {
-        __shared__ uint64_t skey[kThreads];
-        __shared__ int sel_e[32];
-        __shared__ float sel_l[32];
-        __shared__ uint64_t wk[MOE_WAVE];
-        __shared__ int wi[MOE_WAVE];
-        __shared__ int s_slow;
-        const int E = ra.E;
-        const bool writer = x == 0;  // pair 0, unit 0 writes the routing
-        float lg = 0.f;
-        if (tid < E) {
-            const float bv = route.bias ? route.bias[tid] : 0.f;
-            for (int sl0 = 0; sl0 < route.nslices; sl0 += 8) {  // eight slices in flight
-                float xs[8];
-#pragma unroll
-                for (int u = 0; u < 8; ++u)
-                    xs[u] = route.part[((size_t)min(sl0 + u, route.nslices - 1) * route.M + t) * E + tid];
-#pragma unroll
-                for (int u = 0; u < 8; ++u) lg += sl0 + u < route.nslices ? xs[u] : 0.f;  // slice order
-            }
-            if (route.bias) lg += bv;
-            if (route.logits && writer) route.logits[(size_t)t * E + tid] = lg;
-            skey[tid] = order_key((lg != lg) ? -INFINITY : lg, tid);  // NaN ranks as -inf
-        }
-        if (tid == 0) s_slow = 0;
-        __syncthreads();
-        if (tid < MOE_WAVE && !wave_topk<4>(skey, E, k, sel_e, sel_l, wk, wi)) s_slow = 1;
-        __syncthreads();
-        if (s_slow) {  // every key counted
-            if (tid < E) {
-                const int rank = count_greater(skey, 0, E, skey[tid]);
-                if (rank < k) {
-                    sel_e[rank] = tid;
-                    sel_l[rank] = key_logit(skey[tid]);
-                }
-            }
-            __syncthreads();
-        }
-        if (tid < MOE_WAVE) {  // lane s: slot s
-            const float wv = topk_softmax(sel_l[min(tid, k - 1)], tid, k);
-            if (tid < k && writer) {
-                route.ids[(size_t)t * k + tid] = sel_e[tid];
-                route.wts[(size_t)t * k + tid] = wv;
-            }
-            if (tid == 0) s_e = sel_e[s];
-        }
+        // the token's routing (the router's arithmetic); pair 0, unit 0
+        // stores the ids, weights and logits
+        __shared__ RouteLds<kThreads> rlt;
+        route_token<kThreads>(route.part, route.bias, route.nslices, route.M, t, ra.E, k, x == 0, route.logits,
+                              route.ids, route.wts, rlt, false);
+        if (tid == 0) s_e = rlt.sel_e[s];
     } else {
         if (tid == 0) s_e = topk_ids[(size_t)t * k + s];
     }
