@@ -696,6 +696,36 @@ gateup_dense_kernel(PlanArgs plan, const float* __restrict__ h, int H, int I, co
 constexpr int kDownStage = 1024;  // rows of s staged at a time (32 KiB)
 constexpr int kDownNB = 4;        // weight rows per thread and buffer
 
+// The staged p values of one thread for a stage of down rows js .. js + jn:
+// its route's rows 4 q .. 4 q + 3 for the row quads q = (tid >> 3) + 32 u,
+// as 16-byte buffer loads (rows past I read zero) when I % 4 == 0, else one
+// by one (rows past the stage clamped).  Issued before the weights.
+constexpr int kDownQuads = kDownStage / 4 / (kThreads / 8);  // row quads per thread and stage
+
+__device__ __forceinline__ void down_load_p(const float* __restrict__ p, int sr, int I, int js, int jn,
+                                            float4 (&pv)[kDownQuads]) {
+    const int tid = threadIdx.x;
+    if (I % 4 == 0) {  // uniform
+        const __amdgpu_buffer_rsrc_t prs = __builtin_amdgcn_make_buffer_rsrc(
+            const_cast<float*>(p + (size_t)sr * I), (short)0, I * 4, 0x00020000);
+#pragma unroll
+        for (int u = 0; u < kDownQuads; ++u) {
+            const int jq = (tid >> 3) + (kThreads / 8) * u;
+            const u32x4_t x = __builtin_amdgcn_raw_buffer_load_b128(prs, (js + 4 * jq) * 4, 0, 0);
+            pv[u] = make_float4(__uint_as_float(x.x), __uint_as_float(x.y), __uint_as_float(x.z),
+                                __uint_as_float(x.w));
+        }
+    } else {
+#pragma unroll
+        for (int u = 0; u < kDownQuads; ++u) {
+            const int j4 = 4 * ((tid >> 3) + (kThreads / 8) * u);
+            const float* q = p + (size_t)sr * I + js;
+            pv[u] = make_float4(q[min(j4, jn - 1)], q[min(j4 + 1, jn - 1)], q[min(j4 + 2, jn - 1)],
+                                q[min(j4 + 3, jn - 1)]);
+        }
+    }
+}
+
 template <int CB, int RT>
 __device__ __forceinline__ void down_pass(int e, int H, int I, const uint16_t* __restrict__ Wd,
                                           const float* __restrict__ p, const int (&rr)[8], const float (&ra)[8],
@@ -762,19 +792,17 @@ __device__ __forceinline__ void down_pass(int e, int H, int I, const uint16_t* _
             }
         };
         // stage s (the p loads go out before the first weights)
-        float pv[kDownStage / (kThreads / 8)];
-        constexpr int SPT = kDownStage / (kThreads / 8);  // staged rows per thread (upper bound)
-#pragma unroll
-        for (int u = 0; u < SPT; ++u) {
-            const int jj = min((tid >> 3) + (kThreads / 8) * u, jn - 1);
-            pv[u] = p[(size_t)sr * I + js + jj];
-        }
+        float4 pv[kDownQuads];
+        down_load_p(p, sr, I, js, jn, pv);
         issue(w0, 0);
         __syncthreads();  // the previous stage's s is no longer read
 #pragma unroll
-        for (int u = 0; u < SPT; ++u) {
-            const int jj = (tid >> 3) + (kThreads / 8) * u;
-            if (jj < jn) dsm[jj * 8 + si] = sv ? sa * pv[u] : 0.f;
+        for (int u = 0; u < kDownQuads; ++u) {
+            const int j4 = 4 * ((tid >> 3) + (kThreads / 8) * u);
+            const float v4[4] = {pv[u].x, pv[u].y, pv[u].z, pv[u].w};
+#pragma unroll
+            for (int c = 0; c < 4; ++c)
+                if (j4 + c < jn) dsm[(j4 + c) * 8 + si] = sv ? sa * v4[c] : 0.f;
         }
         __syncthreads();
         for (int u0 = 0; u0 < nu; u0 += 2 * kDownNB) {
@@ -888,7 +916,8 @@ __device__ __forceinline__ void down_pass_mfma(int e, int H, int I, const uint16
                 w[i] = load_stream16(wbase + (size_t)(js + jl) * H);
             }
         };
-        // stage s (the p loads go out before the first weights)
+        // stage s (the p loads go out before the first weights; one by one
+        // here: the 16-byte form of the VALU pass measured slower in this one)
         constexpr int SPT = kDownStage / (kThreads / 8);
         float pv[SPT];
 #pragma unroll

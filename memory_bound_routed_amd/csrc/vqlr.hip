@@ -56,25 +56,35 @@ __device__ __forceinline__ void split_bf16(float x, uint32_t& hi, uint32_t& lo) 
     lo = bf16_rne(x - __uint_as_float(hi << 16));
 }
 
+// The index and coefficient streams are read through buffer resources over
+// the route's expert (its index rows, its coefficient rows).  A part that is
+// not valid is read from the resource's end, which returns zeros without a
+// memory access, so no select follows the load: a select on a loaded value
+// is placed next to the load, and the compiler waits for the load there.
+constexpr int kStreamAux = 2;  // non-temporal
+
 // One lane's quarter of a channel's slice segment: 16 index bytes (blocks
-// 16 q .. 16 q + 15 of the slice) as 4 words.  `row` is the channel's index
-// row, `o` the quarter's byte offset in it, `last` the offset of the row's
-// last 16 (JW = 16) or 8 (JW = 8) valid bytes of the slice, `vb` the valid
-// bytes of the quarter (0, 8 or 16; the rest read as index 0 of a zero row
-// of T).  The loads always go out, from clamped addresses, and the value is
-// selected afterwards: a load inside a branch makes the compiler wait for
-// every load in flight at the branch's end.
+// 16 q .. 16 q + 15 of the slice) as 4 words, at byte offset `off` of the
+// index resource `jr` (`end` bytes long); `vb` is the number of valid bytes
+// (0, 8 or 16; the rest read as index 0 of a zero row of T).
 template <int JW>
-__device__ __forceinline__ uint4 load_quarter(const uint8_t* row, int o, int last, int vb) {
+__device__ __forceinline__ uint4 load_quarter(__amdgpu_buffer_rsrc_t jr, int off, int end, int vb) {
     if constexpr (JW == 16) {
-        const u32x4_t x = __builtin_nontemporal_load(reinterpret_cast<const u32x4_t*>(row + min(o, last)));
-        return vb >= 16 ? make_uint4(x.x, x.y, x.z, x.w) : make_uint4(0u, 0u, 0u, 0u);
+        const u32x4_t x = __builtin_amdgcn_raw_buffer_load_b128(jr, vb >= 16 ? off : end, 0, kStreamAux);
+        return make_uint4(x.x, x.y, x.z, x.w);
     } else {
         typedef unsigned int u32x2_t __attribute__((ext_vector_type(2)));
-        const u32x2_t a = __builtin_nontemporal_load(reinterpret_cast<const u32x2_t*>(row + min(o, last)));
-        const u32x2_t b = __builtin_nontemporal_load(reinterpret_cast<const u32x2_t*>(row + min(o + 8, last)));
-        return make_uint4(vb >= 8 ? a.x : 0u, vb >= 8 ? a.y : 0u, vb >= 16 ? b.x : 0u, vb >= 16 ? b.y : 0u);
+        const u32x2_t a = __builtin_amdgcn_raw_buffer_load_b64(jr, vb >= 8 ? off : end, 0, kStreamAux);
+        const u32x2_t b = __builtin_amdgcn_raw_buffer_load_b64(jr, vb >= 16 ? off + 8 : end, 0, kStreamAux);
+        return make_uint4(a.x, a.y, b.x, b.y);
     }
+}
+
+// 8 low-rank coefficients (16 bytes) at byte offset `off` of the coefficient
+// resource `cr` (`end` bytes long), or zeros when !ok.
+__device__ __forceinline__ uint4 load_coef(__amdgpu_buffer_rsrc_t cr, int off, int end, bool ok) {
+    const u32x4_t x = __builtin_amdgcn_raw_buffer_load_b128(cr, ok ? off : end, 0, kStreamAux);
+    return make_uint4(x.x, x.y, x.z, x.w);
 }
 
 // sum over the lane's 16 blocks of T[16 q + i][byte i], in block order.  The
@@ -133,7 +143,7 @@ gateup_vqt_kernel(const int32_t* __restrict__ topk_ids, int R, int k, FastDiv fk
     const int s = blockIdx.y;
     const int nslice = gridDim.y;
     const int tid = threadIdx.x;
-    const int wave = tid / MOE_WAVE;
+    const int wave = __builtin_amdgcn_readfirstlane(tid / MOE_WAVE);  // uniform: the pass logic runs on scalars
     const int lane = tid % MOE_WAVE;
     const int g = lane / 16;   // MFMA K group / operand row group
     const int q = lane % 4;    // gather quarter
@@ -150,45 +160,46 @@ gateup_vqt_kernel(const int32_t* __restrict__ topk_ids, int R, int k, FastDiv fk
 
     // Round 1: the route's expert; code-book operands; h operands; z partials.
     int e = ROUTE ? 0 : topk_ids[r];
+    // (code-book and h operands through buffer resources: the parts a lane
+    // does not use read zero from the resource's end)
+    typedef unsigned int u32x2_t __attribute__((ext_vector_type(2)));
+    const int bend = vq.K * D * 2;
+    const __amdgpu_buffer_rsrc_t br =
+        __builtin_amdgcn_make_buffer_rsrc(const_cast<uint16_t*>(Bb), (short)0, bend, 0x00020000);
     uint4 bw[4];  // B operand words of N tiles 4 wave + u (code 16 (4 wave + u) + lane % 16)
 #pragma unroll
     for (int u = 0; u < 4; ++u) {
         const int c = 16 * (4 * wave + u) + lane % 16;
-        const uint16_t* cw = Bb + (size_t)min(c, vq.K - 1) * D;
-        uint4 v = make_uint4(0u, 0u, 0u, 0u);
-        if (c < vq.K) {
-            if constexpr (D == 8) {
-                if (g < 2) v = load16(cw);
-            } else if constexpr (D == 4) {
-                if (g == 0) {
-                    const uint2 a = *reinterpret_cast<const uint2*>(cw);
-                    v = make_uint4(a.x, a.y, a.x, a.y);
-                }
-            } else {
-                if (g == 0) {
-                    const uint32_t a = *reinterpret_cast<const uint32_t*>(cw);
-                    v = make_uint4(a, a, 0u, 0u);
-                }
-            }
+        if constexpr (D == 8) {
+            const u32x4_t a = __builtin_amdgcn_raw_buffer_load_b128(br, c < vq.K && g < 2 ? c * 16 : bend, 0, 0);
+            bw[u] = make_uint4(a.x, a.y, a.z, a.w);
+        } else if constexpr (D == 4) {
+            const u32x2_t a = __builtin_amdgcn_raw_buffer_load_b64(br, c < vq.K && g == 0 ? c * 8 : bend, 0, 0);
+            bw[u] = make_uint4(a.x, a.y, a.x, a.y);
+        } else {
+            const uint32_t a = __builtin_amdgcn_raw_buffer_load_b32(br, c < vq.K && g == 0 ? c * 4 : bend, 0, 0);
+            bw[u] = make_uint4(a, a, 0u, 0u);
         }
-        bw[u] = v;
     }
+    const int hend = H * 4;
+    const __amdgpu_buffer_rsrc_t hr =
+        __builtin_amdgcn_make_buffer_rsrc(const_cast<float*>(h + (size_t)t * H), (short)0, hend, 0x00020000);
     float hx[4][D];  // h of block 16 m + lane % 16 of the slice (zero past the channel's blocks)
 #pragma unroll
     for (int m = 0; m < 4; ++m) {
         const int b = 16 * m + lane % 16;
         const bool in = b < L && (D == 8 ? g < 2 : g == 0);
-        const float* src = h + (size_t)t * H + (size_t)(s * kSlice + min(b, L - 1)) * D;
+        const int off = (s * kSlice + b) * D * 4;
         if constexpr (D == 2) {
-            const float2 a = *reinterpret_cast<const float2*>(src);
-            hx[m][0] = in ? a.x : 0.f;
-            hx[m][1] = in ? a.y : 0.f;
+            const u32x2_t a = __builtin_amdgcn_raw_buffer_load_b64(hr, in ? off : hend, 0, 0);
+            hx[m][0] = __uint_as_float(a.x);
+            hx[m][1] = __uint_as_float(a.y);
         } else {
 #pragma unroll
             for (int x = 0; x < D; x += 4) {
-                const float4 a = *reinterpret_cast<const float4*>(src + x);
-                hx[m][x] = in ? a.x : 0.f; hx[m][x + 1] = in ? a.y : 0.f;
-                hx[m][x + 2] = in ? a.z : 0.f; hx[m][x + 3] = in ? a.w : 0.f;
+                const u32x4_t a = __builtin_amdgcn_raw_buffer_load_b128(hr, in ? off + 4 * x : hend, 0, 0);
+                hx[m][x] = __uint_as_float(a.x); hx[m][x + 1] = __uint_as_float(a.y);
+                hx[m][x + 2] = __uint_as_float(a.z); hx[m][x + 3] = __uint_as_float(a.w);
             }
         }
     }
@@ -207,7 +218,7 @@ gateup_vqt_kernel(const int32_t* __restrict__ topk_ids, int R, int k, FastDiv fk
         const int slot = r - t * k;
         route_token<kThreads>(route.part, route.bias, route.nslices, route.M, t, E, k, P == 0 && s == 0 && slot == 0,
                               route.logits, route.ids, route.wts, rl, false);
-        e = rl.sel_e[slot];
+        e = __builtin_amdgcn_readfirstlane(rl.sel_e[slot]);
     }
     if (e < 0 || e >= E) {  // an invalid route has no output (uniform)
         if (P == 0 && s == 0 && tid == 0) atomicOr(err, DEVERR_BAD_ROUTE_ID);
@@ -215,29 +226,50 @@ gateup_vqt_kernel(const int32_t* __restrict__ topk_ids, int R, int k, FastDiv fk
     }
     __builtin_amdgcn_sched_barrier(0);  // keeps the loads above ahead of the stream below
 
-    // The index stream: pass p, lane quarter q of channel 64 p + 16 wave + lane / 4.
+    // The index stream: pass p, lane quarter q of channel 64 p + 16 wave +
+    // lane / 4 (channels past I read past the resource's end).
     const int npass = (I + kPassCh - 1) / kPassCh;
     const int vb = min(max(L - 16 * q, 0), 16);
-    const int jlast = s * kSlice + L - JW;  // offset of the slice's last JW valid bytes in a row
+    const int jend = I * nbk;      // bytes of the expert's index rows
+    const int cend = I * rr * 2;   // bytes of its coefficient rows
+    const __amdgpu_buffer_rsrc_t jr = __builtin_amdgcn_make_buffer_rsrc(
+        const_cast<uint8_t*>(Jb + (size_t)e * jend), (short)0, jend, 0x00020000);
+    const __amdgpu_buffer_rsrc_t cr = __builtin_amdgcn_make_buffer_rsrc(
+        const_cast<uint16_t*>(Cb + (size_t)e * I * rr), (short)0, cend, 0x00020000);
     uint4 jq[kRegPasses];
 #pragma unroll
     for (int p = 0; p < kRegPasses; ++p) {
-        const int j = min(kPassCh * p + 16 * wave + lane / 4, I - 1);
-        jq[p] = load_quarter<JW>(Jb + ((size_t)e * I + j) * nbk, s * kSlice + 16 * q, jlast, p < npass ? vb : 0);
+        const int j = kPassCh * p + 16 * wave + lane / 4;
+        jq[p] = load_quarter<JW>(jr, j * nbk + s * kSlice + 16 * q, jend, p < npass ? vb : 0);
     }
-    // The passes whose 16-channel chunk this slice owns for the low-rank term
-    // (wave-uniform), and the coefficients of the first kLrPre of them: the
-    // lane's 16 of the first 64 coordinates, rho = 16 q .. 16 q + 15.
+    // The passes p < kRegPasses whose 16-channel chunk c = 4 p + wave this
+    // slice owns for the low-rank term, owner (c + c / nslice) % nslice: kept
+    // incrementally (c % nslice and (c / nslice) % nslice), on scalars.
+    uint32_t own = 0;
+    if (LR) {
+        int cm = wave, qm = 0;
+        auto carry = [&]() {
+            while (cm >= nslice) {
+                cm -= nslice;
+                qm = qm + 1 == nslice ? 0 : qm + 1;
+            }
+        };
+        carry();
+        for (int p = 0; p < min(npass, kRegPasses); ++p) {
+            const int o = cm + qm;
+            if ((o >= nslice ? o - nslice : o) == s) own |= 1u << p;
+            cm += 4;
+            carry();
+        }
+    }
+    // The first kLrPre owned passes, and their coefficients: the lane's 16 of
+    // the first 64 coordinates, rho = 16 q .. 16 q + 15.
     int po[kLrPre];
-    int nown = 0;
+    uint32_t own_rest = own;
 #pragma unroll
-    for (int u = 0; u < kLrPre; ++u) po[u] = -1;
-    for (int p = 0; LR && p < npass; ++p) {
-        if (lr_owner(4 * p + wave, nslice) != s) continue;
-#pragma unroll
-        for (int u = 0; u < kLrPre; ++u)
-            if (u == nown) po[u] = p;
-        ++nown;
+    for (int u = 0; u < kLrPre; ++u) {
+        po[u] = own_rest ? __builtin_ctz(own_rest) : -1;
+        own_rest &= own_rest - 1;
     }
     uint4 cpre[kLrPre][2];
 #pragma unroll
@@ -246,14 +278,12 @@ gateup_vqt_kernel(const int32_t* __restrict__ topk_ids, int R, int k, FastDiv fk
             cpre[u][0] = cpre[u][1] = make_uint4(0u, 0u, 0u, 0u);
             continue;
         }
-        const int j = min(kPassCh * max(po[u], 0) + 16 * wave + lane / 4, I - 1);
-        const uint16_t* crow = Cb + ((size_t)e * I + j) * rr;
-        const uint4 a = load_stream16(crow + min(16 * q, rr - 8));
-        const uint4 b = load_stream16(crow + min(16 * q + 8, rr - 8));
+        const int off = ((kPassCh * max(po[u], 0) + 16 * wave + lane / 4) * rr + 16 * q) * 2;
         const bool use = po[u] >= 0;
-        cpre[u][0] = use && 16 * q < rr ? a : make_uint4(0u, 0u, 0u, 0u);
-        cpre[u][1] = use && 16 * q + 8 < rr ? b : make_uint4(0u, 0u, 0u, 0u);
+        cpre[u][0] = load_coef(cr, off, cend, use && 16 * q < rr);
+        cpre[u][1] = load_coef(cr, off + 16, cend, use && 16 * q + 8 < rr);
     }
+    __builtin_amdgcn_sched_barrier(0);  // every stream load goes out before T waits for its operands
 
     // T on the matrix cores (its operands arrived before the stream).
     {
@@ -322,15 +352,11 @@ gateup_vqt_kernel(const int32_t* __restrict__ topk_ids, int R, int k, FastDiv fk
         return acc;
     };
     auto lr_rest = [&](int p, float acc) {  // coordinates 64 .. r - 1
-        const int j = min(kPassCh * p + 16 * wave + lane / 4, I - 1);
-        const uint16_t* crow = Cb + ((size_t)e * I + j) * rr;
+        const int row = (kPassCh * p + 16 * wave + lane / 4) * rr;
         for (int c0 = 64; c0 < rr; c0 += 64) {
-            uint4 c[2];
             const int rho0 = c0 + 16 * q;
-            const uint4 a = load_stream16(crow + min(rho0, rr - 8));
-            const uint4 b = load_stream16(crow + min(rho0 + 8, rr - 8));
-            c[0] = rho0 < rr ? a : make_uint4(0u, 0u, 0u, 0u);
-            c[1] = rho0 + 8 < rr ? b : make_uint4(0u, 0u, 0u, 0u);
+            const uint4 c[2] = {load_coef(cr, (row + rho0) * 2, cend, rho0 < rr),
+                                load_coef(cr, (row + rho0 + 8) * 2, cend, rho0 + 8 < rr)};
             acc = lr_dot(c, rho0, acc);
         }
         return acc;
@@ -354,17 +380,10 @@ gateup_vqt_kernel(const int32_t* __restrict__ topk_ids, int R, int k, FastDiv fk
         for (int pp = 0; pp < kRegPasses; ++pp)
             if (pp == p) acc[pp] += v;
     }
-    for (int p = 0, n = 0; LR && p < min(npass, kRegPasses); ++p) {  // owned passes beyond the prefetched ones
-        if (lr_owner(4 * p + wave, nslice) != s || n++ < kLrPre) continue;
-        const uint4 z0 = make_uint4(0u, 0u, 0u, 0u);
-        const uint4 cz[2] = {z0, z0};
-        const int j = min(kPassCh * p + 16 * wave + lane / 4, I - 1);
-        const uint16_t* crow = Cb + ((size_t)e * I + j) * rr;
-        uint4 c[2] = {cz[0], cz[1]};
-        const uint4 a = load_stream16(crow + min(16 * q, rr - 8));
-        const uint4 b = load_stream16(crow + min(16 * q + 8, rr - 8));
-        c[0] = 16 * q < rr ? a : z0;
-        c[1] = 16 * q + 8 < rr ? b : z0;
+    for (uint32_t m = own_rest; LR && m; m &= m - 1) {  // owned passes beyond the prefetched ones
+        const int p = __builtin_ctz(m);
+        const int off = ((kPassCh * p + 16 * wave + lane / 4) * rr + 16 * q) * 2;
+        const uint4 c[2] = {load_coef(cr, off, cend, 16 * q < rr), load_coef(cr, off + 16, cend, 16 * q + 8 < rr)};
         float v = lr_dot(c, 16 * q, 0.f);
         if (rr > 64) v = lr_rest(p, v);
 #pragma unroll
@@ -389,16 +408,11 @@ gateup_vqt_kernel(const int32_t* __restrict__ topk_ids, int R, int k, FastDiv fk
     }
     for (int p = kRegPasses; p < npass; ++p) {  // further passes: indices loaded here
         const int j = kPassCh * p + 16 * wave + lane / 4;
-        const uint4 w = load_quarter<JW>(Jb + ((size_t)e * I + min(j, I - 1)) * nbk, s * kSlice + 16 * q, jlast, vb);
+        const uint4 w = load_quarter<JW>(jr, j * nbk + s * kSlice + 16 * q, jend, vb);
         float a = gather_quarter(T, w, q);
         if (LR && lr_owner(4 * p + wave, nslice) == s) {
-            const uint4 z0 = make_uint4(0u, 0u, 0u, 0u);
-            const uint16_t* crow = Cb + ((size_t)e * I + min(j, I - 1)) * rr;
-            uint4 c[2];
-            const uint4 ca = load_stream16(crow + min(16 * q, rr - 8));
-            const uint4 cb = load_stream16(crow + min(16 * q + 8, rr - 8));
-            c[0] = 16 * q < rr ? ca : z0;
-            c[1] = 16 * q + 8 < rr ? cb : z0;
+            const int off = (j * rr + 16 * q) * 2;
+            const uint4 c[2] = {load_coef(cr, off, cend, 16 * q < rr), load_coef(cr, off + 16, cend, 16 * q + 8 < rr)};
             float v = lr_dot(c, 16 * q, 0.f);
             if (rr > 64) v = lr_rest(p, v);
             a += v;
