@@ -39,6 +39,8 @@ namespace {
 constexpr int kThreads = 256;
 constexpr int kSlice = 64;      // VQ blocks per slice of T
 constexpr int kCodes = 256;     // code words addressable by a uint8 index (entries >= K are zero)
+constexpr int kTRow = kCodes + 4;  // T row stride in floats: the padding puts the four row groups of a
+                                   // matrix-core result on different LDS banks
 constexpr int kMaxR = 512;      // largest low-rank rank
 constexpr int kZBatch = 8;      // z slice partials loaded ahead of the stream
 
@@ -87,56 +89,75 @@ __device__ __forceinline__ uint4 load_coef(__amdgpu_buffer_rsrc_t cr, int off, i
     return make_uint4(x.x, x.y, x.z, x.w);
 }
 
-// sum over the lane's 16 blocks of T[16 q + i][byte i], in block order.  The
-// words pass through an empty asm so that the addresses are formed here, next
-// to their reads (else the compiler forms all of them early and holds them in
-// registers, leaving none for reads in flight).
-__device__ __forceinline__ float gather_quarter(const float* T, uint4 win, int q) {
+// The lane's 16 reads T[16 q + i][byte i] of a quarter (gather_issue) and
+// their sum in block order (gather_sum); split so that the reads of the next
+// pass can go out before this pass is summed.  The words pass through an
+// empty asm so that the addresses are formed here, next to their reads (else
+// the compiler forms all of them early and holds them in registers, leaving
+// none for reads in flight).
+__device__ __forceinline__ void gather_issue(const float* T, uint4 win, int q, float (&v)[16]) {
     uint32_t w[4] = {win.x, win.y, win.z, win.w};
 #pragma unroll
     for (int k = 0; k < 4; ++k) asm volatile("" : "+v"(w[k]));
-    const float* Tq = T + q * 16 * kCodes;
-    float v[16];
+    const float* Tq = T + q * 16 * kTRow;
 #pragma unroll
-    for (int i = 0; i < 16; ++i) v[i] = Tq[i * kCodes + ((w[i >> 2] >> (8 * (i & 3))) & 255u)];
+    for (int i = 0; i < 16; ++i) v[i] = Tq[i * kTRow + ((w[i >> 2] >> (8 * (i & 3))) & 255u)];
+}
+__device__ __forceinline__ float gather_sum(const float (&v)[16]) {
     float acc = 0.f;
 #pragma unroll
     for (int i = 0; i < 16; ++i) acc += v[i];
     return acc;
 }
+__device__ __forceinline__ float gather_quarter(const float* T, uint4 win, int q) {
+    float v[16];
+    gather_issue(T, win, q, v);
+    return gather_sum(v);
+}
 
-// Slice workgroup owning the low-rank term of the 16-channel chunk c.
-__device__ __forceinline__ int lr_owner(int c, int nslice) { return (c + c / nslice) % nslice; }
+constexpr int kVqWaves = 8;                    // waves of a gate/up workgroup (two per SIMD)
+constexpr int kVqThreads = kVqWaves * MOE_WAVE;
+constexpr int kNTiles = 16 / kVqWaves;         // 16-code tiles of T formed per wave
 
-constexpr int kPassCh = 64;                    // channels per pass (16 per wave, 4 lanes each)
-constexpr int kRegPasses = 12;                 // passes whose index quarters are requested up front
+// Slice workgroup owning the low-rank term of the 16-channel chunk c = kVqWaves p + w
+// (pass p, wave w): (p + c) mod nslice, so that a wave's owned passes are
+// spread over the slices.
+__device__ __forceinline__ int lr_owner(int c, int nslice) { return (c + c / kVqWaves) % nslice; }
+
+constexpr int kPassCh = 16 * kVqWaves;         // channels per pass (16 per wave, 4 lanes each)
+constexpr int kRegPasses = 6;                  // passes held in registers (the rest are loaded one at a time)
 constexpr int kLrPre = 4;                      // owned low-rank chunks whose coefficients are requested up front
+constexpr int kAhead = 2;                      // index passes requested before T, then kept in flight ahead of the gathers
 
 // Grid (x = 2 * route + projection, padded to a multiple of 8; y = T
 // slice).  Workgroup (r, P, s) computes slice s of projection P for route r:
 //  * T[b][c] = h_b . B_P[c] for the slice's 64 blocks b and the 256 code
 //    words c, on the matrix cores: [blocks x (h_hi | h_lo)] times
 //    [(B | B) x codes] with bf16 operands (h = h_hi + h_lo to 2^-18, B is
-//    bf16), fp32 accumulation; wave w forms codes 64 w .. 64 w + 63;
-//  * lane l of wave w, in pass p, takes channel 64 p + 16 w + l / 4 and the
+//    bf16), fp32 accumulation; wave w forms codes 32 w .. 32 w + 31;
+//  * lane l of wave w, in pass p, takes channel 128 p + 16 w + l / 4 and the
 //    16 blocks 16 (l % 4) .. +15 of the slice (its 16 index bytes, one load),
 //    sums T over them, and (if the slice owns the channel's chunk) adds its
 //    quarter of the low-rank term; the quad's four sums are then added in a
 //    fixed order.
-// Everything that does not depend on the route's expert (h, z, the code
-// book) is requested together with its id; the index and coefficient
-// stream follows as soon as the id has arrived.  ROUTE (the decode step):
+// Eight waves (two per SIMD): the gathers are random 4-byte LDS reads, whose
+// bank conflicts make them the kernel's largest cost (about 7 cycles per
+// 64-lane read on this chip, against about 3 without conflicts), and a
+// second wave per SIMD fills the gaps of the first.  Everything that does
+// not depend on the route's expert (h, z, the code book) is requested
+// together with its id; the index and coefficient stream follows as soon as
+// the id has arrived.  ROUTE (the decode step):
 // there is no id to read; the workgroup routes its token itself from the
 // router's slice partials (route_token: the router's arithmetic, so the
 // router's ids bit for bit), and the workgroup of the token's first route,
 // gate, slice 0 stores the token's ids, weights and logits.
 template <int D, int JW, bool LR, bool ROUTE>
-__global__ void __launch_bounds__(kThreads)
+__global__ void __launch_bounds__(kVqThreads)
 gateup_vqt_kernel(const int32_t* __restrict__ topk_ids, int R, int k, FastDiv fk, int E, VqArgs vq,
                   const float* __restrict__ h, int H, int I, float* __restrict__ vp, int32_t* __restrict__ err,
                   SelRoute route) {
-    static_assert(kThreads == 4 * MOE_WAVE, "four waves");
-    __shared__ float T[kSlice * kCodes];
+    static_assert(kNTiles * kVqWaves == 16 && kVqThreads <= 1024, "the 16 code tiles are dealt out evenly");
+    __shared__ float T[kSlice * kTRow];
     __shared__ float zsm[kMaxR];
     const int r = blockIdx.x >> 1;
     const int P = blockIdx.x & 1;
@@ -166,10 +187,10 @@ gateup_vqt_kernel(const int32_t* __restrict__ topk_ids, int R, int k, FastDiv fk
     const int bend = vq.K * D * 2;
     const __amdgpu_buffer_rsrc_t br =
         __builtin_amdgcn_make_buffer_rsrc(const_cast<uint16_t*>(Bb), (short)0, bend, 0x00020000);
-    uint4 bw[4];  // B operand words of N tiles 4 wave + u (code 16 (4 wave + u) + lane % 16)
+    uint4 bw[kNTiles];  // B operand words of N tiles kNTiles wave + u (code 16 (kNTiles wave + u) + lane % 16)
 #pragma unroll
-    for (int u = 0; u < 4; ++u) {
-        const int c = 16 * (4 * wave + u) + lane % 16;
+    for (int u = 0; u < kNTiles; ++u) {
+        const int c = 16 * (kNTiles * wave + u) + lane % 16;
         if constexpr (D == 8) {
             const u32x4_t a = __builtin_amdgcn_raw_buffer_load_b128(br, c < vq.K && g < 2 ? c * 16 : bend, 0, 0);
             bw[u] = make_uint4(a.x, a.y, a.z, a.w);
@@ -214,9 +235,9 @@ gateup_vqt_kernel(const int32_t* __restrict__ topk_ids, int R, int k, FastDiv fk
             zx[u] = zp[((size_t)min(u, vq.zslices - 1) * vq.M + t) * rr + min(tid, rr - 1)];
     }
     if constexpr (ROUTE) {
-        __shared__ RouteLds<kThreads> rl;
+        __shared__ RouteLds<kVqThreads> rl;
         const int slot = r - t * k;
-        route_token<kThreads>(route.part, route.bias, route.nslices, route.M, t, E, k, P == 0 && s == 0 && slot == 0,
+        route_token<kVqThreads>(route.part, route.bias, route.nslices, route.M, t, E, k, P == 0 && s == 0 && slot == 0,
                               route.logits, route.ids, route.wts, rl, false);
         e = __builtin_amdgcn_readfirstlane(rl.sel_e[slot]);
     }
@@ -236,31 +257,20 @@ gateup_vqt_kernel(const int32_t* __restrict__ topk_ids, int R, int k, FastDiv fk
         const_cast<uint8_t*>(Jb + (size_t)e * jend), (short)0, jend, 0x00020000);
     const __amdgpu_buffer_rsrc_t cr = __builtin_amdgcn_make_buffer_rsrc(
         const_cast<uint16_t*>(Cb + (size_t)e * I * rr), (short)0, cend, 0x00020000);
+    auto load_pass = [&](int p) {
+        const int j = kPassCh * p + 16 * wave + lane / 4;
+        return load_quarter<JW>(jr, j * nbk + s * kSlice + 16 * q, jend, p < npass ? vb : 0);
+    };
     uint4 jq[kRegPasses];
 #pragma unroll
-    for (int p = 0; p < kRegPasses; ++p) {
-        const int j = kPassCh * p + 16 * wave + lane / 4;
-        jq[p] = load_quarter<JW>(jr, j * nbk + s * kSlice + 16 * q, jend, p < npass ? vb : 0);
-    }
+    for (int p = 0; p < kAhead; ++p) jq[p] = load_pass(p);
     // The passes p < kRegPasses whose 16-channel chunk c = 4 p + wave this
-    // slice owns for the low-rank term, owner (c + c / nslice) % nslice: kept
-    // incrementally (c % nslice and (c / nslice) % nslice), on scalars.
+    // slice owns for the low-rank term: lane p of the wave tests pass p, and
+    // the ballot is the wave's (uniform) mask.
     uint32_t own = 0;
     if (LR) {
-        int cm = wave, qm = 0;
-        auto carry = [&]() {
-            while (cm >= nslice) {
-                cm -= nslice;
-                qm = qm + 1 == nslice ? 0 : qm + 1;
-            }
-        };
-        carry();
-        for (int p = 0; p < min(npass, kRegPasses); ++p) {
-            const int o = cm + qm;
-            if ((o >= nslice ? o - nslice : o) == s) own |= 1u << p;
-            cm += 4;
-            carry();
-        }
+        const int c = kVqWaves * lane + wave;
+        own = (uint32_t)__builtin_amdgcn_ballot_w64(lane < min(npass, kRegPasses) && lr_owner(c, nslice) == s);
     }
     // The first kLrPre owned passes, and their coefficients: the lane's 16 of
     // the first 64 coordinates, rho = 16 q .. 16 q + 15.
@@ -310,14 +320,14 @@ gateup_vqt_kernel(const int32_t* __restrict__ topk_ids, int R, int k, FastDiv fk
 #pragma unroll
         for (int m = 0; m < 4; ++m)
 #pragma unroll
-            for (int u = 0; u < 4; ++u) {
+            for (int u = 0; u < kNTiles; ++u) {
                 const f32x4_t zero = {0.f, 0.f, 0.f, 0.f};
                 const f32x4_t d4 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(
                     __builtin_bit_cast(bf16x8_t, aw[m]), __builtin_bit_cast(bf16x8_t, bw[u]), zero, 0, 0, 0);
-                // lane holds T[16 m + 4 g + i][16 (4 wave + u) + lane % 16]
-                float* dst = T + (16 * m + 4 * g) * kCodes + 16 * (4 * wave + u) + lane % 16;
+                // lane holds T[16 m + 4 g + i][16 (kNTiles wave + u) + lane % 16]
+                float* dst = T + (16 * m + 4 * g) * kTRow + 16 * (kNTiles * wave + u) + lane % 16;
 #pragma unroll
-                for (int i = 0; i < 4; ++i) dst[i * kCodes] = d4[i];
+                for (int i = 0; i < 4; ++i) dst[i * kTRow] = d4[i];
             }
     }
     // z (slice partials in slice order) into LDS; coordinates past 256 and
@@ -329,12 +339,12 @@ gateup_vqt_kernel(const int32_t* __restrict__ topk_ids, int R, int k, FastDiv fk
         for (int sl = kZBatch; sl < vq.zslices; ++sl) z += zp[((size_t)sl * vq.M + t) * rr + tid];
         zsm[tid] = z;
     }
-    for (int rho = tid + kThreads; LR && rho < rr; rho += kThreads) {
+    for (int rho = tid + kVqThreads; LR && rho < rr; rho += kVqThreads) {
         float z = 0.f;
         for (int sl = 0; sl < vq.zslices; ++sl) z += zp[((size_t)sl * vq.M + t) * rr + rho];
         zsm[rho] = z;
     }
-    for (int rho = rr + tid; rho < kMaxR; rho += kThreads) zsm[rho] = 0.f;  // read against zero coefficients
+    for (int rho = rr + tid; rho < kMaxR; rho += kVqThreads) zsm[rho] = 0.f;  // read against zero coefficients
     __syncthreads();
 
     // Low-rank quarter of the lane's channel in an owned pass: coordinates
@@ -362,23 +372,44 @@ gateup_vqt_kernel(const int32_t* __restrict__ topk_ids, int R, int k, FastDiv fk
         return acc;
     };
 
-    // The gathers, pass by pass as the index words arrive (they were
-    // requested before the coefficients).
+    // The gathers, pass by pass as the index words arrive: a workgroup's
+    // share of the stream takes about as long as T and the gathers together,
+    // so the index request of pass p + kAhead goes out before pass p is
+    // gathered (requested all at once, the requests stall the wave until
+    // the memory system takes them, and the arithmetic waits behind them).
+    // The low-rank quarter of an owned pass (first 64 coordinates, from the
+    // prefetched coefficients) follows its gather; coordinates past 64 are
+    // added after the loop, whose loads would otherwise sit between the
+    // stream's.
     float acc[kRegPasses];
+    float vlr[kLrPre];
 #pragma unroll
-    for (int p = 0; p < kRegPasses; ++p) acc[p] = p < npass ? gather_quarter(T, jq[p], q) : 0.f;
-    // The low-rank quarters of the owned passes, added where they belong by
-    // compile-time selects (a run-time index would move the array to scratch
-    // memory).
+    for (int u = 0; u < kLrPre; ++u) vlr[u] = 0.f;
+    float gv[2][16];  // the T reads of passes p and p + 1
+    gather_issue(T, jq[0], q, gv[0]);
 #pragma unroll
-    for (int u = 0; u < kLrPre; ++u) {
-        const int p = po[u];  // wave-uniform
-        if (p < 0) continue;
-        float v = lr_dot(cpre[u], 16 * q, 0.f);
-        if (rr > 64) v = lr_rest(p, v);
+    for (int p = 0; p < kRegPasses; ++p) {
+        if (p + kAhead < kRegPasses) jq[p + kAhead] = load_pass(p + kAhead);
+        if (p + 1 < kRegPasses) gather_issue(T, jq[p + 1], q, gv[(p + 1) & 1]);
+        __builtin_amdgcn_sched_barrier(0);
+        acc[p] = p < npass ? gather_sum(gv[p & 1]) : 0.f;
 #pragma unroll
-        for (int pp = 0; pp < kRegPasses; ++pp)
-            if (pp == p) acc[pp] += v;
+        for (int u = 0; u < kLrPre; ++u) {
+            if (po[u] != p) continue;  // wave-uniform
+            vlr[u] = lr_dot(cpre[u], 16 * q, 0.f);
+            if (rr <= 64) acc[p] += vlr[u];
+        }
+    }
+    if (rr > 64) {
+#pragma unroll
+        for (int u = 0; u < kLrPre; ++u) {
+            const int p = po[u];  // wave-uniform
+            if (p < 0) continue;
+            const float v = lr_rest(p, vlr[u]);
+#pragma unroll
+            for (int pp = 0; pp < kRegPasses; ++pp)
+                if (pp == p) acc[pp] += v;
+        }
     }
     for (uint32_t m = own_rest; LR && m; m &= m - 1) {  // owned passes beyond the prefetched ones
         const int p = __builtin_ctz(m);
@@ -399,18 +430,19 @@ gateup_vqt_kernel(const int32_t* __restrict__ topk_ids, int R, int k, FastDiv fk
     }
     float* dst = vp + ((size_t)(r * nslice + s) * 2 + P) * I + 16 * wave + lane / 4;
 #pragma unroll
-    for (int m = 0; m < kRegPasses / 4; ++m) {
+    for (int m = 0; m < (kRegPasses + 3) / 4; ++m) {
         float v = acc[4 * m];
 #pragma unroll
-        for (int x = 1; x < 4; ++x) v = q == x ? acc[4 * m + x] : v;
+        for (int x = 1; x < 4; ++x)
+            if (4 * m + x < kRegPasses) v = q == x ? acc[4 * m + x] : v;
         const int p = 4 * m + q;
-        if (p < npass && kPassCh * p + 16 * wave + lane / 4 < I) dst[kPassCh * p] = v;
+        if (p < min(npass, kRegPasses) && kPassCh * p + 16 * wave + lane / 4 < I) dst[kPassCh * p] = v;
     }
     for (int p = kRegPasses; p < npass; ++p) {  // further passes: indices loaded here
         const int j = kPassCh * p + 16 * wave + lane / 4;
         const uint4 w = load_quarter<JW>(jr, j * nbk + s * kSlice + 16 * q, jend, vb);
         float a = gather_quarter(T, w, q);
-        if (LR && lr_owner(4 * p + wave, nslice) == s) {
+        if (LR && lr_owner(kVqWaves * p + wave, nslice) == s) {
             const int off = (j * rr + 16 * q) * 2;
             const uint4 c[2] = {load_coef(cr, off, cend, 16 * q < rr), load_coef(cr, off + 16, cend, 16 * q + 8 < rr)};
             float v = lr_dot(c, 16 * q, 0.f);
@@ -430,10 +462,10 @@ hipError_t vqt_lr(const int32_t* ids, int R, int k, int E, const VqArgs& vq, con
     const dim3 grid((2 * R + 7) / 8 * 8, nslice);
     // 16-byte index loads when every quarter segment is 16-byte aligned
     if ((H / D) % 16 == 0)
-        MOE_LAUNCH((gateup_vqt_kernel<D, 16, LR, ROUTE>), grid, dim3(kThreads), 0, stream, ids, R, k,
+        MOE_LAUNCH((gateup_vqt_kernel<D, 16, LR, ROUTE>), grid, dim3(kVqThreads), 0, stream, ids, R, k,
                    FastDiv((uint32_t)k), E, vq, h, H, I, vp, err, route);
     else
-        MOE_LAUNCH((gateup_vqt_kernel<D, 8, LR, ROUTE>), grid, dim3(kThreads), 0, stream, ids, R, k,
+        MOE_LAUNCH((gateup_vqt_kernel<D, 8, LR, ROUTE>), grid, dim3(kVqThreads), 0, stream, ids, R, k,
                    FastDiv((uint32_t)k), E, vq, h, H, I, vp, err, route);
     return hipGetLastError();
 }
