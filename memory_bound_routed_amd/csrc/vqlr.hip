@@ -10,8 +10,10 @@
 // book T_P[t][b][c] = h_b . B_P[c] of the page, h_b the b-th length-d block
 // of h.  An fp32 T is 256 KiB per token and projection at H = 2048, more than
 // a CU's LDS, and a bf16 T is not accurate enough; so T is cut into slices of
-// 64 blocks (64 KiB) and one workgroup owns one (route, projection, slice):
-// it forms its slice of T on the matrix cores and then adds, for every
+// 64 blocks (64 KiB) and one workgroup owns one (route, projection, slice)
+// -- or, when there are more of them than fit on the device at once, a few
+// slices of one (route, projection) taken in turn: for each it forms its
+// slice of T on the matrix cores and then adds, for every
 // channel of the route's expert, T[b][J[j][b]] over its 64 blocks -- one
 // 4-byte LDS read and one add per index byte, where applying each code word
 // to h directly takes a 4d-byte read and d FMAs.  Each slice workgroup also
@@ -115,6 +117,13 @@ __device__ __forceinline__ float gather_quarter(const float* T, uint4 win, int q
     return gather_sum(v);
 }
 
+// x through an empty asm: the compiler cannot see that its value is the
+// argument's.
+__device__ __forceinline__ int opaque_int(int x) {
+    asm volatile("" : "+v"(x));
+    return x;
+}
+
 constexpr int kVqWaves = 8;                    // waves of a gate/up workgroup (two per SIMD)
 constexpr int kVqThreads = kVqWaves * MOE_WAVE;
 constexpr int kNTiles = 16 / kVqWaves;         // 16-code tiles of T formed per wave
@@ -128,9 +137,12 @@ constexpr int kPassCh = 16 * kVqWaves;         // channels per pass (16 per wave
 constexpr int kRegPasses = 6;                  // passes held in registers (the rest are loaded one at a time)
 constexpr int kLrPre = 4;                      // owned low-rank chunks whose coefficients are requested up front
 constexpr int kAhead = 2;                      // index passes requested before T, then kept in flight ahead of the gathers
+constexpr int kVqResident = 512;               // gate/up workgroups resident at once (2 per CU x 256 CUs)
 
-// Grid (x = 2 * route + projection, padded to a multiple of 8; y = T
-// slice).  Workgroup (r, P, s) computes slice s of projection P for route r:
+// Grid (x = 2 * route + projection, padded to a multiple of 8; y = first T
+// slice, the workgroup then takes slices y + gridDim.y, ... in turn).  For
+// each slice s, workgroup (r, P, y) computes slice s of projection P for
+// route r:
 //  * T[b][c] = h_b . B_P[c] for the slice's 64 blocks b and the 256 code
 //    words c, on the matrix cores: [blocks x (h_hi | h_lo)] times
 //    [(B | B) x codes] with bf16 operands (h = h_hi + h_lo to 2^-18, B is
@@ -161,17 +173,16 @@ gateup_vqt_kernel(const int32_t* __restrict__ topk_ids, int R, int k, FastDiv fk
     __shared__ float zsm[kMaxR];
     const int r = blockIdx.x >> 1;
     const int P = blockIdx.x & 1;
-    const int s = blockIdx.y;
-    const int nslice = gridDim.y;
+    const int s0 = blockIdx.y;   // first slice of this workgroup
+    const int ny = gridDim.y;    // it takes slices s0, s0 + ny, ... < nslice in turn
     const int tid = threadIdx.x;
     const int wave = __builtin_amdgcn_readfirstlane(tid / MOE_WAVE);  // uniform: the pass logic runs on scalars
     const int lane = tid % MOE_WAVE;
     const int g = lane / 16;   // MFMA K group / operand row group
-    const int q = lane % 4;    // gather quarter
     if (r >= R) return;  // grid padding
 
-    const int nbk = H / D;                        // VQ blocks per channel
-    const int L = min(kSlice, nbk - s * kSlice);  // valid blocks of this slice (> 0)
+    const int nbk = H / D;                              // VQ blocks per channel
+    const int nslice = (nbk + kSlice - 1) / kSlice;     // slices of T
     const int rr = vq.r;
     const int t = fk.div(r);
     const uint16_t* Cb = P ? vq.C[1] : vq.C[0];
@@ -179,7 +190,8 @@ gateup_vqt_kernel(const int32_t* __restrict__ topk_ids, int R, int k, FastDiv fk
     const uint8_t* Jb = P ? vq.J[1] : vq.J[0];
     const float* zp = P ? vq.zpart[1] : vq.zpart[0];
 
-    // Round 1: the route's expert; code-book operands; h operands; z partials.
+    // Round 1: the route's expert; code-book operands; h operands of the
+    // first slice; z partials.
     int e = ROUTE ? 0 : topk_ids[r];
     // (code-book and h operands through buffer resources: the parts a lane
     // does not use read zero from the resource's end)
@@ -205,25 +217,28 @@ gateup_vqt_kernel(const int32_t* __restrict__ topk_ids, int R, int k, FastDiv fk
     const int hend = H * 4;
     const __amdgpu_buffer_rsrc_t hr =
         __builtin_amdgcn_make_buffer_rsrc(const_cast<float*>(h + (size_t)t * H), (short)0, hend, 0x00020000);
-    float hx[4][D];  // h of block 16 m + lane % 16 of the slice (zero past the channel's blocks)
+    // h of block 16 m + lane % 16 of slice s (zero past the channel's blocks)
+    auto load_h = [&](int s, float (&hx)[4][D]) {
+        const int L = min(kSlice, nbk - s * kSlice);
 #pragma unroll
-    for (int m = 0; m < 4; ++m) {
-        const int b = 16 * m + lane % 16;
-        const bool in = b < L && (D == 8 ? g < 2 : g == 0);
-        const int off = (s * kSlice + b) * D * 4;
-        if constexpr (D == 2) {
-            const u32x2_t a = __builtin_amdgcn_raw_buffer_load_b64(hr, in ? off : hend, 0, 0);
-            hx[m][0] = __uint_as_float(a.x);
-            hx[m][1] = __uint_as_float(a.y);
-        } else {
+        for (int m = 0; m < 4; ++m) {
+            const int b = 16 * m + lane % 16;
+            const bool in = b < L && (D == 8 ? g < 2 : g == 0);
+            const int off = (s * kSlice + b) * D * 4;
+            if constexpr (D == 2) {
+                const u32x2_t a = __builtin_amdgcn_raw_buffer_load_b64(hr, in ? off : hend, 0, 0);
+                hx[m][0] = __uint_as_float(a.x);
+                hx[m][1] = __uint_as_float(a.y);
+            } else {
 #pragma unroll
-            for (int x = 0; x < D; x += 4) {
-                const u32x4_t a = __builtin_amdgcn_raw_buffer_load_b128(hr, in ? off + 4 * x : hend, 0, 0);
-                hx[m][x] = __uint_as_float(a.x); hx[m][x + 1] = __uint_as_float(a.y);
-                hx[m][x + 2] = __uint_as_float(a.z); hx[m][x + 3] = __uint_as_float(a.w);
+                for (int x = 0; x < D; x += 4) {
+                    const u32x4_t a = __builtin_amdgcn_raw_buffer_load_b128(hr, in ? off + 4 * x : hend, 0, 0);
+                    hx[m][x] = __uint_as_float(a.x); hx[m][x + 1] = __uint_as_float(a.y);
+                    hx[m][x + 2] = __uint_as_float(a.z); hx[m][x + 3] = __uint_as_float(a.w);
+                }
             }
         }
-    }
+    };
     // z partials of coordinate rho = tid (the first kZBatch slices; threads
     // past r load nothing)
     float zx[kZBatch];
@@ -237,101 +252,27 @@ gateup_vqt_kernel(const int32_t* __restrict__ topk_ids, int R, int k, FastDiv fk
     if constexpr (ROUTE) {
         __shared__ RouteLds<kVqThreads> rl;
         const int slot = r - t * k;
-        route_token<kVqThreads>(route.part, route.bias, route.nslices, route.M, t, E, k, P == 0 && s == 0 && slot == 0,
+        route_token<kVqThreads>(route.part, route.bias, route.nslices, route.M, t, E, k, P == 0 && s0 == 0 && slot == 0,
                               route.logits, route.ids, route.wts, rl, false);
         e = __builtin_amdgcn_readfirstlane(rl.sel_e[slot]);
     }
     if (e < 0 || e >= E) {  // an invalid route has no output (uniform)
-        if (P == 0 && s == 0 && tid == 0) atomicOr(err, DEVERR_BAD_ROUTE_ID);
+        if (P == 0 && s0 == 0 && tid == 0) atomicOr(err, DEVERR_BAD_ROUTE_ID);
         return;
     }
     __builtin_amdgcn_sched_barrier(0);  // keeps the loads above ahead of the stream below
 
-    // The index stream: pass p, lane quarter q of channel 64 p + 16 wave +
-    // lane / 4 (channels past I read past the resource's end).
     const int npass = (I + kPassCh - 1) / kPassCh;
-    const int vb = min(max(L - 16 * q, 0), 16);
     const int jend = I * nbk;      // bytes of the expert's index rows
     const int cend = I * rr * 2;   // bytes of its coefficient rows
     const __amdgpu_buffer_rsrc_t jr = __builtin_amdgcn_make_buffer_rsrc(
         const_cast<uint8_t*>(Jb + (size_t)e * jend), (short)0, jend, 0x00020000);
     const __amdgpu_buffer_rsrc_t cr = __builtin_amdgcn_make_buffer_rsrc(
         const_cast<uint16_t*>(Cb + (size_t)e * I * rr), (short)0, cend, 0x00020000);
-    auto load_pass = [&](int p) {
-        const int j = kPassCh * p + 16 * wave + lane / 4;
-        return load_quarter<JW>(jr, j * nbk + s * kSlice + 16 * q, jend, p < npass ? vb : 0);
-    };
-    uint4 jq[kRegPasses];
-#pragma unroll
-    for (int p = 0; p < kAhead; ++p) jq[p] = load_pass(p);
-    // The passes p < kRegPasses whose 16-channel chunk c = 4 p + wave this
-    // slice owns for the low-rank term: lane p of the wave tests pass p, and
-    // the ballot is the wave's (uniform) mask.
-    uint32_t own = 0;
-    if (LR) {
-        const int c = kVqWaves * lane + wave;
-        own = (uint32_t)__builtin_amdgcn_ballot_w64(lane < min(npass, kRegPasses) && lr_owner(c, nslice) == s);
-    }
-    // The first kLrPre owned passes, and their coefficients: the lane's 16 of
-    // the first 64 coordinates, rho = 16 q .. 16 q + 15.
-    int po[kLrPre];
-    uint32_t own_rest = own;
-#pragma unroll
-    for (int u = 0; u < kLrPre; ++u) {
-        po[u] = own_rest ? __builtin_ctz(own_rest) : -1;
-        own_rest &= own_rest - 1;
-    }
-    uint4 cpre[kLrPre][2];
-#pragma unroll
-    for (int u = 0; u < kLrPre; ++u) {
-        if constexpr (!LR) {
-            cpre[u][0] = cpre[u][1] = make_uint4(0u, 0u, 0u, 0u);
-            continue;
-        }
-        const int off = ((kPassCh * max(po[u], 0) + 16 * wave + lane / 4) * rr + 16 * q) * 2;
-        const bool use = po[u] >= 0;
-        cpre[u][0] = load_coef(cr, off, cend, use && 16 * q < rr);
-        cpre[u][1] = load_coef(cr, off + 16, cend, use && 16 * q + 8 < rr);
-    }
-    __builtin_amdgcn_sched_barrier(0);  // every stream load goes out before T waits for its operands
 
-    // T on the matrix cores (its operands arrived before the stream).
-    {
-        uint4 aw[4];  // A operand words of M tile m: 8 bf16 of K group g
-#pragma unroll
-        for (int m = 0; m < 4; ++m) {
-            uint32_t hi[D], lo[D];
-#pragma unroll
-            for (int x = 0; x < D; ++x) split_bf16(hx[m][x], hi[x], lo[x]);
-            uint32_t k8[8];  // K slots 8 g .. 8 g + 7 (zero past 2 D)
-            if constexpr (D == 8) {
-#pragma unroll
-                for (int x = 0; x < 8; ++x) k8[x] = g == 0 ? hi[x] : lo[x];
-            } else if constexpr (D == 4) {
-#pragma unroll
-                for (int x = 0; x < 4; ++x) { k8[x] = hi[x]; k8[4 + x] = lo[x]; }
-            } else {
-                k8[0] = hi[0]; k8[1] = hi[1]; k8[2] = lo[0]; k8[3] = lo[1];
-                k8[4] = k8[5] = k8[6] = k8[7] = 0u;
-            }
-            aw[m] = make_uint4(k8[0] | (k8[1] << 16), k8[2] | (k8[3] << 16), k8[4] | (k8[5] << 16),
-                               k8[6] | (k8[7] << 16));
-        }
-#pragma unroll
-        for (int m = 0; m < 4; ++m)
-#pragma unroll
-            for (int u = 0; u < kNTiles; ++u) {
-                const f32x4_t zero = {0.f, 0.f, 0.f, 0.f};
-                const f32x4_t d4 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(
-                    __builtin_bit_cast(bf16x8_t, aw[m]), __builtin_bit_cast(bf16x8_t, bw[u]), zero, 0, 0, 0);
-                // lane holds T[16 m + 4 g + i][16 (kNTiles wave + u) + lane % 16]
-                float* dst = T + (16 * m + 4 * g) * kTRow + 16 * (kNTiles * wave + u) + lane % 16;
-#pragma unroll
-                for (int i = 0; i < 4; ++i) dst[i * kTRow] = d4[i];
-            }
-    }
-    // z (slice partials in slice order) into LDS; coordinates past 256 and
-    // slices past kZBatch are loaded here.
+    // z (slice partials in slice order) into LDS, read after the first
+    // slice's barrier; coordinates past 256 and slices past kZBatch are
+    // loaded here.
     if (LR && tid < rr) {
         float z = 0.f;
 #pragma unroll
@@ -345,121 +286,227 @@ gateup_vqt_kernel(const int32_t* __restrict__ topk_ids, int R, int k, FastDiv fk
         zsm[rho] = z;
     }
     for (int rho = rr + tid; rho < kMaxR; rho += kVqThreads) zsm[rho] = 0.f;  // read against zero coefficients
-    __syncthreads();
 
-    // Low-rank quarter of the lane's channel in an owned pass: coordinates
-    // 64 c0 + 16 q + x, in rho order; the first 64 from the prefetched
-    // coefficients, further ones loaded here.
-    auto lr_dot = [&](const uint4 (&c)[2], int rho0, float acc) {
-#pragma unroll
-        for (int u = 0; u < 2; ++u) {
-            float f[8];
-            unpack8(c[u], f);
-            const int rb = min(rho0 + 8 * u, kMaxR - 8);  // coefficients past r are zero
-#pragma unroll
-            for (int x = 0; x < 8; ++x) acc = fmaf(f[x], zsm[rb + x], acc);
-        }
-        return acc;
-    };
-    auto lr_rest = [&](int p, float acc) {  // coordinates 64 .. r - 1
-        const int row = (kPassCh * p + 16 * wave + lane / 4) * rr;
-        for (int c0 = 64; c0 < rr; c0 += 64) {
-            const int rho0 = c0 + 16 * q;
-            const uint4 c[2] = {load_coef(cr, (row + rho0) * 2, cend, rho0 < rr),
-                                load_coef(cr, (row + rho0 + 8) * 2, cend, rho0 + 8 < rr)};
-            acc = lr_dot(c, rho0, acc);
-        }
-        return acc;
-    };
+    // The workgroup's slices in turn (a grid of fewer slice rows than
+    // slices when the routes would not otherwise fit on the device at
+    // once): the routing, code-book, z and LDS set-up above is done once,
+    // and a later slice's index, coefficient and h loads go out before the
+    // barrier that waits for every wave to finish reading the previous T.
+    for (int s = s0; s < nslice; s += ny) {  // uniform
+        // The lane id through an empty asm: everything derived from it is
+        // formed again per slice instead of being hoisted out of the loop
+        // and held in registers across it.
+        const int lane_s = opaque_int(lane);
+        const int lane = lane_s;
+        const int g = lane / 16;  // MFMA K group / operand row group
+        const int q = lane % 4;   // gather quarter
+        const int L = min(kSlice, nbk - s * kSlice);  // valid blocks of this slice (> 0)
+        float hx[4][D];
+        load_h(s, hx);
 
-    // The gathers, pass by pass as the index words arrive: a workgroup's
-    // share of the stream takes about as long as T and the gathers together,
-    // so the index request of pass p + kAhead goes out before pass p is
-    // gathered (requested all at once, the requests stall the wave until
-    // the memory system takes them, and the arithmetic waits behind them).
-    // The low-rank quarter of an owned pass (first 64 coordinates, from the
-    // prefetched coefficients) follows its gather; coordinates past 64 are
-    // added after the loop, whose loads would otherwise sit between the
-    // stream's.
-    float acc[kRegPasses];
-    float vlr[kLrPre];
+        // Low-rank quarter of the lane's channel in an owned pass: coordinates
+        // 64 c0 + 16 q + x, in rho order; the first 64 from the prefetched
+        // coefficients, further ones loaded here.
+        auto lr_dot = [&](const uint4 (&c)[2], int rho0, float acc) {
+    #pragma unroll
+            for (int u = 0; u < 2; ++u) {
+                float f[8];
+                unpack8(c[u], f);
+                const int rb = min(rho0 + 8 * u, kMaxR - 8);  // coefficients past r are zero
+    #pragma unroll
+                for (int x = 0; x < 8; ++x) acc = fmaf(f[x], zsm[rb + x], acc);
+            }
+            return acc;
+        };
+        auto lr_rest = [&](int p, float acc) {  // coordinates 64 .. r - 1
+            const int row = (kPassCh * p + 16 * wave + lane / 4) * rr;
+            for (int c0 = 64; c0 < rr; c0 += 64) {
+                const int rho0 = c0 + 16 * q;
+                const uint4 c[2] = {load_coef(cr, (row + rho0) * 2, cend, rho0 < rr),
+                                    load_coef(cr, (row + rho0 + 8) * 2, cend, rho0 + 8 < rr)};
+                acc = lr_dot(c, rho0, acc);
+            }
+            return acc;
+        };
+
+        // The index stream: pass p, lane quarter q of channel 128 p + 16 wave
+        // + lane / 4 (channels past I read past the resource's end).
+        const int vb = min(max(L - 16 * q, 0), 16);
+        auto load_pass = [&](int p) {
+            const int j = kPassCh * p + 16 * wave + lane / 4;
+            return load_quarter<JW>(jr, j * nbk + s * kSlice + 16 * q, jend, p < npass ? vb : 0);
+        };
+        uint4 jq[kRegPasses];
 #pragma unroll
-    for (int u = 0; u < kLrPre; ++u) vlr[u] = 0.f;
-    float gv[2][16];  // the T reads of passes p and p + 1
-    gather_issue(T, jq[0], q, gv[0]);
-#pragma unroll
-    for (int p = 0; p < kRegPasses; ++p) {
-        if (p + kAhead < kRegPasses) jq[p + kAhead] = load_pass(p + kAhead);
-        if (p + 1 < kRegPasses) gather_issue(T, jq[p + 1], q, gv[(p + 1) & 1]);
-        __builtin_amdgcn_sched_barrier(0);
-        acc[p] = p < npass ? gather_sum(gv[p & 1]) : 0.f;
+        for (int p = 0; p < kAhead; ++p) jq[p] = load_pass(p);
+        // The passes p < kRegPasses whose 16-channel chunk c = kVqWaves p +
+        // wave this slice owns for the low-rank term: lane p of the wave
+        // tests pass p, and the ballot is the wave's (uniform) mask.
+        uint32_t own = 0;
+        if (LR) {
+            const int c = kVqWaves * lane + wave;
+            own = (uint32_t)__builtin_amdgcn_ballot_w64(lane < min(npass, kRegPasses) && lr_owner(c, nslice) == s);
+        }
+        // The first kLrPre owned passes, and their coefficients: the lane's 16
+        // of the first 64 coordinates, rho = 16 q .. 16 q + 15.
+        int po[kLrPre];
+        uint32_t own_rest = own;
 #pragma unroll
         for (int u = 0; u < kLrPre; ++u) {
-            if (po[u] != p) continue;  // wave-uniform
-            vlr[u] = lr_dot(cpre[u], 16 * q, 0.f);
-            if (rr <= 64) acc[p] += vlr[u];
+            po[u] = own_rest ? __builtin_ctz(own_rest) : -1;
+            own_rest &= own_rest - 1;
         }
-    }
-    if (rr > 64) {
+        uint4 cpre[kLrPre][2];
 #pragma unroll
         for (int u = 0; u < kLrPre; ++u) {
-            const int p = po[u];  // wave-uniform
-            if (p < 0) continue;
-            const float v = lr_rest(p, vlr[u]);
+            if constexpr (!LR) {
+                cpre[u][0] = cpre[u][1] = make_uint4(0u, 0u, 0u, 0u);
+                continue;
+            }
+            const int off = ((kPassCh * max(po[u], 0) + 16 * wave + lane / 4) * rr + 16 * q) * 2;
+            const bool use = po[u] >= 0;
+            cpre[u][0] = load_coef(cr, off, cend, use && 16 * q < rr);
+            cpre[u][1] = load_coef(cr, off + 16, cend, use && 16 * q + 8 < rr);
+        }
+        __builtin_amdgcn_sched_barrier(0);  // every stream load goes out before T waits for its operands
+        __syncthreads();  // the previous slice's T is no longer read (the first: zsm written)
+
+        // T on the matrix cores (its operands arrived before the stream).
+        {
+            uint4 aw[4];  // A operand words of M tile m: 8 bf16 of K group g
+#pragma unroll
+            for (int m = 0; m < 4; ++m) {
+                uint32_t hi[D], lo[D];
+#pragma unroll
+                for (int x = 0; x < D; ++x) split_bf16(hx[m][x], hi[x], lo[x]);
+                uint32_t k8[8];  // K slots 8 g .. 8 g + 7 (zero past 2 D)
+                if constexpr (D == 8) {
+#pragma unroll
+                    for (int x = 0; x < 8; ++x) k8[x] = g == 0 ? hi[x] : lo[x];
+                } else if constexpr (D == 4) {
+#pragma unroll
+                    for (int x = 0; x < 4; ++x) { k8[x] = hi[x]; k8[4 + x] = lo[x]; }
+                } else {
+                    k8[0] = hi[0]; k8[1] = hi[1]; k8[2] = lo[0]; k8[3] = lo[1];
+                    k8[4] = k8[5] = k8[6] = k8[7] = 0u;
+                }
+                aw[m] = make_uint4(k8[0] | (k8[1] << 16), k8[2] | (k8[3] << 16), k8[4] | (k8[5] << 16),
+                                   k8[6] | (k8[7] << 16));
+            }
+#pragma unroll
+            for (int m = 0; m < 4; ++m)
+#pragma unroll
+                for (int u = 0; u < kNTiles; ++u) {
+                    const f32x4_t zero = {0.f, 0.f, 0.f, 0.f};
+                    const f32x4_t d4 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(
+                        __builtin_bit_cast(bf16x8_t, aw[m]), __builtin_bit_cast(bf16x8_t, bw[u]), zero, 0, 0, 0);
+                    // lane holds T[16 m + 4 g + i][16 (kNTiles wave + u) + lane % 16]
+                    float* dst = T + (16 * m + 4 * g) * kTRow + 16 * (kNTiles * wave + u) + lane % 16;
+#pragma unroll
+                    for (int i = 0; i < 4; ++i) dst[i * kTRow] = d4[i];
+                }
+        }
+        __syncthreads();
+
+        // The gathers, pass by pass as the index words arrive: a workgroup's
+        // share of the stream takes about as long as T and the gathers
+        // together, so the index request of pass p + kAhead goes out before
+        // pass p is gathered (requested all at once, the requests stall the
+        // wave until the memory system takes them, and the arithmetic waits
+        // behind them).  The low-rank quarter of an owned pass (first 64
+        // coordinates, from the prefetched coefficients) follows its gather;
+        // coordinates past 64 are added after the loop, whose loads would
+        // otherwise sit between the stream's.
+        float acc[kRegPasses];
+        float vlr[kLrPre];
+#pragma unroll
+        for (int u = 0; u < kLrPre; ++u) vlr[u] = 0.f;
+        float gv[2][16];  // the T reads of passes p and p + 1
+        gather_issue(T, jq[0], q, gv[0]);
+#pragma unroll
+        for (int p = 0; p < kRegPasses; ++p) {
+            if (p + kAhead < kRegPasses) jq[p + kAhead] = load_pass(p + kAhead);
+            if (p + 1 < kRegPasses) gather_issue(T, jq[p + 1], q, gv[(p + 1) & 1]);
+            __builtin_amdgcn_sched_barrier(0);
+            acc[p] = p < npass ? gather_sum(gv[p & 1]) : 0.f;
+#pragma unroll
+            for (int u = 0; u < kLrPre; ++u) {
+                if (po[u] != p) continue;  // wave-uniform
+                vlr[u] = lr_dot(cpre[u], 16 * q, 0.f);
+                if (rr <= 64) acc[p] += vlr[u];
+            }
+        }
+        if (rr > 64) {
+#pragma unroll
+            for (int u = 0; u < kLrPre; ++u) {
+                const int p = po[u];  // wave-uniform
+                if (p < 0) continue;
+                const float v = lr_rest(p, vlr[u]);
+#pragma unroll
+                for (int pp = 0; pp < kRegPasses; ++pp)
+                    if (pp == p) acc[pp] += v;
+            }
+        }
+        for (uint32_t m = own_rest; LR && m; m &= m - 1) {  // owned passes beyond the prefetched ones
+            const int p = __builtin_ctz(m);
+            const int off = ((kPassCh * p + 16 * wave + lane / 4) * rr + 16 * q) * 2;
+            const uint4 c[2] = {load_coef(cr, off, cend, 16 * q < rr),
+                                load_coef(cr, off + 16, cend, 16 * q + 8 < rr)};
+            float v = lr_dot(c, 16 * q, 0.f);
+            if (rr > 64) v = lr_rest(p, v);
 #pragma unroll
             for (int pp = 0; pp < kRegPasses; ++pp)
                 if (pp == p) acc[pp] += v;
         }
-    }
-    for (uint32_t m = own_rest; LR && m; m &= m - 1) {  // owned passes beyond the prefetched ones
-        const int p = __builtin_ctz(m);
-        const int off = ((kPassCh * p + 16 * wave + lane / 4) * rr + 16 * q) * 2;
-        const uint4 c[2] = {load_coef(cr, off, cend, 16 * q < rr), load_coef(cr, off + 16, cend, 16 * q + 8 < rr)};
-        float v = lr_dot(c, 16 * q, 0.f);
-        if (rr > 64) v = lr_rest(p, v);
+        // quad sums (q0 + q1) + (q2 + q3), in every lane of the quad; lane q of a
+        // quad stores passes 4 m + q
 #pragma unroll
-        for (int pp = 0; pp < kRegPasses; ++pp)
-            if (pp == p) acc[pp] += v;
-    }
-    // quad sums (q0 + q1) + (q2 + q3), in every lane of the quad; lane q of a
-    // quad stores passes 4 m + q
-#pragma unroll
-    for (int p = 0; p < kRegPasses; ++p) {
-        acc[p] += dpp<MOE_DPP_QUAD_XOR1>(acc[p]);
-        acc[p] += dpp<MOE_DPP_QUAD_XOR2>(acc[p]);
-    }
-    float* dst = vp + ((size_t)(r * nslice + s) * 2 + P) * I + 16 * wave + lane / 4;
-#pragma unroll
-    for (int m = 0; m < (kRegPasses + 3) / 4; ++m) {
-        float v = acc[4 * m];
-#pragma unroll
-        for (int x = 1; x < 4; ++x)
-            if (4 * m + x < kRegPasses) v = q == x ? acc[4 * m + x] : v;
-        const int p = 4 * m + q;
-        if (p < min(npass, kRegPasses) && kPassCh * p + 16 * wave + lane / 4 < I) dst[kPassCh * p] = v;
-    }
-    for (int p = kRegPasses; p < npass; ++p) {  // further passes: indices loaded here
-        const int j = kPassCh * p + 16 * wave + lane / 4;
-        const uint4 w = load_quarter<JW>(jr, j * nbk + s * kSlice + 16 * q, jend, vb);
-        float a = gather_quarter(T, w, q);
-        if (LR && lr_owner(kVqWaves * p + wave, nslice) == s) {
-            const int off = (j * rr + 16 * q) * 2;
-            const uint4 c[2] = {load_coef(cr, off, cend, 16 * q < rr), load_coef(cr, off + 16, cend, 16 * q + 8 < rr)};
-            float v = lr_dot(c, 16 * q, 0.f);
-            if (rr > 64) v = lr_rest(p, v);
-            a += v;
+        for (int p = 0; p < kRegPasses; ++p) {
+            acc[p] += dpp<MOE_DPP_QUAD_XOR1>(acc[p]);
+            acc[p] += dpp<MOE_DPP_QUAD_XOR2>(acc[p]);
         }
-        a += dpp<MOE_DPP_QUAD_XOR1>(a);
-        a += dpp<MOE_DPP_QUAD_XOR2>(a);
-        if (q == 0 && j < I) vp[((size_t)(r * nslice + s) * 2 + P) * I + j] = a;
+        float* dst = vp + ((size_t)(r * nslice + s) * 2 + P) * I + 16 * wave + lane / 4;
+#pragma unroll
+        for (int m = 0; m < (kRegPasses + 3) / 4; ++m) {
+            float v = acc[4 * m];
+#pragma unroll
+            for (int x = 1; x < 4; ++x)
+                if (4 * m + x < kRegPasses) v = q == x ? acc[4 * m + x] : v;
+            const int p = 4 * m + q;
+            if (p < min(npass, kRegPasses) && kPassCh * p + 16 * wave + lane / 4 < I) dst[kPassCh * p] = v;
+        }
+        for (int p = kRegPasses; p < npass; ++p) {  // further passes: indices loaded here
+            const int j = kPassCh * p + 16 * wave + lane / 4;
+            const uint4 w = load_quarter<JW>(jr, j * nbk + s * kSlice + 16 * q, jend, vb);
+            float a = gather_quarter(T, w, q);
+            if (LR && lr_owner(kVqWaves * p + wave, nslice) == s) {
+                const int off = (j * rr + 16 * q) * 2;
+                const uint4 c[2] = {load_coef(cr, off, cend, 16 * q < rr),
+                                    load_coef(cr, off + 16, cend, 16 * q + 8 < rr)};
+                float v = lr_dot(c, 16 * q, 0.f);
+                if (rr > 64) v = lr_rest(p, v);
+                a += v;
+            }
+            a += dpp<MOE_DPP_QUAD_XOR1>(a);
+            a += dpp<MOE_DPP_QUAD_XOR2>(a);
+            if (q == 0 && j < I) vp[((size_t)(r * nslice + s) * 2 + P) * I + j] = a;
+        }
     }
 }
 
 template <int D, bool LR, bool ROUTE>
 hipError_t vqt_lr(const int32_t* ids, int R, int k, int E, const VqArgs& vq, const float* h, int H, int I, float* vp,
                   int32_t* err, const SelRoute& route, hipStream_t stream) {
+    // Slice rows of the grid: one per slice while the (route, projection,
+    // slice) workgroups fit on the device at once (two per CU, the LDS of
+    // this kernel's T, on 256 CUs); beyond that a workgroup takes several
+    // slices of its route and projection in turn, so no workgroup waits for
+    // a second round and pays the route, code-book and z set-up again.
     const int nslice = (H / D + kSlice - 1) / kSlice;
-    const dim3 grid((2 * R + 7) / 8 * 8, nslice);
+    const int units = 2 * R * nslice;
+    const int per = (units + kVqResident - 1) / kVqResident;  // slices per workgroup
+    const int ny = (nslice + per - 1) / per;
+    const dim3 grid((2 * R + 7) / 8 * 8, ny);
     // 16-byte index loads when every quarter segment is 16-byte aligned
     if ((H / D) % 16 == 0)
         MOE_LAUNCH((gateup_vqt_kernel<D, 16, LR, ROUTE>), grid, dim3(kVqThreads), 0, stream, ids, R, k,

@@ -428,6 +428,32 @@ def test_vq_block_lengths_ragged(mb, d, H, I, r, K):
     layer.close()
 
 
+@pytest.mark.parametrize("d,H,I,r,M", [(8, 2176, 40, 72, 8), (2, 1088, 33, 8, 4), (4, 1600, 24, 0, 9), (8, 2112, 20, 16, 8)])
+def test_vq_slices_taken_in_turn(mb, d, H, I, r, M):
+    """More (route, projection, slice) units than gate/up workgroups fit on
+    the device at once: each workgroup takes several slices of its route in
+    turn (uneven counts, a short last slice), against the oracle; the decode
+    step gives the separate calls' bits."""
+    import torch
+    say("vq slices in turn", dict(d=d, H=H, I=I, r=r, M=M))
+    wl = synth.small_workload("vq_turn_d%d_%d_%d" % (d, H, I), H=H, I=I, E=64, k=8, M=M, seed=H + I + 7 * d, vq=True,
+                              vq_d=d, lr_r=r, vq_K=256)
+    nbk = H // d
+    nslice = (nbk + 63) // 64
+    assert 2 * M * 8 * nslice > 512 and nbk % 64 != 0, "the case must need several slices per workgroup"
+    inp = synth.layer_inputs(wl, 0)
+    inp["h"] = synth.hidden(wl, 0, 0, M=M)
+    layer = make_layer(mb, wl, inp, M)
+    g = run_step(mb, layer, inp["h"])
+    assert g["err"] == 0
+    ref = O.vqlr_forward(inp["h"], g["ids"], g["w"].astype(np.float64), inp, inp["w_down"])
+    say("  ", check_close(g["y"], ref))
+    y1 = layer.decode_step(to_dev(inp["h"]), M).cpu().numpy()
+    torch.cuda.synchronize()
+    assert np.array_equal(y1.view(np.int32), np.asarray(g["y"], np.float32).view(np.int32))
+    layer.close()
+
+
 @pytest.mark.parametrize("name", ["dense_h2048_i768_e128_k8_m8", "dense_h2048_i768_e128_k8_m16",
                                   "vqlr_h2048_i768_e128_k8_m8_d8_K256_r64", "vqlr_h2048_i768_e128_k8_m16_d8_K256_r64",
                                   "vqlr_h2048_i768_e128_k8_m4_d8_K256_r64"])
