@@ -171,6 +171,7 @@ gateup_vqt_kernel(const int32_t* __restrict__ topk_ids, int R, int k, FastDiv fk
     static_assert(kNTiles * kVqWaves == 16 && kVqThreads <= 1024, "the 16 code tiles are dealt out evenly");
     __shared__ float T[kSlice * kTRow];
     __shared__ float zsm[kMaxR];
+    __shared__ uint4 Aop[4 * MOE_WAVE];  // T's A operand words, M tile m at [m][lane]
     const int r = blockIdx.x >> 1;
     const int P = blockIdx.x & 1;
     const int s0 = blockIdx.y;   // first slice of this workgroup
@@ -218,24 +219,21 @@ gateup_vqt_kernel(const int32_t* __restrict__ topk_ids, int R, int k, FastDiv fk
     const __amdgpu_buffer_rsrc_t hr =
         __builtin_amdgcn_make_buffer_rsrc(const_cast<float*>(h + (size_t)t * H), (short)0, hend, 0x00020000);
     // h of block 16 m + lane % 16 of slice s (zero past the channel's blocks)
-    auto load_h = [&](int s, float (&hx)[4][D]) {
+    auto load_h = [&](int s, int m, float (&hx)[D]) {
         const int L = min(kSlice, nbk - s * kSlice);
+        const int b = 16 * m + lane % 16;
+        const bool in = b < L && (D == 8 ? g < 2 : g == 0);
+        const int off = (s * kSlice + b) * D * 4;
+        if constexpr (D == 2) {
+            const u32x2_t a = __builtin_amdgcn_raw_buffer_load_b64(hr, in ? off : hend, 0, 0);
+            hx[0] = __uint_as_float(a.x);
+            hx[1] = __uint_as_float(a.y);
+        } else {
 #pragma unroll
-        for (int m = 0; m < 4; ++m) {
-            const int b = 16 * m + lane % 16;
-            const bool in = b < L && (D == 8 ? g < 2 : g == 0);
-            const int off = (s * kSlice + b) * D * 4;
-            if constexpr (D == 2) {
-                const u32x2_t a = __builtin_amdgcn_raw_buffer_load_b64(hr, in ? off : hend, 0, 0);
-                hx[m][0] = __uint_as_float(a.x);
-                hx[m][1] = __uint_as_float(a.y);
-            } else {
-#pragma unroll
-                for (int x = 0; x < D; x += 4) {
-                    const u32x4_t a = __builtin_amdgcn_raw_buffer_load_b128(hr, in ? off + 4 * x : hend, 0, 0);
-                    hx[m][x] = __uint_as_float(a.x); hx[m][x + 1] = __uint_as_float(a.y);
-                    hx[m][x + 2] = __uint_as_float(a.z); hx[m][x + 3] = __uint_as_float(a.w);
-                }
+            for (int x = 0; x < D; x += 4) {
+                const u32x4_t a = __builtin_amdgcn_raw_buffer_load_b128(hr, in ? off + 4 * x : hend, 0, 0);
+                hx[x] = __uint_as_float(a.x); hx[x + 1] = __uint_as_float(a.y);
+                hx[x + 2] = __uint_as_float(a.z); hx[x + 3] = __uint_as_float(a.w);
             }
         }
     };
@@ -301,8 +299,6 @@ gateup_vqt_kernel(const int32_t* __restrict__ topk_ids, int R, int k, FastDiv fk
         const int g = lane / 16;  // MFMA K group / operand row group
         const int q = lane % 4;   // gather quarter
         const int L = min(kSlice, nbk - s * kSlice);  // valid blocks of this slice (> 0)
-        float hx[4][D];
-        load_h(s, hx);
 
         // Low-rank quarter of the lane's channel in an owned pass: coordinates
         // 64 c0 + 16 q + x, in rho order; the first 64 from the prefetched
@@ -368,31 +364,37 @@ gateup_vqt_kernel(const int32_t* __restrict__ topk_ids, int R, int k, FastDiv fk
             cpre[u][0] = load_coef(cr, off, cend, use && 16 * q < rr);
             cpre[u][1] = load_coef(cr, off + 16, cend, use && 16 * q + 8 < rr);
         }
-        __builtin_amdgcn_sched_barrier(0);  // every stream load goes out before T waits for its operands
-        __syncthreads();  // the previous slice's T is no longer read (the first: zsm written)
+        __builtin_amdgcn_sched_barrier(0);  // every stream load goes out before the h loads below
+        // The A operand words of M tile m = wave (waves 0..3): h of block
+        // 16 m + lane % 16 split into hi + lo bf16, 8 bf16 of K group g, formed
+        // once per workgroup and shared through LDS.
+        if (wave < 4) {  // uniform
+            float hx[D];
+            load_h(s, wave, hx);
+            uint32_t hi[D], lo[D];
+#pragma unroll
+            for (int x = 0; x < D; ++x) split_bf16(hx[x], hi[x], lo[x]);
+            uint32_t k8[8];  // K slots 8 g .. 8 g + 7 (zero past 2 D)
+            if constexpr (D == 8) {
+#pragma unroll
+                for (int x = 0; x < 8; ++x) k8[x] = g == 0 ? hi[x] : lo[x];
+            } else if constexpr (D == 4) {
+#pragma unroll
+                for (int x = 0; x < 4; ++x) { k8[x] = hi[x]; k8[4 + x] = lo[x]; }
+            } else {
+                k8[0] = hi[0]; k8[1] = hi[1]; k8[2] = lo[0]; k8[3] = lo[1];
+                k8[4] = k8[5] = k8[6] = k8[7] = 0u;
+            }
+            Aop[wave * MOE_WAVE + lane] = make_uint4(k8[0] | (k8[1] << 16), k8[2] | (k8[3] << 16),
+                                                     k8[4] | (k8[5] << 16), k8[6] | (k8[7] << 16));
+        }
+        __syncthreads();  // the previous slice's T is no longer read; the A words (and, the first time, z) written
 
-        // T on the matrix cores (its operands arrived before the stream).
+        // T on the matrix cores.
         {
             uint4 aw[4];  // A operand words of M tile m: 8 bf16 of K group g
 #pragma unroll
-            for (int m = 0; m < 4; ++m) {
-                uint32_t hi[D], lo[D];
-#pragma unroll
-                for (int x = 0; x < D; ++x) split_bf16(hx[m][x], hi[x], lo[x]);
-                uint32_t k8[8];  // K slots 8 g .. 8 g + 7 (zero past 2 D)
-                if constexpr (D == 8) {
-#pragma unroll
-                    for (int x = 0; x < 8; ++x) k8[x] = g == 0 ? hi[x] : lo[x];
-                } else if constexpr (D == 4) {
-#pragma unroll
-                    for (int x = 0; x < 4; ++x) { k8[x] = hi[x]; k8[4 + x] = lo[x]; }
-                } else {
-                    k8[0] = hi[0]; k8[1] = hi[1]; k8[2] = lo[0]; k8[3] = lo[1];
-                    k8[4] = k8[5] = k8[6] = k8[7] = 0u;
-                }
-                aw[m] = make_uint4(k8[0] | (k8[1] << 16), k8[2] | (k8[3] << 16), k8[4] | (k8[5] << 16),
-                                   k8[6] | (k8[7] << 16));
-            }
+            for (int m = 0; m < 4; ++m) aw[m] = Aop[m * MOE_WAVE + lane];
 #pragma unroll
             for (int m = 0; m < 4; ++m)
 #pragma unroll
