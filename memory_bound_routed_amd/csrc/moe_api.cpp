@@ -74,6 +74,17 @@ int64_t align_capacity64(int64_t M, int64_t k, int64_t E, int64_t b) {
     return R + (E < R ? E : R) * (b - 1);
 }
 
+constexpr int kMaxTokens = 4096;  // tokens (and routes) of one call at most
+
+// Bytes of the workspace header: the sticky error word and the router's
+// last-workgroup tickets, room for the largest token count whatever the
+// context's, so that the header and every buffer after it sit at the same
+// offsets for calls of any size.  The no-allocation entry point's calls of
+// different sizes share one array, and its tickets must stay where earlier
+// calls left them (re-armed at zero by their last workgroups) rather than
+// land on another call's partials.
+size_t workspace_header_bytes() { return 64 + sizeof(unsigned) * (1 + (size_t)moe::router_groups(kMaxTokens)); }
+
 moe_status check_config(const moe_config* c) {
     if (c->H <= 0 || c->I <= 0 || c->E <= 0 || c->top_k <= 0 || c->block_b <= 0 || c->max_tokens <= 0 ||
         c->max_keep < 0)
@@ -83,7 +94,7 @@ moe_status check_config(const moe_config* c) {
     if (c->E % 8 || c->E < 8 || c->E > 1024) return MOE_ERR_UNSUPPORTED;
     if (c->top_k > 32 || c->top_k > c->E) return MOE_ERR_UNSUPPORTED;
     if (c->block_b > 64) return MOE_ERR_UNSUPPORTED;
-    if (c->max_tokens > 4096 || (int64_t)c->max_tokens * c->top_k > 4096) return MOE_ERR_UNSUPPORTED;
+    if (c->max_tokens > kMaxTokens || (int64_t)c->max_tokens * c->top_k > kMaxTokens) return MOE_ERR_UNSUPPORTED;
     const int64_t nchunk = ((int64_t)c->max_tokens * c->top_k + 63) / 64;
     if (nchunk * c->E > 6144) return MOE_ERR_UNSUPPORTED;
     if (c->wformat != MOE_WFORMAT_DENSE && c->wformat != MOE_WFORMAT_VQLR) return MOE_ERR_UNSUPPORTED;
@@ -155,7 +166,7 @@ size_t workspace_layout(const moe_config& c, size_t MT, char* base, Workspace* w
     const size_t nbq = c.reader ? (size_t)moe::reader_groups(c.H / 128, nullptr) : 0;
     constexpr int kBufs = 13;
     const size_t sizes[kBufs] = {
-        64 + sizeof(unsigned) * (1 + (size_t)moe::router_groups((int)MT)),  // err flag, router tickets
+        workspace_header_bytes(),                                       // err flag, router tickets
         sizeof(float) * moe::gemv_slices(c.H, c.E) * MT * c.E,          // router partials
         sizeof(float) * zsl * MT * c.lr_r,                              // z = D^T h partials (gate)
         sizeof(float) * zsl * MT * c.lr_r,                              // z partials (up)
@@ -194,9 +205,6 @@ size_t workspace_layout(const moe_config& c, size_t MT, char* base, Workspace* w
     return total;
 }
 
-// Header bytes of the workspace that must be zero before the first call
-// (error word and tickets).
-size_t workspace_header_bytes(size_t MT) { return 64 + sizeof(unsigned) * (1 + (size_t)moe::router_groups((int)MT)); }
 
 hipEvent_t take_event(moe_ctx* ctx) {
     if (!ctx->pool.empty()) {
@@ -675,7 +683,7 @@ moe_status moe_create(const moe_config* cfg, const moe_weights* w, moe_ctx** out
     }
     ctx->ws_bytes = total;
     workspace_layout(*cfg, MT, static_cast<char*>(ctx->ws_mem), &ctx->ws);
-    if (hipMemset(ctx->ws_mem, 0, workspace_header_bytes(MT)) != hipSuccess || hipDeviceSynchronize() != hipSuccess) {
+    if (hipMemset(ctx->ws_mem, 0, workspace_header_bytes()) != hipSuccess || hipDeviceSynchronize() != hipSuccess) {
         hipFree(ctx->ws_mem);
         delete ctx;
         return MOE_ERR_HIP;

@@ -99,6 +99,36 @@ def test_noalloc_decode_step_equals_context_call(mb, name, max_tokens, M1, M2, k
     layer.close()
 
 
+@pytest.mark.gpu
+def test_noalloc_calls_of_growing_and_shrinking_size(mb):
+    """Calls of 4, 200 and 3 tokens in a row on the tiny layer (max_tokens
+    256): the router's tickets of the 200-token call lie past those of the
+    4-token call, where a size-dependent layout would have put the first
+    call's router partials; each call equals the context call bit for bit."""
+    import torch
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+    wl = synth.WORKLOADS["tiny_h256_i128_e16_k2"]
+    inp = synth.layer_inputs(wl, 0)
+    dev = upload_layer(inp)
+    cfg = _cfg(mb, wl, 256, 0)
+    layer = mb.Layer(cfg, dev)
+    hs = to_dev(np.concatenate([synth.hidden(wl, 0, step=s, M=1) for s in range(200)]))
+    for M in (4, 200, 3):
+        say("no-alloc tiny layer, M =", M)
+        ref = _buffers(mb, cfg, M, 0)
+        got = _buffers(mb, cfg, M, 0)
+        h = hs[:M].contiguous()
+        _call(mb.moe_decode_step, (layer.ctx,), ref, h, M, 0)
+        _call(mb.moe_decode_step_noalloc, (cfg, layer.weights), got, h, M, 0)
+        torch.cuda.synchronize()
+        a, b = _outputs(ref, M, 0), _outputs(got, M, 0)
+        for k in a:
+            assert torch.equal(a[k], b[k]), "%s differs at M = %d" % (k, M)
+    assert mb.moe_read_device_error(layer.ctx) == 0
+    layer.close()
+
+
 def test_noalloc_rejects_oversized_workspace_before_any_launch(mb):
     """Host checks only (no GPU needed): a layer whose workspace for this M
     exceeds the 16 MiB array, an M above max_tokens and invalid arguments are
