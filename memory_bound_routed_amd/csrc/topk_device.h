@@ -174,6 +174,30 @@ struct __align__(16) RouteLds {
     int slow;
 };
 
+// The router's slice partials of logit tid (< E) of token t, slices 0 .. 7
+// (and the bias), loaded into registers: route_token_load issues the loads
+// and returns, so that a caller can work while they are in flight;
+// route_token_from adds them (and slices past 8) in slice order.
+constexpr int kRoutePre = 8;
+struct RoutePart {
+    float x[kRoutePre];
+    float bias;
+};
+__device__ __forceinline__ void route_token_load(const float* __restrict__ part, const float* __restrict__ bias,
+                                                 int nslices, int M, int t, int E, RoutePart& rp) {
+    const int tid = threadIdx.x;
+    const int ex = min(tid, E - 1);
+    if ((tid / MOE_WAVE) * MOE_WAVE < E) {  // uniform: the waves that hold experts
+#pragma unroll
+        for (int u = 0; u < kRoutePre; ++u) rp.x[u] = part[((size_t)min(u, nslices - 1) * M + t) * E + ex];
+        rp.bias = bias ? bias[ex] : 0.f;
+    } else {
+#pragma unroll
+        for (int u = 0; u < kRoutePre; ++u) rp.x[u] = 0.f;
+        rp.bias = 0.f;
+    }
+}
+
 // One token's routing inside a workgroup of NT threads (E <= NT, k <= 32):
 // the router's slice partials part[slice][t][e] of M tokens added in slice
 // order (+ bias), the top-k by (logit, expert) -- by one wave (wave_topk)
@@ -183,24 +207,26 @@ struct __align__(16) RouteLds {
 // L.sel_e, sel_l[0 .. k) readable by every thread, and with `weights` (or in
 // the writer) sel_w[0 .. k) too (each path ends with a barrier); the writer
 // (uniform) also stores the token's logits (when logits is not null), ids
-// and weights.
+// and weights.  route_token_from takes the first kRoutePre slices (and the
+// bias) from route_token_load.
 template <int NT>
-__device__ inline void route_token(const float* __restrict__ part, const float* __restrict__ bias, int nslices,
-                                   int M, int t, int E, int k, bool writer, float* __restrict__ logits,
-                                   int32_t* __restrict__ ids, float* __restrict__ wts, RouteLds<NT>& L,
-                                   bool weights = true) {
+__device__ inline void route_token_from(const RoutePart& rp, const float* __restrict__ part,
+                                        const float* __restrict__ bias, int nslices, int M, int t, int E, int k,
+                                        bool writer, float* __restrict__ logits, int32_t* __restrict__ ids,
+                                        float* __restrict__ wts, RouteLds<NT>& L, bool weights = true) {
     const int tid = threadIdx.x;
     if (tid < E) {
         float lg = 0.f;
-        const float bv = bias ? bias[tid] : 0.f;
-        for (int sl0 = 0; sl0 < nslices; sl0 += 8) {  // eight slices in flight
+#pragma unroll
+        for (int u = 0; u < kRoutePre; ++u) lg += u < nslices ? rp.x[u] : 0.f;  // slice order
+        for (int sl0 = kRoutePre; sl0 < nslices; sl0 += 8) {  // eight slices in flight
             float xs[8];
 #pragma unroll
             for (int u = 0; u < 8; ++u) xs[u] = part[((size_t)min(sl0 + u, nslices - 1) * M + t) * E + tid];
 #pragma unroll
-            for (int u = 0; u < 8; ++u) lg += sl0 + u < nslices ? xs[u] : 0.f;  // slice order
+            for (int u = 0; u < 8; ++u) lg += sl0 + u < nslices ? xs[u] : 0.f;
         }
-        if (bias) lg += bv;
+        if (bias) lg += rp.bias;
         if (logits && writer) logits[(size_t)t * E + tid] = lg;
         L.skey[tid] = order_key((lg != lg) ? -INFINITY : lg, tid);  // NaN ranks as -inf
     }
@@ -230,6 +256,16 @@ __device__ inline void route_token(const float* __restrict__ part, const float* 
         }
     }
     __syncthreads();
+}
+
+template <int NT>
+__device__ inline void route_token(const float* __restrict__ part, const float* __restrict__ bias, int nslices,
+                                   int M, int t, int E, int k, bool writer, float* __restrict__ logits,
+                                   int32_t* __restrict__ ids, float* __restrict__ wts, RouteLds<NT>& L,
+                                   bool weights = true) {
+    RoutePart rp;
+    route_token_load(part, bias, nslices, M, t, E, rp);
+    route_token_from<NT>(rp, part, bias, nslices, M, t, E, k, writer, logits, ids, wts, L, weights);
 }
 
 }  // namespace moe

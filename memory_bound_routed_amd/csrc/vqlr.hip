@@ -243,6 +243,56 @@ gateup_vqt_kernel(const int32_t* __restrict__ topk_ids, int R, int k, FastDiv fk
     };
     // z partials of coordinate rho = tid (the first kZBatch slices; threads
     // past r load nothing)
+    // The A operand words of M tile m = wave (waves 0..3) for slice s: h of
+    // block 16 m + lane % 16 split into hi + lo bf16, 8 bf16 of K group g,
+    // formed once per workgroup and shared through LDS (the caller's barrier
+    // publishes them).
+    auto make_A = [&](const float (&hx)[D], int ln) {
+        const int gg = ln / 16;
+        uint32_t hi[D], lo[D];
+#pragma unroll
+        for (int x = 0; x < D; ++x) split_bf16(hx[x], hi[x], lo[x]);
+        uint32_t k8[8];  // K slots 8 g .. 8 g + 7 (zero past 2 D)
+        if constexpr (D == 8) {
+#pragma unroll
+            for (int x = 0; x < 8; ++x) k8[x] = gg == 0 ? hi[x] : lo[x];
+        } else if constexpr (D == 4) {
+#pragma unroll
+            for (int x = 0; x < 4; ++x) { k8[x] = hi[x]; k8[4 + x] = lo[x]; }
+        } else {
+            k8[0] = hi[0]; k8[1] = hi[1]; k8[2] = lo[0]; k8[3] = lo[1];
+            k8[4] = k8[5] = k8[6] = k8[7] = 0u;
+        }
+        Aop[wave * MOE_WAVE + ln] = make_uint4(k8[0] | (k8[1] << 16), k8[2] | (k8[3] << 16),
+                                               k8[4] | (k8[5] << 16), k8[6] | (k8[7] << 16));
+    };
+    // T on the matrix cores from the A words in LDS; wave w forms codes
+    // 16 kNTiles w .. + 16 kNTiles - 1.
+    auto make_T = [&](int ln) {
+        const int gg = ln / 16;
+        uint4 aw[4];  // A operand words of M tile m: 8 bf16 of K group g
+#pragma unroll
+        for (int m = 0; m < 4; ++m) aw[m] = Aop[m * MOE_WAVE + ln];
+#pragma unroll
+        for (int m = 0; m < 4; ++m)
+#pragma unroll
+            for (int u = 0; u < kNTiles; ++u) {
+                const f32x4_t zero = {0.f, 0.f, 0.f, 0.f};
+                const f32x4_t d4 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(
+                    __builtin_bit_cast(bf16x8_t, aw[m]), __builtin_bit_cast(bf16x8_t, bw[u]), zero, 0, 0, 0);
+                // lane holds T[16 m + 4 g + i][16 (kNTiles wave + u) + lane % 16]
+                float* dst = T + (16 * m + 4 * gg) * kTRow + 16 * (kNTiles * wave + u) + ln % 16;
+#pragma unroll
+                for (int i = 0; i < 4; ++i) dst[i * kTRow] = d4[i];
+            }
+    };
+
+    // h of the first slice, requested before the routing's loads (a wait
+    // for it then does not wait for them too).
+    float hx0[D];
+    if (wave < 4) load_h(s0, wave, hx0);  // uniform
+    // z partials of coordinate rho = tid (the first kZBatch slices; threads
+    // past r load nothing)
     float zx[kZBatch];
 #pragma unroll
     for (int u = 0; u < kZBatch; ++u) zx[u] = 0.f;
@@ -251,18 +301,29 @@ gateup_vqt_kernel(const int32_t* __restrict__ topk_ids, int R, int k, FastDiv fk
         for (int u = 0; u < kZBatch; ++u)
             zx[u] = zp[((size_t)min(u, vq.zslices - 1) * vq.M + t) * rr + min(tid, rr - 1)];
     }
+    RoutePart rp;
+    if constexpr (ROUTE) route_token_load(route.part, route.bias, route.nslices, route.M, t, E, rp);
+    // T of the first slice does not depend on the route: it is formed while
+    // the routing's loads are in flight.
+    if (wave < 4) make_A(hx0, lane);  // uniform
+    __syncthreads();  // the A words written
+    make_T(lane);
     if constexpr (ROUTE) {
         __shared__ RouteLds<kVqThreads> rl;
         const int slot = r - t * k;
-        route_token<kVqThreads>(route.part, route.bias, route.nslices, route.M, t, E, k, P == 0 && s0 == 0 && slot == 0,
-                              route.logits, route.ids, route.wts, rl, false);
+        route_token_from<kVqThreads>(rp, route.part, route.bias, route.nslices, route.M, t, E, k,
+                                     P == 0 && s0 == 0 && slot == 0, route.logits, route.ids, route.wts, rl, false);
         e = __builtin_amdgcn_readfirstlane(rl.sel_e[slot]);
     }
     if (e < 0 || e >= E) {  // an invalid route has no output (uniform)
         if (P == 0 && s0 == 0 && tid == 0) atomicOr(err, DEVERR_BAD_ROUTE_ID);
         return;
     }
-    __builtin_amdgcn_sched_barrier(0);  // keeps the loads above ahead of the stream below
+    // The z partials pass through an empty asm here, after the routing: else
+    // the compiler starts their sum next to their loads, and the wait for the
+    // first of them delays the routing's own loads by a memory round trip.
+#pragma unroll
+    for (int u = 0; u < kZBatch; ++u) asm volatile("" : "+v"(zx[u]));
 
     const int npass = (I + kPassCh - 1) / kPassCh;
     const int jend = I * nbk;      // bytes of the expert's index rows
@@ -271,6 +332,20 @@ gateup_vqt_kernel(const int32_t* __restrict__ topk_ids, int R, int k, FastDiv fk
         const_cast<uint8_t*>(Jb + (size_t)e * jend), (short)0, jend, 0x00020000);
     const __amdgpu_buffer_rsrc_t cr = __builtin_amdgcn_make_buffer_rsrc(
         const_cast<uint16_t*>(Cb + (size_t)e * I * rr), (short)0, cend, 0x00020000);
+    // The index stream: pass p, lane quarter q of channel 128 p + 16 wave +
+    // lane / 4 of slice s (channels past I read past the resource's end).
+    auto load_pass = [&](int s, int p, int ln) {
+        const int qq = ln % 4;
+        const int L = min(kSlice, nbk - s * kSlice);  // valid blocks of slice s (> 0)
+        const int vb = min(max(L - 16 * qq, 0), 16);
+        const int j = kPassCh * p + 16 * wave + ln / 4;
+        return load_quarter<JW>(jr, j * nbk + s * kSlice + 16 * qq, jend, p < npass ? vb : 0);
+    };
+    // the first slice's first passes go out as soon as the expert is known
+    uint4 jq[kRegPasses];
+#pragma unroll
+    for (int p = 0; p < kAhead; ++p) jq[p] = load_pass(s0, p, lane);
+    __builtin_amdgcn_sched_barrier(0);  // keeps the loads above ahead of what follows
 
     // z (slice partials in slice order) into LDS, read after the first
     // slice's barrier; coordinates past 256 and slices past kZBatch are
@@ -300,20 +375,21 @@ gateup_vqt_kernel(const int32_t* __restrict__ topk_ids, int R, int k, FastDiv fk
         // and held in registers across it.
         const int lane_s = opaque_int(lane);
         const int lane = lane_s;
-        const int g = lane / 16;  // MFMA K group / operand row group
         const int q = lane % 4;   // gather quarter
         const int L = min(kSlice, nbk - s * kSlice);  // valid blocks of this slice (> 0)
+        const int vb = min(max(L - 16 * q, 0), 16);
+        const bool first = s == s0;
 
         // Low-rank quarter of the lane's channel in an owned pass: coordinates
         // 64 c0 + 16 q + x, in rho order; the first 64 from the prefetched
         // coefficients, further ones loaded here.
         auto lr_dot = [&](const uint4 (&c)[2], int rho0, float acc) {
-    #pragma unroll
+#pragma unroll
             for (int u = 0; u < 2; ++u) {
                 float f[8];
                 unpack8(c[u], f);
                 const int rb = min(rho0 + 8 * u, kMaxR - 8);  // coefficients past r are zero
-    #pragma unroll
+#pragma unroll
                 for (int x = 0; x < 8; ++x) acc = fmaf(f[x], zsm[rb + x], acc);
             }
             return acc;
@@ -329,16 +405,10 @@ gateup_vqt_kernel(const int32_t* __restrict__ topk_ids, int R, int k, FastDiv fk
             return acc;
         };
 
-        // The index stream: pass p, lane quarter q of channel 128 p + 16 wave
-        // + lane / 4 (channels past I read past the resource's end).
-        const int vb = min(max(L - 16 * q, 0), 16);
-        auto load_pass = [&](int p) {
-            const int j = kPassCh * p + 16 * wave + lane / 4;
-            return load_quarter<JW>(jr, j * nbk + s * kSlice + 16 * q, jend, p < npass ? vb : 0);
-        };
-        uint4 jq[kRegPasses];
+        if (!first) {
 #pragma unroll
-        for (int p = 0; p < kAhead; ++p) jq[p] = load_pass(p);
+            for (int p = 0; p < kAhead; ++p) jq[p] = load_pass(s, p, lane);
+        }
         // The passes p < kRegPasses whose 16-channel chunk c = kVqWaves p +
         // wave this slice owns for the low-rank term: lane p of the wave
         // tests pass p, and the ballot is the wave's (uniform) mask.
@@ -369,50 +439,16 @@ gateup_vqt_kernel(const int32_t* __restrict__ topk_ids, int R, int k, FastDiv fk
             cpre[u][1] = load_coef(cr, off + 16, cend, use && 16 * q + 8 < rr);
         }
         __builtin_amdgcn_sched_barrier(0);  // every stream load goes out before the h loads below
-        // The A operand words of M tile m = wave (waves 0..3): h of block
-        // 16 m + lane % 16 split into hi + lo bf16, 8 bf16 of K group g, formed
-        // once per workgroup and shared through LDS.
-        if (wave < 4) {  // uniform
-            float hx[D];
-            load_h(s, wave, hx);
-            uint32_t hi[D], lo[D];
-#pragma unroll
-            for (int x = 0; x < D; ++x) split_bf16(hx[x], hi[x], lo[x]);
-            uint32_t k8[8];  // K slots 8 g .. 8 g + 7 (zero past 2 D)
-            if constexpr (D == 8) {
-#pragma unroll
-                for (int x = 0; x < 8; ++x) k8[x] = g == 0 ? hi[x] : lo[x];
-            } else if constexpr (D == 4) {
-#pragma unroll
-                for (int x = 0; x < 4; ++x) { k8[x] = hi[x]; k8[4 + x] = lo[x]; }
-            } else {
-                k8[0] = hi[0]; k8[1] = hi[1]; k8[2] = lo[0]; k8[3] = lo[1];
-                k8[4] = k8[5] = k8[6] = k8[7] = 0u;
+        if (!first) {  // T of this slice (the first slice's was formed during the routing)
+            if (wave < 4) {  // uniform
+                float hx[D];
+                load_h(s, wave, hx);
+                make_A(hx, lane);
             }
-            Aop[wave * MOE_WAVE + lane] = make_uint4(k8[0] | (k8[1] << 16), k8[2] | (k8[3] << 16),
-                                                     k8[4] | (k8[5] << 16), k8[6] | (k8[7] << 16));
+            __syncthreads();  // the previous slice's T is no longer read; the A words written
+            make_T(lane);
         }
-        __syncthreads();  // the previous slice's T is no longer read; the A words (and, the first time, z) written
-
-        // T on the matrix cores.
-        {
-            uint4 aw[4];  // A operand words of M tile m: 8 bf16 of K group g
-#pragma unroll
-            for (int m = 0; m < 4; ++m) aw[m] = Aop[m * MOE_WAVE + lane];
-#pragma unroll
-            for (int m = 0; m < 4; ++m)
-#pragma unroll
-                for (int u = 0; u < kNTiles; ++u) {
-                    const f32x4_t zero = {0.f, 0.f, 0.f, 0.f};
-                    const f32x4_t d4 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(
-                        __builtin_bit_cast(bf16x8_t, aw[m]), __builtin_bit_cast(bf16x8_t, bw[u]), zero, 0, 0, 0);
-                    // lane holds T[16 m + 4 g + i][16 (kNTiles wave + u) + lane % 16]
-                    float* dst = T + (16 * m + 4 * g) * kTRow + 16 * (kNTiles * wave + u) + lane % 16;
-#pragma unroll
-                    for (int i = 0; i < 4; ++i) dst[i * kTRow] = d4[i];
-                }
-        }
-        __syncthreads();
+        __syncthreads();  // T (and, the first time, z) written
 
         // The gathers, pass by pass as the index words arrive: a workgroup's
         // share of the stream takes about as long as T and the gathers
@@ -431,7 +467,7 @@ gateup_vqt_kernel(const int32_t* __restrict__ topk_ids, int R, int k, FastDiv fk
         gather_issue(T, jq[0], q, gv[0]);
 #pragma unroll
         for (int p = 0; p < kRegPasses; ++p) {
-            if (p + kAhead < kRegPasses) jq[p + kAhead] = load_pass(p + kAhead);
+            if (p + kAhead < kRegPasses) jq[p + kAhead] = load_pass(s, p + kAhead, lane);
             if (p + 1 < kRegPasses) gather_issue(T, jq[p + 1], q, gv[(p + 1) & 1]);
             __builtin_amdgcn_sched_barrier(0);
             acc[p] = p < npass ? gather_sum(gv[p & 1]) : 0.f;
