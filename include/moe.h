@@ -293,7 +293,12 @@ moe_status moe_expert_forward(moe_ctx *ctx, const float *h, int32_t M,
  * GEMV launch also rotates and scans h in workgroups of its own, and every
  * screening workgroup routes its token before reading the sketch (E <= 256;
  * above, the routing is moe_route_topk's and the rotation a launch of its
- * own).  Otherwise the calls above are made as they are.
+ * own).  With VQ + low-rank weights (E <= 256, k <= 32) the router GEMV
+ * launch also forms the z = D^T h partials, every gate/up workgroup routes
+ * its token from the router's partials, and up to 64 routes the down
+ * launch adds the gate/up partials and aligns the routes itself (above, a
+ * finishing launch forms SiLU(gate) * up and the plan before it).  Otherwise
+ * the calls above are made as they are.
  *  h, y: fp32 [M][H]; topk_ids, topk_w: [M][k] out; logits_out: [M][E] out
  *  or NULL; sorted_routes, block_expert, counts: as moe_align_blocks.
  */
@@ -455,7 +460,7 @@ enum {
     MOE_KERNEL_ROUTER_ALIGN = 11, /* router + top-k + softmax + alignment (one launch) */
     MOE_KERNEL_ROUTER_GEMV = 12,  /* router GEMV slice partials only (decode step) */
     MOE_KERNEL_DECODE_FUSED = 13, /* per-workgroup top-k + softmax + plan, then as EXPERT_FUSED */
-    MOE_KERNEL_VQ_FINISH = 14,    /* VQ + low rank: slice partials -> SiLU(gate) * up */
+    MOE_KERNEL_VQ_FINISH = 14,    /* VQ + low rank, more than 64 routes: gate/up partials -> SiLU(gate) * up */
     MOE_KERNEL_READER_ROTATE = 15,  /* reader: rotation and scan of h (own launch) */
     MOE_KERNEL_READER_SCREEN = 16,  /* reader: sketch estimates (routing first in the decode step) */
     MOE_KERNEL_READER_SELECT = 17,  /* reader: output-level scores and top K of moe_reader_inspect (the

@@ -31,6 +31,7 @@
 // Both feed combine_kernel: y[t] = sum over the token's routes and chunks.
 #include <type_traits>
 
+#include "align_device.h"
 #include "device_common.h"
 #include "launch.h"
 #include "topk_device.h"
@@ -726,10 +727,85 @@ __device__ __forceinline__ void down_load_p(const float* __restrict__ p, int sr,
     }
 }
 
-template <int CB, int RT>
+// The staged s values of a stage (rows js .. js + jn) from the VQ gate/up
+// partials vp [R][ny][2][I]: s_i[j] = a_i * SiLU(og) * ou, og and ou the sums
+// over the partial rows y in order, for the pass's routes i (8 slots; slots
+// not in `valid` get 0).  Thread t takes rows t, t + 256, ... of each valid
+// route, all of a route's loads in flight (partial rows in batches of 4).
+// Rows nz .. (nz >= jn) of each slot are zero-filled.  MINOR: dsm[j * 8 + i]
+// (the vector-ALU pass); else dsm[i * kDownStage + j] (the matrix-core pass).
+// first() (the caller's first weight requests) runs once the first slot's
+// loads are out, then a barrier (the previous stage's s is no longer read)
+// precedes the first write: waiting for those loads does not wait for the
+// weights.
+constexpr int kVqRowsPT = kDownStage / kThreads;  // rows per thread and stage
+
+template <bool MINOR, typename F>
+__device__ __forceinline__ void stage_vq(const VqP& vq, int I, int js, int jn, int nz, const int (&rr)[8],
+                                         const float (&ra)[8], uint32_t valid, float* dsm, F&& first) {
+    const int tid = threadIdx.x;
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+        float sv[kVqRowsPT];
+        if ((valid >> i) & 1) {  // uniform
+            const float* src = vq.vp + (size_t)rr[i] * vq.ny * 2 * I + js;
+            float og[kVqRowsPT], ou[kVqRowsPT];
+#pragma unroll
+            for (int u = 0; u < kVqRowsPT; ++u) og[u] = ou[u] = 0.f;
+            constexpr int YB = 4;  // partial rows per batch (8 measured slower: fewer waves per SIMD)
+            for (int y0 = 0; y0 < vq.ny; y0 += YB) {
+                float g4[kVqRowsPT][YB], u4[kVqRowsPT][YB];
+#pragma unroll
+                for (int u = 0; u < kVqRowsPT; ++u) {
+                    const int j = min(tid + kThreads * u, jn - 1);
+#pragma unroll
+                    for (int y = 0; y < YB; ++y) {
+                        const int yy = min(y0 + y, vq.ny - 1);
+                        g4[u][y] = src[(size_t)(2 * yy) * I + j];
+                        u4[u][y] = src[(size_t)(2 * yy + 1) * I + j];
+                    }
+                }
+                if (i == 0 && y0 == 0) {  // uniform
+                    first();
+                    __syncthreads();
+                }
+#pragma unroll
+                for (int u = 0; u < kVqRowsPT; ++u)
+#pragma unroll
+                    for (int y = 0; y < YB; ++y) {
+                        og[u] += y0 + y < vq.ny ? g4[u][y] : 0.f;
+                        ou[u] += y0 + y < vq.ny ? u4[u][y] : 0.f;
+                    }
+            }
+#pragma unroll
+            for (int u = 0; u < kVqRowsPT; ++u) sv[u] = ra[i] * silu_mul(og[u], ou[u]);
+        } else {
+#pragma unroll
+            for (int u = 0; u < kVqRowsPT; ++u) sv[u] = 0.f;
+            if (i == 0) {  // uniform
+                first();
+                __syncthreads();
+            }
+        }
+#pragma unroll
+        for (int u = 0; u < kVqRowsPT; ++u) {
+            const int j = tid + kThreads * u;
+            if (j < nz) {
+                const float v = j < jn ? sv[u] : 0.f;
+                if (MINOR)
+                    dsm[j * 8 + i] = v;
+                else
+                    dsm[i * kDownStage + j] = v;
+            }
+        }
+    }
+}
+
+template <int CB, int RT, bool VQ>
 __device__ __forceinline__ void down_pass(int e, int H, int I, const uint16_t* __restrict__ Wd,
-                                          const float* __restrict__ p, const int (&rr)[8], const float (&ra)[8],
-                                          uint32_t valid, float* __restrict__ part, float* dsm) {
+                                          const float* __restrict__ p, const VqP& vq, const int (&rr)[8],
+                                          const float (&ra)[8], uint32_t valid, float* __restrict__ part,
+                                          float* dsm) {
     constexpr int TPR = CB / 8;
     constexpr int RGS = kThreads / TPR;
     const int tid = threadIdx.x;
@@ -791,18 +867,24 @@ __device__ __forceinline__ void down_pass(int e, int H, int I, const uint16_t* _
                 }
             }
         };
-        // stage s (the p loads go out before the first weights)
-        float4 pv[kDownQuads];
-        down_load_p(p, sr, I, js, jn, pv);
-        issue(w0, 0);
-        __syncthreads();  // the previous stage's s is no longer read
+        if constexpr (VQ) {
+            // stage s from the gate/up partials (the first weights go out
+            // right after the first route's partial loads)
+            stage_vq<true>(vq, I, js, jn, jn, rr, ra, valid, dsm, [&] { issue(w0, 0); });
+        } else {
+            // stage s (the p loads go out before the first weights)
+            float4 pv[kDownQuads];
+            down_load_p(p, sr, I, js, jn, pv);
+            issue(w0, 0);
+            __syncthreads();  // the previous stage's s is no longer read
 #pragma unroll
-        for (int u = 0; u < kDownQuads; ++u) {
-            const int j4 = 4 * ((tid >> 3) + (kThreads / 8) * u);
-            const float v4[4] = {pv[u].x, pv[u].y, pv[u].z, pv[u].w};
+            for (int u = 0; u < kDownQuads; ++u) {
+                const int j4 = 4 * ((tid >> 3) + (kThreads / 8) * u);
+                const float v4[4] = {pv[u].x, pv[u].y, pv[u].z, pv[u].w};
 #pragma unroll
-            for (int c = 0; c < 4; ++c)
-                if (j4 + c < jn) dsm[(j4 + c) * 8 + si] = sv ? sa * v4[c] : 0.f;
+                for (int c = 0; c < 4; ++c)
+                    if (j4 + c < jn) dsm[(j4 + c) * 8 + si] = sv ? sa * v4[c] : 0.f;
+            }
         }
         __syncthreads();
         for (int u0 = 0; u0 < nu; u0 += 2 * kDownNB) {
@@ -875,10 +957,11 @@ __device__ __forceinline__ void down_pass(int e, int H, int I, const uint16_t* _
 // column group in wave order, and row i of the result is route i's partial.
 constexpr int kMfmaTile = 32;
 
-template <int CB>
+template <int CB, bool VQ>
 __device__ __forceinline__ void down_pass_mfma(int e, int H, int I, const uint16_t* __restrict__ Wd,
-                                               const float* __restrict__ p, const int (&rr)[8], const float (&ra)[8],
-                                               uint32_t valid, float* __restrict__ part, float* dsm) {
+                                               const float* __restrict__ p, const VqP& vq, const int (&rr)[8],
+                                               const float (&ra)[8], uint32_t valid, float* __restrict__ part,
+                                               float* dsm) {
     constexpr int NCG = CB / 128, NKG = kWaves / NCG;
     static_assert((CB == 128 || CB == 256) && kWaves == 4, "column groups of 128 over four waves");
     typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
@@ -916,21 +999,29 @@ __device__ __forceinline__ void down_pass_mfma(int e, int H, int I, const uint16
                 w[i] = load_stream16(wbase + (size_t)(js + jl) * H);
             }
         };
-        // stage s (the p loads go out before the first weights; one by one
-        // here: the 16-byte form of the VALU pass measured slower in this one)
-        constexpr int SPT = kDownStage / (kThreads / 8);
-        float pv[SPT];
+        if constexpr (VQ) {
+            // stage s from the gate/up partials (the first weights go out
+            // right after the first route's partial loads)
+            stage_vq<false>(vq, I, js, jn, nt * kMfmaTile, rr, ra, valid, dsm, [&] {
+                if (kh < nt) issue(wb[0], kh);
+            });
+        } else {
+            // stage s (the p loads go out before the first weights; one by one
+            // here: the 16-byte form of the VALU pass measured slower in this one)
+            constexpr int SPT = kDownStage / (kThreads / 8);
+            float pv[SPT];
 #pragma unroll
-        for (int u = 0; u < SPT; ++u) {
-            const int jj = min((tid >> 3) + (kThreads / 8) * u, jn - 1);
-            pv[u] = p[(size_t)sr * I + js + jj];
-        }
-        if (kh < nt) issue(wb[0], kh);
-        __syncthreads();  // the previous stage's s is no longer read
+            for (int u = 0; u < SPT; ++u) {
+                const int jj = min((tid >> 3) + (kThreads / 8) * u, jn - 1);
+                pv[u] = p[(size_t)sr * I + js + jj];
+            }
+            if (kh < nt) issue(wb[0], kh);
+            __syncthreads();  // the previous stage's s is no longer read
 #pragma unroll
-        for (int u = 0; u < SPT; ++u) {
-            const int jj = (tid >> 3) + (kThreads / 8) * u;
-            if (jj < nt * kMfmaTile) dsm[si * kDownStage + jj] = (sv && jj < jn) ? sa * pv[u] : 0.f;
+            for (int u = 0; u < SPT; ++u) {
+                const int jj = (tid >> 3) + (kThreads / 8) * u;
+                if (jj < nt * kMfmaTile) dsm[si * kDownStage + jj] = (sv && jj < jn) ? sa * pv[u] : 0.f;
+            }
         }
         __syncthreads();
         // one tile: A from the staged s of channels kt*32 + rsub .., B from w
@@ -1020,16 +1111,92 @@ __device__ __forceinline__ void down_pass_mfma(int e, int H, int I, const uint16
     __syncthreads();  // dsm is reused by the next pass
 }
 
-template <int CB, bool MFMA>
+// The pass of up to 8 rows (routes rr[i], affinities ra[i], slots in valid).
+template <int CB, bool MFMA, bool VQ>
+__device__ __forceinline__ void down_rows(int e, int H, int I, const uint16_t* __restrict__ Wd,
+                                          const float* __restrict__ p, const VqP& vq, const int (&rr)[8],
+                                          const float (&ra)[8], uint32_t valid, float* __restrict__ part,
+                                          float* dsm) {
+    const int nv = 32 - __builtin_clz(valid);  // rows up to the last route
+    if constexpr (MFMA)
+        down_pass_mfma<CB, VQ>(e, H, I, Wd, p, vq, rr, ra, valid, part, dsm);
+    else if (nv <= 2)
+        down_pass<CB, 2, VQ>(e, H, I, Wd, p, vq, rr, ra, valid, part, dsm);
+    else if (nv <= 4)
+        down_pass<CB, 4, VQ>(e, H, I, Wd, p, vq, rr, ra, valid, part, dsm);
+    else
+        down_pass<CB, 8, VQ>(e, H, I, Wd, p, vq, rr, ra, valid, part, dsm);
+}
+
+// VQ: p from the gate/up partials (stage_vq).  ALIGN (R <= 64): no plan is
+// read; lane r of every wave loads route r's id and affinity, the ballots of
+// the id bits give each expert's count, rank and the blocks before it (the
+// canonical plan of align_device.h), and block blk is found among them:
+// its expert and its routes (the routes of that expert ranked b (blk -
+// first block) .. + b - 1, ascending).  Workgroup (0, 0) also writes the
+// whole plan.
+template <int CB, bool MFMA, bool VQ, bool ALIGN>
 __global__ void __launch_bounds__(kThreads)
 down_kernel(PlanArgs plan, int H, int I, const uint16_t* __restrict__ Wd, const float* __restrict__ p,
-            const float* __restrict__ topk_w, float* __restrict__ part, int32_t* __restrict__ err) {
+            const float* __restrict__ topk_w, float* __restrict__ part, int32_t* __restrict__ err, VqP vq,
+            AlignOut ao) {
     static_assert(kWaves == 4, "the final wave sum is written for four waves");
     extern __shared__ __align__(16) float dsm[];
     const int blk = blockIdx.y;
     const int b = plan.b;
     const int tid = threadIdx.x;
     const int lane = tid % MOE_WAVE;
+    if constexpr (ALIGN) {
+        const int R = plan.R;
+        const int raw = lane < R ? plan.topk_ids[lane] : 0;
+        const float wv = topk_w[min(lane, R - 1)];
+        const bool ok = lane < R && raw >= 0 && raw < plan.E;
+        if (blk == 0 && blockIdx.x == 0 && tid < MOE_WAVE)
+            align_wave([&](int) { return raw; }, R, plan.E, plan.fb, ao.sorted_routes, ao.block_expert, ao.counts,
+                       err);
+        const int id = ok ? raw : 0;
+        const uint64_t V = __ballot(ok);
+        uint64_t bs[kIdBits];
+        id_ballots(id, ok, bs);
+        uint64_t eq, lt;
+        id_match(id, V, bs, eq, lt);
+        const int cnt = __popcll(eq);
+        const bool first = ok && mbcnt64(eq) == 0;
+        const int nblk = first ? (int)plan.fb.div(cnt + b - 1) : 0;
+        int before = 0;
+#pragma unroll
+        for (int q = 0; q < 7; ++q) {  // nblk <= 64
+            const uint64_t F = __ballot(first && ((nblk >> q) & 1));
+            before += __popcll(lt & F) << q;
+        }
+        const uint64_t own = __ballot(first && before <= blk && blk < before + nblk);
+        if (!own) return;  // past the last block (uniform)
+        const int L = __builtin_ctzll(own);
+        const int e = __builtin_amdgcn_readlane(id, L);
+        const int skip = (blk - __builtin_amdgcn_readlane(before, L)) * b;  // routes of e in earlier blocks
+        const uint32_t elo = __builtin_amdgcn_readlane((uint32_t)eq, L), ehi = __builtin_amdgcn_readlane((uint32_t)(eq >> 32), L);
+        uint64_t rest = ((uint64_t)ehi << 32) | elo;  // the routes of e, ascending
+        for (int i = 0; i < skip; ++i) rest &= rest - 1;
+        for (int q0 = 0; q0 < b && rest; q0 += 8) {  // uniform
+            int rr[8];
+            float ra[8];
+            uint32_t valid = 0;
+#pragma unroll
+            for (int i = 0; i < 8; ++i) {
+                rr[i] = 0;
+                ra[i] = 0.f;
+                if (rest && q0 + i < b) {
+                    const int q = __builtin_ctzll(rest);
+                    rest &= rest - 1;
+                    rr[i] = q;
+                    ra[i] = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(wv), q));
+                    valid |= 1u << i;
+                }
+            }
+            down_rows<CB, MFMA, VQ>(e, H, I, Wd, p, vq, rr, ra, valid, part, dsm);
+        }
+        return;
+    }
     // First round: counts, the block's expert, its rows (lane q holds row q).
     int nb = plan.counts[0];
     const int e = plan.block_expert[blk];
@@ -1062,15 +1229,7 @@ down_kernel(PlanArgs plan, int H, int I, const uint16_t* __restrict__ Wd, const 
             rr[i] = ((valid >> i) & 1) ? __builtin_amdgcn_readlane(rv, q) : 0;
             ra[i] = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(av), q));
         }
-        const int nv = 32 - __builtin_clz(valid);  // rows up to the last route
-        if constexpr (MFMA)
-            down_pass_mfma<CB>(e, H, I, Wd, p, rr, ra, valid, part, dsm);
-        else if (nv <= 2)
-            down_pass<CB, 2>(e, H, I, Wd, p, rr, ra, valid, part, dsm);
-        else if (nv <= 4)
-            down_pass<CB, 4>(e, H, I, Wd, p, rr, ra, valid, part, dsm);
-        else
-            down_pass<CB, 8>(e, H, I, Wd, p, rr, ra, valid, part, dsm);
+        down_rows<CB, MFMA, VQ>(e, H, I, Wd, p, vq, rr, ra, valid, part, dsm);
     }
 }
 
@@ -1224,22 +1383,40 @@ hipError_t launch_gateup_dense(const PlanArgs& plan, const float* h, int H, int 
     return hipErrorInvalidValue;
 }
 
+namespace {
+template <int CB, bool MFMA>
+hipError_t down_cb(const PlanArgs& plan, int H, int I, const uint16_t* Wd, const float* p, const float* topk_w,
+                   float* part, int32_t* err, hipStream_t stream, const VqP* vq, const AlignOut* align) {
+    const size_t lds = (size_t)kDownStage * 8 * sizeof(float);
+    const dim3 grid((H + CB - 1) / CB, plan.max_blocks);
+    const VqP v = vq ? *vq : VqP{};
+    const AlignOut a = align ? *align : AlignOut{};
+    if (vq && align)
+        MOE_LAUNCH((down_kernel<CB, MFMA, true, true>), grid, dim3(kThreads), lds, stream, plan, H, I, Wd, p, topk_w,
+                   part, err, v, a);
+    else if (vq)
+        MOE_LAUNCH((down_kernel<CB, MFMA, true, false>), grid, dim3(kThreads), lds, stream, plan, H, I, Wd, p, topk_w,
+                   part, err, v, a);
+    else
+        MOE_LAUNCH((down_kernel<CB, MFMA, false, false>), grid, dim3(kThreads), lds, stream, plan, H, I, Wd, p,
+                   topk_w, part, err, v, a);
+    return hipGetLastError();
+}
+}  // namespace
+
 hipError_t launch_down(const PlanArgs& plan, int H, int I, const uint16_t* Wd, const float* p, const float* topk_w,
-                       float* part, int32_t* err, hipStream_t stream) {
+                       float* part, int32_t* err, hipStream_t stream, const VqP* vq, const AlignOut* align) {
+    if ((vq && (!vq->vp || vq->ny < 1)) || (align && (!vq || plan.R > MOE_WAVE || !align->sorted_routes ||
+                                                      !align->block_expert || !align->counts)))
+        return hipErrorInvalidValue;
     // 256-column blocks on the matrix cores when that still gives two
     // workgroups per CU, else 128-column blocks on the vector ALUs (few
     // experts: there the MFMA pass measured slower, 20.4 vs 19.0 us on four
     // tokens of top-8 over 128 experts, 2048 x 768, while on 21 tokens the
     // 256-column MFMA pass took 46.3 us against 54.4 us)
-    const size_t lds = (size_t)kDownStage * 8 * sizeof(float);
-    if ((size_t)plan.max_blocks * ((H + 255) / 256) >= 512) {
-        const dim3 grid((H + 255) / 256, plan.max_blocks);
-        MOE_LAUNCH((down_kernel<256, true>), grid, dim3(kThreads), lds, stream, plan, H, I, Wd, p, topk_w, part, err);
-    } else {
-        const dim3 grid((H + 127) / 128, plan.max_blocks);
-        MOE_LAUNCH((down_kernel<128, false>), grid, dim3(kThreads), lds, stream, plan, H, I, Wd, p, topk_w, part, err);
-    }
-    return hipGetLastError();
+    if ((size_t)plan.max_blocks * ((H + 255) / 256) >= 512)
+        return down_cb<256, true>(plan, H, I, Wd, p, topk_w, part, err, stream, vq, align);
+    return down_cb<128, false>(plan, H, I, Wd, p, topk_w, part, err, stream, vq, align);
 }
 
 hipError_t launch_combine(const int32_t* topk_ids, int M, int k, int E, int H, int nchunk, const float* part, float* y,

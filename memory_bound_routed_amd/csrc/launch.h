@@ -85,6 +85,7 @@ struct PlanArgs {
     int k;
     FastDiv fk;                    // division by k (route -> token)
     int b;
+    FastDiv fb;                    // division by b
     int max_blocks;                // cap / b
     int E;
 };
@@ -118,8 +119,23 @@ hipError_t launch_decode_fused(const PlanArgs& plan, const RouteArgs& route, con
 hipError_t launch_gateup_dense(const PlanArgs& plan, const float* h, int H, int I, const uint16_t* Wg,
                                const uint16_t* Wu, float* p, int32_t* err, hipStream_t stream);
 // part[route][chunk][H] = sum over the chunk's rows of (a_route * p[route][j]) * Wd[e][j][:]
+// With vq: p[r][j] = SiLU(sum_y vp[r][y][0][j]) * sum_y vp[r][y][1][j] from
+// the VQ gate/up partials (rows y in order) instead of a p array.  With
+// align (needs R <= 64): the plan is not read; every workgroup aligns the R
+// routes from plan.topk_ids itself (the canonical plan, ballots of the id
+// bits) and workgroup (0, 0) writes the plan to align's arrays.
+struct VqP {
+    const float* vp;
+    int ny;
+};
+struct AlignOut {
+    int32_t* sorted_routes;
+    int32_t* block_expert;
+    int32_t* counts;
+};
 hipError_t launch_down(const PlanArgs& plan, int H, int I, const uint16_t* Wd, const float* p, const float* topk_w,
-                       float* part, int32_t* err, hipStream_t stream);
+                       float* part, int32_t* err, hipStream_t stream, const VqP* vq = nullptr,
+                       const AlignOut* align = nullptr);
 // y[t][:] = sum over valid routes of token t and chunks of part[route][chunk][:]
 hipError_t launch_combine(const int32_t* topk_ids, int M, int k, int E, int H, int nchunk, const float* part, float* y,
                           hipStream_t stream);
@@ -148,9 +164,14 @@ struct SelRoute;
 bool vq_routes_ok(int E, int k);
 hipError_t launch_gateup_vqlr(const int32_t* topk_ids, int R, int k, int E, const VqArgs& vq, const float* h, int H,
                               int I, float* vp, int32_t* err, hipStream_t stream, const SelRoute* route = nullptr);
-// p[r][j] = SiLU(sum_s vp[r][s][0][j]) * (sum_s vp[r][s][1][j]), sums in
-// slice order, for the R routes.  With plan: also the canonical alignment of
-// the R routes from ids (written by the previous launch), by workgroup (0, 0).
+// Partials per route and projection of the VQ gate/up launch for R routes:
+// vp fp32 [R][vq_rows][2][I], row y the sum over the slices one workgroup
+// took (see vqlr.hip).
+int vq_rows(int R, int H, int d);
+// p[r][j] = SiLU(sum_y vp[r][y][0][j]) * (sum_y vp[r][y][1][j]), sums in
+// row order, for the R routes (ny <= 16 rows).  With plan: also the
+// canonical alignment of the R routes from ids (written by the previous
+// launch), by workgroup (0, 0).
 struct VqPlanJob {
     const int32_t* ids;  // [R]
     int E, b;
@@ -159,7 +180,7 @@ struct VqPlanJob {
     int32_t* counts;
     int32_t* err;
 };
-hipError_t launch_vq_finish(const float* vp, int R, int I, int nslice, float* p, hipStream_t stream,
+hipError_t launch_vq_finish(const float* vp, int R, int I, int ny, float* p, hipStream_t stream,
                             const VqPlanJob* plan = nullptr);
 
 // ---- chansparse.hip

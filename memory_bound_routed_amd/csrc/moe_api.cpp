@@ -170,7 +170,7 @@ size_t workspace_layout(const moe_config& c, size_t MT, char* base, Workspace* w
         sizeof(float) * moe::gemv_slices(c.H, c.E) * MT * c.E,          // router partials
         sizeof(float) * zsl * MT * c.lr_r,                              // z = D^T h partials (gate)
         sizeof(float) * zsl * MT * c.lr_r,                              // z partials (up)
-        sizeof(float) * R * c.I * (c.wformat == MOE_WFORMAT_VQLR ? 1 + 2 * (size_t)moe::vq_slices(c.H, c.vq_d) : 1),  // p (+ VQ slice partials)
+        sizeof(float) * R * c.I * (c.wformat == MOE_WFORMAT_VQLR ? 1 + 2 * (size_t)moe::vq_slices(c.H, c.vq_d) : 1),  // p (+ VQ gate/up partials)
         sizeof(float) * down,                                           // down partials
         c.max_keep > 0 ? sizeof(int32_t) * MT * c.top_k * (1 + (size_t)c.I) : 0,  // per-slot kept lists
         sizeof(float) * MT * nchan * c.H,                               // channel partials
@@ -387,7 +387,7 @@ moe_status expert_forward_impl(const Exec& x, bool z_ready, const float* h, int3
                                const float* topk_w, const int32_t* sorted_routes, const int32_t* block_expert,
                                const int32_t* counts, int32_t keep_channels, int32_t* kept_out, float* y,
                                hipStream_t s, const moe::SelRoute* vq_route = nullptr,
-                               const moe::VqPlanJob* vq_plan = nullptr) {
+                               const moe::AlignOut* vq_plan = nullptr) {
     const moe_config& c = x.c;
     if (M == 0) return MOE_OK;
     if (!h || !topk_ids || !topk_w || !y || !aligned(h, 16) || !aligned(y, 16)) return MOE_ERR_INVALID_ARG;
@@ -411,6 +411,7 @@ moe_status expert_forward_impl(const Exec& x, bool z_ready, const float* h, int3
     plan.k = c.top_k;
     plan.fk = FastDiv((uint32_t)c.top_k);
     plan.b = c.block_b;
+    plan.fb = FastDiv((uint32_t)c.block_b);
     plan.max_blocks = (int)(align_capacity64(M, c.top_k, c.E, c.block_b) / c.block_b);
     plan.E = c.E;
 
@@ -427,6 +428,10 @@ moe_status expert_forward_impl(const Exec& x, bool z_ready, const float* h, int3
             Launch l(x.prof, MOE_KERNEL_GATEUP);
             e = moe::launch_gateup_dense(plan, h, c.H, c.I, x.w.w_gate, x.w.w_up, x.ws.p, x.ws.err, s);
             l.done();
+            if (e != hipSuccess) return MOE_ERR_HIP;
+            Launch ld(x.prof, MOE_KERNEL_DOWN);
+            e = moe::launch_down(plan, c.H, c.I, x.w.w_down, x.ws.p, topk_w, x.ws.down_part, x.ws.err, s);
+            ld.done();
             if (e != hipSuccess) return MOE_ERR_HIP;
         } else {
             moe::GemvJob jobs[2] = {{x.w.lr_basis[0], c.lr_r, x.ws.zpart[0]},
@@ -449,25 +454,36 @@ moe_status expert_forward_impl(const Exec& x, bool z_ready, const float* h, int3
             vq.r = c.lr_r;
             vq.K = c.vq_K;
             vq.d = c.vq_d;
-            // slice partials after p in the same buffer
-            float* vp = x.ws.p + (size_t)plan.R * c.I;
-            const int nsl = moe::vq_slices(c.H, c.vq_d);
+            // the gate/up partials after p in the same buffer
+            float* const vpart = x.ws.p + (size_t)plan.R * c.I;
+            const moe::VqP vqp{vpart, moe::vq_rows(plan.R, c.H, c.vq_d)};
             {
                 Launch l(x.prof, MOE_KERNEL_GATEUP_VQLR);
-                e = moe::launch_gateup_vqlr(topk_ids, plan.R, c.top_k, c.E, vq, h, c.H, c.I, vp, x.ws.err, s,
+                e = moe::launch_gateup_vqlr(topk_ids, plan.R, c.top_k, c.E, vq, h, c.H, c.I, vpart, x.ws.err, s,
                                             vq_route);
                 l.done();
                 if (e != hipSuccess) return MOE_ERR_HIP;
             }
-            Launch l(x.prof, MOE_KERNEL_VQ_FINISH);
-            e = moe::launch_vq_finish(vp, plan.R, c.I, nsl, x.ws.p, s, vq_plan);
+            // Up to 64 routes the down launch adds the partials itself (and in
+            // the decode step aligns the routes); above, a finishing launch
+            // forms p (and aligns), then the down launch reads p.  Both form
+            // p = SiLU(o_gate) * o_up with the same sums, bit for bit.
+            const bool in_down = plan.R <= MOE_WAVE;
+            if (!in_down) {
+                const moe::VqPlanJob pj = vq_plan ? moe::VqPlanJob{topk_ids, c.E, c.block_b, vq_plan->sorted_routes,
+                                                                   vq_plan->block_expert, vq_plan->counts, x.ws.err}
+                                                  : moe::VqPlanJob{};
+                Launch l(x.prof, MOE_KERNEL_VQ_FINISH);
+                e = moe::launch_vq_finish(vqp.vp, plan.R, c.I, vqp.ny, x.ws.p, s, vq_plan ? &pj : nullptr);
+                l.done();
+                if (e != hipSuccess) return MOE_ERR_HIP;
+            }
+            Launch l(x.prof, MOE_KERNEL_DOWN);
+            e = moe::launch_down(plan, c.H, c.I, x.w.w_down, x.ws.p, topk_w, x.ws.down_part, x.ws.err, s,
+                                 in_down ? &vqp : nullptr, in_down && vq_plan ? vq_plan : nullptr);
             l.done();
             if (e != hipSuccess) return MOE_ERR_HIP;
         }
-        Launch l(x.prof, MOE_KERNEL_DOWN);
-        e = moe::launch_down(plan, c.H, c.I, x.w.w_down, x.ws.p, topk_w, x.ws.down_part, x.ws.err, s);
-        l.done();
-        if (e != hipSuccess) return MOE_ERR_HIP;
     }
     Launch l(x.prof, MOE_KERNEL_COMBINE);
     e = moe::launch_combine(topk_ids, M, c.top_k, c.E, c.H, nchunk, x.ws.down_part, y, s);
@@ -515,8 +531,9 @@ moe_status decode_step_impl(const Exec& x, const float* h, int32_t M, int32_t* t
     const int nsl = moe::router_slices(c.H, c.E);
     if (c.wformat == MOE_WFORMAT_VQLR && M > 0 && moe::vq_routes_ok(c.E, c.top_k)) {
         // router GEMV partials (and z = D^T h in workgroups of their own),
-        // then a gate/up launch whose workgroups route their tokens, a finish
-        // launch that also aligns, down and combine
+        // then a gate/up launch whose workgroups route their tokens, a down
+        // launch that adds the gate/up partials (and aligns the routes), and
+        // the combine
         if (!h || !topk_ids || !topk_w || !sorted_routes || !block_expert || !counts || !y || !aligned(h, 16) ||
             !aligned(y, 16))
             return MOE_ERR_INVALID_ARG;
@@ -538,7 +555,7 @@ moe_status decode_step_impl(const Exec& x, const float* h, int32_t M, int32_t* t
         route.ids = topk_ids;
         route.wts = topk_w;
         route.logits = logits_out;
-        const moe::VqPlanJob pj{topk_ids, c.E, c.block_b, sorted_routes, block_expert, counts, x.ws.err};
+        const moe::AlignOut pj{sorted_routes, block_expert, counts};
         return expert_forward_impl(x, true, h, M, topk_ids, topk_w, sorted_routes, block_expert, counts, 0, nullptr,
                                    y, s, &route, &pj);
     }
@@ -565,6 +582,7 @@ moe_status decode_step_impl(const Exec& x, const float* h, int32_t M, int32_t* t
     plan.k = c.top_k;
     plan.fk = FastDiv((uint32_t)c.top_k);
     plan.b = c.block_b;
+    plan.fb = FastDiv((uint32_t)c.block_b);
     plan.max_blocks = c.top_k;
     plan.E = c.E;
     moe::RouteArgs route{};

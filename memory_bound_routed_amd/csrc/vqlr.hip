@@ -141,6 +141,7 @@ constexpr int kPassCh = 16 * kVqWaves;         // channels per pass (16 per wave
 constexpr int kRegPasses = 6;                  // passes held in registers (the rest are loaded one at a time)
 constexpr int kLrPre = 4;                      // owned low-rank chunks whose coefficients are requested up front
 constexpr int kAhead = 2;                      // index passes requested before T, then kept in flight ahead of the gathers
+constexpr int kOutPer = (kRegPasses + 3) / 4;  // passes a lane stores (lane q of a quad: passes 4 m + q)
 constexpr int kVqResident = 512;               // gate/up workgroups resident at once (2 per CU x 256 CUs)
 
 // Grid (x = 2 * route + projection, padded to a multiple of 8; y = first T
@@ -369,6 +370,9 @@ gateup_vqt_kernel(const int32_t* __restrict__ topk_ids, int R, int k, FastDiv fk
     // once): the routing, code-book, z and LDS set-up above is done once,
     // and a later slice's index, coefficient and h loads go out before the
     // barrier that waits for every wave to finish reading the previous T.
+    float osum[kOutPer];  // per lane: the sum over the workgroup's slices of the passes it stores
+#pragma unroll
+    for (int m = 0; m < kOutPer; ++m) osum[m] = 0.f;
     for (int s = s0; s < nslice; s += ny) {  // uniform
         // The lane id through an empty asm: everything derived from it is
         // formed again per slice instead of being hoisted out of the loop
@@ -507,15 +511,13 @@ gateup_vqt_kernel(const int32_t* __restrict__ topk_ids, int R, int k, FastDiv fk
             acc[p] += dpp<MOE_DPP_QUAD_XOR1>(acc[p]);
             acc[p] += dpp<MOE_DPP_QUAD_XOR2>(acc[p]);
         }
-        float* dst = vp + ((size_t)(r * nslice + s) * 2 + P) * I + 16 * wave + lane / 4;
 #pragma unroll
-        for (int m = 0; m < (kRegPasses + 3) / 4; ++m) {
+        for (int m = 0; m < kOutPer; ++m) {
             float v = acc[4 * m];
 #pragma unroll
             for (int x = 1; x < 4; ++x)
                 if (4 * m + x < kRegPasses) v = q == x ? acc[4 * m + x] : v;
-            const int p = 4 * m + q;
-            if (p < min(npass, kRegPasses) && kPassCh * p + 16 * wave + lane / 4 < I) dst[kPassCh * p] = v;
+            osum[m] = first ? v : osum[m] + v;  // the workgroup's slices in ascending order
         }
         for (int p = kRegPasses; p < npass; ++p) {  // further passes: indices loaded here
             const int j = kPassCh * p + 16 * wave + lane / 4;
@@ -531,7 +533,20 @@ gateup_vqt_kernel(const int32_t* __restrict__ topk_ids, int R, int k, FastDiv fk
             }
             a += dpp<MOE_DPP_QUAD_XOR1>(a);
             a += dpp<MOE_DPP_QUAD_XOR2>(a);
-            if (q == 0 && j < I) vp[((size_t)(r * nslice + s) * 2 + P) * I + j] = a;
+            if (q == 0 && j < I) {  // added to the earlier slices' sum this thread stored
+                float* o = vp + ((size_t)(r * ny + s0) * 2 + P) * I + j;
+                *o = first ? a : *o + a;
+            }
+        }
+    }
+    // lane q of a quad stores passes 4 m + q: the sum over the workgroup's slices
+    {
+        const int q = lane % 4;
+        float* dst = vp + ((size_t)(r * ny + s0) * 2 + P) * I + 16 * wave + lane / 4;
+#pragma unroll
+        for (int m = 0; m < kOutPer; ++m) {
+            const int p = 4 * m + q;
+            if (p < min(npass, kRegPasses) && kPassCh * p + 16 * wave + lane / 4 < I) dst[kPassCh * p] = osum[m];
         }
     }
 }
@@ -539,16 +554,7 @@ gateup_vqt_kernel(const int32_t* __restrict__ topk_ids, int R, int k, FastDiv fk
 template <int D, bool LR, bool ROUTE>
 hipError_t vqt_lr(const int32_t* ids, int R, int k, int E, const VqArgs& vq, const float* h, int H, int I, float* vp,
                   int32_t* err, const SelRoute& route, hipStream_t stream) {
-    // Slice rows of the grid: one per slice while the (route, projection,
-    // slice) workgroups fit on the device at once (two per CU, the LDS of
-    // this kernel's T, on 256 CUs); beyond that a workgroup takes several
-    // slices of its route and projection in turn, so no workgroup waits for
-    // a second round and pays the route, code-book and z set-up again.
-    const int nslice = (H / D + kSlice - 1) / kSlice;
-    const int units = 2 * R * nslice;
-    const int per = (units + kVqResident - 1) / kVqResident;  // slices per workgroup
-    const int ny = (nslice + per - 1) / per;
-    const dim3 grid((2 * R + 7) / 8 * 8, ny);
+    const dim3 grid((2 * R + 7) / 8 * 8, vq_rows(R, H, D));
     // 16-byte index loads when every quarter segment is 16-byte aligned
     if ((H / D) % 16 == 0)
         MOE_LAUNCH((gateup_vqt_kernel<D, 16, LR, ROUTE>), grid, dim3(kVqThreads), 0, stream, ids, R, k,
@@ -571,12 +577,12 @@ hipError_t vqt_d(const int32_t* ids, int R, int k, int E, const VqArgs& vq, cons
     return vqt_lr<D, false, false>(ids, R, k, E, vq, h, H, I, vp, err, none, stream);
 }
 
-// One thread per (route, channel): the slice partials of both projections,
-// all loads issued together, added in slice order.  With an alignment job
-// (the decode step, whose gate/up launch routed the tokens itself),
-// workgroup (0, 0) then aligns the routes from the ids that launch stored:
-// the canonical plan of the down projection.
-constexpr int kMaxSlices = 16;
+// One thread per (route, channel): the partial rows of both projections,
+// all loads issued together, added in row order, p = SiLU(o_gate) * o_up.
+// With an alignment job (the decode step, whose gate/up launch routed the
+// tokens itself), workgroup (0, 0) then aligns the routes from the ids that
+// launch stored: the canonical plan of the down projection.
+constexpr int kMaxRows = 16;
 
 struct AlignJob {
     const int32_t* ids;  // [R] route ids (null: no alignment)
@@ -589,26 +595,26 @@ struct AlignJob {
 };
 
 __global__ void __launch_bounds__(kThreads)
-vq_finish_kernel(const float* __restrict__ vp, int R, int I, int nslice, float* __restrict__ p, AlignJob aj) {
+vq_finish_kernel(const float* __restrict__ vp, int R, int I, int ny, float* __restrict__ p, AlignJob aj) {
     extern __shared__ __align__(16) int asm_lds[];
     const int j = blockIdx.x * kThreads + threadIdx.x;
     const int r = blockIdx.y;
     if (j < I) {
-    const float* src = vp + (size_t)r * nslice * 2 * I + j;
-    float g[kMaxSlices], u[kMaxSlices];
+        const float* src = vp + (size_t)r * ny * 2 * I + j;
+        float g[kMaxRows], u[kMaxRows];
 #pragma unroll
-    for (int sl = 0; sl < kMaxSlices; ++sl) {
-        const int sc = min(sl, nslice - 1);
-        g[sl] = src[(size_t)(2 * sc) * I];
-        u[sl] = src[(size_t)(2 * sc + 1) * I];
-    }
-    float og = 0.f, ou = 0.f;
+        for (int y = 0; y < kMaxRows; ++y) {
+            const int yc = min(y, ny - 1);
+            g[y] = src[(size_t)(2 * yc) * I];
+            u[y] = src[(size_t)(2 * yc + 1) * I];
+        }
+        float og = 0.f, ou = 0.f;
 #pragma unroll
-    for (int sl = 0; sl < kMaxSlices; ++sl) {
-        og += sl < nslice ? g[sl] : 0.f;
-        ou += sl < nslice ? u[sl] : 0.f;
-    }
-    p[(size_t)r * I + j] = silu_mul(og, ou);
+        for (int y = 0; y < kMaxRows; ++y) {
+            og += y < ny ? g[y] : 0.f;
+            ou += y < ny ? u[y] : 0.f;
+        }
+        p[(size_t)r * I + j] = silu_mul(og, ou);
     }
     if (aj.ids && blockIdx.x == 0 && blockIdx.y == 0) {  // uniform
         if (R <= MOE_WAVE) {
@@ -624,9 +630,9 @@ vq_finish_kernel(const float* __restrict__ vp, int R, int I, int nslice, float* 
 
 }  // namespace
 
-hipError_t launch_vq_finish(const float* vp, int R, int I, int nslice, float* p, hipStream_t stream,
+hipError_t launch_vq_finish(const float* vp, int R, int I, int ny, float* p, hipStream_t stream,
                             const VqPlanJob* plan) {
-    if (nslice < 1 || nslice > kMaxSlices || R < 1) return hipErrorInvalidValue;
+    if (ny < 1 || ny > kMaxRows || R < 1) return hipErrorInvalidValue;
     AlignJob aj{};
     size_t lds = 0;
     if (plan) {
@@ -636,12 +642,24 @@ hipError_t launch_vq_finish(const float* vp, int R, int I, int nslice, float* p,
                       plan->counts, plan->err};
         lds = R > MOE_WAVE ? align_lds_bytes(R, plan->E) : 0;
     }
-    MOE_LAUNCH(vq_finish_kernel, dim3((I + kThreads - 1) / kThreads, R), dim3(kThreads), lds, stream, vp, R, I,
-               nslice, p, aj);
+    MOE_LAUNCH(vq_finish_kernel, dim3((I + kThreads - 1) / kThreads, R), dim3(kThreads), lds, stream, vp, R, I, ny,
+               p, aj);
     return hipGetLastError();
 }
 
 int vq_slices(int H, int d) { return (H / d + kSlice - 1) / kSlice; }
+
+// Slice rows of the gate/up grid, and so the partials per route and
+// projection: one per slice while the (route, projection, slice) workgroups
+// fit on the device at once (two per CU, the LDS of the kernel's T, on 256
+// CUs); beyond that a workgroup takes several slices of its route and
+// projection in turn and stores their sum, so no workgroup waits for a
+// second round and pays the route, code-book and z set-up again.
+int vq_rows(int R, int H, int d) {
+    const int nslice = vq_slices(H, d);
+    const int per = (2 * R * nslice + kVqResident - 1) / kVqResident;  // slices per workgroup
+    return (nslice + per - 1) / per;
+}
 
 bool vq_routes_ok(int E, int k) { return E <= kThreads && k <= 32; }
 
