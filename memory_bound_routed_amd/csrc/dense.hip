@@ -1307,18 +1307,28 @@ hipError_t gateup_q(const PlanArgs& plan, const float* h, int H, int I, const ui
 
 // Fused tiling: 8 waves, one gate/up channel per wave and chunk; three
 // double-buffered chunks per workgroup (24 channels) up to H = 2048, one
-// chunk (8 channels, no second buffer) up to H = 4096.
+// chunk (8 channels, no second buffer) up to H = 4096.  Narrow experts (one
+// GPU's 96-channel share of a 768-channel expert under channel sharding, say)
+// would leave most CUs idle: where one chunk per workgroup still gives at
+// most one workgroup per CU, each workgroup takes one chunk, so that three
+// times as many CUs stream.  (4-wave workgroups of 4 channels measured no
+// faster on the 96-channel share: the routing prologue, not the stream, sets
+// its time.)
 constexpr int kFusedNW = 8;
 constexpr int kFusedCPW = 1;
+constexpr int kFusedFill = 256;  // workgroups that keep every CU of the device streaming
 constexpr int fused_nch(int Q) { return Q <= 4 ? 3 : 1; }
-constexpr int fused_range(int Q) { return kFusedNW * kFusedCPW * fused_nch(Q); }
+int fused_nch_for(int Q, int I, int k) {
+    constexpr int one = kFusedNW * kFusedCPW;  // channels of one chunk
+    return (long long)k * ((I + one - 1) / one) <= kFusedFill ? 1 : fused_nch(Q);
+}
 
-template <int Q, int CQ, int XG>
-hipError_t fused_q(const PlanArgs& plan, const RouteArgs& route, const float* h, const float* topk_w, int H, int I,
-                   const uint16_t* Wg, const uint16_t* Wu, const uint16_t* Wd, float* part, int32_t* err,
-                   hipStream_t stream) {
-    constexpr int NCH = fused_nch(Q);
-    const int nrange = (I + fused_range(Q) - 1) / fused_range(Q);
+template <int Q, int CQ, int NCH, int XG>
+hipError_t fused_launch(const PlanArgs& plan, const RouteArgs& route, const float* h, const float* topk_w, int H,
+                        int I, const uint16_t* Wg, const uint16_t* Wu, const uint16_t* Wd, float* part, int32_t* err,
+                        hipStream_t stream) {
+    constexpr int range = kFusedNW * kFusedCPW * NCH;
+    const int nrange = (I + range - 1) / range;
     const dim3 grid(plan.max_blocks, nrange);
     const dim3 block(kFusedNW * MOE_WAVE);
     if (H == 512 * Q && H == 2048 * CQ)
@@ -1330,13 +1340,24 @@ hipError_t fused_q(const PlanArgs& plan, const RouteArgs& route, const float* h,
     return hipGetLastError();
 }
 
+template <int Q, int CQ, int XG>
+hipError_t fused_q(const PlanArgs& plan, const RouteArgs& route, const float* h, const float* topk_w, int H, int I,
+                   const uint16_t* Wg, const uint16_t* Wu, const uint16_t* Wd, float* part, int32_t* err,
+                   hipStream_t stream) {
+    if constexpr (fused_nch(Q) > 1) {
+        if (fused_nch_for(Q, I, plan.k) == 1)
+            return fused_launch<Q, CQ, 1, XG>(plan, route, h, topk_w, H, I, Wg, Wu, Wd, part, err, stream);
+    }
+    return fused_launch<Q, CQ, fused_nch(Q), XG>(plan, route, h, topk_w, H, I, Wg, Wu, Wd, part, err, stream);
+}
+
 }  // namespace
 
 bool dense_uses_fused(int M, int H) { return M == 1 && H <= 4096; }
 
-int dense_chunks(int M, int H, int I) {
+int dense_chunks(int M, int H, int I, int k) {
     if (dense_uses_fused(M, H)) {
-        const int range = fused_range((H + 511) / 512 <= 4 ? 4 : 8);
+        const int range = kFusedNW * kFusedCPW * fused_nch_for((H + 511) / 512 <= 4 ? 4 : 8, I, k);
         return (I + range - 1) / range;
     }
     return down_chunks(I);

@@ -91,8 +91,9 @@ struct PlanArgs {
 };
 // Fused gate/up + down partials (one route per plan row group; H <= 4096).
 bool dense_uses_fused(int M, int H);
-// Number of down partial chunks per route of the schedule used for (M, H, I).
-int dense_chunks(int M, int H, int I);
+// Number of down partial chunks per route of the schedule used for (M, H, I)
+// and top-k k.
+int dense_chunks(int M, int H, int I, int k);
 int down_chunks(int I);
 hipError_t launch_expert_fused(const PlanArgs& plan, const float* h, const float* topk_w, int H, int I,
                                const uint16_t* Wg, const uint16_t* Wu, const uint16_t* Wd, float* part, int32_t* err,

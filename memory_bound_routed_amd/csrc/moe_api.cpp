@@ -156,7 +156,7 @@ size_t workspace_layout(const moe_config& c, size_t MT, char* base, Workspace* w
     // (one token) writes dense_chunks of them for each of its top_k routes
     size_t down = R * (size_t)moe::down_chunks(c.I) * c.H;
     if (moe::dense_uses_fused(1, c.H)) {
-        const size_t f = (size_t)c.top_k * moe::dense_chunks(1, c.H, c.I) * c.H;
+        const size_t f = (size_t)c.top_k * moe::dense_chunks(1, c.H, c.I, c.top_k) * c.H;
         down = f > down ? f : down;
     }
     const size_t nchan = c.max_keep > 0 ? (c.max_keep + kChanChunk - 1) / kChanChunk : 0;
@@ -417,7 +417,7 @@ moe_status expert_forward_impl(const Exec& x, bool z_ready, const float* h, int3
 
     int nchunk = moe::down_chunks(c.I);
     if (c.wformat == MOE_WFORMAT_DENSE && moe::dense_uses_fused(M, c.H)) {
-        nchunk = moe::dense_chunks(M, c.H, c.I);
+        nchunk = moe::dense_chunks(M, c.H, c.I, c.top_k);
         Launch l(x.prof, MOE_KERNEL_EXPERT_FUSED);
         e = moe::launch_expert_fused(plan, h, topk_w, c.H, c.I, x.w.w_gate, x.w.w_up, x.w.w_down, x.ws.down_part,
                                      x.ws.err, s);
@@ -603,7 +603,8 @@ moe_status decode_step_impl(const Exec& x, const float* h, int32_t M, int32_t* t
         if (e != hipSuccess) return MOE_ERR_HIP;
     }
     Launch l(x.prof, MOE_KERNEL_COMBINE);
-    e = moe::launch_combine(topk_ids, 1, c.top_k, c.E, c.H, moe::dense_chunks(1, c.H, c.I), x.ws.down_part, y, s);
+    e = moe::launch_combine(topk_ids, 1, c.top_k, c.E, c.H, moe::dense_chunks(1, c.H, c.I, c.top_k),
+                            x.ws.down_part, y, s);
     l.done();
     return hip_status(e);
 }

@@ -189,6 +189,10 @@ WORKLOADS: Dict[str, Workload] = {w.name: w for w in [
     Workload("dense_h2048_i768_e128_k8_m16", H=2048, I=768, E=128, k=8, M=16, seed=1007),
     Workload("vqlr_h2048_i768_e128_k8_m8_d8_K256_r64", H=2048, I=768, E=128, k=8, M=8, seed=1006, vq=True),
     Workload("vqlr_h2048_i768_e128_k8_m16_d8_K256_r64", H=2048, I=768, E=128, k=8, M=16, seed=1007, vq=True),
+    # one GPU's share of the batch-1 dense layer under 8-way channel sharding:
+    # 96 of every expert's 768 channels (same seed: the same router, hidden
+    # states and routing as dense_h2048_i768_e128_k8_m1)
+    Workload("shard8_h2048_i96_e128_k8_m1", H=2048, I=96, E=128, k=8, M=1, seed=1002, layers=48),
 ]}
 
 

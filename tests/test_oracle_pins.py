@@ -434,6 +434,25 @@ def test_sparse_forward_is_the_kept_subset_of_the_channel_sum():
     np.testing.assert_allclose(y[0], want, rtol=1e-12)
 
 
+def test_channel_shards_sum_to_the_full_output():
+    """Any partition of the channels (here G contiguous shards, as channel
+    sharding over G GPUs would own them) splits y into per-shard outputs that
+    add up to the full one: the channel sum of the channel-selection page's
+    background section."""
+    rng = np.random.default_rng(16)
+    H, I, E, G = 16, 12, 5, 4
+    Wg, Wu, Wd = (rand_bf16(rng, (E, I, H), 0.4) for _ in range(3))
+    h = rng.standard_normal((3, H)).astype(np.float32)
+    ids = np.array([[4, 0], [2, 4], [1, 3]])
+    a = np.array([[0.7, 0.3], [0.55, 0.45], [0.9, 0.1]])
+    full = O.dense_forward(h, ids, a, Wg, Wu, Wd)
+    n = I // G
+    parts = [O.dense_forward(h, ids, a, *(np.ascontiguousarray(W[:, g * n:(g + 1) * n, :]) for W in (Wg, Wu, Wd)))
+             for g in range(G)]
+    np.testing.assert_allclose(sum(parts), full, rtol=1e-12, atol=1e-15)
+    assert np.abs(full).max() > 0 and all(np.abs(p).max() > 0 for p in parts)
+
+
 # ---------------------------------------------------------------- VQ + low rank
 
 def test_vq_reconstruction_hand_example():
