@@ -18,10 +18,11 @@
 // 4-byte LDS read and one add per index byte, where applying each code word
 // to h directly takes a 4d-byte read and d FMAs.  Each slice workgroup also
 // adds the low-rank term of a share of the channels (16-channel chunks dealt
-// out over the slices) and stores one partial per (route, slice, projection,
-// channel).  A finishing kernel adds a route's slice partials in slice order
-// and forms p = SiLU(o_gate) * o_up for the down projection (the joint
-// accumulation of the page, split across the two kernels).
+// out over the slices) and stores one partial per (route, projection,
+// channel): the sum, in slice order, of the slices it took.  The down
+// launch (up to 64 routes) or a finishing kernel (more) adds a route's
+// partial rows in row order and forms p = SiLU(o_gate) * o_up (the joint
+// accumulation of the page, split across the kernels).
 //
 // The grid is route-major (one token's use of an expert per workgroup set):
 // a route never waits for another route of its expert, and an expert routed
