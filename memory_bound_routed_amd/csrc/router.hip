@@ -38,6 +38,7 @@ struct GemvJobs {
 // part[slice][t][e] as for slice_partial, but there are cgw/E times fewer
 // slices for the last workgroup to add.
 constexpr int kRouterCG = 32;
+constexpr int kRedPad = 8;  // floats after each of the 8 row-group blocks of a tile's sums
 struct RouterTiles {
     int cgw, tpr, rpt, rows, nrs, ncg;
     __host__ __device__ RouterTiles(int H, int E) {
@@ -93,17 +94,21 @@ __device__ __forceinline__ void router_tile(const float* __restrict__ h, int M, 
 #pragma unroll
             for (int c = 0; c < 8; ++c) acc[t][c] = fmaf(hv[u][t], wf[c], acc[t][c]);
     }
+    // red holds the row-group sums [rg][t][col] in 8 blocks of gpl row
+    // groups, each block padded by kRedPad floats: a block spans 256 TT
+    // floats, a multiple of the LDS banks, so without the padding the 8
+    // lanes that read one column (one per block) would hit one bank.
+    const int gpl = tl.rpt / 8;  // row groups per block (and per lane below), a multiple of 8
 #pragma unroll
     for (int t = 0; t < TT; ++t)
 #pragma unroll
-        for (int c = 0; c < 8; ++c) red[(rg * TT + t) * tl.cgw + c8 * 8 + c] = acc[t][c];
+        for (int c = 0; c < 8; ++c) red[(rg * TT + t) * tl.cgw + c8 * 8 + c + (rg / gpl) * kRedPad] = acc[t][c];
     __syncthreads();
     // output o = t*cgw + c: lanes 8o' .. 8o'+7 of pass p (o = 32p + o'; every
     // lane takes part in the butterfly).  The row groups of a lane (gpl = 8,
     // 16 or 32) are read 8 at a time for every pass at once, and added in
     // row-group order.
     const int sub = tid % 8;
-    const int gpl = tl.rpt / 8;  // row groups per lane, a multiple of 8
     const int nout = Mg * tl.cgw;
     constexpr int kOutPerPass = kThreads / 8;
     constexpr int NP = (TT * kRouterCG + kOutPerPass - 1) / kOutPerPass;  // passes, nout <= TT * cgw
@@ -114,7 +119,7 @@ __device__ __forceinline__ void router_tile(const float* __restrict__ h, int M, 
         v[p] = 0.f;
         const int o = min(p * kOutPerPass + tid / 8, nout - 1);  // clamped reads are dropped below
         const int t = o / tl.cgw, c = o - t * tl.cgw;
-        src[p] = red + ((size_t)sub * gpl * TT + t) * tl.cgw + c;
+        src[p] = red + ((size_t)sub * gpl * TT + t) * tl.cgw + c + sub * kRedPad;
     }
     for (int g0 = 0; g0 < gpl; g0 += 8) {
         float x[NP][8];
@@ -464,15 +469,14 @@ gemv_partials_kernel(const float* __restrict__ h, int M, int H, GemvJobs jobs) {
 
 size_t tile_lds_bytes(int H, int N) {
     const RouterTiles tl(H, N);
-    return (size_t)tl.rpt * kTokTile * tl.cgw * sizeof(float);
+    return ((size_t)tl.rpt * kTokTile * tl.cgw + 8 * kRedPad) * sizeof(float);
 }
 
 // LDS of the one-launch router: the tile's row-group sums, or the keys and
 // rank counts of the top-k (8 + 2*4 bytes per token and expert), whichever
 // is larger.
 size_t router_lds_bytes(int H, int E) {
-    const RouterTiles tl(H, E);
-    const size_t tile = (size_t)tl.rpt * kTokTile * tl.cgw * sizeof(float);
+    const size_t tile = tile_lds_bytes(H, E);
     const size_t topk = (size_t)kTokTile * E * (sizeof(uint64_t) + 2 * sizeof(int));
     return tile > topk ? tile : topk;
 }
@@ -509,7 +513,7 @@ hipError_t launch_router_partials(const float* h, int M, int H, const uint16_t* 
                                   hipStream_t stream, const RotJob* rot, const GemvJob* jobs, int njobs) {
     if (M < 1 || E % 8 != 0 || njobs < 0 || njobs > kMaxJobs || (njobs > 0 && !jobs)) return hipErrorInvalidValue;
     const RouterTiles tl(H, E);
-    size_t lds = (size_t)tl.rpt * (M == 1 ? 1 : kTokTile) * tl.cgw * sizeof(float);
+    size_t lds = ((size_t)tl.rpt * (M == 1 ? 1 : kTokTile) * tl.cgw + 8 * kRedPad) * sizeof(float);
     int grid = router_grid(H, E);
     GemvJobs js{};
     for (int i = 0; i < njobs; ++i) {
