@@ -968,6 +968,8 @@ def _step_outputs(layer, M):
     "k_eq_e",        # k = E = 16: every expert selected
     "ties",          # zero router weights + tied bias: the order is decided by the expert ids
     "m3_fallback",   # three tokens: the separate launches
+    "i256_one_chunk",     # I=256, top-8: one 8-channel chunk per fused workgroup (256 workgroups)
+    "i280_three_chunks",  # I=280: three chunks per workgroup, the last range 16 channels
 ])
 def test_decode_step_matches_separate_calls(mb, case):
     """moe_decode_step gives bit for bit the outputs of moe_route_align +
@@ -983,6 +985,10 @@ def test_decode_step_matches_separate_calls(mb, case):
         "k_eq_e": dict(wl=synth.small_workload("ds_keqe", H=256, I=16, E=16, k=16, M=1, seed=44)),
         "ties": dict(wl=synth.small_workload("ds_ties", H=256, I=16, E=16, k=4, M=1, seed=45)),
         "m3_fallback": dict(wl=synth.small_workload("ds_m3", H=256, I=24, E=32, k=4, M=3, seed=46)),
+        # the edge of the narrow-expert tiling: k * ceil(I / 8) = 256 takes one
+        # 8-channel chunk per workgroup, 280 channels three (ragged last range)
+        "i256_one_chunk": dict(wl=synth.small_workload("ds_i256", H=2048, I=256, E=128, k=8, M=1, seed=47)),
+        "i280_three_chunks": dict(wl=synth.small_workload("ds_i280", H=2048, I=280, E=128, k=8, M=1, seed=48)),
     }[case]
     wl = specs["wl"]
     say("decode step vs separate calls:", case, dict(H=wl.H, I=wl.I, E=wl.E, k=wl.k, M=wl.M, b=wl.block_b))
@@ -1030,7 +1036,8 @@ def test_decode_step_matches_separate_calls(mb, case):
 ])
 def test_vq_decode_step_matches_separate_calls(mb, case):
     """The VQ decode step, whose gate/up workgroups route their tokens from
-    the router's slice partials and whose finish launch aligns the routes,
+    the router's slice partials and whose down launch (up to 64 routes) or
+    finish launch (more) aligns the routes,
     gives bit for bit the ids, affinities, logits, plan and y of
     moe_route_align + moe_expert_forward; y matches the oracle."""
     import torch
